@@ -1,0 +1,549 @@
+"""Plain, slow, CPU reference of the Kitty 2-bit KV cache hot path.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+Sources, cited by name throughout:
+
+* [Kitty] "Kitty: Accurate and Efficient 2-bit KV Cache Quantization with
+  Dynamic Channel-wise Precision Boost" (arXiv 2511.18643), Abstract: Key
+  channels are ranked by sensitivity and a small fraction is kept at higher
+  precision; each mixed-precision Key page is decomposed into two tensors of
+  uniform 2-bit precision inside a page-centric KV layout.
+* [Velox] VeloxQuant-MLX documentation, "Kitty -- Dynamic Channel-wise
+  Mixed-Precision Keys": section "How it works / Prefill phase" steps 1-3
+  (per-channel variance over the token axis, top hi_fraction x D channels at
+  hi_bit = 4, the rest at lo_bit = 2, asymmetric min/max groups of
+  group_size = 32 tokens), section "Effective bit-width" (avg_bits formula),
+  table "Tuning avg_bits".
+
+Arithmetic conventions (the readings are listed in the design doc):
+
+* every float32 operation is a separate IEEE round-to-nearest-even op (numpy
+  float32 arithmetic; no fused multiply-add, denormals kept);
+* ``f16`` is float32 -> float16 round-to-nearest-even, ``f32`` exact widening;
+* the per-page channel statistics use a fixed balanced pairwise tree over the
+  32 tokens in natural order (``tree32``), never ``np.sum``/``np.var``, whose
+  orders are unspecified;
+* quantization: step s16 = f16((max - min) / L) with a correctly rounded fp32
+  division; codes q = clamp(rne((x - min) * (1 / s)), 0, L) with one fp32
+  reciprocal per group; a zero step gives all-zero codes.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+HEAD_DIM = 128          # D, the head dimension every page record assumes
+PAGE_TOKENS = 32        # tokens per page = Key group size ([Velox] group_size)
+V_GROUP = 32            # channels per Value group (one fp16 scale/min each)
+LO_LEVELS = 3           # 2-bit codes 0..3 ([Velox] lo_bit = 2)
+HI_LEVELS = 15          # 4-bit codes 0..15 ([Velox] hi_bit = 4)
+
+_F32 = np.float32
+_F16 = np.float16
+
+
+def f16(x):
+    """float32 -> float16, round to nearest even."""
+    return np.asarray(x, _F32).astype(_F16)
+
+
+def f32(x):
+    """Exact widening to float32."""
+    return np.asarray(x).astype(_F32)
+
+
+# --------------------------------------------------------------------------
+# Key page: statistics, ranking, codes, two-plane decomposition
+# --------------------------------------------------------------------------
+
+def tree32(a, axis=-2):
+    """Balanced pairwise float32 sum of 32 entries along ``axis``:
+    five levels, a'_j = a_2j + a_(2j+1), each add rounded to float32."""
+    a = np.moveaxis(np.asarray(a, _F32), axis, 0)
+    if a.shape[0] != PAGE_TOKENS:
+        raise ValueError("tree32 needs 32 entries")
+    while a.shape[0] > 1:
+        a = (a[0::2] + a[1::2]).astype(_F32)
+    return a[0]
+
+
+def page_stats(x):
+    """Per-channel statistics of one Key page ([Velox] Prefill step 1: the
+    variance of each channel over the token axis; [Kitty] ranks channels by
+    this sensitivity).
+
+    x: float32 [..., 32, D] (values of fp16 keys).  Returns (mu, m2, mn, mx),
+    each [..., D]: mean = tree32(x) / 32, m2 = tree32((x - mu)^2) (the
+    population variance times 32), and the exact min and max."""
+    x = np.asarray(x, _F32)
+    mu = (tree32(x, -2) * _F32(1.0 / PAGE_TOKENS)).astype(_F32)
+    d = (x - mu[..., None, :]).astype(_F32)
+    e = (d * d).astype(_F32)
+    m2 = tree32(e, -2)
+    return mu, m2, x.min(axis=-2), x.max(axis=-2)
+
+
+def rank_channels(m2, n_hi):
+    """Dynamic Channel-wise Precision Boost selection ([Kitty] Abstract;
+    [Velox] Prefill step 2): the n_hi channels with the largest m2, ties
+    to the lower channel index.  Returns (idx, mask): idx [..., n_hi] uint8
+    ascending, mask [..., D] bool."""
+    m2 = np.asarray(m2, _F32)
+    D = m2.shape[-1]
+    order = np.argsort(-m2, axis=-1, kind="stable")[..., :n_hi]
+    idx = np.sort(order, axis=-1)
+    mask = np.zeros(m2.shape, bool)
+    if n_hi:
+        np.put_along_axis(mask, idx, True, axis=-1)
+    if D > 256:
+        raise ValueError("uint8 channel index needs D <= 256")
+    return idx.astype(np.uint8), mask
+
+
+def quantize_levels(x, mn, mx, levels):
+    """Asymmetric min/max quantization of x onto {0..levels} ([Velox] Prefill
+    step 3).  x, mn, mx: float32, broadcastable; levels: int, broadcastable.
+    Returns (codes uint8 shaped like x, s16 float16 shaped like mn)."""
+    x = np.asarray(x, _F32)
+    mn = np.asarray(mn, _F32)
+    mx = np.asarray(mx, _F32)
+    L = np.asarray(levels, _F32)
+    r = (mx - mn).astype(_F32)
+    s16 = f16((r / L).astype(_F32))
+    s = f32(s16)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        inv = np.where(s != 0, (_F32(1.0) / s).astype(_F32), _F32(0.0)).astype(_F32)
+        t = ((x - mn).astype(_F32) * inv).astype(_F32)
+    q = np.clip(np.rint(t), 0, L).astype(np.uint8)
+    q = np.where(s != 0, q, np.uint8(0)).astype(np.uint8)
+    return q, np.broadcast_to(s16, np.broadcast_shapes(s16.shape, mn.shape)).astype(_F16)
+
+
+def quant_k_page(k16, n_hi):
+    """Quantize Key pages.  k16: fp16 [..., 32, D]; n_hi boosted channels.
+
+    Returns a dict with the direct codes ``q`` (4-bit on boosted channels,
+    2-bit elsewhere) and the two uniform 2-bit tensors of the decomposition
+    ([Kitty] Abstract): ``base`` [..., 32, D] = q >> 2 on boosted channels, q
+    elsewhere; ``boost`` [..., 32, n_hi] = the low 2 bits of q on the boosted
+    channels listed by ``idx``; ``kscale`` [..., D] fp16 = 4 * step on boosted
+    channels, step elsewhere; ``kmin`` [..., D] fp16."""
+    x = f32(k16)
+    _, m2, mn, mx = page_stats(x)
+    idx, mask = rank_channels(m2, n_hi)
+    levels = np.where(mask, HI_LEVELS, LO_LEVELS)
+    q, s16 = quantize_levels(x, mn[..., None, :], mx[..., None, :], levels[..., None, :])
+    s16 = s16[..., 0, :]
+    base = np.where(mask[..., None, :], q >> 2, q).astype(np.uint8)
+    gather = np.broadcast_to(idx[..., None, :].astype(np.intp), q.shape[:-1] + (n_hi,))
+    boost = (np.take_along_axis(q, gather, axis=-1) & 3).astype(np.uint8)
+    kscale = np.where(mask, f16(f32(s16) * _F32(4.0)), s16).astype(_F16)
+    kmin = f16(mn)
+    return dict(q=q, m2=m2, mask=mask, idx=idx, step=s16, base=base, boost=boost,
+                kscale=kscale, kmin=kmin)
+
+
+def quant_v_page(v16):
+    """Quantize Value pages: per token, groups of 32 channels, 2-bit
+    asymmetric min/max.  v16: fp16 [..., 32, D].  Returns dict with ``a``
+    [..., 32, D] codes, ``vscale``/``vmin`` [..., 32, D/32] fp16."""
+    y = f32(v16)
+    shp = y.shape
+    yg = y.reshape(shp[:-1] + (shp[-1] // V_GROUP, V_GROUP))
+    mn = yg.min(axis=-1)
+    mx = yg.max(axis=-1)
+    a, s16 = quantize_levels(yg, mn[..., None], mx[..., None], LO_LEVELS)
+    return dict(a=a.reshape(shp), vscale=s16[..., 0], vmin=f16(mn))
+
+
+def dequant_k(base, boost, kscale, kmin, idx):
+    """Dequantized keys k^ [..., 32, D] float32: on boosted channels the full
+    code is 4*base + boost at step kscale/4, elsewhere base at step kscale;
+    k^ = f32(code * step + kmin) (the product is exact, one rounding)."""
+    n_hi = idx.shape[-1]
+    qfull = base.astype(np.int32)
+    mask = np.zeros(kscale.shape, bool)
+    if n_hi:
+        gi = np.broadcast_to(idx[..., None, :].astype(np.intp), base.shape[:-1] + (n_hi,))
+        hi_base = np.take_along_axis(qfull, gi, axis=-1)
+        np.put_along_axis(qfull, gi, 4 * hi_base + boost.astype(np.int32), axis=-1)
+        np.put_along_axis(mask, idx.astype(np.intp), True, axis=-1)
+    ks = f32(kscale)
+    s_eff = np.where(mask, (ks * _F32(0.25)).astype(_F32), ks).astype(_F32)
+    prod = (qfull.astype(_F32) * s_eff[..., None, :]).astype(_F32)
+    return (prod + f32(kmin)[..., None, :]).astype(_F32)
+
+
+def dequant_v(a, vscale, vmin):
+    """Dequantized values v^ [..., 32, D] float32 = f32(a * vscale + vmin)."""
+    rep = a.shape[-1] // vscale.shape[-1]
+    s = np.repeat(f32(vscale), rep, axis=-1)
+    m = np.repeat(f32(vmin), rep, axis=-1)
+    return ((a.astype(_F32) * s).astype(_F32) + m).astype(_F32)
+
+
+# --------------------------------------------------------------------------
+# Byte layout of one page record (one page of 32 tokens x one KV head)
+# --------------------------------------------------------------------------
+#
+# This layout is this library's own design (the pages fix only that a page
+# holds two uniform 2-bit Key tensors plus the boosted channel list).  Field
+# order and sizes, n = n_hi boosted channels (0 or a multiple of 16, <= D):
+#
+#   0            K base codes   1024 B   64 chunks x 16 B
+#   1024         K boost codes  8n B     (see _boost_words)
+#   1024+8n      V codes        1024 B   64 chunks x 16 B
+#   2048+8n      kscale         fp16[128], channel order
+#   2304+8n      kmin           fp16[128]
+#   2560+8n      vscale         fp16[4][32]: [g][kappa] = token tau(kappa)
+#   2816+8n      vmin           fp16[4][32]
+#   3072+8n      idx            uint8[n], ascending
+#   total 3072 + 9n bytes.
+#
+# Code words.  Every code plane is a sequence of little-endian 32-bit words
+# holding 16 two-bit codes for two "combos" A and B of 8 elements e = 0..7:
+# element e of combo A sits at bits 16*(e%2) + 2*(e//2), element e of combo B
+# at bits 16*(e%2) + 8 + 2*(e//2).
+#
+# Chunk c (0..63) of a 16-byte plane is word x = 0..3 at byte 16c + 4x, with
+# u = c % 16 and w = c // 16:
+#   K base:  combo A element e = token u,      channel 32x + 8w + e
+#            combo B element e = token 16 + u, channel 32x + 8w + e
+#   V codes: combo A element e = token tau(w, e), channel 16*(2x) + u
+#            combo B element e = token tau(w, e), channel 16*(2x+1) + u
+# with tau(w, e) = 4w + e for e < 4, else 16 + 4w + (e - 4).
+#
+# K boost: nf = n // 32 full slot blocks, then, if n % 32 == 16, one half
+# block.  Full block b of chunk c (c = 0..63) is the word at byte 4*(c*nf+b):
+# combo A element e = token u, slot 32b + 8w + e; combo B = token 16 + u.
+# The half block is the word at byte 256*nf + 4c for c = 0..31, slots
+# 32nf + 8w + e.
+#
+# Value metadata index kappa = 8w + e stands for token tau(w, e).
+
+def record_bytes(n_hi, head_dim=HEAD_DIM):
+    if head_dim != HEAD_DIM:
+        raise ValueError("the record layout is defined for head_dim 128")
+    if n_hi < 0 or n_hi > head_dim or n_hi % 16:
+        raise ValueError("n_hi must be 0 or a multiple of 16 up to head_dim")
+    return 3072 + 9 * n_hi
+
+
+def page_bytes(n_kv_heads, n_hi):
+    """Bytes of one physical page (all KV heads), padded to 256."""
+    raw = n_kv_heads * record_bytes(n_hi)
+    return (raw + 255) // 256 * 256
+
+
+def tau(w, e):
+    w = np.asarray(w)
+    e = np.asarray(e)
+    return np.where(e < 4, 4 * w + e, 16 + 4 * w + (e - 4))
+
+
+def _word(a8, b8):
+    """Pack combos a8, b8 ([..., 8] codes 0..3) into uint32 words."""
+    a8 = np.asarray(a8, np.uint32)
+    b8 = np.asarray(b8, np.uint32)
+    w = np.zeros(a8.shape[:-1], np.uint32)
+    for e in range(8):
+        sh = 16 * (e % 2) + 2 * (e // 2)
+        w |= (a8[..., e] & 3) << np.uint32(sh)
+        w |= (b8[..., e] & 3) << np.uint32(sh + 8)
+    return w
+
+
+def _unword(w):
+    """Inverse of _word: uint32 [...] -> (a8, b8) uint8 [..., 8]."""
+    w = np.asarray(w, np.uint32)
+    a8 = np.zeros(w.shape + (8,), np.uint8)
+    b8 = np.zeros(w.shape + (8,), np.uint8)
+    for e in range(8):
+        sh = 16 * (e % 2) + 2 * (e // 2)
+        a8[..., e] = (w >> np.uint32(sh)) & 3
+        b8[..., e] = (w >> np.uint32(sh + 8)) & 3
+    return a8, b8
+
+
+_C = np.arange(64)
+_U = _C % 16
+_W = _C // 16
+_E = np.arange(8)
+
+
+def _kbase_index():
+    # [chunk, x, e] -> (token A, token B, channel)
+    ch = 32 * np.arange(4)[None, :, None] + 8 * _W[:, None, None] + _E[None, None, :]
+    tA = np.broadcast_to(_U[:, None, None], ch.shape)
+    return tA, tA + 16, ch
+
+
+def _vcode_index():
+    # [chunk, x, e] -> (token, channel A, channel B)
+    tok = np.broadcast_to(tau(_W[:, None, None], _E[None, None, :]), (64, 4, 8))
+    chA = np.broadcast_to(16 * (2 * np.arange(4))[None, :, None] + _U[:, None, None], (64, 4, 8))
+    return tok, chA, chA + 16
+
+
+def _boost_slots(n_hi):
+    """List of (byte offset array [nw], token A [nw,8], token B, slot [nw,8])."""
+    nf = n_hi // 32
+    offs, tA, sl = [], [], []
+    for c in range(64):
+        for b in range(nf):
+            offs.append(4 * (c * nf + b))
+            tA.append(np.full(8, c % 16))
+            sl.append(32 * b + 8 * (c // 16) + _E)
+    if n_hi % 32:
+        for c in range(32):
+            offs.append(256 * nf + 4 * c)
+            tA.append(np.full(8, c % 16))
+            sl.append(32 * nf + 8 * (c // 16) + _E)
+    if not offs:
+        return (np.zeros(0, int), np.zeros((0, 8), int), np.zeros((0, 8), int), np.zeros((0, 8), int))
+    tA = np.array(tA)
+    return np.array(offs), tA, tA + 16, np.array(sl)
+
+
+def _kappa_tokens():
+    kap = np.arange(32)
+    return tau(kap // 8, kap % 8)
+
+
+def pack_record(kf, vf):
+    """Bytes of one page record (uint8 [3072 + 9n]) from the logical fields
+    of quant_k_page / quant_v_page for a single page (no leading dims)."""
+    n_hi = kf["idx"].shape[-1]
+    out = np.zeros(record_bytes(n_hi), np.uint8)
+    base, boost, a = kf["base"], kf["boost"], vf["a"]
+    tA, tB, ch = _kbase_index()
+    words = _word(base[tA, ch], base[tB, ch])                       # [64, 4]
+    out[0:1024] = words.reshape(-1).astype("<u4").view(np.uint8)
+    o = 1024
+    offs, bA, bB, sl = _boost_slots(n_hi)
+    if len(offs):
+        bw = _word(boost[bA, sl], boost[bB, sl])
+        for off, wv in zip(offs, bw):
+            out[o + off:o + off + 4] = np.array([wv], "<u4").view(np.uint8)
+    o += 8 * n_hi
+    tok, cA, cB = _vcode_index()
+    vw = _word(a[tok, cA], a[tok, cB])
+    out[o:o + 1024] = vw.reshape(-1).astype("<u4").view(np.uint8)
+    o += 1024
+    for arr in (kf["kscale"], kf["kmin"]):
+        out[o:o + 256] = np.asarray(arr, "<f2").view(np.uint8)
+        o += 256
+    kt = _kappa_tokens()
+    for arr in (vf["vscale"], vf["vmin"]):          # [32 tokens, 4 groups]
+        out[o:o + 256] = np.ascontiguousarray(np.asarray(arr, "<f2")[kt, :].T).view(np.uint8).reshape(-1)
+        o += 256
+    out[o:o + n_hi] = kf["idx"]
+    return out
+
+
+def unpack_record(buf, n_hi):
+    """Inverse of pack_record: logical fields from one record's bytes."""
+    buf = np.asarray(buf, np.uint8)
+    if buf.shape[0] != record_bytes(n_hi):
+        raise ValueError("record size mismatch")
+    base = np.zeros((PAGE_TOKENS, HEAD_DIM), np.uint8)
+    tA, tB, ch = _kbase_index()
+    a8, b8 = _unword(buf[0:1024].view("<u4").reshape(64, 4))
+    base[tA, ch] = a8
+    base[tB, ch] = b8
+    o = 1024
+    boost = np.zeros((PAGE_TOKENS, n_hi), np.uint8)
+    offs, bA, bB, sl = _boost_slots(n_hi)
+    if len(offs):
+        ws = np.array([buf[o + off:o + off + 4].view("<u4")[0] for off in offs], np.uint32)
+        a8, b8 = _unword(ws)
+        boost[bA, sl] = a8
+        boost[bB, sl] = b8
+    o += 8 * n_hi
+    a = np.zeros((PAGE_TOKENS, HEAD_DIM), np.uint8)
+    tok, cA, cB = _vcode_index()
+    a8, b8 = _unword(buf[o:o + 1024].view("<u4").reshape(64, 4))
+    a[tok, cA] = a8
+    a[tok, cB] = b8
+    o += 1024
+    kscale = buf[o:o + 256].view("<f2").astype(_F16)
+    kmin = buf[o + 256:o + 512].view("<f2").astype(_F16)
+    o += 512
+    kt = _kappa_tokens()
+    vs = np.zeros((PAGE_TOKENS, HEAD_DIM // V_GROUP), _F16)
+    vm = np.zeros_like(vs)
+    vs[kt, :] = buf[o:o + 256].view("<f2").reshape(4, 32).T
+    vm[kt, :] = buf[o + 256:o + 512].view("<f2").reshape(4, 32).T
+    o += 512
+    idx = buf[o:o + n_hi].copy()
+    return dict(base=base, boost=boost, kscale=kscale, kmin=kmin, idx=idx), dict(a=a, vscale=vs, vmin=vm)
+
+
+# --------------------------------------------------------------------------
+# Paged cache: prefill, append/seal, dequantized view
+# --------------------------------------------------------------------------
+
+class OracleCache:
+    """Logical paged cache of a batch: per sequence b, sealed pages stored
+    as arrays with leading dims [Hkv, P_b], plus an fp16 tail of 32 slots per
+    head ([Kitty] Abstract: page-centric layout; the incomplete tail page
+    stays fp16 until it fills)."""
+
+    def __init__(self, batch, n_kv_heads, n_hi, head_dim=HEAD_DIM):
+        record_bytes(n_hi, head_dim)
+        self.batch, self.n_kv_heads, self.n_hi, self.head_dim = batch, n_kv_heads, n_hi, head_dim
+        self.k = [None] * batch      # dict of arrays [Hkv, P, ...]
+        self.v = [None] * batch
+        self.tail_k = np.zeros((batch, n_kv_heads, PAGE_TOKENS, head_dim), _F16)
+        self.tail_v = np.zeros_like(self.tail_k)
+        self.seq_len = np.zeros(batch, np.int64)
+
+    def n_pages(self, b):
+        return int(self.seq_len[b]) // PAGE_TOKENS
+
+    def _add_pages(self, b, k16, v16):
+        kf = quant_k_page(k16, self.n_hi)
+        vf = quant_v_page(v16)
+        kf = {key: kf[key] for key in ("base", "boost", "kscale", "kmin", "idx", "q", "mask")}
+        if self.k[b] is None:
+            self.k[b], self.v[b] = kf, vf
+        else:
+            self.k[b] = {key: np.concatenate([self.k[b][key], kf[key]], axis=1) for key in kf}
+            self.v[b] = {key: np.concatenate([self.v[b][key], vf[key]], axis=1) for key in vf}
+
+    def page_fields(self, b, h, p):
+        kf = {key: self.k[b][key][h, p] for key in ("base", "boost", "kscale", "kmin", "idx")}
+        vf = {key: self.v[b][key][h, p] for key in ("a", "vscale", "vmin")}
+        return kf, vf
+
+    def dequant_sequence(self, b):
+        """k^, v^ [Hkv, seq_len, D] float32: sealed pages in order, then
+        the tail tokens widened from fp16."""
+        H, D = self.n_kv_heads, self.head_dim
+        P = self.n_pages(b)
+        n_tail = int(self.seq_len[b]) - P * PAGE_TOKENS
+        ks, vs = [], []
+        if P:
+            kf, vf = self.k[b], self.v[b]
+            kh = dequant_k(kf["base"][:, :P], kf["boost"][:, :P], kf["kscale"][:, :P],
+                           kf["kmin"][:, :P], kf["idx"][:, :P])
+            vh = dequant_v(vf["a"][:, :P], vf["vscale"][:, :P], vf["vmin"][:, :P])
+            ks.append(kh.reshape(H, P * PAGE_TOKENS, D))
+            vs.append(vh.reshape(H, P * PAGE_TOKENS, D))
+        ks.append(f32(self.tail_k[b, :, :n_tail]))
+        vs.append(f32(self.tail_v[b, :, :n_tail]))
+        return np.concatenate(ks, axis=1), np.concatenate(vs, axis=1)
+
+
+def quantize_pages(k, v, n_hi, batch_lens=None):
+    """Prefill: split fp16 k, v [B, Hkv, S, D] into P = floor(S/32) sealed
+    pages and an fp16 tail of S mod 32 tokens ([Velox] Prefill steps 1-3 per
+    page of group_size tokens).  ``batch_lens`` (optional, per sequence)
+    quantizes only the first len_b tokens of sequence b."""
+    B, H, S, D = k.shape
+    cache = OracleCache(B, H, n_hi, D)
+    for b in range(B):
+        n = S if batch_lens is None else int(batch_lens[b])
+        P = n // PAGE_TOKENS
+        if P:
+            kp = k[b, :, :P * PAGE_TOKENS].reshape(H, P, PAGE_TOKENS, D)
+            vp = v[b, :, :P * PAGE_TOKENS].reshape(H, P, PAGE_TOKENS, D)
+            cache._add_pages(b, kp, vp)
+        t = n - P * PAGE_TOKENS
+        cache.tail_k[b, :, :t] = k[b, :, P * PAGE_TOKENS:n]
+        cache.tail_v[b, :, :t] = v[b, :, P * PAGE_TOKENS:n]
+        cache.seq_len[b] = n
+    return cache
+
+
+def append_token(cache, k_new, v_new):
+    """Decode-time append of one token per sequence (k_new, v_new fp16
+    [B, Hkv, D]): store into tail slot n mod 32; when that slot is the 32nd,
+    the tail is quantized as page n div 32 exactly like a prefill page and
+    the tail becomes empty."""
+    for b in range(cache.batch):
+        n = int(cache.seq_len[b])
+        slot = n % PAGE_TOKENS
+        cache.tail_k[b, :, slot] = k_new[b]
+        cache.tail_v[b, :, slot] = v_new[b]
+        if slot == PAGE_TOKENS - 1:
+            cache._add_pages(b, cache.tail_k[b][:, None], cache.tail_v[b][:, None])
+        cache.seq_len[b] = n + 1
+    return cache
+
+
+# --------------------------------------------------------------------------
+# Decode attention over the dequantized cache
+# --------------------------------------------------------------------------
+
+def softmax_scale(head_dim=HEAD_DIM):
+    """float32(1/sqrt(D)): 0.088388346 for D = 128."""
+    return _F32(1.0 / math.sqrt(head_dim))
+
+
+def attention_f32(q, khat, vhat):
+    """One decode query per head over all stored tokens, float32.
+
+    q: fp16 [Hq, D]; khat, vhat: float32 [Hkv, S, D].  Query head hq reads
+    KV head hq // (Hq / Hkv).  s_t = f32(1/sqrt(D)) * (q . k^_t); p =
+    softmax(s) with max subtraction; o = sum_t p_t v^_t.  Returns float32
+    [Hq, D]; zeros when S == 0."""
+    Hq, D = q.shape
+    Hkv, S, _ = khat.shape
+    G = Hq // Hkv
+    out = np.zeros((Hq, D), _F32)
+    if S == 0:
+        return out
+    sc = softmax_scale(D)
+    for hq in range(Hq):
+        h = hq // G
+        s = ((khat[h] @ f32(q[hq])).astype(_F32) * sc).astype(_F32)
+        p = np.exp((s - s.max()).astype(_F32)).astype(_F32)
+        out[hq] = ((p @ vhat[h]).astype(_F32) / p.sum(dtype=_F32)).astype(_F32)
+    return out
+
+
+def attention_f64(q, khat, vhat):
+    """Same as attention_f32 in float64 (self-check of the float32 one)."""
+    Hq, D = q.shape
+    Hkv, S, _ = khat.shape
+    G = Hq // Hkv
+    out = np.zeros((Hq, D), np.float64)
+    if S == 0:
+        return out
+    sc = 1.0 / math.sqrt(D)
+    kd = khat.astype(np.float64)
+    vd = vhat.astype(np.float64)
+    for hq in range(Hq):
+        h = hq // G
+        s = (kd[h] @ q[hq].astype(np.float64)) * sc
+        p = np.exp(s - s.max())
+        out[hq] = (p @ vd[h]) / p.sum()
+    return out
+
+
+def decode_attention(cache, q, precision="f32", heads=None):
+    """Decode attention for every sequence of the cache: q fp16 [B, Hq, D]
+    -> float32 [B, Hq, D].  ``heads`` (optional) restricts to a list of
+    KV heads; the other outputs stay zero."""
+    B, Hq, D = q.shape
+    out = np.zeros((B, Hq, D), _F32 if precision == "f32" else np.float64)
+    G = Hq // cache.n_kv_heads
+    fn = attention_f32 if precision == "f32" else attention_f64
+    for b in range(B):
+        kh, vh = cache.dequant_sequence(b)
+        hs = range(cache.n_kv_heads) if heads is None else heads
+        for h in hs:
+            out[b, h * G:(h + 1) * G] = fn(q[b, h * G:(h + 1) * G], kh[h:h + 1], vh[h:h + 1])
+    return out
+
+
+def avg_code_bits(n_hi, head_dim=HEAD_DIM):
+    """Code bits per Key element of a page record: the base plane's 2 bits on
+    every channel plus the boost plane's 2 bits on n_hi channels, counted
+    from the record layout's plane sizes (metadata excluded)."""
+    base_bits = 1024 * 8
+    boost_bits = 8 * n_hi * 8
+    return (base_bits + boost_bits) / (PAGE_TOKENS * head_dim)
