@@ -1,0 +1,137 @@
+/*
+ * kitty.h -- C ABI of the Kitty mixed-precision 2-bit KV cache library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method: "Kitty: Accurate and Efficient 2-bit KV Cache Quantization with
+ * Dynamic Channel-wise Precision Boost" (arXiv 2511.18643), Abstract -- Key
+ * channels are ranked by sensitivity and a small fraction is kept at higher
+ * precision; each mixed-precision Key page is stored as two tensors of uniform
+ * 2-bit codes inside a page-centric KV layout, so that dequantization is the
+ * same for every lane.  The per-page arithmetic follows the VeloxQuant-MLX
+ * documentation page "Kitty -- Dynamic Channel-wise Mixed-Precision Keys",
+ * section "How it works / Prefill phase", steps 1-3 (channel variance over the
+ * token axis, top hi_fraction x D channels at 4 bits, the rest at 2 bits,
+ * asymmetric min/max over groups of 32 tokens), and its "Configuration
+ * reference" (head_dim, hi_fraction, hi_bit = 4, lo_bit = 2, group_size = 32).
+ *
+ * Conventions for every entry point:
+ *  - Return 0 (KITTY_OK) or a negative KITTY_ERR_* code.  On error,
+ *    kitty_last_error() returns a message for the calling thread.  Argument
+ *    validation happens before any HIP call, so an invalid argument never
+ *    touches the device.
+ *  - Every pointer named "device" is HIP device memory owned by the caller.
+ *    The library allocates nothing, keeps no global mutable state besides the
+ *    thread-local error text, and never synchronizes: all work is enqueued
+ *    on `stream` (a hipStream_t; NULL = the default stream) and is
+ *    asynchronous to the host.
+ *  - fp16 arrays are IEEE binary16 passed as uint16_t.
+ *  - Device-side contents (block-table entries, sequence lengths) are read by
+ *    the kernels; a block-table entry outside [0, n_pages) makes the kernels
+ *    skip that page (no access outside the pool), which leaves the result
+ *    undefined but never faults.
+ */
+#ifndef KITTY_H
+#define KITTY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KITTY_ABI_VERSION 1
+
+enum {
+  KITTY_OK = 0,
+  KITTY_ERR_INVALID_ARG = -1, /* null pointer, negative/inconsistent size, misalignment */
+  KITTY_ERR_UNSUPPORTED = -2, /* head_dim != 128, page_tokens != 32, bad n_hi, ... */
+  KITTY_ERR_WORKSPACE = -3,   /* workspace smaller than kitty_decode_workspace_bytes */
+  KITTY_ERR_HIP = -4          /* a kernel launch failed (hipGetLastError) */
+};
+
+/* Cache geometry ("Configuration reference": head_dim, group_size,
+ * hi_fraction; n_hi = hi_fraction * head_dim rounded half to even). */
+typedef struct {
+  int32_t head_dim;    /* D; must be 128 */
+  int32_t page_tokens; /* tokens per page = Key group size; must be 32 */
+  int32_t n_kv_heads;  /* Hkv, 1..1024 */
+  int32_t n_hi;        /* boosted (4-bit) channels per page: 0 or a multiple of 16, <= D */
+} kitty_config_t;
+
+/* A paged cache (Abstract: page-centric KV layout).  One physical page holds
+ * the records of all Hkv heads for 32 consecutive tokens of one sequence; the
+ * block table maps (sequence b, logical page j) to a physical page id.
+ * Record layout of one (page, head): K base plane 1024 B, K boost plane 8*n_hi
+ * B, V codes 1024 B, kscale fp16[128], kmin fp16[128], vscale fp16[4][32],
+ * vmin fp16[4][32], idx uint8[n_hi] -- 3072 + 9*n_hi bytes in total; the bit
+ * placement inside the code planes is specified with the CPU reference
+ * (page record layout) and in the design notes.  Head h's record starts at
+ * byte h * kitty_record_bytes; a physical page is kitty_page_bytes long. */
+typedef struct {
+  void* pages;                /* device; n_pages * page_bytes bytes, 256-byte aligned */
+  int64_t n_pages;            /* physical pages in the pool, >= 1 */
+  const int32_t* block_table; /* device int32 [batch][max_pages] physical page ids */
+  int32_t batch;              /* B >= 1 */
+  int32_t max_pages;          /* block-table row length (logical pages per sequence), >= 1 */
+  uint16_t* tail_k;           /* device fp16 [batch][Hkv][32][D]: the unsealed tail page */
+  uint16_t* tail_v;           /* device fp16 [batch][Hkv][32][D] */
+  int32_t* seq_lens;          /* device int32 [batch]: tokens stored (sealed pages + tail) */
+} kitty_kv_view_t;
+
+/* Version of this ABI (KITTY_ABI_VERSION). */
+int kitty_abi_version(void);
+
+/* Message for the last non-zero return on this thread ("" if none). */
+const char* kitty_last_error(void);
+
+/* Bytes of one (page, head) record: 3072 + 9 * n_hi. */
+int kitty_record_bytes(const kitty_config_t* cfg, size_t* out);
+
+/* Bytes of one physical page: n_kv_heads records, rounded up to 256. */
+int kitty_page_bytes(const kitty_config_t* cfg, size_t* out);
+
+/* Prefill ("How it works / Prefill phase", steps 1-3, per page of 32 tokens).
+ * k, v: device fp16 [batch][Hkv][S][D], contiguous.  For each sequence b with
+ * length n_b = (lens ? lens[b] : S), n_b <= S: the first floor(n_b / 32)
+ * pages are ranked, quantized and packed into the physical pages
+ * block_table[b][0..], the remaining n_b mod 32 tokens are copied verbatim
+ * into tail_k / tail_v slots 0.., and seq_lens[b] = n_b.  lens: optional
+ * device int32 [batch].  Requires floor(S / 32) <= max_pages. */
+int kitty_quantize_pages(const kitty_config_t* cfg, const kitty_kv_view_t* kv,
+                         const uint16_t* k, const uint16_t* v, int32_t S,
+                         const int32_t* lens, void* stream);
+
+/* Decode-time append of one token per sequence.  k_new, v_new: device fp16
+ * [batch][Hkv][D].  With n = seq_lens[b]: the token is stored in tail slot
+ * n mod 32 and seq_lens[b] becomes n + 1; when that slot is the 32nd, the
+ * full tail is quantized exactly like a prefill page and written to physical
+ * page block_table[b][n / 32] (the tail page stays fp16 until it fills).  The
+ * caller maps block_table[b][n / 32] to a free page before that append; a
+ * seal with n / 32 >= max_pages is skipped. */
+int kitty_append_token(const kitty_config_t* cfg, const kitty_kv_view_t* kv,
+                       const uint16_t* k_new, const uint16_t* v_new, void* stream);
+
+/* Workspace bytes kitty_decode_attention needs for this shape (split-KV
+ * partial results).  max_seq_len: an upper bound on every seq_lens[b]. */
+int kitty_decode_workspace_bytes(const kitty_config_t* cfg, int32_t batch, int32_t n_q_heads,
+                                 int32_t max_seq_len, size_t* out);
+
+/* Fused decode attention over the quantized cache (Abstract: page
+ * dequantization fused into the decode kernels).  q: device fp16
+ * [batch][Hq][D], Hq a multiple of Hkv; query head hq reads KV head
+ * hq / (Hq / Hkv).  For each sequence, attends over all seq_lens[b] tokens --
+ * sealed pages in order, then the fp16 tail: out[b][hq] = softmax(q . k^ /
+ * sqrt(D)) . v^ with k^, v^ the dequantized keys and values.  out: device
+ * fp32 [batch][Hq][D] (zeros for an empty sequence).  max_seq_len bounds
+ * seq_lens (tokens beyond it are ignored).  workspace: device, 256-byte
+ * aligned, at least kitty_decode_workspace_bytes(...) bytes. */
+int kitty_decode_attention(const kitty_config_t* cfg, const kitty_kv_view_t* kv,
+                           const uint16_t* q, int32_t n_q_heads, int32_t max_seq_len,
+                           float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KITTY_H */

@@ -1,0 +1,236 @@
+"""ctypes binding of libkitty.so (the C ABI in include/kitty.h).
+
+Argument marshalling only: every step of the hot path runs in the HIP
+kernels behind the C ABI.  PyTorch provides device memory and the stream.
+The functions keep the C names (``kitty_quantize_pages`` ...) and accept
+torch CUDA tensors; ``KittyCache`` owns the caller-side buffers of one paged
+cache (page pool, block table, fp16 tail, sequence lengths).
+
+There is no fallback: if the library is missing or no GPU is present the
+calls fail loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libkitty.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "kitty.h")
+
+KITTY_OK = 0
+KITTY_ERR_INVALID_ARG = -1
+KITTY_ERR_UNSUPPORTED = -2
+KITTY_ERR_WORKSPACE = -3
+KITTY_ERR_HIP = -4
+
+HEAD_DIM = 128
+PAGE_TOKENS = 32
+
+
+class KittyError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"kitty error {code}: {msg}")
+        self.code = code
+
+
+class kitty_config_t(ctypes.Structure):
+    _fields_ = [("head_dim", ctypes.c_int32), ("page_tokens", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("n_hi", ctypes.c_int32)]
+
+
+class kitty_kv_view_t(ctypes.Structure):
+    _fields_ = [("pages", ctypes.c_void_p), ("n_pages", ctypes.c_int64),
+                ("block_table", ctypes.c_void_p), ("batch", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32), ("tail_k", ctypes.c_void_p),
+                ("tail_v", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def declared_symbols(header=HEADER):
+    """Names of the functions include/kitty.h declares."""
+    with open(header) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(kitty_\w+)\s*\(", text, re.M)))
+
+
+def load(path=LIB_PATH):
+    """Load libkitty.so once and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise KittyError(KITTY_ERR_HIP, f"{path} is missing; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    cfgp, viewp = P(kitty_config_t), P(kitty_kv_view_t)
+    sig = {
+        "kitty_abi_version": ([], ctypes.c_int),
+        "kitty_last_error": ([], ctypes.c_char_p),
+        "kitty_record_bytes": ([cfgp, P(sz)], ctypes.c_int),
+        "kitty_page_bytes": ([cfgp, P(sz)], ctypes.c_int),
+        "kitty_quantize_pages": ([cfgp, viewp, vp, vp, i32, vp, vp], ctypes.c_int),
+        "kitty_append_token": ([cfgp, viewp, vp, vp, vp], ctypes.c_int),
+        "kitty_decode_workspace_bytes": ([cfgp, i32, i32, i32, P(sz)], ctypes.c_int),
+        "kitty_decode_attention": ([cfgp, viewp, vp, i32, i32, vp, vp, sz, vp], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(rc):
+    if rc != KITTY_OK:
+        raise KittyError(rc, load().kitty_last_error().decode())
+
+
+def config(n_kv_heads, n_hi, head_dim=HEAD_DIM, page_tokens=PAGE_TOKENS):
+    return kitty_config_t(head_dim, page_tokens, n_kv_heads, n_hi)
+
+
+def kitty_abi_version():
+    return load().kitty_abi_version()
+
+
+def kitty_record_bytes(cfg):
+    out = ctypes.c_size_t()
+    _check(load().kitty_record_bytes(ctypes.byref(cfg), ctypes.byref(out)))
+    return out.value
+
+
+def kitty_page_bytes(cfg):
+    out = ctypes.c_size_t()
+    _check(load().kitty_page_bytes(ctypes.byref(cfg), ctypes.byref(out)))
+    return out.value
+
+
+def kitty_decode_workspace_bytes(cfg, batch, n_q_heads, max_seq_len):
+    out = ctypes.c_size_t()
+    _check(load().kitty_decode_workspace_bytes(ctypes.byref(cfg), batch, n_q_heads, max_seq_len,
+                                               ctypes.byref(out)))
+    return out.value
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, dtype, shape=None, name="tensor"):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise KittyError(KITTY_ERR_INVALID_ARG, f"{name} must be a CUDA tensor")
+    if t.dtype != dtype:
+        raise KittyError(KITTY_ERR_INVALID_ARG, f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise KittyError(KITTY_ERR_INVALID_ARG, f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise KittyError(KITTY_ERR_INVALID_ARG, f"{name} shape {tuple(t.shape)} != {tuple(shape)}")
+
+
+def kitty_quantize_pages(cfg, view, k, v, S, lens=None, stream=None):
+    _check(load().kitty_quantize_pages(ctypes.byref(cfg), ctypes.byref(view), _ptr(k), _ptr(v), S,
+                                       _ptr(lens), _stream(stream)))
+
+
+def kitty_append_token(cfg, view, k_new, v_new, stream=None):
+    _check(load().kitty_append_token(ctypes.byref(cfg), ctypes.byref(view), _ptr(k_new), _ptr(v_new),
+                                     _stream(stream)))
+
+
+def kitty_decode_attention(cfg, view, q, n_q_heads, max_seq_len, out, workspace, stream=None):
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().kitty_decode_attention(ctypes.byref(cfg), ctypes.byref(view), _ptr(q), n_q_heads,
+                                         max_seq_len, _ptr(out), _ptr(workspace), nbytes, _stream(stream)))
+
+
+class KittyCache:
+    """Caller-side buffers of one paged cache on a CUDA device.
+
+    pool        uint8 [n_pages, page_bytes]
+    block_table int32 [batch, max_pages] (identity-like mapping by default:
+                sequence b's page j -> physical page b * max_pages + j)
+    tail_k/v    fp16  [batch, Hkv, 32, 128]
+    seq_lens    int32 [batch]
+    """
+
+    def __init__(self, batch, n_kv_heads, n_hi, max_tokens, device="cuda", block_table=None, n_pages=None):
+        import torch
+        self.cfg = config(n_kv_heads, n_hi)
+        self.batch, self.n_kv_heads, self.n_hi = batch, n_kv_heads, n_hi
+        self.max_pages = max(1, -(-max_tokens // PAGE_TOKENS))
+        self.page_bytes = kitty_page_bytes(self.cfg)
+        self.record_bytes = kitty_record_bytes(self.cfg)
+        if block_table is None:
+            bt = torch.arange(batch * self.max_pages, dtype=torch.int32).reshape(batch, self.max_pages)
+            n_pages = batch * self.max_pages if n_pages is None else n_pages
+        else:
+            bt = torch.as_tensor(block_table, dtype=torch.int32)
+            if bt.dim() != 2 or bt.shape[0] != batch:
+                raise KittyError(KITTY_ERR_INVALID_ARG, "block_table must be [batch, max_pages]")
+            self.max_pages = int(bt.shape[1])
+            if n_pages is None:
+                raise KittyError(KITTY_ERR_INVALID_ARG, "n_pages is required with a block table")
+        self.n_pages = int(n_pages)
+        self.block_table = bt.to(device).contiguous()
+        self.pool = torch.zeros((self.n_pages, self.page_bytes), dtype=torch.uint8, device=device)
+        self.tail_k = torch.zeros((batch, n_kv_heads, PAGE_TOKENS, HEAD_DIM), dtype=torch.float16, device=device)
+        self.tail_v = torch.zeros_like(self.tail_k)
+        self.seq_lens = torch.zeros(batch, dtype=torch.int32, device=device)
+        self.view = kitty_kv_view_t(self.pool.data_ptr(), self.n_pages, self.block_table.data_ptr(), batch,
+                                    self.max_pages, self.tail_k.data_ptr(), self.tail_v.data_ptr(),
+                                    self.seq_lens.data_ptr())
+        self._ws = None
+
+    # -- hot path ---------------------------------------------------------
+    def quantize_pages(self, k, v, lens=None, stream=None):
+        import torch
+        B, H, S, D = k.shape
+        _need(k, torch.float16, (self.batch, self.n_kv_heads, S, HEAD_DIM), "k")
+        _need(v, torch.float16, (self.batch, self.n_kv_heads, S, HEAD_DIM), "v")
+        if lens is not None:
+            _need(lens, torch.int32, (self.batch,), "lens")
+        kitty_quantize_pages(self.cfg, self.view, k, v, S, lens, stream)
+
+    def append_token(self, k_new, v_new, stream=None):
+        import torch
+        _need(k_new, torch.float16, (self.batch, self.n_kv_heads, HEAD_DIM), "k_new")
+        _need(v_new, torch.float16, (self.batch, self.n_kv_heads, HEAD_DIM), "v_new")
+        kitty_append_token(self.cfg, self.view, k_new, v_new, stream)
+
+    def workspace(self, n_q_heads, max_seq_len):
+        import torch
+        nb = kitty_decode_workspace_bytes(self.cfg, self.batch, n_q_heads, max_seq_len)
+        if self._ws is None or self._ws.numel() < max(nb, 256):
+            self._ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=self.pool.device)
+        return self._ws
+
+    def decode_attention(self, q, max_seq_len=None, out=None, workspace=None, stream=None):
+        import torch
+        B, Hq, D = q.shape
+        _need(q, torch.float16, (self.batch, Hq, HEAD_DIM), "q")
+        msl = self.max_pages * PAGE_TOKENS + PAGE_TOKENS - 1 if max_seq_len is None else max_seq_len
+        if out is None:
+            out = torch.empty((self.batch, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+        _need(out, torch.float32, (self.batch, Hq, HEAD_DIM), "out")
+        ws = self.workspace(Hq, msl) if workspace is None else workspace
+        kitty_decode_attention(self.cfg, self.view, q, Hq, msl, out, ws, stream)
+        return out
+
+    # -- inspection -------------------------------------------------------
+    def record(self, b, j, h):
+        """Bytes (torch uint8, on device) of sequence b's page j, head h."""
+        phys = int(self.block_table[b, j])
+        return self.pool[phys, h * self.record_bytes:(h + 1) * self.record_bytes]

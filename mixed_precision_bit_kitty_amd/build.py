@@ -1,0 +1,66 @@
+"""Build libkitty.so (HIP, gfx950) in-tree with hipcc.
+
+Usage: python -m mixed_precision_bit_kitty_amd.build [-v]
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+OBJ = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libkitty.so")
+
+ARCH = "gfx950"
+COMMON = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+    # no packed fp32 instructions anywhere in device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+]
+SOURCES = {
+    # bit-exact quantizer: every float32 op rounded separately
+    "quantize.hip": ["-ffp-contract=off"],
+    "decode.hip": [],
+    "kitty_abi.cpp": ["-x", "hip"],
+}
+
+
+def hipcc():
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"build step failed ({r.returncode}):\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose and r.stderr.strip():
+        print("\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l), flush=True)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source and link libkitty.so; returns its path."""
+    os.makedirs(OBJ, exist_ok=True)
+    cc = hipcc()
+    objs = []
+    for src, extra in SOURCES.items():
+        obj = os.path.join(OBJ, src + ".o")
+        _run([cc, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

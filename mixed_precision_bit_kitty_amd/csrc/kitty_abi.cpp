@@ -1,0 +1,208 @@
+// C ABI of the Kitty library: argument validation (before any HIP call),
+// layout sizes and kernel launches.  See include/kitty.h for the contract.
+#include "../../include/kitty.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "kitty_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return KITTY_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_config(const kitty_config_t* cfg) {
+  if (!cfg) return fail(KITTY_ERR_INVALID_ARG, "cfg is null");
+  if (cfg->head_dim != kitty::kHeadDim)
+    return fail(KITTY_ERR_UNSUPPORTED, "head_dim %d unsupported (only 128)", cfg->head_dim);
+  if (cfg->page_tokens != kitty::kPageTokens)
+    return fail(KITTY_ERR_UNSUPPORTED, "page_tokens %d unsupported (only 32)", cfg->page_tokens);
+  if (cfg->n_kv_heads < 1 || cfg->n_kv_heads > 1024)
+    return fail(KITTY_ERR_INVALID_ARG, "n_kv_heads %d out of range [1, 1024]", cfg->n_kv_heads);
+  if (cfg->n_hi < 0 || cfg->n_hi > cfg->head_dim || cfg->n_hi % 16 != 0)
+    return fail(KITTY_ERR_UNSUPPORTED, "n_hi %d unsupported (0 or a multiple of 16 up to 128)", cfg->n_hi);
+  return KITTY_OK;
+}
+
+int check_view(const kitty_config_t* cfg, const kitty_kv_view_t* kv) {
+  if (!kv) return fail(KITTY_ERR_INVALID_ARG, "kv view is null");
+  if (!kv->pages || !aligned(kv->pages, 256)) return fail(KITTY_ERR_INVALID_ARG, "pages null or not 256-byte aligned");
+  if (kv->n_pages < 1) return fail(KITTY_ERR_INVALID_ARG, "n_pages must be >= 1");
+  if (!kv->block_table || !aligned(kv->block_table, 4)) return fail(KITTY_ERR_INVALID_ARG, "block_table null or misaligned");
+  if (kv->batch < 1 || kv->batch > 65535) return fail(KITTY_ERR_INVALID_ARG, "batch %d out of range [1, 65535]", kv->batch);
+  if (kv->max_pages < 1) return fail(KITTY_ERR_INVALID_ARG, "max_pages must be >= 1");
+  if (!kv->tail_k || !kv->tail_v || !aligned(kv->tail_k, 16) || !aligned(kv->tail_v, 16))
+    return fail(KITTY_ERR_INVALID_ARG, "tail_k / tail_v null or not 16-byte aligned");
+  if (!kv->seq_lens || !aligned(kv->seq_lens, 4)) return fail(KITTY_ERR_INVALID_ARG, "seq_lens null or misaligned");
+  (void)cfg;
+  return KITTY_OK;
+}
+
+int check_launch(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(KITTY_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int kitty_abi_version(void) { return KITTY_ABI_VERSION; }
+
+const char* kitty_last_error(void) { return g_last_error.c_str(); }
+
+int kitty_record_bytes(const kitty_config_t* cfg, size_t* out) {
+  if (int r = check_config(cfg)) return r;
+  if (!out) return fail(KITTY_ERR_INVALID_ARG, "out is null");
+  *out = (size_t)kitty::rec_bytes(cfg->n_hi);
+  return ok();
+}
+
+int kitty_page_bytes(const kitty_config_t* cfg, size_t* out) {
+  if (int r = check_config(cfg)) return r;
+  if (!out) return fail(KITTY_ERR_INVALID_ARG, "out is null");
+  *out = (size_t)kitty::page_stride_bytes(cfg->n_kv_heads, cfg->n_hi);
+  return ok();
+}
+
+int kitty_quantize_pages(const kitty_config_t* cfg, const kitty_kv_view_t* kv, const uint16_t* k,
+                         const uint16_t* v, int32_t S, const int32_t* lens, void* stream) {
+  if (int r = check_config(cfg)) return r;
+  if (int r = check_view(cfg, kv)) return r;
+  if (!k || !v || !aligned(k, 4) || !aligned(v, 4)) return fail(KITTY_ERR_INVALID_ARG, "k / v null or misaligned");
+  if (S < 0) return fail(KITTY_ERR_INVALID_ARG, "S must be >= 0");
+  if (S / kitty::kPageTokens > kv->max_pages)
+    return fail(KITTY_ERR_INVALID_ARG, "S / 32 = %d exceeds max_pages %d", S / kitty::kPageTokens, kv->max_pages);
+  if (S / kitty::kPageTokens + 1 > 2147483647 / 1) return fail(KITTY_ERR_INVALID_ARG, "S too large");
+  if (lens && !aligned(lens, 4)) return fail(KITTY_ERR_INVALID_ARG, "lens misaligned");
+  kitty::QuantizeParams p{};
+  p.pages = static_cast<uint8_t*>(kv->pages);
+  p.n_pages = kv->n_pages;
+  p.page_bytes = kitty::page_stride_bytes(cfg->n_kv_heads, cfg->n_hi);
+  p.block_table = kv->block_table;
+  p.max_pages = kv->max_pages;
+  p.batch = kv->batch;
+  p.n_kv_heads = cfg->n_kv_heads;
+  p.n_hi = cfg->n_hi;
+  p.tail_k = reinterpret_cast<_Float16*>(kv->tail_k);
+  p.tail_v = reinterpret_cast<_Float16*>(kv->tail_v);
+  p.seq_lens = kv->seq_lens;
+  p.k = reinterpret_cast<const _Float16*>(k);
+  p.v = reinterpret_cast<const _Float16*>(v);
+  p.S = S;
+  p.lens = lens;
+  (void)hipGetLastError();
+  return check_launch(kitty::launch_quantize(p, static_cast<hipStream_t>(stream)), "quantize_pages");
+}
+
+int kitty_append_token(const kitty_config_t* cfg, const kitty_kv_view_t* kv, const uint16_t* k_new,
+                       const uint16_t* v_new, void* stream) {
+  if (int r = check_config(cfg)) return r;
+  if (int r = check_view(cfg, kv)) return r;
+  if (!k_new || !v_new || !aligned(k_new, 4) || !aligned(v_new, 4))
+    return fail(KITTY_ERR_INVALID_ARG, "k_new / v_new null or misaligned");
+  kitty::AppendParams p{};
+  p.pages = static_cast<uint8_t*>(kv->pages);
+  p.n_pages = kv->n_pages;
+  p.page_bytes = kitty::page_stride_bytes(cfg->n_kv_heads, cfg->n_hi);
+  p.block_table = kv->block_table;
+  p.max_pages = kv->max_pages;
+  p.batch = kv->batch;
+  p.n_kv_heads = cfg->n_kv_heads;
+  p.n_hi = cfg->n_hi;
+  p.tail_k = reinterpret_cast<_Float16*>(kv->tail_k);
+  p.tail_v = reinterpret_cast<_Float16*>(kv->tail_v);
+  p.seq_lens = kv->seq_lens;
+  p.k_new = reinterpret_cast<const _Float16*>(k_new);
+  p.v_new = reinterpret_cast<const _Float16*>(v_new);
+  (void)hipGetLastError();
+  return check_launch(kitty::launch_append(p, static_cast<hipStream_t>(stream)), "append_token");
+}
+
+static int decode_shape(const kitty_config_t* cfg, int32_t batch, int32_t n_q_heads, int32_t max_seq_len,
+                        kitty::SplitPlan* plan, int* n_head_groups, size_t* ws) {
+  if (batch < 1 || batch > 65535) return fail(KITTY_ERR_INVALID_ARG, "batch %d out of range [1, 65535]", batch);
+  if (n_q_heads < 1 || n_q_heads % cfg->n_kv_heads != 0)
+    return fail(KITTY_ERR_INVALID_ARG, "n_q_heads %d must be a positive multiple of n_kv_heads %d", n_q_heads,
+                cfg->n_kv_heads);
+  if (max_seq_len < 0) return fail(KITTY_ERR_INVALID_ARG, "max_seq_len must be >= 0");
+  const int G = n_q_heads / cfg->n_kv_heads;
+  *n_head_groups = (G + 3) / 4;
+  if ((long)cfg->n_kv_heads * *n_head_groups > 65535) return fail(KITTY_ERR_INVALID_ARG, "too many heads");
+  *plan = kitty::plan_splits(batch, cfg->n_kv_heads, *n_head_groups, max_seq_len);
+  *ws = (size_t)batch * n_q_heads * plan->n_split * kitty::kPartialStride * sizeof(float);
+  return KITTY_OK;
+}
+
+int kitty_decode_workspace_bytes(const kitty_config_t* cfg, int32_t batch, int32_t n_q_heads, int32_t max_seq_len,
+                                 size_t* out) {
+  if (int r = check_config(cfg)) return r;
+  if (!out) return fail(KITTY_ERR_INVALID_ARG, "out is null");
+  kitty::SplitPlan plan;
+  int nhg;
+  size_t ws;
+  if (int r = decode_shape(cfg, batch, n_q_heads, max_seq_len, &plan, &nhg, &ws)) return r;
+  *out = ws;
+  return ok();
+}
+
+int kitty_decode_attention(const kitty_config_t* cfg, const kitty_kv_view_t* kv, const uint16_t* q,
+                           int32_t n_q_heads, int32_t max_seq_len, float* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (int r = check_config(cfg)) return r;
+  if (int r = check_view(cfg, kv)) return r;
+  if (!q || !aligned(q, 4)) return fail(KITTY_ERR_INVALID_ARG, "q null or misaligned");
+  if (!out || !aligned(out, 4)) return fail(KITTY_ERR_INVALID_ARG, "out null or misaligned");
+  kitty::SplitPlan plan;
+  int nhg;
+  size_t need;
+  if (int r = decode_shape(cfg, kv->batch, n_q_heads, max_seq_len, &plan, &nhg, &need)) return r;
+  if (!workspace || !aligned(workspace, 256)) return fail(KITTY_ERR_INVALID_ARG, "workspace null or not 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(KITTY_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+  kitty::DecodeParams p{};
+  p.pages = static_cast<const uint8_t*>(kv->pages);
+  p.n_pages = kv->n_pages;
+  p.page_bytes = kitty::page_stride_bytes(cfg->n_kv_heads, cfg->n_hi);
+  p.block_table = kv->block_table;
+  p.max_pages = kv->max_pages;
+  p.batch = kv->batch;
+  p.n_kv_heads = cfg->n_kv_heads;
+  p.n_hi = cfg->n_hi;
+  p.tail_k = reinterpret_cast<const _Float16*>(kv->tail_k);
+  p.tail_v = reinterpret_cast<const _Float16*>(kv->tail_v);
+  p.seq_lens = kv->seq_lens;
+  p.q = reinterpret_cast<const _Float16*>(q);
+  p.n_q_heads = n_q_heads;
+  p.group = n_q_heads / cfg->n_kv_heads;
+  p.n_head_groups = nhg;
+  p.max_seq_len = max_seq_len;
+  p.n_split = plan.n_split;
+  p.pages_per_split = plan.pages_per_split;
+  p.partial = static_cast<float*>(workspace);
+  p.out = out;
+  (void)hipGetLastError();
+  return check_launch(kitty::launch_decode(p, static_cast<hipStream_t>(stream)), "decode_attention");
+}
+
+}  // extern "C"

@@ -1,0 +1,127 @@
+// Internal declarations of the Kitty HIP library (gfx950 only).
+//
+// Page record of one (page of 32 tokens, KV head), n = n_hi boosted channels
+// (the two uniform 2-bit Key tensors of "Kitty: Accurate and Efficient 2-bit
+// KV Cache Quantization with Dynamic Channel-wise Precision Boost", Abstract,
+// plus 2-bit Values and fp16 metadata):
+//
+//   0          K base plane    1024 B  64 chunks x 16 B, chunk = one lane's MFMA A operand
+//   1024       K boost plane   8n B    one 32-bit word per (lane, 32-slot block)
+//   1024+8n    V code plane    1024 B  64 chunks x 16 B
+//   2048+8n    kscale          fp16[128]  (4 x step on boosted channels, step elsewhere)
+//   2304+8n    kmin            fp16[128]
+//   2560+8n    vscale          fp16[4 groups][32], token order kappa
+//   2816+8n    vmin            fp16[4][32]
+//   3072+8n    idx             uint8[n], ascending boosted channel list
+//
+// Code word: 16 two-bit codes for two combos A, B of 8 elements e; element e
+// of A at bit 16*(e&1) + 2*(e>>1), of B at bit 16*(e&1) + 8 + 2*(e>>1).  With
+// this placement one shift plus one AND-OR turns a word into two fp16 values
+// 4 + code (exponent 17, code in mantissa bits 8..9) for an MFMA operand.
+//
+// Chunk c of a 16-byte plane, u = c & 15, w = c >> 4, word x = 0..3:
+//   K base : A = (token u,      channel 32x + 8w + e), B = (token 16 + u, same channel)
+//   V codes: A = (token tau(w,e), channel 32x + u),    B = (token tau(w,e), channel 32x + 16 + u)
+// tau(w, e) = 4w + e for e < 4, 16 + 4w + e - 4 otherwise: the token order in
+// which a 16x16 MFMA result of QK^T (rows = tokens) lands in the lanes that
+// feed the P operand of the PV MFMA.  Value metadata index kappa = 8w + e.
+// K boost: nf = n / 32 full slot blocks, word of (chunk c, block b) at byte
+// 4*(c*nf + b), slots 32b + 8w + e; if n % 32 == 16 a half block follows at
+// byte 256*nf + 4c for chunks c < 32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kitty {
+
+constexpr int kHeadDim = 128;
+constexpr int kPageTokens = 32;
+constexpr int kVGroup = 32;
+
+__host__ __device__ constexpr int rec_bytes(int n_hi) { return 3072 + 9 * n_hi; }
+__host__ __device__ constexpr int off_kboost() { return 1024; }
+__host__ __device__ constexpr int off_v(int n_hi) { return 1024 + 8 * n_hi; }
+__host__ __device__ constexpr int off_kscale(int n_hi) { return 2048 + 8 * n_hi; }
+__host__ __device__ constexpr int off_kmin(int n_hi) { return 2304 + 8 * n_hi; }
+__host__ __device__ constexpr int off_vscale(int n_hi) { return 2560 + 8 * n_hi; }
+__host__ __device__ constexpr int off_vmin(int n_hi) { return 2816 + 8 * n_hi; }
+__host__ __device__ constexpr int off_idx(int n_hi) { return 3072 + 8 * n_hi; }
+
+__host__ __device__ inline int64_t page_stride_bytes(int n_kv_heads, int n_hi) {
+  int64_t raw = (int64_t)n_kv_heads * rec_bytes(n_hi);
+  return (raw + 255) / 256 * 256;
+}
+
+// Launch-side parameters shared by the ABI layer and the kernels.
+struct QuantizeParams {
+  uint8_t* pages;
+  int64_t n_pages;
+  int64_t page_bytes;
+  const int32_t* block_table;
+  int32_t max_pages;
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t n_hi;
+  _Float16* tail_k;
+  _Float16* tail_v;
+  int32_t* seq_lens;
+  const _Float16* k;
+  const _Float16* v;
+  int32_t S;
+  const int32_t* lens;
+};
+
+struct AppendParams {
+  uint8_t* pages;
+  int64_t n_pages;
+  int64_t page_bytes;
+  const int32_t* block_table;
+  int32_t max_pages;
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t n_hi;
+  _Float16* tail_k;
+  _Float16* tail_v;
+  int32_t* seq_lens;
+  const _Float16* k_new;
+  const _Float16* v_new;
+};
+
+struct DecodeParams {
+  const uint8_t* pages;
+  int64_t n_pages;
+  int64_t page_bytes;
+  const int32_t* block_table;
+  int32_t max_pages;
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t n_hi;
+  const _Float16* tail_k;
+  const _Float16* tail_v;
+  const int32_t* seq_lens;
+  const _Float16* q;
+  int32_t n_q_heads;
+  int32_t group;          // G = Hq / Hkv
+  int32_t n_head_groups;  // ceil(G / 4)
+  int32_t max_seq_len;
+  int32_t n_split;
+  int32_t pages_per_split;
+  float* partial;         // [batch][Hq][n_split][kPartialStride]
+  float* out;             // [batch][Hq][D]
+};
+
+constexpr int kPartialStride = 132;  // m, l, O[128], 2 pad floats
+
+// Split-KV plan shared by the workspace query and the launch.
+struct SplitPlan {
+  int n_split;
+  int pages_per_split;
+};
+SplitPlan plan_splits(int batch, int n_kv_heads, int n_head_groups, int max_seq_len);
+
+hipError_t launch_quantize(const QuantizeParams& p, hipStream_t stream);
+hipError_t launch_append(const AppendParams& p, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+
+}  // namespace kitty

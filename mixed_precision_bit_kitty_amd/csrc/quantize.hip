@@ -1,0 +1,390 @@
+// Page quantizer (prefill) and append/seal kernels for gfx950.
+//
+// One wave64 quantizes one (page of 32 tokens, KV head):
+//  * Key statistics per channel over the page's tokens ("Kitty -- Dynamic
+//    Channel-wise Mixed-Precision Keys", How it works / Prefill phase, step 1):
+//    a fixed balanced pairwise tree sum for the mean and for the sum of
+//    squared deviations m2, exact min and max.  Lane l owns channels 2l, 2l+1
+//    and holds all 32 tokens in registers, so the tree is register-local.
+//  * Dynamic Channel-wise Precision Boost ("Kitty: Accurate and Efficient
+//    2-bit KV Cache Quantization with Dynamic Channel-wise Precision Boost",
+//    Abstract; Prefill step 2): the n_hi channels with the largest m2, ties to
+//    the lower channel index.  The n_hi-th largest m2 is found by a 31-step
+//    bitwise search with wave ballots (m2 >= 0, so its bit pattern orders like
+//    the value); equal keys are ranked by channel index with ballot popcounts.
+//  * Asymmetric min/max codes (Prefill step 3): 4-bit on boosted channels,
+//    2-bit elsewhere, fp16 step, round-half-even, clamp; split into the base
+//    plane (top 2 bits) and the boost plane (low 2 bits of boosted channels).
+//  * Values: per token, groups of 32 channels, 2-bit; the group min/max is a
+//    DPP reduction over one 16-lane row (lane owns channels c and c + 16).
+//  * Codes are staged in LDS as bytes and packed into the record's code words
+//    with coalesced 16-byte stores.
+//
+// All float32 arithmetic here is separately rounded (no contraction); the
+// division is the correctly rounded one; fp32 -> fp16 conversion rounds to
+// nearest even.  Signed zeros of the inputs are read as +0.
+#include "kitty_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace kitty {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float h2f(uint16_t bits) { return (float)__builtin_bit_cast(_Float16, bits); }
+__device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+// fp16 input read as float32 with -0 mapped to +0
+__device__ __forceinline__ float canon16(uint16_t bits) { return h2f(bits == 0x8000u ? (uint16_t)0 : bits); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+// reductions over the 16 lanes of a DPP row: quad xor 1, quad xor 2, half mirror, row mirror
+__device__ __forceinline__ float row_min16(float v) {
+  v = fminf(v, dpp<0xB1>(v));
+  v = fminf(v, dpp<0x4E>(v));
+  v = fminf(v, dpp<0x141>(v));
+  v = fminf(v, dpp<0x140>(v));
+  return v;
+}
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  v = fmaxf(v, dpp<0x140>(v));
+  return v;
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Balanced pairwise tree over 32 values, level by level: a'_i = a_2i + a_2i+1.
+__device__ __forceinline__ float tree32(float (&a)[32]) {
+#pragma unroll
+  for (int s = 16; s >= 1; s >>= 1) {
+#pragma unroll
+    for (int i = 0; i < s; ++i) a[i] = a[2 * i] + a[2 * i + 1];
+  }
+  return a[0];
+}
+
+struct Step {
+  float inv;     // 1 / step, or 0 for a zero step
+  uint16_t s16;  // fp16 step
+};
+
+__device__ __forceinline__ Step make_step(float mn, float mx, float levels) {
+  float r = mx - mn;
+  float q = r / levels;
+  uint16_t s16 = f2h(q);
+  float s = h2f(s16);
+  Step st;
+  st.s16 = s16;
+  st.inv = (s != 0.0f) ? 1.0f / s : 0.0f;
+  return st;
+}
+
+__device__ __forceinline__ uint32_t code_of(float x, float mn, float inv, float levels) {
+  float t = (x - mn) * inv;
+  t = __builtin_rintf(t);
+  t = fminf(fmaxf(t, 0.0f), levels);
+  return (uint32_t)t;
+}
+
+// bytes 0, 2, 4, 6 of x (each a 2-bit code) -> bits 0, 2, 4, 6 of the result
+__device__ __forceinline__ uint32_t gather4(uint64_t x) {
+  x &= 0x0003000300030003ull;
+  x |= x >> 14;
+  x |= x >> 28;
+  return (uint32_t)x & 0xFFu;
+}
+// code word from combos A, B given as 8 code bytes each (element e in byte e)
+__device__ __forceinline__ uint32_t pack_word(uint64_t a, uint64_t b) {
+  return gather4(a) | (gather4(b) << 8) | (gather4(a >> 8) << 16) | (gather4(b >> 8) << 24);
+}
+
+// token t -> value metadata index kappa (inverse of tau)
+__host__ __device__ constexpr int kappa_of(int t) {
+  return t < 16 ? 8 * (t / 4) + (t % 4) : 8 * ((t - 16) / 4) + 4 + ((t - 16) % 4);
+}
+// (w, e) -> token
+__host__ __device__ constexpr int tau_of(int w, int e) { return e < 4 ? 4 * w + e : 16 + 4 * w + (e - 4); }
+
+// Rows of one page: row t at base + t * 128, except that row 31 comes from
+// `last` when it is set (the token being appended).
+struct RowSrc {
+  const _Float16* base;
+  const _Float16* last;
+  __device__ __forceinline__ const _Float16* row(int t) const {
+    return (t == kPageTokens - 1 && last) ? last : base + (size_t)t * kHeadDim;
+  }
+};
+
+// Quantize and pack one (page, head) into `rec`.  Called by a full wave;
+// `lds` is this wave's private 8 KB.
+template <int NHI>
+__device__ void quantize_page_wave(RowSrc ks, RowSrc vs, uint8_t* __restrict__ rec, uint8_t* __restrict__ lds) {
+  const int lane = threadIdx.x & 63;
+  uint8_t* lds_base = lds;          // [32 tokens][128 channels] base codes
+  uint8_t* lds_boost = lds + 4096;  // [32 tokens][NHI slots] boost codes
+  wave_lds_sync();
+
+  // ---------------- Key statistics: channels 2*lane, 2*lane + 1 -----------
+  float x0[32], x1[32];
+#pragma unroll
+  for (int t = 0; t < 32; ++t) {
+    uint32_t w2 = *reinterpret_cast<const uint32_t*>(ks.row(t) + 2 * lane);
+    x0[t] = canon16((uint16_t)(w2 & 0xFFFFu));
+    x1[t] = canon16((uint16_t)(w2 >> 16));
+  }
+  float a[32];
+#pragma unroll
+  for (int t = 0; t < 32; ++t) a[t] = x0[t];
+  const float mu0 = tree32(a) * (1.0f / 32.0f);
+#pragma unroll
+  for (int t = 0; t < 32; ++t) { float d = x0[t] - mu0; a[t] = d * d; }
+  const float m2_0 = tree32(a);
+#pragma unroll
+  for (int t = 0; t < 32; ++t) a[t] = x1[t];
+  const float mu1 = tree32(a) * (1.0f / 32.0f);
+#pragma unroll
+  for (int t = 0; t < 32; ++t) { float d = x1[t] - mu1; a[t] = d * d; }
+  const float m2_1 = tree32(a);
+  float mn0 = x0[0], mx0 = x0[0], mn1 = x1[0], mx1 = x1[0];
+#pragma unroll
+  for (int t = 1; t < 32; ++t) {
+    mn0 = fminf(mn0, x0[t]); mx0 = fmaxf(mx0, x0[t]);
+    mn1 = fminf(mn1, x1[t]); mx1 = fmaxf(mx1, x1[t]);
+  }
+
+  // ---------------- Ranking: top NHI by m2, ties to the lower channel -------
+  const uint64_t below = (1ull << lane) - 1ull;
+  bool h0, h1;
+  if (NHI == 0) {
+    h0 = h1 = false;
+  } else if (NHI == kHeadDim) {
+    h0 = h1 = true;
+  } else {
+    const uint32_t b0 = __builtin_bit_cast(uint32_t, m2_0);
+    const uint32_t b1 = __builtin_bit_cast(uint32_t, m2_1);
+    uint32_t T = 0;
+    for (int bit = 30; bit >= 0; --bit) {
+      const uint32_t cand = T | (1u << bit);
+      const int cnt = __popcll(__ballot(b0 >= cand)) + __popcll(__ballot(b1 >= cand));
+      if (cnt >= NHI) T = cand;
+    }
+    const int gt = __popcll(__ballot(b0 > T)) + __popcll(__ballot(b1 > T));
+    const uint64_t e0 = __ballot(b0 == T), e1 = __ballot(b1 == T);
+    const int before0 = __popcll(e0 & below) + __popcll(e1 & below);
+    const int before1 = before0 + (int)((e0 >> lane) & 1ull);
+    const int need = NHI - gt;
+    h0 = (b0 > T) || (b0 == T && before0 < need);
+    h1 = (b1 > T) || (b1 == T && before1 < need);
+  }
+  const uint64_t H0 = __ballot(h0), H1 = __ballot(h1);
+  const int pos0 = __popcll(H0 & below) + __popcll(H1 & below);
+  const int pos1 = pos0 + (h0 ? 1 : 0);
+
+  // ---------------- Key codes and metadata ---------------------------------
+  const float L0 = h0 ? 15.0f : 3.0f, L1 = h1 ? 15.0f : 3.0f;
+  const Step st0 = make_step(mn0, mx0, L0), st1 = make_step(mn1, mx1, L1);
+  const uint16_t ks0 = h0 ? f2h(4.0f * h2f(st0.s16)) : st0.s16;
+  const uint16_t ks1 = h1 ? f2h(4.0f * h2f(st1.s16)) : st1.s16;
+  *reinterpret_cast<uint32_t*>(rec + off_kscale(NHI) + 4 * lane) = (uint32_t)ks0 | ((uint32_t)ks1 << 16);
+  *reinterpret_cast<uint32_t*>(rec + off_kmin(NHI) + 4 * lane) = (uint32_t)f2h(mn0) | ((uint32_t)f2h(mn1) << 16);
+  // (pos < NHI always holds: exactly NHI channels are selected)
+  const bool w0 = h0 && pos0 < NHI, w1 = h1 && pos1 < NHI;
+  if (NHI > 0) {
+    if (w0) rec[off_idx(NHI) + pos0] = (uint8_t)(2 * lane);
+    if (w1) rec[off_idx(NHI) + pos1] = (uint8_t)(2 * lane + 1);
+  }
+#pragma unroll
+  for (int t = 0; t < 32; ++t) {
+    const uint32_t q0 = code_of(x0[t], mn0, st0.inv, L0);
+    const uint32_t q1 = code_of(x1[t], mn1, st1.inv, L1);
+    const uint32_t bq0 = h0 ? (q0 >> 2) : q0;
+    const uint32_t bq1 = h1 ? (q1 >> 2) : q1;
+    *reinterpret_cast<uint16_t*>(lds_base + t * 128 + 2 * lane) = (uint16_t)(bq0 | (bq1 << 8));
+    if (NHI > 0) {
+      if (w0) lds_boost[t * NHI + pos0] = (uint8_t)(q0 & 3u);
+      if (w1) lds_boost[t * NHI + pos1] = (uint8_t)(q1 & 3u);
+    }
+  }
+
+  // ---------------- Values: channels c0 = 32g + u and c0 + 16 --------------
+  {
+    const int g = lane >> 4, u = lane & 15;
+    const int c0 = 32 * g + u, c1 = c0 + 16;
+    uint32_t a0[32], a1[32];
+    uint16_t vs_lo = 0, vs_hi = 0, vm_lo = 0, vm_hi = 0;
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+      const _Float16* r = vs.row(t);
+      const float y0 = canon16(__builtin_bit_cast(uint16_t, r[c0]));
+      const float y1 = canon16(__builtin_bit_cast(uint16_t, r[c1]));
+      const float mn = row_min16(fminf(y0, y1));
+      const float mx = row_max16(fmaxf(y0, y1));
+      const Step st = make_step(mn, mx, 3.0f);
+      a0[t] = code_of(y0, mn, st.inv, 3.0f);
+      a1[t] = code_of(y1, mn, st.inv, 3.0f);
+      const int kap = kappa_of(t);
+      const uint16_t mnh = f2h(mn);
+      if (kap == u) { vs_lo = st.s16; vm_lo = mnh; }
+      if (kap == u + 16) { vs_hi = st.s16; vm_hi = mnh; }
+    }
+    uint16_t* vsc = reinterpret_cast<uint16_t*>(rec + off_vscale(NHI));
+    uint16_t* vmn = reinterpret_cast<uint16_t*>(rec + off_vmin(NHI));
+    vsc[32 * g + u] = vs_lo;
+    vsc[32 * g + u + 16] = vs_hi;
+    vmn[32 * g + u] = vm_lo;
+    vmn[32 * g + u + 16] = vm_hi;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int t = tau_of(w, e);
+        const int sh = 16 * (e & 1) + 2 * (e >> 1);
+        word |= a0[t] << sh;
+        word |= a1[t] << (sh + 8);
+      }
+      *reinterpret_cast<uint32_t*>(rec + off_v(NHI) + 16 * (16 * w + u) + 4 * g) = word;
+    }
+  }
+
+  // ---------------- Pack Key code planes from LDS ---------------------------
+  wave_lds_sync();
+  {
+    const int u = lane & 15, w = lane >> 4;
+    u32x4 words;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const uint64_t A = *reinterpret_cast<const uint64_t*>(lds_base + u * 128 + 32 * x + 8 * w);
+      const uint64_t B = *reinterpret_cast<const uint64_t*>(lds_base + (16 + u) * 128 + 32 * x + 8 * w);
+      words[x] = pack_word(A, B);
+    }
+    *reinterpret_cast<u32x4*>(rec + 16 * lane) = words;
+    if (NHI > 0) {
+      constexpr int nf = NHI / 32;
+#pragma unroll
+      for (int bb = 0; bb < nf; ++bb) {
+        const uint64_t A = *reinterpret_cast<const uint64_t*>(lds_boost + u * NHI + 32 * bb + 8 * w);
+        const uint64_t B = *reinterpret_cast<const uint64_t*>(lds_boost + (16 + u) * NHI + 32 * bb + 8 * w);
+        *reinterpret_cast<uint32_t*>(rec + off_kboost() + 4 * (lane * nf + bb)) = pack_word(A, B);
+      }
+      if ((NHI % 32) != 0 && lane < 32) {
+        const uint64_t A = *reinterpret_cast<const uint64_t*>(lds_boost + u * NHI + 32 * nf + 8 * w);
+        const uint64_t B = *reinterpret_cast<const uint64_t*>(lds_boost + (16 + u) * NHI + 32 * nf + 8 * w);
+        *reinterpret_cast<uint32_t*>(rec + off_kboost() + 256 * nf + 4 * lane) = pack_word(A, B);
+      }
+    }
+  }
+}
+
+// grid (pages + 1, Hkv, batch), one wave per block
+template <int NHI>
+__global__ __launch_bounds__(64) void quantize_pages_kernel(QuantizeParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[8192];
+  const int page = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+  int n = p.lens ? p.lens[b] : p.S;
+  n = n < 0 ? 0 : (n > p.S ? p.S : n);
+  int P = n / kPageTokens;
+  if (P > p.max_pages) P = p.max_pages;
+  const size_t seq_off = ((size_t)b * p.n_kv_heads + h) * (size_t)p.S * kHeadDim;
+  if (page < P) {
+    const int phys = p.block_table[(size_t)b * p.max_pages + page];
+    if (phys < 0 || (int64_t)phys >= p.n_pages) return;
+    uint8_t* rec = p.pages + (int64_t)phys * p.page_bytes + (int64_t)h * rec_bytes(NHI);
+    const size_t row0 = seq_off + (size_t)page * kPageTokens * kHeadDim;
+    quantize_page_wave<NHI>(RowSrc{p.k + row0, nullptr}, RowSrc{p.v + row0, nullptr}, rec, lds);
+  } else if (page == P) {
+    const int nt = n - P * kPageTokens;
+    const size_t tail_off = ((size_t)b * p.n_kv_heads + h) * kPageTokens * kHeadDim;
+    for (int t = 0; t < nt; ++t) {
+      const size_t src = seq_off + ((size_t)P * kPageTokens + t) * kHeadDim + 2 * lane;
+      const size_t dst = tail_off + (size_t)t * kHeadDim + 2 * lane;
+      *reinterpret_cast<uint32_t*>(p.tail_k + dst) = *reinterpret_cast<const uint32_t*>(p.k + src);
+      *reinterpret_cast<uint32_t*>(p.tail_v + dst) = *reinterpret_cast<const uint32_t*>(p.v + src);
+    }
+    if (h == 0 && lane == 0) p.seq_lens[b] = n;
+  }
+}
+
+// grid (batch), block = min(Hkv, 8) waves (8 KB of LDS each); each wave appends one head at a
+// time and seals it when the tail fills; the sequence length is bumped after
+// every head of the sequence is done.
+template <int NHI>
+__global__ __launch_bounds__(1024) void append_token_kernel(AppendParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+  const int b = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nw = blockDim.x >> 6;
+  int n = p.seq_lens[b];
+  if (n < 0) n = 0;
+  const int slot = n % kPageTokens;
+  for (int h = wave; h < p.n_kv_heads; h += nw) {
+    const size_t tail_off = ((size_t)b * p.n_kv_heads + h) * kPageTokens * kHeadDim;
+    const size_t new_off = ((size_t)b * p.n_kv_heads + h) * kHeadDim;
+    *reinterpret_cast<uint32_t*>(p.tail_k + tail_off + (size_t)slot * kHeadDim + 2 * lane) =
+        *reinterpret_cast<const uint32_t*>(p.k_new + new_off + 2 * lane);
+    *reinterpret_cast<uint32_t*>(p.tail_v + tail_off + (size_t)slot * kHeadDim + 2 * lane) =
+        *reinterpret_cast<const uint32_t*>(p.v_new + new_off + 2 * lane);
+    if (slot == kPageTokens - 1) {
+      const int pg = n / kPageTokens;
+      if (pg < p.max_pages) {
+        const int phys = p.block_table[(size_t)b * p.max_pages + pg];
+        if (phys >= 0 && (int64_t)phys < p.n_pages) {
+          uint8_t* rec = p.pages + (int64_t)phys * p.page_bytes + (int64_t)h * rec_bytes(NHI);
+          quantize_page_wave<NHI>(RowSrc{p.tail_k + tail_off, p.k_new + new_off},
+                                  RowSrc{p.tail_v + tail_off, p.v_new + new_off}, rec, lds_dyn + wave * 8192);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) p.seq_lens[b] = n + 1;
+}
+
+template <int NHI>
+hipError_t launch_quantize_t(const QuantizeParams& p, hipStream_t stream) {
+  dim3 grid(p.S / kPageTokens + 1, p.n_kv_heads, p.batch);
+  hipLaunchKernelGGL(quantize_pages_kernel<NHI>, grid, dim3(64), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int NHI>
+hipError_t launch_append_t(const AppendParams& p, hipStream_t stream) {
+  const int nw = p.n_kv_heads < 8 ? p.n_kv_heads : 8;
+  hipLaunchKernelGGL(append_token_kernel<NHI>, dim3(p.batch), dim3(64 * nw), nw * 8192, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+#define KITTY_NHI_DISPATCH(fn, nhi, ...)                   \
+  switch (nhi) {                                           \
+    case 0: return fn<0>(__VA_ARGS__);                     \
+    case 16: return fn<16>(__VA_ARGS__);                   \
+    case 32: return fn<32>(__VA_ARGS__);                   \
+    case 48: return fn<48>(__VA_ARGS__);                   \
+    case 64: return fn<64>(__VA_ARGS__);                   \
+    case 80: return fn<80>(__VA_ARGS__);                   \
+    case 96: return fn<96>(__VA_ARGS__);                   \
+    case 112: return fn<112>(__VA_ARGS__);                 \
+    case 128: return fn<128>(__VA_ARGS__);                 \
+    default: return hipErrorInvalidValue;                  \
+  }
+
+hipError_t launch_quantize(const QuantizeParams& p, hipStream_t stream) {
+  KITTY_NHI_DISPATCH(launch_quantize_t, p.n_hi, p, stream)
+}
+
+hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
+  KITTY_NHI_DISPATCH(launch_append_t, p.n_hi, p, stream)
+}
+
+}  // namespace kitty

@@ -54,6 +54,12 @@ def f32(x):
     return np.asarray(x).astype(_F32)
 
 
+def f32_stat(x):
+    """fp16 input widened to float32 with -0 read as +0, so that a page's
+    minimum (and the stored fp16 minimum) has a unique sign."""
+    return (np.asarray(x).astype(_F32) + _F32(0.0)).astype(_F32)
+
+
 # --------------------------------------------------------------------------
 # Key page: statistics, ranking, codes, two-plane decomposition
 # --------------------------------------------------------------------------
@@ -130,7 +136,7 @@ def quant_k_page(k16, n_hi):
     elsewhere; ``boost`` [..., 32, n_hi] = the low 2 bits of q on the boosted
     channels listed by ``idx``; ``kscale`` [..., D] fp16 = 4 * step on boosted
     channels, step elsewhere; ``kmin`` [..., D] fp16."""
-    x = f32(k16)
+    x = f32_stat(k16)
     _, m2, mn, mx = page_stats(x)
     idx, mask = rank_channels(m2, n_hi)
     levels = np.where(mask, HI_LEVELS, LO_LEVELS)
@@ -139,7 +145,8 @@ def quant_k_page(k16, n_hi):
     base = np.where(mask[..., None, :], q >> 2, q).astype(np.uint8)
     gather = np.broadcast_to(idx[..., None, :].astype(np.intp), q.shape[:-1] + (n_hi,))
     boost = (np.take_along_axis(q, gather, axis=-1) & 3).astype(np.uint8)
-    kscale = np.where(mask, f16(f32(s16) * _F32(4.0)), s16).astype(_F16)
+    with np.errstate(over="ignore"):   # 4 * step is only kept where it fits (boosted channels)
+        kscale = np.where(mask, f16(f32(s16) * _F32(4.0)), s16).astype(_F16)
     kmin = f16(mn)
     return dict(q=q, m2=m2, mask=mask, idx=idx, step=s16, base=base, boost=boost,
                 kscale=kscale, kmin=kmin)
@@ -149,7 +156,7 @@ def quant_v_page(v16):
     """Quantize Value pages: per token, groups of 32 channels, 2-bit
     asymmetric min/max.  v16: fp16 [..., 32, D].  Returns dict with ``a``
     [..., 32, D] codes, ``vscale``/``vmin`` [..., 32, D/32] fp16."""
-    y = f32(v16)
+    y = f32_stat(v16)
     shp = y.shape
     yg = y.reshape(shp[:-1] + (shp[-1] // V_GROUP, V_GROUP))
     mn = yg.min(axis=-1)

@@ -1,0 +1,88 @@
+"""Helpers of the GPU parity tests: run the HIP path through the C ABI and
+compare against the CPU oracle on the same seeded inputs."""
+import numpy as np
+
+import oracle as O
+
+ATOL = 2e-3  # max abs error of decode attention against the oracle's fp32 attention
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def dev(a):
+    torch = torch_mod()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def new_cache(batch, n_kv_heads, n_hi, max_tokens, **kw):
+    from mixed_precision_bit_kitty_amd import binding as B
+    return B.KittyCache(batch, n_kv_heads, n_hi, max_tokens, **kw)
+
+
+def host(t):
+    torch = torch_mod()
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _diff_fields(got, want, n_hi):
+    gk, gv = O.unpack_record(got, n_hi)
+    wk, wv = O.unpack_record(want, n_hi)
+    out = []
+    for key in gk:
+        d = int(np.sum(np.asarray(gk[key]).view(np.uint8) != np.asarray(wk[key]).view(np.uint8)))
+        if d:
+            out.append(f"{key}:{d}")
+    for key in gv:
+        d = int(np.sum(np.asarray(gv[key]).view(np.uint8) != np.asarray(wv[key]).view(np.uint8)))
+        if d:
+            out.append(f"{key}:{d}")
+    return out
+
+
+def compare_records(cache, oc, samples=None, seq_map=None, pool=None):
+    """Byte-compare GPU page records with the oracle's packed records.
+
+    samples: (b_oracle, page, head) triples, default all sealed pages.
+    seq_map: oracle sequence index -> GPU sequence index (default identity)."""
+    pool = host(cache.pool) if pool is None else pool
+    bt = host(cache.block_table)
+    rb = cache.record_bytes
+    if samples is None:
+        samples = [(b, j, h) for b in range(oc.batch) for j in range(oc.n_pages(b)) for h in range(oc.n_kv_heads)]
+    bad = []
+    for (b, j, h) in samples:
+        gb = b if seq_map is None else seq_map[b]
+        got = pool[bt[gb, j], h * rb:(h + 1) * rb]
+        want = O.pack_record(*oc.page_fields(b, h, j))
+        if not np.array_equal(got, want):
+            bad.append(((b, j, h), _diff_fields(got, want, oc.n_hi)))
+    assert not bad, f"{len(bad)} of {len(samples)} records differ, first: {bad[:5]}"
+    return len(samples)
+
+
+def compare_tails(cache, oc, seq_map=None):
+    tk, tv, sl = host(cache.tail_k), host(cache.tail_v), host(cache.seq_lens)
+    for b in range(oc.batch):
+        gb = b if seq_map is None else seq_map[b]
+        n = int(oc.seq_len[b])
+        assert int(sl[gb]) == n, (b, int(sl[gb]), n)
+        nt = n % 32
+        assert np.array_equal(tk[gb, :, :nt].view(np.uint16), oc.tail_k[b, :, :nt].view(np.uint16))
+        assert np.array_equal(tv[gb, :, :nt].view(np.uint16), oc.tail_v[b, :, :nt].view(np.uint16))
+
+
+def compare_decode(cache, oc, q, max_seq_len=None, seq_map=None, atol=ATOL):
+    """GPU decode attention on all sequences; oracle attention on the oracle's
+    sequences (all, or the subset seq_map names).  Returns the max error."""
+    out = host(cache.decode_attention(dev(q), max_seq_len=max_seq_len))
+    qo = q if seq_map is None else q[[seq_map[b] for b in range(oc.batch)]]
+    ref = O.decode_attention(oc, qo)
+    got = out if seq_map is None else out[[seq_map[b] for b in range(oc.batch)]]
+    assert np.all(np.isfinite(got))
+    err = float(np.abs(got - ref).max()) if ref.size else 0.0
+    assert err <= atol, f"max abs error {err} > {atol}"
+    return err, out

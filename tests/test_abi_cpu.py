@@ -1,0 +1,140 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/kitty.h declares, computes sizes, and rejects invalid arguments
+before touching the device (no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixed_precision_bit_kitty_amd import binding as B
+
+LIB = B.LIB_PATH
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libkitty.so not built")
+
+FAKE = 0x7F0000000000  # an aligned non-null address that is never dereferenced
+
+
+def test_exports_every_declared_symbol():
+    names = B.declared_symbols()
+    assert len(names) == 8
+    lib = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_header_error_codes_match_binding():
+    text = open(B.HEADER).read()
+    codes = dict(re.findall(r"(KITTY_\w+)\s*=\s*(-?\d+)", text))
+    assert int(codes["KITTY_OK"]) == B.KITTY_OK
+    assert int(codes["KITTY_ERR_INVALID_ARG"]) == B.KITTY_ERR_INVALID_ARG
+    assert int(codes["KITTY_ERR_UNSUPPORTED"]) == B.KITTY_ERR_UNSUPPORTED
+    assert int(codes["KITTY_ERR_WORKSPACE"]) == B.KITTY_ERR_WORKSPACE
+    assert int(codes["KITTY_ERR_HIP"]) == B.KITTY_ERR_HIP
+
+
+def test_abi_version():
+    assert B.kitty_abi_version() == 1
+
+
+@pytest.mark.parametrize("n_hi", [0, 16, 32, 48, 64, 128])
+def test_sizes(n_hi):
+    cfg = B.config(8, n_hi)
+    assert B.kitty_record_bytes(cfg) == 3072 + 9 * n_hi
+    pb = B.kitty_page_bytes(cfg)
+    assert pb % 256 == 0 and pb >= 8 * (3072 + 9 * n_hi) and pb - 8 * (3072 + 9 * n_hi) < 256
+
+
+def test_workspace_bytes_cover_partials():
+    cfg = B.config(8, 32)
+    nb = B.kitty_decode_workspace_bytes(cfg, 16, 32, 4096)
+    assert nb > 0 and nb % (16 * 32 * 132 * 4) == 0
+    # an empty cache still needs one split
+    assert B.kitty_decode_workspace_bytes(cfg, 1, 8, 0) == 1 * 8 * 132 * 4
+
+
+@pytest.mark.parametrize("cfg,code", [
+    ((64, 32, 8, 32), B.KITTY_ERR_UNSUPPORTED),
+    ((128, 16, 8, 32), B.KITTY_ERR_UNSUPPORTED),
+    ((128, 32, 0, 32), B.KITTY_ERR_INVALID_ARG),
+    ((128, 32, 8, 8), B.KITTY_ERR_UNSUPPORTED),
+    ((128, 32, 8, 144), B.KITTY_ERR_UNSUPPORTED),
+    ((128, 32, 8, -16), B.KITTY_ERR_UNSUPPORTED),
+])
+def test_config_rejected(cfg, code):
+    c = B.kitty_config_t(*cfg)
+    with pytest.raises(B.KittyError) as e:
+        B.kitty_record_bytes(c)
+    assert e.value.code == code
+    assert B.load().kitty_last_error().decode()
+
+
+def _view(**kw):
+    d = dict(pages=FAKE, n_pages=4, block_table=FAKE, batch=2, max_pages=2, tail_k=FAKE, tail_v=FAKE,
+             seq_lens=FAKE)
+    d.update(kw)
+    return B.kitty_kv_view_t(d["pages"], d["n_pages"], d["block_table"], d["batch"], d["max_pages"],
+                             d["tail_k"], d["tail_v"], d["seq_lens"])
+
+
+BAD_VIEWS = [
+    dict(pages=None), dict(pages=FAKE + 16), dict(n_pages=0), dict(block_table=None),
+    dict(block_table=FAKE + 2), dict(batch=0), dict(batch=70000), dict(max_pages=0),
+    dict(tail_k=None), dict(tail_v=FAKE + 8), dict(seq_lens=None), dict(seq_lens=FAKE + 1),
+]
+
+
+def _call_quantize(view, k=FAKE, v=FAKE, S=64, lens=None, cfg=None):
+    lib = B.load()
+    cfg = B.config(8, 32) if cfg is None else cfg
+    return lib.kitty_quantize_pages(ctypes.byref(cfg), ctypes.byref(view), k, v, S, lens, None)
+
+
+def _call_append(view, k=FAKE, v=FAKE):
+    lib = B.load()
+    return lib.kitty_append_token(ctypes.byref(B.config(8, 32)), ctypes.byref(view), k, v, None)
+
+
+def _call_decode(view, q=FAKE, hq=32, msl=64, out=FAKE, ws=FAKE, nbytes=1 << 30):
+    lib = B.load()
+    return lib.kitty_decode_attention(ctypes.byref(B.config(8, 32)), ctypes.byref(view), q, hq, msl, out, ws,
+                                      nbytes, None)
+
+
+@pytest.mark.parametrize("bad", BAD_VIEWS)
+def test_bad_view_rejected_everywhere(bad):
+    v = _view(**bad)
+    assert _call_quantize(v) == B.KITTY_ERR_INVALID_ARG
+    assert _call_append(v) == B.KITTY_ERR_INVALID_ARG
+    assert _call_decode(v) == B.KITTY_ERR_INVALID_ARG
+    lib = B.load()
+    assert lib.kitty_quantize_pages(None, ctypes.byref(v), FAKE, FAKE, 64, None, None) == B.KITTY_ERR_INVALID_ARG
+
+
+def test_quantize_arguments():
+    v = _view()
+    assert _call_quantize(v, k=None) == B.KITTY_ERR_INVALID_ARG
+    assert _call_quantize(v, v=FAKE + 2) == B.KITTY_ERR_INVALID_ARG
+    assert _call_quantize(v, S=-1) == B.KITTY_ERR_INVALID_ARG
+    assert _call_quantize(v, S=96) == B.KITTY_ERR_INVALID_ARG          # 3 pages > max_pages 2
+    assert _call_quantize(v, lens=FAKE + 2) == B.KITTY_ERR_INVALID_ARG
+    assert _call_quantize(v, cfg=B.config(8, 24)) == B.KITTY_ERR_UNSUPPORTED
+
+
+def test_append_arguments():
+    v = _view()
+    assert _call_append(v, k=None) == B.KITTY_ERR_INVALID_ARG
+    assert _call_append(v, v=FAKE + 1) == B.KITTY_ERR_INVALID_ARG
+
+
+def test_decode_arguments():
+    v = _view()
+    assert _call_decode(v, q=None) == B.KITTY_ERR_INVALID_ARG
+    assert _call_decode(v, hq=12) == B.KITTY_ERR_INVALID_ARG           # not a multiple of Hkv = 8
+    assert _call_decode(v, hq=0) == B.KITTY_ERR_INVALID_ARG
+    assert _call_decode(v, msl=-5) == B.KITTY_ERR_INVALID_ARG
+    assert _call_decode(v, out=None) == B.KITTY_ERR_INVALID_ARG
+    assert _call_decode(v, ws=None) == B.KITTY_ERR_INVALID_ARG
+    assert _call_decode(v, ws=FAKE + 64) == B.KITTY_ERR_INVALID_ARG
+    assert _call_decode(v, nbytes=16) == B.KITTY_ERR_WORKSPACE
+    assert "workspace" in B.load().kitty_last_error().decode()

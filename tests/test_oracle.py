@@ -611,3 +611,15 @@ def test_clamp_when_subnormal_step_rounds_down():
         q, s16 = O.quantize_levels(x, x.min(), x.max(), L)
         assert q[1] == L and q.max() == L
         assert float(s16) == (2 * ulp if L == 3 else ulp)
+
+
+def test_negative_zero_read_as_positive_zero():
+    # A page whose minimum is a signed zero stores kmin = +0 (0x0000).
+    x = np.abs(_page(6)[0])
+    x[:, 3] = np.float16(-0.0)
+    x[5, 3] = np.float16(1.0)
+    kf = O.quant_k_page(x, 32)
+    assert kf["kmin"].view(np.uint16)[3] == 0
+    vf = O.quant_v_page(x)
+    rows = [t for t in range(32) if t != 5]
+    assert np.all(vf["vmin"].view(np.uint16)[rows, 0] == 0)
