@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the Kitty 2-bit KV cache on one MI355X.
+
+A step is one decode step of one attention layer over the whole batch:
+``kitty_append_token`` (store the new token in the fp16 tail, sealing the
+tail into a quantized page every 32nd token: channel statistics, ranking,
+codes, two-plane packing) followed by ``kitty_decode_attention`` (fused
+dequant + QK + online softmax + PV over all pages, then the split merge).
+
+Workload (default): Llama-3-8B shape, batch 16, 32 query heads, 8 KV heads,
+head_dim 128, context 4096, hi_fraction 0.25, seeded synthetic fp16 K/V/Q.
+To keep reads coming from HBM rather than the 256 MB Infinity Cache, the
+steps rotate over L independent layer caches totalling >= 1 GiB.
+
+Printed: one JSON line (metric, value = GB/s of quantized KV read per step,
+tokens/s, a roofline object for the decode kernel measured with HIP events
+on the launch stream, and the CPU oracle timed on a bounded sample).
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+METRIC = "2-bit-KV decode attention: GB/s KV read vs HBM peak; tokens/s at batch×ctx"
+
+
+def _workload(name):
+    from mixed_precision_bit_kitty_amd import synth
+    table = {"llama3_8b": synth.LLAMA3_8B, "qwen3_8b": synth.QWEN3_8B, "batch_sweep": synth.BATCH_SWEEP,
+             "prefill_sweep": synth.PREFILL_SWEEP, "tiny": synth.TINY}
+    return table[name]
+
+
+def kv_bytes(seq_lens, n_kv_heads, record_bytes):
+    """Algorithmic KV bytes one decode call reads: every sealed page record
+    (3072 + 9 n_hi bytes per page and KV head) plus the fp16 tail tokens
+    (2 x 256 bytes per token and KV head)."""
+    tot = 0
+    for n in seq_lens:
+        tot += n_kv_heads * ((n // 32) * record_bytes + (n % 32) * 512)
+    return tot
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in ("decode.hip", "kitty_internal.h"):
+        with open(os.path.join(ROOT, "mixed_precision_bit_kitty_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel_hash, workload):
+    """HBM bytes per decode launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"decode_split_kernel_{workload}_hbm_counters.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha256_16") != kernel_hash:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, seconds):
+    """The oracle as it stands, one thread, on a bounded sample of the same
+    workload: decode steps (append + attention) on a subset of sequences."""
+    import oracle as O
+    from mixed_precision_bit_kitty_amd import synth
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(1)
+    except ImportError:  # pragma: no cover
+        limiter = None
+    n_seq = 2
+    x = synth.batch(w, batch=n_seq, steps=64)
+    oc = O.quantize_pages(x["k"], x["v"], w.n_hi)
+    rec = O.record_bytes(w.n_hi)
+    t0 = time.perf_counter()
+    steps = 0
+    read = 0
+    while True:
+        t = steps % 64
+        O.append_token(oc, x["k_new"][t], x["v_new"][t])
+        O.decode_attention(oc, x["q_new"][t])
+        read += kv_bytes([int(n) for n in oc.seq_len], w.n_kv_heads, rec)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    if limiter is not None:
+        limiter.unregister()
+    return {"value": round(read / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "tokens_per_s": round(steps * n_seq / el, 3),
+            "sample": f"{steps} decode steps (append + attention) of {n_seq} of the {w.batch} sequences, "
+                      f"ctx {w.ctx}, numpy oracle single-threaded, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=640)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--workload", default="llama3_8b",
+                    choices=["llama3_8b", "qwen3_8b", "batch_sweep", "prefill_sweep", "tiny"])
+    ap.add_argument("--batch", type=int, default=None, help="override the workload's batch (sweep points)")
+    ap.add_argument("--layers", type=int, default=0, help="layer caches to rotate (0: enough for >= 1 GiB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 1 GiB device copy (HBM counter calibration under rocprofv3)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mixed_precision_bit_kitty_amd import binding, synth
+
+    w = _workload(args.workload)
+    B = args.batch or w.batch
+    ctx, Hkv, Hq, n_hi = w.ctx, w.n_kv_heads, w.n_q_heads, w.n_hi
+    K, W = args.steps, args.warmup
+    torch.cuda.set_device(0)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    print(f"[bench] generating {w.name} batch {B} ctx {ctx}", file=sys.stderr, flush=True)
+    n_tok = 64
+    x = synth.batch(w, batch=B, steps=n_tok)
+    k_new, v_new, q_new = dev(x["k_new"]), dev(x["v_new"]), dev(x["q_new"])
+
+    max_tokens = ctx + K + W + 32
+    probe = binding.KittyCache(1, Hkv, n_hi, max_tokens)
+    layer_bytes = B * probe.max_pages * probe.page_bytes
+    del probe
+    L = args.layers or max(1, math.ceil((1 << 30) / layer_bytes))
+    print(f"[bench] {L} layer caches x {layer_bytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
+    layers = [binding.KittyCache(B, Hkv, n_hi, max_tokens) for _ in range(L)]
+    kd, vd = dev(x["k"]), dev(x["v"])
+    layers[0].quantize_pages(kd, vd)
+    for c in layers[1:]:
+        c.pool.copy_(layers[0].pool)
+        c.tail_k.copy_(layers[0].tail_k)
+        c.tail_v.copy_(layers[0].tail_v)
+        c.seq_lens.copy_(layers[0].seq_lens)
+    del kd, vd
+    lens = [[ctx] * B for _ in range(L)]
+    msl = max_tokens
+    outs = torch.empty((B, Hq, 128), dtype=torch.float32, device="cuda")
+    ws = layers[0].workspace(Hq, msl)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        c = layers[i % L]
+        t = i % n_tok
+        c.append_token(k_new[t], v_new[t])
+        if ev is not None:
+            ev[0].record()
+        c.decode_attention(q_new[t], max_seq_len=msl, out=outs, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(W):
+        step(i)
+        for b in range(B):
+            lens[i % L][b] += 1
+    torch.cuda.synchronize()
+
+    rec = layers[0].record_bytes
+    bytes_steps = []
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(K):
+        step(W + i, evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    for i in range(K):
+        li = (W + i) % L
+        for b in range(B):
+            lens[li][b] += 1
+        bytes_steps.append(kv_bytes(lens[li], Hkv, rec))
+    total_ms = start.elapsed_time(end)
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    ms_step = total_ms / K
+    avg_bytes = sum(bytes_steps) / K
+    gbs = avg_bytes / (ms_step * 1e-3) / 1e9
+    dec_avg_ms = sum(dec_ms) / K
+    dec_gbs = avg_bytes / (dec_avg_ms * 1e-3) / 1e9
+    print(f"[bench] step {ms_step * 1e3:.2f} us, decode call {dec_avg_ms * 1e3:.2f} us "
+          f"({dec_gbs:.0f} GB/s, {dec_gbs / HBM_PEAK_GBS:.3f} of peak)", file=sys.stderr, flush=True)
+
+    if args.calibrate_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        bcopy = torch.empty_like(a)
+        bcopy.copy_(a)
+        torch.cuda.synchronize()
+        print("[bench] calibration copy: 1 GiB read + 1 GiB written", file=sys.stderr, flush=True)
+        del a, bcopy
+
+    khash = source_hash()
+    roof = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": committed_traffic(khash, args.workload),
+            "kernel": "kitty_decode_attention (decode_split_kernel + combine_kernel)",
+            "bytes_per_launch": int(avg_bytes), "avg_launch_us": round(dec_avg_ms * 1e3, 3),
+            "kernel_source_sha256_16": khash}
+    res = {
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_step, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp16", "data": "synthetic",
+        "tokens_per_s": round(B / (ms_step * 1e-3), 1),
+        "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "config": {"workload": f"{w.name}: one layer, batch {B}, {Hq} query heads, {Hkv} KV heads, head_dim 128, "
+                               f"context {ctx}+, hi_fraction {w.hi_fraction} (n_hi {n_hi}); step = append + decode; "
+                               f"{L} layer caches rotated ({L * layer_bytes / 2**30:.2f} GiB)",
+                   "batch": B, "ctx": ctx, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": 128, "n_hi": n_hi,
+                   "layers_rotated": L},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w.with_(batch=B), args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
