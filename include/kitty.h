@@ -112,8 +112,10 @@ int kitty_quantize_pages(const kitty_config_t* cfg, const kitty_kv_view_t* kv,
 int kitty_append_token(const kitty_config_t* cfg, const kitty_kv_view_t* kv,
                        const uint16_t* k_new, const uint16_t* v_new, void* stream);
 
-/* Workspace bytes kitty_decode_attention needs for this shape (split-KV
- * partial results).  max_seq_len: an upper bound on every seq_lens[b]. */
+/* Workspace bytes kitty_decode_attention needs for this shape: split-KV
+ * partial results (m, l, O per query head and split) followed by one arrival
+ * counter per (sequence, KV head, group of 4 query heads).  max_seq_len: an
+ * upper bound on every seq_lens[b]. */
 int kitty_decode_workspace_bytes(const kitty_config_t* cfg, int32_t batch, int32_t n_q_heads,
                                  int32_t max_seq_len, size_t* out);
 
@@ -124,8 +126,12 @@ int kitty_decode_workspace_bytes(const kitty_config_t* cfg, int32_t batch, int32
  * sealed pages in order, then the fp16 tail: out[b][hq] = softmax(q . k^ /
  * sqrt(D)) . v^ with k^, v^ the dequantized keys and values.  out: device
  * fp32 [batch][Hq][D] (zeros for an empty sequence).  max_seq_len bounds
- * seq_lens (tokens beyond it are ignored).  workspace: device, 256-byte
- * aligned, at least kitty_decode_workspace_bytes(...) bytes. */
+ * seq_lens (tokens beyond it are ignored); at most 131103 (4096 pages plus a
+ * tail), else KITTY_ERR_UNSUPPORTED.  workspace: device, 256-byte
+ * aligned, at least kitty_decode_workspace_bytes(...) bytes, zero-filled by
+ * the caller before its first use (e.g. allocated zeroed); every completed
+ * call leaves its counter area zero again, so one workspace serves any
+ * number of calls, but calls that overlap in time must not share one. */
 int kitty_decode_attention(const kitty_config_t* cfg, const kitty_kv_view_t* kv,
                            const uint16_t* q, int32_t n_q_heads, int32_t max_seq_len,
                            float* out, void* workspace, size_t workspace_bytes, void* stream);

@@ -57,11 +57,13 @@ def declared_symbols(header=HEADER):
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(kitty_\w+)\s*\(", text, re.M)))
 
 
-def load(path=LIB_PATH):
-    """Load libkitty.so once and declare the C signatures."""
+def load(path=None):
+    """Load libkitty.so once and declare the C signatures.  KITTY_LIB (env)
+    selects another build of the same library, e.g. for A/B comparisons."""
     global _lib
     if _lib is not None:
         return _lib
+    path = path or os.environ.get("KITTY_LIB") or LIB_PATH
     if not os.path.exists(path):
         raise KittyError(KITTY_ERR_HIP, f"{path} is missing; run __graft_entry__.build() first")
     lib = ctypes.CDLL(path)
@@ -214,7 +216,7 @@ class KittyCache:
         import torch
         nb = kitty_decode_workspace_bytes(self.cfg, self.batch, n_q_heads, max_seq_len)
         if self._ws is None or self._ws.numel() < max(nb, 256):
-            self._ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=self.pool.device)
+            self._ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device=self.pool.device)
         return self._ws
 
     def decode_attention(self, q, max_seq_len=None, out=None, workspace=None, stream=None):

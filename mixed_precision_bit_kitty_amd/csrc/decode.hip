@@ -1,270 +1,449 @@
 // Fused decode attention over the quantized page records (gfx950).
 //
 // "Kitty: Accurate and Efficient 2-bit KV Cache Quantization with Dynamic
-// Channel-wise Precision Boost", Abstract: the page dequantization is uniform
+// Channel-wise Precision Boost", Abstract: page dequantization is uniform
 // across lanes because each mixed-precision Key page is two uniform 2-bit
-// tensors.  Here the dequantization is folded into the two contractions:
+// tensors.  Here the dequantization is folded into the two contractions,
 //
-//   q . k^_t = sum_c (q_c kscale_c) base_tc + sum_j (q_idx_j kscale_idx_j / 4)
-//              boost_tj + sum_c q_c kmin_c
-//   sum_t p_t v^_tc = sum_t (p_t vscale_t,g) a_tc + sum_t p_t vmin_t,g
+//   q . k^_t = sum_c (q_c kscale_c) base_tc + sum_j (q_idx_j kscale_idx_j) boost_tj / 4
+//              + sum_c q_c kmin_c
+//   sum_t p_t v^_tc = sum_t (p_t vscale_t,g) a_tc + sum_t p_t vmin_t,g ,
 //
-// Codes enter an MFMA (v_mfma_f32_16x16x32_f16) as exact fp16 values 4 + code
-// (one shift + one AND-OR per two codes); the per-page scale is folded into
-// the other operand, which is split into two fp16 limbs (hi + lo represent
-// the fp32 product of two fp16 numbers exactly), placed in different MFMA
-// columns and summed after the product.  The +4 code offset and the minimum
-// terms are per-page constants added on the VALU.
+// which run on v_mfma_f32_16x16x32_f16:
+//  * codes become exact fp16 operands off + code with one shift and one
+//    AND-OR per two codes (off = 4 or 16 by bit position, see unpack_codes);
+//  * the per-page scale goes into the other operand as two fp16 limbs
+//    (hi = f16(x), lo = f16(x - hi)), which together carry the product to
+//    ~22 bits; the limbs sit in different MFMA columns and are summed after;
+//  * the code offsets and the minimum terms are per-page constants that also
+//    run on MFMA (constant A operands), so no VALU reduction is needed.
 //
-// One wave = one (sequence, KV head, group of <= 4 query heads, split of
+// One wave = one (sequence, KV head, group of <= 4 query heads, range of
 // pages).  Lane l: column n = l & 15, row group w = l >> 4.  QK^T is computed
-// transposed (rows = 16 tokens, columns = query head x limb), so each lane
-// ends up holding the logits of tokens tau(w, 0..7) for head n & 3, which is
-// exactly the K-slice it must feed to the PV MFMA: softmax needs no data
-// movement besides the row-group max.  Online softmax runs in the log2
-// domain; each split writes (m, l, O) and a second kernel merges the splits.
+// transposed (rows = 16 tokens, columns = head x limb, columns 8..15 repeat
+// 0..7), so after one DPP add every lane holds the logits of tokens
+// tau(w, 0..7) of head n & 3 -- exactly the K slice it feeds to PV.
+//
+// Pages stream through a per-wave LDS ring with global_load_lds_dwordx4
+// (kRing pages in flight); per page the limbs are computed once per
+// (head, channel) and per (head, token, group) and exchanged through LDS.
+// Online softmax runs in the log2 domain and rescales only when the max
+// grows.  Each wave writes (m, l, O) for its page range; the last wave of a
+// (sequence, KV head, head group) merges them (log-sum-exp) into the output.
 #include "kitty_internal.h"
 
 namespace kitty {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLog2e = 1.4426950408889634f;
-
-__device__ __forceinline__ float h2f(_Float16 h) { return (float)h; }
-
-// Two fp16 MFMA operands 4 + code from one code word (combo 0 = A, 1 = B).
-template <int COMBO>
-__device__ __forceinline__ half8 unpack_codes(uint32_t word) {
-  u32x4 r;
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const int sh = 8 - (2 * d + 8 * COMBO);
-    const uint32_t x = sh >= 0 ? (word << sh) : (word >> (-sh));
-    r[d] = (x & 0x03000300u) | 0x44004400u;
-  }
-  return __builtin_bit_cast(half8, r);
-}
+constexpr int kRing = 2;         // pages in flight per wave (LDS DMA streams at full rate with 2)
+constexpr int kRowRor4 = 0x124;  // DPP: lane i <- lane (i - 4) mod 16 of its row
+constexpr int kRowRor12 = 0x12C; // DPP: lane i <- lane (i + 4) mod 16 of its row
 
 __device__ __forceinline__ floatx4 mfma(half8 a, half8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float xor_sum(float v, int m) { return v + __shfl_xor(v, m); }
-
-// hi / lo fp16 limbs of x; `limb` selects which one this lane supplies
-__device__ __forceinline__ _Float16 limb_of(float x, int limb) {
-  const _Float16 hi = (_Float16)x;
-  const _Float16 lo = (_Float16)(x - (float)hi);
-  return limb == 0 ? hi : (limb == 1 ? lo : (_Float16)0.0f);
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
-struct SoftmaxState {
-  float m;        // running max (log2 domain), -inf before the first token
-  float l;        // this lane's share of the running denominator
-  floatx4 o[8];   // PV accumulators: 8 blocks of 16 channels
-  float corr[4];  // per value group: sum_t p_t (vmin - 4 vscale)
+// s_waitcnt vmcnt(N) only (expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// s_waitcnt lgkmcnt(0) only
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+// Make this wave's LDS writes visible to its later LDS reads by other lanes:
+// wait until the writes have completed (measured on gfx950: a ds_read_b128
+// issued right after a ds_write_b128 of the same wave can return stale data)
+// and keep the compiler from moving memory accesses across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// MFMA operand from one code word: elements of combo COMBO (0 = A, 1 = B) as
+// fp16 (off + code), with four shifts and eight AND-ORs for both combos of a
+// word.  Dword d holds elements 2d, 2d+1, whose codes sit at bits 2d + 8*COMBO
+// and 16 + 2d + 8*COMBO.  They move to bits 8/24 (mantissa bits 8..9 under an
+// exponent field E: value 2^(E-15) (1 + c/4)) or to bits 6/22 (2^(E-15)
+// (1 + c/16)), whichever lets two dwords share a shift:
+//   combo A: d0 <<8 (off 4), d1 <<4 (off 16), d2 <<4 (off 4), d3 as is (off 16)
+//   combo B: d0 as is (off 4), d1 >>4 (off 16), d2 >>4 (off 4), d3 >>8 (off 16)
+// so element j carries offset 4 for j in {0,1,4,5} and 16 for j in {2,3,6,7}.
+// The masks and exponent patterns live in VGPRs (ExpBits, made opaque once at
+// kernel start) so that each AND-OR selects to one v_and_or_b32 with three
+// VGPR operands (gfx9 VOP3 takes no literal and at most one SGPR).  The
+// instruction is left to the compiler, not written as inline asm: the hazard
+// recognizer must see every VALU write that an MFMA reads.
+struct ExpBits {
+  uint32_t e4, e16;  // exponent fields giving 4 + c and 16 + c (or a quarter of them)
+  uint32_t m8, m6;   // code masks at bits 8..9 / 24..25 and 6..7 / 22..23
+};
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {  // loop-invariant, read by VALU only
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(c));
+  return r;
+}
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t orv) { return (x & mask) | orv; }
+template <int COMBO>
+__device__ __forceinline__ half8 unpack_codes(uint32_t w, ExpBits e) {
+  const uint32_t m8 = e.m8, m6 = e.m6;
+  u32x4 r;
+  if (COMBO == 0) {
+    const uint32_t s8 = w << 8, s4 = w << 4;
+    r[0] = and_or(s8, m8, e.e4);
+    r[1] = and_or(s4, m6, e.e16);
+    r[2] = and_or(s4, m8, e.e4);
+    r[3] = and_or(w, m6, e.e16);
+  } else {
+    const uint32_t s4 = w >> 4, s8 = w >> 8;
+    r[0] = and_or(w, m8, e.e4);
+    r[1] = and_or(s4, m6, e.e16);
+    r[2] = and_or(s4, m8, e.e4);
+    r[3] = and_or(s8, m6, e.e16);
+  }
+  return __builtin_bit_cast(half8, r);
+}
+
+// half8 with value a at elements {0,1,4,5} and b at {2,3,6,7}
+__device__ __forceinline__ half8 half8_ab(float a, float b) {
+  half8 v;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = (_Float16)(((j >> 1) & 1) ? b : a);
+  return v;
+}
+
+// Per-wave LDS: ring of kRing records, then the limb exchange areas.
+template <int NHI>
+struct Lds {
+  uint8_t ring[kRing][rec_bytes(NHI)];
+  _Float16 qt[2][4][kHeadDim];  // q * kscale limbs [limb][head][channel]
+  _Float16 pt[4][2][4][4][8];   // p * vscale limbs [group][limb][head][w][j]
+  _Float16 pl[2][4][4][8];      // p limbs [limb][head][w][j]
+  float red[2][4][4];           // final corrections [kind][head][group]
+  float fw[4][64];              // split weights of the merging wave [head][split]
 };
 
-// Online-softmax update with 8 new logits (log2 domain, already scaled).
-__device__ __forceinline__ void softmax_update(SoftmaxState& st, const float (&s)[8], float (&p)[8]) {
-  float mp = s[0];
+template <int NHI>
+constexpr int dma_per_page() { return rec_bytes(NHI) / 1024 + (rec_bytes(NHI) % 1024 ? 1 : 0); }
+
+// Copy one record into an LDS slot: 16 bytes per lane per instruction.
+template <int NHI>
+__device__ __forceinline__ void dma_record(const uint8_t* __restrict__ rec, uint8_t* slot, int lane) {
+  constexpr int rb = rec_bytes(NHI);
+  constexpr int nfull = rb / 1024, rem = rb % 1024;
 #pragma unroll
-  for (int j = 1; j < 8; ++j) mp = fmaxf(mp, s[j]);
-  mp = fmaxf(mp, __shfl_xor(mp, 16));
-  mp = fmaxf(mp, __shfl_xor(mp, 32));
-  const float mn = fmaxf(st.m, mp);
-  const float alpha = exp2f(st.m - mn);
+  for (int m = 0; m < nfull; ++m)
+    __builtin_amdgcn_global_load_lds(rec + 1024 * m + 16 * lane, (lds_void*)(slot + 1024 * m), 16, 0, 0);
+  if (rem != 0 && 16 * lane < rem)
+    __builtin_amdgcn_global_load_lds(rec + 1024 * nfull + 16 * lane, (lds_void*)(slot + 1024 * nfull), 16, 0, 0);
+}
+
+// Wait until the oldest in-flight page has landed; `ahead` pages were issued after it.
+template <int NHI>
+__device__ __forceinline__ void wait_page(int ahead) {
+  constexpr int L = dma_per_page<NHI>();
+  compiler_fence();
+  if (ahead >= 1) wait_vmcnt<L>();
+  else wait_vmcnt<0>();
+  compiler_fence();
+}
+
+// Max over the four 16-lane rows of a wave.  (v_permlane16/32_swap would avoid
+// the LDS crossbar, but on this toolchain their results were not reliable
+// here, so the exchange uses ds_bpermute through __shfl_xor.)
+__device__ __forceinline__ float row_group_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float x) {  // helper for 16-lane row reductions
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp_row<0xB1>(v));
+  v = fmaxf(v, dpp_row<0x4E>(v));
+  v = fmaxf(v, dpp_row<0x141>(v));
+  v = fmaxf(v, dpp_row<0x140>(v));
+  return v;
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_row<0xB1>(v);
+  v += dpp_row<0x4E>(v);
+  v += dpp_row<0x141>(v);
+  v += dpp_row<0x140>(v);
+  return v;
+}
+
+struct WaveState {
+  float m;        // running max of the scaled logits (log2 domain)
+  float l;        // this lane's share of the softmax denominator
+  floatx4 o[8];   // PV accumulators, channel blocks of 16
+  floatx4 corr;   // value-minimum / code-offset correction accumulator
+};
+
+// Online softmax over 8 raw logits s; s becomes the probabilities.
+__device__ __forceinline__ void softmax_step(WaveState& st, float (&s)[8], float sl2) {
+  float mx = s[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) mx = fmaxf(mx, s[j]);
+  mx = row_group_max(mx);
+  const float mnew = fmaxf(st.m, mx * sl2);
+  if (__ballot(mnew > st.m)) {  // wave-uniform: rescale only when some max grew
+    const float alpha = __builtin_amdgcn_exp2f(st.m - mnew);
+    st.l *= alpha;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) st.o[mb] *= alpha;
+    st.corr *= alpha;
+    st.m = mnew;
+  }
+  const bool live = st.m != -INFINITY;
   float ps = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) { p[j] = exp2f(s[j] - mn); ps += p[j]; }
-  st.l = st.l * alpha + ps;
-#pragma unroll
-  for (int mb = 0; mb < 8; ++mb) st.o[mb] *= alpha;
-#pragma unroll
-  for (int g = 0; g < 4; ++g) st.corr[g] *= alpha;
-  st.m = mn;
+  for (int j = 0; j < 8; ++j) {
+    s[j] = live ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], sl2, -st.m)) : 0.0f;
+    ps += s[j];
+  }
+  st.l += ps;
 }
 
 template <int NHI>
-__global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
-  __shared__ float qs[4][kHeadDim];
-  constexpr int NB = (NHI + 31) / 32;  // boost slot blocks
-  constexpr int NF = NHI / 32;         // full ones
+__global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
+  constexpr int NB = (NHI + 31) / 32;  // boost slot blocks (the last may be half)
+  constexpr int NF = NHI / 32;         // full boost blocks
+  constexpr int RB = rec_bytes(NHI);
+  __shared__ __attribute__((aligned(16))) Lds<NHI> sm;
+
   const int split = blockIdx.x;
   const int hk = blockIdx.y / p.n_head_groups, hg = blockIdx.y % p.n_head_groups;
   const int b = blockIdx.z;
-  const int lane = threadIdx.x, n = lane & 15, w = lane >> 4, hl = n & 3, limb = n >> 2;
+  const int lane = threadIdx.x, n = lane & 15, w = lane >> 4, h = n & 3, limb = (n >> 2) & 1;
   const int hq0 = hk * p.group + 4 * hg;
   const int gcount = min(4, p.group - 4 * hg);
-  const bool col_ok = (limb < 2) && (hl < gcount);
 
-  // queries of this head group -> LDS (fp32), zero for absent heads
+  // Independent loads first (one memory round trip before the first DMA):
+  // the sequence length, this split's page ids (lane j: page p0 + j), queries.
+  const int p0 = split * p.pages_per_split;
+  const size_t page_row = (size_t)b * p.max_pages;
+  const int seq_raw = p.seq_lens[b];
+  const int id_raw = (lane < p.pages_per_split && p0 + lane < p.max_pages) ? p.block_table[page_row + p0 + lane] : -1;
+  const _Float16* qg = p.q + ((size_t)b * p.n_q_heads + hq0) * kHeadDim;
+  half8 bq_plain[4];  // plain q as the B operand of the minimum term: limb-0 columns only
 #pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    float q0 = 0.0f, q1 = 0.0f;
-    if (h < gcount) {
-      const _Float16* qp = p.q + ((size_t)b * p.n_q_heads + hq0 + h) * kHeadDim + 2 * lane;
-      q0 = h2f(qp[0]);
-      q1 = h2f(qp[1]);
-    }
-    qs[h][2 * lane] = q0;
-    qs[h][2 * lane + 1] = q1;
+  for (int kb = 0; kb < 4; ++kb) {
+    half8 v = {};
+    if (limb == 0 && h < gcount) v = *reinterpret_cast<const half8*>(qg + h * kHeadDim + 32 * kb + 8 * w);
+    bq_plain[kb] = v;
   }
-  __syncthreads();
-  float qv[32];  // q of head hl at channels 32kb + 8w + j, zero unless col_ok
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) qv[kb * 8 + j] = col_ok ? qs[hl][32 * kb + 8 * w + j] : 0.0f;
+  // producer of the q * kscale limbs: head ph, channels pc .. pc + 7
+  const int ph = lane & 3, pc = 8 * (lane >> 2);
+  half8 q_prod = {};
+  if (ph < gcount) q_prod = *reinterpret_cast<const half8*>(qg + ph * kHeadDim + pc);
 
-  int seq = p.seq_lens[b];
-  seq = seq < 0 ? 0 : (seq > p.max_seq_len ? p.max_seq_len : seq);
+  const int seq = seq_raw < 0 ? 0 : (seq_raw > p.max_seq_len ? p.max_seq_len : seq_raw);
   int P = seq / kPageTokens;
   const int ntail = seq - P * kPageTokens;
   if (P > p.max_pages) P = p.max_pages;
-  const int p0 = split * p.pages_per_split;
   const int p1 = min(p0 + p.pages_per_split, P);
-  const int tail_split = min(P / p.pages_per_split, p.n_split - 1);
-  const bool do_tail = ntail > 0 && split == tail_split;
+  const int npg = p1 > p0 ? p1 - p0 : 0;
+  const bool do_tail = ntail > 0 && split == min(P / p.pages_per_split, p.n_split - 1);
+  const uint8_t* head_base = p.pages + (int64_t)hk * RB;
+  const int ids = lane < npg ? id_raw : -1;  // physical page of p0 + lane (at most 64 per wave)
+  auto phys_of = [&](int i) -> int { return __builtin_amdgcn_readlane(ids, i); };
+  auto rec_of = [&](int phys) -> const uint8_t* {
+    if (phys < 0 || (int64_t)phys >= p.n_pages) phys = 0;  // invalid ids read page 0 and are masked
+    return head_base + (int64_t)phys * p.page_bytes;
+  };
+#pragma unroll
+  for (int d = 0; d < kRing; ++d)
+    if (d < npg) dma_record<NHI>(rec_of(phys_of(d)), sm.ring[d], lane);
 
+  // ---- per-wave constants -------------------------------------------------
+  const uint32_t m8v = vgpr_const(0x03000300u), m6v = vgpr_const(0x00C000C0u);
+  const ExpBits ex_base{vgpr_const(0x44004400u), vgpr_const(0x4C004C00u), m8v, m6v};   // 4 + c, 16 + c
+  const ExpBits ex_boost{vgpr_const(0x3C003C00u), vgpr_const(0x44004400u), m8v, m6v};  // (4 + c) / 4, (16 + c) / 4
+  const half8 a_off = half8_ab(-4.0f, -16.0f);  // base code offsets per element
+  const half8 a_offb = half8_ab(-1.0f, -4.0f);  // boost code offsets (weight 1/4)
+  // correction operand: rows 0..3 vmin (x1), rows 4..7 vscale x (-offset / 16)
+  const half8 corr_mul = n < 4 ? half8_ab(1.0f, 1.0f) : (n < 8 ? half8_ab(-0.25f, -1.0f) : half8_ab(0.0f, 0.0f));
   const float sl2 = (1.0f / sqrtf((float)kHeadDim)) * kLog2e;
-  SoftmaxState st;
+  const float limb_f = (float)limb;
+  // PV B operand source: lanes n < 8 read the group's p * vscale limbs, lanes
+  // n >= 8 the p limbs (same address for every group)
+  const _Float16* b_src = n < 8 ? &sm.pt[0][limb][h][w][0] : &sm.pl[limb][h][w][0];
+  const int b_stride = n < 8 ? 2 * 4 * 4 * 8 : 0;
+
+  WaveState st;
   st.m = -INFINITY;
   st.l = 0.0f;
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) st.o[mb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  st.corr = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int i = 0; i < npg; ++i) {
+    const int slot = i % kRing;
+    const uint8_t* S = sm.ring[slot];
+    wait_page<NHI>(min(kRing - 1, npg - 1 - i));
+    const int phys = phys_of(i);
+    const float vbias = (phys >= 0 && (int64_t)phys < p.n_pages) ? 0.0f : -INFINITY;  // masks invalid pages
+
+    // ---- q * kscale limbs, one (head, 8 channels) per lane --------------------
+    {
+      const half8 ks = *reinterpret_cast<const half8*>(S + off_kscale(NHI) + 2 * pc);
+      half8 hi, lo;
 #pragma unroll
-  for (int g = 0; g < 4; ++g) st.corr[g] = 0.0f;
+      for (int j = 0; j < 8; ++j) {
+        const _Float16 hv = (_Float16)((float)q_prod[j] * (float)ks[j]);
+        hi[j] = hv;
+        lo[j] = (_Float16)__builtin_fmaf((float)q_prod[j], (float)ks[j], -(float)hv);
+      }
+      *reinterpret_cast<half8*>(&sm.qt[0][ph][pc]) = hi;
+      *reinterpret_cast<half8*>(&sm.qt[1][ph][pc]) = lo;
+    }
+    wave_lds_sync();
 
-  const int rb = rec_bytes(NHI);
-  for (int pg = p0; pg < p1; ++pg) {
-    const int phys = p.block_table[(size_t)b * p.max_pages + pg];
-    if (phys < 0 || (int64_t)phys >= p.n_pages) continue;
-    const uint8_t* rec = p.pages + (int64_t)phys * p.page_bytes + (int64_t)hk * rb;
-
-    const u32x4 kw = *reinterpret_cast<const u32x4*>(rec + 16 * lane);
-    const u32x4 vw = *reinterpret_cast<const u32x4*>(rec + off_v(NHI) + 16 * lane);
+    // ---- QK^T ----------------------------------------------------------------
+    const u32x4 kw = *reinterpret_cast<const u32x4*>(S + 16 * lane);
+    half8 bq[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) bq[kb] = *reinterpret_cast<const half8*>(&sm.qt[limb][h][32 * kb + 8 * w]);
+    floatx4 c0 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const half8 kmin = *reinterpret_cast<const half8*>(S + off_kmin(NHI) + 2 * (32 * kb + 8 * w));
+      c0 = mfma(kmin, bq_plain[kb], c0);
+      c0 = mfma(a_off, bq[kb], c0);
+    }
+    half8 bb[NB > 0 ? NB : 1];
     uint32_t bw[NB > 0 ? NB : 1];
 #pragma unroll
-    for (int bb = 0; bb < NF; ++bb) bw[bb] = *reinterpret_cast<const uint32_t*>(rec + off_kboost() + 4 * (lane * NF + bb));
-    if (NB > NF) bw[NF] = lane < 32 ? *reinterpret_cast<const uint32_t*>(rec + off_kboost() + 256 * NF + 4 * lane) : 0u;
-    half8 ksv[4], kmv[4], vsv[4], vmv[4];
+    for (int k2 = 0; k2 < NB; ++k2) {
+      const int s0 = 32 * k2 + 8 * w;
+      half8 v = {};
+      if (s0 < NHI) {
+        const u32x2 ib = *reinterpret_cast<const u32x2*>(S + off_idx(NHI) + s0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = sm.qt[limb][h][(ib[j >> 2] >> (8 * (j & 3))) & 0x7Fu];
+      }
+      bb[k2] = v;
+      if (k2 < NF) bw[k2] = *reinterpret_cast<const uint32_t*>(S + off_kboost() + 4 * (lane * NF + k2));
+      else bw[k2] = lane < 32 ? *reinterpret_cast<const uint32_t*>(S + off_kboost() + 256 * NF + 4 * lane) : 0u;
+      c0 = mfma(a_offb, v, c0);
+    }
+    floatx4 acc0 = c0, acc1 = c0;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      ksv[kb] = *reinterpret_cast<const half8*>(rec + off_kscale(NHI) + 2 * (32 * kb + 8 * w));
-      kmv[kb] = *reinterpret_cast<const half8*>(rec + off_kmin(NHI) + 2 * (32 * kb + 8 * w));
-      vsv[kb] = *reinterpret_cast<const half8*>(rec + off_vscale(NHI) + 2 * (32 * kb + 8 * w));
-      vmv[kb] = *reinterpret_cast<const half8*>(rec + off_vmin(NHI) + 2 * (32 * kb + 8 * w));
+      acc0 = mfma(unpack_codes<0>(kw[kb], ex_base), bq[kb], acc0);
+      acc1 = mfma(unpack_codes<1>(kw[kb], ex_base), bq[kb], acc1);
     }
-
-    // QK operand: limbs of q * kscale; constant part of the logits
-    half8 bq[4];
-    float cpart = 0.0f;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int k2 = 0; k2 < NB; ++k2) {
+      acc0 = mfma(unpack_codes<0>(bw[k2], ex_boost), bb[k2], acc0);
+      acc1 = mfma(unpack_codes<1>(bw[k2], ex_boost), bb[k2], acc1);
+    }
+    float s[8];
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      s[i4] = acc0[i4] + dpp<kRowRor4>(acc0[i4]) + vbias;
+      s[4 + i4] = acc1[i4] + dpp<kRowRor4>(acc1[i4]) + vbias;
+    }
+    softmax_step(st, s, sl2);  // s: probabilities of tokens tau(w, 0..7), head h
+
+    // ---- p * vscale limbs: one (head, group, 8 tokens) per lane ---------------
+    {
+      const int g = n >> 2;
+      const half8 vs = *reinterpret_cast<const half8*>(S + off_vscale(NHI) + 2 * (32 * g + 8 * w));
+      half8 hi, lo;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float prod = qv[kb * 8 + j] * h2f(ksv[kb][j]);
-        const _Float16 val = limb_of(prod, limb);
-        bq[kb][j] = val;
-        cpart += (limb == 0 ? qv[kb * 8 + j] * h2f(kmv[kb][j]) : 0.0f) - 4.0f * (float)val;
+        const _Float16 hv = (_Float16)(s[j] * (float)vs[j]);
+        hi[j] = hv;
+        lo[j] = (_Float16)__builtin_fmaf(s[j], (float)vs[j], -(float)hv);
       }
-    half8 bb_op[NB > 0 ? NB : 1];
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-      const int s0 = 32 * bb + 8 * w;
-      u32x2 ib = {0u, 0u};
-      if (s0 < NHI) ib = *reinterpret_cast<const u32x2*>(rec + off_idx(NHI) + s0);
+      *reinterpret_cast<half8*>(&sm.pt[g][0][h][w][0]) = hi;
+      *reinterpret_cast<half8*>(&sm.pt[g][1][h][w][0]) = lo;
+      // this lane's limb of p itself (hi, or p - hi): the correction columns
+      half8 pv;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        _Float16 val = (_Float16)0.0f;
-        if (s0 + j < NHI) {
-          const int ch = (int)((ib[j >> 2] >> (8 * (j & 3))) & 0x7Fu);  // channel < 128
-          const float ksc = h2f(*reinterpret_cast<const _Float16*>(rec + off_kscale(NHI) + 2 * ch));
-          const float prod = (col_ok ? qs[hl][ch] : 0.0f) * ksc * 0.25f;
-          val = limb_of(prod, limb);
-        }
-        bb_op[bb][j] = val;
-        cpart -= 4.0f * (float)val;
+        const _Float16 hv = (_Float16)s[j];
+        pv[j] = (_Float16)__builtin_fmaf(-limb_f, (float)hv, s[j]);
       }
+      *reinterpret_cast<half8*>(&sm.pl[limb][h][w][0]) = pv;
     }
+    wave_lds_sync();
 
-    floatx4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      acc0 = mfma(unpack_codes<0>(kw[kb]), bq[kb], acc0);
-      acc1 = mfma(unpack_codes<1>(kw[kb]), bq[kb], acc1);
-    }
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-      acc0 = mfma(unpack_codes<0>(bw[bb]), bb_op[bb], acc0);
-      acc1 = mfma(unpack_codes<1>(bw[bb]), bb_op[bb], acc1);
-    }
-    float c = xor_sum(cpart, 4);
-    c = xor_sum(c, 16);
-    c = xor_sum(c, 32);
-    float s[8], pr[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s[i] = (xor_sum(acc0[i], 4) + c) * sl2;
-      s[4 + i] = (xor_sum(acc1[i], 4) + c) * sl2;
-    }
-    softmax_update(st, s, pr);
-
-    // PV: operand limbs of p * vscale per value group, two 16-channel blocks each
+    // ---- PV ----------------------------------------------------------------------
+    const u32x4 vw = *reinterpret_cast<const u32x4*>(S + off_v(NHI) + 16 * lane);
+    half8 bg0 = {};
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      half8 bp;
-      float cg = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float vsc = h2f(vsv[g][j]);
-        bp[j] = col_ok ? limb_of(pr[j] * vsc, limb) : (_Float16)0.0f;
-        cg += pr[j] * (h2f(vmv[g][j]) - 4.0f * vsc);
-      }
-      st.corr[g] += cg;
-      st.o[2 * g] = mfma(unpack_codes<0>(vw[g]), bp, st.o[2 * g]);
-      st.o[2 * g + 1] = mfma(unpack_codes<1>(vw[g]), bp, st.o[2 * g + 1]);
+      // columns 0..7: p * vscale limbs of group g; 8..15: p limbs (for the correction)
+      const half8 bg = *reinterpret_cast<const half8*>(b_src + g * b_stride);
+      if (g == 0) bg0 = bg;
+      st.o[2 * g] = mfma(unpack_codes<0>(vw[g], ex_base), bg, st.o[2 * g]);
+      st.o[2 * g + 1] = mfma(unpack_codes<1>(vw[g], ex_base), bg, st.o[2 * g + 1]);
+    }
+    {
+      const uint8_t* src = S + (n < 4 ? off_vmin(NHI) : off_vscale(NHI)) + 2 * (32 * (n & 3) + 8 * w);
+      const half8 a = *reinterpret_cast<const half8*>(src) * corr_mul;
+      st.corr = mfma(a, bg0, st.corr);
+    }
+
+    // ---- refill this slot --------------------------------------------------------
+    if (i + kRing < npg) {
+      wait_lgkm0();
+      compiler_fence();
+      dma_record<NHI>(rec_of(phys_of(i + kRing)), sm.ring[slot], lane);
     }
   }
 
+  // ---- fp16 tail tokens: same contraction with fp16 K / V values -----------------
   if (do_tail) {
-    // fp16 tail tokens 32P .. seq-1: same contraction with fp16 K/V values
     const size_t toff = ((size_t)b * p.n_kv_heads + hk) * kPageTokens * kHeadDim;
     const _Float16* tk = p.tail_k + toff;
     const _Float16* tv = p.tail_v + toff;
     floatx4 acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      half8 bq;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) bq[j] = limb == 0 ? (_Float16)qv[kb * 8 + j] : (_Float16)0.0f;
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
         const int t = 16 * tb + n;
         half8 a = {};
         if (t < ntail) a = *reinterpret_cast<const half8*>(tk + (size_t)t * kHeadDim + 32 * kb + 8 * w);
-        acc[tb] = mfma(a, bq, acc[tb]);
+        acc[tb] = mfma(a, bq_plain[kb], acc[tb]);
       }
-    }
-    float s[8], pr[8];
+    float s[8];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * tb + 4 * w + i;
-        const float v = xor_sum(acc[tb][i], 4) * sl2;
-        s[4 * tb + i] = t < ntail ? v : -INFINITY;
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int t = 16 * tb + 4 * w + i4;
+        const float v = acc[tb][i4] + dpp<kRowRor4>(acc[tb][i4]);
+        s[4 * tb + i4] = t < ntail ? v : -INFINITY;
       }
-    softmax_update(st, s, pr);
+    softmax_step(st, s, sl2);
     half8 bp;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) bp[j] = col_ok ? limb_of(pr[j], limb) : (_Float16)0.0f;
+    for (int j = 0; j < 8; ++j) {
+      const _Float16 hv = (_Float16)s[j];
+      const _Float16 lv = (_Float16)(s[j] - (float)hv);
+      bp[j] = n < 8 ? (limb == 0 ? hv : lv) : (_Float16)0.0f;
+    }
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
       half8 a;
@@ -277,57 +456,109 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
     }
   }
 
-  // merge lanes: hi + lo columns, row groups; write this split's partial
-  float l = xor_sum(st.l, 16);
-  l = xor_sum(l, 32);
-  float cg[4];
+  // ---- this wave's partial (m, l, O with corrections) ----------------------------
+  float l = st.l + __shfl_xor(st.l, 16);
+  l += __shfl_xor(l, 32);
+  // correction MFMA: rows g (vmin . p) and 4 + g (offset term / 16), columns
+  // 8 + h (hi limb of p) and 12 + h (lo limb); lanes 12..15 add column n - 4.
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    cg[g] = xor_sum(st.corr[g], 16);
-    cg[g] = xor_sum(cg[g], 32);
+  for (int i4 = 0; i4 < 4; ++i4) {
+    const float v = st.corr[i4] + dpp<kRowRor4>(st.corr[i4]);
+    if (n >= 12 && w < 2) sm.red[w][n - 12][i4] = v;
   }
-  float* dst = p.partial + (((size_t)b * p.n_q_heads + hq0 + hl) * p.n_split + split) * kPartialStride;
-  const bool writer = (limb == 0) && (hl < gcount);
+  wave_lds_sync();
+  // Partials are agent-scope atomic stores (written through to the device
+  // coherence point) and the merging wave reads them with agent-scope atomic
+  // loads, so no L2 write-back / invalidate is needed anywhere.
+  float* dst = p.partial + (((size_t)b * p.n_q_heads + hq0 + h) * p.n_split + split) * kPartialStride;
+  const bool writer = n < 4 && h < gcount;
 #pragma unroll
-  for (int mb = 0; mb < 8; ++mb)
+  for (int mb = 0; mb < 8; ++mb) {
+    const int g = mb >> 1;
+    const float cg = sm.red[0][h][g] + 16.0f * sm.red[1][h][g];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float o = xor_sum(st.o[mb][i], 4) + cg[mb >> 1];
-      if (writer) dst[2 + 16 * mb + 4 * w + i] = o;
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const float o = st.o[mb][i4] + dpp<kRowRor12>(st.o[mb][i4]) + cg;  // hi column n + lo column n + 4
+      if (writer) __hip_atomic_store(dst + 2 + 16 * mb + 4 * w + i4, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+  }
   if (writer && w == 0) {
-    dst[0] = st.m;
-    dst[1] = l;
+    __hip_atomic_store(dst, st.m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(dst + 1, l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-}
 
-// grid (batch * Hq), 128 threads: log-sum-exp merge of the splits
-__global__ __launch_bounds__(128) void combine_kernel(DecodeParams p) {
-  const int bh = blockIdx.x, c = threadIdx.x;
-  const float* src = p.partial + (size_t)bh * p.n_split * kPartialStride;
-  float M = -INFINITY;
-  for (int s = 0; s < p.n_split; ++s) M = fmaxf(M, src[s * kPartialStride]);
-  float o = 0.0f;
-  if (M != -INFINITY) {
-    float L = 0.0f, acc = 0.0f;
-    for (int s = 0; s < p.n_split; ++s) {
-      const float* ps = src + s * kPartialStride;
-      const float f = exp2f(ps[0] - M);
-      L += f * ps[1];
-      acc += f * ps[2 + c];
+  // ---- the last wave of this (sequence, KV head, head group) merges -------------
+  compiler_fence();
+  wait_vmcnt<0>();  // this wave's partial stores are complete before it arrives
+  compiler_fence();
+  int* counter = p.counters + ((size_t)b * p.n_kv_heads + hk) * p.n_head_groups + hg;
+  int prev = 0;
+  if (lane == 0) prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  prev = __shfl(prev, 0);
+  if (prev != p.n_split - 1) return;
+  compiler_fence();
+  {
+    // 16 lanes per head; lane u weighs splits u, u + 16, u + 32, u + 48 and
+    // then sums channels 8u .. 8u + 7 over all splits.
+    const int hh = lane >> 4, u = lane & 15;
+    const bool hv = hh < gcount;
+    const float* base = p.partial + ((size_t)b * p.n_q_heads + hq0 + (hv ? hh : 0)) * p.n_split * kPartialStride;
+    auto ld = [](const float* a) { return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+    float ms[4], ls[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int s2 = u + 16 * k;
+      const bool ok = hv && s2 < p.n_split;
+      ms[k] = ok ? ld(base + s2 * kPartialStride) : -INFINITY;
+      ls[k] = ok ? ld(base + s2 * kPartialStride + 1) : 0.0f;
     }
-    o = acc / L;
+    float M = fmaxf(fmaxf(ms[0], ms[1]), fmaxf(ms[2], ms[3]));
+    M = row_max16(M);
+    float lsum = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float f = (M == -INFINITY || ms[k] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms[k] - M);
+      lsum += f * ls[k];
+      const int s2 = u + 16 * k;
+      if (s2 < p.n_split && hh < 4) sm.fw[hh][s2] = f;
+    }
+    lsum = row_sum16(lsum);
+    wave_lds_sync();
+    float acc8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int s0 = 0; s0 < p.n_split; s0 += 8) {
+      uint64_t v[8][4];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int s2 = s0 + k;
+        const uint64_t* src = reinterpret_cast<const uint64_t*>(base + s2 * kPartialStride + 2 + 8 * u);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[k][e] = (hv && s2 < p.n_split) ? __hip_atomic_load(src + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float f = (s0 + k < p.n_split) ? sm.fw[hh][s0 + k] : 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc8[2 * e] += f * __builtin_bit_cast(float, (uint32_t)(v[k][e] & 0xFFFFFFFFu));
+          acc8[2 * e + 1] += f * __builtin_bit_cast(float, (uint32_t)(v[k][e] >> 32));
+        }
+      }
+    }
+    if (hv) {
+      float* o = p.out + ((size_t)b * p.n_q_heads + hq0 + hh) * kHeadDim + 8 * u;
+      const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[j] = acc8[j] * inv;
+    }
   }
-  p.out[(size_t)bh * kHeadDim + c] = o;
+  if (lane == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int NHI>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
   dim3 grid(p.n_split, p.n_kv_heads * p.n_head_groups, p.batch);
-  hipLaunchKernelGGL(decode_split_kernel<NHI>, grid, dim3(64), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3(p.batch * p.n_q_heads), dim3(kHeadDim), 0, stream, p);
+  hipLaunchKernelGGL(decode_kernel<NHI>, grid, dim3(64), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -336,16 +567,18 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
 SplitPlan plan_splits(int batch, int n_kv_heads, int n_head_groups, int max_seq_len) {
   const int P = max_seq_len / kPageTokens;
   const long units = (long)batch * n_kv_heads * n_head_groups;
-  const long target = 2048;  // waves: several per CU on 256 CUs
+  const long target = 2048;  // waves: 8 per CU on 256 CUs
   long ns = (target + units - 1) / units;
   const long cap = P > 1 ? P : 1;
   if (ns > cap) ns = cap;
+  if (ns > 64) ns = 64;  // the merging wave weighs at most 64 splits
   if (ns < 1) ns = 1;
   int pps = (int)((P + ns - 1) / ns);
+  if (pps > 64) pps = 64;  // a wave keeps its page ids in one 64-lane register
   if (pps < 1) pps = 1;
   int n_split = (P + pps - 1) / pps;
   if (n_split < 1) n_split = 1;
-  return SplitPlan{n_split, pps};
+  return SplitPlan{n_split, pps};  // n_split <= 64 whenever P <= 4096 (max_seq_len checked by the ABI)
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {

@@ -108,10 +108,15 @@ struct DecodeParams {
   int32_t n_split;
   int32_t pages_per_split;
   float* partial;         // [batch][Hq][n_split][kPartialStride]
+  int* counters;          // [batch][Hkv][n_head_groups] split arrival counters, zero between calls
   float* out;             // [batch][Hq][D]
 };
 
 constexpr int kPartialStride = 132;  // m, l, O[128], 2 pad floats
+// Longest sequence decode attention accepts: 64 splits x 64 pages x 32 tokens
+// (+ a partial tail page); each wave keeps its page ids in one 64-lane register
+// and the merging wave weighs its splits with 16 lanes x 4.
+constexpr int kMaxSeqLen = 64 * 64 * 32 + 31;
 
 // Split-KV plan shared by the workspace query and the launch.
 struct SplitPlan {

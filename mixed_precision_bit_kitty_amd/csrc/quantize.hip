@@ -57,10 +57,14 @@ __device__ __forceinline__ float row_max16(float v) {
   return v;
 }
 
+// Make this wave's LDS writes visible to its later LDS reads by other lanes:
+// wait until the writes have completed (measured on gfx950: a ds_read_b128
+// issued right after a ds_write_b128 of the same wave can return stale data)
+// and keep the compiler from moving memory accesses across this point.
 __device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  asm volatile("" ::: "memory");
 }
 
 // Balanced pairwise tree over 32 values, level by level: a'_i = a_2i + a_2i+1.

@@ -48,9 +48,12 @@ def test_sizes(n_hi):
 def test_workspace_bytes_cover_partials():
     cfg = B.config(8, 32)
     nb = B.kitty_decode_workspace_bytes(cfg, 16, 32, 4096)
-    assert nb > 0 and nb % (16 * 32 * 132 * 4) == 0
-    # an empty cache still needs one split
-    assert B.kitty_decode_workspace_bytes(cfg, 1, 8, 0) == 1 * 8 * 132 * 4
+    assert nb > 16 * 32 * 132 * 4 and nb % 256 == 0
+    # an empty cache still needs one split: 8 partials + 1 counter
+    assert B.kitty_decode_workspace_bytes(cfg, 1, 8, 0) == 4352 + 256
+    # the longest supported sequence: at most 64 splits
+    big = B.kitty_decode_workspace_bytes(B.config(1, 32), 1, 4, 64 * 64 * 32 + 31)
+    assert big <= 4 * 64 * 132 * 4 + 512
 
 
 @pytest.mark.parametrize("cfg,code", [
@@ -133,6 +136,7 @@ def test_decode_arguments():
     assert _call_decode(v, hq=12) == B.KITTY_ERR_INVALID_ARG           # not a multiple of Hkv = 8
     assert _call_decode(v, hq=0) == B.KITTY_ERR_INVALID_ARG
     assert _call_decode(v, msl=-5) == B.KITTY_ERR_INVALID_ARG
+    assert _call_decode(v, msl=64 * 64 * 32 + 32) == B.KITTY_ERR_UNSUPPORTED
     assert _call_decode(v, out=None) == B.KITTY_ERR_INVALID_ARG
     assert _call_decode(v, ws=None) == B.KITTY_ERR_INVALID_ARG
     assert _call_decode(v, ws=FAKE + 64) == B.KITTY_ERR_INVALID_ARG
