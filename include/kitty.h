@@ -113,9 +113,11 @@ int kitty_append_token(const kitty_config_t* cfg, const kitty_kv_view_t* kv,
                        const uint16_t* k_new, const uint16_t* v_new, void* stream);
 
 /* Workspace bytes kitty_decode_attention needs for this shape: split-KV
- * partial results (m, l, O per query head and split) followed by one arrival
- * counter per (sequence, KV head, group of 4 query heads).  max_seq_len: an
- * upper bound on every seq_lens[b]. */
+ * partial results (m, l, O per query head, for each page split and for the
+ * tail page) followed by one arrival counter per (sequence, KV head, group of
+ * 4 query heads).  max_seq_len: an upper bound on every seq_lens[b].  The
+ * size never decreases as max_seq_len grows, so a workspace sized for the
+ * largest bound serves every call with a smaller one. */
 int kitty_decode_workspace_bytes(const kitty_config_t* cfg, int32_t batch, int32_t n_q_heads,
                                  int32_t max_seq_len, size_t* out);
 

@@ -19,7 +19,8 @@
 //    run on MFMA (constant A operands), so no VALU reduction is needed.
 //
 // One wave = one (sequence, KV head, group of <= 4 query heads, range of
-// pages).  Lane l: column n = l & 15, row group w = l >> 4.  QK^T is computed
+// pages); one more wave per (sequence, KV head, head group) attends over the
+// fp16 tail page, off the critical path of the page waves.  Lane l: column n = l & 15, row group w = l >> 4.  QK^T is computed
 // transposed (rows = 16 tokens, columns = head x limb, columns 8..15 repeat
 // 0..7), so after one DPP add every lane holds the logits of tokens
 // tau(w, 0..7) of head n & 3 -- exactly the K slice it feeds to PV.
@@ -46,6 +47,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kRing = 2;         // pages in flight per wave (LDS DMA streams at full rate with 2)
 constexpr int kRowRor4 = 0x124;  // DPP: lane i <- lane (i - 4) mod 16 of its row
 constexpr int kRowRor12 = 0x12C; // DPP: lane i <- lane (i + 4) mod 16 of its row
+constexpr int kMaxParts = 80;    // partials one merging wave weighs: 16 lanes x 5 per head
+static_assert(kMaxParts >= 64 + 1, "64 page splits plus the tail");
 
 __device__ __forceinline__ floatx4 mfma(half8 a, half8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -134,7 +137,7 @@ struct Lds {
   _Float16 pt[4][2][4][4][8];   // p * vscale limbs [group][limb][head][w][j]
   _Float16 pl[2][4][4][8];      // p limbs [limb][head][w][j]
   float red[2][4][4];           // final corrections [kind][head][group]
-  float fw[4][64];              // split weights of the merging wave [head][split]
+  float fw[4][kMaxParts];       // partial weights of the merging wave [head][partial]
 };
 
 template <int NHI>
@@ -228,19 +231,25 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
   constexpr int RB = rec_bytes(NHI);
   __shared__ __attribute__((aligned(16))) Lds<NHI> sm;
 
-  const int split = blockIdx.x;
+  const int split = blockIdx.x;             // page splits 0 .. n_split-1, then the tail wave
+  const bool tail_wave = split == p.n_split;
+  const int n_parts = p.n_split + 1;        // partial results per (sequence, KV head, head group)
   const int hk = blockIdx.y / p.n_head_groups, hg = blockIdx.y % p.n_head_groups;
   const int b = blockIdx.z;
   const int lane = threadIdx.x, n = lane & 15, w = lane >> 4, h = n & 3, limb = (n >> 2) & 1;
   const int hq0 = hk * p.group + 4 * hg;
   const int gcount = min(4, p.group - 4 * hg);
 
+  // Pages [0, Pm) of the longest allowed sequence are divided evenly over
+  // the splits (range sizes differ by at most one page).
+  const int Pm = min(p.max_seq_len / kPageTokens, p.max_pages);
+  const int p0 = (int)(((int64_t)split * Pm) / p.n_split);
+  const int p1m = (int)(((int64_t)(split + 1) * Pm) / p.n_split);
   // Independent loads first (one memory round trip before the first DMA):
   // the sequence length, this split's page ids (lane j: page p0 + j), queries.
-  const int p0 = split * p.pages_per_split;
   const size_t page_row = (size_t)b * p.max_pages;
   const int seq_raw = p.seq_lens[b];
-  const int id_raw = (lane < p.pages_per_split && p0 + lane < p.max_pages) ? p.block_table[page_row + p0 + lane] : -1;
+  const int id_raw = (!tail_wave && lane < p1m - p0) ? p.block_table[page_row + p0 + lane] : -1;
   const _Float16* qg = p.q + ((size_t)b * p.n_q_heads + hq0) * kHeadDim;
   half8 bq_plain[4];  // plain q as the B operand of the minimum term: limb-0 columns only
 #pragma unroll
@@ -257,10 +266,10 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
   const int seq = seq_raw < 0 ? 0 : (seq_raw > p.max_seq_len ? p.max_seq_len : seq_raw);
   int P = seq / kPageTokens;
   const int ntail = seq - P * kPageTokens;
-  if (P > p.max_pages) P = p.max_pages;
-  const int p1 = min(p0 + p.pages_per_split, P);
-  const int npg = p1 > p0 ? p1 - p0 : 0;
-  const bool do_tail = ntail > 0 && split == min(P / p.pages_per_split, p.n_split - 1);
+  if (P > p.max_pages) P = p.max_pages;  // now P <= Pm
+  const int p1 = min(p1m, P);
+  const int npg = (!tail_wave && p1 > p0) ? p1 - p0 : 0;
+  const bool do_tail = tail_wave && ntail > 0;
   const uint8_t* head_base = p.pages + (int64_t)hk * RB;
   const int ids = lane < npg ? id_raw : -1;  // physical page of p0 + lane (at most 64 per wave)
   auto phys_of = [&](int i) -> int { return __builtin_amdgcn_readlane(ids, i); };
@@ -417,15 +426,30 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
     const size_t toff = ((size_t)b * p.n_kv_heads + hk) * kPageTokens * kHeadDim;
     const _Float16* tk = p.tail_k + toff;
     const _Float16* tv = p.tail_v + toff;
+    // Every load is issued before the first use (one memory round trip).  All
+    // 32 slots lie inside the tail buffer; tokens >= ntail are zeroed after
+    // loading, so stale slot contents never reach the MFMAs.
+    half8 ka[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+        ka[kb][tb] = *reinterpret_cast<const half8*>(tk + (size_t)(16 * tb + n) * kHeadDim + 32 * kb + 8 * w);
+    _Float16 va[8][8];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int t = j < 4 ? 4 * w + j : 16 + 4 * w + (j - 4);
+        va[mb][j] = tv[(size_t)t * kHeadDim + 16 * mb + n];
+      }
     floatx4 acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
-        const int t = 16 * tb + n;
-        half8 a = {};
-        if (t < ntail) a = *reinterpret_cast<const half8*>(tk + (size_t)t * kHeadDim + 32 * kb + 8 * w);
-        acc[tb] = mfma(a, bq_plain[kb], acc[tb]);
+        const half8 z = {};
+        acc[tb] = mfma(16 * tb + n < ntail ? ka[kb][tb] : z, bq_plain[kb], acc[tb]);
       }
     float s[8];
 #pragma unroll
@@ -450,7 +474,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int t = j < 4 ? 4 * w + j : 16 + 4 * w + (j - 4);
-        a[j] = t < ntail ? tv[(size_t)t * kHeadDim + 16 * mb + n] : (_Float16)0.0f;
+        a[j] = t < ntail ? va[mb][j] : (_Float16)0.0f;
       }
       st.o[mb] = mfma(a, bp, st.o[mb]);
     }
@@ -470,7 +494,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
   // Partials are agent-scope atomic stores (written through to the device
   // coherence point) and the merging wave reads them with agent-scope atomic
   // loads, so no L2 write-back / invalidate is needed anywhere.
-  float* dst = p.partial + (((size_t)b * p.n_q_heads + hq0 + h) * p.n_split + split) * kPartialStride;
+  float* dst = p.partial + (((size_t)b * p.n_q_heads + hq0 + h) * n_parts + split) * kPartialStride;
   const bool writer = n < 4 && h < gcount;
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) {
@@ -495,37 +519,40 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
   int prev = 0;
   if (lane == 0) prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   prev = __shfl(prev, 0);
-  if (prev != p.n_split - 1) return;
+  if (prev != n_parts - 1) return;
   compiler_fence();
   {
-    // 16 lanes per head; lane u weighs splits u, u + 16, u + 32, u + 48 and
-    // then sums channels 8u .. 8u + 7 over all splits.
+    // 16 lanes per head; lane u weighs partials u, u + 16, ..., u + 64 and
+    // then sums channels 8u .. 8u + 7 over all partials.
+    constexpr int kPer = kMaxParts / 16;
     const int hh = lane >> 4, u = lane & 15;
     const bool hv = hh < gcount;
-    const float* base = p.partial + ((size_t)b * p.n_q_heads + hq0 + (hv ? hh : 0)) * p.n_split * kPartialStride;
+    const float* base = p.partial + ((size_t)b * p.n_q_heads + hq0 + (hv ? hh : 0)) * n_parts * kPartialStride;
     auto ld = [](const float* a) { return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-    float ms[4], ls[4];
+    float ms[kPer], ls[kPer];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < kPer; ++k) {
       const int s2 = u + 16 * k;
-      const bool ok = hv && s2 < p.n_split;
+      const bool ok = hv && s2 < n_parts;
       ms[k] = ok ? ld(base + s2 * kPartialStride) : -INFINITY;
       ls[k] = ok ? ld(base + s2 * kPartialStride + 1) : 0.0f;
     }
-    float M = fmaxf(fmaxf(ms[0], ms[1]), fmaxf(ms[2], ms[3]));
+    float M = ms[0];
+#pragma unroll
+    for (int k = 1; k < kPer; ++k) M = fmaxf(M, ms[k]);
     M = row_max16(M);
     float lsum = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < kPer; ++k) {
       const float f = (M == -INFINITY || ms[k] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms[k] - M);
       lsum += f * ls[k];
       const int s2 = u + 16 * k;
-      if (s2 < p.n_split && hh < 4) sm.fw[hh][s2] = f;
+      if (s2 < n_parts && hh < 4) sm.fw[hh][s2] = f;
     }
     lsum = row_sum16(lsum);
     wave_lds_sync();
     float acc8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int s0 = 0; s0 < p.n_split; s0 += 8) {
+    for (int s0 = 0; s0 < n_parts; s0 += 8) {
       uint64_t v[8][4];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -533,11 +560,11 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
         const uint64_t* src = reinterpret_cast<const uint64_t*>(base + s2 * kPartialStride + 2 + 8 * u);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          v[k][e] = (hv && s2 < p.n_split) ? __hip_atomic_load(src + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+          v[k][e] = (hv && s2 < n_parts) ? __hip_atomic_load(src + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
       }
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float f = (s0 + k < p.n_split) ? sm.fw[hh][s0 + k] : 0.0f;
+        const float f = (s0 + k < n_parts) ? sm.fw[hh][s0 + k] : 0.0f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           acc8[2 * e] += f * __builtin_bit_cast(float, (uint32_t)(v[k][e] & 0xFFFFFFFFu));
@@ -557,7 +584,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
 
 template <int NHI>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
-  dim3 grid(p.n_split, p.n_kv_heads * p.n_head_groups, p.batch);
+  dim3 grid(p.n_split + 1, p.n_kv_heads * p.n_head_groups, p.batch);
   hipLaunchKernelGGL(decode_kernel<NHI>, grid, dim3(64), 0, stream, p);
   return hipGetLastError();
 }
@@ -565,20 +592,17 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
 }  // namespace
 
 SplitPlan plan_splits(int batch, int n_kv_heads, int n_head_groups, int max_seq_len) {
-  const int P = max_seq_len / kPageTokens;
+  const long P = max_seq_len / kPageTokens;
   const long units = (long)batch * n_kv_heads * n_head_groups;
   const long target = 2048;  // waves: 8 per CU on 256 CUs
   long ns = (target + units - 1) / units;
-  const long cap = P > 1 ? P : 1;
-  if (ns > cap) ns = cap;
-  if (ns > 64) ns = 64;  // the merging wave weighs at most 64 splits
+  if (ns > P) ns = P;
+  if (ns > 64) ns = 64;                     // the merging wave weighs at most 64 splits
+  if (ns < (P + 63) / 64) ns = (P + 63) / 64;  // a wave keeps its page ids in one 64-lane register
   if (ns < 1) ns = 1;
-  int pps = (int)((P + ns - 1) / ns);
-  if (pps > 64) pps = 64;  // a wave keeps its page ids in one 64-lane register
-  if (pps < 1) pps = 1;
-  int n_split = (P + pps - 1) / pps;
-  if (n_split < 1) n_split = 1;
-  return SplitPlan{n_split, pps};  // n_split <= 64 whenever P <= 4096 (max_seq_len checked by the ABI)
+  // Non-decreasing in max_seq_len, so a workspace sized for a bound serves
+  // every shorter call; ns <= 64 whenever P <= 4096 (checked by the ABI).
+  return SplitPlan{(int)ns, (int)((P + ns - 1) / ns)};
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {

@@ -16,8 +16,8 @@
 //
 // Code word: 16 two-bit codes for two combos A, B of 8 elements e; element e
 // of A at bit 16*(e&1) + 2*(e>>1), of B at bit 16*(e&1) + 8 + 2*(e>>1).  With
-// this placement one shift plus one AND-OR turns a word into two fp16 values
-// 4 + code (exponent 17, code in mantissa bits 8..9) for an MFMA operand.
+// this placement a word becomes both combos' MFMA operands (eight dwords of
+// two fp16 values off + code each) with four shifts and eight AND-ORs.
 //
 // Chunk c of a 16-byte plane, u = c & 15, w = c >> 4, word x = 0..3:
 //   K base : A = (token u,      channel 32x + 8w + e), B = (token 16 + u, same channel)
@@ -105,9 +105,9 @@ struct DecodeParams {
   int32_t group;          // G = Hq / Hkv
   int32_t n_head_groups;  // ceil(G / 4)
   int32_t max_seq_len;
-  int32_t n_split;
-  int32_t pages_per_split;
-  float* partial;         // [batch][Hq][n_split][kPartialStride]
+  int32_t n_split;          // splits per (sequence, KV head, head group)
+  int32_t pages_per_split;  // largest split range (pages are divided evenly)
+  float* partial;         // [batch][Hq][n_split + 1][kPartialStride]: page splits, then the tail
   int* counters;          // [batch][Hkv][n_head_groups] split arrival counters, zero between calls
   float* out;             // [batch][Hq][D]
 };
@@ -115,7 +115,7 @@ struct DecodeParams {
 constexpr int kPartialStride = 132;  // m, l, O[128], 2 pad floats
 // Longest sequence decode attention accepts: 64 splits x 64 pages x 32 tokens
 // (+ a partial tail page); each wave keeps its page ids in one 64-lane register
-// and the merging wave weighs its splits with 16 lanes x 4.
+// and the merging wave weighs the 64 + 1 partials with 16 lanes x 5.
 constexpr int kMaxSeqLen = 64 * 64 * 32 + 31;
 
 // Split-KV plan shared by the workspace query and the launch.

@@ -49,11 +49,21 @@ def test_workspace_bytes_cover_partials():
     cfg = B.config(8, 32)
     nb = B.kitty_decode_workspace_bytes(cfg, 16, 32, 4096)
     assert nb > 16 * 32 * 132 * 4 and nb % 256 == 0
-    # an empty cache still needs one split: 8 partials + 1 counter
-    assert B.kitty_decode_workspace_bytes(cfg, 1, 8, 0) == 4352 + 256
-    # the longest supported sequence: at most 64 splits
+    # an empty cache: one page split and the tail, 8 heads x 2 partials + 1 counter
+    assert B.kitty_decode_workspace_bytes(cfg, 1, 8, 0) == 8448 + 256
+    # the longest supported sequence: at most 64 page splits + the tail
     big = B.kitty_decode_workspace_bytes(B.config(1, 32), 1, 4, 64 * 64 * 32 + 31)
-    assert big <= 4 * 64 * 132 * 4 + 512
+    assert big <= 4 * 65 * 132 * 4 + 512
+
+
+def test_workspace_bytes_monotone_in_max_seq_len():
+    cfg = B.config(8, 32)
+    for batch, hq in [(1, 8), (16, 32), (4, 96), (128, 32)]:
+        prev = 0
+        for msl in list(range(0, 6000, 37)) + [64 * 64 * 32 + 31]:
+            nb = B.kitty_decode_workspace_bytes(cfg, batch, hq, msl)
+            assert nb >= prev, (batch, hq, msl)
+            prev = nb
 
 
 @pytest.mark.parametrize("cfg,code", [
