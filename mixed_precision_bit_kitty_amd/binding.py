@@ -66,6 +66,10 @@ def load(path=None):
     path = path or os.environ.get("KITTY_LIB") or LIB_PATH
     if not os.path.exists(path):
         raise KittyError(KITTY_ERR_HIP, f"{path} is missing; run __graft_entry__.build() first")
+    try:  # torch first: its HIP runtime is then the one libkitty binds to (one runtime per process)
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     P = ctypes.POINTER
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t

@@ -47,8 +47,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kRing = 2;         // pages in flight per wave (LDS DMA streams at full rate with 2)
 constexpr int kRowRor4 = 0x124;  // DPP: lane i <- lane (i - 4) mod 16 of its row
 constexpr int kRowRor12 = 0x12C; // DPP: lane i <- lane (i + 4) mod 16 of its row
-constexpr int kMaxParts = 80;    // partials one merging wave weighs: 16 lanes x 5 per head
-static_assert(kMaxParts >= 64 + 1, "64 page splits plus the tail");
 
 __device__ __forceinline__ floatx4 mfma(half8 a, half8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -129,16 +127,21 @@ __device__ __forceinline__ half8 half8_ab(float a, float b) {
   return v;
 }
 
-// Per-wave LDS: ring of kRing records, then the limb exchange areas.
+// Per-wave LDS: ring of kRing records, then the limb exchange areas.  After
+// its page loop a wave writes its partial (m, l, O per head) over its ring.
 template <int NHI>
-struct Lds {
-  uint8_t ring[kRing][rec_bytes(NHI)];
+struct alignas(16) Lds {  // 16-byte aligned size: every wave's area keeps 16-byte alignment
+  union {
+    uint8_t ring[kRing][rec_bytes(NHI)];
+    float part[4][kPartialStride];  // [head][O[128], m, l, pad]: O 16-byte aligned
+  };
   _Float16 qt[2][4][kHeadDim];  // q * kscale limbs [limb][head][channel]
   _Float16 pt[4][2][4][4][8];   // p * vscale limbs [group][limb][head][w][j]
   _Float16 pl[2][4][4][8];      // p limbs [limb][head][w][j]
   float red[2][4][4];           // final corrections [kind][head][group]
-  float fw[4][kMaxParts];       // partial weights of the merging wave [head][partial]
+  int flag;                     // workgroup broadcast of the arrival count (wave 0's copy)
 };
+static_assert(sizeof(float) * 4 * kPartialStride <= kRing * rec_bytes(0), "partial fits over the ring");
 
 template <int NHI>
 constexpr int dma_per_page() { return rec_bytes(NHI) / 1024 + (rec_bytes(NHI) % 1024 ? 1 : 0); }
@@ -224,32 +227,40 @@ __device__ __forceinline__ void softmax_step(WaveState& st, float (&s)[8], float
   st.l += ps;
 }
 
+// A workgroup of W = wg_waves waves (at most twelve: three per SIMD, with
+// registers held to 168 per lane) works on one (sequence, KV head, head
+// group); n_wg such workgroups share it.  Each wave keeps its own LDS area.
 template <int NHI>
-__global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64 * kMaxWgWaves) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void decode_kernel(DecodeParams p) {
   constexpr int NB = (NHI + 31) / 32;  // boost slot blocks (the last may be half)
   constexpr int NF = NHI / 32;         // full boost blocks
   constexpr int RB = rec_bytes(NHI);
-  __shared__ __attribute__((aligned(16))) Lds<NHI> sm;
+  extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
+  const int wave = threadIdx.x >> 6;
+  Lds<NHI>* const all = reinterpret_cast<Lds<NHI>*>(dyn_lds);
+  Lds<NHI>& sm = all[wave];
 
-  const int split = blockIdx.x;             // page splits 0 .. n_split-1, then the tail wave
-  const bool tail_wave = split == p.n_split;
-  const int n_parts = p.n_split + 1;        // partial results per (sequence, KV head, head group)
+  const int W = p.wg_waves;
+  const int n_pw = p.n_wg * W - 1;           // page waves of this unit; the last wave takes the tail
+  const int pw = blockIdx.x * W + wave;
+  const bool tail_wave = pw == n_pw;
   const int hk = blockIdx.y / p.n_head_groups, hg = blockIdx.y % p.n_head_groups;
   const int b = blockIdx.z;
-  const int lane = threadIdx.x, n = lane & 15, w = lane >> 4, h = n & 3, limb = (n >> 2) & 1;
+  const int lane = threadIdx.x & 63, n = lane & 15, w = lane >> 4, h = n & 3, limb = (n >> 2) & 1;
   const int hq0 = hk * p.group + 4 * hg;
   const int gcount = min(4, p.group - 4 * hg);
 
   // Pages [0, Pm) of the longest allowed sequence are divided evenly over
-  // the splits (range sizes differ by at most one page).
+  // the page waves (range sizes differ by at most one page).
   const int Pm = min(p.max_seq_len / kPageTokens, p.max_pages);
-  const int p0 = (int)(((int64_t)split * Pm) / p.n_split);
-  const int p1m = (int)(((int64_t)(split + 1) * Pm) / p.n_split);
+  const int p0 = tail_wave ? 0 : (int)(((int64_t)pw * Pm) / n_pw);
+  const int p1m = tail_wave ? 0 : (int)(((int64_t)(pw + 1) * Pm) / n_pw);
   // Independent loads first (one memory round trip before the first DMA):
-  // the sequence length, this split's page ids (lane j: page p0 + j), queries.
+  // the sequence length, this wave's page ids (lane j: page p0 + j), queries.
   const size_t page_row = (size_t)b * p.max_pages;
   const int seq_raw = p.seq_lens[b];
-  const int id_raw = (!tail_wave && lane < p1m - p0) ? p.block_table[page_row + p0 + lane] : -1;
+  const int id_raw = lane < p1m - p0 ? p.block_table[page_row + p0 + lane] : -1;
   const _Float16* qg = p.q + ((size_t)b * p.n_q_heads + hq0) * kHeadDim;
   half8 bq_plain[4];  // plain q as the B operand of the minimum term: limb-0 columns only
 #pragma unroll
@@ -268,7 +279,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
   const int ntail = seq - P * kPageTokens;
   if (P > p.max_pages) P = p.max_pages;  // now P <= Pm
   const int p1 = min(p1m, P);
-  const int npg = (!tail_wave && p1 > p0) ? p1 - p0 : 0;
+  const int npg = p1 > p0 ? p1 - p0 : 0;
   const bool do_tail = tail_wave && ntail > 0;
   const uint8_t* head_base = p.pages + (int64_t)hk * RB;
   const int ids = lane < npg ? id_raw : -1;  // physical page of p0 + lane (at most 64 per wave)
@@ -480,7 +491,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
     }
   }
 
-  // ---- this wave's partial (m, l, O with corrections) ----------------------------
+  // ---- this wave's partial (m, l, O with corrections) into its LDS area --------
   float l = st.l + __shfl_xor(st.l, 16);
   l += __shfl_xor(l, 32);
   // correction MFMA: rows g (vmin . p) and 4 + g (offset term / 16), columns
@@ -491,101 +502,131 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
     if (n >= 12 && w < 2) sm.red[w][n - 12][i4] = v;
   }
   wave_lds_sync();
-  // Partials are agent-scope atomic stores (written through to the device
-  // coherence point) and the merging wave reads them with agent-scope atomic
-  // loads, so no L2 write-back / invalidate is needed anywhere.
-  float* dst = p.partial + (((size_t)b * p.n_q_heads + hq0 + h) * n_parts + split) * kPartialStride;
-  const bool writer = n < 4 && h < gcount;
+  // The DPP sums run with every lane active (a DPP read of an inactive lane
+  // returns 0); only the stores are predicated.
+  floatx4 ov[8];
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) {
     const int g = mb >> 1;
     const float cg = sm.red[0][h][g] + 16.0f * sm.red[1][h][g];
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const float o = st.o[mb][i4] + dpp<kRowRor12>(st.o[mb][i4]) + cg;  // hi column n + lo column n + 4
-      if (writer) __hip_atomic_store(dst + 2 + 16 * mb + 4 * w + i4, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i4 = 0; i4 < 4; ++i4) ov[mb][i4] = st.o[mb][i4] + dpp<kRowRor12>(st.o[mb][i4]) + cg;  // hi + lo column
+  }
+  if (n < 4) {
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) *reinterpret_cast<floatx4*>(&sm.part[h][16 * mb + 4 * w]) = ov[mb];
+    if (w == 0) {
+      sm.part[h][128] = st.m;
+      sm.part[h][129] = l;
     }
   }
-  if (writer && w == 0) {
-    __hip_atomic_store(dst, st.m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(dst + 1, l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+
+  // ---- merge the W wave partials: (head, channel) outputs t, t + 64W, ... ------
+  // Partials combine by log-sum-exp: M = max m_j, weight 2^(m_j - M).  W >= 2,
+  // so a thread has at most four of the 512 outputs.
+  const int nthr = 64 * W;
+  float* gpart = p.partial + ((size_t)b * p.n_q_heads + hq0) * p.n_wg * kPartialStride;
+  float mo[4], lo_[4], oo[4];  // this thread's merged (m, l, O)
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int o = threadIdx.x + r * nthr;
+    const int hh = (o >> 7) & 3, ch = o & 127;
+    float M = -INFINITY;
+    for (int j = 0; j < W; ++j) M = fmaxf(M, all[j].part[hh][128]);
+    float L = 0.0f, O = 0.0f;
+    for (int j = 0; j < W; ++j) {
+      const float mj = all[j].part[hh][128];
+      const float f = mj == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mj - M);
+      L += f * all[j].part[hh][129];
+      O += f * all[j].part[hh][ch];
+    }
+    mo[r] = M;
+    lo_[r] = L;
+    oo[r] = O;
+  }
+  auto out_of = [&](int o) { return p.out + ((size_t)b * p.n_q_heads + hq0 + (o >> 7)) * kHeadDim + (o & 127); };
+  if (p.n_wg == 1) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int o = threadIdx.x + r * nthr;
+      if (o < 512 && (o >> 7) < gcount) *out_of(o) = lo_[r] > 0.0f ? oo[r] / lo_[r] : 0.0f;
+    }
+    return;
   }
 
-  // ---- the last wave of this (sequence, KV head, head group) merges -------------
-  compiler_fence();
-  wait_vmcnt<0>();  // this wave's partial stores are complete before it arrives
-  compiler_fence();
-  int* counter = p.counters + ((size_t)b * p.n_kv_heads + hk) * p.n_head_groups + hg;
-  int prev = 0;
-  if (lane == 0) prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  prev = __shfl(prev, 0);
-  if (prev != n_parts - 1) return;
-  compiler_fence();
-  {
-    // 16 lanes per head; lane u weighs partials u, u + 16, ..., u + 64 and
-    // then sums channels 8u .. 8u + 7 over all partials.
-    constexpr int kPer = kMaxParts / 16;
-    const int hh = lane >> 4, u = lane & 15;
-    const bool hv = hh < gcount;
-    const float* base = p.partial + ((size_t)b * p.n_q_heads + hq0 + (hv ? hh : 0)) * n_parts * kPartialStride;
-    auto ld = [](const float* a) { return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-    float ms[kPer], ls[kPer];
+  // ---- several workgroups: publish, count arrivals, the last one merges -----------
+  // Partials are agent-scope atomic stores (written through to the device
+  // coherence point) and the merging workgroup reads them with agent-scope
+  // atomic loads, so no L2 write-back / invalidate is needed anywhere.
+  auto st_ag = [](float* a, float v) { __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  auto ld_ag = [](const float* a) { return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int s2 = u + 16 * k;
-      const bool ok = hv && s2 < n_parts;
-      ms[k] = ok ? ld(base + s2 * kPartialStride) : -INFINITY;
-      ls[k] = ok ? ld(base + s2 * kPartialStride + 1) : 0.0f;
-    }
-    float M = ms[0];
-#pragma unroll
-    for (int k = 1; k < kPer; ++k) M = fmaxf(M, ms[k]);
-    M = row_max16(M);
-    float lsum = 0.0f;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const float f = (M == -INFINITY || ms[k] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms[k] - M);
-      lsum += f * ls[k];
-      const int s2 = u + 16 * k;
-      if (s2 < n_parts && hh < 4) sm.fw[hh][s2] = f;
-    }
-    lsum = row_sum16(lsum);
-    wave_lds_sync();
-    float acc8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int s0 = 0; s0 < n_parts; s0 += 8) {
-      uint64_t v[8][4];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int s2 = s0 + k;
-        const uint64_t* src = reinterpret_cast<const uint64_t*>(base + s2 * kPartialStride + 2 + 8 * u);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          v[k][e] = (hv && s2 < n_parts) ? __hip_atomic_load(src + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+  for (int r = 0; r < 4; ++r) {
+    const int o = threadIdx.x + r * nthr;
+    if (o < 512 && (o >> 7) < gcount) {
+      float* d = gpart + ((size_t)(o >> 7) * p.n_wg + blockIdx.x) * kPartialStride;
+      st_ag(d + 2 + (o & 127), oo[r]);
+      if ((o & 127) == 0) {
+        st_ag(d, mo[r]);
+        st_ag(d + 1, lo_[r]);
       }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float f = (s0 + k < n_parts) ? sm.fw[hh][s0 + k] : 0.0f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc8[2 * e] += f * __builtin_bit_cast(float, (uint32_t)(v[k][e] & 0xFFFFFFFFu));
-          acc8[2 * e + 1] += f * __builtin_bit_cast(float, (uint32_t)(v[k][e] >> 32));
-        }
-      }
-    }
-    if (hv) {
-      float* o = p.out + ((size_t)b * p.n_q_heads + hq0 + hh) * kHeadDim + 8 * u;
-      const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) o[j] = acc8[j] * inv;
     }
   }
-  if (lane == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  compiler_fence();
+  wait_vmcnt<0>();  // this thread's partial stores are complete before the workgroup arrives
+  compiler_fence();
+  __syncthreads();
+  int* counter = p.counters + ((size_t)b * p.n_kv_heads + hk) * p.n_head_groups + hg;
+  if (threadIdx.x == 0) all[0].flag = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (all[0].flag != p.n_wg - 1) return;
+  compiler_fence();
+#pragma unroll 1
+  for (int r = 0; r < 4; ++r) {
+    const int o = threadIdx.x + r * nthr;
+    if (o < 512 && (o >> 7) < gcount) {
+      const float* src = gpart + (size_t)(o >> 7) * p.n_wg * kPartialStride;
+      float ms[kMaxWg], ls[kMaxWg], os[kMaxWg];
+#pragma unroll
+      for (int k = 0; k < kMaxWg; ++k) {  // every load issued before the first use
+        const float* sk = src + min(k, p.n_wg - 1) * kPartialStride;  // in bounds; masked below
+        ms[k] = ld_ag(sk);
+        ls[k] = ld_ag(sk + 1);
+        os[k] = ld_ag(sk + 2 + (o & 127));
+      }
+#pragma unroll
+      for (int k = 0; k < kMaxWg; ++k)
+        if (k >= p.n_wg) {
+          ms[k] = -INFINITY;
+          ls[k] = 0.0f;
+          os[k] = 0.0f;
+        }
+      float M = ms[0];
+#pragma unroll
+      for (int k = 1; k < kMaxWg; ++k) M = fmaxf(M, ms[k]);
+      float L = 0.0f, O = 0.0f;
+#pragma unroll
+      for (int k = 0; k < kMaxWg; ++k) {
+        const float f = ms[k] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms[k] - M);
+        L += f * ls[k];
+        O += f * os[k];
+      }
+      *out_of(o) = L > 0.0f ? O / L : 0.0f;
+    }
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int NHI>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
-  dim3 grid(p.n_split + 1, p.n_kv_heads * p.n_head_groups, p.batch);
-  hipLaunchKernelGGL(decode_kernel<NHI>, grid, dim3(64), 0, stream, p);
+  const size_t lds = sizeof(Lds<NHI>) * p.wg_waves;
+  static const hipError_t attr =  // once per instantiation: allow up to twelve waves' LDS
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<NHI>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)(sizeof(Lds<NHI>) * kMaxWgWaves));
+  if (attr != hipSuccess) return attr;
+  dim3 grid(p.n_wg, p.n_kv_heads * p.n_head_groups, p.batch);
+  hipLaunchKernelGGL(decode_kernel<NHI>, grid, dim3(64 * p.wg_waves), lds, stream, p);
   return hipGetLastError();
 }
 
@@ -594,15 +635,18 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
 SplitPlan plan_splits(int batch, int n_kv_heads, int n_head_groups, int max_seq_len) {
   const long P = max_seq_len / kPageTokens;
   const long units = (long)batch * n_kv_heads * n_head_groups;
-  const long target = 2048;  // waves: 8 per CU on 256 CUs
-  long ns = (target + units - 1) / units;
-  if (ns > P) ns = P;
-  if (ns > 64) ns = 64;                     // the merging wave weighs at most 64 splits
-  if (ns < (P + 63) / 64) ns = (P + 63) / 64;  // a wave keeps its page ids in one 64-lane register
-  if (ns < 1) ns = 1;
-  // Non-decreasing in max_seq_len, so a workspace sized for a bound serves
-  // every shorter call; ns <= 64 whenever P <= 4096 (checked by the ABI).
-  return SplitPlan{(int)ns, (int)((P + ns - 1) / ns)};
+  const long resident = 3 * 4 * 256;  // waves: 3 per SIMD on 256 CUs
+  long wpu = resident / units;         // waves per unit, the tail wave included
+  if (wpu > P + 1) wpu = P + 1;        // at least one page per page wave
+  if (wpu < (P + 63) / 64 + 1) wpu = (P + 63) / 64 + 1;  // page ids fit one 64-lane register
+  if (wpu < 2) wpu = 2;
+  long n_wg = (wpu + kMaxWgWaves - 1) / kMaxWgWaves;
+  if (n_wg > kMaxWg) n_wg = kMaxWg;
+  long wg_waves = (wpu + n_wg - 1) / n_wg;
+  if (wg_waves > kMaxWgWaves) wg_waves = kMaxWgWaves;
+  // Every quantity above is non-decreasing in max_seq_len, so a workspace
+  // sized for a bound serves every shorter call.
+  return SplitPlan{(int)n_wg, (int)wg_waves};
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {

@@ -152,7 +152,7 @@ static int decode_shape(const kitty_config_t* cfg, int32_t batch, int32_t n_q_he
   *n_head_groups = (G + 3) / 4;
   if ((long)cfg->n_kv_heads * *n_head_groups > 65535) return fail(KITTY_ERR_INVALID_ARG, "too many heads");
   *plan = kitty::plan_splits(batch, cfg->n_kv_heads, *n_head_groups, max_seq_len);
-  const size_t part = (size_t)batch * n_q_heads * (plan->n_split + 1) * kitty::kPartialStride * sizeof(float);
+  const size_t part = (size_t)batch * n_q_heads * plan->n_wg * kitty::kPartialStride * sizeof(float);
   const size_t cnt = (size_t)batch * cfg->n_kv_heads * *n_head_groups * sizeof(int);
   *ws = (part + 255) / 256 * 256 + (cnt + 255) / 256 * 256;
   return KITTY_OK;
@@ -201,11 +201,11 @@ int kitty_decode_attention(const kitty_config_t* cfg, const kitty_kv_view_t* kv,
   p.group = n_q_heads / cfg->n_kv_heads;
   p.n_head_groups = nhg;
   p.max_seq_len = max_seq_len;
-  p.n_split = plan.n_split;
-  p.pages_per_split = plan.pages_per_split;
+  p.n_wg = plan.n_wg;
+  p.wg_waves = plan.wg_waves;
   p.partial = static_cast<float*>(workspace);
   {
-    const size_t part = (size_t)kv->batch * n_q_heads * (plan.n_split + 1) * kitty::kPartialStride * sizeof(float);
+    const size_t part = (size_t)kv->batch * n_q_heads * plan.n_wg * kitty::kPartialStride * sizeof(float);
     p.counters = reinterpret_cast<int*>(static_cast<uint8_t*>(workspace) + (part + 255) / 256 * 256);
   }
   p.out = out;

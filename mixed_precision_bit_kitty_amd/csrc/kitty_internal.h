@@ -105,23 +105,25 @@ struct DecodeParams {
   int32_t group;          // G = Hq / Hkv
   int32_t n_head_groups;  // ceil(G / 4)
   int32_t max_seq_len;
-  int32_t n_split;          // splits per (sequence, KV head, head group)
-  int32_t pages_per_split;  // largest split range (pages are divided evenly)
-  float* partial;         // [batch][Hq][n_split + 1][kPartialStride]: page splits, then the tail
+  int32_t n_wg;            // workgroups per (sequence, KV head, head group)
+  int32_t wg_waves;        // waves per workgroup; the unit's last wave attends over the tail
+  float* partial;         // [batch][Hq][n_wg][kPartialStride] per-workgroup partials
   int* counters;          // [batch][Hkv][n_head_groups] split arrival counters, zero between calls
   float* out;             // [batch][Hq][D]
 };
 
 constexpr int kPartialStride = 132;  // m, l, O[128], 2 pad floats
-// Longest sequence decode attention accepts: 64 splits x 64 pages x 32 tokens
-// (+ a partial tail page); each wave keeps its page ids in one 64-lane register
-// and the merging wave weighs the 64 + 1 partials with 16 lanes x 5.
-constexpr int kMaxSeqLen = 64 * 64 * 32 + 31;
+constexpr int kMaxWgWaves = 12;      // waves per decode workgroup
+constexpr int kMaxWg = 16;           // decode workgroups per (sequence, KV head, head group)
+// Longest sequence decode attention accepts: 4096 pages of 32 tokens (+ a
+// partial tail page); a page wave keeps its page ids in one 64-lane register,
+// and 16 x 12 - 1 waves x 64 pages cover it.
+constexpr int kMaxSeqLen = 4096 * 32 + 31;
 
 // Split-KV plan shared by the workspace query and the launch.
 struct SplitPlan {
-  int n_split;
-  int pages_per_split;
+  int n_wg;
+  int wg_waves;
 };
 SplitPlan plan_splits(int batch, int n_kv_heads, int n_head_groups, int max_seq_len);
 

@@ -49,18 +49,18 @@ def test_workspace_bytes_cover_partials():
     cfg = B.config(8, 32)
     nb = B.kitty_decode_workspace_bytes(cfg, 16, 32, 4096)
     assert nb > 16 * 32 * 132 * 4 and nb % 256 == 0
-    # an empty cache: one page split and the tail, 8 heads x 2 partials + 1 counter
-    assert B.kitty_decode_workspace_bytes(cfg, 1, 8, 0) == 8448 + 256
-    # the longest supported sequence: at most 64 page splits + the tail
-    big = B.kitty_decode_workspace_bytes(B.config(1, 32), 1, 4, 64 * 64 * 32 + 31)
-    assert big <= 4 * 65 * 132 * 4 + 512
+    # an empty cache: one workgroup, 8 heads x 1 partial + 1 counter
+    assert B.kitty_decode_workspace_bytes(cfg, 1, 8, 0) == 4352 + 256
+    # the longest supported sequence: at most 16 workgroup partials per head
+    big = B.kitty_decode_workspace_bytes(B.config(1, 32), 1, 4, 4096 * 32 + 31)
+    assert big == 4 * 16 * 132 * 4 + 256
 
 
 def test_workspace_bytes_monotone_in_max_seq_len():
     cfg = B.config(8, 32)
     for batch, hq in [(1, 8), (16, 32), (4, 96), (128, 32)]:
         prev = 0
-        for msl in list(range(0, 6000, 37)) + [64 * 64 * 32 + 31]:
+        for msl in list(range(0, 6000, 37)) + [4096 * 32 + 31]:
             nb = B.kitty_decode_workspace_bytes(cfg, batch, hq, msl)
             assert nb >= prev, (batch, hq, msl)
             prev = nb
@@ -146,7 +146,7 @@ def test_decode_arguments():
     assert _call_decode(v, hq=12) == B.KITTY_ERR_INVALID_ARG           # not a multiple of Hkv = 8
     assert _call_decode(v, hq=0) == B.KITTY_ERR_INVALID_ARG
     assert _call_decode(v, msl=-5) == B.KITTY_ERR_INVALID_ARG
-    assert _call_decode(v, msl=64 * 64 * 32 + 32) == B.KITTY_ERR_UNSUPPORTED
+    assert _call_decode(v, msl=4096 * 32 + 32) == B.KITTY_ERR_UNSUPPORTED
     assert _call_decode(v, out=None) == B.KITTY_ERR_INVALID_ARG
     assert _call_decode(v, ws=None) == B.KITTY_ERR_INVALID_ARG
     assert _call_decode(v, ws=FAKE + 64) == B.KITTY_ERR_INVALID_ARG

@@ -152,3 +152,17 @@ def test_max_seq_len_bounds_grid():
     b = host(cache.decode_attention(dev(x["q"])))
     ref = O.decode_attention(oc, x["q"])
     assert np.abs(a - ref).max() <= ATOL and np.abs(b - ref).max() <= ATOL
+
+
+@pytest.mark.parametrize("batch,hkv,hq,ctx,lens", [
+    (2, 2, 8, 2000, [2000, 700]),      # several workgroups per (sequence, KV head), ragged lengths
+    (1, 1, 4, 4113, None),              # one long sequence: 129 pages and a tail over 11 workgroups
+    (3, 1, 6, 900, [900, 17, 416]),     # two head groups (G = 6); a sequence of only a tail
+])
+def test_multi_workgroup_merge(batch, hkv, hq, ctx, lens):
+    w = synth.LLAMA3_8B.with_(n_kv_heads=hkv, n_q_heads=hq)
+    x, cache, oc = _prefill(w, batch, ctx, 32, lens=lens)
+    err, _ = compare_decode(cache, oc, x["q"])
+    # the same cache under a loose bound (another workgroup plan) agrees too
+    err2, _ = compare_decode(cache, oc, x["q"], max_seq_len=4 * ctx)
+    print(f"multi-workgroup {batch}x{hkv}x{hq} ctx {ctx}: max abs err {err:.3g} / {err2:.3g}")
