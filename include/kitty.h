@@ -64,9 +64,10 @@ typedef struct {
  * block table maps (sequence b, logical page j) to a physical page id.
  * Record layout of one (page, head): K base plane 1024 B, K boost plane 8*n_hi
  * B, V codes 1024 B, kscale fp16[128], kmin fp16[128], vscale fp16[4][32],
- * vmin fp16[4][32], idx uint8[n_hi] -- 3072 + 9*n_hi bytes in total; the bit
- * placement inside the code planes is specified with the CPU reference
- * (page record layout) and in the design notes.  Head h's record starts at
+ * vmin fp16[4][32], idx uint8[n_hi] -- 3072 + 9*n_hi bytes in total.  The
+ * code planes are 16-byte chunks, one per lane of a 64-lane wave, each holding
+ * four 32-bit words of sixteen 2-bit codes (the chunk and bit placement is the
+ * one internal header kitty_internal.h documents).  Head h's record starts at
  * byte h * kitty_record_bytes; a physical page is kitty_page_bytes long. */
 typedef struct {
   void* pages;                /* device; n_pages * page_bytes bytes, 256-byte aligned */

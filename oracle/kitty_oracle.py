@@ -16,7 +16,7 @@ Sources, cited by name throughout:
   group_size = 32 tokens), section "Effective bit-width" (avg_bits formula),
   table "Tuning avg_bits".
 
-Arithmetic conventions (the readings are listed in the design doc):
+Arithmetic conventions (readings of points the pages leave open):
 
 * every float32 operation is a separate IEEE round-to-nearest-even op (numpy
   float32 arithmetic; no fused multiply-add, denormals kept);
