@@ -136,8 +136,8 @@ struct alignas(16) Lds {  // 16-byte aligned size: every wave's area keeps 16-by
     float part[4][kPartialStride];  // [head][O[128], m, l, pad]: O 16-byte aligned
   };
   _Float16 qt[2][4][kHeadDim];  // q * kscale limbs [limb][head][channel]
-  _Float16 pt[4][2][4][4][8];   // p * vscale limbs [group][limb][head][w][j]
-  _Float16 pl[2][4][4][8];      // p limbs [limb][head][w][j]
+  _Float16 pt[4][2][4][32];     // p * vscale limbs [group][limb][head][kappa]
+  _Float16 pl[2][4][32];        // p limbs [limb][head][kappa]
   float red[2][4][4];           // final corrections [kind][head][group]
   int flag;                     // workgroup broadcast of the arrival count (wave 0's copy)
 };
@@ -168,14 +168,6 @@ __device__ __forceinline__ void wait_page(int ahead) {
   compiler_fence();
 }
 
-// Max over the four 16-lane rows of a wave.  (v_permlane16/32_swap would avoid
-// the LDS crossbar, but on this toolchain their results were not reliable
-// here, so the exchange uses ds_bpermute through __shfl_xor.)
-__device__ __forceinline__ float row_group_max(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
-}
-
 template <int CTRL>
 __device__ __forceinline__ float dpp_row(float x) {  // helper for 16-lane row reductions
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
@@ -195,41 +187,66 @@ __device__ __forceinline__ float row_sum16(float v) {
   return v;
 }
 
+constexpr float kNegBig = -1.0e30f;  // "no token yet": finite, so exp2(-inf - m) = 0 and m - m = 0
+
 struct WaveState {
-  float m;        // running max of the scaled logits (log2 domain)
-  float l;        // this lane's share of the softmax denominator
+  float m;        // running max of the scaled logits of head w (log2 domain)
+  float l;        // this lane's share of head w's softmax denominator
   floatx4 o[8];   // PV accumulators, channel blocks of 16
   floatx4 corr;   // value-minimum / code-offset correction accumulator
 };
 
-// Online softmax over 8 raw logits s; s becomes the probabilities.
-__device__ __forceinline__ void softmax_step(WaveState& st, float (&s)[8], float sl2) {
-  float mx = s[0];
-#pragma unroll
-  for (int j = 1; j < 8; ++j) mx = fmaxf(mx, s[j]);
-  mx = row_group_max(mx);
+// Value of head (n & 3) from a per-head value held by rows (row h = head h).
+__device__ __forceinline__ float head_of_column(float v_row, int n) {
+  const float a0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v_row), 0));
+  const float a1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v_row), 16));
+  const float a2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v_row), 32));
+  const float a3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v_row), 48));
+  const int hc = n & 3;
+  return hc == 0 ? a0 : (hc == 1 ? a1 : (hc == 2 ? a2 : a3));
+}
+
+// Online softmax step for lane (n, w): raw logits s0, s1 of head w at tokens
+// n and n + 16 of the page; they become probabilities.  The max over the
+// page's 32 tokens is a 16-lane row reduction.  The PV accumulators hold
+// head n & 3 in column n, so their rescale factor is read from that head's row.
+__device__ __forceinline__ void softmax_step(WaveState& st, float& s0, float& s1, float sl2, int n) {
+  const float mx = row_max16(fmaxf(s0, s1));
   const float mnew = fmaxf(st.m, mx * sl2);
   if (__ballot(mnew > st.m)) {  // wave-uniform: rescale only when some max grew
     const float alpha = __builtin_amdgcn_exp2f(st.m - mnew);
     st.l *= alpha;
+    const float ao = head_of_column(alpha, n);
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) st.o[mb] *= alpha;
-    st.corr *= alpha;
+    for (int mb = 0; mb < 8; ++mb) st.o[mb] *= ao;
+    st.corr *= ao;
     st.m = mnew;
   }
-  const bool live = st.m != -INFINITY;
-  float ps = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    s[j] = live ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], sl2, -st.m)) : 0.0f;
-    ps += s[j];
-  }
-  st.l += ps;
+  s0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, sl2, -st.m));
+  s1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, sl2, -st.m));
+  st.l += s0 + s1;
+}
+
+// Write the p limbs (hi = f16(p), lo = f16(p - hi)) of tokens (n, n + 16) of
+// head w at kappa (2n, 2n + 1): dst[limb][w][kappa].
+__device__ __forceinline__ void store_p_limbs(_Float16 (*dst)[4][32], int w, int n, float p0, float p1) {
+  const _Float16 h0 = (_Float16)p0, h1 = (_Float16)p1;
+  half2v hi = {h0, h1};
+  half2v lo = {(_Float16)(p0 - (float)h0), (_Float16)(p1 - (float)h1)};
+  *reinterpret_cast<half2v*>(&dst[0][w][2 * n]) = hi;
+  *reinterpret_cast<half2v*>(&dst[1][w][2 * n]) = lo;
 }
 
 // A workgroup of W = wg_waves waves (at most twelve: three per SIMD, with
 // registers held to 168 per lane) works on one (sequence, KV head, head
 // group); n_wg such workgroups share it.  Each wave keeps its own LDS area.
+//
+// Lane (n = lane & 15, w = lane >> 4) roles:
+//  * QK^T has the query limbs as rows (row r = 4 head + slot, slots 0/1 = hi/lo
+//    limb, 2/3 repeat them) and the tokens as columns, so lane (n, w) ends with
+//    the logits of head w at tokens n (combo A) and n + 16 (combo B);
+//  * PV has channels as rows and (head n & 3, limb (n >> 2) & 1) as columns
+//    0..7, the p limbs for the value-minimum correction as columns 8..15.
 template <int NHI>
 __global__ __launch_bounds__(64 * kMaxWgWaves) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void decode_kernel(DecodeParams p) {
@@ -247,7 +264,9 @@ void decode_kernel(DecodeParams p) {
   const bool tail_wave = pw == n_pw;
   const int hk = blockIdx.y / p.n_head_groups, hg = blockIdx.y % p.n_head_groups;
   const int b = blockIdx.z;
-  const int lane = threadIdx.x & 63, n = lane & 15, w = lane >> 4, h = n & 3, limb = (n >> 2) & 1;
+  const int lane = threadIdx.x & 63, n = lane & 15, w = lane >> 4;
+  const int h = n & 3, limb = (n >> 2) & 1;  // PV column role
+  const int ah = n >> 2, al = n & 1;         // QK row role (A operand)
   const int hq0 = hk * p.group + 4 * hg;
   const int gcount = min(4, p.group - 4 * hg);
 
@@ -262,11 +281,11 @@ void decode_kernel(DecodeParams p) {
   const int seq_raw = p.seq_lens[b];
   const int id_raw = lane < p1m - p0 ? p.block_table[page_row + p0 + lane] : -1;
   const _Float16* qg = p.q + ((size_t)b * p.n_q_heads + hq0) * kHeadDim;
-  half8 bq_plain[4];  // plain q as the B operand of the minimum term: limb-0 columns only
+  half8 bq_plain[4];  // plain q as QK rows 4 head + 0 (the minimum term), zero elsewhere
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     half8 v = {};
-    if (limb == 0 && h < gcount) v = *reinterpret_cast<const half8*>(qg + h * kHeadDim + 32 * kb + 8 * w);
+    if ((n & 3) == 0 && ah < gcount) v = *reinterpret_cast<const half8*>(qg + ah * kHeadDim + 32 * kb + 8 * w);
     bq_plain[kb] = v;
   }
   // producer of the q * kscale limbs: head ph, channels pc .. pc + 7
@@ -296,19 +315,18 @@ void decode_kernel(DecodeParams p) {
   const uint32_t m8v = vgpr_const(0x03000300u), m6v = vgpr_const(0x00C000C0u);
   const ExpBits ex_base{vgpr_const(0x44004400u), vgpr_const(0x4C004C00u), m8v, m6v};   // 4 + c, 16 + c
   const ExpBits ex_boost{vgpr_const(0x3C003C00u), vgpr_const(0x44004400u), m8v, m6v};  // (4 + c) / 4, (16 + c) / 4
-  const half8 a_off = half8_ab(-4.0f, -16.0f);  // base code offsets per element
-  const half8 a_offb = half8_ab(-1.0f, -4.0f);  // boost code offsets (weight 1/4)
+  const half8 b_off = half8_ab(-4.0f, -16.0f);  // base code offsets per element (B operand rows = channels)
+  const half8 b_offb = half8_ab(-1.0f, -4.0f);  // boost code offsets (weight 1/4)
   // correction operand: rows 0..3 vmin (x1), rows 4..7 vscale x (-offset / 16)
   const half8 corr_mul = n < 4 ? half8_ab(1.0f, 1.0f) : (n < 8 ? half8_ab(-0.25f, -1.0f) : half8_ab(0.0f, 0.0f));
   const float sl2 = (1.0f / sqrtf((float)kHeadDim)) * kLog2e;
-  const float limb_f = (float)limb;
   // PV B operand source: lanes n < 8 read the group's p * vscale limbs, lanes
   // n >= 8 the p limbs (same address for every group)
-  const _Float16* b_src = n < 8 ? &sm.pt[0][limb][h][w][0] : &sm.pl[limb][h][w][0];
-  const int b_stride = n < 8 ? 2 * 4 * 4 * 8 : 0;
+  const _Float16* b_src = n < 8 ? &sm.pt[0][limb][h][8 * w] : &sm.pl[limb][h][8 * w];
+  const int b_stride = n < 8 ? 2 * 4 * 32 : 0;
 
   WaveState st;
-  st.m = -INFINITY;
+  st.m = kNegBig;
   st.l = 0.0f;
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) st.o[mb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -319,7 +337,7 @@ void decode_kernel(DecodeParams p) {
     const uint8_t* S = sm.ring[slot];
     wait_page<NHI>(min(kRing - 1, npg - 1 - i));
     const int phys = phys_of(i);
-    const float vbias = (phys >= 0 && (int64_t)phys < p.n_pages) ? 0.0f : -INFINITY;  // masks invalid pages
+    const bool valid = phys >= 0 && (int64_t)phys < p.n_pages;  // wave-uniform
 
     // ---- q * kscale limbs, one (head, 8 channels) per lane --------------------
     {
@@ -336,17 +354,17 @@ void decode_kernel(DecodeParams p) {
     }
     wave_lds_sync();
 
-    // ---- QK^T ----------------------------------------------------------------
+    // ---- QK^T: rows = (head, limb), columns = tokens -----------------------------
     const u32x4 kw = *reinterpret_cast<const u32x4*>(S + 16 * lane);
     half8 bq[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) bq[kb] = *reinterpret_cast<const half8*>(&sm.qt[limb][h][32 * kb + 8 * w]);
-    floatx4 c0 = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int kb = 0; kb < 4; ++kb) bq[kb] = *reinterpret_cast<const half8*>(&sm.qt[al][ah][32 * kb + 8 * w]);
+    floatx4 cmin = {0.0f, 0.0f, 0.0f, 0.0f}, coff = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const half8 kmin = *reinterpret_cast<const half8*>(S + off_kmin(NHI) + 2 * (32 * kb + 8 * w));
-      c0 = mfma(kmin, bq_plain[kb], c0);
-      c0 = mfma(a_off, bq[kb], c0);
+      cmin = mfma(bq_plain[kb], kmin, cmin);
+      coff = mfma(bq[kb], b_off, coff);
     }
     half8 bb[NB > 0 ? NB : 1];
     uint32_t bw[NB > 0 ? NB : 1];
@@ -357,54 +375,46 @@ void decode_kernel(DecodeParams p) {
       if (s0 < NHI) {
         const u32x2 ib = *reinterpret_cast<const u32x2*>(S + off_idx(NHI) + s0);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = sm.qt[limb][h][(ib[j >> 2] >> (8 * (j & 3))) & 0x7Fu];
+        for (int j = 0; j < 8; ++j) v[j] = sm.qt[al][ah][(ib[j >> 2] >> (8 * (j & 3))) & 0x7Fu];
       }
       bb[k2] = v;
       if (k2 < NF) bw[k2] = *reinterpret_cast<const uint32_t*>(S + off_kboost() + 4 * (lane * NF + k2));
       else bw[k2] = lane < 32 ? *reinterpret_cast<const uint32_t*>(S + off_kboost() + 256 * NF + 4 * lane) : 0u;
-      c0 = mfma(a_offb, v, c0);
+      coff = mfma(v, b_offb, coff);
     }
-    floatx4 acc0 = c0, acc1 = c0;
+    floatx4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      acc0 = mfma(unpack_codes<0>(kw[kb], ex_base), bq[kb], acc0);
-      acc1 = mfma(unpack_codes<1>(kw[kb], ex_base), bq[kb], acc1);
+      acc0 = mfma(bq[kb], unpack_codes<0>(kw[kb], ex_base), acc0);
+      acc1 = mfma(bq[kb], unpack_codes<1>(kw[kb], ex_base), acc1);
     }
 #pragma unroll
     for (int k2 = 0; k2 < NB; ++k2) {
-      acc0 = mfma(unpack_codes<0>(bw[k2], ex_boost), bb[k2], acc0);
-      acc1 = mfma(unpack_codes<1>(bw[k2], ex_boost), bb[k2], acc1);
+      acc0 = mfma(bb[k2], unpack_codes<0>(bw[k2], ex_boost), acc0);
+      acc1 = mfma(bb[k2], unpack_codes<1>(bw[k2], ex_boost), acc1);
     }
-    float s[8];
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      s[i4] = acc0[i4] + dpp<kRowRor4>(acc0[i4]) + vbias;
-      s[4 + i4] = acc1[i4] + dpp<kRowRor4>(acc1[i4]) + vbias;
+    // rows 4w (hi limb, with the minimum term) + 4w + 1 (lo limb) of head w
+    const float cst = cmin[0] + coff[0] + coff[1];
+    float s0 = acc0[0] + acc0[1] + cst;  // token n
+    float s1 = acc1[0] + acc1[1] + cst;  // token n + 16
+    if (!valid) {  // invalid block-table entry: the page is masked out
+      s0 = -INFINITY;
+      s1 = -INFINITY;
     }
-    softmax_step(st, s, sl2);  // s: probabilities of tokens tau(w, 0..7), head h
+    softmax_step(st, s0, s1, sl2, n);
 
-    // ---- p * vscale limbs: one (head, group, 8 tokens) per lane ---------------
-    {
-      const int g = n >> 2;
-      const half8 vs = *reinterpret_cast<const half8*>(S + off_vscale(NHI) + 2 * (32 * g + 8 * w));
-      half8 hi, lo;
+    // ---- p * vscale limbs: tokens (n, n + 16) of head w, all four groups ------
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const _Float16 hv = (_Float16)(s[j] * (float)vs[j]);
-        hi[j] = hv;
-        lo[j] = (_Float16)__builtin_fmaf(s[j], (float)vs[j], -(float)hv);
-      }
-      *reinterpret_cast<half8*>(&sm.pt[g][0][h][w][0]) = hi;
-      *reinterpret_cast<half8*>(&sm.pt[g][1][h][w][0]) = lo;
-      // this lane's limb of p itself (hi, or p - hi): the correction columns
-      half8 pv;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const _Float16 hv = (_Float16)s[j];
-        pv[j] = (_Float16)__builtin_fmaf(-limb_f, (float)hv, s[j]);
-      }
-      *reinterpret_cast<half8*>(&sm.pl[limb][h][w][0]) = pv;
+    for (int g = 0; g < 4; ++g) {
+      const half2v vs = *reinterpret_cast<const half2v*>(S + off_vscale(NHI) + 2 * (32 * g + 2 * n));
+      const _Float16 h0 = (_Float16)(s0 * (float)vs[0]), h1 = (_Float16)(s1 * (float)vs[1]);
+      half2v hi = {h0, h1};
+      half2v lo = {(_Float16)__builtin_fmaf(s0, (float)vs[0], -(float)h0),
+                   (_Float16)__builtin_fmaf(s1, (float)vs[1], -(float)h1)};
+      *reinterpret_cast<half2v*>(&sm.pt[g][0][w][2 * n]) = hi;
+      *reinterpret_cast<half2v*>(&sm.pt[g][1][w][2 * n]) = lo;
     }
+    store_p_limbs(sm.pl, w, n, s0, s1);
     wave_lds_sync();
 
     // ---- PV ----------------------------------------------------------------------
@@ -451,7 +461,7 @@ void decode_kernel(DecodeParams p) {
     for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int t = j < 4 ? 4 * w + j : 16 + 4 * w + (j - 4);
+        const int t = 4 * w + (j >> 1) + 16 * (j & 1);  // tau(w, j)
         va[mb][j] = tv[(size_t)t * kHeadDim + 16 * mb + n];
       }
     floatx4 acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
@@ -460,31 +470,21 @@ void decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
         const half8 z = {};
-        acc[tb] = mfma(16 * tb + n < ntail ? ka[kb][tb] : z, bq_plain[kb], acc[tb]);
+        acc[tb] = mfma(bq_plain[kb], 16 * tb + n < ntail ? ka[kb][tb] : z, acc[tb]);
       }
-    float s[8];
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int t = 16 * tb + 4 * w + i4;
-        const float v = acc[tb][i4] + dpp<kRowRor4>(acc[tb][i4]);
-        s[4 * tb + i4] = t < ntail ? v : -INFINITY;
-      }
-    softmax_step(st, s, sl2);
-    half8 bp;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const _Float16 hv = (_Float16)s[j];
-      const _Float16 lv = (_Float16)(s[j] - (float)hv);
-      bp[j] = n < 8 ? (limb == 0 ? hv : lv) : (_Float16)0.0f;
-    }
+    float s0 = n < ntail ? acc[0][0] : -INFINITY;
+    float s1 = 16 + n < ntail ? acc[1][0] : -INFINITY;
+    softmax_step(st, s0, s1, sl2, n);
+    store_p_limbs(sm.pl, w, n, s0, s1);
+    wave_lds_sync();
+    const half8 z = {};
+    const half8 bp = n < 8 ? *reinterpret_cast<const half8*>(&sm.pl[limb][h][8 * w]) : z;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
       half8 a;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int t = j < 4 ? 4 * w + j : 16 + 4 * w + (j - 4);
+        const int t = 4 * w + (j >> 1) + 16 * (j & 1);
         a[j] = t < ntail ? va[mb][j] : (_Float16)0.0f;
       }
       st.o[mb] = mfma(a, bp, st.o[mb]);
@@ -492,8 +492,8 @@ void decode_kernel(DecodeParams p) {
   }
 
   // ---- this wave's partial (m, l, O with corrections) into its LDS area --------
-  float l = st.l + __shfl_xor(st.l, 16);
-  l += __shfl_xor(l, 32);
+  const float l_row = row_sum16(st.l);  // head w's denominator over this wave's tokens
+  const float m_h = head_of_column(st.m, n), l_h = head_of_column(l_row, n);
   // correction MFMA: rows g (vmin . p) and 4 + g (offset term / 16), columns
   // 8 + h (hi limb of p) and 12 + h (lo limb); lanes 12..15 add column n - 4.
 #pragma unroll
@@ -516,8 +516,8 @@ void decode_kernel(DecodeParams p) {
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) *reinterpret_cast<floatx4*>(&sm.part[h][16 * mb + 4 * w]) = ov[mb];
     if (w == 0) {
-      sm.part[h][128] = st.m;
-      sm.part[h][129] = l;
+      sm.part[h][128] = m_h;
+      sm.part[h][129] = l_h;
     }
   }
   __syncthreads();

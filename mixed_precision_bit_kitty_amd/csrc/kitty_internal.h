@@ -22,9 +22,10 @@
 // Chunk c of a 16-byte plane, u = c & 15, w = c >> 4, word x = 0..3:
 //   K base : A = (token u,      channel 32x + 8w + e), B = (token 16 + u, same channel)
 //   V codes: A = (token tau(w,e), channel 32x + u),    B = (token tau(w,e), channel 32x + 16 + u)
-// tau(w, e) = 4w + e for e < 4, 16 + 4w + e - 4 otherwise: the token order in
-// which a 16x16 MFMA result of QK^T (rows = tokens) lands in the lanes that
-// feed the P operand of the PV MFMA.  Value metadata index kappa = 8w + e.
+// tau(w, e) = 4w + (e >> 1) + 16 (e & 1): value index kappa = 8w + e holds
+// token kappa / 2 for even kappa and kappa / 2 + 16 for odd kappa, so the two
+// tokens t, t + 16 that one lane holds after QK (columns = tokens) are one
+// adjacent pair in the P operand of the PV MFMA.
 // K boost: nf = n / 32 full slot blocks, word of (chunk c, block b) at byte
 // 4*(c*nf + b), slots 32b + 8w + e; if n % 32 == 16 a half block follows at
 // byte 256*nf + 4c for chunks c < 32.

@@ -112,12 +112,11 @@ __device__ __forceinline__ uint32_t pack_word(uint64_t a, uint64_t b) {
   return gather4(a) | (gather4(b) << 8) | (gather4(a >> 8) << 16) | (gather4(b >> 8) << 24);
 }
 
-// token t -> value metadata index kappa (inverse of tau)
-__host__ __device__ constexpr int kappa_of(int t) {
-  return t < 16 ? 8 * (t / 4) + (t % 4) : 8 * ((t - 16) / 4) + 4 + ((t - 16) % 4);
-}
-// (w, e) -> token
-__host__ __device__ constexpr int tau_of(int w, int e) { return e < 4 ? 4 * w + e : 16 + 4 * w + (e - 4); }
+// token t -> value metadata index kappa (inverse of tau): tokens t and
+// t + 16 (t < 16) sit at kappa 2t and 2t + 1
+__host__ __device__ constexpr int kappa_of(int t) { return 2 * (t & 15) + (t >> 4); }
+// (w, e) -> token, kappa = 8w + e
+__host__ __device__ constexpr int tau_of(int w, int e) { return 4 * w + (e >> 1) + 16 * (e & 1); }
 
 // Rows of one page: row t at base + t * 128, except that row 31 comes from
 // `last` when it is set (the token being appended).

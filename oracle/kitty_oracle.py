@@ -245,9 +245,11 @@ def page_bytes(n_kv_heads, n_hi):
 
 
 def tau(w, e):
+    """Token of value index kappa = 8w + e: kappa 2t holds token t and
+    kappa 2t + 1 token t + 16 (t < 16)."""
     w = np.asarray(w)
     e = np.asarray(e)
-    return np.where(e < 4, 4 * w + e, 16 + 4 * w + (e - 4))
+    return 4 * w + e // 2 + 16 * (e % 2)
 
 
 def _word(a8, b8):

@@ -425,11 +425,16 @@ def test_layout_positions_by_hand():
     r = _one_code_page("boost", 20, 9, 1)
     assert list(np.nonzero(r)[0]) == [1107] and r[1107] == 1
     # V codes (n_hi = 32: plane at 1280) a[token 22][channel 53] = 3: token 22 =
-    # tau(w=1, e=6) (16 + 4 + 2); channel 53 = 16*3 + 5 -> combo B of x = 1,
-    # u = 5; chunk 16 + 5 = 21; word at 1280 + 16*21 + 4 = 1620; bit 16*0 +
-    # 8 + 2*3 = 14 -> byte 1621, bits 6..7.
+    # tau(w=1, e=5) (4 + 2 + 16); channel 53 = 16*3 + 5 -> combo B of x = 1,
+    # u = 5; chunk 16 + 5 = 21; word at 1280 + 16*21 + 4 = 1620; bit 16*1 +
+    # 8 + 2*2 = 28 -> byte 1623, bits 4..5.
     r = _one_code_page("a", 22, 53, 3)
-    assert list(np.nonzero(r)[0]) == [1621] and r[1621] == 3 << 6
+    assert list(np.nonzero(r)[0]) == [1623] and r[1623] == 3 << 4
+    # a[token 7][channel 2] = 1: token 7 = tau(w=1, e=6) (4 + 3); channel 2 ->
+    # combo A of x = 0, u = 2; chunk 18; word at 1280 + 16*18 = 1568; bit
+    # 16*0 + 2*3 = 6 -> byte 1568, bits 6..7.
+    r = _one_code_page("a", 7, 2, 1)
+    assert list(np.nonzero(r)[0]) == [1568] and r[1568] == 1 << 6
 
 
 def test_layout_half_boost_block():
@@ -449,9 +454,11 @@ def test_layout_metadata_offsets():
     assert np.array_equal(r[o:o + 256].view("<f2"), kf["kscale"])
     assert np.array_equal(r[o + 256:o + 512].view("<f2"), kf["kmin"])
     vs = r[o + 512:o + 768].view("<f2").reshape(4, 32)
-    # kappa = 8w + e -> token tau(w, e); kappa 13 = (1, 5) -> token 16 + 4 + 1 = 21
-    assert vs[2, 13] == vf["vscale"][21, 2]
-    assert vs[0, 3] == vf["vscale"][3, 0]
+    # kappa = 8w + e -> token tau(w, e); kappa 13 = (1, 5) -> token 4 + 2 + 16 = 22,
+    # kappa 3 = (0, 3) -> token 1 + 16 = 17, kappa 6 = (0, 6) -> token 3
+    assert vs[2, 13] == vf["vscale"][22, 2]
+    assert vs[0, 3] == vf["vscale"][17, 0]
+    assert vs[1, 6] == vf["vscale"][3, 1]
     assert np.array_equal(r[o + 1024:o + 1056], kf["idx"])
 
 
