@@ -44,6 +44,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kQtHead = kHeadDim + 16;  // padded head row of the q * kscale limbs (halves)
 constexpr int kRing = 2;         // pages in flight per wave (LDS DMA streams at full rate with 2)
 constexpr int kRowRor4 = 0x124;  // DPP: lane i <- lane (i - 4) mod 16 of its row
 constexpr int kRowRor12 = 0x12C; // DPP: lane i <- lane (i + 4) mod 16 of its row
@@ -135,13 +136,20 @@ struct alignas(16) Lds {  // 16-byte aligned size: every wave's area keeps 16-by
     uint8_t ring[kRing][rec_bytes(NHI)];
     float part[4][kPartialStride];  // [head][O[128], m, l, pad]: O 16-byte aligned
   };
-  _Float16 qt[2][4][kHeadDim];  // q * kscale limbs [limb][head][channel]
+  // q * kscale limbs [limb].h[head][channel]; the head stride (288 B) and the
+  // limb stride (1168 B) put the eight 16-byte rows that one QK read
+  // instruction touches in distinct LDS banks
+  struct QtLimb {
+    _Float16 h[4][kQtHead];
+    _Float16 pad[8];
+  } qt[2];
   _Float16 pt[4][2][4][32];     // p * vscale limbs [group][limb][head][kappa]
   _Float16 pl[2][4][32];        // p limbs [limb][head][kappa]
   float red[2][4][4];           // final corrections [kind][head][group]
   int flag;                     // workgroup broadcast of the arrival count (wave 0's copy)
 };
 static_assert(sizeof(float) * 4 * kPartialStride <= kRing * rec_bytes(0), "partial fits over the ring");
+static_assert(sizeof(Lds<128>) * kMaxWgWaves <= 160 * 1024, "twelve waves' LDS fit one CU");
 
 template <int NHI>
 constexpr int dma_per_page() { return rec_bytes(NHI) / 1024 + (rec_bytes(NHI) % 1024 ? 1 : 0); }
@@ -208,12 +216,17 @@ __device__ __forceinline__ float head_of_column(float v_row, int n) {
 
 // Online softmax step for lane (n, w): raw logits s0, s1 of head w at tokens
 // n and n + 16 of the page; they become probabilities.  The max over the
-// page's 32 tokens is a 16-lane row reduction.  The PV accumulators hold
-// head n & 3 in column n, so their rescale factor is read from that head's row.
+// page's 32 tokens is a 16-lane row reduction.  The reference m is raised
+// only when a logit exceeds it by more than kSlack (log2 units), so after the
+// first page a rescale is rare; until then probabilities may reach 2^kSlack,
+// which the fp16 limbs of p and p * vscale carry without overflow.  The PV
+// accumulators hold head n & 3 in column n, so their rescale factor is read
+// from that head's row.
+constexpr float kSlack = 8.0f;
 __device__ __forceinline__ void softmax_step(WaveState& st, float& s0, float& s1, float sl2, int n) {
-  const float mx = row_max16(fmaxf(s0, s1));
-  const float mnew = fmaxf(st.m, mx * sl2);
-  if (__ballot(mnew > st.m)) {  // wave-uniform: rescale only when some max grew
+  const float mx = row_max16(fmaxf(s0, s1)) * sl2;
+  if (__ballot(mx > st.m + kSlack)) {  // wave-uniform
+    const float mnew = fmaxf(st.m, mx);
     const float alpha = __builtin_amdgcn_exp2f(st.m - mnew);
     st.l *= alpha;
     const float ao = head_of_column(alpha, n);
@@ -349,8 +362,8 @@ void decode_kernel(DecodeParams p) {
         hi[j] = hv;
         lo[j] = (_Float16)__builtin_fmaf((float)q_prod[j], (float)ks[j], -(float)hv);
       }
-      *reinterpret_cast<half8*>(&sm.qt[0][ph][pc]) = hi;
-      *reinterpret_cast<half8*>(&sm.qt[1][ph][pc]) = lo;
+      *reinterpret_cast<half8*>(&sm.qt[0].h[ph][pc]) = hi;
+      *reinterpret_cast<half8*>(&sm.qt[1].h[ph][pc]) = lo;
     }
     wave_lds_sync();
 
@@ -358,7 +371,7 @@ void decode_kernel(DecodeParams p) {
     const u32x4 kw = *reinterpret_cast<const u32x4*>(S + 16 * lane);
     half8 bq[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) bq[kb] = *reinterpret_cast<const half8*>(&sm.qt[al][ah][32 * kb + 8 * w]);
+    for (int kb = 0; kb < 4; ++kb) bq[kb] = *reinterpret_cast<const half8*>(&sm.qt[al].h[ah][32 * kb + 8 * w]);
     floatx4 cmin = {0.0f, 0.0f, 0.0f, 0.0f}, coff = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -375,7 +388,7 @@ void decode_kernel(DecodeParams p) {
       if (s0 < NHI) {
         const u32x2 ib = *reinterpret_cast<const u32x2*>(S + off_idx(NHI) + s0);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = sm.qt[al][ah][(ib[j >> 2] >> (8 * (j & 3))) & 0x7Fu];
+        for (int j = 0; j < 8; ++j) v[j] = sm.qt[al].h[ah][(ib[j >> 2] >> (8 * (j & 3))) & 0x7Fu];
       }
       bb[k2] = v;
       if (k2 < NF) bw[k2] = *reinterpret_cast<const uint32_t*>(S + off_kboost() + 4 * (lane * NF + k2));
@@ -522,57 +535,53 @@ void decode_kernel(DecodeParams p) {
   }
   __syncthreads();
 
-  // ---- merge the W wave partials: (head, channel) outputs t, t + 64W, ... ------
-  // Partials combine by log-sum-exp: M = max m_j, weight 2^(m_j - M).  W >= 2,
-  // so a thread has at most four of the 512 outputs.
+  // ---- merge the W wave partials ----------------------------------------------
+  // Partials combine by log-sum-exp: M = max m_j, weight f_j = 2^(m_j - M),
+  // L = sum f_j l_j, O = sum f_j O_j.  Four lanes of wave 0 form the weights
+  // per head; then each thread sums one (head, channel) over the W waves.
   const int nthr = 64 * W;
-  float* gpart = p.partial + ((size_t)b * p.n_q_heads + hq0) * p.n_wg * kPartialStride;
-  float mo[4], lo_[4], oo[4];  // this thread's merged (m, l, O)
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int o = threadIdx.x + r * nthr;
-    const int hh = (o >> 7) & 3, ch = o & 127;
-    float M = -INFINITY;
+  float* const fwt = &all[0].red[0][0][0];  // reused: f[j][head] for j < W, then M, L per head
+  if (threadIdx.x < 4) {
+    const int hh = threadIdx.x;
+    float M = kNegBig;
     for (int j = 0; j < W; ++j) M = fmaxf(M, all[j].part[hh][128]);
-    float L = 0.0f, O = 0.0f;
+    float L = 0.0f;
     for (int j = 0; j < W; ++j) {
-      const float mj = all[j].part[hh][128];
-      const float f = mj == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mj - M);
+      const float f = __builtin_amdgcn_exp2f(all[j].part[hh][128] - M);
       L += f * all[j].part[hh][129];
-      O += f * all[j].part[hh][ch];
+      all[j].part[hh][130] = f;
     }
-    mo[r] = M;
-    lo_[r] = L;
-    oo[r] = O;
+    all[0].part[hh][131] = L;  // read back below; [130] of wave 0 holds its own weight
+    fwt[hh] = M;
   }
+  __syncthreads();
   auto out_of = [&](int o) { return p.out + ((size_t)b * p.n_q_heads + hq0 + (o >> 7)) * kHeadDim + (o & 127); };
-  if (p.n_wg == 1) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int o = threadIdx.x + r * nthr;
-      if (o < 512 && (o >> 7) < gcount) *out_of(o) = lo_[r] > 0.0f ? oo[r] / lo_[r] : 0.0f;
-    }
-    return;
-  }
-
-  // ---- several workgroups: publish, count arrivals, the last one merges -----------
-  // Partials are agent-scope atomic stores (written through to the device
-  // coherence point) and the merging workgroup reads them with agent-scope
-  // atomic loads, so no L2 write-back / invalidate is needed anywhere.
+  float* gpart = p.partial + ((size_t)b * p.n_q_heads + hq0) * p.n_wg * kPartialStride;
   auto st_ag = [](float* a, float v) { __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
   auto ld_ag = [](const float* a) { return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int o = threadIdx.x + r * nthr;
-    if (o < 512 && (o >> 7) < gcount) {
-      float* d = gpart + ((size_t)(o >> 7) * p.n_wg + blockIdx.x) * kPartialStride;
-      st_ag(d + 2 + (o & 127), oo[r]);
-      if ((o & 127) == 0) {
-        st_ag(d, mo[r]);
-        st_ag(d + 1, lo_[r]);
+  for (int o = threadIdx.x; o < 4 * kHeadDim; o += nthr) {
+    const int hh = o >> 7, ch = o & 127;
+    float O = 0.0f;
+    for (int j = 0; j < W; ++j) O += all[j].part[hh][130] * all[j].part[hh][ch];
+    const float L = all[0].part[hh][131];
+    if (hh >= gcount) continue;
+    if (p.n_wg == 1) {
+      *out_of(o) = L > 0.0f ? O / L : 0.0f;
+    } else {
+      // Partials are agent-scope atomic stores (written through to the device
+      // coherence point) and the merging workgroup reads them with agent-scope
+      // atomic loads, so no L2 write-back / invalidate is needed anywhere.
+      float* d = gpart + ((size_t)hh * p.n_wg + blockIdx.x) * kPartialStride;
+      st_ag(d + 2 + ch, O);
+      if (ch == 0) {
+        st_ag(d, fwt[hh]);
+        st_ag(d + 1, L);
       }
     }
   }
+  if (p.n_wg == 1) return;
+
+  // ---- several workgroups: count arrivals, the last one merges ---------------------
   compiler_fence();
   wait_vmcnt<0>();  // this thread's partial stores are complete before the workgroup arrives
   compiler_fence();
@@ -582,38 +591,40 @@ void decode_kernel(DecodeParams p) {
   __syncthreads();
   if (all[0].flag != p.n_wg - 1) return;
   compiler_fence();
-#pragma unroll 1
-  for (int r = 0; r < 4; ++r) {
-    const int o = threadIdx.x + r * nthr;
-    if (o < 512 && (o >> 7) < gcount) {
-      const float* src = gpart + (size_t)(o >> 7) * p.n_wg * kPartialStride;
-      float ms[kMaxWg], ls[kMaxWg], os[kMaxWg];
+  for (int o = threadIdx.x; o < 4 * kHeadDim; o += nthr) {
+    const int hh = o >> 7, ch = o & 127;
+    if (hh >= gcount) continue;
+    const float* src = gpart + (size_t)hh * p.n_wg * kPartialStride;
+    float M = kNegBig, L = 0.0f, O = 0.0f;
+    for (int k0 = 0; k0 < p.n_wg; k0 += 4) {  // four partials per round trip, folded online
+      float ms[4], ls[4], os[4];
 #pragma unroll
-      for (int k = 0; k < kMaxWg; ++k) {  // every load issued before the first use
-        const float* sk = src + min(k, p.n_wg - 1) * kPartialStride;  // in bounds; masked below
+      for (int k = 0; k < 4; ++k) {  // every load issued before the first use
+        const float* sk = src + min(k0 + k, p.n_wg - 1) * kPartialStride;  // in bounds; masked below
         ms[k] = ld_ag(sk);
         ls[k] = ld_ag(sk + 1);
-        os[k] = ld_ag(sk + 2 + (o & 127));
+        os[k] = ld_ag(sk + 2 + ch);
       }
 #pragma unroll
-      for (int k = 0; k < kMaxWg; ++k)
-        if (k >= p.n_wg) {
-          ms[k] = -INFINITY;
+      for (int k = 0; k < 4; ++k)
+        if (k0 + k >= p.n_wg) {
+          ms[k] = kNegBig;
           ls[k] = 0.0f;
           os[k] = 0.0f;
         }
-      float M = ms[0];
+      const float Mn = fmaxf(fmaxf(M, fmaxf(ms[0], ms[1])), fmaxf(ms[2], ms[3]));
+      const float a = __builtin_amdgcn_exp2f(M - Mn);
+      L *= a;
+      O *= a;
 #pragma unroll
-      for (int k = 1; k < kMaxWg; ++k) M = fmaxf(M, ms[k]);
-      float L = 0.0f, O = 0.0f;
-#pragma unroll
-      for (int k = 0; k < kMaxWg; ++k) {
-        const float f = ms[k] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms[k] - M);
+      for (int k = 0; k < 4; ++k) {
+        const float f = __builtin_amdgcn_exp2f(ms[k] - Mn);
         L += f * ls[k];
         O += f * os[k];
       }
-      *out_of(o) = L > 0.0f ? O / L : 0.0f;
+      M = Mn;
     }
+    *out_of(o) = L > 0.0f ? O / L : 0.0f;
   }
   if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
