@@ -250,6 +250,18 @@ __device__ __forceinline__ void store_p_limbs(_Float16 (*dst)[4][32], int w, int
   *reinterpret_cast<half2v*>(&dst[1][w][2 * n]) = lo;
 }
 
+// Share of the pages given to wave i of a workgroup.  Wave i runs on SIMD
+// i % 4 as its (i / 4)-th resident wave, and the instruction arbiter favours
+// older waves: with equal shares the youngest class finishes last, running
+// alone at the end.  Shares 9 : 7 : 5 measured about 5% faster than equal
+// shares on the batch-16, 4096-token decode.
+__device__ __forceinline__ int page_weight(int i) { return i < 4 ? 9 : (i < 8 ? 7 : 5); }
+// sum of page_weight(j) for j < i (i <= W <= 12)
+__device__ __forceinline__ int weight_prefix(int i, int W) {
+  const int r = min(i, W);
+  return 9 * min(r, 4) + 7 * min(max(r - 4, 0), 4) + 5 * max(r - 8, 0);
+}
+
 // A workgroup of W = wg_waves waves (at most twelve: three per SIMD, with
 // registers held to 168 per lane) works on one (sequence, KV head, head
 // group); n_wg such workgroups share it.  Each wave keeps its own LDS area.
@@ -283,11 +295,13 @@ void decode_kernel(DecodeParams p) {
   const int hq0 = hk * p.group + 4 * hg;
   const int gcount = min(4, p.group - 4 * hg);
 
-  // Pages [0, Pm) of the longest allowed sequence are divided evenly over
-  // the page waves (range sizes differ by at most one page).
+  // Pages [0, Pm) of the longest allowed sequence are divided over the page
+  // waves in proportion to page_weight (the older waves of a SIMD get more).
   const int Pm = min(p.max_seq_len / kPageTokens, p.max_pages);
-  const int p0 = tail_wave ? 0 : (int)(((int64_t)pw * Pm) / n_pw);
-  const int p1m = tail_wave ? 0 : (int)(((int64_t)(pw + 1) * Pm) / n_pw);
+  const int64_t wsum = (int64_t)p.n_wg * weight_prefix(W, W) - page_weight(W - 1);
+  const int64_t c0 = (int64_t)blockIdx.x * weight_prefix(W, W) + weight_prefix(wave, W);
+  const int p0 = tail_wave ? 0 : (int)((c0 * Pm) / wsum);
+  const int p1m = tail_wave ? 0 : (int)(((c0 + page_weight(wave)) * Pm) / wsum);
   // Independent loads first (one memory round trip before the first DMA):
   // the sequence length, this wave's page ids (lane j: page p0 + j), queries.
   const size_t page_row = (size_t)b * p.max_pages;
