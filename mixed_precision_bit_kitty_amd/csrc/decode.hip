@@ -255,9 +255,9 @@ __device__ __forceinline__ void store_p_limbs(_Float16 (*dst)[4][32], int w, int
 // older waves: with equal shares the youngest class finishes last, running
 // alone at the end.  Shares 9 : 7 : 5 measured about 5% faster than equal
 // shares on the batch-16, 4096-token decode.
-__device__ __forceinline__ int page_weight(int i) { return i < 4 ? 9 : (i < 8 ? 7 : 5); }
+__host__ __device__ __forceinline__ int page_weight(int i) { return i < 4 ? 9 : (i < 8 ? 7 : 5); }
 // sum of page_weight(j) for j < i (i <= W <= 12)
-__device__ __forceinline__ int weight_prefix(int i, int W) {
+__host__ __device__ __forceinline__ int weight_prefix(int i, int W) {
   const int r = min(i, W);
   return 9 * min(r, 4) + 7 * min(max(r - 4, 0), 4) + 5 * max(r - 8, 0);
 }
@@ -657,21 +657,40 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
 
 }  // namespace
 
+// Largest page range any page wave gets under plan (n_wg, W) for Pm pages
+// (the same weighted division the kernel computes).
+static long max_range(long Pm, long n_wg, long W) {
+  const long wsum = n_wg * weight_prefix(W, W) - page_weight(W - 1);
+  long best = 0;
+  for (long pw = 0; pw < n_wg * W - 1; ++pw) {
+    const long c0 = (pw / W) * weight_prefix(W, W) + weight_prefix(pw % W, W);
+    const long r = ((c0 + page_weight(pw % W)) * Pm) / wsum - (c0 * Pm) / wsum;
+    if (r > best) best = r;
+  }
+  return best;
+}
+
 SplitPlan plan_splits(int batch, int n_kv_heads, int n_head_groups, int max_seq_len) {
   const long P = max_seq_len / kPageTokens;
   const long units = (long)batch * n_kv_heads * n_head_groups;
   const long resident = 3 * 4 * 256;  // waves: 3 per SIMD on 256 CUs
   long wpu = resident / units;         // waves per unit, the tail wave included
   if (wpu > P + 1) wpu = P + 1;        // at least one page per page wave
-  if (wpu < (P + 63) / 64 + 1) wpu = (P + 63) / 64 + 1;  // page ids fit one 64-lane register
   if (wpu < 2) wpu = 2;
-  long n_wg = (wpu + kMaxWgWaves - 1) / kMaxWgWaves;
-  if (n_wg > kMaxWg) n_wg = kMaxWg;
-  long wg_waves = (wpu + n_wg - 1) / n_wg;
-  if (wg_waves > kMaxWgWaves) wg_waves = kMaxWgWaves;
-  // Every quantity above is non-decreasing in max_seq_len, so a workspace
+  // Every quantity below is non-decreasing in max_seq_len, so a workspace
   // sized for a bound serves every shorter call.
-  return SplitPlan{(int)n_wg, (int)wg_waves};
+  for (;;) {
+    long n_wg = (wpu + kMaxWgWaves - 1) / kMaxWgWaves;
+    if (n_wg > kMaxWg) n_wg = kMaxWg;
+    long wg_waves = (wpu + n_wg - 1) / n_wg;
+    if (wg_waves > kMaxWgWaves) wg_waves = kMaxWgWaves;
+    // a page wave keeps its page ids in one 64-lane register; wpu only
+    // grows, and for every supported length (P <= 4096) it stops well
+    // before 16 x 12 waves
+    if (max_range(P, n_wg, wg_waves) <= 64 || n_wg * wg_waves >= (long)kMaxWg * kMaxWgWaves)
+      return SplitPlan{(int)n_wg, (int)wg_waves};
+    ++wpu;
+  }
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
