@@ -152,3 +152,33 @@ def test_decode_arguments():
     assert _call_decode(v, ws=FAKE + 64) == B.KITTY_ERR_INVALID_ARG
     assert _call_decode(v, nbytes=16) == B.KITTY_ERR_WORKSPACE
     assert "workspace" in B.load().kitty_last_error().decode()
+
+
+def test_decode_plan_fits_page_id_register():
+    """The decode split plan (an internal C++ function of the library) never
+    gives a page wave more than 64 pages, the width of the register that
+    holds its page ids, under the kernel's age-weighted page shares."""
+    lib = ctypes.CDLL(LIB)
+    f = lib._ZN5kitty11plan_splitsEiiii
+    f.restype = ctypes.c_uint64
+    f.argtypes = [ctypes.c_int32] * 4
+
+    def weight(i):
+        return 9 if i < 4 else (7 if i < 8 else 5)
+
+    def prefix(i, W):
+        r = min(i, W)
+        return 9 * min(r, 4) + 7 * min(max(r - 4, 0), 4) + 5 * max(r - 8, 0)
+
+    for batch in (1, 3, 16, 128, 1024):
+        for hkv, hg in ((1, 1), (8, 1), (8, 2), (32, 4)):
+            for msl in list(range(0, 4096 * 32 + 32, 4999)) + [4096 * 32 + 31, 320 * 32]:
+                r = f(batch, hkv, hg, msl)
+                n_wg, W = r & 0xFFFFFFFF, r >> 32
+                assert 1 <= n_wg <= 64 and 2 <= W <= 12
+                P = msl // 32
+                wsum = n_wg * prefix(W, W) - weight(W - 1)
+                for pw in range(n_wg * W - 1):
+                    c0 = (pw // W) * prefix(W, W) + prefix(pw % W, W)
+                    size = ((c0 + weight(pw % W)) * P) // wsum - (c0 * P) // wsum
+                    assert size <= 64, (batch, hkv, hg, msl, n_wg, W, pw, size)

@@ -1,0 +1,134 @@
+"""GPU parity at the full sizes of the four decode workloads.
+
+The whole batch runs on the GPU in the launch configuration bench.py uses
+(a tight max_seq_len bound) and at the cache capacity.  The oracle
+quantizes a seeded sample of the same input sequences on its own.  For
+every sampled sequence the test compares page records byte for byte (all
+pages, or a seeded sample of pages at the long contexts), the tails and
+lengths exactly, and decode attention within 2e-3."""
+import functools
+import numpy as np
+import pytest
+
+import oracle as O
+from mixed_precision_bit_kitty_amd import synth
+
+from _gpu_util import compare_decode, compare_records, compare_tails, dev, host, new_cache
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _oracle_seq(x, b, n_hi):
+    """The oracle's cache of sequence b of the generated batch x."""
+    return O.quantize_pages(x["k"][b:b + 1], x["v"][b:b + 1], n_hi)
+
+
+@functools.lru_cache(maxsize=1)
+def _prefill_sweep_inputs():
+    return synth.batch(synth.PREFILL_SWEEP)
+
+
+def _gpu_prefill(w, n_hi, batch=None, ctx=None, steps=0, x=None):
+    x = synth.batch(w, batch=batch, ctx=ctx, steps=steps) if x is None else x
+    B, _, S, _ = x["k"].shape
+    cache = new_cache(B, w.n_kv_heads, n_hi, S + steps + 32)
+    cache.quantize_pages(dev(x["k"]), dev(x["v"]))
+    return x, cache
+
+
+def _page_sample(oc, n, seed):
+    rng = np.random.default_rng(seed)
+    P = oc.n_pages(0)
+    pages = rng.choice(P, size=min(n, P), replace=False)
+    return [(0, int(j), int(h)) for j in pages for h in range(oc.n_kv_heads)]
+
+
+def test_llama3_8b_full_size():
+    w = synth.LLAMA3_8B
+    x, cache = _gpu_prefill(w, w.n_hi)
+    for b in sorted(np.random.default_rng(101).choice(w.batch, 2, replace=False).tolist()):
+        oc = _oracle_seq(x, b, w.n_hi)
+        n = compare_records(cache, oc, seq_map={0: b})
+        compare_tails(cache, oc, seq_map={0: b})
+        for msl in (w.ctx, w.ctx + 42, None):
+            err, _ = compare_decode(cache, oc, x["q"], max_seq_len=msl, seq_map={0: b})
+            _say(f"llama3_8b seq {b}: {n} records exact; max_seq_len {msl}: max abs err {err:.3g}")
+
+
+def test_qwen3_8b_long_context_with_appends():
+    w = synth.QWEN3_8B
+    steps = w.decode_steps
+    x, cache = _gpu_prefill(w, w.n_hi, steps=steps)
+    b = int(np.random.default_rng(102).integers(w.batch))
+    oc = _oracle_seq(x, b, w.n_hi)
+    compare_records(cache, oc, samples=_page_sample(oc, 24, 7), seq_map={0: b})
+    check = {0, 30, 31, 32, steps - 1}
+    for t in range(steps):
+        cache.append_token(dev(x["k_new"][t]), dev(x["v_new"][t]))
+        O.append_token(oc, x["k_new"][t][b:b + 1], x["v_new"][t][b:b + 1])
+        compare_tails(cache, oc, seq_map={0: b})
+        if t in check:
+            n_now = w.ctx + t + 1
+            err, _ = compare_decode(cache, oc, x["q_new"][t], max_seq_len=n_now, seq_map={0: b})
+            _say(f"qwen3_8b seq {b} step {t}: length {n_now}, max abs err {err:.3g}")
+    # the pages sealed by the appends (ctx 32768 is page aligned: 1024, 1025)
+    sealed = [(0, j, h) for j in (1024, 1025) for h in range(w.n_kv_heads)]
+    compare_records(cache, oc, samples=sealed, seq_map={0: b})
+
+
+def _decode_prefix(cache, bp, q, n_q_heads, msl):
+    """Decode attention on sequences 0..bp-1 of `cache` (a prefix view of the
+    same pool, block table, tails and lengths)."""
+    import torch
+    from mixed_precision_bit_kitty_amd import binding as B
+    v = cache.view
+    sub = B.kitty_kv_view_t(v.pages, v.n_pages, v.block_table, bp, v.max_pages, v.tail_k, v.tail_v, v.seq_lens)
+    out = torch.empty((bp, n_q_heads, 128), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(B.kitty_decode_workspace_bytes(cache.cfg, bp, n_q_heads, msl), dtype=torch.uint8,
+                     device="cuda")
+    B.kitty_decode_attention(cache.cfg, sub, dev(q[:bp]), n_q_heads, msl, out, ws)
+    return host(out)
+
+
+def test_batch_sweep_prefixes():
+    w = synth.BATCH_SWEEP
+    bmax = max(w.sweep)
+    x, cache = _gpu_prefill(w, w.n_hi, batch=bmax)
+    samples = sorted({0, 7, 15, 31, 63, 127})
+    oracle = {}
+    for b in samples:
+        oc = _oracle_seq(x, b, w.n_hi)
+        compare_records(cache, oc, samples=_page_sample(oc, 32, b), seq_map={0: b})
+        oracle[b] = O.decode_attention(oc, x["q"][b:b + 1])[0]
+    del x["k"], x["v"]
+    for bp in w.sweep:
+        out = _decode_prefix(cache, bp, x["q"], w.n_q_heads, w.ctx)
+        assert np.all(np.isfinite(out))
+        for b in samples:
+            if b < bp:
+                err = float(np.abs(out[b] - oracle[b]).max())
+                assert err <= 2e-3, (bp, b, err)
+        _say(f"batch sweep B={bp}: sampled sequences within 2e-3")
+
+
+@pytest.mark.parametrize("hf", synth.PREFILL_SWEEP.sweep)
+def test_prefill_sweep(hf):
+    w = synth.PREFILL_SWEEP.with_(hi_fraction=hf)
+    n_hi = w.n_hi
+    x, cache = _gpu_prefill(w, n_hi, x=_prefill_sweep_inputs())
+    b = int(np.random.default_rng(103).integers(w.batch))
+    oc = _oracle_seq(x, b, n_hi)
+    n = compare_records(cache, oc, samples=_page_sample(oc, 64, 5), seq_map={0: b})
+    err, _ = compare_decode(cache, oc, x["q"], max_seq_len=w.ctx, seq_map={0: b})
+    _say(f"prefill sweep hf {hf} (n_hi {n_hi}): {n} records exact, decode max abs err {err:.3g}")
