@@ -93,7 +93,8 @@ int kitty_record_bytes(const kitty_config_t* cfg, size_t* out);
 int kitty_page_bytes(const kitty_config_t* cfg, size_t* out);
 
 /* Prefill ("How it works / Prefill phase", steps 1-3, per page of 32 tokens).
- * k, v: device fp16 [batch][Hkv][S][D], contiguous.  For each sequence b with
+ * k, v: device fp16 [batch][Hkv][S][D], contiguous, 16-byte aligned.  For each
+ * sequence b with
  * length n_b = (lens ? lens[b] : S), n_b <= S: the first floor(n_b / 32)
  * pages are ranked, quantized and packed into the physical pages
  * block_table[b][0..], the remaining n_b mod 32 tokens are copied verbatim
@@ -104,7 +105,7 @@ int kitty_quantize_pages(const kitty_config_t* cfg, const kitty_kv_view_t* kv,
                          const int32_t* lens, void* stream);
 
 /* Decode-time append of one token per sequence.  k_new, v_new: device fp16
- * [batch][Hkv][D].  With n = seq_lens[b]: the token is stored in tail slot
+ * [batch][Hkv][D], 16-byte aligned.  With n = seq_lens[b]: the token is stored in tail slot
  * n mod 32 and seq_lens[b] becomes n + 1; when that slot is the 32nd, the
  * full tail is quantized exactly like a prefill page and written to physical
  * page block_table[b][n / 32] (the tail page stays fp16 until it fills).  The
@@ -114,8 +115,8 @@ int kitty_append_token(const kitty_config_t* cfg, const kitty_kv_view_t* kv,
                        const uint16_t* k_new, const uint16_t* v_new, void* stream);
 
 /* Workspace bytes kitty_decode_attention needs for this shape: split-KV
- * partial results (m, l, O per query head, for each page split and for the
- * tail page) followed by one arrival counter per (sequence, KV head, group of
+ * partial results (m, l, O per query head and decode workgroup) followed by
+ * one arrival counter per (sequence, KV head, group of
  * 4 query heads).  max_seq_len: an upper bound on every seq_lens[b].  The
  * size never decreases as max_seq_len grows, so a workspace sized for the
  * largest bound serves every call with a smaller one. */
@@ -124,7 +125,7 @@ int kitty_decode_workspace_bytes(const kitty_config_t* cfg, int32_t batch, int32
 
 /* Fused decode attention over the quantized cache (Abstract: page
  * dequantization fused into the decode kernels).  q: device fp16
- * [batch][Hq][D], Hq a multiple of Hkv; query head hq reads KV head
+ * [batch][Hq][D], 16-byte aligned, Hq a multiple of Hkv; query head hq reads KV head
  * hq / (Hq / Hkv).  For each sequence, attends over all seq_lens[b] tokens --
  * sealed pages in order, then the fp16 tail: out[b][hq] = softmax(q . k^ /
  * sqrt(D)) . v^ with k^, v^ the dequantized keys and values.  out: device

@@ -89,7 +89,7 @@ int kitty_quantize_pages(const kitty_config_t* cfg, const kitty_kv_view_t* kv, c
                          const uint16_t* v, int32_t S, const int32_t* lens, void* stream) {
   if (int r = check_config(cfg)) return r;
   if (int r = check_view(cfg, kv)) return r;
-  if (!k || !v || !aligned(k, 4) || !aligned(v, 4)) return fail(KITTY_ERR_INVALID_ARG, "k / v null or misaligned");
+  if (!k || !v || !aligned(k, 16) || !aligned(v, 16)) return fail(KITTY_ERR_INVALID_ARG, "k / v null or not 16-byte aligned");
   if (S < 0) return fail(KITTY_ERR_INVALID_ARG, "S must be >= 0");
   if (S / kitty::kPageTokens > kv->max_pages)
     return fail(KITTY_ERR_INVALID_ARG, "S / 32 = %d exceeds max_pages %d", S / kitty::kPageTokens, kv->max_pages);
@@ -119,8 +119,8 @@ int kitty_append_token(const kitty_config_t* cfg, const kitty_kv_view_t* kv, con
                        const uint16_t* v_new, void* stream) {
   if (int r = check_config(cfg)) return r;
   if (int r = check_view(cfg, kv)) return r;
-  if (!k_new || !v_new || !aligned(k_new, 4) || !aligned(v_new, 4))
-    return fail(KITTY_ERR_INVALID_ARG, "k_new / v_new null or misaligned");
+  if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16))
+    return fail(KITTY_ERR_INVALID_ARG, "k_new / v_new null or not 16-byte aligned");
   kitty::AppendParams p{};
   p.pages = static_cast<uint8_t*>(kv->pages);
   p.n_pages = kv->n_pages;
@@ -175,7 +175,7 @@ int kitty_decode_attention(const kitty_config_t* cfg, const kitty_kv_view_t* kv,
                            size_t workspace_bytes, void* stream) {
   if (int r = check_config(cfg)) return r;
   if (int r = check_view(cfg, kv)) return r;
-  if (!q || !aligned(q, 4)) return fail(KITTY_ERR_INVALID_ARG, "q null or misaligned");
+  if (!q || !aligned(q, 16)) return fail(KITTY_ERR_INVALID_ARG, "q null or not 16-byte aligned");
   if (!out || !aligned(out, 4)) return fail(KITTY_ERR_INVALID_ARG, "out null or misaligned");
   kitty::SplitPlan plan;
   int nhg;

@@ -15,10 +15,12 @@
 //  * Asymmetric min/max codes (Prefill step 3): 4-bit on boosted channels,
 //    2-bit elsewhere, fp16 step, round-half-even, clamp; split into the base
 //    plane (top 2 bits) and the boost plane (low 2 bits of boosted channels).
-//  * Values: per token, groups of 32 channels, 2-bit; the group min/max is a
-//    DPP reduction over one 16-lane row (lane owns channels c and c + 16).
-//  * Codes are staged in LDS as bytes and packed into the record's code words
-//    with coalesced 16-byte stores.
+//  * Values: per token, groups of 32 channels, 2-bit.  Each (token, group)
+//    step is formed once, by the lane that loads that group's 64 bytes
+//    (packed fp16 min/max); the steps go through LDS to the lanes that code
+//    channels c and c + 16 of every token and pack the value words.
+//  * Key codes are staged in LDS as bytes and packed into the record's code
+//    words with coalesced 16-byte stores.
 //
 // All float32 arithmetic here is separately rounded (no contraction); the
 // division is the correctly rounded one; fp32 -> fp16 conversion rounds to
@@ -31,11 +33,23 @@ namespace kitty {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// Per-wave LDS: Key base codes [32 tokens][128] (4 KB), Key boost codes
+// [32][n_hi] (<= 4 KB), value steps (1 / step, min) [4 groups][32 tokens] (1 KB).
+constexpr int kWaveLds = 9216;
 
 __device__ __forceinline__ float h2f(uint16_t bits) { return (float)__builtin_bit_cast(_Float16, bits); }
 __device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
-// fp16 input read as float32 with -0 mapped to +0
-__device__ __forceinline__ float canon16(uint16_t bits) { return h2f(bits == 0x8000u ? (uint16_t)0 : bits); }
+// two fp16 inputs with -0 mapped to +0 (x + 0 rounds -0 to +0 and leaves
+// every other value unchanged)
+__device__ __forceinline__ half2v canon2(uint32_t w) {
+  const half2v z = {(_Float16)0.0f, (_Float16)0.0f};
+  return __builtin_bit_cast(half2v, w) + z;
+}
+__device__ __forceinline__ half2v hmin2(half2v a, half2v b) { return __builtin_elementwise_min(a, b); }
+__device__ __forceinline__ half2v hmax2(half2v a, half2v b) { return __builtin_elementwise_max(a, b); }
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -93,10 +107,11 @@ __device__ __forceinline__ Step make_step(float mn, float mx, float levels) {
   return st;
 }
 
+// clamp(rne((x - mn) * inv), 0, levels); x >= mn, so the lower clamp is idle
 __device__ __forceinline__ uint32_t code_of(float x, float mn, float inv, float levels) {
   float t = (x - mn) * inv;
   t = __builtin_rintf(t);
-  t = fminf(fmaxf(t, 0.0f), levels);
+  t = fminf(t, levels);
   return (uint32_t)t;
 }
 
@@ -129,21 +144,28 @@ struct RowSrc {
 };
 
 // Quantize and pack one (page, head) into `rec`.  Called by a full wave;
-// `lds` is this wave's private 8 KB.
+// `lds` is this wave's private kWaveLds bytes.
 template <int NHI>
-__device__ void quantize_page_wave(RowSrc ks, RowSrc vs, uint8_t* __restrict__ rec, uint8_t* __restrict__ lds) {
+__device__ __forceinline__ void quantize_page_wave(RowSrc ks, RowSrc vs, uint8_t* __restrict__ rec, uint8_t* __restrict__ lds) {
   const int lane = threadIdx.x & 63;
   uint8_t* lds_base = lds;          // [32 tokens][128 channels] base codes
   uint8_t* lds_boost = lds + 4096;  // [32 tokens][NHI slots] boost codes
   wave_lds_sync();
 
   // ---------------- Key statistics: channels 2*lane, 2*lane + 1 -----------
+  // min / max on the fp16 inputs (signed zeros canonical), sums in float32.
+  // The sums need no canonical zeros: a -0 input changes neither m2 nor a code.
   float x0[32], x1[32];
+  half2v kmn, kmx;
 #pragma unroll
   for (int t = 0; t < 32; ++t) {
-    uint32_t w2 = *reinterpret_cast<const uint32_t*>(ks.row(t) + 2 * lane);
-    x0[t] = canon16((uint16_t)(w2 & 0xFFFFu));
-    x1[t] = canon16((uint16_t)(w2 >> 16));
+    const uint32_t w2 = *reinterpret_cast<const uint32_t*>(ks.row(t) + 2 * lane);
+    const half2v hv = __builtin_bit_cast(half2v, w2);
+    x0[t] = (float)hv[0];
+    x1[t] = (float)hv[1];
+    const half2v c = canon2(w2);
+    kmn = t == 0 ? c : hmin2(kmn, c);
+    kmx = t == 0 ? c : hmax2(kmx, c);
   }
   float a[32];
 #pragma unroll
@@ -158,12 +180,7 @@ __device__ void quantize_page_wave(RowSrc ks, RowSrc vs, uint8_t* __restrict__ r
 #pragma unroll
   for (int t = 0; t < 32; ++t) { float d = x1[t] - mu1; a[t] = d * d; }
   const float m2_1 = tree32(a);
-  float mn0 = x0[0], mx0 = x0[0], mn1 = x1[0], mx1 = x1[0];
-#pragma unroll
-  for (int t = 1; t < 32; ++t) {
-    mn0 = fminf(mn0, x0[t]); mx0 = fmaxf(mx0, x0[t]);
-    mn1 = fminf(mn1, x1[t]); mx1 = fmaxf(mx1, x1[t]);
-  }
+  const float mn0 = (float)kmn[0], mx0 = (float)kmx[0], mn1 = (float)kmn[1], mx1 = (float)kmx[1];
 
   // ---------------- Ranking: top NHI by m2, ties to the lower channel -------
   const uint64_t below = (1ull << lane) - 1ull;
@@ -219,33 +236,57 @@ __device__ void quantize_page_wave(RowSrc ks, RowSrc vs, uint8_t* __restrict__ r
     }
   }
 
-  // ---------------- Values: channels c0 = 32g + u and c0 + 16 --------------
+  // ---------------- Value steps: one (token, group) per lane and pass -------
+  {
+    float* vstep = reinterpret_cast<float*>(lds + 8192);  // [group][token] x (1 / step, min)
+    uint16_t* vsc = reinterpret_cast<uint16_t*>(rec + off_vscale(NHI));
+    uint16_t* vmn = reinterpret_cast<uint16_t*>(rec + off_vmin(NHI));
+    const int gp = lane & 3;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int tp = (lane >> 2) + 16 * i;
+      const u32x4* src = reinterpret_cast<const u32x4*>(vs.row(tp) + 32 * gp);
+      u32x4 c[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) c[k] = src[k];
+      half2v mnv = canon2(c[0][0]), mxv = mnv;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if (k == 0) continue;
+        const half2v h = canon2(c[k >> 2][k & 3]);
+        mnv = hmin2(mnv, h);
+        mxv = hmax2(mxv, h);
+      }
+      const float mn = fminf((float)mnv[0], (float)mnv[1]);
+      const float mx = fmaxf((float)mxv[0], (float)mxv[1]);
+      const Step st = make_step(mn, mx, 3.0f);
+      *reinterpret_cast<float2*>(vstep + 2 * (32 * gp + tp)) = make_float2(st.inv, mn);
+      const int kap = kappa_of(tp);
+      vsc[32 * gp + kap] = st.s16;
+      vmn[32 * gp + kap] = f2h(mn);
+    }
+  }
+  wave_lds_sync();
+
+  // ---------------- Value codes: channels c0 = 32g + u and c0 + 16 ----------
   {
     const int g = lane >> 4, u = lane & 15;
     const int c0 = 32 * g + u, c1 = c0 + 16;
+    const floatx4* vstep = reinterpret_cast<const floatx4*>(lds + 8192) + 16 * g;  // two tokens per read
     uint32_t a0[32], a1[32];
-    uint16_t vs_lo = 0, vs_hi = 0, vm_lo = 0, vm_hi = 0;
 #pragma unroll
-    for (int t = 0; t < 32; ++t) {
-      const _Float16* r = vs.row(t);
-      const float y0 = canon16(__builtin_bit_cast(uint16_t, r[c0]));
-      const float y1 = canon16(__builtin_bit_cast(uint16_t, r[c1]));
-      const float mn = row_min16(fminf(y0, y1));
-      const float mx = row_max16(fmaxf(y0, y1));
-      const Step st = make_step(mn, mx, 3.0f);
-      a0[t] = code_of(y0, mn, st.inv, 3.0f);
-      a1[t] = code_of(y1, mn, st.inv, 3.0f);
-      const int kap = kappa_of(t);
-      const uint16_t mnh = f2h(mn);
-      if (kap == u) { vs_lo = st.s16; vm_lo = mnh; }
-      if (kap == u + 16) { vs_hi = st.s16; vm_hi = mnh; }
+    for (int t2 = 0; t2 < 16; ++t2) {
+      const floatx4 st2 = vstep[t2];  // (1 / step, min) of tokens 2 t2 and 2 t2 + 1
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int t = 2 * t2 + k;
+        const _Float16* r = vs.row(t);
+        const float y0 = (float)r[c0];
+        const float y1 = (float)r[c1];
+        a0[t] = code_of(y0, st2[2 * k + 1], st2[2 * k], 3.0f);
+        a1[t] = code_of(y1, st2[2 * k + 1], st2[2 * k], 3.0f);
+      }
     }
-    uint16_t* vsc = reinterpret_cast<uint16_t*>(rec + off_vscale(NHI));
-    uint16_t* vmn = reinterpret_cast<uint16_t*>(rec + off_vmin(NHI));
-    vsc[32 * g + u] = vs_lo;
-    vsc[32 * g + u + 16] = vs_hi;
-    vmn[32 * g + u] = vm_lo;
-    vmn[32 * g + u + 16] = vm_hi;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       uint32_t word = 0;
@@ -292,7 +333,7 @@ __device__ void quantize_page_wave(RowSrc ks, RowSrc vs, uint8_t* __restrict__ r
 // grid (pages + 1, Hkv, batch), one wave per block
 template <int NHI>
 __global__ __launch_bounds__(64) void quantize_pages_kernel(QuantizeParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[8192];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kWaveLds];
   const int page = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
   int n = p.lens ? p.lens[b] : p.S;
   n = n < 0 ? 0 : (n > p.S ? p.S : n);
@@ -318,7 +359,7 @@ __global__ __launch_bounds__(64) void quantize_pages_kernel(QuantizeParams p) {
   }
 }
 
-// grid (batch), block = min(Hkv, 8) waves (8 KB of LDS each); each wave appends one head at a
+// grid (batch), block = min(Hkv, 8) waves (kWaveLds bytes of LDS each); each wave appends one head at a
 // time and seals it when the tail fills; the sequence length is bumped after
 // every head of the sequence is done.
 template <int NHI>
@@ -343,7 +384,7 @@ __global__ __launch_bounds__(1024) void append_token_kernel(AppendParams p) {
         if (phys >= 0 && (int64_t)phys < p.n_pages) {
           uint8_t* rec = p.pages + (int64_t)phys * p.page_bytes + (int64_t)h * rec_bytes(NHI);
           quantize_page_wave<NHI>(RowSrc{p.tail_k + tail_off, p.k_new + new_off},
-                                  RowSrc{p.tail_v + tail_off, p.v_new + new_off}, rec, lds_dyn + wave * 8192);
+                                  RowSrc{p.tail_v + tail_off, p.v_new + new_off}, rec, lds_dyn + wave * kWaveLds);
         }
       }
     }
@@ -362,7 +403,7 @@ hipError_t launch_quantize_t(const QuantizeParams& p, hipStream_t stream) {
 template <int NHI>
 hipError_t launch_append_t(const AppendParams& p, hipStream_t stream) {
   const int nw = p.n_kv_heads < 8 ? p.n_kv_heads : 8;
-  hipLaunchKernelGGL(append_token_kernel<NHI>, dim3(p.batch), dim3(64 * nw), nw * 8192, stream, p);
+  hipLaunchKernelGGL(append_token_kernel<NHI>, dim3(p.batch), dim3(64 * nw), nw * kWaveLds, stream, p);
   return hipGetLastError();
 }
 

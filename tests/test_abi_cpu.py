@@ -128,6 +128,7 @@ def test_quantize_arguments():
     v = _view()
     assert _call_quantize(v, k=None) == B.KITTY_ERR_INVALID_ARG
     assert _call_quantize(v, v=FAKE + 2) == B.KITTY_ERR_INVALID_ARG
+    assert _call_quantize(v, k=FAKE + 4) == B.KITTY_ERR_INVALID_ARG          # 16-byte alignment
     assert _call_quantize(v, S=-1) == B.KITTY_ERR_INVALID_ARG
     assert _call_quantize(v, S=96) == B.KITTY_ERR_INVALID_ARG          # 3 pages > max_pages 2
     assert _call_quantize(v, lens=FAKE + 2) == B.KITTY_ERR_INVALID_ARG
@@ -138,11 +139,13 @@ def test_append_arguments():
     v = _view()
     assert _call_append(v, k=None) == B.KITTY_ERR_INVALID_ARG
     assert _call_append(v, v=FAKE + 1) == B.KITTY_ERR_INVALID_ARG
+    assert _call_append(v, k=FAKE + 8) == B.KITTY_ERR_INVALID_ARG
 
 
 def test_decode_arguments():
     v = _view()
     assert _call_decode(v, q=None) == B.KITTY_ERR_INVALID_ARG
+    assert _call_decode(v, q=FAKE + 4) == B.KITTY_ERR_INVALID_ARG
     assert _call_decode(v, hq=12) == B.KITTY_ERR_INVALID_ARG           # not a multiple of Hkv = 8
     assert _call_decode(v, hq=0) == B.KITTY_ERR_INVALID_ARG
     assert _call_decode(v, msl=-5) == B.KITTY_ERR_INVALID_ARG
