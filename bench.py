@@ -110,6 +110,56 @@ def cpu_baseline(w, seconds):
                       f"ctx {w.ctx}, numpy oracle single-threaded, {el:.1f} s"}
 
 
+def bench_quantize(args, w):
+    """Prefill quantization of the whole batch (kitty_quantize_pages): K
+    statistics, DCPB ranking, codes, two-plane packing, V codes, tail copy.
+    Algorithmic bytes: the fp16 K and V read (512 B per token and KV head)
+    plus the records written (3072 + 9 n_hi per page and KV head).  Each
+    launch quantizes a different one of R input copies (>= 1 GiB in total),
+    so reads come from HBM."""
+    import torch
+    from mixed_precision_bit_kitty_amd import binding, synth
+
+    torch.cuda.set_device(0)
+    B = args.batch or w.batch
+    print(f"[bench] generating {w.name} batch {B} ctx {w.ctx}", file=sys.stderr, flush=True)
+    x = synth.batch(w, batch=B, steps=0)
+    k0 = torch.from_numpy(x["k"]).cuda()
+    v0 = torch.from_numpy(x["v"]).cuda()
+    del x
+    _, Hkv, S, D = k0.shape
+    in_bytes = 2 * k0.numel() * 2
+    R = max(1, math.ceil((1 << 30) / in_bytes))
+    ks = [k0] + [k0.clone() for _ in range(R - 1)]
+    vs = [v0] + [v0.clone() for _ in range(R - 1)]
+    cache = binding.KittyCache(B, Hkv, w.n_hi, S + 32)
+    rec = cache.record_bytes
+    alg = in_bytes + B * Hkv * (S // 32) * rec
+    for i in range(R):
+        cache.quantize_pages(ks[i], vs[i])
+    torch.cuda.synchronize()
+    K = args.steps
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(K):
+        cache.quantize_pages(ks[i % R], vs[i % R])
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / K
+    gbs = alg / (ms * 1e-3) / 1e9
+    print(f"[bench] quantize_pages {ms * 1e3:.2f} us ({gbs:.0f} GB/s, {gbs / HBM_PEAK_GBS:.3f} of peak), "
+          f"{R} input copies", file=sys.stderr, flush=True)
+    res = {"metric": "kitty_quantize_pages: GB/s of fp16 K/V read + page records written", "value": round(gbs, 1),
+           "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": R, "ms_per_step": round(ms, 6),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+           "config": {"workload": f"{w.name}: prefill of batch {B}, {Hkv} KV heads, {S} tokens, n_hi {w.n_hi}",
+                      "batch": B, "ctx": S, "n_kv_heads": Hkv, "n_hi": w.n_hi, "input_copies": R},
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "quantize_pages_kernel",
+                        "bytes_per_launch": int(alg), "avg_launch_us": round(ms * 1e3, 3)}}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -123,6 +173,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device copy (HBM counter calibration under rocprofv3)")
+    ap.add_argument("--quantize", action="store_true",
+                    help="time kitty_quantize_pages (prefill of the whole batch) instead of the decode step")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
@@ -133,6 +185,8 @@ def main():
     from mixed_precision_bit_kitty_amd import binding, synth
 
     w = _workload(args.workload)
+    if args.quantize:
+        return bench_quantize(args, w)
     B = args.batch or w.batch
     ctx, Hkv, Hq, n_hi = w.ctx, w.n_kv_heads, w.n_q_heads, w.n_hi
     K, W = args.steps, args.warmup

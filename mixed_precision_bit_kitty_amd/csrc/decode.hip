@@ -128,6 +128,14 @@ __device__ __forceinline__ half8 half8_ab(float a, float b) {
   return v;
 }
 
+// One limb of the q * kscale exchange: [head][channel]; the head stride
+// (288 B) and the limb stride (1168 B) put the eight 16-byte rows that one QK
+// read instruction touches in distinct LDS banks.
+struct QtLimb {
+  _Float16 h[4][kQtHead];
+  _Float16 pad[8];
+};
+
 // Per-wave LDS: ring of kRing records, then the limb exchange areas.  After
 // its page loop a wave writes its partial (m, l, O per head) over its ring.
 template <int NHI>
@@ -136,15 +144,16 @@ struct alignas(16) Lds {  // 16-byte aligned size: every wave's area keeps 16-by
     uint8_t ring[kRing][rec_bytes(NHI)];
     float part[4][kPartialStride];  // [head][O[128], m, l, pad]: O 16-byte aligned
   };
-  // q * kscale limbs [limb].h[head][channel]; the head stride (288 B) and the
-  // limb stride (1168 B) put the eight 16-byte rows that one QK read
-  // instruction touches in distinct LDS banks
-  struct QtLimb {
-    _Float16 h[4][kQtHead];
-    _Float16 pad[8];
-  } qt[2];
-  _Float16 pt[4][2][4][32];     // p * vscale limbs [group][limb][head][kappa]
-  _Float16 pl[2][4][32];        // p limbs [limb][head][kappa]
+  // The q * kscale limbs are read before the softmax and the p limbs after
+  // it, so the two exchange areas share memory (a wave's LDS accesses run
+  // in program order).
+  union {
+    QtLimb qt[2];  // q * kscale limbs [limb].h[head][channel]
+    struct {
+      _Float16 pt[4][2][4][32];  // p * vscale limbs [group][limb][head][kappa]
+      _Float16 pl[2][4][32];     // p limbs [limb][head][kappa]
+    };
+  };
   float red[2][4][4];           // final corrections [kind][head][group]
   int flag;                     // workgroup broadcast of the arrival count (wave 0's copy)
 };
