@@ -2,23 +2,24 @@
 """Decode-step benchmark of the Kitty 2-bit KV cache on one MI355X.
 
 A step is one decode step of one attention layer over the whole batch:
-``kitty_append_token`` (store the new token in the fp16 tail, sealing the
-tail into a quantized page every 32nd token: channel statistics, ranking,
-codes, two-plane packing) followed by ``kitty_decode_attention`` (fused
-dequant + QK + online softmax + PV over all pages, then the split merge).
+``kitty_decode_step``, one launch that stores the new token in the fp16
+tail (sealing the tail into a quantized page every 32nd token: channel
+statistics, ranking, codes, two-plane packing) and runs the fused decode
+attention (dequant + QK + online softmax + PV over all pages, then the
+split merge).  ``--split`` times the two separate calls instead
+(``kitty_append_token`` then ``kitty_decode_attention``).
 
 Workload (default): Llama-3-8B shape, batch 16, 32 query heads, 8 KV heads,
 head_dim 128, context 4096, hi_fraction 0.25, seeded synthetic fp16 K/V/Q.
 To keep reads coming from HBM rather than the 256 MB Infinity Cache, the
 steps rotate over L independent layer caches totalling >= 1 GiB.
 
-Steps are replayed from HIP graphs (one [append, decode] per layer, L per graph),
-so host launch overhead stays off the GPU timeline.
+Steps are replayed from HIP graphs (L steps per graph), so host launch
+overhead stays off the GPU timeline.
 
 Printed: one JSON line (metric, value = GB/s of quantized KV read per step,
 tokens/s, a roofline object for the decode kernel measured with HIP events
-over back-to-back decode launches on the launch stream, and the CPU oracle
-timed on a bounded sample).
+on the launch stream, and the CPU oracle timed on a bounded sample).
 """
 import argparse
 import hashlib
@@ -62,10 +63,11 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def committed_traffic(kernel_hash, workload):
+def committed_traffic(kernel_hash, workload, entry):
     """HBM bytes per decode launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"decode_kernel_{workload}_hbm_counters.json")
+    summary of that entry point ("step" or "attention") on this workload, if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"decode_kernel_{entry}_{workload}_hbm_counters.json")
     try:
         with open(path) as f:
             d = json.load(f)
@@ -173,6 +175,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device copy (HBM counter calibration under rocprofv3)")
+    ap.add_argument("--split", action="store_true",
+                    help="step = kitty_append_token + kitty_decode_attention (two launches) instead of the fused step")
     ap.add_argument("--quantize", action="store_true",
                     help="time kitty_quantize_pages (prefill of the whole batch) instead of the decode step")
     args = ap.parse_args()
@@ -221,14 +225,18 @@ def main():
     outs = [torch.empty((B, Hq, 128), dtype=torch.float32, device="cuda") for _ in range(L)]
     ws = [c.workspace(Hq, msl) for c in layers]
 
-    # One HIP graph per layer: [append token l, decode], and one graph of L
-    # such steps.  The host only replays graphs, so its launch overhead stays
-    # off the GPU timeline.
+    # One HIP graph per layer (one step of layer l) and one graph of L such
+    # steps.  The host only replays graphs, so its launch overhead stays off
+    # the GPU timeline.
     def step_eager(l, decode_only=False):
         c, t = layers[l], l % n_tok
-        if not decode_only:
+        if decode_only:
+            c.decode_attention(q_new[t], max_seq_len=msl, out=outs[l], workspace=ws[l])
+        elif args.split:
             c.append_token(k_new[t], v_new[t])
-        c.decode_attention(q_new[t], max_seq_len=msl, out=outs[l], workspace=ws[l])
+            c.decode_attention(q_new[t], max_seq_len=msl, out=outs[l], workspace=ws[l])
+        else:
+            c.decode_step(k_new[t], v_new[t], q_new[t], max_seq_len=msl, out=outs[l], workspace=ws[l])
 
     for l in range(L):
         step_eager(l, decode_only=True)  # first launches outside capture
@@ -239,10 +247,12 @@ def main():
         with torch.cuda.graph(g):
             step_eager(l)
         g_step.append(g)
-    g_dec = torch.cuda.CUDAGraph()  # the decode of every layer, back to back
-    with torch.cuda.graph(g_dec):
-        for l in range(L):
-            step_eager(l, decode_only=True)
+    g_dec = None
+    if args.split:  # the decode of every layer, back to back (the roofline's kernel alone)
+        g_dec = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_dec):
+            for l in range(L):
+                step_eager(l, decode_only=True)
     # L consecutive steps (one per layer, in the order the timed loop takes
     # them) in one graph, so the host replays once per L steps
     r0 = W % L
@@ -258,6 +268,8 @@ def main():
         lens[i % L] += 1
     torch.cuda.synchronize()
 
+    # Graph replays run on torch's current stream, which the events below
+    # are recorded on: they bracket exactly the launches of the timed steps.
     rec = layers[0].record_bytes
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -278,20 +290,27 @@ def main():
     avg_bytes = sum(bytes_steps) / K
     gbs = avg_bytes / (ms_step * 1e-3) / 1e9
 
-    # The decode kernel alone: R replays of one graph holding the decode of
-    # every layer back to back (R * L launches on one stream), timed with
-    # events over the whole region.
-    R = max(1, K // L)
-    dec_bytes = sum(kv_bytes([n] * B, Hkv, rec) for n in lens) / L
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(R):
-        g_dec.replay()
-    end.record()
-    torch.cuda.synchronize()
-    dec_avg_ms = start.elapsed_time(end) / (R * L)
-    dec_gbs = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
-    print(f"[bench] step {ms_step * 1e3:.2f} us ({gbs:.0f} GB/s), decode {dec_avg_ms * 1e3:.2f} us "
+    if g_dec is None:
+        # The fused step is one decode-kernel launch per step: the timed
+        # region is K launches of that kernel back to back.
+        dec_avg_ms, dec_bytes, dec_gbs = ms_step, avg_bytes, gbs
+        kernel = "decode_kernel (kitty_decode_step)"
+    else:
+        # The decode kernel alone: R replays of one graph holding the decode
+        # of every layer back to back (R * L launches on one stream), timed
+        # with events over the whole region.
+        R = max(1, K // L)
+        dec_bytes = sum(kv_bytes([n] * B, Hkv, rec) for n in lens) / L
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(R):
+            g_dec.replay()
+        end.record()
+        torch.cuda.synchronize()
+        dec_avg_ms = start.elapsed_time(end) / (R * L)
+        dec_gbs = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
+        kernel = "decode_kernel (kitty_decode_attention)"
+    print(f"[bench] step {ms_step * 1e3:.2f} us ({gbs:.0f} GB/s), decode kernel {dec_avg_ms * 1e3:.2f} us "
           f"({dec_gbs:.0f} GB/s, {dec_gbs / HBM_PEAK_GBS:.3f} of peak)", file=sys.stderr, flush=True)
 
     if args.calibrate_copy:
@@ -304,8 +323,8 @@ def main():
 
     khash = source_hash()
     roof = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": committed_traffic(khash, args.workload),
-            "kernel": "decode_kernel (kitty_decode_attention)",
+            "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": committed_traffic(khash, args.workload, "attention" if args.split else "step"),
+            "kernel": kernel,
             "bytes_per_launch": int(dec_bytes), "avg_launch_us": round(dec_avg_ms * 1e3, 3),
             "kernel_source_sha256_16": khash}
     res = {
@@ -315,7 +334,8 @@ def main():
         "tokens_per_s": round(B / (ms_step * 1e-3), 1),
         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "config": {"workload": f"{w.name}: one layer, batch {B}, {Hq} query heads, {Hkv} KV heads, head_dim 128, "
-                               f"context {ctx}+, hi_fraction {w.hi_fraction} (n_hi {n_hi}); step = append + decode "
+                               f"context {ctx}+, hi_fraction {w.hi_fraction} (n_hi {n_hi}); step = "
+                               f"{'append + decode (two launches)' if args.split else 'fused append + decode (one launch)'} "
                                f"(replayed from HIP graphs of {L} steps); {L} layer caches rotated ({L * layer_bytes / 2**30:.2f} GiB)",
                    "batch": B, "ctx": ctx, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": 128, "n_hi": n_hi,
                    "layers_rotated": L},

@@ -114,10 +114,11 @@ int kitty_quantize_pages(const kitty_config_t* cfg, const kitty_kv_view_t* kv,
 int kitty_append_token(const kitty_config_t* cfg, const kitty_kv_view_t* kv,
                        const uint16_t* k_new, const uint16_t* v_new, void* stream);
 
-/* Workspace bytes kitty_decode_attention needs for this shape: split-KV
- * partial results (m, l, O per query head and decode workgroup) followed by
- * one arrival counter per (sequence, KV head, group of
- * 4 query heads).  max_seq_len: an upper bound on every seq_lens[b].  The
+/* Workspace bytes kitty_decode_attention and kitty_decode_step need for this
+ * shape: split-KV partial results (m, l, O per query head and decode
+ * workgroup), one arrival counter per (sequence, KV head, group of 4 query
+ * heads), one per sequence, and a page record per (sequence, KV head, head
+ * group beyond the first) for the fused step's seal.  max_seq_len: an upper bound on every seq_lens[b].  The
  * size never decreases as max_seq_len grows, so a workspace sized for the
  * largest bound serves every call with a smaller one. */
 int kitty_decode_workspace_bytes(const kitty_config_t* cfg, int32_t batch, int32_t n_q_heads,
@@ -139,6 +140,24 @@ int kitty_decode_workspace_bytes(const kitty_config_t* cfg, int32_t batch, int32
 int kitty_decode_attention(const kitty_config_t* cfg, const kitty_kv_view_t* kv,
                            const uint16_t* q, int32_t n_q_heads, int32_t max_seq_len,
                            float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Fused decode step ("How it works / Decode phase" adapted to sealed pages;
+ * Abstract: decode kernels fused with dequantization): exactly
+ * kitty_append_token(k_new, v_new) followed by kitty_decode_attention(q), in
+ * one launch.  The appended token is stored in tail slot n mod 32
+ * (n = seq_lens[b] before the call); when it fills the tail page, that page
+ * is quantized like a prefill page into block_table[b][n / 32] (skipped if
+ * that entry is >= max_pages or outside the pool, as the append does) and
+ * attended as a sealed page; seq_lens[b] becomes n + 1.  k_new, v_new:
+ * device fp16 [batch][Hkv][D], 16-byte aligned.  max_seq_len bounds the
+ * length after the append.  Other arguments, the workspace (the same size
+ * and zero-fill rules) and the errors are those of kitty_decode_attention.
+ * The result equals the two separate calls' within floating-point rounding
+ * (the page sealed by this call is folded in by another wave); the records,
+ * tails and lengths it writes are identical. */
+int kitty_decode_step(const kitty_config_t* cfg, const kitty_kv_view_t* kv, const uint16_t* k_new,
+                      const uint16_t* v_new, const uint16_t* q, int32_t n_q_heads, int32_t max_seq_len,
+                      float* out, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -83,6 +83,7 @@ def load(path=None):
         "kitty_append_token": ([cfgp, viewp, vp, vp, vp], ctypes.c_int),
         "kitty_decode_workspace_bytes": ([cfgp, i32, i32, i32, P(sz)], ctypes.c_int),
         "kitty_decode_attention": ([cfgp, viewp, vp, i32, i32, vp, vp, sz, vp], ctypes.c_int),
+        "kitty_decode_step": ([cfgp, viewp, vp, vp, vp, i32, i32, vp, vp, sz, vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -162,6 +163,13 @@ def kitty_decode_attention(cfg, view, q, n_q_heads, max_seq_len, out, workspace,
                                          max_seq_len, _ptr(out), _ptr(workspace), nbytes, _stream(stream)))
 
 
+def kitty_decode_step(cfg, view, k_new, v_new, q, n_q_heads, max_seq_len, out, workspace, stream=None):
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().kitty_decode_step(ctypes.byref(cfg), ctypes.byref(view), _ptr(k_new), _ptr(v_new), _ptr(q),
+                                    n_q_heads, max_seq_len, _ptr(out), _ptr(workspace), nbytes,
+                                    _stream(stream)))
+
+
 class KittyCache:
     """Caller-side buffers of one paged cache on a CUDA device.
 
@@ -233,6 +241,21 @@ class KittyCache:
         _need(out, torch.float32, (self.batch, Hq, HEAD_DIM), "out")
         ws = self.workspace(Hq, msl) if workspace is None else workspace
         kitty_decode_attention(self.cfg, self.view, q, Hq, msl, out, ws, stream)
+        return out
+
+    def decode_step(self, k_new, v_new, q, max_seq_len=None, out=None, workspace=None, stream=None):
+        """append_token(k_new, v_new) then decode_attention(q), in one launch."""
+        import torch
+        B, Hq, D = q.shape
+        _need(k_new, torch.float16, (self.batch, self.n_kv_heads, HEAD_DIM), "k_new")
+        _need(v_new, torch.float16, (self.batch, self.n_kv_heads, HEAD_DIM), "v_new")
+        _need(q, torch.float16, (self.batch, Hq, HEAD_DIM), "q")
+        msl = self.max_pages * PAGE_TOKENS + PAGE_TOKENS - 1 if max_seq_len is None else max_seq_len
+        if out is None:
+            out = torch.empty((self.batch, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+        _need(out, torch.float32, (self.batch, Hq, HEAD_DIM), "out")
+        ws = self.workspace(Hq, msl) if workspace is None else workspace
+        kitty_decode_step(self.cfg, self.view, k_new, v_new, q, Hq, msl, out, ws, stream)
         return out
 
     # -- inspection -------------------------------------------------------

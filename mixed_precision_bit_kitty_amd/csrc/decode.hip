@@ -32,6 +32,7 @@
 // grows.  Each wave writes (m, l, O) for its page range; the last wave of a
 // (sequence, KV head, head group) merges them (log-sum-exp) into the output.
 #include "kitty_internal.h"
+#include "page_quant.h"
 
 namespace kitty {
 namespace {
@@ -164,15 +165,16 @@ template <int NHI>
 constexpr int dma_per_page() { return rec_bytes(NHI) / 1024 + (rec_bytes(NHI) % 1024 ? 1 : 0); }
 
 // Copy one record into an LDS slot: 16 bytes per lane per instruction.
-template <int NHI>
+// AUX = 16 (sc1) reads at agent scope, past this CU's vector L1.
+template <int NHI, int AUX = 0>
 __device__ __forceinline__ void dma_record(const uint8_t* __restrict__ rec, uint8_t* slot, int lane) {
   constexpr int rb = rec_bytes(NHI);
   constexpr int nfull = rb / 1024, rem = rb % 1024;
 #pragma unroll
   for (int m = 0; m < nfull; ++m)
-    __builtin_amdgcn_global_load_lds(rec + 1024 * m + 16 * lane, (lds_void*)(slot + 1024 * m), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(rec + 1024 * m + 16 * lane, (lds_void*)(slot + 1024 * m), 16, 0, AUX);
   if (rem != 0 && 16 * lane < rem)
-    __builtin_amdgcn_global_load_lds(rec + 1024 * nfull + 16 * lane, (lds_void*)(slot + 1024 * nfull), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(rec + 1024 * nfull + 16 * lane, (lds_void*)(slot + 1024 * nfull), 16, 0, AUX);
 }
 
 // Wait until the oldest in-flight page has landed; `ahead` pages were issued after it.
@@ -287,8 +289,9 @@ void decode_kernel(DecodeParams p) {
   constexpr int NB = (NHI + 31) / 32;  // boost slot blocks (the last may be half)
   constexpr int NF = NHI / 32;         // full boost blocks
   constexpr int RB = rec_bytes(NHI);
+  static_assert(sizeof(Lds<NHI>) >= pq::quant_lds_bytes(NHI), "a wave's LDS holds the page quantizer's scratch");
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   Lds<NHI>* const all = reinterpret_cast<Lds<NHI>*>(dyn_lds);
   Lds<NHI>& sm = all[wave];
 
@@ -307,10 +310,11 @@ void decode_kernel(DecodeParams p) {
   // Pages [0, Pm) of the longest allowed sequence are divided over the page
   // waves in proportion to page_weight (the older waves of a SIMD get more).
   const int Pm = min(p.max_seq_len / kPageTokens, p.max_pages);
-  const int64_t wsum = (int64_t)p.n_wg * weight_prefix(W, W) - page_weight(W - 1);
-  const int64_t c0 = (int64_t)blockIdx.x * weight_prefix(W, W) + weight_prefix(wave, W);
-  const int p0 = tail_wave ? 0 : (int)((c0 * Pm) / wsum);
-  const int p1m = tail_wave ? 0 : (int)(((c0 + page_weight(wave)) * Pm) / wsum);
+  // (32-bit products: c0 + 9 <= 16 x 84 + 9 and Pm <= 4096)
+  const int wsum = p.n_wg * weight_prefix(W, W) - page_weight(W - 1);
+  const int c0 = (int)blockIdx.x * weight_prefix(W, W) + weight_prefix(wave, W);
+  const int p0 = tail_wave ? 0 : (c0 * Pm) / wsum;
+  const int p1m = tail_wave ? 0 : ((c0 + page_weight(wave)) * Pm) / wsum;
   // Independent loads first (one memory round trip before the first DMA):
   // the sequence length, this wave's page ids (lane j: page p0 + j), queries.
   const size_t page_row = (size_t)b * p.max_pages;
@@ -328,14 +332,50 @@ void decode_kernel(DecodeParams p) {
   const int ph = lane & 3, pc = 8 * (lane >> 2);
   half8 q_prod = {};
   if (ph < gcount) q_prod = *reinterpret_cast<const half8*>(qg + ph * kHeadDim + pc);
+  // The fused step appends one token first: the tail wave stores it (and
+  // seals the tail page it fills) before its own attention, while few
+  // registers are live; every wave attends as if that append had happened
+  // before the call.
+  const bool fused = p.k_new != nullptr;
+  const int n0 = seq_raw < 0 ? 0 : seq_raw;  // tokens stored before this call
+  const int total = fused ? n0 + 1 : n0;
+  const size_t toff = ((size_t)b * p.n_kv_heads + hk) * kPageTokens * kHeadDim;  // (b, hk) tail
+  const size_t noff = ((size_t)b * p.n_kv_heads + hk) * kHeadDim;  // (b, hk) row of k_new / v_new
+  uint8_t* seal_rec = nullptr;  // the record this call sealed (wave-uniform; tail wave only)
+  if (tail_wave && fused) {
+    if (hg == 0) {  // the append: the token goes to tail slot n0 mod 32
+      const int slot = n0 % kPageTokens;
+      *reinterpret_cast<uint32_t*>(p.tail_k + toff + (size_t)slot * kHeadDim + 2 * lane) =
+          *reinterpret_cast<const uint32_t*>(p.k_new + noff + 2 * lane);
+      *reinterpret_cast<uint32_t*>(p.tail_v + toff + (size_t)slot * kHeadDim + 2 * lane) =
+          *reinterpret_cast<const uint32_t*>(p.v_new + noff + 2 * lane);
+    }
+    const int pg = n0 / kPageTokens;
+    const int phys = n0 % kPageTokens == kPageTokens - 1 && pg < p.max_pages ? p.block_table[page_row + pg] : -1;
+    if (phys >= 0 && (int64_t)phys < p.n_pages) {  // wave-uniform; else there is no seal (or it is skipped)
+      // The filled tail (slots 0..30 and the new token) becomes page n0 / 32,
+      // quantized exactly as prefill and append do.  Head group 0 writes the
+      // record into the pool; other head groups quantize their own copy into
+      // the workspace.
+      seal_rec = hg == 0 ? p.pages + (int64_t)phys * p.page_bytes + (int64_t)hk * RB
+                         : p.seal_scratch + ((((size_t)b * p.n_kv_heads + hk) * (p.n_head_groups - 1)) +
+                                             (hg - 1)) * RB;
+      pq::quantize_page_wave<NHI>(pq::RowSrc{p.tail_k + toff, p.k_new + noff},
+                                  pq::RowSrc{p.tail_v + toff, p.v_new + noff}, seal_rec,
+                                  reinterpret_cast<uint8_t*>(&sm));
+    }
+  }
 
-  const int seq = seq_raw < 0 ? 0 : (seq_raw > p.max_seq_len ? p.max_seq_len : seq_raw);
+  const int seq = total > p.max_seq_len ? p.max_seq_len : total;
   int P = seq / kPageTokens;
   const int ntail = seq - P * kPageTokens;
   if (P > p.max_pages) P = p.max_pages;  // now P <= Pm
-  const int p1 = min(p1m, P);
+  // A seal by this call makes page n0 / 32: the tail wave attends it (when
+  // its block table entry is valid; else, like any invalid page, it adds
+  // nothing) and the page waves leave it out.
+  const bool new_page = fused && n0 % kPageTokens == kPageTokens - 1 && P > n0 / kPageTokens;
+  const int p1 = min(p1m, new_page ? P - 1 : P);
   const int npg = p1 > p0 ? p1 - p0 : 0;
-  const bool do_tail = tail_wave && ntail > 0;
   const uint8_t* head_base = p.pages + (int64_t)hk * RB;
   const int ids = lane < npg ? id_raw : -1;  // physical page of p0 + lane (at most 64 per wave)
   auto phys_of = [&](int i) -> int { return __builtin_amdgcn_readlane(ids, i); };
@@ -368,29 +408,26 @@ void decode_kernel(DecodeParams p) {
   for (int mb = 0; mb < 8; ++mb) st.o[mb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   st.corr = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (int i = 0; i < npg; ++i) {
-    const int slot = i % kRing;
-    const uint8_t* S = sm.ring[slot];
-    wait_page<NHI>(min(kRing - 1, npg - 1 - i));
+  auto valid_of = [&](int i) {
     const int phys = phys_of(i);
-    const bool valid = phys >= 0 && (int64_t)phys < p.n_pages;  // wave-uniform
-
-    // ---- q * kscale limbs, one (head, 8 channels) per lane --------------------
-    {
-      const half8 ks = *reinterpret_cast<const half8*>(S + off_kscale(NHI) + 2 * pc);
-      half8 hi, lo;
+    return phys >= 0 && (int64_t)phys < p.n_pages;  // wave-uniform
+  };
+  // q * kscale limbs of the page in S, one (head, 8 channels) per lane
+  auto produce_qt = [&](const uint8_t* S) {
+    const half8 ks = *reinterpret_cast<const half8*>(S + off_kscale(NHI) + 2 * pc);
+    half8 hi, lo;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const _Float16 hv = (_Float16)((float)q_prod[j] * (float)ks[j]);
-        hi[j] = hv;
-        lo[j] = (_Float16)__builtin_fmaf((float)q_prod[j], (float)ks[j], -(float)hv);
-      }
-      *reinterpret_cast<half8*>(&sm.qt[0].h[ph][pc]) = hi;
-      *reinterpret_cast<half8*>(&sm.qt[1].h[ph][pc]) = lo;
+    for (int j = 0; j < 8; ++j) {
+      const _Float16 hv = (_Float16)((float)q_prod[j] * (float)ks[j]);
+      hi[j] = hv;
+      lo[j] = (_Float16)__builtin_fmaf((float)q_prod[j], (float)ks[j], -(float)hv);
     }
-    wave_lds_sync();
-
-    // ---- QK^T: rows = (head, limb), columns = tokens -----------------------------
+    *reinterpret_cast<half8*>(&sm.qt[0].h[ph][pc]) = hi;
+    *reinterpret_cast<half8*>(&sm.qt[1].h[ph][pc]) = lo;
+  };
+  // QK^T of the page in S (its q * kscale limbs in LDS): rows = (head, limb),
+  // columns = tokens; the logits of head w at tokens n and n + 16
+  auto qk = [&](const uint8_t* S, bool valid, float& s0, float& s1) {
     const u32x4 kw = *reinterpret_cast<const u32x4*>(S + 16 * lane);
     half8 bq[4];
 #pragma unroll
@@ -406,10 +443,10 @@ void decode_kernel(DecodeParams p) {
     uint32_t bw[NB > 0 ? NB : 1];
 #pragma unroll
     for (int k2 = 0; k2 < NB; ++k2) {
-      const int s0 = 32 * k2 + 8 * w;
+      const int q0 = 32 * k2 + 8 * w;
       half8 v = {};
-      if (s0 < NHI) {
-        const u32x2 ib = *reinterpret_cast<const u32x2*>(S + off_idx(NHI) + s0);
+      if (q0 < NHI) {
+        const u32x2 ib = *reinterpret_cast<const u32x2*>(S + off_idx(NHI) + q0);
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = sm.qt[al].h[ah][(ib[j >> 2] >> (8 * (j & 3))) & 0x7Fu];
       }
@@ -431,15 +468,11 @@ void decode_kernel(DecodeParams p) {
     }
     // rows 4w (hi limb, with the minimum term) + 4w + 1 (lo limb) of head w
     const float cst = cmin[0] + coff[0] + coff[1];
-    float s0 = acc0[0] + acc0[1] + cst;  // token n
-    float s1 = acc1[0] + acc1[1] + cst;  // token n + 16
-    if (!valid) {  // invalid block-table entry: the page is masked out
-      s0 = -INFINITY;
-      s1 = -INFINITY;
-    }
-    softmax_step(st, s0, s1, sl2, n);
-
-    // ---- p * vscale limbs: tokens (n, n + 16) of head w, all four groups ------
+    s0 = valid ? acc0[0] + acc0[1] + cst : -INFINITY;  // token n
+    s1 = valid ? acc1[0] + acc1[1] + cst : -INFINITY;  // token n + 16
+  };
+  // p * vscale limbs (tokens n, n + 16 of head w, all four groups) and p limbs
+  auto produce_pt = [&](const uint8_t* S, float s0, float s1) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const half2v vs = *reinterpret_cast<const half2v*>(S + off_vscale(NHI) + 2 * (32 * g + 2 * n));
@@ -451,9 +484,9 @@ void decode_kernel(DecodeParams p) {
       *reinterpret_cast<half2v*>(&sm.pt[g][1][w][2 * n]) = lo;
     }
     store_p_limbs(sm.pl, w, n, s0, s1);
-    wave_lds_sync();
-
-    // ---- PV ----------------------------------------------------------------------
+  };
+  // PV of the page in S (its p limbs in LDS)
+  auto pv = [&](const uint8_t* S) {
     const u32x4 vw = *reinterpret_cast<const u32x4*>(S + off_v(NHI) + 16 * lane);
     half8 bg0 = {};
 #pragma unroll
@@ -464,66 +497,101 @@ void decode_kernel(DecodeParams p) {
       st.o[2 * g] = mfma(unpack_codes<0>(vw[g], ex_base), bg, st.o[2 * g]);
       st.o[2 * g + 1] = mfma(unpack_codes<1>(vw[g], ex_base), bg, st.o[2 * g + 1]);
     }
-    {
-      const uint8_t* src = S + (n < 4 ? off_vmin(NHI) : off_vscale(NHI)) + 2 * (32 * (n & 3) + 8 * w);
-      const half8 a = *reinterpret_cast<const half8*>(src) * corr_mul;
-      st.corr = mfma(a, bg0, st.corr);
-    }
+    const uint8_t* src = S + (n < 4 ? off_vmin(NHI) : off_vscale(NHI)) + 2 * (32 * (n & 3) + 8 * w);
+    const half8 a = *reinterpret_cast<const half8*>(src) * corr_mul;
+    st.corr = mfma(a, bg0, st.corr);
+  };
+  // one page through the whole contraction
+  auto attend_page = [&](const uint8_t* S, bool valid) {
+    produce_qt(S);
+    wave_lds_sync();
+    float s0, s1;
+    qk(S, valid, s0, s1);
+    softmax_step(st, s0, s1, sl2, n);
+    produce_pt(S, s0, s1);
+    wave_lds_sync();
+    pv(S);
+  };
 
-    // ---- refill this slot --------------------------------------------------------
-    if (i + kRing < npg) {
+  for (int i = 0; i < npg; ++i) {
+    const int slot = i % kRing;
+    const uint8_t* S = sm.ring[slot];
+    wait_page<NHI>(min(kRing - 1, npg - 1 - i));
+    attend_page(S, valid_of(i));
+    if (i + kRing < npg) {  // refill this slot
       wait_lgkm0();
       compiler_fence();
       dma_record<NHI>(rec_of(phys_of(i + kRing)), sm.ring[slot], lane);
     }
   }
 
-  // ---- fp16 tail tokens: same contraction with fp16 K / V values -----------------
-  if (do_tail) {
-    const size_t toff = ((size_t)b * p.n_kv_heads + hk) * kPageTokens * kHeadDim;
-    const _Float16* tk = p.tail_k + toff;
-    const _Float16* tv = p.tail_v + toff;
-    // Every load is issued before the first use (one memory round trip).  All
-    // 32 slots lie inside the tail buffer; tokens >= ntail are zeroed after
-    // loading, so stale slot contents never reach the MFMAs.
-    half8 ka[4][2];
+  // ---- the tail wave: the page sealed by this call, then the newest tokens -------
+  if (tail_wave) {
+    if (new_page && seal_rec != nullptr) {  // read the record back through the device coherence point
+      wait_lgkm0();  // the quantizer's LDS reads are done before the ring is refilled
+      compiler_fence();
+      wait_vmcnt<0>();  // the record's stores are complete
+      compiler_fence();
+      dma_record<NHI, 16>(seal_rec, sm.ring[0], lane);
+      wait_page<NHI>(0);
+      attend_page(sm.ring[0], true);
+      wave_lds_sync();
+    }
+    // With a seal attended, the tail is empty; a seal beyond a smaller
+    // max_seq_len leaves the older tail tokens to attend.
+    if (ntail > 0 && !new_page) {
+      // fp16 tail tokens: the same contraction with fp16 K / V values.  The
+      // appended token (slot ntail - 1 when this call appends it) comes from
+      // k_new / v_new.  Every load is issued before the first use (one
+      // memory round trip).  All 32 slots lie inside the tail buffer; tokens
+      // >= ntail are zeroed after loading, so stale slot contents never reach
+      // the MFMAs.
+      const _Float16* tk = p.tail_k + toff;
+      const _Float16* tv = p.tail_v + toff;
+      const int newslot = (fused && seq == total) ? ntail - 1 : -1;
+      half8 ka[4][2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-        ka[kb][tb] = *reinterpret_cast<const half8*>(tk + (size_t)(16 * tb + n) * kHeadDim + 32 * kb + 8 * w);
-    _Float16 va[8][8];
+        for (int tb = 0; tb < 2; ++tb) {
+          const int t = 16 * tb + n;
+          const _Float16* row = t == newslot ? p.k_new + noff : tk + (size_t)t * kHeadDim;
+          ka[kb][tb] = *reinterpret_cast<const half8*>(row + 32 * kb + 8 * w);
+        }
+      _Float16 va[8][8];
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
+      for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int t = 4 * w + (j >> 1) + 16 * (j & 1);  // tau(w, j)
-        va[mb][j] = tv[(size_t)t * kHeadDim + 16 * mb + n];
+        for (int j = 0; j < 8; ++j) {
+          const int t = 4 * w + (j >> 1) + 16 * (j & 1);  // tau(w, j)
+          const _Float16* row = t == newslot ? p.v_new + noff : tv + (size_t)t * kHeadDim;
+          va[mb][j] = row[16 * mb + n];
+        }
+      floatx4 acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          const half8 z = {};
+          acc[tb] = mfma(bq_plain[kb], 16 * tb + n < ntail ? ka[kb][tb] : z, acc[tb]);
+        }
+      float s0 = n < ntail ? acc[0][0] : -INFINITY;
+      float s1 = 16 + n < ntail ? acc[1][0] : -INFINITY;
+      softmax_step(st, s0, s1, sl2, n);
+      store_p_limbs(sm.pl, w, n, s0, s1);
+      wave_lds_sync();
+      const half8 z = {};
+      const half8 bp = n < 8 ? *reinterpret_cast<const half8*>(&sm.pl[limb][h][8 * w]) : z;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+        half8 a;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int t = 4 * w + (j >> 1) + 16 * (j & 1);
+          a[j] = t < ntail ? va[mb][j] : (_Float16)0.0f;
+        }
+        st.o[mb] = mfma(a, bp, st.o[mb]);
       }
-    floatx4 acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        const half8 z = {};
-        acc[tb] = mfma(bq_plain[kb], 16 * tb + n < ntail ? ka[kb][tb] : z, acc[tb]);
-      }
-    float s0 = n < ntail ? acc[0][0] : -INFINITY;
-    float s1 = 16 + n < ntail ? acc[1][0] : -INFINITY;
-    softmax_step(st, s0, s1, sl2, n);
-    store_p_limbs(sm.pl, w, n, s0, s1);
-    wave_lds_sync();
-    const half8 z = {};
-    const half8 bp = n < 8 ? *reinterpret_cast<const half8*>(&sm.pl[limb][h][8 * w]) : z;
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-      half8 a;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int t = 4 * w + (j >> 1) + 16 * (j & 1);
-        a[j] = t < ntail ? va[mb][j] : (_Float16)0.0f;
-      }
-      st.o[mb] = mfma(a, bp, st.o[mb]);
     }
   }
 
@@ -602,7 +670,20 @@ void decode_kernel(DecodeParams p) {
       }
     }
   }
-  if (p.n_wg == 1) return;
+  // The fused step's new length is stored once every unit of the sequence
+  // has finished (every wave of the sequence has read the old one).
+  auto sequence_done = [&]() {
+    if (!fused || threadIdx.x != 0) return;
+    const int units = p.n_kv_heads * p.n_head_groups;
+    if (__hip_atomic_fetch_add(p.seq_counters + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == units - 1) {
+      __hip_atomic_store(p.seq_lens + b, n0 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p.seq_counters + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+  if (p.n_wg == 1) {
+    sequence_done();
+    return;
+  }
 
   // ---- several workgroups: count arrivals, the last one merges ---------------------
   compiler_fence();
@@ -650,6 +731,7 @@ void decode_kernel(DecodeParams p) {
     *out_of(o) = L > 0.0f ? O / L : 0.0f;
   }
   if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  sequence_done();
 }
 
 template <int NHI>

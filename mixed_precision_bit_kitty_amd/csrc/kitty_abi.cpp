@@ -139,8 +139,15 @@ int kitty_append_token(const kitty_config_t* cfg, const kitty_kv_view_t* kv, con
   return check_launch(kitty::launch_append(p, static_cast<hipStream_t>(stream)), "append_token");
 }
 
+// Workspace of decode attention and the fused decode step, in order:
+// per-workgroup partials, workgroup arrival counters, per-sequence arrival
+// counters, and the records that head groups >= 1 re-quantize at a seal.
+struct DecodeWorkspace {
+  size_t partials, counters, seq_counters, seal_scratch, total;
+};
+
 static int decode_shape(const kitty_config_t* cfg, int32_t batch, int32_t n_q_heads, int32_t max_seq_len,
-                        kitty::SplitPlan* plan, int* n_head_groups, size_t* ws) {
+                        kitty::SplitPlan* plan, int* n_head_groups, DecodeWorkspace* ws) {
   if (batch < 1 || batch > 65535) return fail(KITTY_ERR_INVALID_ARG, "batch %d out of range [1, 65535]", batch);
   if (n_q_heads < 1 || n_q_heads % cfg->n_kv_heads != 0)
     return fail(KITTY_ERR_INVALID_ARG, "n_q_heads %d must be a positive multiple of n_kv_heads %d", n_q_heads,
@@ -152,9 +159,16 @@ static int decode_shape(const kitty_config_t* cfg, int32_t batch, int32_t n_q_he
   *n_head_groups = (G + 3) / 4;
   if ((long)cfg->n_kv_heads * *n_head_groups > 65535) return fail(KITTY_ERR_INVALID_ARG, "too many heads");
   *plan = kitty::plan_splits(batch, cfg->n_kv_heads, *n_head_groups, max_seq_len);
+  auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t part = (size_t)batch * n_q_heads * plan->n_wg * kitty::kPartialStride * sizeof(float);
   const size_t cnt = (size_t)batch * cfg->n_kv_heads * *n_head_groups * sizeof(int);
-  *ws = (part + 255) / 256 * 256 + (cnt + 255) / 256 * 256;
+  const size_t seqc = (size_t)batch * sizeof(int);
+  const size_t seal = (size_t)batch * cfg->n_kv_heads * (*n_head_groups - 1) * kitty::rec_bytes(cfg->n_hi);
+  ws->partials = 0;
+  ws->counters = r256(part);
+  ws->seq_counters = ws->counters + r256(cnt);
+  ws->seal_scratch = ws->seq_counters + r256(seqc);
+  ws->total = ws->seal_scratch + r256(seal);
   return KITTY_OK;
 }
 
@@ -164,28 +178,31 @@ int kitty_decode_workspace_bytes(const kitty_config_t* cfg, int32_t batch, int32
   if (!out) return fail(KITTY_ERR_INVALID_ARG, "out is null");
   kitty::SplitPlan plan;
   int nhg;
-  size_t ws;
+  DecodeWorkspace ws;
   if (int r = decode_shape(cfg, batch, n_q_heads, max_seq_len, &plan, &nhg, &ws)) return r;
-  *out = ws;
+  *out = ws.total;
   return ok();
 }
 
-int kitty_decode_attention(const kitty_config_t* cfg, const kitty_kv_view_t* kv, const uint16_t* q,
-                           int32_t n_q_heads, int32_t max_seq_len, float* out, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+// Shared by kitty_decode_attention (k_new == v_new == null) and
+// kitty_decode_step.
+static int decode_launch(const kitty_config_t* cfg, const kitty_kv_view_t* kv, const uint16_t* k_new,
+                         const uint16_t* v_new, const uint16_t* q, int32_t n_q_heads, int32_t max_seq_len,
+                         float* out, void* workspace, size_t workspace_bytes, void* stream, const char* what) {
   if (int r = check_config(cfg)) return r;
   if (int r = check_view(cfg, kv)) return r;
   if (!q || !aligned(q, 16)) return fail(KITTY_ERR_INVALID_ARG, "q null or not 16-byte aligned");
   if (!out || !aligned(out, 4)) return fail(KITTY_ERR_INVALID_ARG, "out null or misaligned");
   kitty::SplitPlan plan;
   int nhg;
-  size_t need;
-  if (int r = decode_shape(cfg, kv->batch, n_q_heads, max_seq_len, &plan, &nhg, &need)) return r;
+  DecodeWorkspace ws;
+  if (int r = decode_shape(cfg, kv->batch, n_q_heads, max_seq_len, &plan, &nhg, &ws)) return r;
   if (!workspace || !aligned(workspace, 256)) return fail(KITTY_ERR_INVALID_ARG, "workspace null or not 256-byte aligned");
-  if (workspace_bytes < need)
-    return fail(KITTY_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+  if (workspace_bytes < ws.total)
+    return fail(KITTY_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, ws.total);
+  uint8_t* wsb = static_cast<uint8_t*>(workspace);
   kitty::DecodeParams p{};
-  p.pages = static_cast<const uint8_t*>(kv->pages);
+  p.pages = static_cast<uint8_t*>(kv->pages);
   p.n_pages = kv->n_pages;
   p.page_bytes = kitty::page_stride_bytes(cfg->n_kv_heads, cfg->n_hi);
   p.block_table = kv->block_table;
@@ -193,24 +210,41 @@ int kitty_decode_attention(const kitty_config_t* cfg, const kitty_kv_view_t* kv,
   p.batch = kv->batch;
   p.n_kv_heads = cfg->n_kv_heads;
   p.n_hi = cfg->n_hi;
-  p.tail_k = reinterpret_cast<const _Float16*>(kv->tail_k);
-  p.tail_v = reinterpret_cast<const _Float16*>(kv->tail_v);
+  p.tail_k = reinterpret_cast<_Float16*>(kv->tail_k);
+  p.tail_v = reinterpret_cast<_Float16*>(kv->tail_v);
   p.seq_lens = kv->seq_lens;
   p.q = reinterpret_cast<const _Float16*>(q);
+  p.k_new = reinterpret_cast<const _Float16*>(k_new);
+  p.v_new = reinterpret_cast<const _Float16*>(v_new);
   p.n_q_heads = n_q_heads;
   p.group = n_q_heads / cfg->n_kv_heads;
   p.n_head_groups = nhg;
   p.max_seq_len = max_seq_len;
   p.n_wg = plan.n_wg;
   p.wg_waves = plan.wg_waves;
-  p.partial = static_cast<float*>(workspace);
-  {
-    const size_t part = (size_t)kv->batch * n_q_heads * plan.n_wg * kitty::kPartialStride * sizeof(float);
-    p.counters = reinterpret_cast<int*>(static_cast<uint8_t*>(workspace) + (part + 255) / 256 * 256);
-  }
+  p.partial = reinterpret_cast<float*>(wsb + ws.partials);
+  p.counters = reinterpret_cast<int*>(wsb + ws.counters);
+  p.seq_counters = reinterpret_cast<int*>(wsb + ws.seq_counters);
+  p.seal_scratch = wsb + ws.seal_scratch;
   p.out = out;
   (void)hipGetLastError();
-  return check_launch(kitty::launch_decode(p, static_cast<hipStream_t>(stream)), "decode_attention");
+  return check_launch(kitty::launch_decode(p, static_cast<hipStream_t>(stream)), what);
+}
+
+int kitty_decode_attention(const kitty_config_t* cfg, const kitty_kv_view_t* kv, const uint16_t* q,
+                           int32_t n_q_heads, int32_t max_seq_len, float* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return decode_launch(cfg, kv, nullptr, nullptr, q, n_q_heads, max_seq_len, out, workspace, workspace_bytes,
+                       stream, "decode_attention");
+}
+
+int kitty_decode_step(const kitty_config_t* cfg, const kitty_kv_view_t* kv, const uint16_t* k_new,
+                      const uint16_t* v_new, const uint16_t* q, int32_t n_q_heads, int32_t max_seq_len,
+                      float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16))
+    return fail(KITTY_ERR_INVALID_ARG, "k_new / v_new null or not 16-byte aligned");
+  return decode_launch(cfg, kv, k_new, v_new, q, n_q_heads, max_seq_len, out, workspace, workspace_bytes, stream,
+                       "decode_step");
 }
 
 }  // extern "C"

@@ -90,7 +90,7 @@ struct AppendParams {
 };
 
 struct DecodeParams {
-  const uint8_t* pages;
+  uint8_t* pages;          // written only by the fused step's seal
   int64_t n_pages;
   int64_t page_bytes;
   const int32_t* block_table;
@@ -98,19 +98,23 @@ struct DecodeParams {
   int32_t batch;
   int32_t n_kv_heads;
   int32_t n_hi;
-  const _Float16* tail_k;
-  const _Float16* tail_v;
-  const int32_t* seq_lens;
+  _Float16* tail_k;        // written only by the fused step's append
+  _Float16* tail_v;
+  int32_t* seq_lens;       // written only by the fused step's append
   const _Float16* q;
+  const _Float16* k_new;   // fused step: the appended token [batch][Hkv][D]; null for a plain decode
+  const _Float16* v_new;
   int32_t n_q_heads;
-  int32_t group;          // G = Hq / Hkv
-  int32_t n_head_groups;  // ceil(G / 4)
+  int32_t group;           // G = Hq / Hkv
+  int32_t n_head_groups;   // ceil(G / 4)
   int32_t max_seq_len;
   int32_t n_wg;            // workgroups per (sequence, KV head, head group)
   int32_t wg_waves;        // waves per workgroup; the unit's last wave attends over the tail
-  float* partial;         // [batch][Hq][n_wg][kPartialStride] per-workgroup partials
-  int* counters;          // [batch][Hkv][n_head_groups] split arrival counters, zero between calls
-  float* out;             // [batch][Hq][D]
+  float* partial;          // [batch][Hq][n_wg][kPartialStride] per-workgroup partials
+  int* counters;           // [batch][Hkv][n_head_groups] workgroup arrival counters, zero between calls
+  int* seq_counters;       // [batch] finished units per sequence (fused step), zero between calls
+  uint8_t* seal_scratch;   // [batch][Hkv][n_head_groups - 1] records re-quantized by head groups >= 1
+  float* out;              // [batch][Hq][D]
 };
 
 constexpr int kPartialStride = 132;  // m, l, O[128], 2 pad floats

@@ -1,334 +1,19 @@
-// Page quantizer (prefill) and append/seal kernels for gfx950.
-//
-// One wave64 quantizes one (page of 32 tokens, KV head):
-//  * Key statistics per channel over the page's tokens ("Kitty -- Dynamic
-//    Channel-wise Mixed-Precision Keys", How it works / Prefill phase, step 1):
-//    a fixed balanced pairwise tree sum for the mean and for the sum of
-//    squared deviations m2, exact min and max.  Lane l owns channels 2l, 2l+1
-//    and holds all 32 tokens in registers, so the tree is register-local.
-//  * Dynamic Channel-wise Precision Boost ("Kitty: Accurate and Efficient
-//    2-bit KV Cache Quantization with Dynamic Channel-wise Precision Boost",
-//    Abstract; Prefill step 2): the n_hi channels with the largest m2, ties to
-//    the lower channel index.  The n_hi-th largest m2 is found by a 31-step
-//    bitwise search with wave ballots (m2 >= 0, so its bit pattern orders like
-//    the value); equal keys are ranked by channel index with ballot popcounts.
-//  * Asymmetric min/max codes (Prefill step 3): 4-bit on boosted channels,
-//    2-bit elsewhere, fp16 step, round-half-even, clamp; split into the base
-//    plane (top 2 bits) and the boost plane (low 2 bits of boosted channels).
-//  * Values: per token, groups of 32 channels, 2-bit.  Each (token, group)
-//    step is formed once, by the lane that loads that group's 64 bytes
-//    (packed fp16 min/max); the steps go through LDS to the lanes that code
-//    channels c and c + 16 of every token and pack the value words.
-//  * Key codes are staged in LDS as bytes and packed into the record's code
-//    words with coalesced 16-byte stores.
-//
-// All float32 arithmetic here is separately rounded (no contraction); the
-// division is the correctly rounded one; fp32 -> fp16 conversion rounds to
-// nearest even.  Signed zeros of the inputs are read as +0.
+// Prefill and append/seal kernels for gfx950.  One wave quantizes one
+// (page of 32 tokens, KV head) with quantize_page_wave (page_quant.h): Key
+// channel statistics and the Dynamic Channel-wise Precision Boost ranking
+// ("Kitty: Accurate and Efficient 2-bit KV Cache Quantization with Dynamic
+// Channel-wise Precision Boost", Abstract; "Kitty -- Dynamic Channel-wise
+// Mixed-Precision Keys", How it works / Prefill phase, steps 1-3), two-plane
+// Key codes and 2-bit Value codes.
 #include "kitty_internal.h"
+#include "page_quant.h"
 
 #pragma clang fp contract(off)
 
 namespace kitty {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
-// Per-wave LDS: Key base codes [32 tokens][128] (4 KB), Key boost codes
-// [32][n_hi] (<= 4 KB), value steps (1 / step, min) [4 groups][32 tokens] (1 KB).
-constexpr int kWaveLds = 9216;
-
-__device__ __forceinline__ float h2f(uint16_t bits) { return (float)__builtin_bit_cast(_Float16, bits); }
-__device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
-// two fp16 inputs with -0 mapped to +0 (x + 0 rounds -0 to +0 and leaves
-// every other value unchanged)
-__device__ __forceinline__ half2v canon2(uint32_t w) {
-  const half2v z = {(_Float16)0.0f, (_Float16)0.0f};
-  return __builtin_bit_cast(half2v, w) + z;
-}
-__device__ __forceinline__ half2v hmin2(half2v a, half2v b) { return __builtin_elementwise_min(a, b); }
-__device__ __forceinline__ half2v hmax2(half2v a, half2v b) { return __builtin_elementwise_max(a, b); }
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
-}
-// reductions over the 16 lanes of a DPP row: quad xor 1, quad xor 2, half mirror, row mirror
-__device__ __forceinline__ float row_min16(float v) {
-  v = fminf(v, dpp<0xB1>(v));
-  v = fminf(v, dpp<0x4E>(v));
-  v = fminf(v, dpp<0x141>(v));
-  v = fminf(v, dpp<0x140>(v));
-  return v;
-}
-__device__ __forceinline__ float row_max16(float v) {
-  v = fmaxf(v, dpp<0xB1>(v));
-  v = fmaxf(v, dpp<0x4E>(v));
-  v = fmaxf(v, dpp<0x141>(v));
-  v = fmaxf(v, dpp<0x140>(v));
-  return v;
-}
-
-// Make this wave's LDS writes visible to its later LDS reads by other lanes:
-// wait until the writes have completed (measured on gfx950: a ds_read_b128
-// issued right after a ds_write_b128 of the same wave can return stale data)
-// and keep the compiler from moving memory accesses across this point.
-__device__ __forceinline__ void wave_lds_sync() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_wave_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Balanced pairwise tree over 32 values, level by level: a'_i = a_2i + a_2i+1.
-__device__ __forceinline__ float tree32(float (&a)[32]) {
-#pragma unroll
-  for (int s = 16; s >= 1; s >>= 1) {
-#pragma unroll
-    for (int i = 0; i < s; ++i) a[i] = a[2 * i] + a[2 * i + 1];
-  }
-  return a[0];
-}
-
-struct Step {
-  float inv;     // 1 / step, or 0 for a zero step
-  uint16_t s16;  // fp16 step
-};
-
-__device__ __forceinline__ Step make_step(float mn, float mx, float levels) {
-  float r = mx - mn;
-  float q = r / levels;
-  uint16_t s16 = f2h(q);
-  float s = h2f(s16);
-  Step st;
-  st.s16 = s16;
-  st.inv = (s != 0.0f) ? 1.0f / s : 0.0f;
-  return st;
-}
-
-// clamp(rne((x - mn) * inv), 0, levels); x >= mn, so the lower clamp is idle
-__device__ __forceinline__ uint32_t code_of(float x, float mn, float inv, float levels) {
-  float t = (x - mn) * inv;
-  t = __builtin_rintf(t);
-  t = fminf(t, levels);
-  return (uint32_t)t;
-}
-
-// bytes 0, 2, 4, 6 of x (each a 2-bit code) -> bits 0, 2, 4, 6 of the result
-__device__ __forceinline__ uint32_t gather4(uint64_t x) {
-  x &= 0x0003000300030003ull;
-  x |= x >> 14;
-  x |= x >> 28;
-  return (uint32_t)x & 0xFFu;
-}
-// code word from combos A, B given as 8 code bytes each (element e in byte e)
-__device__ __forceinline__ uint32_t pack_word(uint64_t a, uint64_t b) {
-  return gather4(a) | (gather4(b) << 8) | (gather4(a >> 8) << 16) | (gather4(b >> 8) << 24);
-}
-
-// token t -> value metadata index kappa (inverse of tau): tokens t and
-// t + 16 (t < 16) sit at kappa 2t and 2t + 1
-__host__ __device__ constexpr int kappa_of(int t) { return 2 * (t & 15) + (t >> 4); }
-// (w, e) -> token, kappa = 8w + e
-__host__ __device__ constexpr int tau_of(int w, int e) { return 4 * w + (e >> 1) + 16 * (e & 1); }
-
-// Rows of one page: row t at base + t * 128, except that row 31 comes from
-// `last` when it is set (the token being appended).
-struct RowSrc {
-  const _Float16* base;
-  const _Float16* last;
-  __device__ __forceinline__ const _Float16* row(int t) const {
-    return (t == kPageTokens - 1 && last) ? last : base + (size_t)t * kHeadDim;
-  }
-};
-
-// Quantize and pack one (page, head) into `rec`.  Called by a full wave;
-// `lds` is this wave's private kWaveLds bytes.
-template <int NHI>
-__device__ __forceinline__ void quantize_page_wave(RowSrc ks, RowSrc vs, uint8_t* __restrict__ rec, uint8_t* __restrict__ lds) {
-  const int lane = threadIdx.x & 63;
-  uint8_t* lds_base = lds;          // [32 tokens][128 channels] base codes
-  uint8_t* lds_boost = lds + 4096;  // [32 tokens][NHI slots] boost codes
-  wave_lds_sync();
-
-  // ---------------- Key statistics: channels 2*lane, 2*lane + 1 -----------
-  // min / max on the fp16 inputs (signed zeros canonical), sums in float32.
-  // The sums need no canonical zeros: a -0 input changes neither m2 nor a code.
-  float x0[32], x1[32];
-  half2v kmn, kmx;
-#pragma unroll
-  for (int t = 0; t < 32; ++t) {
-    const uint32_t w2 = *reinterpret_cast<const uint32_t*>(ks.row(t) + 2 * lane);
-    const half2v hv = __builtin_bit_cast(half2v, w2);
-    x0[t] = (float)hv[0];
-    x1[t] = (float)hv[1];
-    const half2v c = canon2(w2);
-    kmn = t == 0 ? c : hmin2(kmn, c);
-    kmx = t == 0 ? c : hmax2(kmx, c);
-  }
-  float a[32];
-#pragma unroll
-  for (int t = 0; t < 32; ++t) a[t] = x0[t];
-  const float mu0 = tree32(a) * (1.0f / 32.0f);
-#pragma unroll
-  for (int t = 0; t < 32; ++t) { float d = x0[t] - mu0; a[t] = d * d; }
-  const float m2_0 = tree32(a);
-#pragma unroll
-  for (int t = 0; t < 32; ++t) a[t] = x1[t];
-  const float mu1 = tree32(a) * (1.0f / 32.0f);
-#pragma unroll
-  for (int t = 0; t < 32; ++t) { float d = x1[t] - mu1; a[t] = d * d; }
-  const float m2_1 = tree32(a);
-  const float mn0 = (float)kmn[0], mx0 = (float)kmx[0], mn1 = (float)kmn[1], mx1 = (float)kmx[1];
-
-  // ---------------- Ranking: top NHI by m2, ties to the lower channel -------
-  const uint64_t below = (1ull << lane) - 1ull;
-  bool h0, h1;
-  if (NHI == 0) {
-    h0 = h1 = false;
-  } else if (NHI == kHeadDim) {
-    h0 = h1 = true;
-  } else {
-    const uint32_t b0 = __builtin_bit_cast(uint32_t, m2_0);
-    const uint32_t b1 = __builtin_bit_cast(uint32_t, m2_1);
-    uint32_t T = 0;
-    for (int bit = 30; bit >= 0; --bit) {
-      const uint32_t cand = T | (1u << bit);
-      const int cnt = __popcll(__ballot(b0 >= cand)) + __popcll(__ballot(b1 >= cand));
-      if (cnt >= NHI) T = cand;
-    }
-    const int gt = __popcll(__ballot(b0 > T)) + __popcll(__ballot(b1 > T));
-    const uint64_t e0 = __ballot(b0 == T), e1 = __ballot(b1 == T);
-    const int before0 = __popcll(e0 & below) + __popcll(e1 & below);
-    const int before1 = before0 + (int)((e0 >> lane) & 1ull);
-    const int need = NHI - gt;
-    h0 = (b0 > T) || (b0 == T && before0 < need);
-    h1 = (b1 > T) || (b1 == T && before1 < need);
-  }
-  const uint64_t H0 = __ballot(h0), H1 = __ballot(h1);
-  const int pos0 = __popcll(H0 & below) + __popcll(H1 & below);
-  const int pos1 = pos0 + (h0 ? 1 : 0);
-
-  // ---------------- Key codes and metadata ---------------------------------
-  const float L0 = h0 ? 15.0f : 3.0f, L1 = h1 ? 15.0f : 3.0f;
-  const Step st0 = make_step(mn0, mx0, L0), st1 = make_step(mn1, mx1, L1);
-  const uint16_t ks0 = h0 ? f2h(4.0f * h2f(st0.s16)) : st0.s16;
-  const uint16_t ks1 = h1 ? f2h(4.0f * h2f(st1.s16)) : st1.s16;
-  *reinterpret_cast<uint32_t*>(rec + off_kscale(NHI) + 4 * lane) = (uint32_t)ks0 | ((uint32_t)ks1 << 16);
-  *reinterpret_cast<uint32_t*>(rec + off_kmin(NHI) + 4 * lane) = (uint32_t)f2h(mn0) | ((uint32_t)f2h(mn1) << 16);
-  // (pos < NHI always holds: exactly NHI channels are selected)
-  const bool w0 = h0 && pos0 < NHI, w1 = h1 && pos1 < NHI;
-  if (NHI > 0) {
-    if (w0) rec[off_idx(NHI) + pos0] = (uint8_t)(2 * lane);
-    if (w1) rec[off_idx(NHI) + pos1] = (uint8_t)(2 * lane + 1);
-  }
-#pragma unroll
-  for (int t = 0; t < 32; ++t) {
-    const uint32_t q0 = code_of(x0[t], mn0, st0.inv, L0);
-    const uint32_t q1 = code_of(x1[t], mn1, st1.inv, L1);
-    const uint32_t bq0 = h0 ? (q0 >> 2) : q0;
-    const uint32_t bq1 = h1 ? (q1 >> 2) : q1;
-    *reinterpret_cast<uint16_t*>(lds_base + t * 128 + 2 * lane) = (uint16_t)(bq0 | (bq1 << 8));
-    if (NHI > 0) {
-      if (w0) lds_boost[t * NHI + pos0] = (uint8_t)(q0 & 3u);
-      if (w1) lds_boost[t * NHI + pos1] = (uint8_t)(q1 & 3u);
-    }
-  }
-
-  // ---------------- Value steps: one (token, group) per lane and pass -------
-  {
-    float* vstep = reinterpret_cast<float*>(lds + 8192);  // [group][token] x (1 / step, min)
-    uint16_t* vsc = reinterpret_cast<uint16_t*>(rec + off_vscale(NHI));
-    uint16_t* vmn = reinterpret_cast<uint16_t*>(rec + off_vmin(NHI));
-    const int gp = lane & 3;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int tp = (lane >> 2) + 16 * i;
-      const u32x4* src = reinterpret_cast<const u32x4*>(vs.row(tp) + 32 * gp);
-      u32x4 c[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) c[k] = src[k];
-      half2v mnv = canon2(c[0][0]), mxv = mnv;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        if (k == 0) continue;
-        const half2v h = canon2(c[k >> 2][k & 3]);
-        mnv = hmin2(mnv, h);
-        mxv = hmax2(mxv, h);
-      }
-      const float mn = fminf((float)mnv[0], (float)mnv[1]);
-      const float mx = fmaxf((float)mxv[0], (float)mxv[1]);
-      const Step st = make_step(mn, mx, 3.0f);
-      *reinterpret_cast<float2*>(vstep + 2 * (32 * gp + tp)) = make_float2(st.inv, mn);
-      const int kap = kappa_of(tp);
-      vsc[32 * gp + kap] = st.s16;
-      vmn[32 * gp + kap] = f2h(mn);
-    }
-  }
-  wave_lds_sync();
-
-  // ---------------- Value codes: channels c0 = 32g + u and c0 + 16 ----------
-  {
-    const int g = lane >> 4, u = lane & 15;
-    const int c0 = 32 * g + u, c1 = c0 + 16;
-    const floatx4* vstep = reinterpret_cast<const floatx4*>(lds + 8192) + 16 * g;  // two tokens per read
-    uint32_t a0[32], a1[32];
-#pragma unroll
-    for (int t2 = 0; t2 < 16; ++t2) {
-      const floatx4 st2 = vstep[t2];  // (1 / step, min) of tokens 2 t2 and 2 t2 + 1
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int t = 2 * t2 + k;
-        const _Float16* r = vs.row(t);
-        const float y0 = (float)r[c0];
-        const float y1 = (float)r[c1];
-        a0[t] = code_of(y0, st2[2 * k + 1], st2[2 * k], 3.0f);
-        a1[t] = code_of(y1, st2[2 * k + 1], st2[2 * k], 3.0f);
-      }
-    }
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int t = tau_of(w, e);
-        const int sh = 16 * (e & 1) + 2 * (e >> 1);
-        word |= a0[t] << sh;
-        word |= a1[t] << (sh + 8);
-      }
-      *reinterpret_cast<uint32_t*>(rec + off_v(NHI) + 16 * (16 * w + u) + 4 * g) = word;
-    }
-  }
-
-  // ---------------- Pack Key code planes from LDS ---------------------------
-  wave_lds_sync();
-  {
-    const int u = lane & 15, w = lane >> 4;
-    u32x4 words;
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const uint64_t A = *reinterpret_cast<const uint64_t*>(lds_base + u * 128 + 32 * x + 8 * w);
-      const uint64_t B = *reinterpret_cast<const uint64_t*>(lds_base + (16 + u) * 128 + 32 * x + 8 * w);
-      words[x] = pack_word(A, B);
-    }
-    *reinterpret_cast<u32x4*>(rec + 16 * lane) = words;
-    if (NHI > 0) {
-      constexpr int nf = NHI / 32;
-#pragma unroll
-      for (int bb = 0; bb < nf; ++bb) {
-        const uint64_t A = *reinterpret_cast<const uint64_t*>(lds_boost + u * NHI + 32 * bb + 8 * w);
-        const uint64_t B = *reinterpret_cast<const uint64_t*>(lds_boost + (16 + u) * NHI + 32 * bb + 8 * w);
-        *reinterpret_cast<uint32_t*>(rec + off_kboost() + 4 * (lane * nf + bb)) = pack_word(A, B);
-      }
-      if ((NHI % 32) != 0 && lane < 32) {
-        const uint64_t A = *reinterpret_cast<const uint64_t*>(lds_boost + u * NHI + 32 * nf + 8 * w);
-        const uint64_t B = *reinterpret_cast<const uint64_t*>(lds_boost + (16 + u) * NHI + 32 * nf + 8 * w);
-        *reinterpret_cast<uint32_t*>(rec + off_kboost() + 256 * nf + 4 * lane) = pack_word(A, B);
-      }
-    }
-  }
-}
+using namespace pq;
 
 // grid (pages + 1, Hkv, batch), one wave per block
 template <int NHI>

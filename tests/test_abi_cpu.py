@@ -17,7 +17,7 @@ FAKE = 0x7F0000000000  # an aligned non-null address that is never dereferenced
 
 def test_exports_every_declared_symbol():
     names = B.declared_symbols()
-    assert len(names) == 8
+    assert len(names) == 9
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -49,11 +49,16 @@ def test_workspace_bytes_cover_partials():
     cfg = B.config(8, 32)
     nb = B.kitty_decode_workspace_bytes(cfg, 16, 32, 4096)
     assert nb > 16 * 32 * 132 * 4 and nb % 256 == 0
-    # an empty cache: one workgroup, 8 heads x 1 partial + 1 counter
-    assert B.kitty_decode_workspace_bytes(cfg, 1, 8, 0) == 4352 + 256
+    # an empty cache: one workgroup, 8 heads x 1 partial, one unit counter
+    # block, one sequence counter block, no seal records (one head group)
+    assert B.kitty_decode_workspace_bytes(cfg, 1, 8, 0) == 4352 + 256 + 256
     # the longest supported sequence: at most 16 workgroup partials per head
     big = B.kitty_decode_workspace_bytes(B.config(1, 32), 1, 4, 4096 * 32 + 31)
-    assert big == 4 * 16 * 132 * 4 + 256
+    assert big == 4 * 16 * 132 * 4 + 256 + 256
+    # 12 query heads per KV head: 3 head groups, two of which re-quantize a
+    # sealed page into their own record of the workspace
+    nb = B.kitty_decode_workspace_bytes(cfg, 2, 96, 0)
+    assert nb == 2 * 96 * 132 * 4 + 256 + 256 + 2 * 8 * 2 * (3072 + 9 * 32)
 
 
 def test_workspace_bytes_monotone_in_max_seq_len():
@@ -114,12 +119,19 @@ def _call_decode(view, q=FAKE, hq=32, msl=64, out=FAKE, ws=FAKE, nbytes=1 << 30)
                                       nbytes, None)
 
 
+def _call_step(view, k=FAKE, v=FAKE, q=FAKE, hq=32, msl=64, out=FAKE, ws=FAKE, nbytes=1 << 30):
+    lib = B.load()
+    return lib.kitty_decode_step(ctypes.byref(B.config(8, 32)), ctypes.byref(view), k, v, q, hq, msl, out, ws,
+                                 nbytes, None)
+
+
 @pytest.mark.parametrize("bad", BAD_VIEWS)
 def test_bad_view_rejected_everywhere(bad):
     v = _view(**bad)
     assert _call_quantize(v) == B.KITTY_ERR_INVALID_ARG
     assert _call_append(v) == B.KITTY_ERR_INVALID_ARG
     assert _call_decode(v) == B.KITTY_ERR_INVALID_ARG
+    assert _call_step(v) == B.KITTY_ERR_INVALID_ARG
     lib = B.load()
     assert lib.kitty_quantize_pages(None, ctypes.byref(v), FAKE, FAKE, 64, None, None) == B.KITTY_ERR_INVALID_ARG
 
@@ -155,6 +167,19 @@ def test_decode_arguments():
     assert _call_decode(v, ws=FAKE + 64) == B.KITTY_ERR_INVALID_ARG
     assert _call_decode(v, nbytes=16) == B.KITTY_ERR_WORKSPACE
     assert "workspace" in B.load().kitty_last_error().decode()
+
+
+def test_decode_step_arguments():
+    v = _view()
+    assert _call_step(v, k=None) == B.KITTY_ERR_INVALID_ARG
+    assert _call_step(v, v=None) == B.KITTY_ERR_INVALID_ARG
+    assert _call_step(v, k=FAKE + 8) == B.KITTY_ERR_INVALID_ARG          # 16-byte alignment
+    assert _call_step(v, v=FAKE + 2) == B.KITTY_ERR_INVALID_ARG
+    assert _call_step(v, q=FAKE + 4) == B.KITTY_ERR_INVALID_ARG
+    assert _call_step(v, hq=12) == B.KITTY_ERR_INVALID_ARG
+    assert _call_step(v, msl=4096 * 32 + 32) == B.KITTY_ERR_UNSUPPORTED
+    assert _call_step(v, ws=FAKE + 64) == B.KITTY_ERR_INVALID_ARG
+    assert _call_step(v, nbytes=16) == B.KITTY_ERR_WORKSPACE
 
 
 def test_decode_plan_fits_page_id_register():
