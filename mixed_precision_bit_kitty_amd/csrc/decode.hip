@@ -646,6 +646,22 @@ void decode_kernel(DecodeParams p) {
     fwt[hh] = M;
   }
   __syncthreads();
+  // The fused step stores the new length once every wave of the sequence
+  // has read the old one: each unit, once all its workgroups are past that
+  // read, counts itself at the per-sequence counter (one 128-byte line per
+  // sequence), and the last unit stores n0 + 1 and clears the counter.  The
+  // atomic is issued before the unit's remaining output work, which hides
+  // its round trip.
+  int* const seq_counter = p.seq_counters + (size_t)b * kSeqCounterStride;
+  int seq_old = 0;
+  if (fused && threadIdx.x == 0 && p.n_wg == 1)
+    seq_old = __hip_atomic_fetch_add(seq_counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  auto sequence_arrival = [&](int old, int units) {
+    if (fused && threadIdx.x == 0 && old == units - 1) {
+      __hip_atomic_store(p.seq_lens + b, n0 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(seq_counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
   auto out_of = [&](int o) { return p.out + ((size_t)b * p.n_q_heads + hq0 + (o >> 7)) * kHeadDim + (o & 127); };
   float* gpart = p.partial + ((size_t)b * p.n_q_heads + hq0) * p.n_wg * kPartialStride;
   auto st_ag = [](float* a, float v) { __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
@@ -670,18 +686,8 @@ void decode_kernel(DecodeParams p) {
       }
     }
   }
-  // The fused step's new length is stored once every unit of the sequence
-  // has finished (every wave of the sequence has read the old one).
-  auto sequence_done = [&]() {
-    if (!fused || threadIdx.x != 0) return;
-    const int units = p.n_kv_heads * p.n_head_groups;
-    if (__hip_atomic_fetch_add(p.seq_counters + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == units - 1) {
-      __hip_atomic_store(p.seq_lens + b, n0 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(p.seq_counters + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  };
   if (p.n_wg == 1) {
-    sequence_done();
+    sequence_arrival(seq_old, p.n_kv_heads * p.n_head_groups);
     return;
   }
 
@@ -695,6 +701,8 @@ void decode_kernel(DecodeParams p) {
   __syncthreads();
   if (all[0].flag != p.n_wg - 1) return;
   compiler_fence();
+  if (fused && threadIdx.x == 0)  // the unit is complete: count it for the sequence
+    seq_old = __hip_atomic_fetch_add(seq_counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (int o = threadIdx.x; o < 4 * kHeadDim; o += nthr) {
     const int hh = o >> 7, ch = o & 127;
     if (hh >= gcount) continue;
@@ -731,7 +739,7 @@ void decode_kernel(DecodeParams p) {
     *out_of(o) = L > 0.0f ? O / L : 0.0f;
   }
   if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  sequence_done();
+  sequence_arrival(seq_old, p.n_kv_heads * p.n_head_groups);
 }
 
 template <int NHI>

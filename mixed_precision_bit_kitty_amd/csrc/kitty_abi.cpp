@@ -162,7 +162,7 @@ static int decode_shape(const kitty_config_t* cfg, int32_t batch, int32_t n_q_he
   auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t part = (size_t)batch * n_q_heads * plan->n_wg * kitty::kPartialStride * sizeof(float);
   const size_t cnt = (size_t)batch * cfg->n_kv_heads * *n_head_groups * sizeof(int);
-  const size_t seqc = (size_t)batch * sizeof(int);
+  const size_t seqc = (size_t)batch * kitty::kSeqCounterStride * sizeof(int);
   const size_t seal = (size_t)batch * cfg->n_kv_heads * (*n_head_groups - 1) * kitty::rec_bytes(cfg->n_hi);
   ws->partials = 0;
   ws->counters = r256(part);

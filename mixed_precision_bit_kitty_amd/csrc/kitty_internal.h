@@ -124,6 +124,7 @@ constexpr int kMaxWg = 16;           // decode workgroups per (sequence, KV head
 // partial tail page); a page wave keeps its page ids in one 64-lane register,
 // and 16 x 12 - 1 waves x 64 pages cover it.
 constexpr int kMaxSeqLen = 4096 * 32 + 31;
+constexpr int kSeqCounterStride = 32;  // ints: one 128-byte line per sequence counter
 
 // Split-KV plan shared by the workspace query and the launch.
 struct SplitPlan {

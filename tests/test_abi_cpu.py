@@ -50,7 +50,7 @@ def test_workspace_bytes_cover_partials():
     nb = B.kitty_decode_workspace_bytes(cfg, 16, 32, 4096)
     assert nb > 16 * 32 * 132 * 4 and nb % 256 == 0
     # an empty cache: one workgroup, 8 heads x 1 partial, one unit counter
-    # block, one sequence counter block, no seal records (one head group)
+    # block, one sequence counter line, no seal records (one head group)
     assert B.kitty_decode_workspace_bytes(cfg, 1, 8, 0) == 4352 + 256 + 256
     # the longest supported sequence: at most 16 workgroup partials per head
     big = B.kitty_decode_workspace_bytes(B.config(1, 32), 1, 4, 4096 * 32 + 31)
@@ -59,6 +59,9 @@ def test_workspace_bytes_cover_partials():
     # sealed page into their own record of the workspace
     nb = B.kitty_decode_workspace_bytes(cfg, 2, 96, 0)
     assert nb == 2 * 96 * 132 * 4 + 256 + 256 + 2 * 8 * 2 * (3072 + 9 * 32)
+    # one 128-byte counter line per sequence
+    nb3 = B.kitty_decode_workspace_bytes(cfg, 3, 8, 0)
+    assert nb3 == 12800 + 256 + 512
 
 
 def test_workspace_bytes_monotone_in_max_seq_len():
