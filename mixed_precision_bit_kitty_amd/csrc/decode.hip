@@ -101,6 +101,12 @@ __device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {  // loop-invariant,
   return r;
 }
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t orv) { return (x & mask) | orv; }
+// A value the compiler may not re-derive (keeps a bitfield extract from being
+// rewritten into shift-and-mask pairs once it is scaled into an address).
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm("" : "+v"(x));
+  return x;
+}
 template <int COMBO>
 __device__ __forceinline__ half8 unpack_codes(uint32_t w, ExpBits e) {
   const uint32_t m8 = e.m8, m6 = e.m6;
@@ -164,17 +170,28 @@ static_assert(sizeof(Lds<128>) * kMaxWgWaves <= 160 * 1024, "twelve waves' LDS f
 template <int NHI>
 constexpr int dma_per_page() { return rec_bytes(NHI) / 1024 + (rec_bytes(NHI) % 1024 ? 1 : 0); }
 
-// Copy one record into an LDS slot: 16 bytes per lane per instruction.
-// AUX = 16 (sc1) reads at agent scope, past this CU's vector L1.
+// Copy one record into an LDS slot: 16 bytes per lane per instruction.  The
+// instruction offset advances the global and the LDS address alike, so one
+// address serves the 1024-byte chunks within the offset field's reach (up to
+// 3072); a chunk at 4096 (n_hi >= 112) takes its own address.  AUX = 16
+// (sc1) reads at agent scope, past this CU's vector L1.
+template <int AUX, int M, int NCHUNK, int REM>
+__device__ __forceinline__ void dma_chunks(const uint8_t* src, uint8_t* slot, int lane) {
+  if constexpr (M < NCHUNK) {
+    const bool full = M < NCHUNK - 1 || REM == 0;
+    if (full || 16 * lane < REM) {
+      if constexpr (1024 * M <= 3072)
+        __builtin_amdgcn_global_load_lds(src, (lds_void*)slot, 16, 1024 * M, AUX);
+      else
+        __builtin_amdgcn_global_load_lds(src + 1024 * M, (lds_void*)(slot + 1024 * M), 16, 0, AUX);
+    }
+    dma_chunks<AUX, M + 1, NCHUNK, REM>(src, slot, lane);
+  }
+}
 template <int NHI, int AUX = 0>
 __device__ __forceinline__ void dma_record(const uint8_t* __restrict__ rec, uint8_t* slot, int lane) {
   constexpr int rb = rec_bytes(NHI);
-  constexpr int nfull = rb / 1024, rem = rb % 1024;
-#pragma unroll
-  for (int m = 0; m < nfull; ++m)
-    __builtin_amdgcn_global_load_lds(rec + 1024 * m + 16 * lane, (lds_void*)(slot + 1024 * m), 16, 0, AUX);
-  if (rem != 0 && 16 * lane < rem)
-    __builtin_amdgcn_global_load_lds(rec + 1024 * nfull + 16 * lane, (lds_void*)(slot + 1024 * nfull), 16, 0, AUX);
+  dma_chunks<AUX, 0, (rb + 1023) / 1024, rb % 1024>(rec + 16 * lane, slot, lane);
 }
 
 // Wait until the oldest in-flight page has landed; `ahead` pages were issued after it.
@@ -251,15 +268,31 @@ __device__ __forceinline__ void softmax_step(WaveState& st, float& s0, float& s1
   st.l += s0 + s1;
 }
 
-// Write the p limbs (hi = f16(p), lo = f16(p - hi)) of tokens (n, n + 16) of
-// head w at kappa (2n, 2n + 1): dst[limb][w][kappa].
-__device__ __forceinline__ void store_p_limbs(_Float16 (*dst)[4][32], int w, int n, float p0, float p1) {
-  const _Float16 h0 = (_Float16)p0, h1 = (_Float16)p1;
-  half2v hi = {h0, h1};
-  half2v lo = {(_Float16)(p0 - (float)h0), (_Float16)(p1 - (float)h1)};
-  *reinterpret_cast<half2v*>(&dst[0][w][2 * n]) = hi;
-  *reinterpret_cast<half2v*>(&dst[1][w][2 * n]) = lo;
+// p limbs (hi = f16(p), lo = f16(p - hi)) of tokens (n, n + 16)
+struct PLimbs {
+  half2v hi, lo;
+};
+__device__ __forceinline__ PLimbs p_limbs(float p0, float p1) {
+  const half2v hi = {(_Float16)p0, (_Float16)p1};
+  const half2v lo = {(_Float16)(p0 - (float)hi[0]), (_Float16)(p1 - (float)hi[1])};
+  return PLimbs{hi, lo};
 }
+// Write the p limbs of tokens (n, n + 16) of head w at kappa (2n, 2n + 1):
+// dst[limb][w][kappa].
+__device__ __forceinline__ void store_p_limbs(_Float16 (*dst)[4][32], int w, int n, PLimbs pl) {
+  *reinterpret_cast<half2v*>(&dst[0][w][2 * n]) = pl.hi;
+  *reinterpret_cast<half2v*>(&dst[1][w][2 * n]) = pl.lo;
+}
+// Two fp16 limbs of a * b for fp16 a, b (exact product: 22 significant
+// bits): hi = f16(a b) by a correctly rounded fp16 multiply and lo = the
+// residual a b - hi, which one fused fp16 multiply-add forms exactly (it has
+// at most 11 significant bits) unless it falls below the fp16 normal range.
+// Packed: one instruction per limb for two products.
+__device__ __forceinline__ half2v mul_hi(half2v a, half2v b) {
+#pragma clang fp contract(off)
+  return a * b;
+}
+__device__ __forceinline__ half2v fma2(half2v a, half2v b, half2v c) { return __builtin_elementwise_fma(a, b, c); }
 
 // Share of the pages given to wave i of a workgroup.  Wave i runs on SIMD
 // i % 4 as its (i / 4)-th resident wave, and the instruction arbiter favours
@@ -377,11 +410,15 @@ void decode_kernel(DecodeParams p) {
   const int p1 = min(p1m, new_page ? P - 1 : P);
   const int npg = p1 > p0 ? p1 - p0 : 0;
   const uint8_t* head_base = p.pages + (int64_t)hk * RB;
+  // page ids are int32 and the page stride is below 2^32 (at most 1024 KV
+  // heads): id checks and record offsets stay in scalar 32-bit arithmetic
+  const int np32 = p.n_pages > 0x7FFFFFFF ? 0x7FFFFFFF : (int)p.n_pages;
+  const uint32_t pb32 = (uint32_t)p.page_bytes;
   const int ids = lane < npg ? id_raw : -1;  // physical page of p0 + lane (at most 64 per wave)
   auto phys_of = [&](int i) -> int { return __builtin_amdgcn_readlane(ids, i); };
   auto rec_of = [&](int phys) -> const uint8_t* {
-    if (phys < 0 || (int64_t)phys >= p.n_pages) phys = 0;  // invalid ids read page 0 and are masked
-    return head_base + (int64_t)phys * p.page_bytes;
+    if (phys < 0 || phys >= np32) phys = 0;  // invalid ids read page 0 and are masked
+    return head_base + (uint64_t)(uint32_t)phys * pb32;
   };
 #pragma unroll
   for (int d = 0; d < kRing; ++d)
@@ -410,17 +447,21 @@ void decode_kernel(DecodeParams p) {
 
   auto valid_of = [&](int i) {
     const int phys = phys_of(i);
-    return phys >= 0 && (int64_t)phys < p.n_pages;  // wave-uniform
+    return phys >= 0 && phys < np32;  // wave-uniform
   };
   // q * kscale limbs of the page in S, one (head, 8 channels) per lane
   auto produce_qt = [&](const uint8_t* S) {
     const half8 ks = *reinterpret_cast<const half8*>(S + off_kscale(NHI) + 2 * pc);
     half8 hi, lo;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const _Float16 hv = (_Float16)((float)q_prod[j] * (float)ks[j]);
-      hi[j] = hv;
-      lo[j] = (_Float16)__builtin_fmaf((float)q_prod[j], (float)ks[j], -(float)hv);
+    for (int j = 0; j < 8; j += 2) {
+      const half2v a = {q_prod[j], q_prod[j + 1]}, b = {ks[j], ks[j + 1]};
+      const half2v h2 = mul_hi(a, b);
+      const half2v l2 = fma2(a, b, -h2);
+      hi[j] = h2[0];
+      hi[j + 1] = h2[1];
+      lo[j] = l2[0];
+      lo[j + 1] = l2[1];
     }
     *reinterpret_cast<half8*>(&sm.qt[0].h[ph][pc]) = hi;
     *reinterpret_cast<half8*>(&sm.qt[1].h[ph][pc]) = lo;
@@ -448,7 +489,7 @@ void decode_kernel(DecodeParams p) {
       if (q0 < NHI) {
         const u32x2 ib = *reinterpret_cast<const u32x2*>(S + off_idx(NHI) + q0);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = sm.qt[al].h[ah][(ib[j >> 2] >> (8 * (j & 3))) & 0x7Fu];
+        for (int j = 0; j < 8; ++j) v[j] = sm.qt[al].h[ah][opaque(__builtin_amdgcn_ubfe(ib[j >> 2], 8 * (j & 3), 7))];
       }
       bb[k2] = v;
       if (k2 < NF) bw[k2] = *reinterpret_cast<const uint32_t*>(S + off_kboost() + 4 * (lane * NF + k2));
@@ -471,19 +512,22 @@ void decode_kernel(DecodeParams p) {
     s0 = valid ? acc0[0] + acc0[1] + cst : -INFINITY;  // token n
     s1 = valid ? acc1[0] + acc1[1] + cst : -INFINITY;  // token n + 16
   };
-  // p * vscale limbs (tokens n, n + 16 of head w, all four groups) and p limbs
+  // p * vscale limbs (tokens n, n + 16 of head w, all four groups) and p
+  // limbs.  With p = p_hi + p_lo (fp16 limbs), p * vscale = hi + lo where
+  // hi = f16(p_hi vscale), lo = f16(p_lo vscale + (p_hi vscale - hi)): the
+  // inner residual is exact and lo is rounded once, so the pair carries
+  // p * vscale to about 2^-21 relative.
   auto produce_pt = [&](const uint8_t* S, float s0, float s1) {
+    const PLimbs pl = p_limbs(s0, s1);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const half2v vs = *reinterpret_cast<const half2v*>(S + off_vscale(NHI) + 2 * (32 * g + 2 * n));
-      const _Float16 h0 = (_Float16)(s0 * (float)vs[0]), h1 = (_Float16)(s1 * (float)vs[1]);
-      half2v hi = {h0, h1};
-      half2v lo = {(_Float16)__builtin_fmaf(s0, (float)vs[0], -(float)h0),
-                   (_Float16)__builtin_fmaf(s1, (float)vs[1], -(float)h1)};
+      const half2v hi = mul_hi(pl.hi, vs);
+      const half2v lo = fma2(pl.lo, vs, fma2(pl.hi, vs, -hi));
       *reinterpret_cast<half2v*>(&sm.pt[g][0][w][2 * n]) = hi;
       *reinterpret_cast<half2v*>(&sm.pt[g][1][w][2 * n]) = lo;
     }
-    store_p_limbs(sm.pl, w, n, s0, s1);
+    store_p_limbs(sm.pl, w, n, pl);
   };
   // PV of the page in S (its p limbs in LDS)
   auto pv = [&](const uint8_t* S) {
@@ -513,6 +557,7 @@ void decode_kernel(DecodeParams p) {
     pv(S);
   };
 
+#pragma unroll 2
   for (int i = 0; i < npg; ++i) {
     const int slot = i % kRing;
     const uint8_t* S = sm.ring[slot];
@@ -578,7 +623,7 @@ void decode_kernel(DecodeParams p) {
       float s0 = n < ntail ? acc[0][0] : -INFINITY;
       float s1 = 16 + n < ntail ? acc[1][0] : -INFINITY;
       softmax_step(st, s0, s1, sl2, n);
-      store_p_limbs(sm.pl, w, n, s0, s1);
+      store_p_limbs(sm.pl, w, n, p_limbs(s0, s1));
       wave_lds_sync();
       const half8 z = {};
       const half8 bp = n < 8 ? *reinterpret_cast<const half8*>(&sm.pl[limb][h][8 * w]) : z;
