@@ -31,6 +31,8 @@
 // Online softmax runs in the log2 domain and rescales only when the max
 // grows.  Each wave writes (m, l, O) for its page range; the last wave of a
 // (sequence, KV head, head group) merges them (log-sum-exp) into the output.
+#include <type_traits>
+
 #include "kitty_internal.h"
 #include "page_quant.h"
 
@@ -274,7 +276,8 @@ struct PLimbs {
 };
 __device__ __forceinline__ PLimbs p_limbs(float p0, float p1) {
   const half2v hi = {(_Float16)p0, (_Float16)p1};
-  const half2v lo = {(_Float16)(p0 - (float)hi[0]), (_Float16)(p1 - (float)hi[1])};
+  // p - hi is exact in fp32; one mixed-precision fma rounds it to fp16
+  const half2v lo = {(_Float16)__builtin_fmaf((float)hi[0], -1.0f, p0), (_Float16)__builtin_fmaf((float)hi[1], -1.0f, p1)};
   return PLimbs{hi, lo};
 }
 // Write the p limbs of tokens (n, n + 16) of head w at kappa (2n, 2n + 1):
@@ -557,17 +560,22 @@ void decode_kernel(DecodeParams p) {
     pv(S);
   };
 
-#pragma unroll 2
-  for (int i = 0; i < npg; ++i) {
-    const int slot = i % kRing;
-    const uint8_t* S = sm.ring[slot];
+  // The loop runs two pages per trip so that each ring slot, and with it
+  // every LDS address of the page, is a compile-time offset.
+  auto page_step = [&](int i, auto slot_c) {
+    constexpr int slot = decltype(slot_c)::value;
     wait_page<NHI>(min(kRing - 1, npg - 1 - i));
-    attend_page(S, valid_of(i));
+    attend_page(sm.ring[slot], valid_of(i));
     if (i + kRing < npg) {  // refill this slot
       wait_lgkm0();
       compiler_fence();
       dma_record<NHI>(rec_of(phys_of(i + kRing)), sm.ring[slot], lane);
     }
+  };
+  static_assert(kRing == 2, "the page loop alternates two ring slots");
+  for (int i = 0; i < npg; i += 2) {
+    page_step(i, std::integral_constant<int, 0>{});
+    if (i + 1 < npg) page_step(i + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- the tail wave: the page sealed by this call, then the newest tokens -------
@@ -673,24 +681,10 @@ void decode_kernel(DecodeParams p) {
 
   // ---- merge the W wave partials ----------------------------------------------
   // Partials combine by log-sum-exp: M = max m_j, weight f_j = 2^(m_j - M),
-  // L = sum f_j l_j, O = sum f_j O_j.  Four lanes of wave 0 form the weights
-  // per head; then each thread sums one (head, channel) over the W waves.
+  // L = sum f_j l_j, O = sum f_j O_j.  Each thread forms one (head, channel)
+  // output from the W partials on its own (m and l are broadcast reads), so
+  // every LDS read is issued up front and no second barrier is needed.
   const int nthr = 64 * W;
-  float* const fwt = &all[0].red[0][0][0];  // reused: f[j][head] for j < W, then M, L per head
-  if (threadIdx.x < 4) {
-    const int hh = threadIdx.x;
-    float M = kNegBig;
-    for (int j = 0; j < W; ++j) M = fmaxf(M, all[j].part[hh][128]);
-    float L = 0.0f;
-    for (int j = 0; j < W; ++j) {
-      const float f = __builtin_amdgcn_exp2f(all[j].part[hh][128] - M);
-      L += f * all[j].part[hh][129];
-      all[j].part[hh][130] = f;
-    }
-    all[0].part[hh][131] = L;  // read back below; [130] of wave 0 holds its own weight
-    fwt[hh] = M;
-  }
-  __syncthreads();
   // The fused step stores the new length once every wave of the sequence
   // has read the old one: each unit, once all its workgroups are past that
   // read, counts itself at the per-sequence counter (one 128-byte line per
@@ -713,10 +707,23 @@ void decode_kernel(DecodeParams p) {
   auto ld_ag = [](const float* a) { return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
   for (int o = threadIdx.x; o < 4 * kHeadDim; o += nthr) {
     const int hh = o >> 7, ch = o & 127;
-    float O = 0.0f;
-    for (int j = 0; j < W; ++j) O += all[j].part[hh][130] * all[j].part[hh][ch];
-    const float L = all[0].part[hh][131];
     if (hh >= gcount) continue;
+    float mj[kMaxWgWaves], lj[kMaxWgWaves], oj[kMaxWgWaves];
+    float M = kNegBig;
+#pragma unroll
+    for (int j = 0; j < kMaxWgWaves; ++j) {
+      mj[j] = j < W ? all[j].part[hh][128] : kNegBig;
+      lj[j] = j < W ? all[j].part[hh][129] : 0.0f;
+      oj[j] = j < W ? all[j].part[hh][ch] : 0.0f;
+      M = fmaxf(M, mj[j]);
+    }
+    float L = 0.0f, O = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxWgWaves; ++j) {
+      const float f = __builtin_amdgcn_exp2f(mj[j] - M);
+      L += f * lj[j];
+      O += f * oj[j];
+    }
     if (p.n_wg == 1) {
       *out_of(o) = L > 0.0f ? O / L : 0.0f;
     } else {
@@ -726,7 +733,7 @@ void decode_kernel(DecodeParams p) {
       float* d = gpart + ((size_t)hh * p.n_wg + blockIdx.x) * kPartialStride;
       st_ag(d + 2 + ch, O);
       if (ch == 0) {
-        st_ag(d, fwt[hh]);
+        st_ag(d, M);
         st_ag(d + 1, L);
       }
     }
