@@ -47,7 +47,8 @@ enum {
   KITTY_ERR_INVALID_ARG = -1, /* null pointer, negative/inconsistent size, misalignment */
   KITTY_ERR_UNSUPPORTED = -2, /* head_dim != 128, page_tokens != 32, bad n_hi, ... */
   KITTY_ERR_WORKSPACE = -3,   /* workspace smaller than kitty_decode_workspace_bytes */
-  KITTY_ERR_HIP = -4          /* a kernel launch failed (hipGetLastError) */
+  KITTY_ERR_HIP = -4,         /* a kernel launch failed (hipGetLastError) */
+  KITTY_ERR_NO_PAGES = -5     /* kitty_pool_reserve: the pool has too few free pages */
 };
 
 /* Cache geometry ("Configuration reference": head_dim, group_size,
@@ -99,13 +100,16 @@ int kitty_page_bytes(const kitty_config_t* cfg, size_t* out);
  * pages are ranked, quantized and packed into the physical pages
  * block_table[b][0..], the remaining n_b mod 32 tokens are copied verbatim
  * into tail_k / tail_v slots 0.., and seq_lens[b] = n_b.  lens: optional
- * device int32 [batch].  Requires floor(S / 32) <= max_pages. */
+ * device int32 [batch]; a negative lens[b] leaves sequence b untouched (no
+ * page, tail or length written), so that one call can fill some slots of a
+ * serving batch while the others keep decoding.  Requires floor(S / 32) <= max_pages. */
 int kitty_quantize_pages(const kitty_config_t* cfg, const kitty_kv_view_t* kv,
                          const uint16_t* k, const uint16_t* v, int32_t S,
                          const int32_t* lens, void* stream);
 
 /* Decode-time append of one token per sequence.  k_new, v_new: device fp16
- * [batch][Hkv][D], 16-byte aligned.  With n = seq_lens[b]: the token is stored in tail slot
+ * [batch][Hkv][D], 16-byte aligned.  A sequence with seq_lens[b] < 0 is an
+ * inactive slot and is skipped.  With n = seq_lens[b]: the token is stored in tail slot
  * n mod 32 and seq_lens[b] becomes n + 1; when that slot is the 32nd, the
  * full tail is quantized exactly like a prefill page and written to physical
  * page block_table[b][n / 32] (the tail page stays fp16 until it fills).  The
@@ -130,7 +134,8 @@ int kitty_decode_workspace_bytes(const kitty_config_t* cfg, int32_t batch, int32
  * hq / (Hq / Hkv).  For each sequence, attends over all seq_lens[b] tokens --
  * sealed pages in order, then the fp16 tail: out[b][hq] = softmax(q . k^ /
  * sqrt(D)) . v^ with k^, v^ the dequantized keys and values.  out: device
- * fp32 [batch][Hq][D] (zeros for an empty sequence).  max_seq_len bounds
+ * fp32 [batch][Hq][D] (zeros for an empty sequence or an inactive slot,
+ * seq_lens[b] < 0).  max_seq_len bounds
  * seq_lens (tokens beyond it are ignored); at most 131103 (4096 pages plus a
  * tail), else KITTY_ERR_UNSUPPORTED.  workspace: device, 256-byte
  * aligned, at least kitty_decode_workspace_bytes(...) bytes, zero-filled by
@@ -148,7 +153,8 @@ int kitty_decode_attention(const kitty_config_t* cfg, const kitty_kv_view_t* kv,
  * (n = seq_lens[b] before the call); when it fills the tail page, that page
  * is quantized like a prefill page into block_table[b][n / 32] (skipped if
  * that entry is >= max_pages or outside the pool, as the append does) and
- * attended as a sealed page; seq_lens[b] becomes n + 1.  k_new, v_new:
+ * attended as a sealed page; seq_lens[b] becomes n + 1.  Inactive slots
+ * (seq_lens[b] < 0) append nothing and attend nothing.  k_new, v_new:
  * device fp16 [batch][Hkv][D], 16-byte aligned.  max_seq_len bounds the
  * length after the append.  Other arguments, the workspace (the same size
  * and zero-fill rules) and the errors are those of kitty_decode_attention.
@@ -158,6 +164,37 @@ int kitty_decode_attention(const kitty_config_t* cfg, const kitty_kv_view_t* kv,
 int kitty_decode_step(const kitty_config_t* cfg, const kitty_kv_view_t* kv, const uint16_t* k_new,
                       const uint16_t* v_new, const uint16_t* q, int32_t n_q_heads, int32_t max_seq_len,
                       float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Page pool for ragged serving (the page-centric layout of the Abstract
+ * lets sequences of any length share one pool).  Host only: these calls
+ * touch no device memory and allocate nothing.  The caller owns the pool
+ * struct, its free list and a host mirror of the block table, whose rows it
+ * passes in; after a call that changes a row, the caller copies that row to
+ * the device block table before the next kernel that reads it.  Unmapped
+ * entries are -1.  Not thread-safe: one pool, one thread at a time. */
+typedef struct {
+  int32_t* free_list; /* host int32 [n_pages], caller-owned: entries [0, n_free) are free page ids */
+  int64_t n_pages;    /* physical pages in the pool, 1 .. 2^31 - 1 */
+  int64_t n_free;     /* free pages */
+} kitty_pool_t;
+
+/* Make every page of [0, n_pages) free; later reservations take pages 0, 1,
+ * 2, ... in that order, and released pages are taken again first. */
+int kitty_pool_init(kitty_pool_t* pool, int32_t* free_list, int64_t n_pages);
+
+/* Map the pages a sequence needs to hold n_tokens tokens: entries
+ * 0 .. floor(n_tokens / 32) - 1 of its row (the pages that its prefill, or
+ * its appends up to that length, seal).  Call it with the length a prefill
+ * or a decode step will reach, before that call.  All or nothing: with too
+ * few free pages it returns KITTY_ERR_NO_PAGES and changes nothing.  row:
+ * host int32 [max_pages]; every entry must be -1 or a page id below n_pages;
+ * floor(n_tokens / 32) <= max_pages. */
+int kitty_pool_reserve(kitty_pool_t* pool, int32_t* row, int32_t max_pages, int32_t n_tokens);
+
+/* Return every mapped page of a row to the pool (e.g. when its sequence
+ * ends); its entries become -1.  Releasing more pages than the pool holds
+ * (a page released twice) is KITTY_ERR_INVALID_ARG, with nothing changed. */
+int kitty_pool_release(kitty_pool_t* pool, int32_t* row, int32_t max_pages);
 
 #ifdef __cplusplus
 }

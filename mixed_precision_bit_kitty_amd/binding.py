@@ -24,6 +24,7 @@ KITTY_ERR_INVALID_ARG = -1
 KITTY_ERR_UNSUPPORTED = -2
 KITTY_ERR_WORKSPACE = -3
 KITTY_ERR_HIP = -4
+KITTY_ERR_NO_PAGES = -5
 
 HEAD_DIM = 128
 PAGE_TOKENS = 32
@@ -45,6 +46,10 @@ class kitty_kv_view_t(ctypes.Structure):
                 ("block_table", ctypes.c_void_p), ("batch", ctypes.c_int32),
                 ("max_pages", ctypes.c_int32), ("tail_k", ctypes.c_void_p),
                 ("tail_v", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p)]
+
+
+class kitty_pool_t(ctypes.Structure):
+    _fields_ = [("free_list", ctypes.c_void_p), ("n_pages", ctypes.c_int64), ("n_free", ctypes.c_int64)]
 
 
 _lib = None
@@ -84,6 +89,9 @@ def load(path=None):
         "kitty_decode_workspace_bytes": ([cfgp, i32, i32, i32, P(sz)], ctypes.c_int),
         "kitty_decode_attention": ([cfgp, viewp, vp, i32, i32, vp, vp, sz, vp], ctypes.c_int),
         "kitty_decode_step": ([cfgp, viewp, vp, vp, vp, i32, i32, vp, vp, sz, vp], ctypes.c_int),
+        "kitty_pool_init": ([P(kitty_pool_t), vp, ctypes.c_int64], ctypes.c_int),
+        "kitty_pool_reserve": ([P(kitty_pool_t), vp, i32, i32], ctypes.c_int),
+        "kitty_pool_release": ([P(kitty_pool_t), vp, i32], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -170,6 +178,37 @@ def kitty_decode_step(cfg, view, k_new, v_new, q, n_q_heads, max_seq_len, out, w
                                     _stream(stream)))
 
 
+class PagePool:
+    """Host-side page pool (kitty_pool_*): a free list of physical page ids
+    and the reservation / release of block-table rows (host numpy int32
+    arrays, -1 = unmapped)."""
+
+    def __init__(self, n_pages):
+        import numpy as np
+        self.free_list = np.empty(n_pages, dtype=np.int32)
+        self.pool = kitty_pool_t()
+        _check(load().kitty_pool_init(ctypes.byref(self.pool), self.free_list.ctypes.data, n_pages))
+
+    @property
+    def n_free(self):
+        return int(self.pool.n_free)
+
+    @staticmethod
+    def _row(row):
+        import numpy as np
+        if not (isinstance(row, np.ndarray) and row.dtype == np.int32 and row.flags.c_contiguous and row.ndim == 1):
+            raise KittyError(KITTY_ERR_INVALID_ARG, "row must be a contiguous 1-d numpy int32 array")
+        return row
+
+    def reserve(self, row, n_tokens):
+        row = self._row(row)
+        _check(load().kitty_pool_reserve(ctypes.byref(self.pool), row.ctypes.data, row.shape[0], n_tokens))
+
+    def release(self, row):
+        row = self._row(row)
+        _check(load().kitty_pool_release(ctypes.byref(self.pool), row.ctypes.data, row.shape[0]))
+
+
 class KittyCache:
     """Caller-side buffers of one paged cache on a CUDA device.
 
@@ -207,6 +246,35 @@ class KittyCache:
                                     self.max_pages, self.tail_k.data_ptr(), self.tail_v.data_ptr(),
                                     self.seq_lens.data_ptr())
         self._ws = None
+
+    @classmethod
+    def with_pool(cls, batch, n_kv_heads, n_hi, max_tokens, n_pages, device="cuda"):
+        """A serving cache: every slot starts inactive (seq_lens -1, no page
+        mapped) and pages come from a shared PagePool of n_pages pages."""
+        import numpy as np
+        max_pages = max(1, -(-max_tokens // PAGE_TOKENS))
+        c = cls(batch, n_kv_heads, n_hi, max_tokens, device=device,
+                block_table=np.full((batch, max_pages), -1, np.int32), n_pages=n_pages)
+        c.bt_host = np.full((batch, c.max_pages), -1, np.int32)
+        c.page_pool = PagePool(n_pages)
+        c.seq_lens.fill_(-1)
+        return c
+
+    def reserve(self, b, n_tokens):
+        """Map the pages slot b needs to hold n_tokens tokens (before the
+        prefill or decode step that reaches that length)."""
+        import torch
+        before = self.bt_host[b].copy()
+        self.page_pool.reserve(self.bt_host[b], n_tokens)
+        if not (before == self.bt_host[b]).all():
+            self.block_table[b].copy_(torch.from_numpy(self.bt_host[b]))
+
+    def release(self, b):
+        """Return slot b's pages to the pool and mark the slot inactive."""
+        import torch
+        self.page_pool.release(self.bt_host[b])
+        self.block_table[b].copy_(torch.from_numpy(self.bt_host[b]))
+        self.seq_lens[b] = -1
 
     # -- hot path ---------------------------------------------------------
     def quantize_pages(self, k, v, lens=None, stream=None):

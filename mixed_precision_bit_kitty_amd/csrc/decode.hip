@@ -372,7 +372,7 @@ void decode_kernel(DecodeParams p) {
   // seals the tail page it fills) before its own attention, while few
   // registers are live; every wave attends as if that append had happened
   // before the call.
-  const bool fused = p.k_new != nullptr;
+  const bool fused = p.k_new != nullptr && seq_raw >= 0;  // a negative length marks an inactive slot
   const int n0 = seq_raw < 0 ? 0 : seq_raw;  // tokens stored before this call
   const int total = fused ? n0 + 1 : n0;
   const size_t toff = ((size_t)b * p.n_kv_heads + hk) * kPageTokens * kHeadDim;  // (b, hk) tail

@@ -247,4 +247,60 @@ int kitty_decode_step(const kitty_config_t* cfg, const kitty_kv_view_t* kv, cons
                        "decode_step");
 }
 
+
+// ---- page pool (host only) -------------------------------------------------------
+
+int kitty_pool_init(kitty_pool_t* pool, int32_t* free_list, int64_t n_pages) {
+  if (!pool || !free_list) return fail(KITTY_ERR_INVALID_ARG, "pool or free_list is null");
+  if (n_pages < 1 || n_pages > 0x7FFFFFFF) return fail(KITTY_ERR_INVALID_ARG, "n_pages %lld out of range", (long long)n_pages);
+  for (int64_t i = 0; i < n_pages; ++i) free_list[i] = (int32_t)(n_pages - 1 - i);  // the stack top is page 0
+  pool->free_list = free_list;
+  pool->n_pages = n_pages;
+  pool->n_free = n_pages;
+  return ok();
+}
+
+}  // extern "C"
+
+static int check_pool(const kitty_pool_t* pool, const int32_t* row, int32_t max_pages) {
+  if (!pool || !pool->free_list || !row) return fail(KITTY_ERR_INVALID_ARG, "pool, its free list or row is null");
+  if (pool->n_pages < 1 || pool->n_pages > 0x7FFFFFFF || pool->n_free < 0 || pool->n_free > pool->n_pages)
+    return fail(KITTY_ERR_INVALID_ARG, "pool state is inconsistent");
+  if (max_pages < 1) return fail(KITTY_ERR_INVALID_ARG, "max_pages must be >= 1");
+  for (int32_t j = 0; j < max_pages; ++j)
+    if (row[j] < -1 || row[j] >= pool->n_pages)
+      return fail(KITTY_ERR_INVALID_ARG, "row entry %d = %d is neither -1 nor a page id", j, row[j]);
+  return KITTY_OK;
+}
+
+extern "C" {
+
+int kitty_pool_reserve(kitty_pool_t* pool, int32_t* row, int32_t max_pages, int32_t n_tokens) {
+  if (int r = check_pool(pool, row, max_pages)) return r;
+  if (n_tokens < 0) return fail(KITTY_ERR_INVALID_ARG, "n_tokens must be >= 0");
+  const int32_t need = n_tokens / kitty::kPageTokens;
+  if (need > max_pages) return fail(KITTY_ERR_INVALID_ARG, "%d tokens need %d pages > max_pages %d", n_tokens, need, max_pages);
+  int64_t missing = 0;
+  for (int32_t j = 0; j < need; ++j) missing += row[j] < 0;
+  if (missing > pool->n_free)
+    return fail(KITTY_ERR_NO_PAGES, "%lld pages needed, %lld free", (long long)missing, (long long)pool->n_free);
+  for (int32_t j = 0; j < need; ++j)
+    if (row[j] < 0) row[j] = pool->free_list[--pool->n_free];
+  return ok();
+}
+
+int kitty_pool_release(kitty_pool_t* pool, int32_t* row, int32_t max_pages) {
+  if (int r = check_pool(pool, row, max_pages)) return r;
+  int64_t mapped = 0;
+  for (int32_t j = 0; j < max_pages; ++j) mapped += row[j] >= 0;
+  if (pool->n_free + mapped > pool->n_pages)
+    return fail(KITTY_ERR_INVALID_ARG, "releasing %lld pages overflows the pool (a page released twice?)", (long long)mapped);
+  for (int32_t j = 0; j < max_pages; ++j)
+    if (row[j] >= 0) {
+      pool->free_list[pool->n_free++] = row[j];
+      row[j] = -1;
+    }
+  return ok();
+}
+
 }  // extern "C"

@@ -21,7 +21,8 @@ __global__ __launch_bounds__(64) void quantize_pages_kernel(QuantizeParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kWaveLds];
   const int page = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
   int n = p.lens ? p.lens[b] : p.S;
-  n = n < 0 ? 0 : (n > p.S ? p.S : n);
+  if (n < 0) return;  // a negative length leaves sequence b as it is
+  n = n > p.S ? p.S : n;
   int P = n / kPageTokens;
   if (P > p.max_pages) P = p.max_pages;
   const size_t seq_off = ((size_t)b * p.n_kv_heads + h) * (size_t)p.S * kHeadDim;
@@ -52,8 +53,8 @@ __global__ __launch_bounds__(1024) void append_token_kernel(AppendParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
   const int b = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nw = blockDim.x >> 6;
-  int n = p.seq_lens[b];
-  if (n < 0) n = 0;
+  const int n = p.seq_lens[b];
+  if (n < 0) return;  // an inactive slot: nothing appended (block-uniform)
   const int slot = n % kPageTokens;
   for (int h = wave; h < p.n_kv_heads; h += nw) {
     const size_t tail_off = ((size_t)b * p.n_kv_heads + h) * kPageTokens * kHeadDim;

@@ -17,7 +17,7 @@ FAKE = 0x7F0000000000  # an aligned non-null address that is never dereferenced
 
 def test_exports_every_declared_symbol():
     names = B.declared_symbols()
-    assert len(names) == 9
+    assert len(names) == 12
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -31,6 +31,7 @@ def test_header_error_codes_match_binding():
     assert int(codes["KITTY_ERR_UNSUPPORTED"]) == B.KITTY_ERR_UNSUPPORTED
     assert int(codes["KITTY_ERR_WORKSPACE"]) == B.KITTY_ERR_WORKSPACE
     assert int(codes["KITTY_ERR_HIP"]) == B.KITTY_ERR_HIP
+    assert int(codes["KITTY_ERR_NO_PAGES"]) == B.KITTY_ERR_NO_PAGES
 
 
 def test_abi_version():

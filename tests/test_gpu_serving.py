@@ -1,0 +1,104 @@
+"""Ragged serving on one shared page pool: requests of different prompt and
+generation lengths come and go in four batch slots whose pages come from a
+pool smaller than the slots could ever map at once, so pages are recycled.
+
+Each request is checked against its own oracle cache (its prompt prefilled,
+then its tokens appended one by one): page records and tails bit-exact after
+its prefill and at the end, attention within 2e-3 at every step.  Idle
+slots (seq_lens -1) must stay idle and read zeros.  Steps alternate between
+the fused step and append + decode."""
+import numpy as np
+import pytest
+
+import oracle as O
+from mixed_precision_bit_kitty_amd import synth
+
+from _gpu_util import ATOL, compare_records, compare_tails, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+
+
+# (prompt tokens, generated tokens) per request, served in this order
+REQUESTS = [(45, 40), (0, 35), (100, 20), (31, 33), (64, 10), (7, 50), (200, 12), (33, 30)]
+
+
+def test_serving_with_a_shared_pool():
+    import torch
+    from mixed_precision_bit_kitty_amd import binding as B
+    w = synth.LLAMA3_8B.with_(n_kv_heads=2, n_q_heads=8)
+    n_slots, H, Hq, n_hi = 4, w.n_kv_heads, w.n_q_heads, w.n_hi
+    cache = B.KittyCache.with_pool(n_slots, H, n_hi, max_tokens=256, n_pages=14)
+    reqs = []
+    for r, (prompt, gen) in enumerate(REQUESTS):
+        x = synth.batch(w.with_(seed=200 + r), batch=1, ctx=max(prompt, 1), steps=gen)
+        reqs.append(dict(prompt=prompt, gen=gen, x=x, oc=None, done=0))
+    pending = list(range(len(reqs)))
+    slot_req = [None] * n_slots
+    finished, step = 0, 0
+    zero_kv = torch.zeros((n_slots, H, 128), dtype=torch.float16, device="cuda")
+    zero_q = torch.zeros((n_slots, Hq, 128), dtype=torch.float16, device="cuda")
+    while finished < len(reqs):
+        # start waiting requests in free slots (a prefill that leaves every other slot as it is)
+        for b in range(n_slots):
+            if slot_req[b] is None and pending:
+                r = pending.pop(0)
+                q = reqs[r]
+                S = max(q["prompt"], 1)
+                k = torch.zeros((n_slots, H, S, 128), dtype=torch.float16, device="cuda")
+                v = torch.zeros_like(k)
+                k[b], v[b] = dev(q["x"]["k"][0]), dev(q["x"]["v"][0])
+                lens = np.full(n_slots, -1, np.int32)
+                lens[b] = q["prompt"]
+                before = host(cache.seq_lens).copy()
+                cache.reserve(b, q["prompt"])
+                cache.quantize_pages(k, v, lens=dev(lens))
+                q["oc"] = O.quantize_pages(q["x"]["k"], q["x"]["v"], n_hi, batch_lens=[q["prompt"]])
+                after = host(cache.seq_lens)
+                others = [i for i in range(n_slots) if i != b]
+                assert np.array_equal(after[others], before[others]), "a prefill touched another slot"
+                compare_records(cache, q["oc"], seq_map={0: b})
+                compare_tails(cache, q["oc"], seq_map={0: b})
+                slot_req[b] = r
+        # one decode step over all slots
+        k_new, v_new, qv = zero_kv.clone(), zero_kv.clone(), zero_q.clone()
+        for b, r in enumerate(slot_req):
+            if r is not None:
+                q = reqs[r]
+                g = q["done"]
+                k_new[b], v_new[b] = dev(q["x"]["k_new"][g][0]), dev(q["x"]["v_new"][g][0])
+                qv[b] = dev(q["x"]["q_new"][g][0])
+                cache.reserve(b, q["prompt"] + g + 1)
+        if step % 2 == 0:
+            out = host(cache.decode_step(k_new, v_new, qv))
+        else:
+            cache.append_token(k_new, v_new)
+            out = host(cache.decode_attention(qv))
+        lens_now = host(cache.seq_lens)
+        for b, r in enumerate(slot_req):
+            if r is None:
+                assert lens_now[b] == -1 and not out[b].any(), f"idle slot {b} changed"
+                continue
+            q = reqs[r]
+            g = q["done"]
+            O.append_token(q["oc"], q["x"]["k_new"][g], q["x"]["v_new"][g])
+            ref = O.decode_attention(q["oc"], q["x"]["q_new"][g])[0]
+            err = float(np.abs(out[b] - ref).max())
+            assert err <= ATOL, f"step {step} slot {b} request {r}: max abs err {err}"
+            assert lens_now[b] == q["prompt"] + g + 1
+            q["done"] += 1
+            if q["done"] == q["gen"]:  # the request ends: check it, free its slot and pages
+                compare_records(cache, q["oc"], seq_map={0: b})
+                compare_tails(cache, q["oc"], seq_map={0: b})
+                cache.release(b)
+                slot_req[b] = None
+                finished += 1
+        step += 1
+    assert cache.page_pool.n_free == 14
+    print(f"served {len(reqs)} requests in {step} steps on a 14-page pool")
