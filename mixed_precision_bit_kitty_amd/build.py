@@ -23,8 +23,9 @@ COMMON = [
     "-I", os.path.join(ROOT, "include"),
 ]
 SOURCES = {
-    # bit-exact quantizer: every float32 op rounded separately
-    "quantize.hip": ["-ffp-contract=off"],
+    # bit-exact quantizer: every float32 op rounded separately; inputs are
+    # finite, so min/max need no NaN-quieting canonicalize of their inputs
+    "quantize.hip": ["-ffp-contract=off", "-fno-honor-nans"],
     # inputs are finite: max reductions need no NaN-quieting canonicalize,
     # which lets the DPP row reductions fold into v_max_f32_dpp
     "decode.hip": ["-fno-honor-nans"],

@@ -38,9 +38,11 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 // Per-wave LDS: Key base codes [32 tokens][128] (4 KB), Key boost codes
-// [32][n_hi] (32 n_hi bytes), value steps (1 / step, min) [4 groups][32 tokens]
-// (1 KB).
-__host__ __device__ constexpr int lds_vstep(int n_hi) { return 4096 + 32 * n_hi; }
+// [32][n_hi + 8] (a row per token; column n_hi takes the stores of lanes
+// with no boosted channel, so every lane stores unconditionally), value
+// steps (1 / step, min) [4 groups][32 tokens] (1 KB).
+__host__ __device__ constexpr int boost_row(int n_hi) { return n_hi + 8; }
+__host__ __device__ constexpr int lds_vstep(int n_hi) { return 4096 + 32 * boost_row(n_hi); }
 __host__ __device__ constexpr int quant_lds_bytes(int n_hi) { return lds_vstep(n_hi) + 1024; }
 constexpr int kWaveLds = quant_lds_bytes(128);  // enough for every n_hi
 
@@ -113,13 +115,16 @@ __device__ __forceinline__ Step make_step(float mn, float mx, float levels) {
   return st;
 }
 
-// clamp(rne((x - mn) * inv), 0, levels); x >= mn, so the lower clamp is idle
-__device__ __forceinline__ uint32_t code_of(float x, float mn, float inv, float levels) {
+// clamp(rne((x - mn) * inv), 0, levels), inserted as byte `byte` of `into`.
+// t = (x - mn) * inv is >= 0 and finite (x >= mn, inv <= 2^24), and
+// min(rne(t), L) = rne(min(t, L)) for an integer L, so the clamp goes first
+// and v_cvt_pk_u8_f32 (round half to even, saturating to [0, 255]; checked
+// on gfx950) rounds and packs in one instruction.
+__device__ __forceinline__ uint32_t code_of(float x, float mn, float inv, float levels, uint32_t byte = 0, uint32_t into = 0) {
 #pragma clang fp contract(off)
   float t = (x - mn) * inv;
-  t = __builtin_rintf(t);
   t = fminf(t, levels);
-  return (uint32_t)t;
+  return __builtin_amdgcn_cvt_pk_u8_f32(t, byte, into);
 }
 
 // bytes 0, 2, 4, 6 of x (each a 2-bit code) -> bits 0, 2, 4, 6 of the result
@@ -157,12 +162,14 @@ __device__ __forceinline__ void quantize_page_wave(RowSrc ks, RowSrc vs, uint8_t
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63;
   uint8_t* lds_base = lds;          // [32 tokens][128 channels] base codes
-  uint8_t* lds_boost = lds + 4096;  // [32 tokens][NHI slots] boost codes
+  uint8_t* lds_boost = lds + 4096;  // [32 tokens][boost_row(NHI)] boost codes
   wave_lds_sync();
 
   // ---------------- Key statistics: channels 2*lane, 2*lane + 1 -----------
-  // min / max on the fp16 inputs (signed zeros canonical), sums in float32.
-  // The sums need no canonical zeros: a -0 input changes neither m2 nor a code.
+  // min / max on the fp16 inputs, sums in float32.  A zero extreme may come
+  // out as -0 whatever the order, so the extremes are made canonical once at
+  // the end (-0 -> +0); the sums need no canonical zeros: a -0 input changes
+  // neither m2 nor a code.
   float x0[32], x1[32];
   half2v kmn, kmx;
 #pragma unroll
@@ -171,10 +178,11 @@ __device__ __forceinline__ void quantize_page_wave(RowSrc ks, RowSrc vs, uint8_t
     const half2v hv = __builtin_bit_cast(half2v, w2);
     x0[t] = (float)hv[0];
     x1[t] = (float)hv[1];
-    const half2v c = canon2(w2);
-    kmn = t == 0 ? c : hmin2(kmn, c);
-    kmx = t == 0 ? c : hmax2(kmx, c);
+    kmn = t == 0 ? hv : hmin2(kmn, hv);
+    kmx = t == 0 ? hv : hmax2(kmx, hv);
   }
+  kmn = canon2(__builtin_bit_cast(uint32_t, kmn));
+  kmx = canon2(__builtin_bit_cast(uint32_t, kmx));
   float a[32];
 #pragma unroll
   for (int t = 0; t < 32; ++t) a[t] = x0[t];
@@ -231,16 +239,19 @@ __device__ __forceinline__ void quantize_page_wave(RowSrc ks, RowSrc vs, uint8_t
     if (w0) rec[off_idx(NHI) + pos0] = (uint8_t)(2 * lane);
     if (w1) rec[off_idx(NHI) + pos1] = (uint8_t)(2 * lane + 1);
   }
+  // Codes go to LDS as bytes of which only the low two bits are read back:
+  // base = q >> 2 on a boosted channel, q elsewhere; boost = q (low bits).
+  const uint32_t sh0 = h0 ? 2u : 0u, sh1 = h1 ? 2u : 0u;
+  uint8_t* const bst0 = lds_boost + (w0 ? pos0 : NHI);  // column NHI: a lane's discarded stores
+  uint8_t* const bst1 = lds_boost + (w1 ? pos1 : NHI);
 #pragma unroll
   for (int t = 0; t < 32; ++t) {
-    const uint32_t q0 = code_of(x0[t], mn0, st0.inv, L0);
-    const uint32_t q1 = code_of(x1[t], mn1, st1.inv, L1);
-    const uint32_t bq0 = h0 ? (q0 >> 2) : q0;
-    const uint32_t bq1 = h1 ? (q1 >> 2) : q1;
-    *reinterpret_cast<uint16_t*>(lds_base + t * 128 + 2 * lane) = (uint16_t)(bq0 | (bq1 << 8));
+    const uint32_t q = code_of(x1[t], mn1, st1.inv, L1, 1, code_of(x0[t], mn0, st0.inv, L0));  // bytes q0, q1
+    const uint32_t base = __builtin_amdgcn_ubfe(q, sh0, 8) | ((q >> sh1) & 0xFF00u);
+    *reinterpret_cast<uint16_t*>(lds_base + t * 128 + 2 * lane) = (uint16_t)base;
     if (NHI > 0) {
-      if (w0) lds_boost[t * NHI + pos0] = (uint8_t)(q0 & 3u);
-      if (w1) lds_boost[t * NHI + pos1] = (uint8_t)(q1 & 3u);
+      bst0[t * boost_row(NHI)] = (uint8_t)q;
+      bst1[t * boost_row(NHI)] = (uint8_t)(q >> 8);
     }
   }
 
@@ -257,14 +268,21 @@ __device__ __forceinline__ void quantize_page_wave(RowSrc ks, RowSrc vs, uint8_t
       u32x4 c[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) c[k] = src[k];
-      half2v mnv = canon2(c[0][0]), mxv = mnv;
+      // (each element is copied to a scalar first: a bit cast of a vector
+      // element expression would read the vector's first element)
+      const uint32_t w00 = c[0][0];
+      half2v mnv = __builtin_bit_cast(half2v, w00), mxv = mnv;
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         if (k == 0) continue;
-        const half2v h = canon2(c[k >> 2][k & 3]);
+        const uint32_t wk = c[k >> 2][k & 3];
+        const half2v h = __builtin_bit_cast(half2v, wk);
         mnv = hmin2(mnv, h);
         mxv = hmax2(mxv, h);
       }
+      // zero extremes made canonical once (-0 -> +0), as for the keys
+      mnv = canon2(__builtin_bit_cast(uint32_t, mnv));
+      mxv = canon2(__builtin_bit_cast(uint32_t, mxv));
       const float mn = fminf((float)mnv[0], (float)mnv[1]);
       const float mx = fmaxf((float)mxv[0], (float)mxv[1]);
       const Step st = make_step(mn, mx, 3.0f);
@@ -292,7 +310,7 @@ __device__ __forceinline__ void quantize_page_wave(RowSrc ks, RowSrc vs, uint8_t
         const float y0 = (float)r[c0];
         const float y1 = (float)r[c1];
         a0[t] = code_of(y0, st2[2 * k + 1], st2[2 * k], 3.0f);
-        a1[t] = code_of(y1, st2[2 * k + 1], st2[2 * k], 3.0f);
+        a1[t] = code_of(y1, st2[2 * k + 1], st2[2 * k], 3.0f);  // codes <= 3: no masking needed below
       }
     }
 #pragma unroll
@@ -325,13 +343,13 @@ __device__ __forceinline__ void quantize_page_wave(RowSrc ks, RowSrc vs, uint8_t
       constexpr int nf = NHI / 32;
 #pragma unroll
       for (int bb = 0; bb < nf; ++bb) {
-        const uint64_t A = *reinterpret_cast<const uint64_t*>(lds_boost + u * NHI + 32 * bb + 8 * w);
-        const uint64_t B = *reinterpret_cast<const uint64_t*>(lds_boost + (16 + u) * NHI + 32 * bb + 8 * w);
+        const uint64_t A = *reinterpret_cast<const uint64_t*>(lds_boost + u * boost_row(NHI) + 32 * bb + 8 * w);
+        const uint64_t B = *reinterpret_cast<const uint64_t*>(lds_boost + (16 + u) * boost_row(NHI) + 32 * bb + 8 * w);
         *reinterpret_cast<uint32_t*>(rec + off_kboost() + 4 * (lane * nf + bb)) = pack_word(A, B);
       }
       if ((NHI % 32) != 0 && lane < 32) {
-        const uint64_t A = *reinterpret_cast<const uint64_t*>(lds_boost + u * NHI + 32 * nf + 8 * w);
-        const uint64_t B = *reinterpret_cast<const uint64_t*>(lds_boost + (16 + u) * NHI + 32 * nf + 8 * w);
+        const uint64_t A = *reinterpret_cast<const uint64_t*>(lds_boost + u * boost_row(NHI) + 32 * nf + 8 * w);
+        const uint64_t B = *reinterpret_cast<const uint64_t*>(lds_boost + (16 + u) * boost_row(NHI) + 32 * nf + 8 * w);
         *reinterpret_cast<uint32_t*>(rec + off_kboost() + 256 * nf + 4 * lane) = pack_word(A, B);
       }
     }

@@ -18,7 +18,7 @@ using namespace pq;
 // grid (pages + 1, Hkv, batch), one wave per block
 template <int NHI>
 __global__ __launch_bounds__(64) void quantize_pages_kernel(QuantizeParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kWaveLds];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[quant_lds_bytes(NHI)];
   const int page = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
   int n = p.lens ? p.lens[b] : p.S;
   if (n < 0) return;  // a negative length leaves sequence b as it is
