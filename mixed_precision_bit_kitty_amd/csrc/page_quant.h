@@ -155,10 +155,11 @@ struct RowSrc {
   }
 };
 
-// Quantize and pack one (page, head) into `rec`.  Called by a full wave;
-// `lds` is this wave's private quant_lds_bytes(NHI) bytes.
+// The Key half of a (page, head) record: statistics, ranking, codes, the two
+// code planes and the Key metadata.  Called by a full wave; uses the first
+// lds_vstep(NHI) bytes of `lds`.
 template <int NHI>
-__device__ __forceinline__ void quantize_page_wave(RowSrc ks, RowSrc vs, uint8_t* __restrict__ rec, uint8_t* __restrict__ lds) {
+__device__ __forceinline__ void quantize_keys_wave(RowSrc ks, uint8_t* __restrict__ rec, uint8_t* __restrict__ lds) {
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63;
   uint8_t* lds_base = lds;          // [32 tokens][128 channels] base codes
@@ -255,6 +256,45 @@ __device__ __forceinline__ void quantize_page_wave(RowSrc ks, RowSrc vs, uint8_t
     }
   }
 
+  // ---------------- Pack Key code planes from LDS ---------------------------
+  wave_lds_sync();
+  {
+    const int u = lane & 15, w = lane >> 4;
+    u32x4 words;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const uint64_t A = *reinterpret_cast<const uint64_t*>(lds_base + u * 128 + 32 * x + 8 * w);
+      const uint64_t B = *reinterpret_cast<const uint64_t*>(lds_base + (16 + u) * 128 + 32 * x + 8 * w);
+      words[x] = pack_word(A, B);
+    }
+    *reinterpret_cast<u32x4*>(rec + 16 * lane) = words;
+    if (NHI > 0) {
+      constexpr int nf = NHI / 32;
+#pragma unroll
+      for (int bb = 0; bb < nf; ++bb) {
+        const uint64_t A = *reinterpret_cast<const uint64_t*>(lds_boost + u * boost_row(NHI) + 32 * bb + 8 * w);
+        const uint64_t B = *reinterpret_cast<const uint64_t*>(lds_boost + (16 + u) * boost_row(NHI) + 32 * bb + 8 * w);
+        *reinterpret_cast<uint32_t*>(rec + off_kboost() + 4 * (lane * nf + bb)) = pack_word(A, B);
+      }
+      if ((NHI % 32) != 0 && lane < 32) {
+        const uint64_t A = *reinterpret_cast<const uint64_t*>(lds_boost + u * boost_row(NHI) + 32 * nf + 8 * w);
+        const uint64_t B = *reinterpret_cast<const uint64_t*>(lds_boost + (16 + u) * boost_row(NHI) + 32 * nf + 8 * w);
+        *reinterpret_cast<uint32_t*>(rec + off_kboost() + 256 * nf + 4 * lane) = pack_word(A, B);
+      }
+    }
+  }
+}
+
+// The Value half of a (page, head) record: per-token steps and minima of
+// each group of 32 channels, and the 2-bit codes.  Called by a full wave;
+// uses bytes [lds_vstep(NHI), quant_lds_bytes(NHI)) of `lds`, so a Key wave
+// and a Value wave can share one area.
+template <int NHI>
+__device__ __forceinline__ void quantize_values_wave(RowSrc vs, uint8_t* __restrict__ rec, uint8_t* __restrict__ lds) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63;
+  wave_lds_sync();
+
   // ---------------- Value steps: one (token, group) per lane and pass -------
   {
     float* vstep = reinterpret_cast<float*>(lds + lds_vstep(NHI));  // [group][token] x (1 / step, min)
@@ -326,35 +366,16 @@ __device__ __forceinline__ void quantize_page_wave(RowSrc ks, RowSrc vs, uint8_t
       *reinterpret_cast<uint32_t*>(rec + off_v(NHI) + 16 * (16 * w + u) + 4 * g) = word;
     }
   }
-
-  // ---------------- Pack Key code planes from LDS ---------------------------
-  wave_lds_sync();
-  {
-    const int u = lane & 15, w = lane >> 4;
-    u32x4 words;
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const uint64_t A = *reinterpret_cast<const uint64_t*>(lds_base + u * 128 + 32 * x + 8 * w);
-      const uint64_t B = *reinterpret_cast<const uint64_t*>(lds_base + (16 + u) * 128 + 32 * x + 8 * w);
-      words[x] = pack_word(A, B);
-    }
-    *reinterpret_cast<u32x4*>(rec + 16 * lane) = words;
-    if (NHI > 0) {
-      constexpr int nf = NHI / 32;
-#pragma unroll
-      for (int bb = 0; bb < nf; ++bb) {
-        const uint64_t A = *reinterpret_cast<const uint64_t*>(lds_boost + u * boost_row(NHI) + 32 * bb + 8 * w);
-        const uint64_t B = *reinterpret_cast<const uint64_t*>(lds_boost + (16 + u) * boost_row(NHI) + 32 * bb + 8 * w);
-        *reinterpret_cast<uint32_t*>(rec + off_kboost() + 4 * (lane * nf + bb)) = pack_word(A, B);
-      }
-      if ((NHI % 32) != 0 && lane < 32) {
-        const uint64_t A = *reinterpret_cast<const uint64_t*>(lds_boost + u * boost_row(NHI) + 32 * nf + 8 * w);
-        const uint64_t B = *reinterpret_cast<const uint64_t*>(lds_boost + (16 + u) * boost_row(NHI) + 32 * nf + 8 * w);
-        *reinterpret_cast<uint32_t*>(rec + off_kboost() + 256 * nf + 4 * lane) = pack_word(A, B);
-      }
-    }
-  }
 }
+
+// Quantize and pack one (page, head) into `rec` with one wave; `lds` is this
+// wave's private quant_lds_bytes(NHI) bytes.
+template <int NHI>
+__device__ __forceinline__ void quantize_page_wave(RowSrc ks, RowSrc vs, uint8_t* __restrict__ rec, uint8_t* __restrict__ lds) {
+  quantize_keys_wave<NHI>(ks, rec, lds);
+  quantize_values_wave<NHI>(vs, rec, lds);
+}
+
 
 }  // namespace pq
 }  // namespace kitty

@@ -15,11 +15,14 @@ namespace {
 
 using namespace pq;
 
-// grid (pages + 1, Hkv, batch), one wave per block
+// grid (pages + 1, Hkv, batch), two waves per block: wave 0 quantizes the
+// page's keys, wave 1 its values (disjoint parts of one LDS area), so the
+// two halves' memory latency overlaps.
 template <int NHI>
-__global__ __launch_bounds__(64) void quantize_pages_kernel(QuantizeParams p) {
+__global__ __launch_bounds__(128) void quantize_pages_kernel(QuantizeParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[quant_lds_bytes(NHI)];
-  const int page = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+  const int page = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int n = p.lens ? p.lens[b] : p.S;
   if (n < 0) return;  // a negative length leaves sequence b as it is
   n = n > p.S ? p.S : n;
@@ -31,17 +34,21 @@ __global__ __launch_bounds__(64) void quantize_pages_kernel(QuantizeParams p) {
     if (phys < 0 || (int64_t)phys >= p.n_pages) return;
     uint8_t* rec = p.pages + (int64_t)phys * p.page_bytes + (int64_t)h * rec_bytes(NHI);
     const size_t row0 = seq_off + (size_t)page * kPageTokens * kHeadDim;
-    quantize_page_wave<NHI>(RowSrc{p.k + row0, nullptr}, RowSrc{p.v + row0, nullptr}, rec, lds);
-  } else if (page == P) {
+    if (wave == 0)
+      quantize_keys_wave<NHI>(RowSrc{p.k + row0, nullptr}, rec, lds);
+    else
+      quantize_values_wave<NHI>(RowSrc{p.v + row0, nullptr}, rec, lds);
+  } else if (page == P) {  // the tail: wave 0 copies keys, wave 1 values
     const int nt = n - P * kPageTokens;
     const size_t tail_off = ((size_t)b * p.n_kv_heads + h) * kPageTokens * kHeadDim;
+    const _Float16* src_base = wave == 0 ? p.k : p.v;
+    _Float16* dst_base = wave == 0 ? p.tail_k : p.tail_v;
     for (int t = 0; t < nt; ++t) {
       const size_t src = seq_off + ((size_t)P * kPageTokens + t) * kHeadDim + 2 * lane;
       const size_t dst = tail_off + (size_t)t * kHeadDim + 2 * lane;
-      *reinterpret_cast<uint32_t*>(p.tail_k + dst) = *reinterpret_cast<const uint32_t*>(p.k + src);
-      *reinterpret_cast<uint32_t*>(p.tail_v + dst) = *reinterpret_cast<const uint32_t*>(p.v + src);
+      *reinterpret_cast<uint32_t*>(dst_base + dst) = *reinterpret_cast<const uint32_t*>(src_base + src);
     }
-    if (h == 0 && lane == 0) p.seq_lens[b] = n;
+    if (h == 0 && threadIdx.x == 0) p.seq_lens[b] = n;
   }
 }
 
@@ -49,7 +56,7 @@ __global__ __launch_bounds__(64) void quantize_pages_kernel(QuantizeParams p) {
 // time and seals it when the tail fills; the sequence length is bumped after
 // every head of the sequence is done.
 template <int NHI>
-__global__ __launch_bounds__(1024) void append_token_kernel(AppendParams p) {
+__global__ __launch_bounds__(512) void append_token_kernel(AppendParams p) {  // at most 8 waves
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
   const int b = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nw = blockDim.x >> 6;
@@ -82,7 +89,7 @@ __global__ __launch_bounds__(1024) void append_token_kernel(AppendParams p) {
 template <int NHI>
 hipError_t launch_quantize_t(const QuantizeParams& p, hipStream_t stream) {
   dim3 grid(p.S / kPageTokens + 1, p.n_kv_heads, p.batch);
-  hipLaunchKernelGGL(quantize_pages_kernel<NHI>, grid, dim3(64), 0, stream, p);
+  hipLaunchKernelGGL(quantize_pages_kernel<NHI>, grid, dim3(128), 0, stream, p);
   return hipGetLastError();
 }
 
