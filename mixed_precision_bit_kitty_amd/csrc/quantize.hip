@@ -15,12 +15,33 @@ namespace {
 
 using namespace pq;
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Copy the 8 KB of a page's values (32 contiguous rows) into LDS with the
+// LDS DMA path, 1 KB per instruction; returns once they have landed.
+__device__ __forceinline__ void stage_value_page(const _Float16* src, uint8_t* dst, int lane) {
+  const uint8_t* s0 = reinterpret_cast<const uint8_t*>(src) + 16 * lane;
+  const uint8_t* s1 = s0 + 4096;
+  __builtin_amdgcn_global_load_lds(s0, (lds_void*)dst, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(s0, (lds_void*)dst, 16, 1024, 0);
+  __builtin_amdgcn_global_load_lds(s0, (lds_void*)dst, 16, 2048, 0);
+  __builtin_amdgcn_global_load_lds(s0, (lds_void*)dst, 16, 3072, 0);
+  __builtin_amdgcn_global_load_lds(s1, (lds_void*)(dst + 4096), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(s1, (lds_void*)(dst + 4096), 16, 1024, 0);
+  __builtin_amdgcn_global_load_lds(s1, (lds_void*)(dst + 4096), 16, 2048, 0);
+  __builtin_amdgcn_global_load_lds(s1, (lds_void*)(dst + 4096), 16, 3072, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // grid (pages + 1, Hkv, batch), two waves per block: wave 0 quantizes the
 // page's keys, wave 1 its values (disjoint parts of one LDS area), so the
-// two halves' memory latency overlaps.
+// two halves' memory latency overlaps.  The value wave first stages its
+// page in LDS, so the per-token steps and the per-channel codes read it
+// from there rather than from global memory twice.
 template <int NHI>
 __global__ __launch_bounds__(128) void quantize_pages_kernel(QuantizeParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[quant_lds_bytes(NHI)];
+  constexpr int kVStage = quant_lds_bytes(NHI);  // the value page: 32 x 128 fp16
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kVStage + kPageTokens * kHeadDim * 2];
   const int page = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int n = p.lens ? p.lens[b] : p.S;
@@ -34,10 +55,12 @@ __global__ __launch_bounds__(128) void quantize_pages_kernel(QuantizeParams p) {
     if (phys < 0 || (int64_t)phys >= p.n_pages) return;
     uint8_t* rec = p.pages + (int64_t)phys * p.page_bytes + (int64_t)h * rec_bytes(NHI);
     const size_t row0 = seq_off + (size_t)page * kPageTokens * kHeadDim;
-    if (wave == 0)
+    if (wave == 0) {
       quantize_keys_wave<NHI>(RowSrc{p.k + row0, nullptr}, rec, lds);
-    else
-      quantize_values_wave<NHI>(RowSrc{p.v + row0, nullptr}, rec, lds);
+    } else {
+      stage_value_page(p.v + row0, lds + kVStage, lane);
+      quantize_values_wave<NHI>(RowSrc{reinterpret_cast<const _Float16*>(lds + kVStage), nullptr}, rec, lds);
+    }
   } else if (page == P) {  // the tail: wave 0 copies keys, wave 1 values
     const int nt = n - P * kPageTokens;
     const size_t tail_off = ((size_t)b * p.n_kv_heads + h) * kPageTokens * kHeadDim;
