@@ -55,19 +55,24 @@ def kv_bytes(seq_lens, n_kv_heads, record_bytes):
     return tot
 
 
-def source_hash():
+DECODE_SOURCES = ("decode.hip", "kitty_internal.h")
+QUANTIZE_SOURCES = ("quantize.hip", "page_quant.h", "kitty_internal.h")
+
+
+def source_hash(files=DECODE_SOURCES):
     h = hashlib.sha256()
-    for f in ("decode.hip", "kitty_internal.h"):
+    for f in files:
         with open(os.path.join(ROOT, "mixed_precision_bit_kitty_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def committed_traffic(kernel_hash, workload, entry):
-    """HBM bytes per decode launch from the committed rocprofv3 counter
-    summary of that entry point ("step" or "attention") on this workload, if
-    it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"decode_kernel_{entry}_{workload}_hbm_counters.json")
+def committed_traffic(kernel_hash, workload, entry, kernel="decode_kernel"):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    that kernel and entry point (decode: "step" or "attention") on this
+    workload, if it was taken on the current kernel source; else None."""
+    name = f"{kernel}_{entry}_{workload}" if entry else f"{kernel}_{workload}"
+    path = os.path.join(ROOT, "profiles", f"{name}_hbm_counters.json")
     try:
         with open(path) as f:
             d = json.load(f)
@@ -151,14 +156,24 @@ def bench_quantize(args, w):
     gbs = alg / (ms * 1e-3) / 1e9
     print(f"[bench] quantize_pages {ms * 1e3:.2f} us ({gbs:.0f} GB/s, {gbs / HBM_PEAK_GBS:.3f} of peak), "
           f"{R} input copies", file=sys.stderr, flush=True)
+    if args.calibrate_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        bcopy = torch.empty_like(a)
+        bcopy.copy_(a)
+        torch.cuda.synchronize()
+        print("[bench] calibration copy: 1 GiB read + 1 GiB written", file=sys.stderr, flush=True)
+        del a, bcopy
+    khash = source_hash(QUANTIZE_SOURCES)
     res = {"metric": "kitty_quantize_pages: GB/s of fp16 K/V read + page records written", "value": round(gbs, 1),
            "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": R, "ms_per_step": round(ms, 6),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
            "config": {"workload": f"{w.name}: prefill of batch {B}, {Hkv} KV heads, {S} tokens, n_hi {w.n_hi}",
                       "batch": B, "ctx": S, "n_kv_heads": Hkv, "n_hi": w.n_hi, "input_copies": R},
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "quantize_pages_kernel",
-                        "bytes_per_launch": int(alg), "avg_launch_us": round(ms * 1e3, 3)}}
+                        "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "traffic": committed_traffic(khash, args.workload, None, "quantize_pages_kernel"),
+                        "kernel": "quantize_pages_kernel", "bytes_per_launch": int(alg),
+                        "avg_launch_us": round(ms * 1e3, 3), "kernel_source_sha256_16": khash}}
     print(json.dumps(res), flush=True)
 
 
@@ -321,7 +336,7 @@ def main():
         print("[bench] calibration copy: 1 GiB read + 1 GiB written", file=sys.stderr, flush=True)
         del a, bcopy
 
-    khash = source_hash()
+    khash = source_hash(DECODE_SOURCES)
     roof = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": committed_traffic(khash, args.workload, "attention" if args.split else "step"),
             "kernel": kernel,
