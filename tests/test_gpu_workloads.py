@@ -87,6 +87,34 @@ def test_qwen3_8b_long_context_with_appends():
     compare_records(cache, oc, samples=sealed, seq_map={0: b})
 
 
+def test_llama3_8b_fused_steps_across_a_seal():
+    """The bench's path at its full size: batch 16 at 4096 tokens, 40 fused
+    steps in the launch configuration bench.py uses (the bound is the
+    longest length reached), across the seal of page 128 (token 4127)."""
+    import torch
+    w = synth.LLAMA3_8B
+    steps = 40
+    x, cache = _gpu_prefill(w, w.n_hi, steps=steps)
+    b = int(np.random.default_rng(104).integers(w.batch))
+    oc = _oracle_seq(x, b, w.n_hi)
+    msl = w.ctx + steps + 1
+    out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device="cuda")
+    ws = cache.workspace(w.n_q_heads, msl)
+    for t in range(steps):
+        cache.decode_step(dev(x["k_new"][t]), dev(x["v_new"][t]), dev(x["q_new"][t]), max_seq_len=msl,
+                          out=out, workspace=ws)
+        O.append_token(oc, x["k_new"][t][b:b + 1], x["v_new"][t][b:b + 1])
+        if t in (0, 30, 31, 32, steps - 1):
+            ref = O.decode_attention(oc, x["q_new"][t][b:b + 1])[0]
+            err = float(np.abs(host(out)[b] - ref).max())
+            assert err <= 2e-3, (t, err)
+            _say(f"llama3_8b fused step {t} (length {w.ctx + t + 1}), seq {b}: max abs err {err:.3g}")
+    compare_tails(cache, oc, seq_map={0: b})
+    sealed = [(0, 128, h) for h in range(w.n_kv_heads)]  # tokens 4096..4127, sealed by step 31
+    compare_records(cache, oc, samples=sealed, seq_map={0: b})
+    assert (host(cache.seq_lens) == w.ctx + steps).all()
+
+
 def _decode_prefix(cache, bp, q, n_q_heads, msl):
     """Decode attention on sequences 0..bp-1 of `cache` (a prefix view of the
     same pool, block table, tails and lengths)."""
