@@ -220,7 +220,8 @@ def dequant_v(a, vscale, vmin):
 #            combo B element e = token 16 + u, channel 32x + 8w + e
 #   V codes: combo A element e = token tau(w, e), channel 16*(2x) + u
 #            combo B element e = token tau(w, e), channel 16*(2x+1) + u
-# with tau(w, e) = 4w + e for e < 4, else 16 + 4w + (e - 4).
+# with tau(w, e) = 4w + e // 2 + 16 * (e % 2): value index kappa = 8w + e holds
+# token kappa // 2 + 16 * (kappa % 2) (see ``tau``).
 #
 # K boost: nf = n // 32 full slot blocks, then, if n % 32 == 16, one half
 # block.  Full block b of chunk c (c = 0..63) is the word at byte 4*(c*nf+b):
