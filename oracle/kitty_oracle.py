@@ -14,7 +14,10 @@ Sources, cited by name throughout:
   (per-channel variance over the token axis, top hi_fraction x D channels at
   hi_bit = 4, the rest at lo_bit = 2, asymmetric min/max groups of
   group_size = 32 tokens), section "Effective bit-width" (avg_bits formula),
-  table "Tuning avg_bits".
+  table "Tuning avg_bits".  Two bit-width pairs are built: (hi_bit, lo_bit)
+  = (4, 2), the default, and (8, 4), the table's last row; ``lo_bit`` names
+  the pair (hi_bit = 2 lo_bit, so a boosted code splits into two lo_bit
+  planes exactly like the default's).
 
 Arithmetic conventions (readings of points the pages leave open):
 
@@ -39,6 +42,14 @@ PAGE_TOKENS = 32        # tokens per page = Key group size ([Velox] group_size)
 V_GROUP = 32            # channels per Value group (one fp16 scale/min each)
 LO_LEVELS = 3           # 2-bit codes 0..3 ([Velox] lo_bit = 2)
 HI_LEVELS = 15          # 4-bit codes 0..15 ([Velox] hi_bit = 4)
+LO_BITS = (2, 4)        # supported lo_bit; hi_bit = 2 * lo_bit ("Tuning avg_bits": (4, 2) and (8, 4))
+
+
+def levels(lo_bit):
+    """(lo, hi) level counts of a bit-width pair: 2^lo_bit - 1, 2^(2 lo_bit) - 1."""
+    if lo_bit not in LO_BITS:
+        raise ValueError("lo_bit must be 2 or 4")
+    return (1 << lo_bit) - 1, (1 << (2 * lo_bit)) - 1
 
 _F32 = np.float32
 _F16 = np.float16
@@ -127,58 +138,63 @@ def quantize_levels(x, mn, mx, levels):
     return q, np.broadcast_to(s16, np.broadcast_shapes(s16.shape, mn.shape)).astype(_F16)
 
 
-def quant_k_page(k16, n_hi):
-    """Quantize Key pages.  k16: fp16 [..., 32, D]; n_hi boosted channels.
+def quant_k_page(k16, n_hi, lo_bit=2):
+    """Quantize Key pages.  k16: fp16 [..., 32, D]; n_hi boosted channels;
+    lo_bit 2 (hi_bit 4) or 4 (hi_bit 8).
 
-    Returns a dict with the direct codes ``q`` (4-bit on boosted channels,
-    2-bit elsewhere) and the two uniform 2-bit tensors of the decomposition
-    ([Kitty] Abstract): ``base`` [..., 32, D] = q >> 2 on boosted channels, q
-    elsewhere; ``boost`` [..., 32, n_hi] = the low 2 bits of q on the boosted
-    channels listed by ``idx``; ``kscale`` [..., D] fp16 = 4 * step on boosted
-    channels, step elsewhere; ``kmin`` [..., D] fp16."""
+    Returns a dict with the direct codes ``q`` (hi_bit on boosted channels,
+    lo_bit elsewhere) and the two uniform lo_bit tensors of the decomposition
+    ([Kitty] Abstract): ``base`` [..., 32, D] = q >> lo_bit on boosted
+    channels, q elsewhere; ``boost`` [..., 32, n_hi] = the low lo_bit bits of
+    q on the boosted channels listed by ``idx``; ``kscale`` [..., D] fp16 =
+    2^lo_bit * step on boosted channels, step elsewhere; ``kmin`` [..., D]
+    fp16."""
+    lo_l, hi_l = levels(lo_bit)
     x = f32_stat(k16)
     _, m2, mn, mx = page_stats(x)
     idx, mask = rank_channels(m2, n_hi)
-    levels = np.where(mask, HI_LEVELS, LO_LEVELS)
-    q, s16 = quantize_levels(x, mn[..., None, :], mx[..., None, :], levels[..., None, :])
+    lv = np.where(mask, hi_l, lo_l)
+    q, s16 = quantize_levels(x, mn[..., None, :], mx[..., None, :], lv[..., None, :])
     s16 = s16[..., 0, :]
-    base = np.where(mask[..., None, :], q >> 2, q).astype(np.uint8)
+    base = np.where(mask[..., None, :], q >> lo_bit, q).astype(np.uint8)
     gather = np.broadcast_to(idx[..., None, :].astype(np.intp), q.shape[:-1] + (n_hi,))
-    boost = (np.take_along_axis(q, gather, axis=-1) & 3).astype(np.uint8)
-    with np.errstate(over="ignore"):   # 4 * step is only kept where it fits (boosted channels)
-        kscale = np.where(mask, f16(f32(s16) * _F32(4.0)), s16).astype(_F16)
+    boost = (np.take_along_axis(q, gather, axis=-1) & lo_l).astype(np.uint8)
+    with np.errstate(over="ignore"):   # 2^lo_bit * step is only kept where it fits (boosted channels)
+        kscale = np.where(mask, f16(f32(s16) * _F32(1 << lo_bit)), s16).astype(_F16)
     kmin = f16(mn)
     return dict(q=q, m2=m2, mask=mask, idx=idx, step=s16, base=base, boost=boost,
-                kscale=kscale, kmin=kmin)
+                kscale=kscale, kmin=kmin, lo_bit=lo_bit)
 
 
-def quant_v_page(v16):
-    """Quantize Value pages: per token, groups of 32 channels, 2-bit
+def quant_v_page(v16, lo_bit=2):
+    """Quantize Value pages: per token, groups of 32 channels, lo_bit
     asymmetric min/max.  v16: fp16 [..., 32, D].  Returns dict with ``a``
     [..., 32, D] codes, ``vscale``/``vmin`` [..., 32, D/32] fp16."""
+    lo_l, _ = levels(lo_bit)
     y = f32_stat(v16)
     shp = y.shape
     yg = y.reshape(shp[:-1] + (shp[-1] // V_GROUP, V_GROUP))
     mn = yg.min(axis=-1)
     mx = yg.max(axis=-1)
-    a, s16 = quantize_levels(yg, mn[..., None], mx[..., None], LO_LEVELS)
+    a, s16 = quantize_levels(yg, mn[..., None], mx[..., None], lo_l)
     return dict(a=a.reshape(shp), vscale=s16[..., 0], vmin=f16(mn))
 
 
-def dequant_k(base, boost, kscale, kmin, idx):
+def dequant_k(base, boost, kscale, kmin, idx, lo_bit=2):
     """Dequantized keys k^ [..., 32, D] float32: on boosted channels the full
-    code is 4*base + boost at step kscale/4, elsewhere base at step kscale;
-    k^ = f32(code * step + kmin) (the product is exact, one rounding)."""
+    code is 2^lo_bit * base + boost at step kscale / 2^lo_bit, elsewhere base
+    at step kscale; k^ = f32(code * step + kmin) (one rounding)."""
     n_hi = idx.shape[-1]
+    scale = 1 << lo_bit
     qfull = base.astype(np.int32)
     mask = np.zeros(kscale.shape, bool)
     if n_hi:
         gi = np.broadcast_to(idx[..., None, :].astype(np.intp), base.shape[:-1] + (n_hi,))
         hi_base = np.take_along_axis(qfull, gi, axis=-1)
-        np.put_along_axis(qfull, gi, 4 * hi_base + boost.astype(np.int32), axis=-1)
+        np.put_along_axis(qfull, gi, scale * hi_base + boost.astype(np.int32), axis=-1)
         np.put_along_axis(mask, idx.astype(np.intp), True, axis=-1)
     ks = f32(kscale)
-    s_eff = np.where(mask, (ks * _F32(0.25)).astype(_F32), ks).astype(_F32)
+    s_eff = np.where(mask, (ks * _F32(1.0 / scale)).astype(_F32), ks).astype(_F32)
     prod = (qfull.astype(_F32) * s_eff[..., None, :]).astype(_F32)
     return (prod + f32(kmin)[..., None, :]).astype(_F32)
 
@@ -223,6 +239,15 @@ def dequant_v(a, vscale, vmin):
 # with tau(w, e) = 4w + e // 2 + 16 * (e % 2): value index kappa = 8w + e holds
 # token kappa // 2 + 16 * (kappa % 2) (see ``tau``).
 #
+# The (8, 4) pair (lo_bit 4) uses 4-bit planes of the same shape: a word
+# holds one combo of 8 elements, element e at bits 16*(e%2) + 4*(e//2), and
+# a chunk has twice the words, combo A at word 2x and combo B at word 2x + 1
+# (byte 32c + 4(2x + combo)), with the same tokens and channels as above.
+# The boost plane has two words per lane and slot block (byte 8(c*nf + b) +
+# 4*combo; a half block at byte 512 nf + 8c + 4*combo for c < 32).  Field
+# sizes: K base 2048 B, K boost 16n B, V codes 2048 B, then the same metadata
+# and idx: 5120 + 17n bytes.
+#
 # K boost: nf = n // 32 full slot blocks, then, if n % 32 == 16, one half
 # block.  Full block b of chunk c (c = 0..63) is the word at byte 4*(c*nf+b):
 # combo A element e = token u, slot 32b + 8w + e; combo B = token 16 + u.
@@ -231,17 +256,18 @@ def dequant_v(a, vscale, vmin):
 #
 # Value metadata index kappa = 8w + e stands for token tau(w, e).
 
-def record_bytes(n_hi, head_dim=HEAD_DIM):
+def record_bytes(n_hi, head_dim=HEAD_DIM, lo_bit=2):
     if head_dim != HEAD_DIM:
         raise ValueError("the record layout is defined for head_dim 128")
     if n_hi < 0 or n_hi > head_dim or n_hi % 16:
         raise ValueError("n_hi must be 0 or a multiple of 16 up to head_dim")
-    return 3072 + 9 * n_hi
+    levels(lo_bit)
+    return 1024 * lo_bit + 4 * lo_bit * n_hi + 1024 + n_hi
 
 
-def page_bytes(n_kv_heads, n_hi):
+def page_bytes(n_kv_heads, n_hi, lo_bit=2):
     """Bytes of one physical page (all KV heads), padded to 256."""
-    raw = n_kv_heads * record_bytes(n_hi)
+    raw = n_kv_heads * record_bytes(n_hi, lo_bit=lo_bit)
     return (raw + 255) // 256 * 256
 
 
@@ -283,6 +309,25 @@ _W = _C // 16
 _E = np.arange(8)
 
 
+def _word4(a8):
+    """Pack one combo a8 ([..., 8] codes 0..15) into uint32 words: element e
+    at bits 16*(e%2) + 4*(e//2)."""
+    a8 = np.asarray(a8, np.uint32)
+    w = np.zeros(a8.shape[:-1], np.uint32)
+    for e in range(8):
+        w |= (a8[..., e] & 15) << np.uint32(16 * (e % 2) + 4 * (e // 2))
+    return w
+
+
+def _unword4(w):
+    """Inverse of _word4: uint32 [...] -> uint8 [..., 8]."""
+    w = np.asarray(w, np.uint32)
+    a8 = np.zeros(w.shape + (8,), np.uint8)
+    for e in range(8):
+        a8[..., e] = (w >> np.uint32(16 * (e % 2) + 4 * (e // 2))) & 15
+    return a8
+
+
 def _kbase_index():
     # [chunk, x, e] -> (token A, token B, channel)
     ch = 32 * np.arange(4)[None, :, None] + 8 * _W[:, None, None] + _E[None, None, :]
@@ -322,26 +367,69 @@ def _kappa_tokens():
     return tau(kap // 8, kap % 8)
 
 
+def _put_plane(out, o, codesA, codesB, lo_bit):
+    """Write a 64-chunk code plane at byte o: codesA/codesB [64, 4, 8] (chunk,
+    word x, element) -> 2-bit words (16 B per chunk) or 4-bit word pairs
+    (32 B per chunk)."""
+    if lo_bit == 2:
+        words = _word(codesA, codesB)                                # [64, 4]
+    else:
+        words = np.stack([_word4(codesA), _word4(codesB)], axis=-1)  # [64, 4, 2]
+    raw = words.reshape(-1).astype("<u4").view(np.uint8)
+    out[o:o + raw.size] = raw
+    return o + raw.size
+
+
+def _get_plane(buf, o, lo_bit):
+    """Inverse of _put_plane: (codesA, codesB) [64, 4, 8] and the next offset."""
+    if lo_bit == 2:
+        n = 1024
+        a8, b8 = _unword(buf[o:o + n].view("<u4").reshape(64, 4))
+    else:
+        n = 2048
+        ws = buf[o:o + n].view("<u4").reshape(64, 4, 2)
+        a8, b8 = _unword4(ws[..., 0]), _unword4(ws[..., 1])
+    return a8, b8, o + n
+
+
+def _boost_offsets(n_hi, lo_bit):
+    """Byte offsets (within the boost plane) of the words of _boost_slots:
+    (combo A offsets, combo B offsets); equal for the 2-bit planes, whose
+    words hold both combos."""
+    offs, _, _, _ = _boost_slots(n_hi)
+    if lo_bit == 2:
+        return offs, offs
+    nf = n_hi // 32
+    # 2-bit byte 4*(c*nf + b) -> 4-bit byte 8*(c*nf + b); half block 256nf + 4c -> 512nf + 8c
+    o2 = np.asarray(offs)
+    oA = np.where(o2 < 256 * nf, 2 * o2, 512 * nf + 2 * (o2 - 256 * nf)) if len(o2) else o2
+    return oA, oA + 4
+
+
 def pack_record(kf, vf):
-    """Bytes of one page record (uint8 [3072 + 9n]) from the logical fields
-    of quant_k_page / quant_v_page for a single page (no leading dims)."""
+    """Bytes of one page record (uint8 [record_bytes]) from the logical fields
+    of quant_k_page / quant_v_page for a single page (no leading dims); the
+    bit-width pair is kf["lo_bit"] (2 if absent)."""
     n_hi = kf["idx"].shape[-1]
-    out = np.zeros(record_bytes(n_hi), np.uint8)
+    lo_bit = int(kf.get("lo_bit", 2))
+    out = np.zeros(record_bytes(n_hi, lo_bit=lo_bit), np.uint8)
     base, boost, a = kf["base"], kf["boost"], vf["a"]
     tA, tB, ch = _kbase_index()
-    words = _word(base[tA, ch], base[tB, ch])                       # [64, 4]
-    out[0:1024] = words.reshape(-1).astype("<u4").view(np.uint8)
-    o = 1024
+    o = _put_plane(out, 0, base[tA, ch], base[tB, ch], lo_bit)
     offs, bA, bB, sl = _boost_slots(n_hi)
     if len(offs):
-        bw = _word(boost[bA, sl], boost[bB, sl])
-        for off, wv in zip(offs, bw):
-            out[o + off:o + off + 4] = np.array([wv], "<u4").view(np.uint8)
-    o += 8 * n_hi
+        oA, oB = _boost_offsets(n_hi, lo_bit)
+        if lo_bit == 2:
+            bw = _word(boost[bA, sl], boost[bB, sl])
+            for off, wv in zip(oA, bw):
+                out[o + off:o + off + 4] = np.array([wv], "<u4").view(np.uint8)
+        else:
+            for offa, offb, wa, wb in zip(oA, oB, _word4(boost[bA, sl]), _word4(boost[bB, sl])):
+                out[o + offa:o + offa + 4] = np.array([wa], "<u4").view(np.uint8)
+                out[o + offb:o + offb + 4] = np.array([wb], "<u4").view(np.uint8)
+    o += 4 * lo_bit * n_hi
     tok, cA, cB = _vcode_index()
-    vw = _word(a[tok, cA], a[tok, cB])
-    out[o:o + 1024] = vw.reshape(-1).astype("<u4").view(np.uint8)
-    o += 1024
+    o = _put_plane(out, o, a[tok, cA], a[tok, cB], lo_bit)
     for arr in (kf["kscale"], kf["kmin"]):
         out[o:o + 256] = np.asarray(arr, "<f2").view(np.uint8)
         o += 256
@@ -353,31 +441,34 @@ def pack_record(kf, vf):
     return out
 
 
-def unpack_record(buf, n_hi):
+def unpack_record(buf, n_hi, lo_bit=2):
     """Inverse of pack_record: logical fields from one record's bytes."""
     buf = np.asarray(buf, np.uint8)
-    if buf.shape[0] != record_bytes(n_hi):
+    if buf.shape[0] != record_bytes(n_hi, lo_bit=lo_bit):
         raise ValueError("record size mismatch")
     base = np.zeros((PAGE_TOKENS, HEAD_DIM), np.uint8)
     tA, tB, ch = _kbase_index()
-    a8, b8 = _unword(buf[0:1024].view("<u4").reshape(64, 4))
+    a8, b8, o = _get_plane(buf, 0, lo_bit)
     base[tA, ch] = a8
     base[tB, ch] = b8
-    o = 1024
     boost = np.zeros((PAGE_TOKENS, n_hi), np.uint8)
     offs, bA, bB, sl = _boost_slots(n_hi)
     if len(offs):
-        ws = np.array([buf[o + off:o + off + 4].view("<u4")[0] for off in offs], np.uint32)
-        a8, b8 = _unword(ws)
+        oA, oB = _boost_offsets(n_hi, lo_bit)
+        wA = np.array([buf[o + off:o + off + 4].view("<u4")[0] for off in oA], np.uint32)
+        if lo_bit == 2:
+            a8, b8 = _unword(wA)
+        else:
+            wB = np.array([buf[o + off:o + off + 4].view("<u4")[0] for off in oB], np.uint32)
+            a8, b8 = _unword4(wA), _unword4(wB)
         boost[bA, sl] = a8
         boost[bB, sl] = b8
-    o += 8 * n_hi
+    o += 4 * lo_bit * n_hi
     a = np.zeros((PAGE_TOKENS, HEAD_DIM), np.uint8)
     tok, cA, cB = _vcode_index()
-    a8, b8 = _unword(buf[o:o + 1024].view("<u4").reshape(64, 4))
+    a8, b8, o = _get_plane(buf, o, lo_bit)
     a[tok, cA] = a8
     a[tok, cB] = b8
-    o += 1024
     kscale = buf[o:o + 256].view("<f2").astype(_F16)
     kmin = buf[o + 256:o + 512].view("<f2").astype(_F16)
     o += 512
@@ -388,7 +479,8 @@ def unpack_record(buf, n_hi):
     vm[kt, :] = buf[o + 256:o + 512].view("<f2").reshape(4, 32).T
     o += 512
     idx = buf[o:o + n_hi].copy()
-    return dict(base=base, boost=boost, kscale=kscale, kmin=kmin, idx=idx), dict(a=a, vscale=vs, vmin=vm)
+    return (dict(base=base, boost=boost, kscale=kscale, kmin=kmin, idx=idx, lo_bit=lo_bit),
+            dict(a=a, vscale=vs, vmin=vm))
 
 
 # --------------------------------------------------------------------------
@@ -401,9 +493,10 @@ class OracleCache:
     head ([Kitty] Abstract: page-centric layout; the incomplete tail page
     stays fp16 until it fills)."""
 
-    def __init__(self, batch, n_kv_heads, n_hi, head_dim=HEAD_DIM):
-        record_bytes(n_hi, head_dim)
+    def __init__(self, batch, n_kv_heads, n_hi, head_dim=HEAD_DIM, lo_bit=2):
+        record_bytes(n_hi, head_dim, lo_bit)
         self.batch, self.n_kv_heads, self.n_hi, self.head_dim = batch, n_kv_heads, n_hi, head_dim
+        self.lo_bit = lo_bit
         self.k = [None] * batch      # dict of arrays [Hkv, P, ...]
         self.v = [None] * batch
         self.tail_k = np.zeros((batch, n_kv_heads, PAGE_TOKENS, head_dim), _F16)
@@ -414,8 +507,8 @@ class OracleCache:
         return int(self.seq_len[b]) // PAGE_TOKENS
 
     def _add_pages(self, b, k16, v16):
-        kf = quant_k_page(k16, self.n_hi)
-        vf = quant_v_page(v16)
+        kf = quant_k_page(k16, self.n_hi, self.lo_bit)
+        vf = quant_v_page(v16, self.lo_bit)
         kf = {key: kf[key] for key in ("base", "boost", "kscale", "kmin", "idx", "q", "mask")}
         if self.k[b] is None:
             self.k[b], self.v[b] = kf, vf
@@ -425,6 +518,7 @@ class OracleCache:
 
     def page_fields(self, b, h, p):
         kf = {key: self.k[b][key][h, p] for key in ("base", "boost", "kscale", "kmin", "idx")}
+        kf["lo_bit"] = self.lo_bit
         vf = {key: self.v[b][key][h, p] for key in ("a", "vscale", "vmin")}
         return kf, vf
 
@@ -438,7 +532,7 @@ class OracleCache:
         if P:
             kf, vf = self.k[b], self.v[b]
             kh = dequant_k(kf["base"][:, :P], kf["boost"][:, :P], kf["kscale"][:, :P],
-                           kf["kmin"][:, :P], kf["idx"][:, :P])
+                           kf["kmin"][:, :P], kf["idx"][:, :P], self.lo_bit)
             vh = dequant_v(vf["a"][:, :P], vf["vscale"][:, :P], vf["vmin"][:, :P])
             ks.append(kh.reshape(H, P * PAGE_TOKENS, D))
             vs.append(vh.reshape(H, P * PAGE_TOKENS, D))
@@ -447,13 +541,14 @@ class OracleCache:
         return np.concatenate(ks, axis=1), np.concatenate(vs, axis=1)
 
 
-def quantize_pages(k, v, n_hi, batch_lens=None):
+def quantize_pages(k, v, n_hi, batch_lens=None, lo_bit=2):
     """Prefill: split fp16 k, v [B, Hkv, S, D] into P = floor(S/32) sealed
     pages and an fp16 tail of S mod 32 tokens ([Velox] Prefill steps 1-3 per
     page of group_size tokens).  ``batch_lens`` (optional, per sequence)
-    quantizes only the first len_b tokens of sequence b."""
+    quantizes only the first len_b tokens of sequence b; ``lo_bit`` picks the
+    bit-width pair (2: hi 4 / lo 2, 4: hi 8 / lo 4)."""
     B, H, S, D = k.shape
-    cache = OracleCache(B, H, n_hi, D)
+    cache = OracleCache(B, H, n_hi, D, lo_bit)
     for b in range(B):
         n = S if batch_lens is None else int(batch_lens[b])
         P = n // PAGE_TOKENS
@@ -550,10 +645,11 @@ def decode_attention(cache, q, precision="f32", heads=None):
     return out
 
 
-def avg_code_bits(n_hi, head_dim=HEAD_DIM):
-    """Code bits per Key element of a page record: the base plane's 2 bits on
-    every channel plus the boost plane's 2 bits on n_hi channels, counted
-    from the record layout's plane sizes (metadata excluded)."""
-    base_bits = 1024 * 8
-    boost_bits = 8 * n_hi * 8
+def avg_code_bits(n_hi, head_dim=HEAD_DIM, lo_bit=2):
+    """Code bits per Key element of a page record: the base plane's lo_bit
+    bits on every channel plus the boost plane's lo_bit bits on n_hi
+    channels, counted from the record layout's plane sizes (metadata
+    excluded)."""
+    base_bits = 512 * lo_bit * 8
+    boost_bits = 4 * lo_bit * n_hi * 8
     return (base_bits + boost_bits) / (PAGE_TOKENS * head_dim)
