@@ -40,36 +40,43 @@
 extern "C" {
 #endif
 
-#define KITTY_ABI_VERSION 1
+#define KITTY_ABI_VERSION 2
 
 enum {
   KITTY_OK = 0,
   KITTY_ERR_INVALID_ARG = -1, /* null pointer, negative/inconsistent size, misalignment */
-  KITTY_ERR_UNSUPPORTED = -2, /* head_dim != 128, page_tokens != 32, bad n_hi, ... */
+  KITTY_ERR_UNSUPPORTED = -2, /* head_dim != 128, page_tokens != 32, bad n_hi or lo_bit */
   KITTY_ERR_WORKSPACE = -3,   /* workspace smaller than kitty_decode_workspace_bytes */
   KITTY_ERR_HIP = -4,         /* a kernel launch failed (hipGetLastError) */
   KITTY_ERR_NO_PAGES = -5     /* kitty_pool_reserve: the pool has too few free pages */
 };
 
 /* Cache geometry ("Configuration reference": head_dim, group_size,
- * hi_fraction; n_hi = hi_fraction * head_dim rounded half to even). */
+ * hi_fraction, hi_bit, lo_bit; n_hi = hi_fraction * head_dim rounded half to
+ * even).  Two bit-width pairs are supported, the two ends of the table
+ * "Tuning avg_bits": (hi_bit, lo_bit) = (4, 2), the default, and (8, 4).  A
+ * boosted Key code of hi_bit = 2 * lo_bit bits is stored as two lo_bit codes
+ * (base = high half, boost = low half); Values use lo_bit. */
 typedef struct {
   int32_t head_dim;    /* D; must be 128 */
   int32_t page_tokens; /* tokens per page = Key group size; must be 32 */
   int32_t n_kv_heads;  /* Hkv, 1..1024 */
-  int32_t n_hi;        /* boosted (4-bit) channels per page: 0 or a multiple of 16, <= D */
+  int32_t n_hi;        /* boosted channels per page: 0 or a multiple of 16, <= D */
+  int32_t lo_bit;      /* 2 (hi_bit 4) or 4 (hi_bit 8) */
 } kitty_config_t;
 
 /* A paged cache (Abstract: page-centric KV layout).  One physical page holds
  * the records of all Hkv heads for 32 consecutive tokens of one sequence; the
  * block table maps (sequence b, logical page j) to a physical page id.
- * Record layout of one (page, head): K base plane 1024 B, K boost plane 8*n_hi
- * B, V codes 1024 B, kscale fp16[128], kmin fp16[128], vscale fp16[4][32],
- * vmin fp16[4][32], idx uint8[n_hi] -- 3072 + 9*n_hi bytes in total.  The
- * code planes are 16-byte chunks, one per lane of a 64-lane wave, each holding
- * four 32-bit words of sixteen 2-bit codes (the chunk and bit placement is the
- * one internal header kitty_internal.h documents).  Head h's record starts at
- * byte h * kitty_record_bytes; a physical page is kitty_page_bytes long. */
+ * Record layout of one (page, head), with b = lo_bit: K base plane 512*b B,
+ * K boost plane 4*b*n_hi B, V codes 512*b B, kscale fp16[128], kmin
+ * fp16[128], vscale fp16[4][32], vmin fp16[4][32], idx uint8[n_hi] --
+ * 1024*(b + 1) + (4*b + 1)*n_hi bytes in total (3072 + 9*n_hi at lo_bit 2,
+ * 5120 + 17*n_hi at lo_bit 4).  The code planes are 16*b-byte chunks, one per
+ * lane of a 64-lane wave, of 32-bit words of 32/b codes each (the chunk and
+ * bit placement is the one internal header kitty_internal.h documents).  Head
+ * h's record starts at byte h * kitty_record_bytes; a physical page is
+ * kitty_page_bytes long. */
 typedef struct {
   void* pages;                /* device; n_pages * page_bytes bytes, 256-byte aligned */
   int64_t n_pages;            /* physical pages in the pool, >= 1 */
@@ -87,7 +94,7 @@ int kitty_abi_version(void);
 /* Message for the last non-zero return on this thread ("" if none). */
 const char* kitty_last_error(void);
 
-/* Bytes of one (page, head) record: 3072 + 9 * n_hi. */
+/* Bytes of one (page, head) record: 1024 * (lo_bit + 1) + (4 * lo_bit + 1) * n_hi. */
 int kitty_record_bytes(const kitty_config_t* cfg, size_t* out);
 
 /* Bytes of one physical page: n_kv_heads records, rounded up to 256. */

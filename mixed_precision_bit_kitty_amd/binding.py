@@ -38,7 +38,7 @@ class KittyError(RuntimeError):
 
 class kitty_config_t(ctypes.Structure):
     _fields_ = [("head_dim", ctypes.c_int32), ("page_tokens", ctypes.c_int32),
-                ("n_kv_heads", ctypes.c_int32), ("n_hi", ctypes.c_int32)]
+                ("n_kv_heads", ctypes.c_int32), ("n_hi", ctypes.c_int32), ("lo_bit", ctypes.c_int32)]
 
 
 class kitty_kv_view_t(ctypes.Structure):
@@ -106,8 +106,9 @@ def _check(rc):
         raise KittyError(rc, load().kitty_last_error().decode())
 
 
-def config(n_kv_heads, n_hi, head_dim=HEAD_DIM, page_tokens=PAGE_TOKENS):
-    return kitty_config_t(head_dim, page_tokens, n_kv_heads, n_hi)
+def config(n_kv_heads, n_hi, head_dim=HEAD_DIM, page_tokens=PAGE_TOKENS, lo_bit=2):
+    """lo_bit 2: (hi_bit 4, lo_bit 2); lo_bit 4: (hi_bit 8, lo_bit 4)."""
+    return kitty_config_t(head_dim, page_tokens, n_kv_heads, n_hi, lo_bit)
 
 
 def kitty_abi_version():
@@ -219,10 +220,11 @@ class KittyCache:
     seq_lens    int32 [batch]
     """
 
-    def __init__(self, batch, n_kv_heads, n_hi, max_tokens, device="cuda", block_table=None, n_pages=None):
+    def __init__(self, batch, n_kv_heads, n_hi, max_tokens, device="cuda", block_table=None, n_pages=None,
+                 lo_bit=2):
         import torch
-        self.cfg = config(n_kv_heads, n_hi)
-        self.batch, self.n_kv_heads, self.n_hi = batch, n_kv_heads, n_hi
+        self.cfg = config(n_kv_heads, n_hi, lo_bit=lo_bit)
+        self.batch, self.n_kv_heads, self.n_hi, self.lo_bit = batch, n_kv_heads, n_hi, lo_bit
         self.max_pages = max(1, -(-max_tokens // PAGE_TOKENS))
         self.page_bytes = kitty_page_bytes(self.cfg)
         self.record_bytes = kitty_record_bytes(self.cfg)
@@ -248,13 +250,13 @@ class KittyCache:
         self._ws = None
 
     @classmethod
-    def with_pool(cls, batch, n_kv_heads, n_hi, max_tokens, n_pages, device="cuda"):
+    def with_pool(cls, batch, n_kv_heads, n_hi, max_tokens, n_pages, device="cuda", lo_bit=2):
         """A serving cache: every slot starts inactive (seq_lens -1, no page
         mapped) and pages come from a shared PagePool of n_pages pages."""
         import numpy as np
         max_pages = max(1, -(-max_tokens // PAGE_TOKENS))
         c = cls(batch, n_kv_heads, n_hi, max_tokens, device=device,
-                block_table=np.full((batch, max_pages), -1, np.int32), n_pages=n_pages)
+                block_table=np.full((batch, max_pages), -1, np.int32), n_pages=n_pages, lo_bit=lo_bit)
         c.bt_host = np.full((batch, c.max_pages), -1, np.int32)
         c.page_pool = PagePool(n_pages)
         c.seq_lens.fill_(-1)

@@ -41,6 +41,8 @@ int check_config(const kitty_config_t* cfg) {
     return fail(KITTY_ERR_INVALID_ARG, "n_kv_heads %d out of range [1, 1024]", cfg->n_kv_heads);
   if (cfg->n_hi < 0 || cfg->n_hi > cfg->head_dim || cfg->n_hi % 16 != 0)
     return fail(KITTY_ERR_UNSUPPORTED, "n_hi %d unsupported (0 or a multiple of 16 up to 128)", cfg->n_hi);
+  if (cfg->lo_bit != 2 && cfg->lo_bit != 4)
+    return fail(KITTY_ERR_UNSUPPORTED, "lo_bit %d unsupported (2 or 4)", cfg->lo_bit);
   return KITTY_OK;
 }
 
@@ -74,14 +76,14 @@ const char* kitty_last_error(void) { return g_last_error.c_str(); }
 int kitty_record_bytes(const kitty_config_t* cfg, size_t* out) {
   if (int r = check_config(cfg)) return r;
   if (!out) return fail(KITTY_ERR_INVALID_ARG, "out is null");
-  *out = (size_t)kitty::rec_bytes(cfg->n_hi);
+  *out = (size_t)kitty::rec_bytes(cfg->n_hi, cfg->lo_bit);
   return ok();
 }
 
 int kitty_page_bytes(const kitty_config_t* cfg, size_t* out) {
   if (int r = check_config(cfg)) return r;
   if (!out) return fail(KITTY_ERR_INVALID_ARG, "out is null");
-  *out = (size_t)kitty::page_stride_bytes(cfg->n_kv_heads, cfg->n_hi);
+  *out = (size_t)kitty::page_stride_bytes(cfg->n_kv_heads, cfg->n_hi, cfg->lo_bit);
   return ok();
 }
 
@@ -98,12 +100,13 @@ int kitty_quantize_pages(const kitty_config_t* cfg, const kitty_kv_view_t* kv, c
   kitty::QuantizeParams p{};
   p.pages = static_cast<uint8_t*>(kv->pages);
   p.n_pages = kv->n_pages;
-  p.page_bytes = kitty::page_stride_bytes(cfg->n_kv_heads, cfg->n_hi);
+  p.page_bytes = kitty::page_stride_bytes(cfg->n_kv_heads, cfg->n_hi, cfg->lo_bit);
   p.block_table = kv->block_table;
   p.max_pages = kv->max_pages;
   p.batch = kv->batch;
   p.n_kv_heads = cfg->n_kv_heads;
   p.n_hi = cfg->n_hi;
+  p.lo_bit = cfg->lo_bit;
   p.tail_k = reinterpret_cast<_Float16*>(kv->tail_k);
   p.tail_v = reinterpret_cast<_Float16*>(kv->tail_v);
   p.seq_lens = kv->seq_lens;
@@ -124,12 +127,13 @@ int kitty_append_token(const kitty_config_t* cfg, const kitty_kv_view_t* kv, con
   kitty::AppendParams p{};
   p.pages = static_cast<uint8_t*>(kv->pages);
   p.n_pages = kv->n_pages;
-  p.page_bytes = kitty::page_stride_bytes(cfg->n_kv_heads, cfg->n_hi);
+  p.page_bytes = kitty::page_stride_bytes(cfg->n_kv_heads, cfg->n_hi, cfg->lo_bit);
   p.block_table = kv->block_table;
   p.max_pages = kv->max_pages;
   p.batch = kv->batch;
   p.n_kv_heads = cfg->n_kv_heads;
   p.n_hi = cfg->n_hi;
+  p.lo_bit = cfg->lo_bit;
   p.tail_k = reinterpret_cast<_Float16*>(kv->tail_k);
   p.tail_v = reinterpret_cast<_Float16*>(kv->tail_v);
   p.seq_lens = kv->seq_lens;
@@ -163,7 +167,7 @@ static int decode_shape(const kitty_config_t* cfg, int32_t batch, int32_t n_q_he
   const size_t part = (size_t)batch * n_q_heads * plan->n_wg * kitty::kPartialStride * sizeof(float);
   const size_t cnt = (size_t)batch * cfg->n_kv_heads * *n_head_groups * sizeof(int);
   const size_t seqc = (size_t)batch * kitty::kSeqCounterStride * sizeof(int);
-  const size_t seal = (size_t)batch * cfg->n_kv_heads * (*n_head_groups - 1) * kitty::rec_bytes(cfg->n_hi);
+  const size_t seal = (size_t)batch * cfg->n_kv_heads * (*n_head_groups - 1) * kitty::rec_bytes(cfg->n_hi, cfg->lo_bit);
   ws->partials = 0;
   ws->counters = r256(part);
   ws->seq_counters = ws->counters + r256(cnt);
@@ -197,6 +201,7 @@ static int decode_launch(const kitty_config_t* cfg, const kitty_kv_view_t* kv, c
   int nhg;
   DecodeWorkspace ws;
   if (int r = decode_shape(cfg, kv->batch, n_q_heads, max_seq_len, &plan, &nhg, &ws)) return r;
+  if (cfg->lo_bit != 2) return fail(KITTY_ERR_UNSUPPORTED, "%s: lo_bit %d not built yet", what, cfg->lo_bit);
   if (!workspace || !aligned(workspace, 256)) return fail(KITTY_ERR_INVALID_ARG, "workspace null or not 256-byte aligned");
   if (workspace_bytes < ws.total)
     return fail(KITTY_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, ws.total);
@@ -204,12 +209,13 @@ static int decode_launch(const kitty_config_t* cfg, const kitty_kv_view_t* kv, c
   kitty::DecodeParams p{};
   p.pages = static_cast<uint8_t*>(kv->pages);
   p.n_pages = kv->n_pages;
-  p.page_bytes = kitty::page_stride_bytes(cfg->n_kv_heads, cfg->n_hi);
+  p.page_bytes = kitty::page_stride_bytes(cfg->n_kv_heads, cfg->n_hi, cfg->lo_bit);
   p.block_table = kv->block_table;
   p.max_pages = kv->max_pages;
   p.batch = kv->batch;
   p.n_kv_heads = cfg->n_kv_heads;
   p.n_hi = cfg->n_hi;
+  p.lo_bit = cfg->lo_bit;
   p.tail_k = reinterpret_cast<_Float16*>(kv->tail_k);
   p.tail_v = reinterpret_cast<_Float16*>(kv->tail_v);
   p.seq_lens = kv->seq_lens;

@@ -29,6 +29,16 @@
 // K boost: nf = n / 32 full slot blocks, word of (chunk c, block b) at byte
 // 4*(c*nf + b), slots 32b + 8w + e; if n % 32 == 16 a half block follows at
 // byte 256*nf + 4c for chunks c < 32.
+//
+// The (hi_bit 8, lo_bit 4) pair ("Kitty -- Dynamic Channel-wise
+// Mixed-Precision Keys", table "Tuning avg_bits") stores 4-bit planes of the
+// same shape: a word holds ONE combo of 8 elements, element e at bit
+// 16*(e&1) + 4*(e>>1); a chunk is 32 B, combo A at word 2x and combo B at
+// word 2x + 1 (same tokens and channels as above); boost words are pairs at
+// byte 8*(c*nf + b) (+4 for B), the half block at 512*nf + 8c.  Sizes: planes
+// 2048 B, boost 16n B; metadata as above; 5120 + 17n bytes in total.  In
+// general, with b = lo_bit: base 512b, boost 4bn, values 512b, metadata 1024,
+// idx n.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -40,17 +50,19 @@ constexpr int kHeadDim = 128;
 constexpr int kPageTokens = 32;
 constexpr int kVGroup = 32;
 
-__host__ __device__ constexpr int rec_bytes(int n_hi) { return 3072 + 9 * n_hi; }
-__host__ __device__ constexpr int off_kboost() { return 1024; }
-__host__ __device__ constexpr int off_v(int n_hi) { return 1024 + 8 * n_hi; }
-__host__ __device__ constexpr int off_kscale(int n_hi) { return 2048 + 8 * n_hi; }
-__host__ __device__ constexpr int off_kmin(int n_hi) { return 2304 + 8 * n_hi; }
-__host__ __device__ constexpr int off_vscale(int n_hi) { return 2560 + 8 * n_hi; }
-__host__ __device__ constexpr int off_vmin(int n_hi) { return 2816 + 8 * n_hi; }
-__host__ __device__ constexpr int off_idx(int n_hi) { return 3072 + 8 * n_hi; }
+// b = lo_bit (2 or 4)
+__host__ __device__ constexpr int rec_bytes(int n_hi, int b = 2) { return 1024 * b + 4 * b * n_hi + 1024 + n_hi; }
+__host__ __device__ constexpr int off_kboost(int b = 2) { return 512 * b; }
+__host__ __device__ constexpr int off_v(int n_hi, int b = 2) { return 512 * b + 4 * b * n_hi; }
+__host__ __device__ constexpr int off_kscale(int n_hi, int b = 2) { return 1024 * b + 4 * b * n_hi; }
+__host__ __device__ constexpr int off_kmin(int n_hi, int b = 2) { return off_kscale(n_hi, b) + 256; }
+__host__ __device__ constexpr int off_vscale(int n_hi, int b = 2) { return off_kscale(n_hi, b) + 512; }
+__host__ __device__ constexpr int off_vmin(int n_hi, int b = 2) { return off_kscale(n_hi, b) + 768; }
+__host__ __device__ constexpr int off_idx(int n_hi, int b = 2) { return off_kscale(n_hi, b) + 1024; }
+static_assert(rec_bytes(32) == 3360 && off_idx(32) == 3328 && rec_bytes(32, 4) == 5664, "record layout");
 
-__host__ __device__ inline int64_t page_stride_bytes(int n_kv_heads, int n_hi) {
-  int64_t raw = (int64_t)n_kv_heads * rec_bytes(n_hi);
+__host__ __device__ inline int64_t page_stride_bytes(int n_kv_heads, int n_hi, int b = 2) {
+  int64_t raw = (int64_t)n_kv_heads * rec_bytes(n_hi, b);
   return (raw + 255) / 256 * 256;
 }
 
@@ -64,6 +76,7 @@ struct QuantizeParams {
   int32_t batch;
   int32_t n_kv_heads;
   int32_t n_hi;
+  int32_t lo_bit;
   _Float16* tail_k;
   _Float16* tail_v;
   int32_t* seq_lens;
@@ -82,6 +95,7 @@ struct AppendParams {
   int32_t batch;
   int32_t n_kv_heads;
   int32_t n_hi;
+  int32_t lo_bit;
   _Float16* tail_k;
   _Float16* tail_v;
   int32_t* seq_lens;
@@ -98,6 +112,7 @@ struct DecodeParams {
   int32_t batch;
   int32_t n_kv_heads;
   int32_t n_hi;
+  int32_t lo_bit;
   _Float16* tail_k;        // written only by the fused step's append
   _Float16* tail_v;
   int32_t* seq_lens;       // written only by the fused step's append

@@ -34,6 +34,7 @@ namespace kitty {
 namespace pq {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
@@ -139,6 +140,15 @@ __device__ __forceinline__ uint32_t pack_word(uint64_t a, uint64_t b) {
   return gather4(a) | (gather4(b) << 8) | (gather4(a >> 8) << 16) | (gather4(b >> 8) << 24);
 }
 
+// bytes 0, 2, 4, 6 of x (each a 4-bit code in its low nibble) -> bits 0, 4, 8, 12
+__device__ __forceinline__ uint32_t gather4_nib(uint64_t x) {
+  x &= 0x000F000F000F000Full;
+  return (uint32_t)((x | (x >> 12) | (x >> 24) | (x >> 36)) & 0xFFFFu);
+}
+// 4-bit code word of one combo given as 8 code bytes (element e in byte e):
+// element e at bit 16 (e & 1) + 4 (e >> 1)
+__device__ __forceinline__ uint32_t pack_word4(uint64_t a) { return gather4_nib(a) | (gather4_nib(a >> 8) << 16); }
+
 // token t -> value metadata index kappa (inverse of tau): tokens t and
 // t + 16 (t < 16) sit at kappa 2t and 2t + 1
 __host__ __device__ constexpr int kappa_of(int t) { return 2 * (t & 15) + (t >> 4); }
@@ -157,10 +167,13 @@ struct RowSrc {
 
 // The Key half of a (page, head) record: statistics, ranking, codes, the two
 // code planes and the Key metadata.  Called by a full wave; uses the first
-// lds_vstep(NHI) bytes of `lds`.
-template <int NHI>
+// lds_vstep(NHI) bytes of `lds`.  BITS = lo_bit: 2 (hi 4 / lo 2) or 4
+// (hi 8 / lo 4).
+template <int NHI, int BITS = 2>
 __device__ __forceinline__ void quantize_keys_wave(RowSrc ks, uint8_t* __restrict__ rec, uint8_t* __restrict__ lds) {
 #pragma clang fp contract(off)
+  static_assert(BITS == 2 || BITS == 4, "lo_bit 2 or 4");
+  constexpr float kLo = (float)((1 << BITS) - 1), kHi = (float)((1 << (2 * BITS)) - 1);
   const int lane = threadIdx.x & 63;
   uint8_t* lds_base = lds;          // [32 tokens][128 channels] base codes
   uint8_t* lds_boost = lds + 4096;  // [32 tokens][boost_row(NHI)] boost codes
@@ -228,21 +241,22 @@ __device__ __forceinline__ void quantize_keys_wave(RowSrc ks, uint8_t* __restric
   const int pos1 = pos0 + (h0 ? 1 : 0);
 
   // ---------------- Key codes and metadata ---------------------------------
-  const float L0 = h0 ? 15.0f : 3.0f, L1 = h1 ? 15.0f : 3.0f;
+  const float L0 = h0 ? kHi : kLo, L1 = h1 ? kHi : kLo;
   const Step st0 = make_step(mn0, mx0, L0), st1 = make_step(mn1, mx1, L1);
-  const uint16_t ks0 = h0 ? f2h(4.0f * h2f(st0.s16)) : st0.s16;
-  const uint16_t ks1 = h1 ? f2h(4.0f * h2f(st1.s16)) : st1.s16;
-  *reinterpret_cast<uint32_t*>(rec + off_kscale(NHI) + 4 * lane) = (uint32_t)ks0 | ((uint32_t)ks1 << 16);
-  *reinterpret_cast<uint32_t*>(rec + off_kmin(NHI) + 4 * lane) = (uint32_t)f2h(mn0) | ((uint32_t)f2h(mn1) << 16);
+  constexpr float kBoostScale = (float)(1 << BITS);  // kscale = 2^lo_bit * step on boosted channels
+  const uint16_t ks0 = h0 ? f2h(kBoostScale * h2f(st0.s16)) : st0.s16;
+  const uint16_t ks1 = h1 ? f2h(kBoostScale * h2f(st1.s16)) : st1.s16;
+  *reinterpret_cast<uint32_t*>(rec + off_kscale(NHI, BITS) + 4 * lane) = (uint32_t)ks0 | ((uint32_t)ks1 << 16);
+  *reinterpret_cast<uint32_t*>(rec + off_kmin(NHI, BITS) + 4 * lane) = (uint32_t)f2h(mn0) | ((uint32_t)f2h(mn1) << 16);
   // (pos < NHI always holds: exactly NHI channels are selected)
   const bool w0 = h0 && pos0 < NHI, w1 = h1 && pos1 < NHI;
   if (NHI > 0) {
-    if (w0) rec[off_idx(NHI) + pos0] = (uint8_t)(2 * lane);
-    if (w1) rec[off_idx(NHI) + pos1] = (uint8_t)(2 * lane + 1);
+    if (w0) rec[off_idx(NHI, BITS) + pos0] = (uint8_t)(2 * lane);
+    if (w1) rec[off_idx(NHI, BITS) + pos1] = (uint8_t)(2 * lane + 1);
   }
-  // Codes go to LDS as bytes of which only the low two bits are read back:
-  // base = q >> 2 on a boosted channel, q elsewhere; boost = q (low bits).
-  const uint32_t sh0 = h0 ? 2u : 0u, sh1 = h1 ? 2u : 0u;
+  // Codes go to LDS as bytes of which only the low BITS bits are read back:
+  // base = q >> BITS on a boosted channel, q elsewhere; boost = q (low bits).
+  const uint32_t sh0 = h0 ? (uint32_t)BITS : 0u, sh1 = h1 ? (uint32_t)BITS : 0u;
   uint8_t* const bst0 = lds_boost + (w0 ? pos0 : NHI);  // column NHI: a lane's discarded stores
   uint8_t* const bst1 = lds_boost + (w1 ? pos1 : NHI);
 #pragma unroll
@@ -260,46 +274,77 @@ __device__ __forceinline__ void quantize_keys_wave(RowSrc ks, uint8_t* __restric
   wave_lds_sync();
   {
     const int u = lane & 15, w = lane >> 4;
-    u32x4 words;
+    if (BITS == 2) {
+      u32x4 words;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const uint64_t A = *reinterpret_cast<const uint64_t*>(lds_base + u * 128 + 32 * x + 8 * w);
-      const uint64_t B = *reinterpret_cast<const uint64_t*>(lds_base + (16 + u) * 128 + 32 * x + 8 * w);
-      words[x] = pack_word(A, B);
+      for (int x = 0; x < 4; ++x) {
+        const uint64_t A = *reinterpret_cast<const uint64_t*>(lds_base + u * 128 + 32 * x + 8 * w);
+        const uint64_t B = *reinterpret_cast<const uint64_t*>(lds_base + (16 + u) * 128 + 32 * x + 8 * w);
+        words[x] = pack_word(A, B);
+      }
+      *reinterpret_cast<u32x4*>(rec + 16 * lane) = words;
+    } else {  // 4-bit: a 32-byte chunk, combo A at word 2x, combo B at 2x + 1
+      u32x4 lo, hi;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const uint64_t A = *reinterpret_cast<const uint64_t*>(lds_base + u * 128 + 32 * x + 8 * w);
+        const uint64_t B = *reinterpret_cast<const uint64_t*>(lds_base + (16 + u) * 128 + 32 * x + 8 * w);
+        const uint32_t wa = pack_word4(A), wb = pack_word4(B);
+        if (x < 2) {
+          lo[2 * x] = wa;
+          lo[2 * x + 1] = wb;
+        } else {
+          hi[2 * x - 4] = wa;
+          hi[2 * x - 3] = wb;
+        }
+      }
+      *reinterpret_cast<u32x4*>(rec + 32 * lane) = lo;
+      *reinterpret_cast<u32x4*>(rec + 32 * lane + 16) = hi;
     }
-    *reinterpret_cast<u32x4*>(rec + 16 * lane) = words;
     if (NHI > 0) {
       constexpr int nf = NHI / 32;
+      uint8_t* const bp = rec + off_kboost(BITS);
 #pragma unroll
       for (int bb = 0; bb < nf; ++bb) {
         const uint64_t A = *reinterpret_cast<const uint64_t*>(lds_boost + u * boost_row(NHI) + 32 * bb + 8 * w);
         const uint64_t B = *reinterpret_cast<const uint64_t*>(lds_boost + (16 + u) * boost_row(NHI) + 32 * bb + 8 * w);
-        *reinterpret_cast<uint32_t*>(rec + off_kboost() + 4 * (lane * nf + bb)) = pack_word(A, B);
+        if (BITS == 2) {
+          *reinterpret_cast<uint32_t*>(bp + 4 * (lane * nf + bb)) = pack_word(A, B);
+        } else {
+          const u32x2 pr = {pack_word4(A), pack_word4(B)};
+          *reinterpret_cast<u32x2*>(bp + 8 * (lane * nf + bb)) = pr;
+        }
       }
       if ((NHI % 32) != 0 && lane < 32) {
         const uint64_t A = *reinterpret_cast<const uint64_t*>(lds_boost + u * boost_row(NHI) + 32 * nf + 8 * w);
         const uint64_t B = *reinterpret_cast<const uint64_t*>(lds_boost + (16 + u) * boost_row(NHI) + 32 * nf + 8 * w);
-        *reinterpret_cast<uint32_t*>(rec + off_kboost() + 256 * nf + 4 * lane) = pack_word(A, B);
+        if (BITS == 2) {
+          *reinterpret_cast<uint32_t*>(bp + 256 * nf + 4 * lane) = pack_word(A, B);
+        } else {
+          const u32x2 pr = {pack_word4(A), pack_word4(B)};
+          *reinterpret_cast<u32x2*>(bp + 512 * nf + 8 * lane) = pr;
+        }
       }
     }
   }
 }
 
 // The Value half of a (page, head) record: per-token steps and minima of
-// each group of 32 channels, and the 2-bit codes.  Called by a full wave;
+// each group of 32 channels, and the lo_bit codes.  Called by a full wave;
 // uses bytes [lds_vstep(NHI), quant_lds_bytes(NHI)) of `lds`, so a Key wave
 // and a Value wave can share one area.
-template <int NHI>
+template <int NHI, int BITS = 2>
 __device__ __forceinline__ void quantize_values_wave(RowSrc vs, uint8_t* __restrict__ rec, uint8_t* __restrict__ lds) {
 #pragma clang fp contract(off)
+  constexpr float kLo = (float)((1 << BITS) - 1);
   const int lane = threadIdx.x & 63;
   wave_lds_sync();
 
   // ---------------- Value steps: one (token, group) per lane and pass -------
   {
     float* vstep = reinterpret_cast<float*>(lds + lds_vstep(NHI));  // [group][token] x (1 / step, min)
-    uint16_t* vsc = reinterpret_cast<uint16_t*>(rec + off_vscale(NHI));
-    uint16_t* vmn = reinterpret_cast<uint16_t*>(rec + off_vmin(NHI));
+    uint16_t* vsc = reinterpret_cast<uint16_t*>(rec + off_vscale(NHI, BITS));
+    uint16_t* vmn = reinterpret_cast<uint16_t*>(rec + off_vmin(NHI, BITS));
     const int gp = lane & 3;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -325,7 +370,7 @@ __device__ __forceinline__ void quantize_values_wave(RowSrc vs, uint8_t* __restr
       mxv = canon2(__builtin_bit_cast(uint32_t, mxv));
       const float mn = fminf((float)mnv[0], (float)mnv[1]);
       const float mx = fmaxf((float)mxv[0], (float)mxv[1]);
-      const Step st = make_step(mn, mx, 3.0f);
+      const Step st = make_step(mn, mx, kLo);
       *reinterpret_cast<float2*>(vstep + 2 * (32 * gp + tp)) = make_float2(st.inv, mn);
       const int kap = kappa_of(tp);
       vsc[32 * gp + kap] = st.s16;
@@ -349,31 +394,44 @@ __device__ __forceinline__ void quantize_values_wave(RowSrc vs, uint8_t* __restr
         const _Float16* r = vs.row(t);
         const float y0 = (float)r[c0];
         const float y1 = (float)r[c1];
-        a0[t] = code_of(y0, st2[2 * k + 1], st2[2 * k], 3.0f);
-        a1[t] = code_of(y1, st2[2 * k + 1], st2[2 * k], 3.0f);  // codes <= 3: no masking needed below
+        a0[t] = code_of(y0, st2[2 * k + 1], st2[2 * k], kLo);
+        a1[t] = code_of(y1, st2[2 * k + 1], st2[2 * k], kLo);  // codes <= 2^BITS - 1: no masking needed below
       }
     }
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      uint32_t word = 0;
+      if (BITS == 2) {
+        uint32_t word = 0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int t = tau_of(w, e);
-        const int sh = 16 * (e & 1) + 2 * (e >> 1);
-        word |= a0[t] << sh;
-        word |= a1[t] << (sh + 8);
+        for (int e = 0; e < 8; ++e) {
+          const int t = tau_of(w, e);
+          const int sh = 16 * (e & 1) + 2 * (e >> 1);
+          word |= a0[t] << sh;
+          word |= a1[t] << (sh + 8);
+        }
+        *reinterpret_cast<uint32_t*>(rec + off_v(NHI, BITS) + 16 * (16 * w + u) + 4 * g) = word;
+      } else {  // 4-bit: combo A (channel c0) at word 2g, combo B (c1) at 2g + 1 of a 32-byte chunk
+        uint32_t wa = 0, wb = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int t = tau_of(w, e);
+          const int sh = 16 * (e & 1) + 4 * (e >> 1);
+          wa |= a0[t] << sh;
+          wb |= a1[t] << sh;
+        }
+        const u32x2 pr = {wa, wb};
+        *reinterpret_cast<u32x2*>(rec + off_v(NHI, BITS) + 32 * (16 * w + u) + 8 * g) = pr;
       }
-      *reinterpret_cast<uint32_t*>(rec + off_v(NHI) + 16 * (16 * w + u) + 4 * g) = word;
     }
   }
 }
 
 // Quantize and pack one (page, head) into `rec` with one wave; `lds` is this
 // wave's private quant_lds_bytes(NHI) bytes.
-template <int NHI>
+template <int NHI, int BITS = 2>
 __device__ __forceinline__ void quantize_page_wave(RowSrc ks, RowSrc vs, uint8_t* __restrict__ rec, uint8_t* __restrict__ lds) {
-  quantize_keys_wave<NHI>(ks, rec, lds);
-  quantize_values_wave<NHI>(vs, rec, lds);
+  quantize_keys_wave<NHI, BITS>(ks, rec, lds);
+  quantize_values_wave<NHI, BITS>(vs, rec, lds);
 }
 
 

@@ -38,7 +38,7 @@ __device__ __forceinline__ void stage_value_page(const _Float16* src, uint8_t* d
 // two halves' memory latency overlaps.  The value wave first stages its
 // page in LDS, so the per-token steps and the per-channel codes read it
 // from there rather than from global memory twice.
-template <int NHI>
+template <int NHI, int BITS>
 __global__ __launch_bounds__(128) void quantize_pages_kernel(QuantizeParams p) {
   constexpr int kVStage = quant_lds_bytes(NHI);  // the value page: 32 x 128 fp16
   __shared__ __attribute__((aligned(16))) uint8_t lds[kVStage + kPageTokens * kHeadDim * 2];
@@ -53,13 +53,13 @@ __global__ __launch_bounds__(128) void quantize_pages_kernel(QuantizeParams p) {
   if (page < P) {
     const int phys = p.block_table[(size_t)b * p.max_pages + page];
     if (phys < 0 || (int64_t)phys >= p.n_pages) return;
-    uint8_t* rec = p.pages + (int64_t)phys * p.page_bytes + (int64_t)h * rec_bytes(NHI);
+    uint8_t* rec = p.pages + (int64_t)phys * p.page_bytes + (int64_t)h * rec_bytes(NHI, BITS);
     const size_t row0 = seq_off + (size_t)page * kPageTokens * kHeadDim;
     if (wave == 0) {
-      quantize_keys_wave<NHI>(RowSrc{p.k + row0, nullptr}, rec, lds);
+      quantize_keys_wave<NHI, BITS>(RowSrc{p.k + row0, nullptr}, rec, lds);
     } else {
       stage_value_page(p.v + row0, lds + kVStage, lane);
-      quantize_values_wave<NHI>(RowSrc{reinterpret_cast<const _Float16*>(lds + kVStage), nullptr}, rec, lds);
+      quantize_values_wave<NHI, BITS>(RowSrc{reinterpret_cast<const _Float16*>(lds + kVStage), nullptr}, rec, lds);
     }
   } else if (page == P) {  // the tail: wave 0 copies keys, wave 1 values
     const int nt = n - P * kPageTokens;
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(128) void quantize_pages_kernel(QuantizeParams p) {
 // grid (batch), block = min(Hkv, 8) waves (kWaveLds bytes of LDS each); each wave appends one head at a
 // time and seals it when the tail fills; the sequence length is bumped after
 // every head of the sequence is done.
-template <int NHI>
+template <int NHI, int BITS>
 __global__ __launch_bounds__(512) void append_token_kernel(AppendParams p) {  // at most 8 waves
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
   const int b = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -98,8 +98,8 @@ __global__ __launch_bounds__(512) void append_token_kernel(AppendParams p) {  //
       if (pg < p.max_pages) {
         const int phys = p.block_table[(size_t)b * p.max_pages + pg];
         if (phys >= 0 && (int64_t)phys < p.n_pages) {
-          uint8_t* rec = p.pages + (int64_t)phys * p.page_bytes + (int64_t)h * rec_bytes(NHI);
-          quantize_page_wave<NHI>(RowSrc{p.tail_k + tail_off, p.k_new + new_off},
+          uint8_t* rec = p.pages + (int64_t)phys * p.page_bytes + (int64_t)h * rec_bytes(NHI, BITS);
+          quantize_page_wave<NHI, BITS>(RowSrc{p.tail_k + tail_off, p.k_new + new_off},
                                   RowSrc{p.tail_v + tail_off, p.v_new + new_off}, rec, lds_dyn + wave * kWaveLds);
         }
       }
@@ -112,14 +112,20 @@ __global__ __launch_bounds__(512) void append_token_kernel(AppendParams p) {  //
 template <int NHI>
 hipError_t launch_quantize_t(const QuantizeParams& p, hipStream_t stream) {
   dim3 grid(p.S / kPageTokens + 1, p.n_kv_heads, p.batch);
-  hipLaunchKernelGGL(quantize_pages_kernel<NHI>, grid, dim3(128), 0, stream, p);
+  if (p.lo_bit == 4)
+    hipLaunchKernelGGL((quantize_pages_kernel<NHI, 4>), grid, dim3(128), 0, stream, p);
+  else
+    hipLaunchKernelGGL((quantize_pages_kernel<NHI, 2>), grid, dim3(128), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int NHI>
 hipError_t launch_append_t(const AppendParams& p, hipStream_t stream) {
   const int nw = p.n_kv_heads < 8 ? p.n_kv_heads : 8;
-  hipLaunchKernelGGL(append_token_kernel<NHI>, dim3(p.batch), dim3(64 * nw), nw * kWaveLds, stream, p);
+  if (p.lo_bit == 4)
+    hipLaunchKernelGGL((append_token_kernel<NHI, 4>), dim3(p.batch), dim3(64 * nw), nw * kWaveLds, stream, p);
+  else
+    hipLaunchKernelGGL((append_token_kernel<NHI, 2>), dim3(p.batch), dim3(64 * nw), nw * kWaveLds, stream, p);
   return hipGetLastError();
 }
 

@@ -28,9 +28,9 @@ def host(t):
     return t.cpu().numpy()
 
 
-def _diff_fields(got, want, n_hi):
-    gk, gv = O.unpack_record(got, n_hi)
-    wk, wv = O.unpack_record(want, n_hi)
+def _diff_fields(got, want, n_hi, lo_bit):
+    gk, gv = O.unpack_record(got, n_hi, lo_bit)
+    wk, wv = O.unpack_record(want, n_hi, lo_bit)
     out = []
     for key in gk:
         d = int(np.sum(np.asarray(gk[key]).view(np.uint8) != np.asarray(wk[key]).view(np.uint8)))
@@ -59,7 +59,7 @@ def compare_records(cache, oc, samples=None, seq_map=None, pool=None):
         got = pool[bt[gb, j], h * rb:(h + 1) * rb]
         want = O.pack_record(*oc.page_fields(b, h, j))
         if not np.array_equal(got, want):
-            bad.append(((b, j, h), _diff_fields(got, want, oc.n_hi)))
+            bad.append(((b, j, h), _diff_fields(got, want, oc.n_hi, oc.lo_bit)))
     assert not bad, f"{len(bad)} of {len(samples)} records differ, first: {bad[:5]}"
     return len(samples)
 

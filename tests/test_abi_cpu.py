@@ -35,15 +35,17 @@ def test_header_error_codes_match_binding():
 
 
 def test_abi_version():
-    assert B.kitty_abi_version() == 1
+    assert B.kitty_abi_version() == 2
 
 
+@pytest.mark.parametrize("lo_bit,base,per_hi", [(2, 3072, 9), (4, 5120, 17)])
 @pytest.mark.parametrize("n_hi", [0, 16, 32, 48, 64, 128])
-def test_sizes(n_hi):
-    cfg = B.config(8, n_hi)
-    assert B.kitty_record_bytes(cfg) == 3072 + 9 * n_hi
+def test_sizes(n_hi, lo_bit, base, per_hi):
+    cfg = B.config(8, n_hi, lo_bit=lo_bit)
+    rb = base + per_hi * n_hi
+    assert B.kitty_record_bytes(cfg) == rb
     pb = B.kitty_page_bytes(cfg)
-    assert pb % 256 == 0 and pb >= 8 * (3072 + 9 * n_hi) and pb - 8 * (3072 + 9 * n_hi) < 256
+    assert pb % 256 == 0 and pb >= 8 * rb and pb - 8 * rb < 256
 
 
 def test_workspace_bytes_cover_partials():
@@ -76,12 +78,15 @@ def test_workspace_bytes_monotone_in_max_seq_len():
 
 
 @pytest.mark.parametrize("cfg,code", [
-    ((64, 32, 8, 32), B.KITTY_ERR_UNSUPPORTED),
-    ((128, 16, 8, 32), B.KITTY_ERR_UNSUPPORTED),
-    ((128, 32, 0, 32), B.KITTY_ERR_INVALID_ARG),
-    ((128, 32, 8, 8), B.KITTY_ERR_UNSUPPORTED),
-    ((128, 32, 8, 144), B.KITTY_ERR_UNSUPPORTED),
-    ((128, 32, 8, -16), B.KITTY_ERR_UNSUPPORTED),
+    ((64, 32, 8, 32, 2), B.KITTY_ERR_UNSUPPORTED),
+    ((128, 16, 8, 32, 2), B.KITTY_ERR_UNSUPPORTED),
+    ((128, 32, 0, 32, 2), B.KITTY_ERR_INVALID_ARG),
+    ((128, 32, 8, 8, 2), B.KITTY_ERR_UNSUPPORTED),
+    ((128, 32, 8, 144, 2), B.KITTY_ERR_UNSUPPORTED),
+    ((128, 32, 8, -16, 2), B.KITTY_ERR_UNSUPPORTED),
+    ((128, 32, 8, 32, 3), B.KITTY_ERR_UNSUPPORTED),
+    ((128, 32, 8, 32, 8), B.KITTY_ERR_UNSUPPORTED),
+    ((128, 32, 8, 32, 0), B.KITTY_ERR_UNSUPPORTED),
 ])
 def test_config_rejected(cfg, code):
     c = B.kitty_config_t(*cfg)

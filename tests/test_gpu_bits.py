@@ -1,0 +1,113 @@
+"""GPU parity of the (hi_bit 8, lo_bit 4) pair ("Kitty -- Dynamic
+Channel-wise Mixed-Precision Keys", table "Tuning avg_bits") against the CPU
+oracle: prefill and append records (4-bit planes, 5120 + 17 n_hi bytes) and
+fp16 tails bit-exact, for every boosted-channel width, ragged lengths and
+the edge values of the 2-bit tests."""
+import numpy as np
+import pytest
+
+import oracle as O
+from mixed_precision_bit_kitty_amd import synth
+
+from _gpu_util import compare_records, compare_tails, dev, new_cache
+
+pytestmark = pytest.mark.gpu
+
+LO = 4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    from mixed_precision_bit_kitty_amd import binding as B
+    B.load()
+
+
+def _prefill(w, batch, ctx, n_hi, lens=None, max_tokens=None):
+    x = synth.batch(w, batch=batch, ctx=ctx, steps=0)
+    cache = new_cache(batch, w.n_kv_heads, n_hi, max_tokens or max(ctx, 32), lo_bit=LO)
+    lt = None if lens is None else dev(np.array(lens, np.int32))
+    cache.quantize_pages(dev(x["k"]), dev(x["v"]), lens=lt)
+    oc = O.quantize_pages(x["k"], x["v"], n_hi, batch_lens=lens, lo_bit=LO)
+    return x, cache, oc
+
+
+def test_record_size():
+    cache = new_cache(1, 2, 32, 64, lo_bit=LO)
+    assert cache.record_bytes == 5120 + 17 * 32 == O.record_bytes(32, lo_bit=LO)
+
+
+@pytest.mark.parametrize("n_hi", [0, 16, 32, 48, 64, 96, 112, 128])
+def test_prefill_boost_widths(n_hi):
+    w = synth.LLAMA3_8B.with_(n_kv_heads=2, n_q_heads=8)
+    x, cache, oc = _prefill(w, 2, 100, n_hi, lens=[100, 45])
+    compare_records(cache, oc)
+    compare_tails(cache, oc)
+
+
+def test_prefill_edge_lengths():
+    lens = [0, 1, 31, 32, 33, 64]
+    w = synth.LLAMA3_8B.with_(n_kv_heads=2, n_q_heads=4)
+    x, cache, oc = _prefill(w, len(lens), 64, 32, lens=lens)
+    compare_records(cache, oc)
+    compare_tails(cache, oc)
+
+
+def test_prefill_edge_values():
+    rng = np.random.default_rng(5)
+    k = (rng.standard_normal((1, 2, 96, 128)) * 2).astype(np.float16)
+    v = (rng.standard_normal((1, 2, 96, 128)) * 2).astype(np.float16)
+    k[0, 0, :32, 3] = np.float16(-2.5)                       # constant channel
+    k[0, 0, :32, 4] = np.float16(0.0)                        # all zero
+    k[0, 0, :32, 5] = np.float16(-0.0)                       # signed zeros
+    k[0, 0, 7, 5] = np.float16(1.0)
+    k[0, 0, :32, 6] = np.float16(1.0)                        # tiny range -> subnormal step
+    k[0, 0, 9, 6] = np.nextafter(np.float16(1.0), np.float16(2.0))
+    k[0, 0, :32, 7] = np.float16(0.0)
+    k[0, 0, 3, 7] = np.float16(21 * 2.0 ** -24)              # step rounds down -> clamp
+    k[0, 0, :32, 8] = np.float16(0.0)
+    k[0, 0, 5, 8] = np.float16(300 * 2.0 ** -24)             # 255 levels: step of one subnormal ulp
+    k[0, 1, 32:64, :] = (rng.standard_normal((32, 128)) * 60000 / 4).clip(-60000, 60000).astype(np.float16)
+    v[0, 1, 32:64, :] = (rng.standard_normal((32, 128)) * 60000 / 4).clip(-60000, 60000).astype(np.float16)
+    v[0, 0, 40, :] = np.float16(3.0)                         # constant value group row
+    v[0, 0, 41, :32] = np.float16(-0.0)
+    k[0, 0, 64:96, :] = k[0, 0, 64:65, :]                     # identical tokens in a page
+    for n_hi in (0, 32, 128):
+        cache = new_cache(1, 2, n_hi, 96, lo_bit=LO)
+        cache.quantize_pages(dev(k), dev(v))
+        oc = O.quantize_pages(k, v, n_hi, lo_bit=LO)
+        compare_records(cache, oc)
+
+
+@pytest.mark.parametrize("n_hi", [16, 32, 128])
+def test_append_stream(n_hi):
+    w = synth.LLAMA3_8B.with_(n_kv_heads=2, n_q_heads=8)
+    steps = 70
+    x = synth.batch(w, batch=3, ctx=40, steps=steps)
+    lens = [0, 20, 40]
+    cache = new_cache(3, 2, n_hi, 40 + steps + 32, lo_bit=LO)
+    cache.quantize_pages(dev(x["k"]), dev(x["v"]), lens=dev(np.array(lens, np.int32)))
+    oc = O.quantize_pages(x["k"], x["v"], n_hi, batch_lens=lens, lo_bit=LO)
+    for t in range(steps):
+        cache.append_token(dev(x["k_new"][t]), dev(x["v_new"][t]))
+        O.append_token(oc, x["k_new"][t], x["v_new"][t])
+        compare_tails(cache, oc)
+        if any(int(oc.seq_len[b]) % 32 == 0 for b in range(3)) or t == steps - 1:
+            compare_records(cache, oc)
+
+
+def test_append_many_heads():
+    # 8 KV heads: the append kernel's eight waves each seal one head's page
+    w = synth.LLAMA3_8B
+    steps = 3
+    x = synth.batch(w, batch=2, ctx=62, steps=steps)
+    cache = new_cache(2, w.n_kv_heads, w.n_hi, 62 + steps + 32, lo_bit=LO)
+    cache.quantize_pages(dev(x["k"]), dev(x["v"]))
+    oc = O.quantize_pages(x["k"], x["v"], w.n_hi, lo_bit=LO)
+    for t in range(steps):
+        cache.append_token(dev(x["k_new"][t]), dev(x["v_new"][t]))
+        O.append_token(oc, x["k_new"][t], x["v_new"][t])
+    compare_records(cache, oc)
+    compare_tails(cache, oc)
