@@ -11,6 +11,7 @@ split merge).  ``--split`` times the two separate calls instead
 
 Workload (default): Llama-3-8B shape, batch 16, 32 query heads, 8 KV heads,
 head_dim 128, context 4096, hi_fraction 0.25, seeded synthetic fp16 K/V/Q.
+``--lo-bit 4`` runs the (hi_bit 8, lo_bit 4) pair instead of (4, 2).
 To keep reads coming from HBM rather than the 256 MB Infinity Cache, the
 steps rotate over L independent layer caches totalling >= 1 GiB.
 
@@ -47,8 +48,9 @@ def _workload(name):
 
 def kv_bytes(seq_lens, n_kv_heads, record_bytes):
     """Algorithmic KV bytes one decode call reads: every sealed page record
-    (3072 + 9 n_hi bytes per page and KV head) plus the fp16 tail tokens
-    (2 x 256 bytes per token and KV head)."""
+    (3072 + 9 n_hi bytes per page and KV head at lo_bit 2, 5120 + 17 n_hi at
+    lo_bit 4) plus the fp16 tail tokens (2 x 256 bytes per token and KV
+    head)."""
     tot = 0
     for n in seq_lens:
         tot += n_kv_heads * ((n // 32) * record_bytes + (n % 32) * 512)
@@ -83,7 +85,7 @@ def committed_traffic(kernel_hash, workload, entry, kernel="decode_kernel"):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, seconds):
+def cpu_baseline(w, seconds, lo_bit=2):
     """The oracle as it stands, one thread, on a bounded sample of the same
     workload: decode steps (append + attention) on a subset of sequences."""
     import oracle as O
@@ -95,8 +97,8 @@ def cpu_baseline(w, seconds):
         limiter = None
     n_seq = 2
     x = synth.batch(w, batch=n_seq, steps=64)
-    oc = O.quantize_pages(x["k"], x["v"], w.n_hi)
-    rec = O.record_bytes(w.n_hi)
+    oc = O.quantize_pages(x["k"], x["v"], w.n_hi, lo_bit=lo_bit)
+    rec = O.record_bytes(w.n_hi, lo_bit=lo_bit)
     t0 = time.perf_counter()
     steps = 0
     read = 0
@@ -121,7 +123,7 @@ def bench_quantize(args, w):
     """Prefill quantization of the whole batch (kitty_quantize_pages): K
     statistics, DCPB ranking, codes, two-plane packing, V codes, tail copy.
     Algorithmic bytes: the fp16 K and V read (512 B per token and KV head)
-    plus the records written (3072 + 9 n_hi per page and KV head).  Each
+    plus the records written (rec bytes per page and KV head).  Each
     launch quantizes a different one of R input copies (>= 1 GiB in total),
     so reads come from HBM."""
     import torch
@@ -139,7 +141,7 @@ def bench_quantize(args, w):
     R = max(1, math.ceil((1 << 30) / in_bytes))
     ks = [k0] + [k0.clone() for _ in range(R - 1)]
     vs = [v0] + [v0.clone() for _ in range(R - 1)]
-    cache = binding.KittyCache(B, Hkv, w.n_hi, S + 32)
+    cache = binding.KittyCache(B, Hkv, w.n_hi, S + 32, lo_bit=args.lo_bit)
     rec = cache.record_bytes
     alg = in_bytes + B * Hkv * (S // 32) * rec
     for i in range(R):
@@ -167,14 +169,23 @@ def bench_quantize(args, w):
     res = {"metric": "kitty_quantize_pages: GB/s of fp16 K/V read + page records written", "value": round(gbs, 1),
            "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": R, "ms_per_step": round(ms, 6),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
-           "config": {"workload": f"{w.name}: prefill of batch {B}, {Hkv} KV heads, {S} tokens, n_hi {w.n_hi}",
-                      "batch": B, "ctx": S, "n_kv_heads": Hkv, "n_hi": w.n_hi, "input_copies": R},
+           "config": {"workload": f"{w.name}: prefill of batch {B}, {Hkv} KV heads, {S} tokens, n_hi {w.n_hi}"
+                                  + ("" if args.lo_bit == 2 else f", hi_bit 8 / lo_bit 4"),
+                      "batch": B, "ctx": S, "n_kv_heads": Hkv, "n_hi": w.n_hi, "hi_bit": 2 * args.lo_bit,
+                      "lo_bit": args.lo_bit, "input_copies": R},
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(gbs / HBM_PEAK_GBS, 4),
-                        "traffic": committed_traffic(khash, args.workload, None, "quantize_pages_kernel"),
+                        "traffic": committed_traffic(khash, args.workload + _lo_suffix(args), None,
+                                                     "quantize_pages_kernel"),
                         "kernel": "quantize_pages_kernel", "bytes_per_launch": int(alg),
                         "avg_launch_us": round(ms * 1e3, 3), "kernel_source_sha256_16": khash}}
     print(json.dumps(res), flush=True)
+
+
+def _lo_suffix(args):
+    """Name suffix of the committed counter summaries of the 4-bit pair and
+    of a hi_fraction other than the workload's."""
+    return ("" if args.lo_bit == 2 else "_lo4") + ("" if args.hi_fraction is None else f"_hf{args.hi_fraction:g}")
 
 
 def main():
@@ -192,6 +203,10 @@ def main():
                     help="also run one 1 GiB device copy (HBM counter calibration under rocprofv3)")
     ap.add_argument("--split", action="store_true",
                     help="step = kitty_append_token + kitty_decode_attention (two launches) instead of the fused step")
+    ap.add_argument("--lo-bit", type=int, default=2, choices=[2, 4],
+                    help="bit-width pair: 2 = (hi_bit 4, lo_bit 2), 4 = (hi_bit 8, lo_bit 4)")
+    ap.add_argument("--hi-fraction", type=float, default=None,
+                    help="override the workload's hi_fraction (n_hi = hi_fraction x 128, a multiple of 16)")
     ap.add_argument("--quantize", action="store_true",
                     help="time kitty_quantize_pages (prefill of the whole batch) instead of the decode step")
     args = ap.parse_args()
@@ -204,6 +219,8 @@ def main():
     from mixed_precision_bit_kitty_amd import binding, synth
 
     w = _workload(args.workload)
+    if args.hi_fraction is not None:
+        w = w.with_(hi_fraction=args.hi_fraction)
     if args.quantize:
         return bench_quantize(args, w)
     B = args.batch or w.batch
@@ -218,12 +235,12 @@ def main():
     k_new, v_new, q_new = dev(x["k_new"]), dev(x["v_new"]), dev(x["q_new"])
 
     max_tokens = ctx + K + W + 32
-    probe = binding.KittyCache(1, Hkv, n_hi, max_tokens)
+    probe = binding.KittyCache(1, Hkv, n_hi, max_tokens, lo_bit=args.lo_bit)
     layer_bytes = B * probe.max_pages * probe.page_bytes
     del probe
     L = args.layers or max(1, math.ceil((1 << 30) / layer_bytes))
     print(f"[bench] {L} layer caches x {layer_bytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
-    layers = [binding.KittyCache(B, Hkv, n_hi, max_tokens) for _ in range(L)]
+    layers = [binding.KittyCache(B, Hkv, n_hi, max_tokens, lo_bit=args.lo_bit) for _ in range(L)]
     kd, vd = dev(x["k"]), dev(x["v"])
     layers[0].quantize_pages(kd, vd)
     for c in layers[1:]:
@@ -338,27 +355,29 @@ def main():
 
     khash = source_hash(DECODE_SOURCES)
     roof = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": committed_traffic(khash, args.workload, "attention" if args.split else "step"),
+            "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": committed_traffic(khash, args.workload + _lo_suffix(args), "attention" if args.split else "step"),
             "kernel": kernel,
             "bytes_per_launch": int(dec_bytes), "avg_launch_us": round(dec_avg_ms * 1e3, 3),
             "kernel_source_sha256_16": khash}
     res = {
-        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "metric": METRIC if args.lo_bit == 2 else METRIC.replace("2-bit-KV", "4-bit-KV (hi_bit 8, lo_bit 4)"),
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms_step, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp16", "data": "synthetic",
         "tokens_per_s": round(B / (ms_step * 1e-3), 1),
         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "config": {"workload": f"{w.name}: one layer, batch {B}, {Hq} query heads, {Hkv} KV heads, head_dim 128, "
-                               f"context {ctx}+, hi_fraction {w.hi_fraction} (n_hi {n_hi}); step = "
+                               f"context {ctx}+, hi_fraction {w.hi_fraction} (n_hi {n_hi}), "
+                               f"hi_bit {2 * args.lo_bit} / lo_bit {args.lo_bit}; step = "
                                f"{'append + decode (two launches)' if args.split else 'fused append + decode (one launch)'} "
                                f"(replayed from HIP graphs of {L} steps); {L} layer caches rotated ({L * layer_bytes / 2**30:.2f} GiB)",
                    "batch": B, "ctx": ctx, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": 128, "n_hi": n_hi,
-                   "layers_rotated": L},
+                   "hi_bit": 2 * args.lo_bit, "lo_bit": args.lo_bit, "layers_rotated": L},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(w.with_(batch=B), args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(w.with_(batch=B), args.cpu_seconds, args.lo_bit)
     print(json.dumps(res), flush=True)
 
 

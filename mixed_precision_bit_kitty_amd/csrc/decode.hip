@@ -11,7 +11,8 @@
 //
 // which run on v_mfma_f32_16x16x32_f16:
 //  * codes become exact fp16 operands off + code with one shift and one
-//    AND-OR per two codes (off = 4 or 16 by bit position, see unpack_codes);
+//    AND-OR per two codes (off = 4 or 16 by bit position, see unpack_codes;
+//    4-bit codes of the (hi_bit 8, lo_bit 4) pair: off = 16, unpack_codes4);
 //  * the per-page scale goes into the other operand as two fp16 limbs
 //    (hi = f16(x), lo = f16(x - hi)), which together carry the product to
 //    ~22 bits; the limbs sit in different MFMA columns and are summed after;
@@ -45,6 +46,11 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
+
+// The per-page steps are lambdas over the kernel's registers; inlining them
+// keeps every operand in VGPRs (an out-of-line call would pass them through
+// the stack in scratch memory).
+#define KITTY_INLINE __attribute__((always_inline))
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kQtHead = kHeadDim + 16;  // padded head row of the q * kscale limbs (halves)
@@ -129,6 +135,20 @@ __device__ __forceinline__ half8 unpack_codes(uint32_t w, ExpBits e) {
   return __builtin_bit_cast(half8, r);
 }
 
+// MFMA operand from one 4-bit code word (one combo; element e at bit
+// 16*(e&1) + 4*(e>>1), so dword d's two codes sit at bits 4d and 16 + 4d):
+// each dword's pair moves to mantissa bits 6..9 / 22..25 under exponent
+// pattern e, giving 2^(E-15) (1 + c/16): 16 + c for E = 19, 1 + c/16 for
+// E = 15.  Four shifts and four AND-ORs for eight codes.
+__device__ __forceinline__ half8 unpack_codes4(uint32_t w, uint32_t mask, uint32_t e) {
+  u32x4 r;
+  r[0] = and_or(w << 6, mask, e);
+  r[1] = and_or(w << 2, mask, e);
+  r[2] = and_or(w >> 2, mask, e);
+  r[3] = and_or(w >> 6, mask, e);
+  return __builtin_bit_cast(half8, r);
+}
+
 // half8 with value a at elements {0,1,4,5} and b at {2,3,6,7}
 __device__ __forceinline__ half8 half8_ab(float a, float b) {
   half8 v;
@@ -147,10 +167,10 @@ struct QtLimb {
 
 // Per-wave LDS: ring of kRing records, then the limb exchange areas.  After
 // its page loop a wave writes its partial (m, l, O per head) over its ring.
-template <int NHI>
+template <int NHI, int BITS>
 struct alignas(16) Lds {  // 16-byte aligned size: every wave's area keeps 16-byte alignment
   union {
-    uint8_t ring[kRing][rec_bytes(NHI)];
+    uint8_t ring[kRing][rec_bytes(NHI, BITS)];
     float part[4][kPartialStride];  // [head][O[128], m, l, pad]: O 16-byte aligned
   };
   // The q * kscale limbs are read before the softmax and the p limbs after
@@ -167,15 +187,25 @@ struct alignas(16) Lds {  // 16-byte aligned size: every wave's area keeps 16-by
   int flag;                     // workgroup broadcast of the arrival count (wave 0's copy)
 };
 static_assert(sizeof(float) * 4 * kPartialStride <= kRing * rec_bytes(0), "partial fits over the ring");
-static_assert(sizeof(Lds<128>) * kMaxWgWaves <= 160 * 1024, "twelve waves' LDS fit one CU");
+constexpr int kLdsPerCu = 160 * 1024;
+static_assert(sizeof(Lds<128, 2>) * kMaxWgWaves <= kLdsPerCu, "twelve waves' LDS fit one CU (lo_bit 2)");
+// Waves whose LDS areas fit one CU: twelve for every 2-bit record, nine to
+// twelve for 4-bit records (a twice larger ring).
+template <int NHI, int BITS>
+constexpr int max_wg_waves() {
+  constexpr int w = kLdsPerCu / (int)sizeof(Lds<NHI, BITS>);
+  return w < kMaxWgWaves ? w : kMaxWgWaves;
+}
+static_assert(max_wg_waves<128, 4>() >= 8, "4-bit records keep two waves per SIMD");
 
-template <int NHI>
-constexpr int dma_per_page() { return rec_bytes(NHI) / 1024 + (rec_bytes(NHI) % 1024 ? 1 : 0); }
+template <int NHI, int BITS>
+constexpr int dma_per_page() { return (rec_bytes(NHI, BITS) + 1023) / 1024; }
 
 // Copy one record into an LDS slot: 16 bytes per lane per instruction.  The
 // instruction offset advances the global and the LDS address alike, so one
 // address serves the 1024-byte chunks within the offset field's reach (up to
-// 3072); a chunk at 4096 (n_hi >= 112) takes its own address.  AUX = 16
+// 3072); a chunk at 4096 or beyond (n_hi >= 112, or any 4-bit record) takes
+// its own address.  AUX = 16
 // (sc1) reads at agent scope, past this CU's vector L1.
 template <int AUX, int M, int NCHUNK, int REM>
 __device__ __forceinline__ void dma_chunks(const uint8_t* src, uint8_t* slot, int lane) {
@@ -190,16 +220,16 @@ __device__ __forceinline__ void dma_chunks(const uint8_t* src, uint8_t* slot, in
     dma_chunks<AUX, M + 1, NCHUNK, REM>(src, slot, lane);
   }
 }
-template <int NHI, int AUX = 0>
+template <int NHI, int BITS, int AUX = 0>
 __device__ __forceinline__ void dma_record(const uint8_t* __restrict__ rec, uint8_t* slot, int lane) {
-  constexpr int rb = rec_bytes(NHI);
+  constexpr int rb = rec_bytes(NHI, BITS);
   dma_chunks<AUX, 0, (rb + 1023) / 1024, rb % 1024>(rec + 16 * lane, slot, lane);
 }
 
 // Wait until the oldest in-flight page has landed; `ahead` pages were issued after it.
-template <int NHI>
+template <int NHI, int BITS>
 __device__ __forceinline__ void wait_page(int ahead) {
-  constexpr int L = dma_per_page<NHI>();
+  constexpr int L = dma_per_page<NHI, BITS>();
   compiler_fence();
   if (ahead >= 1) wait_vmcnt<L>();
   else wait_vmcnt<0>();
@@ -319,17 +349,18 @@ __host__ __device__ __forceinline__ int weight_prefix(int i, int W) {
 //    the logits of head w at tokens n (combo A) and n + 16 (combo B);
 //  * PV has channels as rows and (head n & 3, limb (n >> 2) & 1) as columns
 //    0..7, the p limbs for the value-minimum correction as columns 8..15.
-template <int NHI>
+template <int NHI, int BITS>
 __global__ __launch_bounds__(64 * kMaxWgWaves) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void decode_kernel(DecodeParams p) {
   constexpr int NB = (NHI + 31) / 32;  // boost slot blocks (the last may be half)
   constexpr int NF = NHI / 32;         // full boost blocks
-  constexpr int RB = rec_bytes(NHI);
-  static_assert(sizeof(Lds<NHI>) >= pq::quant_lds_bytes(NHI), "a wave's LDS holds the page quantizer's scratch");
+  constexpr int RB = rec_bytes(NHI, BITS);
+  static_assert(BITS == 2 || BITS == 4, "lo_bit 2 or 4");
+  static_assert(sizeof(Lds<NHI, BITS>) >= pq::quant_lds_bytes(NHI), "a wave's LDS holds the page quantizer's scratch");
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  Lds<NHI>* const all = reinterpret_cast<Lds<NHI>*>(dyn_lds);
-  Lds<NHI>& sm = all[wave];
+  Lds<NHI, BITS>* const all = reinterpret_cast<Lds<NHI, BITS>*>(dyn_lds);
+  Lds<NHI, BITS>& sm = all[wave];
 
   const int W = p.wg_waves;
   const int n_pw = p.n_wg * W - 1;           // page waves of this unit; the last wave takes the tail
@@ -396,7 +427,7 @@ void decode_kernel(DecodeParams p) {
       seal_rec = hg == 0 ? p.pages + (int64_t)phys * p.page_bytes + (int64_t)hk * RB
                          : p.seal_scratch + ((((size_t)b * p.n_kv_heads + hk) * (p.n_head_groups - 1)) +
                                              (hg - 1)) * RB;
-      pq::quantize_page_wave<NHI>(pq::RowSrc{p.tail_k + toff, p.k_new + noff},
+      pq::quantize_page_wave<NHI, BITS>(pq::RowSrc{p.tail_k + toff, p.k_new + noff},
                                   pq::RowSrc{p.tail_v + toff, p.v_new + noff}, seal_rec,
                                   reinterpret_cast<uint8_t*>(&sm));
     }
@@ -425,16 +456,24 @@ void decode_kernel(DecodeParams p) {
   };
 #pragma unroll
   for (int d = 0; d < kRing; ++d)
-    if (d < npg) dma_record<NHI>(rec_of(phys_of(d)), sm.ring[d], lane);
+    if (d < npg) dma_record<NHI, BITS>(rec_of(phys_of(d)), sm.ring[d], lane);
 
   // ---- per-wave constants -------------------------------------------------
   const uint32_t m8v = vgpr_const(0x03000300u), m6v = vgpr_const(0x00C000C0u);
   const ExpBits ex_base{vgpr_const(0x44004400u), vgpr_const(0x4C004C00u), m8v, m6v};   // 4 + c, 16 + c
   const ExpBits ex_boost{vgpr_const(0x3C003C00u), vgpr_const(0x44004400u), m8v, m6v};  // (4 + c) / 4, (16 + c) / 4
-  const half8 b_off = half8_ab(-4.0f, -16.0f);  // base code offsets per element (B operand rows = channels)
-  const half8 b_offb = half8_ab(-1.0f, -4.0f);  // boost code offsets (weight 1/4)
+  // 4-bit codes: mask of mantissa bits 6..9 / 22..25, exponents of 16 + c and (16 + c) / 16
+  const uint32_t m4v = BITS == 4 ? vgpr_const(0x03C003C0u) : 0u;
+  const uint32_t e4_base = BITS == 4 ? vgpr_const(0x4C004C00u) : 0u;
+  const uint32_t e4_boost = BITS == 4 ? vgpr_const(0x3C003C00u) : 0u;
+  // base code offsets per element (B operand rows = channels); boost code
+  // offsets (weight 2^-lo_bit)
+  const half8 b_off = BITS == 2 ? half8_ab(-4.0f, -16.0f) : half8_ab(-16.0f, -16.0f);
+  const half8 b_offb = BITS == 2 ? half8_ab(-1.0f, -4.0f) : half8_ab(-1.0f, -1.0f);
   // correction operand: rows 0..3 vmin (x1), rows 4..7 vscale x (-offset / 16)
-  const half8 corr_mul = n < 4 ? half8_ab(1.0f, 1.0f) : (n < 8 ? half8_ab(-0.25f, -1.0f) : half8_ab(0.0f, 0.0f));
+  const half8 corr_mul = n < 4 ? half8_ab(1.0f, 1.0f)
+                               : (n < 8 ? (BITS == 2 ? half8_ab(-0.25f, -1.0f) : half8_ab(-1.0f, -1.0f))
+                                        : half8_ab(0.0f, 0.0f));
   const float sl2 = (1.0f / sqrtf((float)kHeadDim)) * kLog2e;
   // PV B operand source: lanes n < 8 read the group's p * vscale limbs, lanes
   // n >= 8 the p limbs (same address for every group)
@@ -453,8 +492,8 @@ void decode_kernel(DecodeParams p) {
     return phys >= 0 && phys < np32;  // wave-uniform
   };
   // q * kscale limbs of the page in S, one (head, 8 channels) per lane
-  auto produce_qt = [&](const uint8_t* S) {
-    const half8 ks = *reinterpret_cast<const half8*>(S + off_kscale(NHI) + 2 * pc);
+  auto produce_qt = [&](const uint8_t* S) KITTY_INLINE {
+    const half8 ks = *reinterpret_cast<const half8*>(S + off_kscale(NHI, BITS) + 2 * pc);
     half8 hi, lo;
 #pragma unroll
     for (int j = 0; j < 8; j += 2) {
@@ -471,44 +510,63 @@ void decode_kernel(DecodeParams p) {
   };
   // QK^T of the page in S (its q * kscale limbs in LDS): rows = (head, limb),
   // columns = tokens; the logits of head w at tokens n and n + 16
-  auto qk = [&](const uint8_t* S, bool valid, float& s0, float& s1) {
-    const u32x4 kw = *reinterpret_cast<const u32x4*>(S + 16 * lane);
+  auto qk = [&](const uint8_t* S, bool valid, float& s0, float& s1) KITTY_INLINE {
+    // this lane's K base chunk: four words (2-bit) or eight (4-bit: combos A, B of word x at 2x, 2x + 1)
+    const u32x4 kw = *reinterpret_cast<const u32x4*>(S + 16 * BITS / 2 * lane);
+    const u32x4 kw2 = BITS == 4 ? *reinterpret_cast<const u32x4*>(S + 32 * lane + 16) : u32x4{};
     half8 bq[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) bq[kb] = *reinterpret_cast<const half8*>(&sm.qt[al].h[ah][32 * kb + 8 * w]);
     floatx4 cmin = {0.0f, 0.0f, 0.0f, 0.0f}, coff = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const half8 kmin = *reinterpret_cast<const half8*>(S + off_kmin(NHI) + 2 * (32 * kb + 8 * w));
+      const half8 kmin = *reinterpret_cast<const half8*>(S + off_kmin(NHI, BITS) + 2 * (32 * kb + 8 * w));
       cmin = mfma(bq_plain[kb], kmin, cmin);
       coff = mfma(bq[kb], b_off, coff);
     }
     half8 bb[NB > 0 ? NB : 1];
-    uint32_t bw[NB > 0 ? NB : 1];
+    u32x2 bw[NB > 0 ? NB : 1];  // 2-bit: one word (both combos); 4-bit: the combo A, B pair
 #pragma unroll
     for (int k2 = 0; k2 < NB; ++k2) {
       const int q0 = 32 * k2 + 8 * w;
       half8 v = {};
       if (q0 < NHI) {
-        const u32x2 ib = *reinterpret_cast<const u32x2*>(S + off_idx(NHI) + q0);
+        const u32x2 ib = *reinterpret_cast<const u32x2*>(S + off_idx(NHI, BITS) + q0);
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = sm.qt[al].h[ah][opaque(__builtin_amdgcn_ubfe(ib[j >> 2], 8 * (j & 3), 7))];
       }
       bb[k2] = v;
-      if (k2 < NF) bw[k2] = *reinterpret_cast<const uint32_t*>(S + off_kboost() + 4 * (lane * NF + k2));
-      else bw[k2] = lane < 32 ? *reinterpret_cast<const uint32_t*>(S + off_kboost() + 256 * NF + 4 * lane) : 0u;
+      if constexpr (BITS == 2) {
+        if (k2 < NF) bw[k2][0] = *reinterpret_cast<const uint32_t*>(S + off_kboost() + 4 * (lane * NF + k2));
+        else bw[k2][0] = lane < 32 ? *reinterpret_cast<const uint32_t*>(S + off_kboost() + 256 * NF + 4 * lane) : 0u;
+      } else {
+        if (k2 < NF) bw[k2] = *reinterpret_cast<const u32x2*>(S + off_kboost(4) + 8 * (lane * NF + k2));
+        else bw[k2] = lane < 32 ? *reinterpret_cast<const u32x2*>(S + off_kboost(4) + 512 * NF + 8 * lane) : u32x2{};
+      }
       coff = mfma(v, b_offb, coff);
     }
     floatx4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      acc0 = mfma(bq[kb], unpack_codes<0>(kw[kb], ex_base), acc0);
-      acc1 = mfma(bq[kb], unpack_codes<1>(kw[kb], ex_base), acc1);
+      if constexpr (BITS == 2) {
+        acc0 = mfma(bq[kb], unpack_codes<0>(kw[kb], ex_base), acc0);
+        acc1 = mfma(bq[kb], unpack_codes<1>(kw[kb], ex_base), acc1);
+      } else {
+        const uint32_t wa = kb < 2 ? kw[2 * kb] : kw2[2 * kb - 4];
+        const uint32_t wb = kb < 2 ? kw[2 * kb + 1] : kw2[2 * kb - 3];
+        acc0 = mfma(bq[kb], unpack_codes4(wa, m4v, e4_base), acc0);
+        acc1 = mfma(bq[kb], unpack_codes4(wb, m4v, e4_base), acc1);
+      }
     }
 #pragma unroll
     for (int k2 = 0; k2 < NB; ++k2) {
-      acc0 = mfma(bb[k2], unpack_codes<0>(bw[k2], ex_boost), acc0);
-      acc1 = mfma(bb[k2], unpack_codes<1>(bw[k2], ex_boost), acc1);
+      if constexpr (BITS == 2) {
+        acc0 = mfma(bb[k2], unpack_codes<0>(bw[k2][0], ex_boost), acc0);
+        acc1 = mfma(bb[k2], unpack_codes<1>(bw[k2][0], ex_boost), acc1);
+      } else {
+        acc0 = mfma(bb[k2], unpack_codes4(bw[k2][0], m4v, e4_boost), acc0);
+        acc1 = mfma(bb[k2], unpack_codes4(bw[k2][1], m4v, e4_boost), acc1);
+      }
     }
     // rows 4w (hi limb, with the minimum term) + 4w + 1 (lo limb) of head w
     const float cst = cmin[0] + coff[0] + coff[1];
@@ -520,11 +578,11 @@ void decode_kernel(DecodeParams p) {
   // hi = f16(p_hi vscale), lo = f16(p_lo vscale + (p_hi vscale - hi)): the
   // inner residual is exact and lo is rounded once, so the pair carries
   // p * vscale to about 2^-21 relative.
-  auto produce_pt = [&](const uint8_t* S, float s0, float s1) {
+  auto produce_pt = [&](const uint8_t* S, float s0, float s1) KITTY_INLINE {
     const PLimbs pl = p_limbs(s0, s1);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const half2v vs = *reinterpret_cast<const half2v*>(S + off_vscale(NHI) + 2 * (32 * g + 2 * n));
+      const half2v vs = *reinterpret_cast<const half2v*>(S + off_vscale(NHI, BITS) + 2 * (32 * g + 2 * n));
       const half2v hi = mul_hi(pl.hi, vs);
       const half2v lo = fma2(pl.lo, vs, fma2(pl.hi, vs, -hi));
       *reinterpret_cast<half2v*>(&sm.pt[g][0][w][2 * n]) = hi;
@@ -533,23 +591,31 @@ void decode_kernel(DecodeParams p) {
     store_p_limbs(sm.pl, w, n, pl);
   };
   // PV of the page in S (its p limbs in LDS)
-  auto pv = [&](const uint8_t* S) {
-    const u32x4 vw = *reinterpret_cast<const u32x4*>(S + off_v(NHI) + 16 * lane);
+  auto pv = [&](const uint8_t* S) KITTY_INLINE {
+    const u32x4 vw = *reinterpret_cast<const u32x4*>(S + off_v(NHI, BITS) + 16 * BITS / 2 * lane);
+    const u32x4 vw2 = BITS == 4 ? *reinterpret_cast<const u32x4*>(S + off_v(NHI, BITS) + 32 * lane + 16) : u32x4{};
     half8 bg0 = {};
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       // columns 0..7: p * vscale limbs of group g; 8..15: p limbs (for the correction)
       const half8 bg = *reinterpret_cast<const half8*>(b_src + g * b_stride);
       if (g == 0) bg0 = bg;
-      st.o[2 * g] = mfma(unpack_codes<0>(vw[g], ex_base), bg, st.o[2 * g]);
-      st.o[2 * g + 1] = mfma(unpack_codes<1>(vw[g], ex_base), bg, st.o[2 * g + 1]);
+      if constexpr (BITS == 2) {
+        st.o[2 * g] = mfma(unpack_codes<0>(vw[g], ex_base), bg, st.o[2 * g]);
+        st.o[2 * g + 1] = mfma(unpack_codes<1>(vw[g], ex_base), bg, st.o[2 * g + 1]);
+      } else {
+        const uint32_t wa = g < 2 ? vw[2 * g] : vw2[2 * g - 4];
+        const uint32_t wb = g < 2 ? vw[2 * g + 1] : vw2[2 * g - 3];
+        st.o[2 * g] = mfma(unpack_codes4(wa, m4v, e4_base), bg, st.o[2 * g]);
+        st.o[2 * g + 1] = mfma(unpack_codes4(wb, m4v, e4_base), bg, st.o[2 * g + 1]);
+      }
     }
-    const uint8_t* src = S + (n < 4 ? off_vmin(NHI) : off_vscale(NHI)) + 2 * (32 * (n & 3) + 8 * w);
+    const uint8_t* src = S + (n < 4 ? off_vmin(NHI, BITS) : off_vscale(NHI, BITS)) + 2 * (32 * (n & 3) + 8 * w);
     const half8 a = *reinterpret_cast<const half8*>(src) * corr_mul;
     st.corr = mfma(a, bg0, st.corr);
   };
   // one page through the whole contraction
-  auto attend_page = [&](const uint8_t* S, bool valid) {
+  auto attend_page = [&](const uint8_t* S, bool valid) KITTY_INLINE {
     produce_qt(S);
     wave_lds_sync();
     float s0, s1;
@@ -562,14 +628,14 @@ void decode_kernel(DecodeParams p) {
 
   // The loop runs two pages per trip so that each ring slot, and with it
   // every LDS address of the page, is a compile-time offset.
-  auto page_step = [&](int i, auto slot_c) {
+  auto page_step = [&](int i, auto slot_c) KITTY_INLINE {
     constexpr int slot = decltype(slot_c)::value;
-    wait_page<NHI>(min(kRing - 1, npg - 1 - i));
+    wait_page<NHI, BITS>(min(kRing - 1, npg - 1 - i));
     attend_page(sm.ring[slot], valid_of(i));
     if (i + kRing < npg) {  // refill this slot
       wait_lgkm0();
       compiler_fence();
-      dma_record<NHI>(rec_of(phys_of(i + kRing)), sm.ring[slot], lane);
+      dma_record<NHI, BITS>(rec_of(phys_of(i + kRing)), sm.ring[slot], lane);
     }
   };
   static_assert(kRing == 2, "the page loop alternates two ring slots");
@@ -585,8 +651,8 @@ void decode_kernel(DecodeParams p) {
       compiler_fence();
       wait_vmcnt<0>();  // the record's stores are complete
       compiler_fence();
-      dma_record<NHI, 16>(seal_rec, sm.ring[0], lane);
-      wait_page<NHI>(0);
+      dma_record<NHI, BITS, 16>(seal_rec, sm.ring[0], lane);
+      wait_page<NHI, BITS>(0);
       attend_page(sm.ring[0], true);
       wave_lds_sync();
     }
@@ -794,16 +860,30 @@ void decode_kernel(DecodeParams p) {
   sequence_arrival(seq_old, p.n_kv_heads * p.n_head_groups);
 }
 
-template <int NHI>
-hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
-  const size_t lds = sizeof(Lds<NHI>) * p.wg_waves;
-  static const hipError_t attr =  // once per instantiation: allow up to twelve waves' LDS
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<NHI>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)(sizeof(Lds<NHI>) * kMaxWgWaves));
+template <int NHI, int BITS>
+hipError_t launch_decode_nb(const DecodeParams& p, hipStream_t stream) {
+  constexpr int wmax = max_wg_waves<NHI, BITS>();
+  if (p.wg_waves < 2 || p.wg_waves > wmax) return hipErrorInvalidValue;
+  const size_t lds = sizeof(Lds<NHI, BITS>) * p.wg_waves;
+  static const hipError_t attr =  // once per instantiation: allow the largest workgroup's LDS
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<NHI, BITS>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)(sizeof(Lds<NHI, BITS>) * wmax));
   if (attr != hipSuccess) return attr;
   dim3 grid(p.n_wg, p.n_kv_heads * p.n_head_groups, p.batch);
-  hipLaunchKernelGGL(decode_kernel<NHI>, grid, dim3(64 * p.wg_waves), lds, stream, p);
+  hipLaunchKernelGGL((decode_kernel<NHI, BITS>), grid, dim3(64 * p.wg_waves), lds, stream, p);
   return hipGetLastError();
+}
+
+template <int NHI>
+hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
+  if (p.lo_bit == 4) return launch_decode_nb<NHI, 4>(p, stream);
+  if (p.lo_bit == 2) return launch_decode_nb<NHI, 2>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+template <int NHI>
+int max_wg_waves_t(int lo_bit) {
+  return lo_bit == 4 ? max_wg_waves<NHI, 4>() : max_wg_waves<NHI, 2>();
 }
 
 }  // namespace
@@ -821,24 +901,39 @@ static long max_range(long Pm, long n_wg, long W) {
   return best;
 }
 
-SplitPlan plan_splits(int batch, int n_kv_heads, int n_head_groups, int max_seq_len) {
+int decode_max_wg_waves(int n_hi, int lo_bit) {
+  switch (n_hi) {
+    case 0: return max_wg_waves_t<0>(lo_bit);
+    case 16: return max_wg_waves_t<16>(lo_bit);
+    case 32: return max_wg_waves_t<32>(lo_bit);
+    case 48: return max_wg_waves_t<48>(lo_bit);
+    case 64: return max_wg_waves_t<64>(lo_bit);
+    case 80: return max_wg_waves_t<80>(lo_bit);
+    case 96: return max_wg_waves_t<96>(lo_bit);
+    case 112: return max_wg_waves_t<112>(lo_bit);
+    case 128: return max_wg_waves_t<128>(lo_bit);
+    default: return kMaxWgWaves;
+  }
+}
+
+SplitPlan plan_splits(int batch, int n_kv_heads, int n_head_groups, int max_seq_len, int wmax) {
   const long P = max_seq_len / kPageTokens;
   const long units = (long)batch * n_kv_heads * n_head_groups;
-  const long resident = 3 * 4 * 256;  // waves: 3 per SIMD on 256 CUs
+  const long resident = (long)wmax * 256;  // waves: up to 3 per SIMD on 256 CUs, as LDS allows
   long wpu = resident / units;         // waves per unit, the tail wave included
   if (wpu > P + 1) wpu = P + 1;        // at least one page per page wave
   if (wpu < 2) wpu = 2;
   // Every quantity below is non-decreasing in max_seq_len, so a workspace
   // sized for a bound serves every shorter call.
   for (;;) {
-    long n_wg = (wpu + kMaxWgWaves - 1) / kMaxWgWaves;
+    long n_wg = (wpu + wmax - 1) / wmax;
     if (n_wg > kMaxWg) n_wg = kMaxWg;
     long wg_waves = (wpu + n_wg - 1) / n_wg;
-    if (wg_waves > kMaxWgWaves) wg_waves = kMaxWgWaves;
+    if (wg_waves > wmax) wg_waves = wmax;
     // a page wave keeps its page ids in one 64-lane register; wpu only
     // grows, and for every supported length (P <= 4096) it stops well
     // before 16 x 12 waves
-    if (max_range(P, n_wg, wg_waves) <= 64 || n_wg * wg_waves >= (long)kMaxWg * kMaxWgWaves)
+    if (max_range(P, n_wg, wg_waves) <= 64 || n_wg * wg_waves >= (long)kMaxWg * wmax)
       return SplitPlan{(int)n_wg, (int)wg_waves};
     ++wpu;
   }

@@ -162,7 +162,8 @@ static int decode_shape(const kitty_config_t* cfg, int32_t batch, int32_t n_q_he
   const int G = n_q_heads / cfg->n_kv_heads;
   *n_head_groups = (G + 3) / 4;
   if ((long)cfg->n_kv_heads * *n_head_groups > 65535) return fail(KITTY_ERR_INVALID_ARG, "too many heads");
-  *plan = kitty::plan_splits(batch, cfg->n_kv_heads, *n_head_groups, max_seq_len);
+  *plan = kitty::plan_splits(batch, cfg->n_kv_heads, *n_head_groups, max_seq_len,
+                             kitty::decode_max_wg_waves(cfg->n_hi, cfg->lo_bit));
   auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t part = (size_t)batch * n_q_heads * plan->n_wg * kitty::kPartialStride * sizeof(float);
   const size_t cnt = (size_t)batch * cfg->n_kv_heads * *n_head_groups * sizeof(int);
@@ -201,7 +202,6 @@ static int decode_launch(const kitty_config_t* cfg, const kitty_kv_view_t* kv, c
   int nhg;
   DecodeWorkspace ws;
   if (int r = decode_shape(cfg, kv->batch, n_q_heads, max_seq_len, &plan, &nhg, &ws)) return r;
-  if (cfg->lo_bit != 2) return fail(KITTY_ERR_UNSUPPORTED, "%s: lo_bit %d not built yet", what, cfg->lo_bit);
   if (!workspace || !aligned(workspace, 256)) return fail(KITTY_ERR_INVALID_ARG, "workspace null or not 256-byte aligned");
   if (workspace_bytes < ws.total)
     return fail(KITTY_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, ws.total);

@@ -146,7 +146,9 @@ struct SplitPlan {
   int n_wg;
   int wg_waves;
 };
-SplitPlan plan_splits(int batch, int n_kv_heads, int n_head_groups, int max_seq_len);
+// wmax: waves per workgroup that the record size allows (decode_max_wg_waves)
+SplitPlan plan_splits(int batch, int n_kv_heads, int n_head_groups, int max_seq_len, int wmax);
+int decode_max_wg_waves(int n_hi, int lo_bit);
 
 hipError_t launch_quantize(const QuantizeParams& p, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);

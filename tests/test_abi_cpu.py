@@ -67,6 +67,35 @@ def test_workspace_bytes_cover_partials():
     assert nb3 == 12800 + 256 + 512
 
 
+def test_decode_waves_per_workgroup():
+    """Waves per decode workgroup that the per-wave LDS (a ring of two
+    records) allows on one CU: twelve for 2-bit records, fewer for the
+    larger 4-bit ones."""
+    f = ctypes.CDLL(LIB)._ZN5kitty19decode_max_wg_wavesEii
+    f.restype, f.argtypes = ctypes.c_int, [ctypes.c_int32, ctypes.c_int32]
+    for n_hi in range(0, 129, 16):
+        assert f(n_hi, 2) == 12
+        w4 = f(n_hi, 4)
+        # a wave's area: the ring, two fp16 limb tables of 4 x 144 (+ 8 pad)
+        # halves, 32 correction floats and a flag, in 16-byte units
+        area = -(-(2 * (5120 + 17 * n_hi) + 2 * 1168 + 128 + 4) // 16) * 16
+        assert w4 == min(12, 160 * 1024 // area)
+    assert f(0, 4) == 12 and f(128, 4) == 9
+
+
+def test_workspace_bytes_4bit():
+    # seal records of head groups >= 1 are 4-bit records; the plan differs
+    cfg = B.config(8, 32, lo_bit=4)
+    assert B.kitty_decode_workspace_bytes(cfg, 1, 8, 0) == 4352 + 256 + 256
+    nb = B.kitty_decode_workspace_bytes(cfg, 2, 96, 0)
+    assert nb == 2 * 96 * 132 * 4 + 256 + 256 + 2 * 8 * 2 * (5120 + 17 * 32)
+    prev = 0
+    for msl in list(range(0, 6000, 37)) + [4096 * 32 + 31]:
+        nb = B.kitty_decode_workspace_bytes(cfg, 16, 32, msl)
+        assert nb >= prev
+        prev = nb
+
+
 def test_workspace_bytes_monotone_in_max_seq_len():
     cfg = B.config(8, 32)
     for batch, hq in [(1, 8), (16, 32), (4, 96), (128, 32)]:
@@ -196,9 +225,9 @@ def test_decode_plan_fits_page_id_register():
     gives a page wave more than 64 pages, the width of the register that
     holds its page ids, under the kernel's age-weighted page shares."""
     lib = ctypes.CDLL(LIB)
-    f = lib._ZN5kitty11plan_splitsEiiii
+    f = lib._ZN5kitty11plan_splitsEiiiii
     f.restype = ctypes.c_uint64
-    f.argtypes = [ctypes.c_int32] * 4
+    f.argtypes = [ctypes.c_int32] * 5
 
     def weight(i):
         return 9 if i < 4 else (7 if i < 8 else 5)
@@ -207,12 +236,12 @@ def test_decode_plan_fits_page_id_register():
         r = min(i, W)
         return 9 * min(r, 4) + 7 * min(max(r - 4, 0), 4) + 5 * max(r - 8, 0)
 
-    for batch in (1, 3, 16, 128, 1024):
+    for batch, wmax in ((1, 12), (3, 9), (16, 12), (16, 11), (16, 9), (128, 10), (1024, 12)):
         for hkv, hg in ((1, 1), (8, 1), (8, 2), (32, 4)):
             for msl in list(range(0, 4096 * 32 + 32, 4999)) + [4096 * 32 + 31, 320 * 32]:
-                r = f(batch, hkv, hg, msl)
+                r = f(batch, hkv, hg, msl, wmax)
                 n_wg, W = r & 0xFFFFFFFF, r >> 32
-                assert 1 <= n_wg <= 64 and 2 <= W <= 12
+                assert 1 <= n_wg <= 16 and 2 <= W <= wmax
                 P = msl // 32
                 wsum = n_wg * prefix(W, W) - weight(W - 1)
                 for pw in range(n_wg * W - 1):

@@ -2,14 +2,16 @@
 Channel-wise Mixed-Precision Keys", table "Tuning avg_bits") against the CPU
 oracle: prefill and append records (4-bit planes, 5120 + 17 n_hi bytes) and
 fp16 tails bit-exact, for every boosted-channel width, ragged lengths and
-the edge values of the 2-bit tests."""
+the edge values of the 2-bit tests; decode attention and the fused decode
+step within 2e-3 of the oracle's attention, also split over several
+workgroups, across seals and at the full batch-16, 4096-token size."""
 import numpy as np
 import pytest
 
 import oracle as O
 from mixed_precision_bit_kitty_amd import synth
 
-from _gpu_util import compare_records, compare_tails, dev, new_cache
+from _gpu_util import ATOL, compare_decode, compare_records, compare_tails, dev, host, new_cache
 
 pytestmark = pytest.mark.gpu
 
@@ -111,3 +113,147 @@ def test_append_many_heads():
         O.append_token(oc, x["k_new"][t], x["v_new"][t])
     compare_records(cache, oc)
     compare_tails(cache, oc)
+
+
+@pytest.mark.parametrize("n_hi", [0, 16, 32, 48, 80, 112, 128])
+def test_decode_boost_widths(n_hi):
+    w = synth.LLAMA3_8B.with_(n_kv_heads=2, n_q_heads=8)
+    x, cache, oc = _prefill(w, 2, 100, n_hi, lens=[100, 45])
+    err, _ = compare_decode(cache, oc, x["q"])
+    print(f"lo_bit 4, n_hi {n_hi}: max abs err {err:.3g}")
+
+
+@pytest.mark.parametrize("hq", [2, 6, 12, 16])
+def test_decode_query_groups(hq):
+    w = synth.LLAMA3_8B.with_(n_kv_heads=2, n_q_heads=hq)
+    x, cache, oc = _prefill(w, 2, 200, 32)
+    compare_decode(cache, oc, x["q"])
+
+
+def test_decode_edge_lengths():
+    lens = [0, 1, 31, 32, 33, 64]
+    w = synth.LLAMA3_8B.with_(n_kv_heads=2, n_q_heads=4)
+    x, cache, oc = _prefill(w, len(lens), 64, 32, lens=lens)
+    err, out = compare_decode(cache, oc, x["q"])
+    assert np.all(out[0] == 0)
+
+
+@pytest.mark.parametrize("n_hi", [32, 128])
+def test_decode_several_workgroups(n_hi):
+    # long sequences: every (sequence, KV head) is split over several
+    # workgroups of at most nine (n_hi 128) or eleven (n_hi 32) waves
+    w = synth.LLAMA3_8B.with_(n_kv_heads=2, n_q_heads=8)
+    x, cache, oc = _prefill(w, 3, 2015, n_hi, lens=[2015, 1500, 7])
+    for msl in (2015, 2015 + 100, None):
+        err, _ = compare_decode(cache, oc, x["q"], max_seq_len=msl)
+        print(f"lo_bit 4, n_hi {n_hi}, max_seq_len {msl}: max abs err {err:.3g}")
+
+
+def test_decode_edge_values():
+    rng = np.random.default_rng(6)
+    k = (rng.standard_normal((1, 2, 96, 128)) * 2).astype(np.float16)
+    v = (rng.standard_normal((1, 2, 96, 128)) * 2).astype(np.float16)
+    k[0, :, :32, 3] = np.float16(-2.5)
+    k[0, :, :32, 4] = np.float16(0.0)
+    k[0, :, :32, 6] = np.float16(1.0)
+    k[0, :, 9, 6] = np.nextafter(np.float16(1.0), np.float16(2.0))
+    v[0, :, 40, :] = np.float16(3.0)
+    k[0, :, 64:96, :] = k[0, :, 64:65, :]
+    q = (rng.standard_normal((1, 8, 128))).astype(np.float16)
+    for n_hi in (0, 32, 128):
+        cache = new_cache(1, 2, n_hi, 96, lo_bit=LO)
+        cache.quantize_pages(dev(k), dev(v))
+        oc = O.quantize_pages(k, v, n_hi, lo_bit=LO)
+        compare_decode(cache, oc, q)
+
+
+def _step_twins(w, lens, steps, ctx, n_hi=32, msl=None, check_every=1):
+    """Twin 4-bit caches: one through the fused step, one through append +
+    decode attention; pools, tails, lengths byte-equal after every step,
+    outputs bit-equal on steps without a seal, both within 2e-3 of the
+    oracle."""
+    import torch
+    batch = len(lens)
+    x = synth.batch(w, batch=batch, ctx=ctx, steps=steps)
+    cap = max(lens) + steps + 32
+    fused, split = [new_cache(batch, w.n_kv_heads, n_hi, cap, lo_bit=LO) for _ in range(2)]
+    for c in (fused, split):
+        c.quantize_pages(dev(x["k"]), dev(x["v"]), lens=dev(np.array(lens, np.int32)))
+    oc = O.quantize_pages(x["k"], x["v"], n_hi, batch_lens=lens, lo_bit=LO)
+    msl = max(lens) + steps if msl is None else msl
+    outs = [torch.zeros((batch, w.n_q_heads, 128), dtype=torch.float32, device="cuda") for _ in range(2)]
+    worst = 0.0
+    for t in range(steps):
+        k, v, q = dev(x["k_new"][t]), dev(x["v_new"][t]), dev(x["q_new"][t])
+        seals = [b for b in range(batch) if int(oc.seq_len[b]) % 32 == 31]
+        fused.decode_step(k, v, q, max_seq_len=msl, out=outs[0])
+        split.append_token(k, v)
+        split.decode_attention(q, max_seq_len=msl, out=outs[1])
+        O.append_token(oc, x["k_new"][t], x["v_new"][t])
+        a, b = host(outs[0]), host(outs[1])
+        if not seals:
+            assert np.array_equal(a, b), f"step {t}: fused and separate outputs differ without a seal"
+        assert np.array_equal(host(fused.seq_lens), host(split.seq_lens)), f"step {t}"
+        assert np.array_equal(host(fused.tail_k), host(split.tail_k)), f"step {t}"
+        if seals or t % check_every == 0 or t == steps - 1:
+            assert np.array_equal(host(fused.pool), host(split.pool)), f"step {t}: page pools differ"
+            compare_tails(fused, oc)
+            ref = O.decode_attention(oc, x["q_new"][t])
+            err = float(np.abs(a - ref).max())
+            worst = max(worst, err)
+            assert err <= ATOL, f"step {t}: max abs err {err}"
+    compare_records(fused, oc)
+    return worst
+
+
+@pytest.mark.parametrize("hkv,hq", [(2, 8), (2, 12), (1, 2)])
+def test_step_ragged_batch_across_seals(hkv, hq):
+    w = synth.LLAMA3_8B.with_(n_kv_heads=hkv, n_q_heads=hq)
+    worst = _step_twins(w, [0, 31, 45, 63], 40, 64)
+    print(f"lo_bit 4 fused step Hkv {hkv} Hq {hq}: max abs err {worst:.3g}")
+
+
+@pytest.mark.parametrize("n_hi", [0, 128])
+def test_step_boost_widths(n_hi):
+    w = synth.LLAMA3_8B.with_(n_kv_heads=2, n_q_heads=8)
+    _step_twins(w, [30, 62], 4, 64, n_hi=n_hi)
+
+
+def test_step_several_workgroups():
+    w = synth.LLAMA3_8B.with_(n_kv_heads=2, n_q_heads=8)
+    worst = _step_twins(w, [2015, 1500, 7], 36, 2015, check_every=5)
+    print(f"lo_bit 4 fused step, several workgroups: max abs err {worst:.3g}")
+
+
+def test_llama3_8b_full_size_fused_steps():
+    """Batch 16 at 4096 tokens, 8 KV heads, 32 query heads, n_hi 32, with
+    4-bit records: prefill, then fused steps across the seal of page 128;
+    one seeded sequence checked against the oracle."""
+    import torch
+    w = synth.LLAMA3_8B
+    steps = 34
+    x = synth.batch(w, steps=steps)
+    cache = new_cache(w.batch, w.n_kv_heads, w.n_hi, w.ctx + steps + 32, lo_bit=LO)
+    cache.quantize_pages(dev(x["k"]), dev(x["v"]))
+    b = int(np.random.default_rng(105).integers(w.batch))
+    oc = O.quantize_pages(x["k"][b:b + 1], x["v"][b:b + 1], w.n_hi, lo_bit=LO)
+    rng = np.random.default_rng(8)
+    pages = rng.choice(w.ctx // 32, size=16, replace=False)
+    compare_records(cache, oc, samples=[(0, int(j), h) for j in pages for h in range(w.n_kv_heads)],
+                    seq_map={0: b})
+    err, _ = compare_decode(cache, oc, x["q"], max_seq_len=w.ctx, seq_map={0: b})
+    print(f"lo_bit 4 llama3_8b prefill, seq {b}: max abs err {err:.3g}", flush=True)
+    msl = w.ctx + steps + 1
+    out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device="cuda")
+    ws = cache.workspace(w.n_q_heads, msl)
+    for t in range(steps):
+        cache.decode_step(dev(x["k_new"][t]), dev(x["v_new"][t]), dev(x["q_new"][t]), max_seq_len=msl,
+                          out=out, workspace=ws)
+        O.append_token(oc, x["k_new"][t][b:b + 1], x["v_new"][t][b:b + 1])
+        if t in (0, 31, 32, steps - 1):
+            ref = O.decode_attention(oc, x["q_new"][t][b:b + 1])[0]
+            err = float(np.abs(host(out)[b] - ref).max())
+            assert err <= ATOL, (t, err)
+            print(f"lo_bit 4 llama3_8b fused step {t}, seq {b}: max abs err {err:.3g}", flush=True)
+    compare_tails(cache, oc, seq_map={0: b})
+    compare_records(cache, oc, samples=[(0, 128, h) for h in range(w.n_kv_heads)], seq_map={0: b})
