@@ -61,18 +61,19 @@ typedef struct {
   int32_t head_dim;    /* D; must be 128 */
   int32_t page_tokens; /* tokens per page = Key group size; must be 32 */
   int32_t n_kv_heads;  /* Hkv, 1..1024 */
-  int32_t n_hi;        /* boosted channels per page: 0 or a multiple of 16, <= D */
+  int32_t n_hi;        /* boosted channels per page, 0..D (any count) */
   int32_t lo_bit;      /* 2 (hi_bit 4) or 4 (hi_bit 8) */
 } kitty_config_t;
 
 /* A paged cache (Abstract: page-centric KV layout).  One physical page holds
  * the records of all Hkv heads for 32 consecutive tokens of one sequence; the
  * block table maps (sequence b, logical page j) to a physical page id.
- * Record layout of one (page, head), with b = lo_bit: K base plane 512*b B,
- * K boost plane 4*b*n_hi B, V codes 512*b B, kscale fp16[128], kmin
- * fp16[128], vscale fp16[4][32], vmin fp16[4][32], idx uint8[n_hi] --
- * 1024*(b + 1) + (4*b + 1)*n_hi bytes in total (3072 + 9*n_hi at lo_bit 2,
- * 5120 + 17*n_hi at lo_bit 4).  The code planes are 16*b-byte chunks, one per
+ * Record layout of one (page, head), with b = lo_bit and s = n_hi rounded up
+ * to a multiple of 16 (boost slots; slots n_hi .. s-1 hold code 0 and index
+ * 0): K base plane 512*b B, K boost plane 4*b*s B, V codes 512*b B, kscale
+ * fp16[128], kmin fp16[128], vscale fp16[4][32], vmin fp16[4][32], idx
+ * uint8[s] -- 1024*(b + 1) + (4*b + 1)*s bytes in total (3072 + 9*s at
+ * lo_bit 2, 5120 + 17*s at lo_bit 4).  The code planes are 16*b-byte chunks, one per
  * lane of a 64-lane wave, of 32-bit words of 32/b codes each (the chunk and
  * bit placement is the one internal header kitty_internal.h documents).  Head
  * h's record starts at byte h * kitty_record_bytes; a physical page is
@@ -94,7 +95,8 @@ int kitty_abi_version(void);
 /* Message for the last non-zero return on this thread ("" if none). */
 const char* kitty_last_error(void);
 
-/* Bytes of one (page, head) record: 1024 * (lo_bit + 1) + (4 * lo_bit + 1) * n_hi. */
+/* Bytes of one (page, head) record: 1024 * (lo_bit + 1) + (4 * lo_bit + 1) * s,
+ * s = n_hi rounded up to a multiple of 16. */
 int kitty_record_bytes(const kitty_config_t* cfg, size_t* out);
 
 /* Bytes of one physical page: n_kv_heads records, rounded up to 256. */

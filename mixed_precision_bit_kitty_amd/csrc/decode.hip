@@ -428,8 +428,8 @@ void decode_kernel(DecodeParams p) {
                          : p.seal_scratch + ((((size_t)b * p.n_kv_heads + hk) * (p.n_head_groups - 1)) +
                                              (hg - 1)) * RB;
       pq::quantize_page_wave<NHI, BITS>(pq::RowSrc{p.tail_k + toff, p.k_new + noff},
-                                  pq::RowSrc{p.tail_v + toff, p.v_new + noff}, seal_rec,
-                                  reinterpret_cast<uint8_t*>(&sm));
+                                        pq::RowSrc{p.tail_v + toff, p.v_new + noff}, seal_rec,
+                                        reinterpret_cast<uint8_t*>(&sm), p.n_hi);
     }
   }
 
@@ -902,7 +902,7 @@ static long max_range(long Pm, long n_wg, long W) {
 }
 
 int decode_max_wg_waves(int n_hi, int lo_bit) {
-  switch (n_hi) {
+  switch (boost_slots(n_hi)) {
     case 0: return max_wg_waves_t<0>(lo_bit);
     case 16: return max_wg_waves_t<16>(lo_bit);
     case 32: return max_wg_waves_t<32>(lo_bit);
@@ -940,7 +940,7 @@ SplitPlan plan_splits(int batch, int n_kv_heads, int n_head_groups, int max_seq_
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
-  switch (p.n_hi) {
+  switch (boost_slots(p.n_hi)) {  // instantiations by boost slots; the seal ranks p.n_hi channels
     case 0: return launch_decode_t<0>(p, stream);
     case 16: return launch_decode_t<16>(p, stream);
     case 32: return launch_decode_t<32>(p, stream);

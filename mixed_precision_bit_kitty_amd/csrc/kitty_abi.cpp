@@ -39,8 +39,8 @@ int check_config(const kitty_config_t* cfg) {
     return fail(KITTY_ERR_UNSUPPORTED, "page_tokens %d unsupported (only 32)", cfg->page_tokens);
   if (cfg->n_kv_heads < 1 || cfg->n_kv_heads > 1024)
     return fail(KITTY_ERR_INVALID_ARG, "n_kv_heads %d out of range [1, 1024]", cfg->n_kv_heads);
-  if (cfg->n_hi < 0 || cfg->n_hi > cfg->head_dim || cfg->n_hi % 16 != 0)
-    return fail(KITTY_ERR_UNSUPPORTED, "n_hi %d unsupported (0 or a multiple of 16 up to 128)", cfg->n_hi);
+  if (cfg->n_hi < 0 || cfg->n_hi > cfg->head_dim)
+    return fail(KITTY_ERR_UNSUPPORTED, "n_hi %d unsupported (0 to 128)", cfg->n_hi);
   if (cfg->lo_bit != 2 && cfg->lo_bit != 4)
     return fail(KITTY_ERR_UNSUPPORTED, "lo_bit %d unsupported (2 or 4)", cfg->lo_bit);
   return KITTY_OK;
@@ -76,7 +76,7 @@ const char* kitty_last_error(void) { return g_last_error.c_str(); }
 int kitty_record_bytes(const kitty_config_t* cfg, size_t* out) {
   if (int r = check_config(cfg)) return r;
   if (!out) return fail(KITTY_ERR_INVALID_ARG, "out is null");
-  *out = (size_t)kitty::rec_bytes(cfg->n_hi, cfg->lo_bit);
+  *out = (size_t)kitty::rec_bytes(kitty::boost_slots(cfg->n_hi), cfg->lo_bit);
   return ok();
 }
 
@@ -168,7 +168,7 @@ static int decode_shape(const kitty_config_t* cfg, int32_t batch, int32_t n_q_he
   const size_t part = (size_t)batch * n_q_heads * plan->n_wg * kitty::kPartialStride * sizeof(float);
   const size_t cnt = (size_t)batch * cfg->n_kv_heads * *n_head_groups * sizeof(int);
   const size_t seqc = (size_t)batch * kitty::kSeqCounterStride * sizeof(int);
-  const size_t seal = (size_t)batch * cfg->n_kv_heads * (*n_head_groups - 1) * kitty::rec_bytes(cfg->n_hi, cfg->lo_bit);
+  const size_t seal = (size_t)batch * cfg->n_kv_heads * (*n_head_groups - 1) * kitty::rec_bytes(kitty::boost_slots(cfg->n_hi), cfg->lo_bit);
   ws->partials = 0;
   ws->counters = r256(part);
   ws->seq_counters = ws->counters + r256(cnt);

@@ -50,8 +50,12 @@ constexpr int kHeadDim = 128;
 constexpr int kPageTokens = 32;
 constexpr int kVGroup = 32;
 
-// b = lo_bit (2 or 4)
+// b = lo_bit (2 or 4); n_hi here is the record's boost slot count, a
+// multiple of 16 (boost_slots of the boosted channel count)
 __host__ __device__ constexpr int rec_bytes(int n_hi, int b = 2) { return 1024 * b + 4 * b * n_hi + 1024 + n_hi; }
+// Boost slots of a record for n_hi boosted channels: n_hi rounded up to a
+// multiple of 16; slots n_hi .. boost_slots - 1 hold code 0 and index 0.
+__host__ __device__ constexpr int boost_slots(int n_hi) { return (n_hi + 15) / 16 * 16; }
 __host__ __device__ constexpr int off_kboost(int b = 2) { return 512 * b; }
 __host__ __device__ constexpr int off_v(int n_hi, int b = 2) { return 512 * b + 4 * b * n_hi; }
 __host__ __device__ constexpr int off_kscale(int n_hi, int b = 2) { return 1024 * b + 4 * b * n_hi; }
@@ -61,8 +65,9 @@ __host__ __device__ constexpr int off_vmin(int n_hi, int b = 2) { return off_ksc
 __host__ __device__ constexpr int off_idx(int n_hi, int b = 2) { return off_kscale(n_hi, b) + 1024; }
 static_assert(rec_bytes(32) == 3360 && off_idx(32) == 3328 && rec_bytes(32, 4) == 5664, "record layout");
 
+// n_hi: boosted channels (any count 0..128)
 __host__ __device__ inline int64_t page_stride_bytes(int n_kv_heads, int n_hi, int b = 2) {
-  int64_t raw = (int64_t)n_kv_heads * rec_bytes(n_hi, b);
+  int64_t raw = (int64_t)n_kv_heads * rec_bytes(boost_slots(n_hi), b);
   return (raw + 255) / 256 * 256;
 }
 

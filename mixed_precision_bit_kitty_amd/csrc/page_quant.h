@@ -168,9 +168,12 @@ struct RowSrc {
 // The Key half of a (page, head) record: statistics, ranking, codes, the two
 // code planes and the Key metadata.  Called by a full wave; uses the first
 // lds_vstep(NHI) bytes of `lds`.  BITS = lo_bit: 2 (hi 4 / lo 2) or 4
-// (hi 8 / lo 4).
+// (hi 8 / lo 4).  n (wave-uniform) channels are boosted, NHI - 16 < n <= NHI:
+// the record has NHI boost slots, and slots n .. NHI - 1 hold code 0 and
+// index 0.
 template <int NHI, int BITS = 2>
-__device__ __forceinline__ void quantize_keys_wave(RowSrc ks, uint8_t* __restrict__ rec, uint8_t* __restrict__ lds) {
+__device__ __forceinline__ void quantize_keys_wave(RowSrc ks, uint8_t* __restrict__ rec, uint8_t* __restrict__ lds,
+                                                   int n = NHI) {
 #pragma clang fp contract(off)
   static_assert(BITS == 2 || BITS == 4, "lo_bit 2 or 4");
   constexpr float kLo = (float)((1 << BITS) - 1), kHi = (float)((1 << (2 * BITS)) - 1);
@@ -212,12 +215,12 @@ __device__ __forceinline__ void quantize_keys_wave(RowSrc ks, uint8_t* __restric
   const float m2_1 = tree32(a);
   const float mn0 = (float)kmn[0], mx0 = (float)kmx[0], mn1 = (float)kmn[1], mx1 = (float)kmx[1];
 
-  // ---------------- Ranking: top NHI by m2, ties to the lower channel -------
+  // ---------------- Ranking: top n by m2, ties to the lower channel ---------
   const uint64_t below = (1ull << lane) - 1ull;
   bool h0, h1;
   if (NHI == 0) {
     h0 = h1 = false;
-  } else if (NHI == kHeadDim) {
+  } else if (NHI == kHeadDim && n == kHeadDim) {
     h0 = h1 = true;
   } else {
     const uint32_t b0 = __builtin_bit_cast(uint32_t, m2_0);
@@ -226,13 +229,13 @@ __device__ __forceinline__ void quantize_keys_wave(RowSrc ks, uint8_t* __restric
     for (int bit = 30; bit >= 0; --bit) {
       const uint32_t cand = T | (1u << bit);
       const int cnt = __popcll(__ballot(b0 >= cand)) + __popcll(__ballot(b1 >= cand));
-      if (cnt >= NHI) T = cand;
+      if (cnt >= n) T = cand;
     }
     const int gt = __popcll(__ballot(b0 > T)) + __popcll(__ballot(b1 > T));
     const uint64_t e0 = __ballot(b0 == T), e1 = __ballot(b1 == T);
     const int before0 = __popcll(e0 & below) + __popcll(e1 & below);
     const int before1 = before0 + (int)((e0 >> lane) & 1ull);
-    const int need = NHI - gt;
+    const int need = n - gt;
     h0 = (b0 > T) || (b0 == T && before0 < need);
     h1 = (b1 > T) || (b1 == T && before1 < need);
   }
@@ -248,11 +251,13 @@ __device__ __forceinline__ void quantize_keys_wave(RowSrc ks, uint8_t* __restric
   const uint16_t ks1 = h1 ? f2h(kBoostScale * h2f(st1.s16)) : st1.s16;
   *reinterpret_cast<uint32_t*>(rec + off_kscale(NHI, BITS) + 4 * lane) = (uint32_t)ks0 | ((uint32_t)ks1 << 16);
   *reinterpret_cast<uint32_t*>(rec + off_kmin(NHI, BITS) + 4 * lane) = (uint32_t)f2h(mn0) | ((uint32_t)f2h(mn1) << 16);
-  // (pos < NHI always holds: exactly NHI channels are selected)
+  // (pos < n always holds: exactly n channels are selected)
   const bool w0 = h0 && pos0 < NHI, w1 = h1 && pos1 < NHI;
   if (NHI > 0) {
     if (w0) rec[off_idx(NHI, BITS) + pos0] = (uint8_t)(2 * lane);
     if (w1) rec[off_idx(NHI, BITS) + pos1] = (uint8_t)(2 * lane + 1);
+    if (lane >= n && lane < NHI) rec[off_idx(NHI, BITS) + lane] = 0;  // padding slots (n < NHI)
+    if (lane + 64 >= n && lane + 64 < NHI) rec[off_idx(NHI, BITS) + lane + 64] = 0;
   }
   // Codes go to LDS as bytes of which only the low BITS bits are read back:
   // base = q >> BITS on a boosted channel, q elsewhere; boost = q (low bits).
@@ -304,10 +309,21 @@ __device__ __forceinline__ void quantize_keys_wave(RowSrc ks, uint8_t* __restric
     if (NHI > 0) {
       constexpr int nf = NHI / 32;
       uint8_t* const bp = rec + off_kboost(BITS);
+      // slots s >= n are padding: their LDS bytes were never written and
+      // pack as code 0 (a wave-uniform branch, taken only when n < NHI)
+      auto keep = [&](int s0) -> uint64_t {
+        const int v = n - s0;  // valid slots among s0 .. s0 + 7
+        return v >= 8 ? ~0ull : (v <= 0 ? 0ull : (1ull << (8 * v)) - 1ull);
+      };
 #pragma unroll
       for (int bb = 0; bb < nf; ++bb) {
-        const uint64_t A = *reinterpret_cast<const uint64_t*>(lds_boost + u * boost_row(NHI) + 32 * bb + 8 * w);
-        const uint64_t B = *reinterpret_cast<const uint64_t*>(lds_boost + (16 + u) * boost_row(NHI) + 32 * bb + 8 * w);
+        uint64_t A = *reinterpret_cast<const uint64_t*>(lds_boost + u * boost_row(NHI) + 32 * bb + 8 * w);
+        uint64_t B = *reinterpret_cast<const uint64_t*>(lds_boost + (16 + u) * boost_row(NHI) + 32 * bb + 8 * w);
+        if (n < NHI) {
+          const uint64_t m = keep(32 * bb + 8 * w);
+          A &= m;
+          B &= m;
+        }
         if (BITS == 2) {
           *reinterpret_cast<uint32_t*>(bp + 4 * (lane * nf + bb)) = pack_word(A, B);
         } else {
@@ -316,8 +332,13 @@ __device__ __forceinline__ void quantize_keys_wave(RowSrc ks, uint8_t* __restric
         }
       }
       if ((NHI % 32) != 0 && lane < 32) {
-        const uint64_t A = *reinterpret_cast<const uint64_t*>(lds_boost + u * boost_row(NHI) + 32 * nf + 8 * w);
-        const uint64_t B = *reinterpret_cast<const uint64_t*>(lds_boost + (16 + u) * boost_row(NHI) + 32 * nf + 8 * w);
+        uint64_t A = *reinterpret_cast<const uint64_t*>(lds_boost + u * boost_row(NHI) + 32 * nf + 8 * w);
+        uint64_t B = *reinterpret_cast<const uint64_t*>(lds_boost + (16 + u) * boost_row(NHI) + 32 * nf + 8 * w);
+        if (n < NHI) {
+          const uint64_t m = keep(32 * nf + 8 * w);
+          A &= m;
+          B &= m;
+        }
         if (BITS == 2) {
           *reinterpret_cast<uint32_t*>(bp + 256 * nf + 4 * lane) = pack_word(A, B);
         } else {
@@ -427,10 +448,12 @@ __device__ __forceinline__ void quantize_values_wave(RowSrc vs, uint8_t* __restr
 }
 
 // Quantize and pack one (page, head) into `rec` with one wave; `lds` is this
-// wave's private quant_lds_bytes(NHI) bytes.
+// wave's private quant_lds_bytes(NHI) bytes; n boosted channels (NHI - 16 <
+// n <= NHI).
 template <int NHI, int BITS = 2>
-__device__ __forceinline__ void quantize_page_wave(RowSrc ks, RowSrc vs, uint8_t* __restrict__ rec, uint8_t* __restrict__ lds) {
-  quantize_keys_wave<NHI, BITS>(ks, rec, lds);
+__device__ __forceinline__ void quantize_page_wave(RowSrc ks, RowSrc vs, uint8_t* __restrict__ rec, uint8_t* __restrict__ lds,
+                                                   int n = NHI) {
+  quantize_keys_wave<NHI, BITS>(ks, rec, lds, n);
   quantize_values_wave<NHI, BITS>(vs, rec, lds);
 }
 

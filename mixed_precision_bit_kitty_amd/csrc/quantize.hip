@@ -56,7 +56,7 @@ __global__ __launch_bounds__(128) void quantize_pages_kernel(QuantizeParams p) {
     uint8_t* rec = p.pages + (int64_t)phys * p.page_bytes + (int64_t)h * rec_bytes(NHI, BITS);
     const size_t row0 = seq_off + (size_t)page * kPageTokens * kHeadDim;
     if (wave == 0) {
-      quantize_keys_wave<NHI, BITS>(RowSrc{p.k + row0, nullptr}, rec, lds);
+      quantize_keys_wave<NHI, BITS>(RowSrc{p.k + row0, nullptr}, rec, lds, p.n_hi);
     } else {
       stage_value_page(p.v + row0, lds + kVStage, lane);
       quantize_values_wave<NHI, BITS>(RowSrc{reinterpret_cast<const _Float16*>(lds + kVStage), nullptr}, rec, lds);
@@ -100,7 +100,8 @@ __global__ __launch_bounds__(512) void append_token_kernel(AppendParams p) {  //
         if (phys >= 0 && (int64_t)phys < p.n_pages) {
           uint8_t* rec = p.pages + (int64_t)phys * p.page_bytes + (int64_t)h * rec_bytes(NHI, BITS);
           quantize_page_wave<NHI, BITS>(RowSrc{p.tail_k + tail_off, p.k_new + new_off},
-                                  RowSrc{p.tail_v + tail_off, p.v_new + new_off}, rec, lds_dyn + wave * kWaveLds);
+                                        RowSrc{p.tail_v + tail_off, p.v_new + new_off}, rec, lds_dyn + wave * kWaveLds,
+                                        p.n_hi);
         }
       }
     }
@@ -131,8 +132,9 @@ hipError_t launch_append_t(const AppendParams& p, hipStream_t stream) {
 
 }  // namespace
 
+// Instantiations by boost slots: n_hi rounded up to a multiple of 16.
 #define KITTY_NHI_DISPATCH(fn, nhi, ...)                   \
-  switch (nhi) {                                           \
+  switch (boost_slots(nhi)) {                              \
     case 0: return fn<0>(__VA_ARGS__);                     \
     case 16: return fn<16>(__VA_ARGS__);                   \
     case 32: return fn<32>(__VA_ARGS__);                   \

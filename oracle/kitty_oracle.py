@@ -213,7 +213,8 @@ def dequant_v(a, vscale, vmin):
 #
 # This layout is this library's own design (the pages fix only that a page
 # holds two uniform 2-bit Key tensors plus the boosted channel list).  Field
-# order and sizes, n = n_hi boosted channels (0 or a multiple of 16, <= D):
+# order and sizes, n = boost slots = n_hi rounded up to a multiple of 16
+# (slots n_hi .. n - 1 are padding: boost code 0, index 0; see boost_slots):
 #
 #   0            K base codes   1024 B   64 chunks x 16 B
 #   1024         K boost codes  8n B     (see _boost_words)
@@ -256,13 +257,22 @@ def dequant_v(a, vscale, vmin):
 #
 # Value metadata index kappa = 8w + e stands for token tau(w, e).
 
+def boost_slots(n_hi):
+    """Boost slots of a record holding n_hi boosted channels: n_hi rounded up
+    to a multiple of 16, so the slot blocks keep their shape for any
+    hi_fraction; the padding slots hold code 0 and index 0 and stand for no
+    channel."""
+    return -(-int(n_hi) // 16) * 16
+
+
 def record_bytes(n_hi, head_dim=HEAD_DIM, lo_bit=2):
     if head_dim != HEAD_DIM:
         raise ValueError("the record layout is defined for head_dim 128")
-    if n_hi < 0 or n_hi > head_dim or n_hi % 16:
-        raise ValueError("n_hi must be 0 or a multiple of 16 up to head_dim")
+    if n_hi < 0 or n_hi > head_dim:
+        raise ValueError("n_hi must be in 0..head_dim")
     levels(lo_bit)
-    return 1024 * lo_bit + 4 * lo_bit * n_hi + 1024 + n_hi
+    n = boost_slots(n_hi)
+    return 1024 * lo_bit + 4 * lo_bit * n + 1024 + n
 
 
 def page_bytes(n_kv_heads, n_hi, lo_bit=2):
@@ -409,11 +419,17 @@ def _boost_offsets(n_hi, lo_bit):
 def pack_record(kf, vf):
     """Bytes of one page record (uint8 [record_bytes]) from the logical fields
     of quant_k_page / quant_v_page for a single page (no leading dims); the
-    bit-width pair is kf["lo_bit"] (2 if absent)."""
-    n_hi = kf["idx"].shape[-1]
+    bit-width pair is kf["lo_bit"] (2 if absent).  Padding slots beyond the
+    n_hi boosted channels get code 0 and index 0."""
+    n_real = kf["idx"].shape[-1]
+    n_hi = boost_slots(n_real)
     lo_bit = int(kf.get("lo_bit", 2))
-    out = np.zeros(record_bytes(n_hi, lo_bit=lo_bit), np.uint8)
-    base, boost, a = kf["base"], kf["boost"], vf["a"]
+    out = np.zeros(record_bytes(n_real, lo_bit=lo_bit), np.uint8)
+    base, a = kf["base"], vf["a"]
+    boost = np.zeros((PAGE_TOKENS, n_hi), np.uint8)
+    boost[:, :n_real] = kf["boost"]
+    idx = np.zeros(n_hi, np.uint8)
+    idx[:n_real] = kf["idx"]
     tA, tB, ch = _kbase_index()
     o = _put_plane(out, 0, base[tA, ch], base[tB, ch], lo_bit)
     offs, bA, bB, sl = _boost_slots(n_hi)
@@ -437,15 +453,17 @@ def pack_record(kf, vf):
     for arr in (vf["vscale"], vf["vmin"]):          # [32 tokens, 4 groups]
         out[o:o + 256] = np.ascontiguousarray(np.asarray(arr, "<f2")[kt, :].T).view(np.uint8).reshape(-1)
         o += 256
-    out[o:o + n_hi] = kf["idx"]
+    out[o:o + n_hi] = idx
     return out
 
 
 def unpack_record(buf, n_hi, lo_bit=2):
-    """Inverse of pack_record: logical fields from one record's bytes."""
+    """Inverse of pack_record: logical fields from one record's bytes (the
+    n_hi boosted channels; padding slots are dropped)."""
     buf = np.asarray(buf, np.uint8)
     if buf.shape[0] != record_bytes(n_hi, lo_bit=lo_bit):
         raise ValueError("record size mismatch")
+    n_real, n_hi = n_hi, boost_slots(n_hi)
     base = np.zeros((PAGE_TOKENS, HEAD_DIM), np.uint8)
     tA, tB, ch = _kbase_index()
     a8, b8, o = _get_plane(buf, 0, lo_bit)
@@ -478,7 +496,8 @@ def unpack_record(buf, n_hi, lo_bit=2):
     vs[kt, :] = buf[o:o + 256].view("<f2").reshape(4, 32).T
     vm[kt, :] = buf[o + 256:o + 512].view("<f2").reshape(4, 32).T
     o += 512
-    idx = buf[o:o + n_hi].copy()
+    idx = buf[o:o + n_real].copy()
+    boost = boost[:, :n_real].copy()
     return (dict(base=base, boost=boost, kscale=kscale, kmin=kmin, idx=idx, lo_bit=lo_bit),
             dict(a=a, vscale=vs, vmin=vm))
 

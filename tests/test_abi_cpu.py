@@ -7,6 +7,7 @@ import re
 
 import pytest
 
+import oracle as O
 from mixed_precision_bit_kitty_amd import binding as B
 
 LIB = B.LIB_PATH
@@ -39,10 +40,12 @@ def test_abi_version():
 
 
 @pytest.mark.parametrize("lo_bit,base,per_hi", [(2, 3072, 9), (4, 5120, 17)])
-@pytest.mark.parametrize("n_hi", [0, 16, 32, 48, 64, 128])
+@pytest.mark.parametrize("n_hi", [0, 1, 13, 16, 32, 45, 48, 64, 100, 127, 128])
 def test_sizes(n_hi, lo_bit, base, per_hi):
     cfg = B.config(8, n_hi, lo_bit=lo_bit)
-    rb = base + per_hi * n_hi
+    slots = -(-n_hi // 16) * 16  # boost slots: n_hi rounded up to a multiple of 16
+    rb = base + per_hi * slots
+    assert rb == O.record_bytes(n_hi, lo_bit=lo_bit)
     assert B.kitty_record_bytes(cfg) == rb
     pb = B.kitty_page_bytes(cfg)
     assert pb % 256 == 0 and pb >= 8 * rb and pb - 8 * rb < 256
@@ -110,7 +113,7 @@ def test_workspace_bytes_monotone_in_max_seq_len():
     ((64, 32, 8, 32, 2), B.KITTY_ERR_UNSUPPORTED),
     ((128, 16, 8, 32, 2), B.KITTY_ERR_UNSUPPORTED),
     ((128, 32, 0, 32, 2), B.KITTY_ERR_INVALID_ARG),
-    ((128, 32, 8, 8, 2), B.KITTY_ERR_UNSUPPORTED),
+    ((128, 32, 8, 129, 2), B.KITTY_ERR_UNSUPPORTED),
     ((128, 32, 8, 144, 2), B.KITTY_ERR_UNSUPPORTED),
     ((128, 32, 8, -16, 2), B.KITTY_ERR_UNSUPPORTED),
     ((128, 32, 8, 32, 3), B.KITTY_ERR_UNSUPPORTED),
@@ -182,7 +185,8 @@ def test_quantize_arguments():
     assert _call_quantize(v, S=-1) == B.KITTY_ERR_INVALID_ARG
     assert _call_quantize(v, S=96) == B.KITTY_ERR_INVALID_ARG          # 3 pages > max_pages 2
     assert _call_quantize(v, lens=FAKE + 2) == B.KITTY_ERR_INVALID_ARG
-    assert _call_quantize(v, cfg=B.config(8, 24)) == B.KITTY_ERR_UNSUPPORTED
+    assert _call_quantize(v, cfg=B.config(8, 136)) == B.KITTY_ERR_UNSUPPORTED
+    assert _call_quantize(v, cfg=B.config(8, 32, lo_bit=3)) == B.KITTY_ERR_UNSUPPORTED
 
 
 def test_append_arguments():

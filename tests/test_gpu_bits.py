@@ -11,7 +11,7 @@ import pytest
 import oracle as O
 from mixed_precision_bit_kitty_amd import synth
 
-from _gpu_util import ATOL, compare_decode, compare_records, compare_tails, dev, host, new_cache
+from _gpu_util import ATOL, compare_decode, compare_records, compare_tails, dev, host, new_cache, step_twins
 
 pytestmark = pytest.mark.gpu
 
@@ -167,61 +167,22 @@ def test_decode_edge_values():
         compare_decode(cache, oc, q)
 
 
-def _step_twins(w, lens, steps, ctx, n_hi=32, msl=None, check_every=1):
-    """Twin 4-bit caches: one through the fused step, one through append +
-    decode attention; pools, tails, lengths byte-equal after every step,
-    outputs bit-equal on steps without a seal, both within 2e-3 of the
-    oracle."""
-    import torch
-    batch = len(lens)
-    x = synth.batch(w, batch=batch, ctx=ctx, steps=steps)
-    cap = max(lens) + steps + 32
-    fused, split = [new_cache(batch, w.n_kv_heads, n_hi, cap, lo_bit=LO) for _ in range(2)]
-    for c in (fused, split):
-        c.quantize_pages(dev(x["k"]), dev(x["v"]), lens=dev(np.array(lens, np.int32)))
-    oc = O.quantize_pages(x["k"], x["v"], n_hi, batch_lens=lens, lo_bit=LO)
-    msl = max(lens) + steps if msl is None else msl
-    outs = [torch.zeros((batch, w.n_q_heads, 128), dtype=torch.float32, device="cuda") for _ in range(2)]
-    worst = 0.0
-    for t in range(steps):
-        k, v, q = dev(x["k_new"][t]), dev(x["v_new"][t]), dev(x["q_new"][t])
-        seals = [b for b in range(batch) if int(oc.seq_len[b]) % 32 == 31]
-        fused.decode_step(k, v, q, max_seq_len=msl, out=outs[0])
-        split.append_token(k, v)
-        split.decode_attention(q, max_seq_len=msl, out=outs[1])
-        O.append_token(oc, x["k_new"][t], x["v_new"][t])
-        a, b = host(outs[0]), host(outs[1])
-        if not seals:
-            assert np.array_equal(a, b), f"step {t}: fused and separate outputs differ without a seal"
-        assert np.array_equal(host(fused.seq_lens), host(split.seq_lens)), f"step {t}"
-        assert np.array_equal(host(fused.tail_k), host(split.tail_k)), f"step {t}"
-        if seals or t % check_every == 0 or t == steps - 1:
-            assert np.array_equal(host(fused.pool), host(split.pool)), f"step {t}: page pools differ"
-            compare_tails(fused, oc)
-            ref = O.decode_attention(oc, x["q_new"][t])
-            err = float(np.abs(a - ref).max())
-            worst = max(worst, err)
-            assert err <= ATOL, f"step {t}: max abs err {err}"
-    compare_records(fused, oc)
-    return worst
-
-
 @pytest.mark.parametrize("hkv,hq", [(2, 8), (2, 12), (1, 2)])
 def test_step_ragged_batch_across_seals(hkv, hq):
     w = synth.LLAMA3_8B.with_(n_kv_heads=hkv, n_q_heads=hq)
-    worst = _step_twins(w, [0, 31, 45, 63], 40, 64)
+    worst = step_twins(w, [0, 31, 45, 63], 40, 64, lo_bit=LO)
     print(f"lo_bit 4 fused step Hkv {hkv} Hq {hq}: max abs err {worst:.3g}")
 
 
 @pytest.mark.parametrize("n_hi", [0, 128])
 def test_step_boost_widths(n_hi):
     w = synth.LLAMA3_8B.with_(n_kv_heads=2, n_q_heads=8)
-    _step_twins(w, [30, 62], 4, 64, n_hi=n_hi)
+    step_twins(w, [30, 62], 4, 64, n_hi=n_hi, lo_bit=LO)
 
 
 def test_step_several_workgroups():
     w = synth.LLAMA3_8B.with_(n_kv_heads=2, n_q_heads=8)
-    worst = _step_twins(w, [2015, 1500, 7], 36, 2015, check_every=5)
+    worst = step_twins(w, [2015, 1500, 7], 36, 2015, check_every=5, lo_bit=LO)
     print(f"lo_bit 4 fused step, several workgroups: max abs err {worst:.3g}")
 
 

@@ -74,10 +74,14 @@ def test_record_sizes():
     for n in (0, 16, 32, 64, 128):
         assert O.record_bytes(n) == 3072 + 9 * n
         assert O.record_bytes(n) % 16 == 0
+    # other widths keep the shape of the next multiple of 16
+    for n, slots in ((1, 16), (8, 16), (13, 16), (17, 32), (45, 48), (127, 128)):
+        assert O.boost_slots(n) == slots
+        assert O.record_bytes(n) == 3072 + 9 * slots
     with pytest.raises(ValueError):
-        O.record_bytes(8)
+        O.record_bytes(129)
     with pytest.raises(ValueError):
-        O.record_bytes(144)
+        O.record_bytes(-1)
     assert O.page_bytes(8, 32) == 26880
 
 
