@@ -40,12 +40,12 @@
 extern "C" {
 #endif
 
-#define KITTY_ABI_VERSION 2
+#define KITTY_ABI_VERSION 3
 
 enum {
   KITTY_OK = 0,
   KITTY_ERR_INVALID_ARG = -1, /* null pointer, negative/inconsistent size, misalignment */
-  KITTY_ERR_UNSUPPORTED = -2, /* head_dim != 128, page_tokens != 32, bad n_hi or lo_bit */
+  KITTY_ERR_UNSUPPORTED = -2, /* head_dim != 128, page_tokens != 32, bad n_hi, lo_bit or rank_mode */
   KITTY_ERR_WORKSPACE = -3,   /* workspace smaller than kitty_decode_workspace_bytes */
   KITTY_ERR_HIP = -4,         /* a kernel launch failed (hipGetLastError) */
   KITTY_ERR_NO_PAGES = -5     /* kitty_pool_reserve: the pool has too few free pages */
@@ -63,7 +63,27 @@ typedef struct {
   int32_t n_kv_heads;  /* Hkv, 1..1024 */
   int32_t n_hi;        /* boosted channels per page, 0..D (any count) */
   int32_t lo_bit;      /* 2 (hi_bit 4) or 4 (hi_bit 8) */
+  int32_t rank_mode;   /* KITTY_RANK_PAGE or KITTY_RANK_RUNNING */
 } kitty_config_t;
+
+/* Ranking modes (which channels of a page are boosted):
+ *  KITTY_RANK_PAGE: by the page's own per-channel variance over its 32 tokens
+ *    ("How it works / Prefill phase" steps 1-2 applied per page).
+ *  KITTY_RANK_RUNNING: by the head's running variance ("How it works":
+ *    Prefill step 1 over the whole prefill sequence, step 5 and "Decode
+ *    phase" steps 1-2 running sums of k and k^2): prefill pages take the
+ *    ranking over all prefill tokens of their sequence (tail included), a page
+ *    sealed by an append the ranking over every token stored at that moment.
+ *    The sums are exact (k * 2^24 is an integer for every fp16 k), so the
+ *    ranking does not depend on the order of accumulation.  Needs
+ *    kitty_kv_view_t.key_stats; at most 2^23 tokens per sequence. */
+enum { KITTY_RANK_PAGE = 0, KITTY_RANK_RUNNING = 1 };
+
+/* Bytes of running-mode state per (sequence, KV head): int64 s1[128] (sum of
+ * k * 2^24), uint64 s2_lo[128] and s2_hi[128] (the 128-bit sum of (k * 2^24)^2),
+ * uint32 mask[4] (the ranking of the last prefill: channel c at bit c & 31 of
+ * word c >> 5), then reserved bytes. */
+#define KITTY_KEY_STATS_BYTES 4096
 
 /* A paged cache (Abstract: page-centric KV layout).  One physical page holds
  * the records of all Hkv heads for 32 consecutive tokens of one sequence; the
@@ -87,6 +107,10 @@ typedef struct {
   uint16_t* tail_k;           /* device fp16 [batch][Hkv][32][D]: the unsealed tail page */
   uint16_t* tail_v;           /* device fp16 [batch][Hkv][32][D] */
   int32_t* seq_lens;          /* device int32 [batch]: tokens stored (sealed pages + tail) */
+  void* key_stats;            /* device [batch][Hkv][KITTY_KEY_STATS_BYTES], 16-byte aligned: running
+                                 sums (KITTY_RANK_RUNNING only; ignored, may be NULL, otherwise).  Prefill
+                                 writes them for the sequences it fills, append and the fused step add
+                                 every appended token; their contents are only meaningful to this library */
 } kitty_kv_view_t;
 
 /* Version of this ABI (KITTY_ABI_VERSION). */
@@ -111,7 +135,11 @@ int kitty_page_bytes(const kitty_config_t* cfg, size_t* out);
  * into tail_k / tail_v slots 0.., and seq_lens[b] = n_b.  lens: optional
  * device int32 [batch]; a negative lens[b] leaves sequence b untouched (no
  * page, tail or length written), so that one call can fill some slots of a
- * serving batch while the others keep decoding.  Requires floor(S / 32) <= max_pages. */
+ * serving batch while the others keep decoding.  Requires floor(S / 32) <= max_pages.
+ * KITTY_RANK_RUNNING: first the exact running sums over each filled
+ * sequence's n_b tokens are written to its key_stats (replacing what was
+ * there), then every page of the sequence is quantized with the ranking
+ * they give; S <= 2^23. */
 int kitty_quantize_pages(const kitty_config_t* cfg, const kitty_kv_view_t* kv,
                          const uint16_t* k, const uint16_t* v, int32_t S,
                          const int32_t* lens, void* stream);
@@ -123,7 +151,9 @@ int kitty_quantize_pages(const kitty_config_t* cfg, const kitty_kv_view_t* kv,
  * full tail is quantized exactly like a prefill page and written to physical
  * page block_table[b][n / 32] (the tail page stays fp16 until it fills).  The
  * caller maps block_table[b][n / 32] to a free page before that append; a
- * seal with n / 32 >= max_pages is skipped. */
+ * seal with n / 32 >= max_pages is skipped.  KITTY_RANK_RUNNING: the token is
+ * added to the sequence's key_stats first, and a sealed page takes the
+ * ranking over all n + 1 tokens. */
 int kitty_append_token(const kitty_config_t* cfg, const kitty_kv_view_t* kv,
                        const uint16_t* k_new, const uint16_t* v_new, void* stream);
 
@@ -169,7 +199,7 @@ int kitty_decode_attention(const kitty_config_t* cfg, const kitty_kv_view_t* kv,
  * and zero-fill rules) and the errors are those of kitty_decode_attention.
  * The result equals the two separate calls' within floating-point rounding
  * (the page sealed by this call is folded in by another wave); the records,
- * tails and lengths it writes are identical. */
+ * tails, lengths and (KITTY_RANK_RUNNING) key_stats it writes are identical. */
 int kitty_decode_step(const kitty_config_t* cfg, const kitty_kv_view_t* kv, const uint16_t* k_new,
                       const uint16_t* v_new, const uint16_t* q, int32_t n_q_heads, int32_t max_seq_len,
                       float* out, void* workspace, size_t workspace_bytes, void* stream);

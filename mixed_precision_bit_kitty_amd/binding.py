@@ -25,6 +25,9 @@ KITTY_ERR_UNSUPPORTED = -2
 KITTY_ERR_WORKSPACE = -3
 KITTY_ERR_HIP = -4
 KITTY_ERR_NO_PAGES = -5
+KITTY_RANK_PAGE = 0
+KITTY_RANK_RUNNING = 1
+KITTY_KEY_STATS_BYTES = 4096
 
 HEAD_DIM = 128
 PAGE_TOKENS = 32
@@ -38,14 +41,15 @@ class KittyError(RuntimeError):
 
 class kitty_config_t(ctypes.Structure):
     _fields_ = [("head_dim", ctypes.c_int32), ("page_tokens", ctypes.c_int32),
-                ("n_kv_heads", ctypes.c_int32), ("n_hi", ctypes.c_int32), ("lo_bit", ctypes.c_int32)]
+                ("n_kv_heads", ctypes.c_int32), ("n_hi", ctypes.c_int32), ("lo_bit", ctypes.c_int32),
+                ("rank_mode", ctypes.c_int32)]
 
 
 class kitty_kv_view_t(ctypes.Structure):
     _fields_ = [("pages", ctypes.c_void_p), ("n_pages", ctypes.c_int64),
                 ("block_table", ctypes.c_void_p), ("batch", ctypes.c_int32),
                 ("max_pages", ctypes.c_int32), ("tail_k", ctypes.c_void_p),
-                ("tail_v", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p)]
+                ("tail_v", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p), ("key_stats", ctypes.c_void_p)]
 
 
 class kitty_pool_t(ctypes.Structure):
@@ -106,9 +110,10 @@ def _check(rc):
         raise KittyError(rc, load().kitty_last_error().decode())
 
 
-def config(n_kv_heads, n_hi, head_dim=HEAD_DIM, page_tokens=PAGE_TOKENS, lo_bit=2):
-    """lo_bit 2: (hi_bit 4, lo_bit 2); lo_bit 4: (hi_bit 8, lo_bit 4)."""
-    return kitty_config_t(head_dim, page_tokens, n_kv_heads, n_hi, lo_bit)
+def config(n_kv_heads, n_hi, head_dim=HEAD_DIM, page_tokens=PAGE_TOKENS, lo_bit=2, rank_mode=0):
+    """lo_bit 2: (hi_bit 4, lo_bit 2); lo_bit 4: (hi_bit 8, lo_bit 4).
+    rank_mode: KITTY_RANK_PAGE (0) or KITTY_RANK_RUNNING (1)."""
+    return kitty_config_t(head_dim, page_tokens, n_kv_heads, n_hi, lo_bit, rank_mode)
 
 
 def kitty_abi_version():
@@ -218,13 +223,15 @@ class KittyCache:
                 sequence b's page j -> physical page b * max_pages + j)
     tail_k/v    fp16  [batch, Hkv, 32, 128]
     seq_lens    int32 [batch]
+    key_stats   uint8 [batch, Hkv, 4096] running sums (rank_mode KITTY_RANK_RUNNING only, else None)
     """
 
     def __init__(self, batch, n_kv_heads, n_hi, max_tokens, device="cuda", block_table=None, n_pages=None,
-                 lo_bit=2):
+                 lo_bit=2, rank_mode=KITTY_RANK_PAGE):
         import torch
-        self.cfg = config(n_kv_heads, n_hi, lo_bit=lo_bit)
+        self.cfg = config(n_kv_heads, n_hi, lo_bit=lo_bit, rank_mode=rank_mode)
         self.batch, self.n_kv_heads, self.n_hi, self.lo_bit = batch, n_kv_heads, n_hi, lo_bit
+        self.rank_mode = rank_mode
         self.max_pages = max(1, -(-max_tokens // PAGE_TOKENS))
         self.page_bytes = kitty_page_bytes(self.cfg)
         self.record_bytes = kitty_record_bytes(self.cfg)
@@ -244,19 +251,24 @@ class KittyCache:
         self.tail_k = torch.zeros((batch, n_kv_heads, PAGE_TOKENS, HEAD_DIM), dtype=torch.float16, device=device)
         self.tail_v = torch.zeros_like(self.tail_k)
         self.seq_lens = torch.zeros(batch, dtype=torch.int32, device=device)
+        self.key_stats = None
+        if rank_mode == KITTY_RANK_RUNNING:
+            self.key_stats = torch.zeros((batch, n_kv_heads, KITTY_KEY_STATS_BYTES), dtype=torch.uint8, device=device)
         self.view = kitty_kv_view_t(self.pool.data_ptr(), self.n_pages, self.block_table.data_ptr(), batch,
                                     self.max_pages, self.tail_k.data_ptr(), self.tail_v.data_ptr(),
-                                    self.seq_lens.data_ptr())
+                                    self.seq_lens.data_ptr(),
+                                    None if self.key_stats is None else self.key_stats.data_ptr())
         self._ws = None
 
     @classmethod
-    def with_pool(cls, batch, n_kv_heads, n_hi, max_tokens, n_pages, device="cuda", lo_bit=2):
+    def with_pool(cls, batch, n_kv_heads, n_hi, max_tokens, n_pages, device="cuda", lo_bit=2, rank_mode=KITTY_RANK_PAGE):
         """A serving cache: every slot starts inactive (seq_lens -1, no page
         mapped) and pages come from a shared PagePool of n_pages pages."""
         import numpy as np
         max_pages = max(1, -(-max_tokens // PAGE_TOKENS))
         c = cls(batch, n_kv_heads, n_hi, max_tokens, device=device,
-                block_table=np.full((batch, max_pages), -1, np.int32), n_pages=n_pages, lo_bit=lo_bit)
+                block_table=np.full((batch, max_pages), -1, np.int32), n_pages=n_pages, lo_bit=lo_bit,
+                rank_mode=rank_mode)
         c.bt_host = np.full((batch, c.max_pages), -1, np.int32)
         c.page_pool = PagePool(n_pages)
         c.seq_lens.fill_(-1)

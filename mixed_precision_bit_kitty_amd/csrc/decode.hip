@@ -185,6 +185,7 @@ struct alignas(16) Lds {  // 16-byte aligned size: every wave's area keeps 16-by
   };
   float red[2][4][4];           // final corrections [kind][head][group]
   int flag;                     // workgroup broadcast of the arrival count (wave 0's copy)
+  int seq_flag;                 // workgroup broadcast of the sequence arrival count (wave 0's copy)
 };
 static_assert(sizeof(float) * 4 * kPartialStride <= kRing * rec_bytes(0), "partial fits over the ring");
 constexpr int kLdsPerCu = 160 * 1024;
@@ -349,7 +350,9 @@ __host__ __device__ __forceinline__ int weight_prefix(int i, int W) {
 //    the logits of head w at tokens n (combo A) and n + 16 (combo B);
 //  * PV has channels as rows and (head n & 3, limb (n >> 2) & 1) as columns
 //    0..7, the p limbs for the value-minimum correction as columns 8..15.
-template <int NHI, int BITS>
+// RUN: the fused step in the running ranking mode (p.key_stats set); a
+// separate instantiation, so the page mode's kernels carry none of its code.
+template <int NHI, int BITS, bool RUN>
 __global__ __launch_bounds__(64 * kMaxWgWaves) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void decode_kernel(DecodeParams p) {
   constexpr int NB = (NHI + 31) / 32;  // boost slot blocks (the last may be half)
@@ -427,9 +430,18 @@ void decode_kernel(DecodeParams p) {
       seal_rec = hg == 0 ? p.pages + (int64_t)phys * p.page_bytes + (int64_t)hk * RB
                          : p.seal_scratch + ((((size_t)b * p.n_kv_heads + hk) * (p.n_head_groups - 1)) +
                                              (hg - 1)) * RB;
+      pq::RankIn rk{false, false, false};
+      if constexpr (RUN) {
+        // running ranking mode ("Kitty -- Dynamic Channel-wise Mixed-Precision
+        // Keys", Decode phase steps 1-2): the head's sums with the new token
+        // (in registers; the sequence's last unit stores them) rank the page
+        pq::LaneSums r = pq::load_sums(p.key_stats + ((size_t)b * p.n_kv_heads + hk) * pq::kStatsBytes, lane);
+        pq::add_token(r, *reinterpret_cast<const uint32_t*>(p.k_new + noff + 2 * lane));
+        rk = pq::running_rank(r, (uint32_t)n0 + 1, p.n_hi, lane);
+      }
       pq::quantize_page_wave<NHI, BITS>(pq::RowSrc{p.tail_k + toff, p.k_new + noff},
                                         pq::RowSrc{p.tail_v + toff, p.v_new + noff}, seal_rec,
-                                        reinterpret_cast<uint8_t*>(&sm), p.n_hi);
+                                        reinterpret_cast<uint8_t*>(&sm), p.n_hi, rk);
     }
   }
 
@@ -766,6 +778,22 @@ void decode_kernel(DecodeParams p) {
       __hip_atomic_store(p.seq_lens + b, n0 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(seq_counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    if (RUN && fused) {
+      // running mode: every unit of the sequence has read the old sums (its
+      // tail wave did, before the unit counted itself), so the last unit adds
+      // the new token to the sums of every KV head of the sequence
+      if (threadIdx.x == 0) all[0].seq_flag = old;
+      __syncthreads();
+      if (all[0].seq_flag == units - 1) {
+        for (int i = threadIdx.x; i < p.n_kv_heads * 64; i += nthr) {
+          const int h2 = i >> 6, l2 = i & 63;
+          uint8_t* st = p.key_stats + ((size_t)b * p.n_kv_heads + h2) * pq::kStatsBytes;
+          pq::LaneSums r = pq::load_sums(st, l2);
+          pq::add_token(r, *reinterpret_cast<const uint32_t*>(p.k_new + ((size_t)b * p.n_kv_heads + h2) * kHeadDim + 2 * l2));
+          pq::store_sums(st, l2, r);
+        }
+      }
+    }
   };
   auto out_of = [&](int o) { return p.out + ((size_t)b * p.n_q_heads + hq0 + (o >> 7)) * kHeadDim + (o & 127); };
   float* gpart = p.partial + ((size_t)b * p.n_q_heads + hq0) * p.n_wg * kPartialStride;
@@ -860,18 +888,25 @@ void decode_kernel(DecodeParams p) {
   sequence_arrival(seq_old, p.n_kv_heads * p.n_head_groups);
 }
 
-template <int NHI, int BITS>
-hipError_t launch_decode_nb(const DecodeParams& p, hipStream_t stream) {
+template <int NHI, int BITS, bool RUN>
+hipError_t launch_decode_nbr(const DecodeParams& p, hipStream_t stream) {
   constexpr int wmax = max_wg_waves<NHI, BITS>();
   if (p.wg_waves < 2 || p.wg_waves > wmax) return hipErrorInvalidValue;
   const size_t lds = sizeof(Lds<NHI, BITS>) * p.wg_waves;
   static const hipError_t attr =  // once per instantiation: allow the largest workgroup's LDS
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<NHI, BITS>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<NHI, BITS, RUN>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)(sizeof(Lds<NHI, BITS>) * wmax));
   if (attr != hipSuccess) return attr;
   dim3 grid(p.n_wg, p.n_kv_heads * p.n_head_groups, p.batch);
-  hipLaunchKernelGGL((decode_kernel<NHI, BITS>), grid, dim3(64 * p.wg_waves), lds, stream, p);
+  hipLaunchKernelGGL((decode_kernel<NHI, BITS, RUN>), grid, dim3(64 * p.wg_waves), lds, stream, p);
   return hipGetLastError();
+}
+
+template <int NHI, int BITS>
+hipError_t launch_decode_nb(const DecodeParams& p, hipStream_t stream) {
+  // only the fused step uses the running sums; plain decode attention reads records alone
+  if (p.k_new && p.key_stats) return launch_decode_nbr<NHI, BITS, true>(p, stream);
+  return launch_decode_nbr<NHI, BITS, false>(p, stream);
 }
 
 template <int NHI>

@@ -43,6 +43,9 @@ int check_config(const kitty_config_t* cfg) {
     return fail(KITTY_ERR_UNSUPPORTED, "n_hi %d unsupported (0 to 128)", cfg->n_hi);
   if (cfg->lo_bit != 2 && cfg->lo_bit != 4)
     return fail(KITTY_ERR_UNSUPPORTED, "lo_bit %d unsupported (2 or 4)", cfg->lo_bit);
+  if (cfg->rank_mode != KITTY_RANK_PAGE && cfg->rank_mode != KITTY_RANK_RUNNING)
+    return fail(KITTY_ERR_UNSUPPORTED, "rank_mode %d unsupported (KITTY_RANK_PAGE or KITTY_RANK_RUNNING)",
+                cfg->rank_mode);
   return KITTY_OK;
 }
 
@@ -56,8 +59,14 @@ int check_view(const kitty_config_t* cfg, const kitty_kv_view_t* kv) {
   if (!kv->tail_k || !kv->tail_v || !aligned(kv->tail_k, 16) || !aligned(kv->tail_v, 16))
     return fail(KITTY_ERR_INVALID_ARG, "tail_k / tail_v null or not 16-byte aligned");
   if (!kv->seq_lens || !aligned(kv->seq_lens, 4)) return fail(KITTY_ERR_INVALID_ARG, "seq_lens null or misaligned");
-  (void)cfg;
+  if (cfg->rank_mode == KITTY_RANK_RUNNING && (!kv->key_stats || !aligned(kv->key_stats, 16)))
+    return fail(KITTY_ERR_INVALID_ARG, "the running ranking mode needs key_stats, 16-byte aligned");
   return KITTY_OK;
+}
+
+// the running sums of a (sequence, KV head), or null in the page ranking mode
+uint8_t* key_stats_of(const kitty_config_t* cfg, const kitty_kv_view_t* kv) {
+  return cfg->rank_mode == KITTY_RANK_RUNNING ? static_cast<uint8_t*>(kv->key_stats) : nullptr;
 }
 
 int check_launch(hipError_t e, const char* what) {
@@ -97,6 +106,8 @@ int kitty_quantize_pages(const kitty_config_t* cfg, const kitty_kv_view_t* kv, c
     return fail(KITTY_ERR_INVALID_ARG, "S / 32 = %d exceeds max_pages %d", S / kitty::kPageTokens, kv->max_pages);
   if (S / kitty::kPageTokens + 1 > 2147483647 / 1) return fail(KITTY_ERR_INVALID_ARG, "S too large");
   if (lens && !aligned(lens, 4)) return fail(KITTY_ERR_INVALID_ARG, "lens misaligned");
+  if (cfg->rank_mode == KITTY_RANK_RUNNING && S > kitty::kMaxRunningTokens)
+    return fail(KITTY_ERR_UNSUPPORTED, "S %d exceeds %d tokens in the running ranking mode", S, kitty::kMaxRunningTokens);
   kitty::QuantizeParams p{};
   p.pages = static_cast<uint8_t*>(kv->pages);
   p.n_pages = kv->n_pages;
@@ -114,6 +125,7 @@ int kitty_quantize_pages(const kitty_config_t* cfg, const kitty_kv_view_t* kv, c
   p.v = reinterpret_cast<const _Float16*>(v);
   p.S = S;
   p.lens = lens;
+  p.key_stats = key_stats_of(cfg, kv);
   (void)hipGetLastError();
   return check_launch(kitty::launch_quantize(p, static_cast<hipStream_t>(stream)), "quantize_pages");
 }
@@ -139,6 +151,7 @@ int kitty_append_token(const kitty_config_t* cfg, const kitty_kv_view_t* kv, con
   p.seq_lens = kv->seq_lens;
   p.k_new = reinterpret_cast<const _Float16*>(k_new);
   p.v_new = reinterpret_cast<const _Float16*>(v_new);
+  p.key_stats = key_stats_of(cfg, kv);
   (void)hipGetLastError();
   return check_launch(kitty::launch_append(p, static_cast<hipStream_t>(stream)), "append_token");
 }
@@ -233,6 +246,7 @@ static int decode_launch(const kitty_config_t* cfg, const kitty_kv_view_t* kv, c
   p.seq_counters = reinterpret_cast<int*>(wsb + ws.seq_counters);
   p.seal_scratch = wsb + ws.seal_scratch;
   p.out = out;
+  p.key_stats = key_stats_of(cfg, kv);
   (void)hipGetLastError();
   return check_launch(kitty::launch_decode(p, static_cast<hipStream_t>(stream)), what);
 }

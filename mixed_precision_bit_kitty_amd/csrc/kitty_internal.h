@@ -89,6 +89,7 @@ struct QuantizeParams {
   const _Float16* v;
   int32_t S;
   const int32_t* lens;
+  uint8_t* key_stats;      // running ranking mode: [batch][Hkv] states of kKeyStatsBytes; null in the page mode
 };
 
 struct AppendParams {
@@ -106,6 +107,7 @@ struct AppendParams {
   int32_t* seq_lens;
   const _Float16* k_new;
   const _Float16* v_new;
+  uint8_t* key_stats;      // running ranking mode (see QuantizeParams)
 };
 
 struct DecodeParams {
@@ -135,6 +137,7 @@ struct DecodeParams {
   int* seq_counters;       // [batch] finished units per sequence (fused step), zero between calls
   uint8_t* seal_scratch;   // [batch][Hkv][n_head_groups - 1] records re-quantized by head groups >= 1
   float* out;              // [batch][Hq][D]
+  uint8_t* key_stats;      // running ranking mode: written only by the fused step (the sequence's last unit)
 };
 
 constexpr int kPartialStride = 132;  // m, l, O[128], 2 pad floats
@@ -154,6 +157,9 @@ struct SplitPlan {
 // wmax: waves per workgroup that the record size allows (decode_max_wg_waves)
 SplitPlan plan_splits(int batch, int n_kv_heads, int n_head_groups, int max_seq_len, int wmax);
 int decode_max_wg_waves(int n_hi, int lo_bit);
+
+constexpr int kKeyStatsBytes = 4096;  // running-mode state of one (sequence, KV head)
+constexpr int kMaxRunningTokens = 1 << 23;  // running mode: exact scores stay below 2^127
 
 hipError_t launch_quantize(const QuantizeParams& p, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);

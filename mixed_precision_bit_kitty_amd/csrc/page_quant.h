@@ -13,6 +13,9 @@
 //    the lower channel index.  The n_hi-th largest m2 is found by a 31-step
 //    bitwise search with wave ballots (m2 >= 0, so its bit pattern orders like
 //    the value); equal keys are ranked by channel index with ballot popcounts.
+//  * In the running ranking mode the boosted channels come from outside the
+//    page instead (the head's exact running variance; see select_top and
+//    the running-sum helpers below).
 //  * Asymmetric min/max codes (Prefill step 3): 4-bit on boosted channels,
 //    2-bit elsewhere, fp16 step, round-half-even, clamp; split into the base
 //    plane (top 2 bits) and the boost plane (low 2 bits of boosted channels).
@@ -149,6 +152,120 @@ __device__ __forceinline__ uint32_t gather4_nib(uint64_t x) {
 // element e at bit 16 (e & 1) + 4 (e >> 1)
 __device__ __forceinline__ uint32_t pack_word4(uint64_t a) { return gather4_nib(a) | (gather4_nib(a >> 8) << 16); }
 
+// ---- Top-n selection ------------------------------------------------------
+// Lane l holds the keys of channels 2l and 2l + 1 (unsigned; a larger key is
+// a more sensitive channel).  Selects the n largest keys, ties to the lower
+// channel index: the n-th largest key T is found bit by bit with wave
+// ballots (TOPBIT = the highest bit a key can have), then the keys equal to
+// T are taken in channel order by ballot popcounts.
+template <typename K, int TOPBIT>
+__device__ __forceinline__ void select_top(K k0, K k1, int n, int lane, bool& h0, bool& h1) {
+  const uint64_t below = (1ull << lane) - 1ull;
+  K T = 0;
+  for (int bit = TOPBIT; bit >= 0; --bit) {
+    const K cand = T | ((K)1 << bit);
+    const int cnt = __popcll(__ballot(k0 >= cand)) + __popcll(__ballot(k1 >= cand));
+    if (cnt >= n) T = cand;
+  }
+  const int gt = __popcll(__ballot(k0 > T)) + __popcll(__ballot(k1 > T));
+  const uint64_t e0 = __ballot(k0 == T), e1 = __ballot(k1 == T);
+  const int before0 = __popcll(e0 & below) + __popcll(e1 & below);
+  const int before1 = before0 + (int)((e0 >> lane) & 1ull);
+  const int need = n - gt;
+  h0 = (k0 > T) || (k0 == T && before0 < need);
+  h1 = (k1 > T) || (k1 == T && before1 < need);
+}
+
+// ---- Running sums (the "running" ranking mode) ---------------------------
+// "Kitty -- Dynamic Channel-wise Mixed-Precision Keys", How it works:
+// Prefill step 1 ranks a head's channels by their variance over the prefill
+// sequence, step 5 starts running sums of k and k^2, Decode phase steps 1-2
+// update them per token and re-derive the ranking from
+// sum k^2 / n - (sum k / n)^2.  The sums are kept exactly: a = k * 2^24 is
+// an integer for every finite fp16 k (|a| < 2^40), s1 = sum a in int64,
+// s2 = sum a^2 in 128 bits, and the score n s2 - s1^2 (n^2 times that
+// variance, in units of 2^-48) is exact, so no accumulation order matters.
+typedef unsigned __int128 u128;
+
+// State of one (sequence, KV head), kStatsBytes bytes: int64 s1[128],
+// uint64 s2 low halves [128], uint64 s2 high halves [128], uint32 mask[4]
+// (channel c at bit c & 31 of word c >> 5: the ranking of the last prefill),
+// then reserved bytes.  Lane l's channels 2l, 2l + 1 are 16 contiguous bytes
+// of each array.
+constexpr int kStatsS1 = 0, kStatsS2Lo = 1024, kStatsS2Hi = 2048, kStatsMask = 3072, kStatsBytes = kKeyStatsBytes;
+static_assert(kStatsMask + 16 <= kStatsBytes, "key statistics layout");
+
+__device__ __forceinline__ int64_t fixed24(uint32_t h16) {
+  const uint32_t e = (h16 >> 10) & 31u, m = h16 & 1023u;
+  const int64_t mag = e ? (int64_t)(1024u | m) << (e - 1) : (int64_t)m;  // normal: (1024 + m) 2^(e-1); subnormal: m
+  return (h16 & 0x8000u) ? -mag : mag;
+}
+__device__ __forceinline__ u128 square(int64_t a) {
+  const uint64_t m = a < 0 ? 0ull - (uint64_t)a : (uint64_t)a;
+  return (u128)m * m;
+}
+// n s2 - s1^2 >= 0 (Cauchy-Schwarz); below 2^127 for n < 2^23
+__device__ __forceinline__ u128 running_score(int64_t s1, u128 s2, uint32_t n) {
+  const uint64_t m = s1 < 0 ? 0ull - (uint64_t)s1 : (uint64_t)s1;
+  return (u128)n * s2 - (u128)m * m;
+}
+
+// Lane l's part of a state: the sums of channels 2l, 2l + 1.
+struct LaneSums {
+  int64_t s1[2];
+  u128 s2[2];
+};
+__device__ __forceinline__ LaneSums load_sums(const uint8_t* st, int lane) {
+  typedef int64_t i64x2 __attribute__((ext_vector_type(2)));
+  typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+  const i64x2 a = *reinterpret_cast<const i64x2*>(st + kStatsS1 + 16 * lane);
+  const u64x2 lo = *reinterpret_cast<const u64x2*>(st + kStatsS2Lo + 16 * lane);
+  const u64x2 hi = *reinterpret_cast<const u64x2*>(st + kStatsS2Hi + 16 * lane);
+  LaneSums r;
+  r.s1[0] = a[0];
+  r.s1[1] = a[1];
+  r.s2[0] = ((u128)hi[0] << 64) | lo[0];
+  r.s2[1] = ((u128)hi[1] << 64) | lo[1];
+  return r;
+}
+__device__ __forceinline__ void store_sums(uint8_t* st, int lane, const LaneSums& r) {
+  typedef int64_t i64x2 __attribute__((ext_vector_type(2)));
+  typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+  *reinterpret_cast<i64x2*>(st + kStatsS1 + 16 * lane) = i64x2{r.s1[0], r.s1[1]};
+  *reinterpret_cast<u64x2*>(st + kStatsS2Lo + 16 * lane) = u64x2{(uint64_t)r.s2[0], (uint64_t)r.s2[1]};
+  *reinterpret_cast<u64x2*>(st + kStatsS2Hi + 16 * lane) = u64x2{(uint64_t)(r.s2[0] >> 64), (uint64_t)(r.s2[1] >> 64)};
+}
+// add one token (channels 2l, 2l + 1 as the fp16 pair `k2`, low half first)
+__device__ __forceinline__ void add_token(LaneSums& r, uint32_t k2) {
+  const int64_t a0 = fixed24(k2 & 0xFFFFu), a1 = fixed24(k2 >> 16);
+  r.s1[0] += a0;
+  r.s1[1] += a1;
+  r.s2[0] += square(a0);
+  r.s2[1] += square(a1);
+}
+
+// Boosted channels given from outside the page (the running mode) or, when
+// `given` is false, ranked by the page's own m2.
+struct RankIn {
+  bool given, h0, h1;
+};
+// The running ranking over n tokens from lane sums.
+__device__ __forceinline__ RankIn running_rank(const LaneSums& r, uint32_t n, int n_hi, int lane) {
+  RankIn rk{true, false, false};
+  if (n_hi >= kHeadDim) {
+    rk.h0 = rk.h1 = true;
+  } else if (n_hi > 0) {
+    select_top<u128, 127>(running_score(r.s1[0], r.s2[0], n), running_score(r.s1[1], r.s2[1], n), n_hi, lane,
+                          rk.h0, rk.h1);
+  }
+  return rk;
+}
+// RankIn of lane l's channels from a stored mask (uint32[4])
+__device__ __forceinline__ RankIn rank_from_mask(const uint8_t* st, int lane) {
+  const uint32_t w = reinterpret_cast<const uint32_t*>(st + kStatsMask)[lane >> 4];
+  return RankIn{true, ((w >> ((2 * lane) & 31)) & 1u) != 0, ((w >> ((2 * lane + 1) & 31)) & 1u) != 0};
+}
+
 // token t -> value metadata index kappa (inverse of tau): tokens t and
 // t + 16 (t < 16) sit at kappa 2t and 2t + 1
 __host__ __device__ constexpr int kappa_of(int t) { return 2 * (t & 15) + (t >> 4); }
@@ -173,7 +290,7 @@ struct RowSrc {
 // index 0.
 template <int NHI, int BITS = 2>
 __device__ __forceinline__ void quantize_keys_wave(RowSrc ks, uint8_t* __restrict__ rec, uint8_t* __restrict__ lds,
-                                                   int n = NHI) {
+                                                   int n = NHI, RankIn rk = RankIn{false, false, false}) {
 #pragma clang fp contract(off)
   static_assert(BITS == 2 || BITS == 4, "lo_bit 2 or 4");
   constexpr float kLo = (float)((1 << BITS) - 1), kHi = (float)((1 << (2 * BITS)) - 1);
@@ -200,44 +317,35 @@ __device__ __forceinline__ void quantize_keys_wave(RowSrc ks, uint8_t* __restric
   }
   kmn = canon2(__builtin_bit_cast(uint32_t, kmn));
   kmx = canon2(__builtin_bit_cast(uint32_t, kmx));
-  float a[32];
-#pragma unroll
-  for (int t = 0; t < 32; ++t) a[t] = x0[t];
-  const float mu0 = tree32(a) * (1.0f / 32.0f);
-#pragma unroll
-  for (int t = 0; t < 32; ++t) { float d = x0[t] - mu0; a[t] = d * d; }
-  const float m2_0 = tree32(a);
-#pragma unroll
-  for (int t = 0; t < 32; ++t) a[t] = x1[t];
-  const float mu1 = tree32(a) * (1.0f / 32.0f);
-#pragma unroll
-  for (int t = 0; t < 32; ++t) { float d = x1[t] - mu1; a[t] = d * d; }
-  const float m2_1 = tree32(a);
   const float mn0 = (float)kmn[0], mx0 = (float)kmx[0], mn1 = (float)kmn[1], mx1 = (float)kmx[1];
 
   // ---------------- Ranking: top n by m2, ties to the lower channel ---------
+  // (or the boosted channels given by the running ranking)
   const uint64_t below = (1ull << lane) - 1ull;
   bool h0, h1;
-  if (NHI == 0) {
+  if (rk.given) {
+    h0 = rk.h0;
+    h1 = rk.h1;
+  } else if (NHI == 0) {
     h0 = h1 = false;
   } else if (NHI == kHeadDim && n == kHeadDim) {
     h0 = h1 = true;
   } else {
-    const uint32_t b0 = __builtin_bit_cast(uint32_t, m2_0);
-    const uint32_t b1 = __builtin_bit_cast(uint32_t, m2_1);
-    uint32_t T = 0;
-    for (int bit = 30; bit >= 0; --bit) {
-      const uint32_t cand = T | (1u << bit);
-      const int cnt = __popcll(__ballot(b0 >= cand)) + __popcll(__ballot(b1 >= cand));
-      if (cnt >= n) T = cand;
-    }
-    const int gt = __popcll(__ballot(b0 > T)) + __popcll(__ballot(b1 > T));
-    const uint64_t e0 = __ballot(b0 == T), e1 = __ballot(b1 == T);
-    const int before0 = __popcll(e0 & below) + __popcll(e1 & below);
-    const int before1 = before0 + (int)((e0 >> lane) & 1ull);
-    const int need = n - gt;
-    h0 = (b0 > T) || (b0 == T && before0 < need);
-    h1 = (b1 > T) || (b1 == T && before1 < need);
+    float a[32];
+#pragma unroll
+    for (int t = 0; t < 32; ++t) a[t] = x0[t];
+    const float mu0 = tree32(a) * (1.0f / 32.0f);
+#pragma unroll
+    for (int t = 0; t < 32; ++t) { float d = x0[t] - mu0; a[t] = d * d; }
+    const float m2_0 = tree32(a);
+#pragma unroll
+    for (int t = 0; t < 32; ++t) a[t] = x1[t];
+    const float mu1 = tree32(a) * (1.0f / 32.0f);
+#pragma unroll
+    for (int t = 0; t < 32; ++t) { float d = x1[t] - mu1; a[t] = d * d; }
+    const float m2_1 = tree32(a);
+    // m2 >= 0: its bit pattern orders like its value (bit 31 is clear)
+    select_top<uint32_t, 30>(__builtin_bit_cast(uint32_t, m2_0), __builtin_bit_cast(uint32_t, m2_1), n, lane, h0, h1);
   }
   const uint64_t H0 = __ballot(h0), H1 = __ballot(h1);
   const int pos0 = __popcll(H0 & below) + __popcll(H1 & below);
@@ -452,8 +560,8 @@ __device__ __forceinline__ void quantize_values_wave(RowSrc vs, uint8_t* __restr
 // n <= NHI).
 template <int NHI, int BITS = 2>
 __device__ __forceinline__ void quantize_page_wave(RowSrc ks, RowSrc vs, uint8_t* __restrict__ rec, uint8_t* __restrict__ lds,
-                                                   int n = NHI) {
-  quantize_keys_wave<NHI, BITS>(ks, rec, lds, n);
+                                                   int n = NHI, RankIn rk = RankIn{false, false, false}) {
+  quantize_keys_wave<NHI, BITS>(ks, rec, lds, n, rk);
   quantize_values_wave<NHI, BITS>(vs, rec, lds);
 }
 

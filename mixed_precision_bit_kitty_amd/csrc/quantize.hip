@@ -33,6 +33,103 @@ __device__ __forceinline__ void stage_value_page(const _Float16* src, uint8_t* d
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int mask) {
+  const uint32_t lo = __shfl_xor((uint32_t)x, mask), hi = __shfl_xor((uint32_t)(x >> 32), mask);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Running ranking mode, ahead of the prefill: the exact running sums of
+// every (sequence, KV head) over the sequence's n_b tokens (tail included;
+// "Kitty -- Dynamic Channel-wise Mixed-Precision Keys", How it works /
+// Prefill phase, steps 1 and 5) become its state, and their ranking is
+// stored for quantize_pages_kernel.  grid (Hkv, batch), 16 waves: lane
+// (cb = lane & 15, tg = lane >> 4) of wave w sums channels 8cb .. 8cb + 7
+// over tokens 32j + tg + 4i (i = 0..7) of the token blocks j = w, w + 16,
+// ...; integer sums may be added in any order.
+__global__ __launch_bounds__(1024) void key_stats_kernel(QuantizeParams p) {
+  __shared__ int64_t ws1[16][kHeadDim];
+  __shared__ u128 ws2[16][kHeadDim];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, cb = lane & 15, tg = lane >> 4;
+  int n = p.lens ? p.lens[b] : p.S;
+  if (n < 0) return;  // a negative length leaves sequence b as it is (block-uniform)
+  n = n > p.S ? p.S : n;
+  const _Float16* kb = p.k + ((size_t)b * p.n_kv_heads + h) * (size_t)p.S * kHeadDim + 8 * cb;
+  int64_t s1[8];
+  u128 s2[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    s1[e] = 0;
+    s2[e] = 0;
+  }
+  for (int j = wave; kPageTokens * j < n; j += 16) {
+    u32x4 rows[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {  // every load issued before the first use
+      const int t = kPageTokens * j + tg + 4 * i;
+      rows[i] = t < n ? *reinterpret_cast<const u32x4*>(kb + (size_t)t * kHeadDim) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {  // +0 halves of skipped tokens add nothing
+        const int64_t a = fixed24((rows[i][e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+        s1[e] += a;
+        s2[e] += square(a);
+      }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+#pragma unroll
+    for (int m = 16; m <= 32; m <<= 1) {
+      s1[e] += (int64_t)shfl_xor_u64((uint64_t)s1[e], m);
+      const uint64_t lo = shfl_xor_u64((uint64_t)s2[e], m), hi = shfl_xor_u64((uint64_t)(s2[e] >> 64), m);
+      s2[e] += ((u128)hi << 64) | lo;
+    }
+  if (tg == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ws1[wave][8 * cb + e] = s1[e];
+      ws2[wave][8 * cb + e] = s2[e];
+    }
+  }
+  __syncthreads();
+  uint8_t* st = p.key_stats + ((size_t)b * p.n_kv_heads + h) * kStatsBytes;
+  if (threadIdx.x < kHeadDim) {
+    const int c = threadIdx.x;
+    int64_t t1 = 0;
+    u128 t2 = 0;
+    for (int w = 0; w < 16; ++w) {
+      t1 += ws1[w][c];
+      t2 += ws2[w][c];
+    }
+    ws1[0][c] = t1;  // only this thread touches column c
+    ws2[0][c] = t2;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    LaneSums r;
+    r.s1[0] = ws1[0][2 * lane];
+    r.s1[1] = ws1[0][2 * lane + 1];
+    r.s2[0] = ws2[0][2 * lane];
+    r.s2[1] = ws2[0][2 * lane + 1];
+    store_sums(st, lane, r);
+    const RankIn rk = running_rank(r, (uint32_t)n, p.n_hi, lane);
+    // mask word m: channel 32m + 2i + j at bit 2i + j, from lanes 16m + i
+    const uint64_t B0 = __ballot(rk.h0), B1 = __ballot(rk.h1);
+    if (lane < 4) {
+      auto spread = [](uint32_t x) {  // bit i -> bit 2i, 16 bits
+        x = (x | (x << 8)) & 0x00FF00FFu;
+        x = (x | (x << 4)) & 0x0F0F0F0Fu;
+        x = (x | (x << 2)) & 0x33333333u;
+        return (x | (x << 1)) & 0x55555555u;
+      };
+      const uint32_t w0 = (uint32_t)(B0 >> (16 * lane)) & 0xFFFFu, w1 = (uint32_t)(B1 >> (16 * lane)) & 0xFFFFu;
+      reinterpret_cast<uint32_t*>(st + kStatsMask)[lane] = spread(w0) | (spread(w1) << 1);
+    }
+  }
+}
+
 // grid (pages + 1, Hkv, batch), two waves per block: wave 0 quantizes the
 // page's keys, wave 1 its values (disjoint parts of one LDS area), so the
 // two halves' memory latency overlaps.  The value wave first stages its
@@ -56,7 +153,13 @@ __global__ __launch_bounds__(128) void quantize_pages_kernel(QuantizeParams p) {
     uint8_t* rec = p.pages + (int64_t)phys * p.page_bytes + (int64_t)h * rec_bytes(NHI, BITS);
     const size_t row0 = seq_off + (size_t)page * kPageTokens * kHeadDim;
     if (wave == 0) {
-      quantize_keys_wave<NHI, BITS>(RowSrc{p.k + row0, nullptr}, rec, lds, p.n_hi);
+      // the running mode takes the ranking key_stats_kernel stored (two
+      // inlined copies: one register allocation each)
+      if (p.key_stats)
+        quantize_keys_wave<NHI, BITS>(RowSrc{p.k + row0, nullptr}, rec, lds, p.n_hi,
+                                      rank_from_mask(p.key_stats + ((size_t)b * p.n_kv_heads + h) * kStatsBytes, lane));
+      else
+        quantize_keys_wave<NHI, BITS>(RowSrc{p.k + row0, nullptr}, rec, lds, p.n_hi);
     } else {
       stage_value_page(p.v + row0, lds + kVStage, lane);
       quantize_values_wave<NHI, BITS>(RowSrc{reinterpret_cast<const _Float16*>(lds + kVStage), nullptr}, rec, lds);
@@ -89,10 +192,20 @@ __global__ __launch_bounds__(512) void append_token_kernel(AppendParams p) {  //
   for (int h = wave; h < p.n_kv_heads; h += nw) {
     const size_t tail_off = ((size_t)b * p.n_kv_heads + h) * kPageTokens * kHeadDim;
     const size_t new_off = ((size_t)b * p.n_kv_heads + h) * kHeadDim;
-    *reinterpret_cast<uint32_t*>(p.tail_k + tail_off + (size_t)slot * kHeadDim + 2 * lane) =
-        *reinterpret_cast<const uint32_t*>(p.k_new + new_off + 2 * lane);
+    const uint32_t k2 = *reinterpret_cast<const uint32_t*>(p.k_new + new_off + 2 * lane);
+    *reinterpret_cast<uint32_t*>(p.tail_k + tail_off + (size_t)slot * kHeadDim + 2 * lane) = k2;
     *reinterpret_cast<uint32_t*>(p.tail_v + tail_off + (size_t)slot * kHeadDim + 2 * lane) =
         *reinterpret_cast<const uint32_t*>(p.v_new + new_off + 2 * lane);
+    // running mode (Decode phase steps 1-2): the token joins the head's
+    // running sums, and a page sealed now is ranked over all n + 1 tokens
+    RankIn rk{false, false, false};
+    if (p.key_stats) {
+      uint8_t* st = p.key_stats + ((size_t)b * p.n_kv_heads + h) * kStatsBytes;
+      LaneSums r = load_sums(st, lane);
+      add_token(r, k2);
+      store_sums(st, lane, r);
+      if (slot == kPageTokens - 1) rk = running_rank(r, (uint32_t)n + 1, p.n_hi, lane);
+    }
     if (slot == kPageTokens - 1) {
       const int pg = n / kPageTokens;
       if (pg < p.max_pages) {
@@ -101,7 +214,7 @@ __global__ __launch_bounds__(512) void append_token_kernel(AppendParams p) {  //
           uint8_t* rec = p.pages + (int64_t)phys * p.page_bytes + (int64_t)h * rec_bytes(NHI, BITS);
           quantize_page_wave<NHI, BITS>(RowSrc{p.tail_k + tail_off, p.k_new + new_off},
                                         RowSrc{p.tail_v + tail_off, p.v_new + new_off}, rec, lds_dyn + wave * kWaveLds,
-                                        p.n_hi);
+                                        p.n_hi, rk);
         }
       }
     }
@@ -112,6 +225,11 @@ __global__ __launch_bounds__(512) void append_token_kernel(AppendParams p) {  //
 
 template <int NHI>
 hipError_t launch_quantize_t(const QuantizeParams& p, hipStream_t stream) {
+  if (p.key_stats) {  // running mode: sums and ranking first, on the same stream
+    hipLaunchKernelGGL(key_stats_kernel, dim3(p.n_kv_heads, p.batch), dim3(1024), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   dim3 grid(p.S / kPageTokens + 1, p.n_kv_heads, p.batch);
   if (p.lo_bit == 4)
     hipLaunchKernelGGL((quantize_pages_kernel<NHI, 4>), grid, dim3(128), 0, stream, p);

@@ -30,6 +30,18 @@ Arithmetic conventions (readings of points the pages leave open):
 * quantization: step s16 = f16((max - min) / L) with a correctly rounded fp32
   division; codes q = clamp(rne((x - min) * (1 / s)), 0, L) with one fp32
   reciprocal per group; a zero step gives all-zero codes.
+
+Ranking modes.  "page" (the default) ranks each page by its own variance.
+"running" follows [Velox] "How it works": Prefill step 1 ranks a head's
+channels by their variance over the whole prefill sequence, and the Decode
+phase (steps 1-2) re-derives the ranking from running sums of k and k^2.
+Sealed pages cannot change afterwards, so a page takes the ranking current
+when it is sealed: the prefill ranking for prefill pages, the running one
+over all tokens stored so far for a page sealed by an append.  The sums are
+kept exactly (integers in units of 2^-24 and 2^-48; ``fixed24``), and the
+score n * sum(k^2) - (sum k)^2 (n^2 times the population variance of the
+formula in Decode step 2) is exact, so its value does not depend on the
+order of accumulation.
 """
 from __future__ import annotations
 
@@ -119,6 +131,39 @@ def rank_channels(m2, n_hi):
     return idx.astype(np.uint8), mask
 
 
+RANK_MODES = ("page", "running")
+
+
+def fixed24(k16):
+    """fp16 values as exact integers in units of 2^-24 (every fp16 value is a
+    multiple of 2^-24 below 2^16): Python ints in an object array."""
+    a = np.asarray(k16, _F16).astype(np.float64) * 2.0 ** 24     # exact, |a| < 2^40
+    return a.astype(np.int64).astype(object)
+
+
+def running_scores(s1, s2, n):
+    """Exact running-variance score per channel ([Velox] Decode phase step
+    2): with s1 = sum a, s2 = sum a^2 over n tokens (a = fixed24(k)),
+    n * s2 - s1^2 = n^2 * (sum k^2 / n - (sum k / n)^2) in units of 2^-48."""
+    return n * s2 - s1 * s1
+
+
+def rank_scores(scores, n_hi):
+    """The n_hi channels with the largest exact score, ties to the lower
+    channel index (the same rule as rank_channels).  scores: object array
+    [..., D] of Python ints.  Returns (idx uint8 ascending, mask bool)."""
+    sc = np.asarray(scores, object)
+    D = sc.shape[-1]
+    flat = sc.reshape(-1, D)
+    mask = np.zeros(flat.shape, bool)
+    for r in range(flat.shape[0]):
+        order = sorted(range(D), key=lambda c: (-flat[r, c], c))[:n_hi]
+        mask[r, order] = True
+    mask = mask.reshape(sc.shape)
+    idx = np.nonzero(mask.reshape(-1, D))[1].reshape(sc.shape[:-1] + (n_hi,)).astype(np.uint8)
+    return idx, mask
+
+
 def quantize_levels(x, mn, mx, levels):
     """Asymmetric min/max quantization of x onto {0..levels} ([Velox] Prefill
     step 3).  x, mn, mx: float32, broadcastable; levels: int, broadcastable.
@@ -138,9 +183,11 @@ def quantize_levels(x, mn, mx, levels):
     return q, np.broadcast_to(s16, np.broadcast_shapes(s16.shape, mn.shape)).astype(_F16)
 
 
-def quant_k_page(k16, n_hi, lo_bit=2):
+def quant_k_page(k16, n_hi, lo_bit=2, mask=None):
     """Quantize Key pages.  k16: fp16 [..., 32, D]; n_hi boosted channels;
-    lo_bit 2 (hi_bit 4) or 4 (hi_bit 8).
+    lo_bit 2 (hi_bit 4) or 4 (hi_bit 8); ``mask`` (optional, bool
+    broadcastable to [..., D] with n_hi True per row) gives the boosted
+    channels instead of the page's own ranking (the "running" mode).
 
     Returns a dict with the direct codes ``q`` (hi_bit on boosted channels,
     lo_bit elsewhere) and the two uniform lo_bit tensors of the decomposition
@@ -152,7 +199,12 @@ def quant_k_page(k16, n_hi, lo_bit=2):
     lo_l, hi_l = levels(lo_bit)
     x = f32_stat(k16)
     _, m2, mn, mx = page_stats(x)
-    idx, mask = rank_channels(m2, n_hi)
+    if mask is None:
+        idx, mask = rank_channels(m2, n_hi)
+    else:
+        mask = np.broadcast_to(np.asarray(mask, bool), m2.shape)
+        D = mask.shape[-1]
+        idx = np.nonzero(mask.reshape(-1, D))[1].reshape(mask.shape[:-1] + (n_hi,)).astype(np.uint8)
     lv = np.where(mask, hi_l, lo_l)
     q, s16 = quantize_levels(x, mn[..., None, :], mx[..., None, :], lv[..., None, :])
     s16 = s16[..., 0, :]
@@ -512,10 +564,18 @@ class OracleCache:
     head ([Kitty] Abstract: page-centric layout; the incomplete tail page
     stays fp16 until it fills)."""
 
-    def __init__(self, batch, n_kv_heads, n_hi, head_dim=HEAD_DIM, lo_bit=2):
+    def __init__(self, batch, n_kv_heads, n_hi, head_dim=HEAD_DIM, lo_bit=2, rank_mode="page"):
         record_bytes(n_hi, head_dim, lo_bit)
+        if rank_mode not in RANK_MODES:
+            raise ValueError("rank_mode must be 'page' or 'running'")
         self.batch, self.n_kv_heads, self.n_hi, self.head_dim = batch, n_kv_heads, n_hi, head_dim
         self.lo_bit = lo_bit
+        self.rank_mode = rank_mode
+        # running sums of a = fixed24(k) and a^2 per (sequence, head, channel)
+        self.s1 = np.zeros((batch, n_kv_heads, head_dim), object)
+        self.s2 = np.zeros((batch, n_kv_heads, head_dim), object)
+        self.s1[...] = 0
+        self.s2[...] = 0
         self.k = [None] * batch      # dict of arrays [Hkv, P, ...]
         self.v = [None] * batch
         self.tail_k = np.zeros((batch, n_kv_heads, PAGE_TOKENS, head_dim), _F16)
@@ -525,8 +585,25 @@ class OracleCache:
     def n_pages(self, b):
         return int(self.seq_len[b]) // PAGE_TOKENS
 
+    def add_tokens_to_sums(self, b, k16):
+        """Running sums ([Velox] Prefill step 5, Decode step 1): add the
+        tokens k16 fp16 [Hkv, T, D] of sequence b (kept in the "running"
+        mode only)."""
+        if self.rank_mode != "running":
+            return
+        a = fixed24(k16)
+        self.s1[b] = self.s1[b] + a.sum(axis=1)
+        self.s2[b] = self.s2[b] + (a * a).sum(axis=1)
+
+    def running_mask(self, b):
+        """Boosted channels [Hkv, D] from the running sums over the
+        sequence's seq_len[b] tokens."""
+        _, mask = rank_scores(running_scores(self.s1[b], self.s2[b], int(self.seq_len[b])), self.n_hi)
+        return mask
+
     def _add_pages(self, b, k16, v16):
-        kf = quant_k_page(k16, self.n_hi, self.lo_bit)
+        mask = self.running_mask(b)[:, None, :] if self.rank_mode == "running" else None
+        kf = quant_k_page(k16, self.n_hi, self.lo_bit, mask=mask)
         vf = quant_v_page(v16, self.lo_bit)
         kf = {key: kf[key] for key in ("base", "boost", "kscale", "kmin", "idx", "q", "mask")}
         if self.k[b] is None:
@@ -560,17 +637,22 @@ class OracleCache:
         return np.concatenate(ks, axis=1), np.concatenate(vs, axis=1)
 
 
-def quantize_pages(k, v, n_hi, batch_lens=None, lo_bit=2):
+def quantize_pages(k, v, n_hi, batch_lens=None, lo_bit=2, rank_mode="page"):
     """Prefill: split fp16 k, v [B, Hkv, S, D] into P = floor(S/32) sealed
     pages and an fp16 tail of S mod 32 tokens ([Velox] Prefill steps 1-3 per
     page of group_size tokens).  ``batch_lens`` (optional, per sequence)
     quantizes only the first len_b tokens of sequence b; ``lo_bit`` picks the
-    bit-width pair (2: hi 4 / lo 2, 4: hi 8 / lo 4)."""
+    bit-width pair (2: hi 4 / lo 2, 4: hi 8 / lo 4).  ``rank_mode``
+    "running": every page of sequence b takes the ranking by the exact
+    variance over all len_b prefill tokens (tail included), and the running
+    sums start from those tokens."""
     B, H, S, D = k.shape
-    cache = OracleCache(B, H, n_hi, D, lo_bit)
+    cache = OracleCache(B, H, n_hi, D, lo_bit, rank_mode)
     for b in range(B):
         n = S if batch_lens is None else int(batch_lens[b])
         P = n // PAGE_TOKENS
+        cache.add_tokens_to_sums(b, k[b, :, :n])
+        cache.seq_len[b] = n
         if P:
             kp = k[b, :, :P * PAGE_TOKENS].reshape(H, P, PAGE_TOKENS, D)
             vp = v[b, :, :P * PAGE_TOKENS].reshape(H, P, PAGE_TOKENS, D)
@@ -578,7 +660,6 @@ def quantize_pages(k, v, n_hi, batch_lens=None, lo_bit=2):
         t = n - P * PAGE_TOKENS
         cache.tail_k[b, :, :t] = k[b, :, P * PAGE_TOKENS:n]
         cache.tail_v[b, :, :t] = v[b, :, P * PAGE_TOKENS:n]
-        cache.seq_len[b] = n
     return cache
 
 
@@ -586,15 +667,17 @@ def append_token(cache, k_new, v_new):
     """Decode-time append of one token per sequence (k_new, v_new fp16
     [B, Hkv, D]): store into tail slot n mod 32; when that slot is the 32nd,
     the tail is quantized as page n div 32 exactly like a prefill page and
-    the tail becomes empty."""
+    the tail becomes empty.  In the "running" mode the token first joins the
+    running sums, and a sealed page takes the ranking over all n + 1 tokens."""
     for b in range(cache.batch):
         n = int(cache.seq_len[b])
         slot = n % PAGE_TOKENS
         cache.tail_k[b, :, slot] = k_new[b]
         cache.tail_v[b, :, slot] = v_new[b]
+        cache.add_tokens_to_sums(b, k_new[b][:, None, :])
+        cache.seq_len[b] = n + 1
         if slot == PAGE_TOKENS - 1:
             cache._add_pages(b, cache.tail_k[b][:, None], cache.tail_v[b][:, None])
-        cache.seq_len[b] = n + 1
     return cache
 
 

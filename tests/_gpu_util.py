@@ -88,7 +88,38 @@ def compare_decode(cache, oc, q, max_seq_len=None, seq_map=None, atol=ATOL):
     return err, out
 
 
-def step_twins(w, lens, steps, ctx, n_hi=32, msl=None, check_every=1, lo_bit=2):
+def oracle_state_bytes(oc, b, h, with_mask=None):
+    """The library's running-mode state layout of (sequence b, head h) from
+    the oracle's exact sums: int64 s1[128], uint64 low / high halves of the
+    128-bit s2[128] (and, if given, the uint32 mask[4] of a ranking)."""
+    out = np.zeros(4096, np.uint8)
+    s1 = np.array([int(x) for x in oc.s1[b, h]], dtype=object)
+    s2 = np.array([int(x) for x in oc.s2[b, h]], dtype=object)
+    out[0:1024] = np.array([int(x) & (2 ** 64 - 1) for x in s1], dtype=np.uint64).view(np.uint8)
+    out[1024:2048] = np.array([int(x) & (2 ** 64 - 1) for x in s2], dtype=np.uint64).view(np.uint8)
+    out[2048:3072] = np.array([int(x) >> 64 for x in s2], dtype=np.uint64).view(np.uint8)
+    if with_mask is not None:
+        words = np.zeros(4, np.uint32)
+        for c in np.nonzero(with_mask)[0]:
+            words[c >> 5] |= np.uint32(1 << (c & 31))
+        out[3072:3088] = words.view(np.uint8)
+    return out
+
+
+def compare_state(cache, oc, seq_map=None, masks=False):
+    """Running sums of every (sequence, head) byte-equal to the oracle's;
+    with masks=True also the stored prefill ranking."""
+    ks = host(cache.key_stats)
+    for b in range(oc.batch):
+        gb = b if seq_map is None else seq_map[b]
+        for h in range(oc.n_kv_heads):
+            m = oc.running_mask(b)[h] if masks else None
+            want = oracle_state_bytes(oc, b, h, m)
+            n = 3088 if masks else 3072
+            assert np.array_equal(ks[gb, h, :n], want[:n]), f"state of sequence {b} head {h} differs"
+
+
+def step_twins(w, lens, steps, ctx, n_hi=32, msl=None, check_every=1, lo_bit=2, rank_mode="page"):
     """Twin caches: one through the fused step, one through append +
     decode attention; pools, tails, lengths byte-equal after every step,
     outputs bit-equal on steps without a seal, both within 2e-3 of the
@@ -98,10 +129,11 @@ def step_twins(w, lens, steps, ctx, n_hi=32, msl=None, check_every=1, lo_bit=2):
     batch = len(lens)
     x = synth.batch(w, batch=batch, ctx=ctx, steps=steps)
     cap = max(lens) + steps + 32
-    fused, split = [new_cache(batch, w.n_kv_heads, n_hi, cap, lo_bit=lo_bit) for _ in range(2)]
+    rm = 1 if rank_mode == "running" else 0
+    fused, split = [new_cache(batch, w.n_kv_heads, n_hi, cap, lo_bit=lo_bit, rank_mode=rm) for _ in range(2)]
     for c in (fused, split):
         c.quantize_pages(dev(x["k"]), dev(x["v"]), lens=dev(np.array(lens, np.int32)))
-    oc = O.quantize_pages(x["k"], x["v"], n_hi, batch_lens=lens, lo_bit=lo_bit)
+    oc = O.quantize_pages(x["k"], x["v"], n_hi, batch_lens=lens, lo_bit=lo_bit, rank_mode=rank_mode)
     msl = max(lens) + steps if msl is None else msl
     outs = [torch.zeros((batch, w.n_q_heads, 128), dtype=torch.float32, device="cuda") for _ in range(2)]
     worst = 0.0
@@ -117,9 +149,13 @@ def step_twins(w, lens, steps, ctx, n_hi=32, msl=None, check_every=1, lo_bit=2):
             assert np.array_equal(a, b), f"step {t}: fused and separate outputs differ without a seal"
         assert np.array_equal(host(fused.seq_lens), host(split.seq_lens)), f"step {t}"
         assert np.array_equal(host(fused.tail_k), host(split.tail_k)), f"step {t}"
+        if rm:
+            assert np.array_equal(host(fused.key_stats), host(split.key_stats)), f"step {t}: running sums differ"
         if seals or t % check_every == 0 or t == steps - 1:
             assert np.array_equal(host(fused.pool), host(split.pool)), f"step {t}: page pools differ"
             compare_tails(fused, oc)
+            if rm:
+                compare_state(fused, oc)
             ref = O.decode_attention(oc, x["q_new"][t])
             err = float(np.abs(a - ref).max())
             worst = max(worst, err)

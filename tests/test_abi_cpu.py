@@ -33,10 +33,13 @@ def test_header_error_codes_match_binding():
     assert int(codes["KITTY_ERR_WORKSPACE"]) == B.KITTY_ERR_WORKSPACE
     assert int(codes["KITTY_ERR_HIP"]) == B.KITTY_ERR_HIP
     assert int(codes["KITTY_ERR_NO_PAGES"]) == B.KITTY_ERR_NO_PAGES
+    assert int(codes["KITTY_RANK_PAGE"]) == B.KITTY_RANK_PAGE
+    assert int(codes["KITTY_RANK_RUNNING"]) == B.KITTY_RANK_RUNNING
+    assert int(re.search(r"#define KITTY_KEY_STATS_BYTES (\d+)", text).group(1)) == B.KITTY_KEY_STATS_BYTES
 
 
 def test_abi_version():
-    assert B.kitty_abi_version() == 2
+    assert B.kitty_abi_version() == 3
 
 
 @pytest.mark.parametrize("lo_bit,base,per_hi", [(2, 3072, 9), (4, 5120, 17)])
@@ -110,15 +113,17 @@ def test_workspace_bytes_monotone_in_max_seq_len():
 
 
 @pytest.mark.parametrize("cfg,code", [
-    ((64, 32, 8, 32, 2), B.KITTY_ERR_UNSUPPORTED),
-    ((128, 16, 8, 32, 2), B.KITTY_ERR_UNSUPPORTED),
-    ((128, 32, 0, 32, 2), B.KITTY_ERR_INVALID_ARG),
-    ((128, 32, 8, 129, 2), B.KITTY_ERR_UNSUPPORTED),
-    ((128, 32, 8, 144, 2), B.KITTY_ERR_UNSUPPORTED),
-    ((128, 32, 8, -16, 2), B.KITTY_ERR_UNSUPPORTED),
-    ((128, 32, 8, 32, 3), B.KITTY_ERR_UNSUPPORTED),
-    ((128, 32, 8, 32, 8), B.KITTY_ERR_UNSUPPORTED),
-    ((128, 32, 8, 32, 0), B.KITTY_ERR_UNSUPPORTED),
+    ((64, 32, 8, 32, 2, 0), B.KITTY_ERR_UNSUPPORTED),
+    ((128, 16, 8, 32, 2, 0), B.KITTY_ERR_UNSUPPORTED),
+    ((128, 32, 0, 32, 2, 0), B.KITTY_ERR_INVALID_ARG),
+    ((128, 32, 8, 129, 2, 0), B.KITTY_ERR_UNSUPPORTED),
+    ((128, 32, 8, 144, 2, 0), B.KITTY_ERR_UNSUPPORTED),
+    ((128, 32, 8, -16, 2, 0), B.KITTY_ERR_UNSUPPORTED),
+    ((128, 32, 8, 32, 3, 0), B.KITTY_ERR_UNSUPPORTED),
+    ((128, 32, 8, 32, 8, 0), B.KITTY_ERR_UNSUPPORTED),
+    ((128, 32, 8, 32, 0, 0), B.KITTY_ERR_UNSUPPORTED),
+    ((128, 32, 8, 32, 2, 2), B.KITTY_ERR_UNSUPPORTED),
+    ((128, 32, 8, 32, 2, -1), B.KITTY_ERR_UNSUPPORTED),
 ])
 def test_config_rejected(cfg, code):
     c = B.kitty_config_t(*cfg)
@@ -130,10 +135,10 @@ def test_config_rejected(cfg, code):
 
 def _view(**kw):
     d = dict(pages=FAKE, n_pages=4, block_table=FAKE, batch=2, max_pages=2, tail_k=FAKE, tail_v=FAKE,
-             seq_lens=FAKE)
+             seq_lens=FAKE, key_stats=None)
     d.update(kw)
     return B.kitty_kv_view_t(d["pages"], d["n_pages"], d["block_table"], d["batch"], d["max_pages"],
-                             d["tail_k"], d["tail_v"], d["seq_lens"])
+                             d["tail_k"], d["tail_v"], d["seq_lens"], d["key_stats"])
 
 
 BAD_VIEWS = [
@@ -252,3 +257,24 @@ def test_decode_plan_fits_page_id_register():
                     c0 = (pw // W) * prefix(W, W) + prefix(pw % W, W)
                     size = ((c0 + weight(pw % W)) * P) // wsum - (c0 * P) // wsum
                     assert size <= 64, (batch, hkv, hg, msl, n_wg, W, pw, size)
+
+
+def test_running_mode_arguments():
+    lib = B.load()
+    run = B.config(8, 32, rank_mode=B.KITTY_RANK_RUNNING)
+    # the running mode needs 16-byte aligned key_stats; the page mode ignores them
+    for view in (_view(), _view(key_stats=FAKE + 8)):
+        assert lib.kitty_quantize_pages(ctypes.byref(run), ctypes.byref(view), FAKE, FAKE, 64, None, None) == \
+            B.KITTY_ERR_INVALID_ARG
+        assert lib.kitty_append_token(ctypes.byref(run), ctypes.byref(view), FAKE, FAKE, None) == B.KITTY_ERR_INVALID_ARG
+        assert lib.kitty_decode_step(ctypes.byref(run), ctypes.byref(view), FAKE, FAKE, FAKE, 32, 64, FAKE, FAKE,
+                                     1 << 30, None) == B.KITTY_ERR_INVALID_ARG
+    assert "key_stats" in lib.kitty_last_error().decode()
+    # at most 2^23 tokens per sequence in the running mode
+    big = _view(key_stats=FAKE, max_pages=1 << 20)
+    assert lib.kitty_quantize_pages(ctypes.byref(run), ctypes.byref(big), FAKE, FAKE, (1 << 23) + 32, None, None) == \
+        B.KITTY_ERR_UNSUPPORTED
+    # workspace and record sizes do not depend on the ranking mode
+    page = B.config(8, 32)
+    assert B.kitty_record_bytes(run) == B.kitty_record_bytes(page)
+    assert B.kitty_decode_workspace_bytes(run, 4, 32, 4096) == B.kitty_decode_workspace_bytes(page, 4, 32, 4096)

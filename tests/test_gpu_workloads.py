@@ -121,7 +121,8 @@ def _decode_prefix(cache, bp, q, n_q_heads, msl):
     import torch
     from mixed_precision_bit_kitty_amd import binding as B
     v = cache.view
-    sub = B.kitty_kv_view_t(v.pages, v.n_pages, v.block_table, bp, v.max_pages, v.tail_k, v.tail_v, v.seq_lens)
+    sub = B.kitty_kv_view_t(v.pages, v.n_pages, v.block_table, bp, v.max_pages, v.tail_k, v.tail_v, v.seq_lens,
+                            v.key_stats)
     out = torch.empty((bp, n_q_heads, 128), dtype=torch.float32, device="cuda")
     ws = torch.zeros(B.kitty_decode_workspace_bytes(cache.cfg, bp, n_q_heads, msl), dtype=torch.uint8,
                      device="cuda")

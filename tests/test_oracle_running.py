@@ -1,0 +1,162 @@
+"""Pins of the oracle's "running" ranking mode ([Velox] "How it works":
+Prefill step 1 ranks a head's channels by variance over the prefill
+sequence, step 5 starts running sums, Decode phase steps 1-2 update them and
+re-derive the ranking from sum k^2 / n - (sum k / n)^2).
+
+Fixed by: exact rational arithmetic (``fractions``) for the fixed-point
+conversion and the variance score, brute force for the ranking rule, the
+prefill ranking recomputed from the definition over the whole prefill, a
+seal's ranking recomputed from scratch over the tokens stored at that
+moment, and the identity of running sums built by prefill and by
+token-by-token appends."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+from mixed_precision_bit_kitty_amd import synth
+
+
+def _fp16_samples(rng, n):
+    x = (rng.standard_normal(n) * np.exp(rng.uniform(-12, 10, n))).astype(np.float32)
+    x = np.clip(x, -65504, 65504).astype(np.float16)
+    x[:6] = np.array([0.0, -0.0, 2.0 ** -24, -(2.0 ** -24), 65504.0, -65504.0], np.float16)
+    return x
+
+
+def test_fixed24_is_exact():
+    x = _fp16_samples(np.random.default_rng(1), 4000)
+    a = O.fixed24(x)
+    for xi, ai in zip(x, a):
+        assert isinstance(ai, int)
+        assert Fraction(ai, 1 << 24) == Fraction(float(xi))
+
+
+def _variance_times_n2(col):
+    # n^2 * (mean of squares - square of mean), in units of 2^-48, exactly
+    n = len(col)
+    s1 = sum(Fraction(float(v)) for v in col)
+    s2 = sum(Fraction(float(v)) ** 2 for v in col)
+    return (n * s2 - s1 * s1) * (1 << 48)
+
+
+def test_score_is_exact_variance():
+    rng = np.random.default_rng(2)
+    for n in (1, 2, 7, 32, 101):
+        k = _fp16_samples(rng, n * 16).reshape(n, 16)
+        a = O.fixed24(k)
+        sc = O.running_scores(a.sum(axis=0), (a * a).sum(axis=0), n)
+        for c in range(16):
+            want = _variance_times_n2(k[:, c])
+            assert want.denominator == 1 and sc[c] == want.numerator
+            assert sc[c] >= 0
+    # a constant channel scores 0
+    a = O.fixed24(np.full((9, 1), np.float16(-3.5)))
+    assert O.running_scores(a.sum(axis=0), (a * a).sum(axis=0), 9)[0] == 0
+
+
+@pytest.mark.parametrize("k", [0, 1, 13, 32, 128])
+def test_rank_scores_bruteforce(k):
+    rng = np.random.default_rng([k, 3])
+    for trial in range(3):
+        sc = rng.integers(0, 4 if trial else 10 ** 6, 128).astype(object) * (10 ** 20)  # big ints, ties
+        idx, mask = O.rank_scores(sc, k)
+        want = [c for c in range(128)
+                if sum(1 for d in range(128) if sc[d] > sc[c] or (sc[d] == sc[c] and d < c)) < k]
+        assert list(idx) == want and mask.sum() == k
+
+
+def _ranking_from_definition(k_head, n_hi):
+    """k_head fp16 [T, D]: boosted channels by exact variance over the T
+    tokens (Fractions), ties to the lower index."""
+    T, D = k_head.shape
+    sc = [_variance_times_n2(k_head[:, c]) for c in range(D)]
+    order = sorted(range(D), key=lambda c: (-sc[c], c))[:n_hi]
+    return sorted(order)
+
+
+def test_prefill_pages_share_the_whole_prefill_ranking():
+    w = synth.TINY.with_(n_kv_heads=2, n_q_heads=4)
+    x = synth.batch(w, batch=2, ctx=100)
+    lens = [100, 70]
+    c = O.quantize_pages(x["k"], x["v"], 13, batch_lens=lens, rank_mode="running")
+    for b, n in enumerate(lens):
+        for h in range(2):
+            want = _ranking_from_definition(x["k"][b, h, :n], 13)   # the tail tokens count
+            for p in range(n // 32):
+                assert list(c.k[b]["idx"][h, p]) == want
+
+
+def test_append_seals_rank_over_all_stored_tokens():
+    w = synth.TINY.with_(n_kv_heads=1, n_q_heads=1)
+    steps = 70
+    x = synth.batch(w, batch=1, ctx=40, steps=steps)
+    c = O.quantize_pages(x["k"], x["v"], 32, rank_mode="running")
+    allk = [x["k"][0, 0, t] for t in range(40)]
+    for t in range(steps):
+        O.append_token(c, x["k_new"][t], x["v_new"][t])
+        allk.append(x["k_new"][t][0, 0])
+        n = len(allk)
+        if n % 32 == 0:   # this append sealed page n / 32 - 1
+            want = _ranking_from_definition(np.array(allk), 32)
+            assert list(c.k[0]["idx"][0, n // 32 - 1]) == want
+
+
+def test_running_sums_prefill_equal_appends():
+    w = synth.TINY.with_(n_kv_heads=2, n_q_heads=2)
+    x = synth.batch(w, batch=2, ctx=75)
+    pre = O.quantize_pages(x["k"], x["v"], 32, rank_mode="running")
+    st = O.OracleCache(2, 2, 32, rank_mode="running")
+    for t in range(75):
+        O.append_token(st, x["k"][:, :, t], x["v"][:, :, t])
+    assert (pre.s1 == st.s1).all() and (pre.s2 == st.s2).all()
+    assert np.array_equal(pre.seq_len, st.seq_len)
+
+
+def test_single_page_running_equals_page_ranking_on_exact_data():
+    # Integer-valued keys: the page's fp32 statistics are exact, so the
+    # page's own ranking and the running ranking over the same 32 tokens
+    # are the same variance order (ties to the lower index in both).
+    rng = np.random.default_rng(9)
+    k = rng.integers(-20, 21, (1, 1, 32, 128)).astype(np.float16)
+    k[..., 5] = 3.0                                  # ties at zero variance
+    v = np.zeros_like(k)
+    for n_hi in (0, 16, 32, 100):
+        a = O.quantize_pages(k, v, n_hi)
+        b = O.quantize_pages(k, v, n_hi, rank_mode="running")
+        assert np.array_equal(a.k[0]["idx"], b.k[0]["idx"])
+        for key in ("base", "boost", "kscale", "kmin"):
+            assert np.array_equal(a.k[0][key], b.k[0][key])
+
+
+def test_rank_mode_validated():
+    with pytest.raises(ValueError):
+        O.OracleCache(1, 1, 32, rank_mode="sliding")
+
+
+def test_tail_tokens_and_sealing_token_count():
+    # Channel c has standard deviation 0.1 + 0.9 c / 127 over tokens 0..31;
+    # the 8 tail tokens of a 40-token prefill give channel 0 (the smallest)
+    # a huge variance, so the prefill ranking (over all 40 tokens) boosts it
+    # while page 0's own ranking cannot.  Then 23 appends bring the length
+    # to 63 and the 24th (token 63, which seals page 1) puts a huge value in
+    # channel 1: page 1 must boost it, a ranking without the sealing token
+    # would not.
+    rng = np.random.default_rng(12)
+    sig = np.linspace(0.1, 1.0, 128)
+    k = (rng.standard_normal((1, 1, 40, 128)) * sig).astype(np.float16)
+    k[0, 0, 32:, 0] = np.array([300, -300] * 4, np.float16)
+    v = np.zeros_like(k)
+    run = O.quantize_pages(k, v, 4, rank_mode="running")
+    page = O.quantize_pages(k, v, 4)
+    assert 0 in run.k[0]["idx"][0, 0] and 0 not in page.k[0]["idx"][0, 0]
+    new = (rng.standard_normal((24, 1, 1, 128)) * sig).astype(np.float16)
+    new[-1, 0, 0, 1] = 2000.0
+    for t in range(24):
+        O.append_token(run, new[t], np.zeros_like(new[t]))
+    assert int(run.seq_len[0]) == 64 and run.n_pages(0) == 2
+    assert 1 in run.k[0]["idx"][0, 1]
+    allk = np.concatenate([k[0, 0], new[:, 0, 0]])
+    assert list(run.k[0]["idx"][0, 1]) == _ranking_from_definition(allk, 4)
+    assert list(run.k[0]["idx"][0, 1]) != _ranking_from_definition(allk[:63], 4)
