@@ -11,7 +11,9 @@ split merge).  ``--split`` times the two separate calls instead
 
 Workload (default): Llama-3-8B shape, batch 16, 32 query heads, 8 KV heads,
 head_dim 128, context 4096, hi_fraction 0.25, seeded synthetic fp16 K/V/Q.
-``--lo-bit 4`` runs the (hi_bit 8, lo_bit 4) pair instead of (4, 2).
+``--lo-bit 4`` runs the (hi_bit 8, lo_bit 4) pair instead of (4, 2);
+``--rank-mode running`` the running-variance ranking instead of per-page
+ranking.
 To keep reads coming from HBM rather than the 256 MB Infinity Cache, the
 steps rotate over L independent layer caches totalling >= 1 GiB.
 
@@ -85,7 +87,7 @@ def committed_traffic(kernel_hash, workload, entry, kernel="decode_kernel"):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, seconds, lo_bit=2):
+def cpu_baseline(w, seconds, lo_bit=2, rank_mode="page"):
     """The oracle as it stands, one thread, on a bounded sample of the same
     workload: decode steps (append + attention) on a subset of sequences."""
     import oracle as O
@@ -97,7 +99,7 @@ def cpu_baseline(w, seconds, lo_bit=2):
         limiter = None
     n_seq = 2
     x = synth.batch(w, batch=n_seq, steps=64)
-    oc = O.quantize_pages(x["k"], x["v"], w.n_hi, lo_bit=lo_bit)
+    oc = O.quantize_pages(x["k"], x["v"], w.n_hi, lo_bit=lo_bit, rank_mode=rank_mode)
     rec = O.record_bytes(w.n_hi, lo_bit=lo_bit)
     t0 = time.perf_counter()
     steps = 0
@@ -141,9 +143,10 @@ def bench_quantize(args, w):
     R = max(1, math.ceil((1 << 30) / in_bytes))
     ks = [k0] + [k0.clone() for _ in range(R - 1)]
     vs = [v0] + [v0.clone() for _ in range(R - 1)]
-    cache = binding.KittyCache(B, Hkv, w.n_hi, S + 32, lo_bit=args.lo_bit)
+    cache = binding.KittyCache(B, Hkv, w.n_hi, S + 32, lo_bit=args.lo_bit, rank_mode=_rank(args))
     rec = cache.record_bytes
-    alg = in_bytes + B * Hkv * (S // 32) * rec
+    # the running mode also writes each (sequence, KV head)'s 4 KB of sums
+    alg = in_bytes + B * Hkv * (S // 32) * rec + (B * Hkv * binding.KITTY_KEY_STATS_BYTES if _rank(args) else 0)
     for i in range(R):
         cache.quantize_pages(ks[i], vs[i])
     torch.cuda.synchronize()
@@ -170,14 +173,17 @@ def bench_quantize(args, w):
            "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": R, "ms_per_step": round(ms, 6),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
            "config": {"workload": f"{w.name}: prefill of batch {B}, {Hkv} KV heads, {S} tokens, n_hi {w.n_hi}"
-                                  + ("" if args.lo_bit == 2 else f", hi_bit 8 / lo_bit 4"),
+                                  + ("" if args.lo_bit == 2 else f", hi_bit 8 / lo_bit 4")
+                                  + ("" if not _rank(args) else ", running-variance ranking"),
                       "batch": B, "ctx": S, "n_kv_heads": Hkv, "n_hi": w.n_hi, "hi_bit": 2 * args.lo_bit,
-                      "lo_bit": args.lo_bit, "input_copies": R},
+                      "lo_bit": args.lo_bit, "rank_mode": args.rank_mode, "input_copies": R},
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(gbs / HBM_PEAK_GBS, 4),
                         "traffic": committed_traffic(khash, args.workload + _lo_suffix(args), None,
                                                      "quantize_pages_kernel"),
-                        "kernel": "quantize_pages_kernel", "bytes_per_launch": int(alg),
+                        "kernel": "quantize_pages_kernel" if not _rank(args) else
+                                  "key_stats_kernel + quantize_pages_kernel (one call)",
+                        "bytes_per_launch": int(alg),
                         "avg_launch_us": round(ms * 1e3, 3), "kernel_source_sha256_16": khash}}
     print(json.dumps(res), flush=True)
 
@@ -185,7 +191,13 @@ def bench_quantize(args, w):
 def _lo_suffix(args):
     """Name suffix of the committed counter summaries of the 4-bit pair and
     of a hi_fraction other than the workload's."""
-    return ("" if args.lo_bit == 2 else "_lo4") + ("" if args.hi_fraction is None else f"_hf{args.hi_fraction:g}")
+    return (("" if args.lo_bit == 2 else "_lo4") + ("" if args.hi_fraction is None else f"_hf{args.hi_fraction:g}")
+            + ("_running" if _rank(args) else ""))
+
+
+def _rank(args):
+    """The ABI's rank_mode value of --rank-mode."""
+    return 1 if args.rank_mode == "running" else 0
 
 
 def main():
@@ -205,6 +217,8 @@ def main():
                     help="step = kitty_append_token + kitty_decode_attention (two launches) instead of the fused step")
     ap.add_argument("--lo-bit", type=int, default=2, choices=[2, 4],
                     help="bit-width pair: 2 = (hi_bit 4, lo_bit 2), 4 = (hi_bit 8, lo_bit 4)")
+    ap.add_argument("--rank-mode", default="page", choices=["page", "running"],
+                    help="boosted channels by each page's variance (page) or the head's running variance (running)")
     ap.add_argument("--hi-fraction", type=float, default=None,
                     help="override the workload's hi_fraction (n_hi = hi_fraction x 128, a multiple of 16)")
     ap.add_argument("--quantize", action="store_true",
@@ -235,12 +249,12 @@ def main():
     k_new, v_new, q_new = dev(x["k_new"]), dev(x["v_new"]), dev(x["q_new"])
 
     max_tokens = ctx + K + W + 32
-    probe = binding.KittyCache(1, Hkv, n_hi, max_tokens, lo_bit=args.lo_bit)
+    probe = binding.KittyCache(1, Hkv, n_hi, max_tokens, lo_bit=args.lo_bit, rank_mode=_rank(args))
     layer_bytes = B * probe.max_pages * probe.page_bytes
     del probe
     L = args.layers or max(1, math.ceil((1 << 30) / layer_bytes))
     print(f"[bench] {L} layer caches x {layer_bytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
-    layers = [binding.KittyCache(B, Hkv, n_hi, max_tokens, lo_bit=args.lo_bit) for _ in range(L)]
+    layers = [binding.KittyCache(B, Hkv, n_hi, max_tokens, lo_bit=args.lo_bit, rank_mode=_rank(args)) for _ in range(L)]
     kd, vd = dev(x["k"]), dev(x["v"])
     layers[0].quantize_pages(kd, vd)
     for c in layers[1:]:
@@ -248,6 +262,8 @@ def main():
         c.tail_k.copy_(layers[0].tail_k)
         c.tail_v.copy_(layers[0].tail_v)
         c.seq_lens.copy_(layers[0].seq_lens)
+        if c.key_stats is not None:
+            c.key_stats.copy_(layers[0].key_stats)
     del kd, vd
     # Every sequence of a layer has the same length.  Layer l takes its steps
     # i = l, l + L, ...; the decode bound max_seq_len is the longest length
@@ -368,16 +384,16 @@ def main():
         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "config": {"workload": f"{w.name}: one layer, batch {B}, {Hq} query heads, {Hkv} KV heads, head_dim 128, "
                                f"context {ctx}+, hi_fraction {w.hi_fraction} (n_hi {n_hi}), "
-                               f"hi_bit {2 * args.lo_bit} / lo_bit {args.lo_bit}; step = "
+                               f"hi_bit {2 * args.lo_bit} / lo_bit {args.lo_bit}, {args.rank_mode} ranking; step = "
                                f"{'append + decode (two launches)' if args.split else 'fused append + decode (one launch)'} "
                                f"(replayed from HIP graphs of {L} steps); {L} layer caches rotated ({L * layer_bytes / 2**30:.2f} GiB)",
                    "batch": B, "ctx": ctx, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": 128, "n_hi": n_hi,
-                   "hi_bit": 2 * args.lo_bit, "lo_bit": args.lo_bit, "layers_rotated": L},
+                   "hi_bit": 2 * args.lo_bit, "lo_bit": args.lo_bit, "rank_mode": args.rank_mode, "layers_rotated": L},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(w.with_(batch=B), args.cpu_seconds, args.lo_bit)
+        res["cpu_baseline"] = cpu_baseline(w.with_(batch=B), args.cpu_seconds, args.lo_bit, args.rank_mode)
     print(json.dumps(res), flush=True)
 
 

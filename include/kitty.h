@@ -79,11 +79,13 @@ typedef struct {
  *    kitty_kv_view_t.key_stats; at most 2^23 tokens per sequence. */
 enum { KITTY_RANK_PAGE = 0, KITTY_RANK_RUNNING = 1 };
 
-/* Bytes of running-mode state per (sequence, KV head): int64 s1[128] (sum of
- * k * 2^24), uint64 s2_lo[128] and s2_hi[128] (the 128-bit sum of (k * 2^24)^2),
- * uint32 mask[4] (the ranking of the last prefill: channel c at bit c & 31 of
- * word c >> 5), then reserved bytes. */
-#define KITTY_KEY_STATS_BYTES 4096
+/* Bytes of running-mode state per (sequence, KV head): two copies of the
+ * sums at bytes 0 and 3072, each int64 s1[128] (sum of k * 2^24), uint64
+ * s2_lo[128] and s2_hi[128] (the 128-bit sum of (k * 2^24)^2); a sequence of
+ * n tokens keeps its sums in copy n & 1.  Then uint32 mask[4] at byte 6144
+ * (the ranking of the last prefill: channel c at bit c & 31 of word c >> 5)
+ * and reserved bytes. */
+#define KITTY_KEY_STATS_BYTES 8192
 
 /* A paged cache (Abstract: page-centric KV layout).  One physical page holds
  * the records of all Hkv heads for 32 consecutive tokens of one sequence; the

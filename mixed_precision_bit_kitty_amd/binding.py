@@ -27,7 +27,7 @@ KITTY_ERR_HIP = -4
 KITTY_ERR_NO_PAGES = -5
 KITTY_RANK_PAGE = 0
 KITTY_RANK_RUNNING = 1
-KITTY_KEY_STATS_BYTES = 4096
+KITTY_KEY_STATS_BYTES = 8192
 
 HEAD_DIM = 128
 PAGE_TOKENS = 32
@@ -223,7 +223,7 @@ class KittyCache:
                 sequence b's page j -> physical page b * max_pages + j)
     tail_k/v    fp16  [batch, Hkv, 32, 128]
     seq_lens    int32 [batch]
-    key_stats   uint8 [batch, Hkv, 4096] running sums (rank_mode KITTY_RANK_RUNNING only, else None)
+    key_stats   uint8 [batch, Hkv, 8192] running sums (rank_mode KITTY_RANK_RUNNING only, else None)
     """
 
     def __init__(self, batch, n_kv_heads, n_hi, max_tokens, device="cuda", block_table=None, n_pages=None,

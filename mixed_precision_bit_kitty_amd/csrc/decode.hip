@@ -185,7 +185,6 @@ struct alignas(16) Lds {  // 16-byte aligned size: every wave's area keeps 16-by
   };
   float red[2][4][4];           // final corrections [kind][head][group]
   int flag;                     // workgroup broadcast of the arrival count (wave 0's copy)
-  int seq_flag;                 // workgroup broadcast of the sequence arrival count (wave 0's copy)
 };
 static_assert(sizeof(float) * 4 * kPartialStride <= kRing * rec_bytes(0), "partial fits over the ring");
 constexpr int kLdsPerCu = 160 * 1024;
@@ -412,7 +411,18 @@ void decode_kernel(DecodeParams p) {
   const size_t toff = ((size_t)b * p.n_kv_heads + hk) * kPageTokens * kHeadDim;  // (b, hk) tail
   const size_t noff = ((size_t)b * p.n_kv_heads + hk) * kHeadDim;  // (b, hk) row of k_new / v_new
   uint8_t* seal_rec = nullptr;  // the record this call sealed (wave-uniform; tail wave only)
+  pq::LaneSums run{};  // running mode: the head's sums with the new token
   if (tail_wave && fused) {
+    if constexpr (RUN) {
+      // running ranking mode ("Kitty -- Dynamic Channel-wise Mixed-Precision
+      // Keys", Decode phase steps 1-2): every head group adds the new token to
+      // the current copy of the sums; head group 0 stores the result as the
+      // next copy, which no wave of this launch reads
+      uint8_t* st = p.key_stats + ((size_t)b * p.n_kv_heads + hk) * pq::kStatsBytes;
+      run = pq::load_sums(pq::sums_copy(st, (uint32_t)n0), lane);
+      pq::add_token(run, *reinterpret_cast<const uint32_t*>(p.k_new + noff + 2 * lane));
+      if (hg == 0) pq::store_sums(pq::sums_copy(st, (uint32_t)n0 + 1), lane, run);
+    }
     if (hg == 0) {  // the append: the token goes to tail slot n0 mod 32
       const int slot = n0 % kPageTokens;
       *reinterpret_cast<uint32_t*>(p.tail_k + toff + (size_t)slot * kHeadDim + 2 * lane) =
@@ -431,14 +441,7 @@ void decode_kernel(DecodeParams p) {
                          : p.seal_scratch + ((((size_t)b * p.n_kv_heads + hk) * (p.n_head_groups - 1)) +
                                              (hg - 1)) * RB;
       pq::RankIn rk{false, false, false};
-      if constexpr (RUN) {
-        // running ranking mode ("Kitty -- Dynamic Channel-wise Mixed-Precision
-        // Keys", Decode phase steps 1-2): the head's sums with the new token
-        // (in registers; the sequence's last unit stores them) rank the page
-        pq::LaneSums r = pq::load_sums(p.key_stats + ((size_t)b * p.n_kv_heads + hk) * pq::kStatsBytes, lane);
-        pq::add_token(r, *reinterpret_cast<const uint32_t*>(p.k_new + noff + 2 * lane));
-        rk = pq::running_rank(r, (uint32_t)n0 + 1, p.n_hi, lane);
-      }
+      if constexpr (RUN) rk = pq::running_rank(run, (uint32_t)n0 + 1, p.n_hi, lane);
       pq::quantize_page_wave<NHI, BITS>(pq::RowSrc{p.tail_k + toff, p.k_new + noff},
                                         pq::RowSrc{p.tail_v + toff, p.v_new + noff}, seal_rec,
                                         reinterpret_cast<uint8_t*>(&sm), p.n_hi, rk);
@@ -777,22 +780,6 @@ void decode_kernel(DecodeParams p) {
     if (fused && threadIdx.x == 0 && old == units - 1) {
       __hip_atomic_store(p.seq_lens + b, n0 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(seq_counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (RUN && fused) {
-      // running mode: every unit of the sequence has read the old sums (its
-      // tail wave did, before the unit counted itself), so the last unit adds
-      // the new token to the sums of every KV head of the sequence
-      if (threadIdx.x == 0) all[0].seq_flag = old;
-      __syncthreads();
-      if (all[0].seq_flag == units - 1) {
-        for (int i = threadIdx.x; i < p.n_kv_heads * 64; i += nthr) {
-          const int h2 = i >> 6, l2 = i & 63;
-          uint8_t* st = p.key_stats + ((size_t)b * p.n_kv_heads + h2) * pq::kStatsBytes;
-          pq::LaneSums r = pq::load_sums(st, l2);
-          pq::add_token(r, *reinterpret_cast<const uint32_t*>(p.k_new + ((size_t)b * p.n_kv_heads + h2) * kHeadDim + 2 * l2));
-          pq::store_sums(st, l2, r);
-        }
-      }
     }
   };
   auto out_of = [&](int o) { return p.out + ((size_t)b * p.n_q_heads + hq0 + (o >> 7)) * kHeadDim + (o & 127); };

@@ -137,7 +137,7 @@ struct DecodeParams {
   int* seq_counters;       // [batch] finished units per sequence (fused step), zero between calls
   uint8_t* seal_scratch;   // [batch][Hkv][n_head_groups - 1] records re-quantized by head groups >= 1
   float* out;              // [batch][Hq][D]
-  uint8_t* key_stats;      // running ranking mode: written only by the fused step (the sequence's last unit)
+  uint8_t* key_stats;      // running ranking mode: the fused step reads copy n & 1 and writes copy (n + 1) & 1
 };
 
 constexpr int kPartialStride = 132;  // m, l, O[128], 2 pad floats
@@ -158,7 +158,7 @@ struct SplitPlan {
 SplitPlan plan_splits(int batch, int n_kv_heads, int n_head_groups, int max_seq_len, int wmax);
 int decode_max_wg_waves(int n_hi, int lo_bit);
 
-constexpr int kKeyStatsBytes = 4096;  // running-mode state of one (sequence, KV head)
+constexpr int kKeyStatsBytes = 8192;  // running-mode state of one (sequence, KV head)
 constexpr int kMaxRunningTokens = 1 << 23;  // running mode: exact scores stay below 2^127
 
 hipError_t launch_quantize(const QuantizeParams& p, hipStream_t stream);

@@ -159,10 +159,10 @@ __device__ __forceinline__ uint32_t pack_word4(uint64_t a) { return gather4_nib(
 // ballots (TOPBIT = the highest bit a key can have), then the keys equal to
 // T are taken in channel order by ballot popcounts.
 template <typename K, int TOPBIT>
-__device__ __forceinline__ void select_top(K k0, K k1, int n, int lane, bool& h0, bool& h1) {
+__device__ __forceinline__ void select_top(K k0, K k1, int n, int lane, bool& h0, bool& h1, int top = TOPBIT) {
   const uint64_t below = (1ull << lane) - 1ull;
   K T = 0;
-  for (int bit = TOPBIT; bit >= 0; --bit) {
+  for (int bit = top; bit >= 0; --bit) {  // bits above `top` are clear in every key
     const K cand = T | ((K)1 << bit);
     const int cnt = __popcll(__ballot(k0 >= cand)) + __popcll(__ballot(k1 >= cand));
     if (cnt >= n) T = cand;
@@ -187,22 +187,33 @@ __device__ __forceinline__ void select_top(K k0, K k1, int n, int lane, bool& h0
 // variance, in units of 2^-48) is exact, so no accumulation order matters.
 typedef unsigned __int128 u128;
 
-// State of one (sequence, KV head), kStatsBytes bytes: int64 s1[128],
-// uint64 s2 low halves [128], uint64 s2 high halves [128], uint32 mask[4]
-// (channel c at bit c & 31 of word c >> 5: the ranking of the last prefill),
-// then reserved bytes.  Lane l's channels 2l, 2l + 1 are 16 contiguous bytes
-// of each array.
-constexpr int kStatsS1 = 0, kStatsS2Lo = 1024, kStatsS2Hi = 2048, kStatsMask = 3072, kStatsBytes = kKeyStatsBytes;
+// State of one (sequence, KV head), kStatsBytes bytes: two copies of the
+// sums, copy c at byte kStatsCopy * c, each int64 s1[128], uint64 s2 low
+// halves [128], uint64 s2 high halves [128]; then uint32 mask[4] (channel c
+// at bit c & 31 of word c >> 5: the ranking of the last prefill) and
+// reserved bytes.  A sequence holding n tokens keeps its sums in copy n & 1,
+// so the step that appends token n reads copy n & 1 and writes copy
+// (n + 1) & 1 while other waves of the same launch still read copy n & 1.
+// Lane l's channels 2l, 2l + 1 are 16 contiguous bytes of each array.
+constexpr int kStatsS1 = 0, kStatsS2Lo = 1024, kStatsS2Hi = 2048, kStatsCopy = 3072;
+constexpr int kStatsMask = 2 * kStatsCopy, kStatsBytes = kKeyStatsBytes;
 static_assert(kStatsMask + 16 <= kStatsBytes, "key statistics layout");
+__device__ __forceinline__ uint8_t* sums_copy(uint8_t* st, uint32_t n) { return st + kStatsCopy * (n & 1u); }
 
-__device__ __forceinline__ int64_t fixed24(uint32_t h16) {
+// s1 += a, s2 += a^2 for a = k * 2^24 (k the fp16 value with bits h16),
+// without a wide multiply: |a| =
+// M 2^s with M < 2^11, so a^2 = (M M) 2^(2s) is one 24-bit product shifted
+// into 128 bits (below 2^80; its high word is nonzero only for 2s > 42).
+__device__ __forceinline__ void accumulate(uint32_t h16, int64_t& s1, u128& s2) {
   const uint32_t e = (h16 >> 10) & 31u, m = h16 & 1023u;
-  const int64_t mag = e ? (int64_t)(1024u | m) << (e - 1) : (int64_t)m;  // normal: (1024 + m) 2^(e-1); subnormal: m
-  return (h16 & 0x8000u) ? -mag : mag;
-}
-__device__ __forceinline__ u128 square(int64_t a) {
-  const uint64_t m = a < 0 ? 0ull - (uint64_t)a : (uint64_t)a;
-  return (u128)m * m;
+  const uint32_t M = e ? (m | 1024u) : m;
+  const uint32_t s = e ? e - 1u : 0u;
+  const int64_t a = (int64_t)((uint64_t)M << s);
+  s1 += (h16 & 0x8000u) ? -a : a;
+  const uint64_t mm = (uint64_t)(M * M);
+  const uint32_t sh = 2 * s;
+  const uint64_t hi = sh > 42 ? (mm >> (64 - sh)) : 0ull;
+  s2 += ((u128)hi << 64) | (mm << sh);
 }
 // n s2 - s1^2 >= 0 (Cauchy-Schwarz); below 2^127 for n < 2^23
 __device__ __forceinline__ u128 running_score(int64_t s1, u128 s2, uint32_t n) {
@@ -237,11 +248,8 @@ __device__ __forceinline__ void store_sums(uint8_t* st, int lane, const LaneSums
 }
 // add one token (channels 2l, 2l + 1 as the fp16 pair `k2`, low half first)
 __device__ __forceinline__ void add_token(LaneSums& r, uint32_t k2) {
-  const int64_t a0 = fixed24(k2 & 0xFFFFu), a1 = fixed24(k2 >> 16);
-  r.s1[0] += a0;
-  r.s1[1] += a1;
-  r.s2[0] += square(a0);
-  r.s2[1] += square(a1);
+  accumulate(k2 & 0xFFFFu, r.s1[0], r.s2[0]);
+  accumulate(k2 >> 16, r.s1[1], r.s2[1]);
 }
 
 // Boosted channels given from outside the page (the running mode) or, when
@@ -249,14 +257,21 @@ __device__ __forceinline__ void add_token(LaneSums& r, uint32_t k2) {
 struct RankIn {
   bool given, h0, h1;
 };
-// The running ranking over n tokens from lane sums.
+// The running ranking over n tokens from lane sums.  The bitwise search
+// starts at the highest bit set in any score (a wave maximum), which skips
+// most of the 128-bit range.
 __device__ __forceinline__ RankIn running_rank(const LaneSums& r, uint32_t n, int n_hi, int lane) {
   RankIn rk{true, false, false};
   if (n_hi >= kHeadDim) {
     rk.h0 = rk.h1 = true;
   } else if (n_hi > 0) {
-    select_top<u128, 127>(running_score(r.s1[0], r.s2[0], n), running_score(r.s1[1], r.s2[1], n), n_hi, lane,
-                          rk.h0, rk.h1);
+    const u128 k0 = running_score(r.s1[0], r.s2[0], n), k1 = running_score(r.s1[1], r.s2[1], n);
+    const u128 m = k0 > k1 ? k0 : k1;
+    const uint64_t mh = (uint64_t)(m >> 64), ml = (uint64_t)m;
+    int top = mh ? 127 - __builtin_clzll(mh) : (ml ? 63 - __builtin_clzll(ml) : 0);
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) top = max(top, __shfl_xor(top, s));
+    select_top<u128, 127>(k0, k1, n_hi, lane, rk.h0, rk.h1, top);
   }
   return rk;
 }

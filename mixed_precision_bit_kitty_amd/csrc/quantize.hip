@@ -38,22 +38,45 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int mask) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// Running ranking mode, ahead of the prefill: the exact running sums of
-// every (sequence, KV head) over the sequence's n_b tokens (tail included;
-// "Kitty -- Dynamic Channel-wise Mixed-Precision Keys", How it works /
-// Prefill phase, steps 1 and 5) become its state, and their ranking is
-// stored for quantize_pages_kernel.  grid (Hkv, batch), 16 waves: lane
-// (cb = lane & 15, tg = lane >> 4) of wave w sums channels 8cb .. 8cb + 7
-// over tokens 32j + tg + 4i (i = 0..7) of the token blocks j = w, w + 16,
-// ...; integer sums may be added in any order.
-__global__ __launch_bounds__(1024) void key_stats_kernel(QuantizeParams p) {
-  __shared__ int64_t ws1[16][kHeadDim];
-  __shared__ u128 ws2[16][kHeadDim];
-  const int h = blockIdx.x, b = blockIdx.y;
+// Running ranking mode, ahead of the prefill ("Kitty -- Dynamic
+// Channel-wise Mixed-Precision Keys", How it works / Prefill phase, steps 1
+// and 5): the exact running sums of every filled (sequence, KV head) over
+// its n_b tokens (tail included) become its state, and their ranking is
+// stored for quantize_pages_kernel.  Integer sums may be added in any
+// order, so the work is split in chunks of kChunkPages pages:
+//  * key_chunk_kernel sums one chunk and writes the partial sums into the
+//    record slot of the chunk's first page, which quantize_pages_kernel
+//    overwrites later (3072 bytes; every record is at least that long);
+//  * key_rank_kernel adds the partials of a (sequence, KV head) and the
+//    tokens of a chunk without a sealed page (fewer than 32 tail tokens),
+//    stores the state and ranks it.
+constexpr int kChunkPages = 8;
+constexpr int kChunkTokens = kChunkPages * kPageTokens;
+static_assert(rec_bytes(0, 2) >= kStatsCopy, "a chunk's partial sums fit the smallest record");
+
+__device__ __forceinline__ int prefill_len(const QuantizeParams& p, int b) {
+  const int n = p.lens ? p.lens[b] : p.S;
+  return n > p.S ? p.S : n;  // negative: the sequence is left as it is
+}
+// the record slot of (b, page, h), or null when its block table entry is invalid
+__device__ __forceinline__ uint8_t* record_of(const QuantizeParams& p, int b, int page, int h) {
+  const int phys = p.block_table[(size_t)b * p.max_pages + page];
+  if (phys < 0 || (int64_t)phys >= p.n_pages) return nullptr;
+  return p.pages + (int64_t)phys * p.page_bytes + (int64_t)h * rec_bytes(boost_slots(p.n_hi), p.lo_bit);
+}
+
+// grid (chunks, Hkv, batch), 4 waves.  Lane (cb = lane & 15, tg = lane >> 4)
+// of wave w sums channels 8cb .. 8cb + 7 over tokens 32j + tg + 4i (i =
+// 0..7) of pages j = 8c + 2w, 8c + 2w + 1 of chunk c.
+__global__ __launch_bounds__(256) void key_chunk_kernel(QuantizeParams p) {
+  __shared__ int64_t ws1[4][kHeadDim];
+  __shared__ u128 ws2[4][kHeadDim];
+  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, cb = lane & 15, tg = lane >> 4;
-  int n = p.lens ? p.lens[b] : p.S;
-  if (n < 0) return;  // a negative length leaves sequence b as it is (block-uniform)
-  n = n > p.S ? p.S : n;
+  const int n = prefill_len(p, b);
+  const int P = n < 0 ? 0 : n / kPageTokens;
+  if (kChunkPages * chunk >= P) return;  // no sealed page here: key_rank_kernel sums these tokens (block-uniform)
+  const int t_end = min(n, kChunkTokens * (chunk + 1));
   const _Float16* kb = p.k + ((size_t)b * p.n_kv_heads + h) * (size_t)p.S * kHeadDim + 8 * cb;
   int64_t s1[8];
   u128 s2[8];
@@ -62,21 +85,20 @@ __global__ __launch_bounds__(1024) void key_stats_kernel(QuantizeParams p) {
     s1[e] = 0;
     s2[e] = 0;
   }
-  for (int j = wave; kPageTokens * j < n; j += 16) {
+#pragma unroll
+  for (int pg = 0; pg < 2; ++pg) {
+    const int t0 = kChunkTokens * chunk + kPageTokens * (2 * wave + pg);
     u32x4 rows[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {  // every load issued before the first use
-      const int t = kPageTokens * j + tg + 4 * i;
-      rows[i] = t < n ? *reinterpret_cast<const u32x4*>(kb + (size_t)t * kHeadDim) : u32x4{0u, 0u, 0u, 0u};
+      const int t = t0 + tg + 4 * i;
+      rows[i] = t < t_end ? *reinterpret_cast<const u32x4*>(kb + (size_t)t * kHeadDim) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {  // +0 halves of skipped tokens add nothing
-        const int64_t a = fixed24((rows[i][e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-        s1[e] += a;
-        s2[e] += square(a);
-      }
+      for (int e = 0; e < 8; ++e)  // +0 halves of skipped tokens add nothing
+        accumulate((rows[i][e >> 1] >> (16 * (e & 1))) & 0xFFFFu, s1[e], s2[e]);
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e)
@@ -94,26 +116,64 @@ __global__ __launch_bounds__(1024) void key_stats_kernel(QuantizeParams p) {
     }
   }
   __syncthreads();
-  uint8_t* st = p.key_stats + ((size_t)b * p.n_kv_heads + h) * kStatsBytes;
   if (threadIdx.x < kHeadDim) {
     const int c = threadIdx.x;
-    int64_t t1 = 0;
-    u128 t2 = 0;
-    for (int w = 0; w < 16; ++w) {
-      t1 += ws1[w][c];
-      t2 += ws2[w][c];
+    int64_t t1 = ws1[0][c] + ws1[1][c] + ws1[2][c] + ws1[3][c];
+    const u128 t2 = ws2[0][c] + ws2[1][c] + ws2[2][c] + ws2[3][c];
+    uint8_t* rec = record_of(p, b, kChunkPages * chunk, h);
+    if (rec) {
+      reinterpret_cast<int64_t*>(rec + kStatsS1)[c] = t1;
+      reinterpret_cast<uint64_t*>(rec + kStatsS2Lo)[c] = (uint64_t)t2;
+      reinterpret_cast<uint64_t*>(rec + kStatsS2Hi)[c] = (uint64_t)(t2 >> 64);
     }
-    ws1[0][c] = t1;  // only this thread touches column c
-    ws2[0][c] = t2;
   }
+}
+
+// grid (Hkv, batch), 2 waves: thread c adds channel c's chunk partials (and
+// the tokens of a chunk without a sealed page), stores the state; wave 0
+// ranks it and stores the mask.
+__global__ __launch_bounds__(128) void key_rank_kernel(QuantizeParams p) {
+  __shared__ int64_t ts1[kHeadDim];
+  __shared__ u128 ts2[kHeadDim];
+  const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x, lane = threadIdx.x & 63;
+  const int n = prefill_len(p, b);
+  if (n < 0) return;  // block-uniform
+  const int P = n / kPageTokens;
+  int64_t s1 = 0;
+  u128 s2 = 0;
+  const int chunks = (P + kChunkPages - 1) / kChunkPages;  // chunks with a sealed page
+  for (int j0 = 0; j0 < chunks; j0 += 8) {  // eight chunks per round trip
+    const uint8_t* recs[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) recs[u] = j0 + u < chunks ? record_of(p, b, kChunkPages * (j0 + u), h) : nullptr;
+    int64_t v1[8];
+    uint64_t vlo[8], vhi[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {  // an invalid block table entry: the result is undefined, nothing is read
+      v1[u] = recs[u] ? reinterpret_cast<const int64_t*>(recs[u] + kStatsS1)[c] : 0;
+      vlo[u] = recs[u] ? reinterpret_cast<const uint64_t*>(recs[u] + kStatsS2Lo)[c] : 0;
+      vhi[u] = recs[u] ? reinterpret_cast<const uint64_t*>(recs[u] + kStatsS2Hi)[c] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      s1 += v1[u];
+      s2 += ((u128)vhi[u] << 64) | vlo[u];
+    }
+  }
+  const _Float16* kb = p.k + ((size_t)b * p.n_kv_heads + h) * (size_t)p.S * kHeadDim + c;
+  for (int t = kChunkTokens * chunks; t < n; ++t)  // fewer than 32 tail tokens
+    accumulate(__builtin_bit_cast(uint16_t, kb[(size_t)t * kHeadDim]), s1, s2);
+  ts1[c] = s1;
+  ts2[c] = s2;
   __syncthreads();
-  if (wave == 0) {
+  uint8_t* st = p.key_stats + ((size_t)b * p.n_kv_heads + h) * kStatsBytes;
+  if (threadIdx.x < 64) {
     LaneSums r;
-    r.s1[0] = ws1[0][2 * lane];
-    r.s1[1] = ws1[0][2 * lane + 1];
-    r.s2[0] = ws2[0][2 * lane];
-    r.s2[1] = ws2[0][2 * lane + 1];
-    store_sums(st, lane, r);
+    r.s1[0] = ts1[2 * lane];
+    r.s1[1] = ts1[2 * lane + 1];
+    r.s2[0] = ts2[2 * lane];
+    r.s2[1] = ts2[2 * lane + 1];
+    store_sums(sums_copy(st, (uint32_t)n), lane, r);
     const RankIn rk = running_rank(r, (uint32_t)n, p.n_hi, lane);
     // mask word m: channel 32m + 2i + j at bit 2i + j, from lanes 16m + i
     const uint64_t B0 = __ballot(rk.h0), B1 = __ballot(rk.h1);
@@ -201,9 +261,9 @@ __global__ __launch_bounds__(512) void append_token_kernel(AppendParams p) {  //
     RankIn rk{false, false, false};
     if (p.key_stats) {
       uint8_t* st = p.key_stats + ((size_t)b * p.n_kv_heads + h) * kStatsBytes;
-      LaneSums r = load_sums(st, lane);
+      LaneSums r = load_sums(sums_copy(st, (uint32_t)n), lane);
       add_token(r, k2);
-      store_sums(st, lane, r);
+      store_sums(sums_copy(st, (uint32_t)n + 1), lane, r);
       if (slot == kPageTokens - 1) rk = running_rank(r, (uint32_t)n + 1, p.n_hi, lane);
     }
     if (slot == kPageTokens - 1) {
@@ -226,7 +286,9 @@ __global__ __launch_bounds__(512) void append_token_kernel(AppendParams p) {  //
 template <int NHI>
 hipError_t launch_quantize_t(const QuantizeParams& p, hipStream_t stream) {
   if (p.key_stats) {  // running mode: sums and ranking first, on the same stream
-    hipLaunchKernelGGL(key_stats_kernel, dim3(p.n_kv_heads, p.batch), dim3(1024), 0, stream, p);
+    const int chunks = (p.S / kPageTokens + kChunkPages - 1) / kChunkPages;
+    if (chunks > 0) hipLaunchKernelGGL(key_chunk_kernel, dim3(chunks, p.n_kv_heads, p.batch), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(key_rank_kernel, dim3(p.n_kv_heads, p.batch), dim3(128), 0, stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

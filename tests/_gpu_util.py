@@ -89,10 +89,11 @@ def compare_decode(cache, oc, q, max_seq_len=None, seq_map=None, atol=ATOL):
 
 
 def oracle_state_bytes(oc, b, h, with_mask=None):
-    """The library's running-mode state layout of (sequence b, head h) from
-    the oracle's exact sums: int64 s1[128], uint64 low / high halves of the
-    128-bit s2[128] (and, if given, the uint32 mask[4] of a ranking)."""
-    out = np.zeros(4096, np.uint8)
+    """One copy of the library's running-mode sums of (sequence b, head h)
+    from the oracle's exact sums: int64 s1[128], uint64 low / high halves of
+    the 128-bit s2[128] (3072 bytes), and, if given, the uint32 mask[4] of a
+    ranking (16 more bytes)."""
+    out = np.zeros(3088, np.uint8)
     s1 = np.array([int(x) for x in oc.s1[b, h]], dtype=object)
     s2 = np.array([int(x) for x in oc.s2[b, h]], dtype=object)
     out[0:1024] = np.array([int(x) & (2 ** 64 - 1) for x in s1], dtype=np.uint64).view(np.uint8)
@@ -107,16 +108,19 @@ def oracle_state_bytes(oc, b, h, with_mask=None):
 
 
 def compare_state(cache, oc, seq_map=None, masks=False):
-    """Running sums of every (sequence, head) byte-equal to the oracle's;
-    with masks=True also the stored prefill ranking."""
+    """Current running sums (copy seq_len & 1) of every (sequence, head)
+    byte-equal to the oracle's; with masks=True also the stored prefill
+    ranking (byte 6144)."""
     ks = host(cache.key_stats)
     for b in range(oc.batch):
         gb = b if seq_map is None else seq_map[b]
+        o = 3072 * (int(oc.seq_len[b]) & 1)
         for h in range(oc.n_kv_heads):
             m = oc.running_mask(b)[h] if masks else None
             want = oracle_state_bytes(oc, b, h, m)
-            n = 3088 if masks else 3072
-            assert np.array_equal(ks[gb, h, :n], want[:n]), f"state of sequence {b} head {h} differs"
+            assert np.array_equal(ks[gb, h, o:o + 3072], want[:3072]), f"sums of sequence {b} head {h} differ"
+            if masks:
+                assert np.array_equal(ks[gb, h, 6144:6160], want[3072:3088]), f"ranking of sequence {b} head {h}"
 
 
 def step_twins(w, lens, steps, ctx, n_hi=32, msl=None, check_every=1, lo_bit=2, rank_mode="page"):
@@ -149,8 +153,11 @@ def step_twins(w, lens, steps, ctx, n_hi=32, msl=None, check_every=1, lo_bit=2, 
             assert np.array_equal(a, b), f"step {t}: fused and separate outputs differ without a seal"
         assert np.array_equal(host(fused.seq_lens), host(split.seq_lens)), f"step {t}"
         assert np.array_equal(host(fused.tail_k), host(split.tail_k)), f"step {t}"
-        if rm:
-            assert np.array_equal(host(fused.key_stats), host(split.key_stats)), f"step {t}: running sums differ"
+        if rm:  # the current copy of the sums (the other copy holds older sums in both)
+            ka, kb_ = host(fused.key_stats), host(split.key_stats)
+            for bb in range(batch):
+                o = 3072 * (int(oc.seq_len[bb]) & 1)
+                assert np.array_equal(ka[bb, :, o:o + 3072], kb_[bb, :, o:o + 3072]), f"step {t}: running sums differ"
         if seals or t % check_every == 0 or t == steps - 1:
             assert np.array_equal(host(fused.pool), host(split.pool)), f"step {t}: page pools differ"
             compare_tails(fused, oc)

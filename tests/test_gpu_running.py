@@ -45,7 +45,7 @@ def test_prefill_leaves_negative_slots_alone():
     w = synth.LLAMA3_8B.with_(n_kv_heads=2, n_q_heads=8)
     x = synth.batch(w, batch=2, ctx=64, steps=0)
     cache = new_cache(2, 2, 32, 64, rank_mode=RUN)
-    cache.key_stats.copy_(torch.arange(2 * 2 * 4096, device="cuda").reshape(2, 2, 4096).to(torch.uint8))
+    cache.key_stats.copy_(torch.arange(2 * 2 * 8192, device="cuda").reshape(2, 2, 8192).to(torch.uint8))
     before = host(cache.key_stats)[1].copy()
     cache.quantize_pages(dev(x["k"]), dev(x["v"]), lens=dev(np.array([64, -1], np.int32)))
     assert np.array_equal(host(cache.key_stats)[1], before)

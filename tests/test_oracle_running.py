@@ -160,3 +160,20 @@ def test_tail_tokens_and_sealing_token_count():
     allk = np.concatenate([k[0, 0], new[:, 0, 0]])
     assert list(run.k[0]["idx"][0, 1]) == _ranking_from_definition(allk, 4)
     assert list(run.k[0]["idx"][0, 1]) != _ranking_from_definition(allk[:63], 4)
+
+
+def test_stored_mode_comparison_reproduces():
+    # tests/golden/ranking_mse.txt is written by tests/golden/ranking_mse.py;
+    # its first row (the tiny workload, 64 appends) is recomputed here
+    import importlib.util
+    import os
+    here = os.path.join(os.path.dirname(__file__), "golden")
+    spec = importlib.util.spec_from_file_location("ranking_mse", os.path.join(here, "ranking_mse.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    w, hf, n_seq, steps = mod.CASES[0]
+    w2, n_hi, err, same = mod.measure(w, hf, n_seq, steps)
+    row = (f"{w2.name} | {n_hi} | {n_seq} | {steps} | {err['page']:.5e} | {err['running']:.5e} | "
+           f"{err['running'] / err['page']:.4f} | {same:.3f}")
+    rows = [l.strip() for l in open(os.path.join(here, "ranking_mse.txt")) if not l.startswith("#")]
+    assert rows[0] == row
