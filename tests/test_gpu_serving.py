@@ -13,7 +13,7 @@ import pytest
 import oracle as O
 from mixed_precision_bit_kitty_amd import synth
 
-from _gpu_util import ATOL, compare_records, compare_tails, dev, host
+from _gpu_util import ATOL, compare_records, compare_state, compare_tails, dev, host
 
 pytestmark = pytest.mark.gpu
 
@@ -29,12 +29,15 @@ def _gpu():
 REQUESTS = [(45, 40), (0, 35), (100, 20), (31, 33), (64, 10), (7, 50), (200, 12), (33, 30)]
 
 
-def test_serving_with_a_shared_pool():
+@pytest.mark.parametrize("rank_mode", ["page", "running"])
+def test_serving_with_a_shared_pool(rank_mode):
+    # running mode: a reused slot's sums restart with its new prefill
     import torch
     from mixed_precision_bit_kitty_amd import binding as B
     w = synth.LLAMA3_8B.with_(n_kv_heads=2, n_q_heads=8)
     n_slots, H, Hq, n_hi = 4, w.n_kv_heads, w.n_q_heads, w.n_hi
-    cache = B.KittyCache.with_pool(n_slots, H, n_hi, max_tokens=256, n_pages=14)
+    cache = B.KittyCache.with_pool(n_slots, H, n_hi, max_tokens=256, n_pages=14,
+                                   rank_mode=B.KITTY_RANK_RUNNING if rank_mode == "running" else B.KITTY_RANK_PAGE)
     reqs = []
     for r, (prompt, gen) in enumerate(REQUESTS):
         x = synth.batch(w.with_(seed=200 + r), batch=1, ctx=max(prompt, 1), steps=gen)
@@ -59,12 +62,14 @@ def test_serving_with_a_shared_pool():
                 before = host(cache.seq_lens).copy()
                 cache.reserve(b, q["prompt"])
                 cache.quantize_pages(k, v, lens=dev(lens))
-                q["oc"] = O.quantize_pages(q["x"]["k"], q["x"]["v"], n_hi, batch_lens=[q["prompt"]])
+                q["oc"] = O.quantize_pages(q["x"]["k"], q["x"]["v"], n_hi, batch_lens=[q["prompt"]], rank_mode=rank_mode)
                 after = host(cache.seq_lens)
                 others = [i for i in range(n_slots) if i != b]
                 assert np.array_equal(after[others], before[others]), "a prefill touched another slot"
                 compare_records(cache, q["oc"], seq_map={0: b})
                 compare_tails(cache, q["oc"], seq_map={0: b})
+                if rank_mode == "running":
+                    compare_state(cache, q["oc"], seq_map={0: b}, masks=True)
                 slot_req[b] = r
         # one decode step over all slots
         k_new, v_new, qv = zero_kv.clone(), zero_kv.clone(), zero_q.clone()
@@ -96,6 +101,8 @@ def test_serving_with_a_shared_pool():
             if q["done"] == q["gen"]:  # the request ends: check it, free its slot and pages
                 compare_records(cache, q["oc"], seq_map={0: b})
                 compare_tails(cache, q["oc"], seq_map={0: b})
+                if rank_mode == "running":
+                    compare_state(cache, q["oc"], seq_map={0: b})
                 cache.release(b)
                 slot_req[b] = None
                 finished += 1

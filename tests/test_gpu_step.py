@@ -116,15 +116,18 @@ def test_step_boost_widths(n_hi):
     _run(w, [30, 62], 4, 64, n_hi=n_hi)
 
 
-def test_step_graph_replays_match_eager():
+@pytest.mark.parametrize("rank_mode", [0, 1])
+def test_step_graph_replays_match_eager(rank_mode):
     """The fused step captured in a HIP graph replays like eager launches
-    (bitwise), with eager work and synchronizations between replays."""
+    (bitwise), with eager work and synchronizations between replays; in
+    both ranking modes (the running mode's sums alternate between two
+    copies from step to step)."""
     torch = pytest.importorskip("torch")
     w = synth.LLAMA3_8B.with_(n_kv_heads=2, n_q_heads=12)
     steps = 40
     lens = [1000, 700, 31]
     x = synth.batch(w, batch=3, ctx=1000, steps=steps)
-    caches = [new_cache(3, 2, 32, 1000 + steps + 32) for _ in range(2)]
+    caches = [new_cache(3, 2, 32, 1000 + steps + 32, rank_mode=rank_mode) for _ in range(2)]
     msl = 1000 + steps
     k_buf, v_buf, q_buf = dev(x["k_new"][0]), dev(x["v_new"][0]), dev(x["q_new"][0])
     outs = [torch.zeros((3, 12, 128), dtype=torch.float32, device="cuda") for _ in range(2)]
@@ -150,3 +153,5 @@ def test_step_graph_replays_match_eager():
     assert np.array_equal(host(caches[0].pool), host(caches[1].pool))
     assert np.array_equal(host(caches[0].tail_k), host(caches[1].tail_k))
     assert np.array_equal(host(caches[0].tail_v), host(caches[1].tail_v))
+    if rank_mode:
+        assert np.array_equal(host(caches[0].key_stats), host(caches[1].key_stats))
