@@ -29,6 +29,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -63,11 +64,25 @@ DECODE_SOURCES = ("decode.hip", "kitty_internal.h")
 QUANTIZE_SOURCES = ("quantize.hip", "page_quant.h", "kitty_internal.h")
 
 
-def source_hash(files=DECODE_SOURCES):
+def code_text(text):
+    """Source text without comments, blank lines and trailing spaces: what
+    the compiler sees of it (string literals here hold no comment markers)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", l).rstrip() for l in text.splitlines())
+    return "\n".join(l for l in lines if l)
+
+
+def source_hash(files=DECODE_SOURCES, read=None):
+    """Hash of the kernel sources' code (comments ignored), naming the
+    kernel build that committed counter summaries were taken on."""
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "mixed_precision_bit_kitty_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        if read is None:
+            with open(os.path.join(ROOT, "mixed_precision_bit_kitty_amd", "csrc", f)) as fh:
+                text = fh.read()
+        else:
+            text = read(f)
+        h.update(code_text(text).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,9 +1,11 @@
 // Internal declarations of the Kitty HIP library (gfx950 only).
 //
-// Page record of one (page of 32 tokens, KV head), n = n_hi boosted channels
-// (the two uniform 2-bit Key tensors of "Kitty: Accurate and Efficient 2-bit
-// KV Cache Quantization with Dynamic Channel-wise Precision Boost", Abstract,
-// plus 2-bit Values and fp16 metadata):
+// Page record of one (page of 32 tokens, KV head) for the default (hi_bit 4,
+// lo_bit 2) pair, n = boost slots (n_hi rounded up to a multiple of 16;
+// slots n_hi .. n - 1 hold code 0 and index 0) (the two uniform 2-bit Key
+// tensors of "Kitty: Accurate and Efficient 2-bit KV Cache Quantization with
+// Dynamic Channel-wise Precision Boost", Abstract, plus 2-bit Values and fp16
+// metadata):
 //
 //   0          K base plane    1024 B  64 chunks x 16 B, chunk = one lane's MFMA A operand
 //   1024       K boost plane   8n B    one 32-bit word per (lane, 32-slot block)

@@ -16,10 +16,12 @@
 //  * In the running ranking mode the boosted channels come from outside the
 //    page instead (the head's exact running variance; see select_top and
 //    the running-sum helpers below).
-//  * Asymmetric min/max codes (Prefill step 3): 4-bit on boosted channels,
-//    2-bit elsewhere, fp16 step, round-half-even, clamp; split into the base
-//    plane (top 2 bits) and the boost plane (low 2 bits of boosted channels).
-//  * Values: per token, groups of 32 channels, 2-bit.  Each (token, group)
+//  * Asymmetric min/max codes (Prefill step 3): hi_bit on boosted channels,
+//    lo_bit elsewhere, fp16 step, round-half-even, clamp; split into the base
+//    plane (top lo_bit bits) and the boost plane (low lo_bit bits of boosted
+//    channels).  BITS = lo_bit: 2 (hi_bit 4) or 4 (hi_bit 8, the last row of
+//    the table "Tuning avg_bits").
+//  * Values: per token, groups of 32 channels, lo_bit.  Each (token, group)
 //    step is formed once, by the lane that loads that group's 64 bytes
 //    (packed fp16 min/max); the steps go through LDS to the lanes that code
 //    channels c and c + 16 of every token and pack the value words.

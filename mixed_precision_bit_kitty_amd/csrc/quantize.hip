@@ -4,7 +4,9 @@
 // ("Kitty: Accurate and Efficient 2-bit KV Cache Quantization with Dynamic
 // Channel-wise Precision Boost", Abstract; "Kitty -- Dynamic Channel-wise
 // Mixed-Precision Keys", How it works / Prefill phase, steps 1-3), two-plane
-// Key codes and 2-bit Value codes.
+// Key codes and lo_bit Value codes.  In the running ranking mode the
+// boosted channels come from the head's exact running sums instead
+// (key_chunk_kernel, key_rank_kernel and the append below).
 #include "kitty_internal.h"
 #include "page_quant.h"
 

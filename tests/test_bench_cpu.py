@@ -1,0 +1,34 @@
+"""bench.py's host logic (CPU only): the kernel code hash that ties the
+committed counter summaries to a kernel build, and the refusal of more
+than one GPU."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_code_hash_ignores_comments_only():
+    src = {"a.hip": "int f(int x) {  // doubles\n  return 2 * x; /* done */\n}\n",
+           "b.h": "#pragma once\n"}
+    h0 = bench.source_hash(("a.hip", "b.h"), read=src.get)
+    src2 = dict(src)
+    src2["a.hip"] = "// header comment\n\nint f(int x) {\n  return 2 * x;   \n}\n/* a\nblock */\n"
+    assert bench.source_hash(("a.hip", "b.h"), read=src2.get) == h0
+    src3 = dict(src)
+    src3["a.hip"] = src["a.hip"].replace("2 * x", "3 * x")
+    assert bench.source_hash(("a.hip", "b.h"), read=src3.get) != h0
+
+
+def test_committed_traffic_needs_the_same_kernel_code():
+    assert bench.committed_traffic("0" * 16, "llama3_8b", "step") is None
+    assert bench.committed_traffic(bench.source_hash(bench.DECODE_SOURCES), "no_such_workload", "step") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
