@@ -102,16 +102,19 @@ def committed_traffic(kernel_hash, workload, entry, kernel="decode_kernel"):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, seconds, lo_bit=2, rank_mode="page"):
-    """The oracle as it stands, one thread, on a bounded sample of the same
-    workload: decode steps (append + attention) on a subset of sequences."""
+def _oracle_decode_rate(w, seconds, lo_bit, rank_mode, threads):
+    """Decode steps (append + attention) of the oracle on 2 sequences of the
+    workload for about `seconds`, with the BLAS pool limited to `threads`
+    (None: its default).  Returns (steps, sequences, bytes read, seconds,
+    threads used)."""
     import oracle as O
     from mixed_precision_bit_kitty_amd import synth
     try:
-        from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(1)
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limiter = threadpool_limits(threads)
+        used = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except ImportError:  # pragma: no cover
-        limiter = None
+        limiter, used = None, threads or 1
     n_seq = 2
     x = synth.batch(w, batch=n_seq, steps=64)
     oc = O.quantize_pages(x["k"], x["v"], w.n_hi, lo_bit=lo_bit, rank_mode=rank_mode)
@@ -130,10 +133,24 @@ def cpu_baseline(w, seconds, lo_bit=2, rank_mode="page"):
             break
     if limiter is not None:
         limiter.unregister()
+    return steps, n_seq, read, el, used
+
+
+def cpu_baseline(w, seconds, lo_bit=2, rank_mode="page"):
+    """The oracle as it stands on a bounded sample of the same workload:
+    decode steps (append + attention) on 2 of the sequences, single-threaded
+    (the reported value) and with the BLAS pool at its default size (all
+    host threads; context)."""
+    steps, n_seq, read, el, _ = _oracle_decode_rate(w, seconds, lo_bit, rank_mode, 1)
+    s2, _, r2, e2, used = _oracle_decode_rate(w, seconds, lo_bit, rank_mode, None)
     return {"value": round(read / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "tokens_per_s": round(steps * n_seq / el, 3),
             "sample": f"{steps} decode steps (append + attention) of {n_seq} of the {w.batch} sequences, "
-                      f"ctx {w.ctx}, numpy oracle single-threaded, {el:.1f} s"}
+                      f"ctx {w.ctx}, numpy oracle single-threaded, {el:.1f} s",
+            "all_threads": {"value": round(r2 / e2 / 1e9, 4), "unit": "GB/s", "cores": used,
+                            "tokens_per_s": round(s2 * n_seq / e2, 3),
+                            "sample": f"{s2} decode steps, BLAS pool of {used} threads "
+                                      f"(os.cpu_count() = {os.cpu_count()}), {e2:.1f} s"}}
 
 
 def bench_quantize(args, w):
