@@ -60,7 +60,7 @@ def kv_bytes(seq_lens, n_kv_heads, record_bytes):
     return tot
 
 
-DECODE_SOURCES = ("decode.hip", "kitty_internal.h")
+DECODE_SOURCES = ("decode.hip", "page_quant.h", "kitty_internal.h")  # the fused step seals with page_quant.h
 QUANTIZE_SOURCES = ("quantize.hip", "page_quant.h", "kitty_internal.h")
 
 

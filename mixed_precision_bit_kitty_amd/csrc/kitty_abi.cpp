@@ -104,7 +104,6 @@ int kitty_quantize_pages(const kitty_config_t* cfg, const kitty_kv_view_t* kv, c
   if (S < 0) return fail(KITTY_ERR_INVALID_ARG, "S must be >= 0");
   if (S / kitty::kPageTokens > kv->max_pages)
     return fail(KITTY_ERR_INVALID_ARG, "S / 32 = %d exceeds max_pages %d", S / kitty::kPageTokens, kv->max_pages);
-  if (S / kitty::kPageTokens + 1 > 2147483647 / 1) return fail(KITTY_ERR_INVALID_ARG, "S too large");
   if (lens && !aligned(lens, 4)) return fail(KITTY_ERR_INVALID_ARG, "lens misaligned");
   if (cfg->rank_mode == KITTY_RANK_RUNNING && S > kitty::kMaxRunningTokens)
     return fail(KITTY_ERR_UNSUPPORTED, "S %d exceeds %d tokens in the running ranking mode", S, kitty::kMaxRunningTokens);
