@@ -20,8 +20,9 @@
 //    run on MFMA (constant A operands), so no VALU reduction is needed.
 //
 // One wave = one (sequence, KV head, group of <= 4 query heads, range of
-// pages); one more wave per (sequence, KV head, head group) attends over the
-// fp16 tail page, off the critical path of the page waves.  Lane l: column n = l & 15, row group w = l >> 4.  QK^T is computed
+// pages); the last wave of each (sequence, KV head, head group) also attends
+// over the fp16 tail page (first, while its first pages load) and takes a
+// smaller page range.  Lane l: column n = l & 15, row group w = l >> 4.  QK^T is computed
 // transposed (rows = 16 tokens, columns = head x limb, columns 8..15 repeat
 // 0..7), so after one DPP add every lane holds the logits of tokens
 // tau(w, 0..7) of head n & 3 -- exactly the K slice it feeds to PV.
@@ -333,6 +334,15 @@ __device__ __forceinline__ half2v fma2(half2v a, half2v b, half2v c) { return __
 // alone at the end.  Shares 9 : 7 : 5 measured about 5% faster than equal
 // shares on the batch-16, 4096-token decode.
 __host__ __device__ __forceinline__ int page_weight(int i) { return i < 4 ? 9 : (i < 8 ? 7 : 5); }
+// Share of the tail wave (the last wave of a unit, wave W - 1 of its last
+// workgroup): it streams pages too, after its fp16 tail.
+#ifndef KITTY_TAIL_DROP
+#define KITTY_TAIL_DROP 2
+#endif
+__host__ __device__ __forceinline__ int tail_weight(int W) {
+  const int t = page_weight(W - 1) - KITTY_TAIL_DROP;
+  return t > 0 ? t : 0;
+}
 // sum of page_weight(j) for j < i (i <= W <= 12)
 __host__ __device__ __forceinline__ int weight_prefix(int i, int W) {
   const int r = min(i, W);
@@ -365,7 +375,7 @@ void decode_kernel(DecodeParams p) {
   Lds<NHI, BITS>& sm = all[wave];
 
   const int W = p.wg_waves;
-  const int n_pw = p.n_wg * W - 1;           // page waves of this unit; the last wave takes the tail
+  const int n_pw = p.n_wg * W - 1;           // the last wave of this unit also takes the tail
   const int pw = blockIdx.x * W + wave;
   const bool tail_wave = pw == n_pw;
   const int hk = blockIdx.y / p.n_head_groups, hg = blockIdx.y % p.n_head_groups;
@@ -380,10 +390,11 @@ void decode_kernel(DecodeParams p) {
   // waves in proportion to page_weight (the older waves of a SIMD get more).
   const int Pm = min(p.max_seq_len / kPageTokens, p.max_pages);
   // (32-bit products: c0 + 9 <= 16 x 84 + 9 and Pm <= 4096)
-  const int wsum = p.n_wg * weight_prefix(W, W) - page_weight(W - 1);
+  const int tw = tail_weight(W);
+  const int wsum = p.n_wg * weight_prefix(W, W) - page_weight(W - 1) + tw;
   const int c0 = (int)blockIdx.x * weight_prefix(W, W) + weight_prefix(wave, W);
-  const int p0 = tail_wave ? 0 : (c0 * Pm) / wsum;
-  const int p1m = tail_wave ? 0 : ((c0 + page_weight(wave)) * Pm) / wsum;
+  const int p0 = (c0 * Pm) / wsum;  // the tail wave's range ends at Pm
+  const int p1m = ((c0 + (tail_wave ? tw : page_weight(wave))) * Pm) / wsum;
   // Independent loads first (one memory round trip before the first DMA):
   // the sequence length, this wave's page ids (lane j: page p0 + j), queries.
   const size_t page_row = (size_t)b * p.max_pages;
@@ -469,6 +480,10 @@ void decode_kernel(DecodeParams p) {
     if (phys < 0 || phys >= np32) phys = 0;  // invalid ids read page 0 and are masked
     return head_base + (uint64_t)(uint32_t)phys * pb32;
   };
+  if (seal_rec != nullptr) {  // the ring overlaps the quantizer's LDS scratch: its accesses are done first
+    wait_lgkm0();
+    compiler_fence();
+  }
 #pragma unroll
   for (int d = 0; d < kRing; ++d)
     if (d < npg) dma_record<NHI, BITS>(rec_of(phys_of(d)), sm.ring[d], lane);
@@ -641,6 +656,63 @@ void decode_kernel(DecodeParams p) {
     pv(S);
   };
 
+  // With a seal attended, the tail is empty; a seal beyond a smaller
+  // max_seq_len leaves the older tail tokens to attend.
+  if (tail_wave && ntail > 0 && !new_page) {
+    // fp16 tail tokens: the same contraction with fp16 K / V values.  The
+    // appended token (slot ntail - 1 when this call appends it) comes from
+    // k_new / v_new.  Every load is issued before the first use (one
+    // memory round trip).  All 32 slots lie inside the tail buffer; tokens
+    // >= ntail are zeroed after loading, so stale slot contents never reach
+    // the MFMAs.
+    const _Float16* tk = p.tail_k + toff;
+    const _Float16* tv = p.tail_v + toff;
+    const int newslot = (fused && seq == total) ? ntail - 1 : -1;
+    half8 ka[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const int t = 16 * tb + n;
+        const _Float16* row = t == newslot ? p.k_new + noff : tk + (size_t)t * kHeadDim;
+        ka[kb][tb] = *reinterpret_cast<const half8*>(row + 32 * kb + 8 * w);
+      }
+    _Float16 va[8][8];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int t = 4 * w + (j >> 1) + 16 * (j & 1);  // tau(w, j)
+        const _Float16* row = t == newslot ? p.v_new + noff : tv + (size_t)t * kHeadDim;
+        va[mb][j] = row[16 * mb + n];
+      }
+    floatx4 acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const half8 z = {};
+        acc[tb] = mfma(bq_plain[kb], 16 * tb + n < ntail ? ka[kb][tb] : z, acc[tb]);
+      }
+    float s0 = n < ntail ? acc[0][0] : -INFINITY;
+    float s1 = 16 + n < ntail ? acc[1][0] : -INFINITY;
+    softmax_step(st, s0, s1, sl2, n);
+    store_p_limbs(sm.pl, w, n, p_limbs(s0, s1));
+    wave_lds_sync();
+    const half8 z = {};
+    const half8 bp = n < 8 ? *reinterpret_cast<const half8*>(&sm.pl[limb][h][8 * w]) : z;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      half8 a;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int t = 4 * w + (j >> 1) + 16 * (j & 1);
+        a[j] = t < ntail ? va[mb][j] : (_Float16)0.0f;
+      }
+      st.o[mb] = mfma(a, bp, st.o[mb]);
+    }
+  }
+
   // The loop runs two pages per trip so that each ring slot, and with it
   // every LDS address of the page, is a compile-time offset.
   auto page_step = [&](int i, auto slot_c) KITTY_INLINE {
@@ -670,62 +742,6 @@ void decode_kernel(DecodeParams p) {
       wait_page<NHI, BITS>(0);
       attend_page(sm.ring[0], true);
       wave_lds_sync();
-    }
-    // With a seal attended, the tail is empty; a seal beyond a smaller
-    // max_seq_len leaves the older tail tokens to attend.
-    if (ntail > 0 && !new_page) {
-      // fp16 tail tokens: the same contraction with fp16 K / V values.  The
-      // appended token (slot ntail - 1 when this call appends it) comes from
-      // k_new / v_new.  Every load is issued before the first use (one
-      // memory round trip).  All 32 slots lie inside the tail buffer; tokens
-      // >= ntail are zeroed after loading, so stale slot contents never reach
-      // the MFMAs.
-      const _Float16* tk = p.tail_k + toff;
-      const _Float16* tv = p.tail_v + toff;
-      const int newslot = (fused && seq == total) ? ntail - 1 : -1;
-      half8 ka[4][2];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          const int t = 16 * tb + n;
-          const _Float16* row = t == newslot ? p.k_new + noff : tk + (size_t)t * kHeadDim;
-          ka[kb][tb] = *reinterpret_cast<const half8*>(row + 32 * kb + 8 * w);
-        }
-      _Float16 va[8][8];
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int t = 4 * w + (j >> 1) + 16 * (j & 1);  // tau(w, j)
-          const _Float16* row = t == newslot ? p.v_new + noff : tv + (size_t)t * kHeadDim;
-          va[mb][j] = row[16 * mb + n];
-        }
-      floatx4 acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          const half8 z = {};
-          acc[tb] = mfma(bq_plain[kb], 16 * tb + n < ntail ? ka[kb][tb] : z, acc[tb]);
-        }
-      float s0 = n < ntail ? acc[0][0] : -INFINITY;
-      float s1 = 16 + n < ntail ? acc[1][0] : -INFINITY;
-      softmax_step(st, s0, s1, sl2, n);
-      store_p_limbs(sm.pl, w, n, p_limbs(s0, s1));
-      wave_lds_sync();
-      const half8 z = {};
-      const half8 bp = n < 8 ? *reinterpret_cast<const half8*>(&sm.pl[limb][h][8 * w]) : z;
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
-        half8 a;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int t = 4 * w + (j >> 1) + 16 * (j & 1);
-          a[j] = t < ntail ? va[mb][j] : (_Float16)0.0f;
-        }
-        st.o[mb] = mfma(a, bp, st.o[mb]);
-      }
     }
   }
 
@@ -913,11 +929,13 @@ int max_wg_waves_t(int lo_bit) {
 // Largest page range any page wave gets under plan (n_wg, W) for Pm pages
 // (the same weighted division the kernel computes).
 static long max_range(long Pm, long n_wg, long W) {
-  const long wsum = n_wg * weight_prefix(W, W) - page_weight(W - 1);
+  const long tw = tail_weight((int)W);
+  const long wsum = n_wg * weight_prefix(W, W) - page_weight(W - 1) + tw;
   long best = 0;
-  for (long pw = 0; pw < n_wg * W - 1; ++pw) {
+  for (long pw = 0; pw < n_wg * W; ++pw) {
     const long c0 = (pw / W) * weight_prefix(W, W) + weight_prefix(pw % W, W);
-    const long r = ((c0 + page_weight(pw % W)) * Pm) / wsum - (c0 * Pm) / wsum;
+    const long wt = pw == n_wg * W - 1 ? tw : page_weight(pw % W);
+    const long r = ((c0 + wt) * Pm) / wsum - (c0 * Pm) / wsum;
     if (r > best) best = r;
   }
   return best;

@@ -245,6 +245,9 @@ def test_decode_plan_fits_page_id_register():
         r = min(i, W)
         return 9 * min(r, 4) + 7 * min(max(r - 4, 0), 4) + 5 * max(r - 8, 0)
 
+    def tail(W):  # the last wave of a unit also attends the fp16 tail: a smaller share
+        return max(weight(W - 1) - 2, 0)
+
     for batch, wmax in ((1, 12), (3, 9), (16, 12), (16, 11), (16, 9), (128, 10), (1024, 12)):
         for hkv, hg in ((1, 1), (8, 1), (8, 2), (32, 4)):
             for msl in list(range(0, 4096 * 32 + 32, 4999)) + [4096 * 32 + 31, 320 * 32]:
@@ -252,11 +255,15 @@ def test_decode_plan_fits_page_id_register():
                 n_wg, W = r & 0xFFFFFFFF, r >> 32
                 assert 1 <= n_wg <= 16 and 2 <= W <= wmax
                 P = msl // 32
-                wsum = n_wg * prefix(W, W) - weight(W - 1)
-                for pw in range(n_wg * W - 1):
+                wsum = n_wg * prefix(W, W) - weight(W - 1) + tail(W)
+                covered = 0
+                for pw in range(n_wg * W):
                     c0 = (pw // W) * prefix(W, W) + prefix(pw % W, W)
-                    size = ((c0 + weight(pw % W)) * P) // wsum - (c0 * P) // wsum
+                    wt = tail(W) if pw == n_wg * W - 1 else weight(pw % W)
+                    size = ((c0 + wt) * P) // wsum - (c0 * P) // wsum
                     assert size <= 64, (batch, hkv, hg, msl, n_wg, W, pw, size)
+                    covered += size
+                assert covered == P  # the ranges tile the pages
 
 
 def test_running_mode_arguments():
