@@ -180,8 +180,8 @@ struct alignas(16) Lds {  // 16-byte aligned size: every wave's area keeps 16-by
   union {
     QtLimb qt[2];  // q * kscale limbs [limb].h[head][channel]
     struct {
-      _Float16 pt[4][2][4][32];  // p * vscale limbs [group][limb][head][kappa]
-      _Float16 pl[2][4][32];     // p limbs [limb][head][kappa]
+      _Float16 pt[4][2][4][32];  // p * vscale limbs [group][limb][head][p_swz(kappa)]
+      _Float16 pl[2][4][32];     // p limbs [limb][head][p_swz(kappa)]
     };
   };
   float red[2][4][4];           // final corrections [kind][head][group]
@@ -311,11 +311,16 @@ __device__ __forceinline__ PLimbs p_limbs(float p0, float p1) {
   const half2v lo = {(_Float16)__builtin_fmaf((float)hi[0], -1.0f, p0), (_Float16)__builtin_fmaf((float)hi[1], -1.0f, p1)};
   return PLimbs{hi, lo};
 }
+// Position of kappa in row r = 4 limb + head of a p-limb table: the 16-byte
+// chunk kappa / 8 is XOR-swizzled with (r / 2) mod 4, so the eight rows that
+// one PV operand read touches (same chunk) fall in eight distinct 4-bank
+// groups instead of two; the half2 writes stay conflict-free.
+__device__ __forceinline__ int p_swz(int r, int kappa) { return (((kappa >> 3) ^ ((r >> 1) & 3)) << 3) | (kappa & 7); }
 // Write the p limbs of tokens (n, n + 16) of head w at kappa (2n, 2n + 1):
-// dst[limb][w][kappa].
+// dst[limb][w][p_swz(4 limb + w, kappa)].
 __device__ __forceinline__ void store_p_limbs(_Float16 (*dst)[4][32], int w, int n, PLimbs pl) {
-  *reinterpret_cast<half2v*>(&dst[0][w][2 * n]) = pl.hi;
-  *reinterpret_cast<half2v*>(&dst[1][w][2 * n]) = pl.lo;
+  *reinterpret_cast<half2v*>(&dst[0][w][p_swz(w, 2 * n)]) = pl.hi;
+  *reinterpret_cast<half2v*>(&dst[1][w][p_swz(4 + w, 2 * n)]) = pl.lo;
 }
 // Two fp16 limbs of a * b for fp16 a, b (exact product: 22 significant
 // bits): hi = f16(a b) by a correctly rounded fp16 multiply and lo = the
@@ -507,7 +512,8 @@ void decode_kernel(DecodeParams p) {
   const float sl2 = (1.0f / sqrtf((float)kHeadDim)) * kLog2e;
   // PV B operand source: lanes n < 8 read the group's p * vscale limbs, lanes
   // n >= 8 the p limbs (same address for every group)
-  const _Float16* b_src = n < 8 ? &sm.pt[0][limb][h][8 * w] : &sm.pl[limb][h][8 * w];
+  const int pk = p_swz(4 * limb + h, 8 * w);  // this lane's operand chunk in its row
+  const _Float16* b_src = n < 8 ? &sm.pt[0][limb][h][pk] : &sm.pl[limb][h][pk];
   const int b_stride = n < 8 ? 2 * 4 * 32 : 0;
 
   WaveState st;
@@ -615,8 +621,8 @@ void decode_kernel(DecodeParams p) {
       const half2v vs = *reinterpret_cast<const half2v*>(S + off_vscale(NHI, BITS) + 2 * (32 * g + 2 * n));
       const half2v hi = mul_hi(pl.hi, vs);
       const half2v lo = fma2(pl.lo, vs, fma2(pl.hi, vs, -hi));
-      *reinterpret_cast<half2v*>(&sm.pt[g][0][w][2 * n]) = hi;
-      *reinterpret_cast<half2v*>(&sm.pt[g][1][w][2 * n]) = lo;
+      *reinterpret_cast<half2v*>(&sm.pt[g][0][w][p_swz(w, 2 * n)]) = hi;
+      *reinterpret_cast<half2v*>(&sm.pt[g][1][w][p_swz(4 + w, 2 * n)]) = lo;
     }
     store_p_limbs(sm.pl, w, n, pl);
   };
@@ -700,7 +706,7 @@ void decode_kernel(DecodeParams p) {
     store_p_limbs(sm.pl, w, n, p_limbs(s0, s1));
     wave_lds_sync();
     const half8 z = {};
-    const half8 bp = n < 8 ? *reinterpret_cast<const half8*>(&sm.pl[limb][h][8 * w]) : z;
+    const half8 bp = n < 8 ? *reinterpret_cast<const half8*>(&sm.pl[limb][h][pk]) : z;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
       half8 a;
