@@ -962,6 +962,45 @@ int decode_max_wg_waves(int n_hi, int lo_bit) {
   }
 }
 
+// Workgroups of this kernel that one CU holds at once.  Registers allow 3
+// waves per SIMD, and the waves of a workgroup go to the CU's 4 SIMDs in
+// turn: workgroups of up to 4 waves pack until every SIMD holds 3 (12 / W of
+// them), but a second workgroup of 5 to 11 waves finds one of its SIMDs full
+// and waits for another CU (measured with a residency probe: 6, 4 and 3
+// workgroups of 2, 3 and 4 waves share a CU, workgroups of 5, 6, 8 or 12
+// waves run alone).  LDS may allow fewer.
+static long wgs_per_cu(long W, int wmax) {
+  const long by_simd = W <= 4 ? 12 / W : 1;
+  const long by_lds = wmax / W;  // wmax waves' LDS fit one CU
+  return by_lds < 1 ? 1 : (by_simd < by_lds ? by_simd : by_lds);
+}
+
+// A single-workgroup plan that needs more workgroups than there are CUs, with
+// a workgroup size that runs alone on a CU, leaves SIMD slots idle: take
+// instead the size among 2, 3, 4 and wmax waves that needs the fewest rounds
+// of resident workgroups times (pages per wave + 2), the 2 standing for a
+// round's start and merge.  Only the workgroup size changes, so the workspace
+// (sized by n_wg) does not.
+static SplitPlan pack_workgroups(SplitPlan plan, long P, long units, int wmax) {
+  constexpr long kCus = 256;
+  if (plan.n_wg != 1 || plan.wg_waves <= 4 || plan.wg_waves >= wmax || units <= kCus) return plan;
+  auto cost = [&](long W) {
+    const long per_round = kCus * wgs_per_cu(W, wmax);
+    return (units + per_round - 1) / per_round * (max_range(P, 1, W) + 2);
+  };
+  long best = plan.wg_waves, best_cost = cost(best);
+  for (long W : {2L, 3L, 4L, (long)wmax}) {
+    if (W > wmax || max_range(P, 1, W) > 64) continue;
+    const long c = cost(W);
+    if (c < best_cost) {
+      best = W;
+      best_cost = c;
+    }
+  }
+  plan.wg_waves = (int)best;
+  return plan;
+}
+
 SplitPlan plan_splits(int batch, int n_kv_heads, int n_head_groups, int max_seq_len, int wmax) {
   const long P = max_seq_len / kPageTokens;
   const long units = (long)batch * n_kv_heads * n_head_groups;
@@ -980,7 +1019,7 @@ SplitPlan plan_splits(int batch, int n_kv_heads, int n_head_groups, int max_seq_
     // grows, and for every supported length (P <= 4096) it stops well
     // before 16 x 12 waves
     if (max_range(P, n_wg, wg_waves) <= 64 || n_wg * wg_waves >= (long)kMaxWg * wmax)
-      return SplitPlan{(int)n_wg, (int)wg_waves};
+      return pack_workgroups(SplitPlan{(int)n_wg, (int)wg_waves}, P, units, wmax);
     ++wpu;
   }
 }

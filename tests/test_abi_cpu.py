@@ -266,6 +266,10 @@ def test_decode_plan_fits_page_id_register():
                     assert size <= 64, (batch, hkv, hg, msl, n_wg, W, pw, size)
                     covered += size
                 assert covered == P  # the ranges tile the pages
+                if n_wg == 1 and batch * hkv * hg > 256 and P >= 64:
+                    # more workgroups than CUs: only sizes that share a CU (<= 4
+                    # waves) or that fill one (wmax waves)
+                    assert W <= 4 or W == wmax, (batch, hkv, hg, msl, W)
 
 
 def test_running_mode_arguments():
