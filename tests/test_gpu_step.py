@@ -89,6 +89,24 @@ def test_step_several_workgroups():
     print(f"fused step, several workgroups: max abs err {worst:.3g}")
 
 
+def test_step_packed_workgroups():
+    # 40 sequences x 8 KV heads = 320 units, more than the 256 CUs hold at
+    # one workgroup each: the plan packs 4-wave workgroups, three per CU
+    import ctypes
+    from mixed_precision_bit_kitty_amd import binding as B
+    so = ctypes.CDLL(B.LIB_PATH)
+    plan, wmax = so._ZN5kitty11plan_splitsEiiiii, so._ZN5kitty19decode_max_wg_wavesEii
+    plan.restype, plan.argtypes = ctypes.c_uint64, [ctypes.c_int32] * 5
+    wmax.restype, wmax.argtypes = ctypes.c_int, [ctypes.c_int32] * 2
+    rng = np.random.default_rng(41)
+    lens = [int(n) for n in rng.integers(250, 300, 40)]
+    steps = 34
+    r = plan(40, 8, 1, max(lens) + steps, wmax(32, 2))
+    assert (r & 0xFFFFFFFF, r >> 32) == (1, 4)
+    worst = _run(synth.LLAMA3_8B, lens, steps, 300, check_every=8)
+    print(f"fused step, packed 4-wave workgroups: max abs err {worst:.3g}")
+
+
 def test_step_capacity_bound():
     # the default bound (cache capacity) plans another split than the tight one
     w = synth.LLAMA3_8B.with_(n_kv_heads=2, n_q_heads=8)
