@@ -31,6 +31,7 @@ KITTY_KEY_STATS_BYTES = 8192
 
 HEAD_DIM = 128
 PAGE_TOKENS = 32
+MAX_SEQ_LEN = 4096 * 32 + 31  # the largest max_seq_len decode accepts (4096 pages and a tail)
 
 
 class KittyError(RuntimeError):
@@ -306,6 +307,11 @@ class KittyCache:
         _need(v_new, torch.float16, (self.batch, self.n_kv_heads, HEAD_DIM), "v_new")
         kitty_append_token(self.cfg, self.view, k_new, v_new, stream)
 
+    def default_max_seq_len(self):
+        """The bound decode calls use by default: the block table's capacity
+        (a full tail page past its pages), at most MAX_SEQ_LEN."""
+        return min(self.max_pages * PAGE_TOKENS + PAGE_TOKENS - 1, MAX_SEQ_LEN)
+
     def workspace(self, n_q_heads, max_seq_len):
         import torch
         nb = kitty_decode_workspace_bytes(self.cfg, self.batch, n_q_heads, max_seq_len)
@@ -317,7 +323,7 @@ class KittyCache:
         import torch
         B, Hq, D = q.shape
         _need(q, torch.float16, (self.batch, Hq, HEAD_DIM), "q")
-        msl = self.max_pages * PAGE_TOKENS + PAGE_TOKENS - 1 if max_seq_len is None else max_seq_len
+        msl = self.default_max_seq_len() if max_seq_len is None else max_seq_len
         if out is None:
             out = torch.empty((self.batch, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
         _need(out, torch.float32, (self.batch, Hq, HEAD_DIM), "out")
@@ -332,7 +338,7 @@ class KittyCache:
         _need(k_new, torch.float16, (self.batch, self.n_kv_heads, HEAD_DIM), "k_new")
         _need(v_new, torch.float16, (self.batch, self.n_kv_heads, HEAD_DIM), "v_new")
         _need(q, torch.float16, (self.batch, Hq, HEAD_DIM), "q")
-        msl = self.max_pages * PAGE_TOKENS + PAGE_TOKENS - 1 if max_seq_len is None else max_seq_len
+        msl = self.default_max_seq_len() if max_seq_len is None else max_seq_len
         if out is None:
             out = torch.empty((self.batch, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
         _need(out, torch.float32, (self.batch, Hq, HEAD_DIM), "out")

@@ -73,6 +73,14 @@ def test_workspace_bytes_cover_partials():
     assert nb3 == 12800 + 256 + 512
 
 
+def test_binding_default_bound_within_the_limit():
+    # the binding's default decode bound never exceeds the library's limit
+    cfg = B.config(8, 32)
+    assert B.kitty_decode_workspace_bytes(cfg, 1, 8, B.MAX_SEQ_LEN) > 0
+    with pytest.raises(B.KittyError):
+        B.kitty_decode_workspace_bytes(cfg, 1, 8, B.MAX_SEQ_LEN + 1)
+
+
 def test_decode_waves_per_workgroup():
     """Waves per decode workgroup that the per-wave LDS (a ring of two
     records) allows on one CU: twelve for 2-bit records, fewer for the

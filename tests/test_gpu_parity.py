@@ -166,3 +166,28 @@ def test_multi_workgroup_merge(batch, hkv, hq, ctx, lens):
     # the same cache under a loose bound (another workgroup plan) agrees too
     err2, _ = compare_decode(cache, oc, x["q"], max_seq_len=4 * ctx)
     print(f"multi-workgroup {batch}x{hkv}x{hq} ctx {ctx}: max abs err {err:.3g} / {err2:.3g}")
+
+
+def test_maximum_length():
+    # the longest supported sequence: 4096 sealed pages and a 31-token tail
+    # (131,103 tokens), prefilled one token short and completed by a fused
+    # step; records bit-exact, attention under the tight and the capacity
+    # bound within 2e-3
+    n = 4096 * 32 + 31
+    w = synth.LLAMA3_8B.with_(n_kv_heads=1, n_q_heads=4)
+    x = synth.batch(w, batch=1, ctx=n, steps=0)
+    cache = new_cache(1, 1, 32, 4096 * 32)
+    assert cache.max_pages == 4096 and cache.default_max_seq_len() == n
+    cache.quantize_pages(dev(x["k"][:, :, :n - 1]), dev(x["v"][:, :, :n - 1]))
+    out = host(cache.decode_step(dev(np.ascontiguousarray(x["k"][:, :, n - 1])),
+                                 dev(np.ascontiguousarray(x["v"][:, :, n - 1])), dev(x["q"]), max_seq_len=n))
+    oc = O.quantize_pages(x["k"], x["v"], 32)
+    assert int(host(cache.seq_lens)[0]) == n
+    compare_records(cache, oc)
+    compare_tails(cache, oc)
+    ref = O.decode_attention(oc, x["q"])
+    err = float(np.abs(out - ref).max())
+    assert err <= ATOL, err
+    err2, _ = compare_decode(cache, oc, x["q"], max_seq_len=n)
+    err3, _ = compare_decode(cache, oc, x["q"])
+    print(f"maximum length {n}: fused step {err:.3g}, decode {err2:.3g} / {err3:.3g}")
