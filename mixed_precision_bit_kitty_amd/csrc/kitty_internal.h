@@ -133,7 +133,7 @@ struct DecodeParams {
   int32_t n_head_groups;   // ceil(G / 4)
   int32_t max_seq_len;
   int32_t n_wg;            // workgroups per (sequence, KV head, head group)
-  int32_t wg_waves;        // waves per workgroup; the unit's last wave attends over the tail
+  int32_t wg_waves;        // waves per workgroup; the unit's last wave also attends over the tail
   float* partial;          // [batch][Hq][n_wg][kPartialStride] per-workgroup partials
   int* counters;           // [batch][Hkv][n_head_groups] workgroup arrival counters, zero between calls
   int* seq_counters;       // [batch] finished units per sequence (fused step), zero between calls
@@ -146,8 +146,8 @@ constexpr int kPartialStride = 132;  // m, l, O[128], 2 pad floats
 constexpr int kMaxWgWaves = 12;      // waves per decode workgroup
 constexpr int kMaxWg = 16;           // decode workgroups per (sequence, KV head, head group)
 // Longest sequence decode attention accepts: 4096 pages of 32 tokens (+ a
-// partial tail page); a page wave keeps its page ids in one 64-lane register,
-// and 16 x 12 - 1 waves x 64 pages cover it.
+// partial tail page); a wave keeps its page ids in one 64-lane register, and
+// 16 workgroups x 9 to 12 waves x 64 pages cover it.
 constexpr int kMaxSeqLen = 4096 * 32 + 31;
 constexpr int kSeqCounterStride = 32;  // ints: one 128-byte line per sequence counter
 
