@@ -8,6 +8,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -54,11 +55,12 @@ def build(verbose: bool = False) -> str:
     """Compile every HIP source and link libkitty.so; returns its path."""
     os.makedirs(OBJ, exist_ok=True)
     cc = hipcc()
-    objs = []
-    for src, extra in SOURCES.items():
-        obj = os.path.join(OBJ, src + ".o")
-        _run([cc, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
-        objs.append(obj)
+    objs = [os.path.join(OBJ, src + ".o") for src in SOURCES]
+    cmds = [[cc, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+            for (src, extra), obj in zip(SOURCES.items(), objs)]
+    with ThreadPoolExecutor(len(cmds)) as pool:  # the sources compile independently
+        for f in [pool.submit(_run, cmd, verbose) for cmd in cmds]:
+            f.result()
     tmp = LIB + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
