@@ -546,20 +546,27 @@ void decode_kernel(DecodeParams p) {
   };
   // QK^T of the page in S (its q * kscale limbs in LDS): rows = (head, limb),
   // columns = tokens; the logits of head w at tokens n and n + 16
-  auto qk = [&](const uint8_t* S, bool valid, float& s0, float& s1) KITTY_INLINE {
+  // the boosted channels' indices of the page in S (4 per word), read before
+  // the limb exchange so that the gathers can follow its barrier at once
+  struct BoostIdx {
+    u32x2 ib[NB > 0 ? NB : 1];
+  };
+  auto boost_idx = [&](const uint8_t* S) KITTY_INLINE {
+    BoostIdx r;
+#pragma unroll
+    for (int k2 = 0; k2 < NB; ++k2) {
+      const int q0 = 32 * k2 + 8 * w;
+      r.ib[k2] = q0 < NHI ? *reinterpret_cast<const u32x2*>(S + off_idx(NHI, BITS) + q0) : u32x2{};
+    }
+    return r;
+  };
+  auto qk = [&](const uint8_t* S, const BoostIdx& bi, bool valid, float& s0, float& s1) KITTY_INLINE {
     // this lane's K base chunk: four words (2-bit) or eight (4-bit: combos A, B of word x at 2x, 2x + 1)
     const u32x4 kw = *reinterpret_cast<const u32x4*>(S + 16 * BITS / 2 * lane);
     const u32x4 kw2 = BITS == 4 ? *reinterpret_cast<const u32x4*>(S + 32 * lane + 16) : u32x4{};
     half8 bq[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) bq[kb] = *reinterpret_cast<const half8*>(&sm.qt[al].h[ah][32 * kb + 8 * w]);
-    floatx4 cmin = {0.0f, 0.0f, 0.0f, 0.0f}, coff = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const half8 kmin = *reinterpret_cast<const half8*>(S + off_kmin(NHI, BITS) + 2 * (32 * kb + 8 * w));
-      cmin = mfma(bq_plain[kb], kmin, cmin);
-      coff = mfma(bq[kb], b_off, coff);
-    }
     half8 bb[NB > 0 ? NB : 1];
     u32x2 bw[NB > 0 ? NB : 1];  // 2-bit: one word (both combos); 4-bit: the combo A, B pair
 #pragma unroll
@@ -567,7 +574,7 @@ void decode_kernel(DecodeParams p) {
       const int q0 = 32 * k2 + 8 * w;
       half8 v = {};
       if (q0 < NHI) {
-        const u32x2 ib = *reinterpret_cast<const u32x2*>(S + off_idx(NHI, BITS) + q0);
+        const u32x2 ib = bi.ib[k2];
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = sm.qt[al].h[ah][opaque(__builtin_amdgcn_ubfe(ib[j >> 2], 8 * (j & 3), 7))];
       }
@@ -579,8 +586,19 @@ void decode_kernel(DecodeParams p) {
         if (k2 < NF) bw[k2] = *reinterpret_cast<const u32x2*>(S + off_kboost(4) + 8 * (lane * NF + k2));
         else bw[k2] = lane < 32 ? *reinterpret_cast<const u32x2*>(S + off_kboost(4) + 512 * NF + 8 * lane) : u32x2{};
       }
-      coff = mfma(v, b_offb, coff);
     }
+    // the gathers (a second LDS round trip after the index read) issue with
+    // the limb reads, ahead of the MFMAs that do not need them
+    __builtin_amdgcn_sched_barrier(0);
+    floatx4 cmin = {0.0f, 0.0f, 0.0f, 0.0f}, coff = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const half8 kmin = *reinterpret_cast<const half8*>(S + off_kmin(NHI, BITS) + 2 * (32 * kb + 8 * w));
+      cmin = mfma(bq_plain[kb], kmin, cmin);
+      coff = mfma(bq[kb], b_off, coff);
+    }
+#pragma unroll
+    for (int k2 = 0; k2 < NB; ++k2) coff = mfma(bb[k2], b_offb, coff);
     floatx4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -616,9 +634,14 @@ void decode_kernel(DecodeParams p) {
   // p * vscale to about 2^-21 relative.
   auto produce_pt = [&](const uint8_t* S, float s0, float s1) KITTY_INLINE {
     const PLimbs pl = p_limbs(s0, s1);
+    // all four reads before the first write: the compiler cannot tell the
+    // limb writes from the record, and would otherwise wait for each read
+    half2v vsg[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) vsg[g] = *reinterpret_cast<const half2v*>(S + off_vscale(NHI, BITS) + 2 * (32 * g + 2 * n));
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const half2v vs = *reinterpret_cast<const half2v*>(S + off_vscale(NHI, BITS) + 2 * (32 * g + 2 * n));
+      const half2v vs = vsg[g];
       const half2v hi = mul_hi(pl.hi, vs);
       const half2v lo = fma2(pl.lo, vs, fma2(pl.hi, vs, -hi));
       *reinterpret_cast<half2v*>(&sm.pt[g][0][w][p_swz(w, 2 * n)]) = hi;
@@ -652,10 +675,11 @@ void decode_kernel(DecodeParams p) {
   };
   // one page through the whole contraction
   auto attend_page = [&](const uint8_t* S, bool valid) KITTY_INLINE {
+    const BoostIdx bi = boost_idx(S);
     produce_qt(S);
     wave_lds_sync();
     float s0, s1;
-    qk(S, valid, s0, s1);
+    qk(S, bi, valid, s0, s1);
     softmax_step(st, s0, s1, sl2, n);
     produce_pt(S, s0, s1);
     wave_lds_sync();
