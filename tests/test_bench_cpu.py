@@ -32,3 +32,22 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_code_hash_covers_every_local_include():
+    # a kernel's hash must change when any source it is compiled from changes:
+    # the .hip file and every header it includes from csrc/, transitively
+    import re
+    csrc = os.path.join(os.path.dirname(bench.__file__), "mixed_precision_bit_kitty_amd", "csrc")
+
+    def local_includes(name, seen):
+        for inc in re.findall(r'#include\s+"([^"]+)"', open(os.path.join(csrc, name)).read()):
+            base = os.path.basename(inc)
+            if os.path.exists(os.path.join(csrc, base)) and base not in seen:
+                seen.add(base)
+                local_includes(base, seen)
+        return seen
+
+    for sources in (bench.DECODE_SOURCES, bench.QUANTIZE_SOURCES):
+        need = local_includes(sources[0], {sources[0]})
+        assert need <= set(sources), (sources, need - set(sources))
