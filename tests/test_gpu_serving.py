@@ -29,14 +29,14 @@ def _gpu():
 REQUESTS = [(45, 40), (0, 35), (100, 20), (31, 33), (64, 10), (7, 50), (200, 12), (33, 30)]
 
 
-@pytest.mark.parametrize("rank_mode", ["page", "running"])
-def test_serving_with_a_shared_pool(rank_mode):
+@pytest.mark.parametrize("rank_mode,lo_bit", [("page", 2), ("running", 2), ("page", 4)])
+def test_serving_with_a_shared_pool(rank_mode, lo_bit):
     # running mode: a reused slot's sums restart with its new prefill
     import torch
     from mixed_precision_bit_kitty_amd import binding as B
     w = synth.LLAMA3_8B.with_(n_kv_heads=2, n_q_heads=8)
     n_slots, H, Hq, n_hi = 4, w.n_kv_heads, w.n_q_heads, w.n_hi
-    cache = B.KittyCache.with_pool(n_slots, H, n_hi, max_tokens=256, n_pages=14,
+    cache = B.KittyCache.with_pool(n_slots, H, n_hi, max_tokens=256, n_pages=14, lo_bit=lo_bit,
                                    rank_mode=B.KITTY_RANK_RUNNING if rank_mode == "running" else B.KITTY_RANK_PAGE)
     reqs = []
     for r, (prompt, gen) in enumerate(REQUESTS):
@@ -62,7 +62,8 @@ def test_serving_with_a_shared_pool(rank_mode):
                 before = host(cache.seq_lens).copy()
                 cache.reserve(b, q["prompt"])
                 cache.quantize_pages(k, v, lens=dev(lens))
-                q["oc"] = O.quantize_pages(q["x"]["k"], q["x"]["v"], n_hi, batch_lens=[q["prompt"]], rank_mode=rank_mode)
+                q["oc"] = O.quantize_pages(q["x"]["k"], q["x"]["v"], n_hi, batch_lens=[q["prompt"]], lo_bit=lo_bit,
+                                           rank_mode=rank_mode)
                 after = host(cache.seq_lens)
                 others = [i for i in range(n_slots) if i != b]
                 assert np.array_equal(after[others], before[others]), "a prefill touched another slot"
