@@ -159,15 +159,22 @@ __device__ __forceinline__ uint32_t pack_word4(uint64_t a) { return gather4_nib(
 // a more sensitive channel).  Selects the n largest keys, ties to the lower
 // channel index: the n-th largest key T is found bit by bit with wave
 // ballots (TOPBIT = the highest bit a key can have), then the keys equal to
-// T are taken in channel order by ballot popcounts.
+// T are taken in channel order by ballot popcounts.  The search stops early
+// once exactly n keys are >= the threshold found so far: the lower bits can
+// then only raise it to the n-th key itself, and the keys >= it stay the same
+// n (all of them are selected below, ties included).
 template <typename K, int TOPBIT>
 __device__ __forceinline__ void select_top(K k0, K k1, int n, int lane, bool& h0, bool& h1, int top = TOPBIT) {
   const uint64_t below = (1ull << lane) - 1ull;
   K T = 0;
-  for (int bit = top; bit >= 0; --bit) {  // bits above `top` are clear in every key
+  int cnt_t = 2 * 64;  // keys >= T: every key is >= 0
+  for (int bit = top; bit >= 0 && cnt_t != n; --bit) {  // bits above `top` are clear in every key
     const K cand = T | ((K)1 << bit);
     const int cnt = __popcll(__ballot(k0 >= cand)) + __popcll(__ballot(k1 >= cand));
-    if (cnt >= n) T = cand;
+    if (cnt >= n) {
+      T = cand;
+      cnt_t = cnt;
+    }
   }
   const int gt = __popcll(__ballot(k0 > T)) + __popcll(__ballot(k1 > T));
   const uint64_t e0 = __ballot(k0 == T), e1 = __ballot(k1 == T);
