@@ -67,6 +67,35 @@ __device__ __forceinline__ uint8_t* record_of(const QuantizeParams& p, int b, in
   return p.pages + (int64_t)phys * p.page_bytes + (int64_t)h * rec_bytes(boost_slots(p.n_hi), p.lo_bit);
 }
 
+// Chunk sums without carries or lane masks.  For a = M 2^s (the fixed-point
+// value of one fp16 key, as in accumulate): sum a is kept as sum (a ^ m) plus
+// the count of negative terms (m = -1 for a negative key, and a ^ -1 = -a - 1);
+// sum a^2 is kept as S0 + 2^32 S1, where a^2 = (M M << (2s & 31)) << (2s & 32)
+// adds its shifted product (below 2^53) to S0 or S1.  Neither 64-bit
+// accumulator can overflow within a chunk (256 terms below 2^53).
+struct ChunkSums {
+  uint64_t x1;    // sum of a ^ m
+  uint32_t nneg;  // negative terms
+  uint64_t s0, s1;
+};
+__device__ __forceinline__ void chunk_add(uint32_t h16, ChunkSums& c) {
+  const uint32_t e = (h16 >> 10) & 31u, m = h16 & 1023u;
+  const uint32_t nrm = (e + 31u) >> 5;  // 1 for a normal value (e >= 1), else 0
+  const uint32_t M = m | (nrm << 10);   // with its implicit bit
+  const uint32_t sh = e - nrm;          // a = M 2^sh
+  const uint64_t a = (uint64_t)M << sh;
+  const uint32_t neg = (uint32_t)((int32_t)(h16 << 16) >> 31);  // all ones for a negative key
+  const uint64_t neg64 = ((uint64_t)neg << 32) | neg;
+  c.x1 += a ^ neg64;
+  c.nneg -= neg;
+  const uint32_t sq = 2u * sh;
+  const uint64_t t = (uint64_t)(M * M) << (sq & 31u);
+  const uint32_t him = (uint32_t)((int32_t)(sq << 26) >> 31);  // all ones when sq >= 32
+  const uint64_t hi = ((uint64_t)him << 32) | him;
+  c.s0 += t & ~hi;
+  c.s1 += t & hi;
+}
+
 // grid (chunks, Hkv, batch), 4 waves.  Lane (cb = lane & 15, tg = lane >> 4)
 // of wave w sums channels 8cb .. 8cb + 7 over tokens 32j + tg + 4i (i =
 // 0..7) of pages j = 8c + 2w, 8c + 2w + 1 of chunk c.
@@ -80,13 +109,9 @@ __global__ __launch_bounds__(256) void key_chunk_kernel(QuantizeParams p) {
   if (kChunkPages * chunk >= P) return;  // no sealed page here: key_rank_kernel sums these tokens (block-uniform)
   const int t_end = min(n, kChunkTokens * (chunk + 1));
   const _Float16* kb = p.k + ((size_t)b * p.n_kv_heads + h) * (size_t)p.S * kHeadDim + 8 * cb;
-  int64_t s1[8];
-  u128 s2[8];
+  ChunkSums acc[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    s1[e] = 0;
-    s2[e] = 0;
-  }
+  for (int e = 0; e < 8; ++e) acc[e] = ChunkSums{0ull, 0u, 0ull, 0ull};
 #pragma unroll
   for (int pg = 0; pg < 2; ++pg) {
     const int t0 = kChunkTokens * chunk + kPageTokens * (2 * wave + pg);
@@ -100,7 +125,14 @@ __global__ __launch_bounds__(256) void key_chunk_kernel(QuantizeParams p) {
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int e = 0; e < 8; ++e)  // +0 halves of skipped tokens add nothing
-        accumulate((rows[i][e >> 1] >> (16 * (e & 1))) & 0xFFFFu, s1[e], s2[e]);
+        chunk_add((rows[i][e >> 1] >> (16 * (e & 1))) & 0xFFFFu, acc[e]);
+  }
+  int64_t s1[8];
+  u128 s2[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    s1[e] = (int64_t)(acc[e].x1 + acc[e].nneg);
+    s2[e] = (u128)acc[e].s0 + ((u128)acc[e].s1 << 32);
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e)
