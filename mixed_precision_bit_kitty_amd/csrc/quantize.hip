@@ -96,57 +96,53 @@ __device__ __forceinline__ void chunk_add(uint32_t h16, ChunkSums& c) {
   c.s1 += t & hi;
 }
 
-// grid (chunks, Hkv, batch), 4 waves.  Lane (cb = lane & 15, tg = lane >> 4)
-// of wave w sums channels 8cb .. 8cb + 7 over tokens 32j + tg + 4i (i =
-// 0..7) of pages j = 8c + 2w, 8c + 2w + 1 of chunk c.
+// grid (chunks, Hkv, batch), 4 waves.  Lane (cb = lane & 31, tg = lane >> 5)
+// of wave w sums channels 4cb .. 4cb + 3 over tokens 32j + tg + 2i (i =
+// 0..15) of pages j = 8c + 2w, 8c + 2w + 1 of chunk c (four channels a lane
+// keep the accumulators within four waves per SIMD).
 __global__ __launch_bounds__(256) void key_chunk_kernel(QuantizeParams p) {
   __shared__ int64_t ws1[4][kHeadDim];
   __shared__ u128 ws2[4][kHeadDim];
   const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, cb = lane & 15, tg = lane >> 4;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, cb = lane & 31, tg = lane >> 5;
   const int n = prefill_len(p, b);
   const int P = n < 0 ? 0 : n / kPageTokens;
   if (kChunkPages * chunk >= P) return;  // no sealed page here: key_rank_kernel sums these tokens (block-uniform)
   const int t_end = min(n, kChunkTokens * (chunk + 1));
-  const _Float16* kb = p.k + ((size_t)b * p.n_kv_heads + h) * (size_t)p.S * kHeadDim + 8 * cb;
-  ChunkSums acc[8];
+  const _Float16* kb = p.k + ((size_t)b * p.n_kv_heads + h) * (size_t)p.S * kHeadDim + 4 * cb;
+  ChunkSums acc[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = ChunkSums{0ull, 0u, 0ull, 0ull};
+  for (int e = 0; e < 4; ++e) acc[e] = ChunkSums{0ull, 0u, 0ull, 0ull};
 #pragma unroll
   for (int pg = 0; pg < 2; ++pg) {
     const int t0 = kChunkTokens * chunk + kPageTokens * (2 * wave + pg);
-    u32x4 rows[8];
+    u32x2 rows[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {  // every load issued before the first use
-      const int t = t0 + tg + 4 * i;
-      rows[i] = t < t_end ? *reinterpret_cast<const u32x4*>(kb + (size_t)t * kHeadDim) : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < 16; ++i) {  // every load issued before the first use
+      const int t = t0 + tg + 2 * i;
+      rows[i] = t < t_end ? *reinterpret_cast<const u32x2*>(kb + (size_t)t * kHeadDim) : u32x2{0u, 0u};
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 16; ++i)
 #pragma unroll
-      for (int e = 0; e < 8; ++e)  // +0 halves of skipped tokens add nothing
+      for (int e = 0; e < 4; ++e)  // +0 halves of skipped tokens add nothing
         chunk_add((rows[i][e >> 1] >> (16 * (e & 1))) & 0xFFFFu, acc[e]);
   }
-  int64_t s1[8];
-  u128 s2[8];
+  int64_t s1[4];
+  u128 s2[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
+  for (int e = 0; e < 4; ++e) {
     s1[e] = (int64_t)(acc[e].x1 + acc[e].nneg);
     s2[e] = (u128)acc[e].s0 + ((u128)acc[e].s1 << 32);
+    s1[e] += (int64_t)shfl_xor_u64((uint64_t)s1[e], 32);  // the other token group
+    const uint64_t lo = shfl_xor_u64((uint64_t)s2[e], 32), hi = shfl_xor_u64((uint64_t)(s2[e] >> 64), 32);
+    s2[e] += ((u128)hi << 64) | lo;
   }
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-#pragma unroll
-    for (int m = 16; m <= 32; m <<= 1) {
-      s1[e] += (int64_t)shfl_xor_u64((uint64_t)s1[e], m);
-      const uint64_t lo = shfl_xor_u64((uint64_t)s2[e], m), hi = shfl_xor_u64((uint64_t)(s2[e] >> 64), m);
-      s2[e] += ((u128)hi << 64) | lo;
-    }
   if (tg == 0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      ws1[wave][8 * cb + e] = s1[e];
-      ws2[wave][8 * cb + e] = s2[e];
+    for (int e = 0; e < 4; ++e) {
+      ws1[wave][4 * cb + e] = s1[e];
+      ws2[wave][4 * cb + e] = s2[e];
     }
   }
   __syncthreads();
