@@ -9,11 +9,16 @@ attention (dequant + QK + online softmax + PV over all pages, then the
 split merge).  ``--split`` times the two separate calls instead
 (``kitty_append_token`` then ``kitty_decode_attention``).
 
-Workload (default): Llama-3-8B shape, batch 16, 32 query heads, 8 KV heads,
-head_dim 128, context 4096, hi_fraction 0.25, seeded synthetic fp16 K/V/Q.
-``--lo-bit 4`` runs the (hi_bit 8, lo_bit 4) pair instead of (4, 2);
-``--rank-mode running`` the running-variance ranking instead of per-page
-ranking.
+Workload (default): the memory-budget batch sweep at its largest point --
+batch 128, 32 query heads, 8 KV heads, head_dim 128, context 8192,
+hi_fraction 0.25, seeded synthetic fp16 K/V/Q (880.8 MB of quantized KV read
+per step).  The default run also times the Llama-3-8B-shape step (batch 16,
+context 4096) and a read-only kernel over 2 GiB (the read-stream ceiling),
+reported beside the headline as context.  ``--workload`` / ``--batch``
+select another configuration; ``--lo-bit 4`` runs the (hi_bit 8, lo_bit 4)
+pair instead of (4, 2); ``--rank-mode running`` the running-variance ranking
+instead of per-page ranking; ``--ceiling`` times only the read-only kernels
+over a sweep of launch shapes.
 To keep reads coming from HBM rather than the 256 MB Infinity Cache, the
 steps rotate over L independent layer caches totalling >= 1 GiB.
 
@@ -232,53 +237,44 @@ def _rank(args):
     return 1 if args.rank_mode == "running" else 0
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=640)
-    ap.add_argument("--warmup", type=int, default=64)
-    ap.add_argument("--workload", default="llama3_8b",
-                    choices=["llama3_8b", "qwen3_8b", "batch_sweep", "prefill_sweep", "tiny"])
-    ap.add_argument("--batch", type=int, default=None, help="override the workload's batch (sweep points)")
-    ap.add_argument("--layers", type=int, default=0, help="layer caches to rotate (0: enough for >= 1 GiB)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="also run one 1 GiB device copy (HBM counter calibration under rocprofv3)")
-    ap.add_argument("--split", action="store_true",
-                    help="step = kitty_append_token + kitty_decode_attention (two launches) instead of the fused step")
-    ap.add_argument("--lo-bit", type=int, default=2, choices=[2, 4],
-                    help="bit-width pair: 2 = (hi_bit 4, lo_bit 2), 4 = (hi_bit 8, lo_bit 4)")
-    ap.add_argument("--rank-mode", default="page", choices=["page", "running"],
-                    help="boosted channels by each page's variance (page) or the head's running variance (running)")
-    ap.add_argument("--hi-fraction", type=float, default=None,
-                    help="override the workload's hi_fraction (n_hi = hi_fraction x 128, a multiple of 16)")
-    ap.add_argument("--quantize", action="store_true",
-                    help="time kitty_quantize_pages (prefill of the whole batch) instead of the decode step")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
-              file=sys.stderr)
-        sys.exit(2)
-
+def _gpu_inputs(w, B, steps):
+    """Seeded synthetic inputs of sequences 0..B-1 (the same per-sequence
+    streams as synth.batch), with K and V copied to the GPU in chunks so the
+    host holds only a few sequences at a time.  Returns (k, v on the GPU;
+    k_new, v_new, q_new [steps, B, ...] on the GPU)."""
     import torch
-    from mixed_precision_bit_kitty_amd import binding, synth
-
-    w = _workload(args.workload)
-    if args.hi_fraction is not None:
-        w = w.with_(hi_fraction=args.hi_fraction)
-    if args.quantize:
-        return bench_quantize(args, w)
-    B = args.batch or w.batch
-    ctx, Hkv, Hq, n_hi = w.ctx, w.n_kv_heads, w.n_q_heads, w.n_hi
-    K, W = args.steps, args.warmup
-    torch.cuda.set_device(0)
+    from concurrent.futures import ThreadPoolExecutor
+    from mixed_precision_bit_kitty_amd import synth
+    H, D, Hq = w.n_kv_heads, w.head_dim, w.n_q_heads
+    kd = torch.empty((B, H, w.ctx, D), dtype=torch.float16, device="cuda")
+    vd = torch.empty_like(kd)
+    kn = np.empty((steps, B, H, D), np.float16)
+    vn = np.empty_like(kn)
+    qn = np.empty((steps, B, Hq, D), np.float16)
+    chunk = 16
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        for b0 in range(0, B, chunk):
+            seqs = list(ex.map(lambda b: synth.sequence(w, b, steps=steps), range(b0, min(B, b0 + chunk))))
+            for j, x in enumerate(seqs):
+                kd[b0 + j].copy_(torch.from_numpy(x["k"]))
+                vd[b0 + j].copy_(torch.from_numpy(x["v"]))
+                kn[:, b0 + j], vn[:, b0 + j], qn[:, b0 + j] = x["k_new"], x["v_new"], x["q_new"]
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    return kd, vd, dev(kn), dev(vn), dev(qn)
 
+
+def time_decode(args, w, B, K, W, split=False):
+    """K timed decode steps (after W untimed ones) of workload w at batch B
+    over L rotated layer caches, replayed from HIP graphs.  Returns the step
+    time, the decode kernel's own average launch time and the algorithmic
+    bytes of both."""
+    import torch
+    from mixed_precision_bit_kitty_amd import binding
+
+    ctx, Hkv, Hq, n_hi = w.ctx, w.n_kv_heads, w.n_q_heads, w.n_hi
     print(f"[bench] generating {w.name} batch {B} ctx {ctx}", file=sys.stderr, flush=True)
     n_tok = 64
-    x = synth.batch(w, batch=B, steps=n_tok)
-    k_new, v_new, q_new = dev(x["k_new"]), dev(x["v_new"]), dev(x["q_new"])
+    kd, vd, k_new, v_new, q_new = _gpu_inputs(w, B, n_tok)
 
     max_tokens = ctx + K + W + 32
     probe = binding.KittyCache(1, Hkv, n_hi, max_tokens, lo_bit=args.lo_bit, rank_mode=_rank(args))
@@ -287,7 +283,6 @@ def main():
     L = args.layers or max(1, math.ceil((1 << 30) / layer_bytes))
     print(f"[bench] {L} layer caches x {layer_bytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
     layers = [binding.KittyCache(B, Hkv, n_hi, max_tokens, lo_bit=args.lo_bit, rank_mode=_rank(args)) for _ in range(L)]
-    kd, vd = dev(x["k"]), dev(x["v"])
     layers[0].quantize_pages(kd, vd)
     for c in layers[1:]:
         c.pool.copy_(layers[0].pool)
@@ -297,6 +292,8 @@ def main():
         if c.key_stats is not None:
             c.key_stats.copy_(layers[0].key_stats)
     del kd, vd
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     # Every sequence of a layer has the same length.  Layer l takes its steps
     # i = l, l + L, ...; the decode bound max_seq_len is the longest length
     # the layer reaches in this run, so the page split stays balanced.
@@ -312,7 +309,7 @@ def main():
         c, t = layers[l], l % n_tok
         if decode_only:
             c.decode_attention(q_new[t], max_seq_len=msl, out=outs[l], workspace=ws[l])
-        elif args.split:
+        elif split:
             c.append_token(k_new[t], v_new[t])
             c.decode_attention(q_new[t], max_seq_len=msl, out=outs[l], workspace=ws[l])
         else:
@@ -328,7 +325,7 @@ def main():
             step_eager(l)
         g_step.append(g)
     g_dec = None
-    if args.split:  # the decode of every layer, back to back (the roofline's kernel alone)
+    if split:  # the decode of every layer, back to back (the roofline's kernel alone)
         g_dec = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_dec):
             for l in range(L):
@@ -365,15 +362,13 @@ def main():
         li = (W + i) % L
         lens[li] += 1
         bytes_steps.append(kv_bytes([lens[li]] * B, Hkv, rec))
-    total_ms = start.elapsed_time(end)
-    ms_step = total_ms / K
+    ms_step = start.elapsed_time(end) / K
     avg_bytes = sum(bytes_steps) / K
-    gbs = avg_bytes / (ms_step * 1e-3) / 1e9
 
     if g_dec is None:
         # The fused step is one decode-kernel launch per step: the timed
         # region is K launches of that kernel back to back.
-        dec_avg_ms, dec_bytes, dec_gbs = ms_step, avg_bytes, gbs
+        dec_ms, dec_bytes = ms_step, avg_bytes
         kernel = "decode_kernel (kitty_decode_step)"
     else:
         # The decode kernel alone: R replays of one graph holding the decode
@@ -387,11 +382,129 @@ def main():
             g_dec.replay()
         end.record()
         torch.cuda.synchronize()
-        dec_avg_ms = start.elapsed_time(end) / (R * L)
-        dec_gbs = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
+        dec_ms = start.elapsed_time(end) / (R * L)
         kernel = "decode_kernel (kitty_decode_attention)"
-    print(f"[bench] step {ms_step * 1e3:.2f} us ({gbs:.0f} GB/s), decode kernel {dec_avg_ms * 1e3:.2f} us "
-          f"({dec_gbs:.0f} GB/s, {dec_gbs / HBM_PEAK_GBS:.3f} of peak)", file=sys.stderr, flush=True)
+    gbs = avg_bytes / (ms_step * 1e-3) / 1e9
+    dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
+    print(f"[bench] {w.name} batch {B}: step {ms_step * 1e3:.2f} us ({gbs:.0f} GB/s), decode kernel "
+          f"{dec_ms * 1e3:.2f} us ({dec_gbs:.0f} GB/s, {dec_gbs / HBM_PEAK_GBS:.3f} of peak)", file=sys.stderr, flush=True)
+    del g_step, g_dec, g_round, layers, outs, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {"ms_step": ms_step, "gbs": gbs, "bytes": avg_bytes, "dec_ms": dec_ms, "dec_gbs": dec_gbs,
+            "dec_bytes": dec_bytes, "kernel": kernel, "layers": L, "layer_bytes": layer_bytes}
+
+
+CEILING_DEFAULT = (0, 16, 4)  # mode, waves per CU, loads in flight per lane: the best of the sweep on MI355X
+CEILING_SWEEP = [(0, w, d) for w in (8, 16, 32) for d in (2, 4, 8)] + \
+                [(1, w, d) for w in (8, 12) for d in (2, 3, 4) if w * d * 3360 <= 160 * 1024]
+
+
+def read_ceiling(configs, gib=2, reps=10):
+    """GB/s of the read-only kernels over `gib` GiB: per (mode, waves per
+    CU, depth), the average of `reps` launches timed with HIP events on the
+    launch stream (after one untimed launch)."""
+    import torch
+    from mixed_precision_bit_kitty_amd import binding
+    lib = binding.load_bench()
+    nbytes = gib << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    out = []
+    for mode, waves, depth in configs:
+        used = nbytes if mode == 0 else nbytes // 3360 * 3360
+
+        def launch():
+            rc = lib.kitty_read_ceiling(src.data_ptr(), nbytes, mode, waves, depth, sink.data_ptr(), sink.numel(),
+                                        stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"kitty_read_ceiling({mode}, {waves}, {depth}) returned {rc}")
+        launch()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(reps):
+            launch()
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / reps
+        gbs = used / (ms * 1e-3) / 1e9
+        name = ("read_vgpr_kernel" if mode == 0 else "read_lds_kernel") + f"<{depth}>"
+        print(f"[bench] ceiling {name}, {waves} waves/CU: {ms * 1e3:.1f} us per {used / 2**30:.2f} GiB, "
+              f"{gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.3f} of peak)", file=sys.stderr, flush=True)
+        out.append({"kernel": name, "mode": "registers" if mode == 0 else "lds_records", "waves_per_cu": waves,
+                    "depth": depth, "gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                    "us": round(ms * 1e3, 2), "bytes": used})
+    del src, sink
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_ceiling(args):
+    res = read_ceiling(CEILING_SWEEP)
+    best = max(res, key=lambda r: r["gbs"])
+    best_lds = max((r for r in res if r["mode"] == "lds_records"), key=lambda r: r["gbs"])
+    print(json.dumps({"metric": "HBM read-stream ceiling: GB/s of read-only kernels over 2 GiB",
+                      "value": best["gbs"], "unit": "GB/s", "n_gpus": 1, "higher_is_better": True,
+                      "frac_of_hbm_peak": best["frac"], "best": best, "best_lds_records": best_lds,
+                      "sweep": res}), flush=True)
+
+
+def _workload_key(args, w, B):
+    """Name of a configuration in the committed counter summaries."""
+    return args.workload + ("" if B == w.batch else f"_b{B}") + _lo_suffix(args)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="batch_sweep",
+                    choices=["llama3_8b", "qwen3_8b", "batch_sweep", "prefill_sweep", "tiny"])
+    ap.add_argument("--batch", type=int, default=None,
+                    help="override the workload's batch (default: 128 for batch_sweep, the sweep's largest point)")
+    ap.add_argument("--layers", type=int, default=0, help="layer caches to rotate (0: enough for >= 1 GiB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the extra llama3_8b step and read-ceiling measurements of the default run")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 1 GiB device copy (HBM counter calibration under rocprofv3)")
+    ap.add_argument("--split", action="store_true",
+                    help="step = kitty_append_token + kitty_decode_attention (two launches) instead of the fused step")
+    ap.add_argument("--lo-bit", type=int, default=2, choices=[2, 4],
+                    help="bit-width pair: 2 = (hi_bit 4, lo_bit 2), 4 = (hi_bit 8, lo_bit 4)")
+    ap.add_argument("--rank-mode", default="page", choices=["page", "running"],
+                    help="boosted channels by each page's variance (page) or the head's running variance (running)")
+    ap.add_argument("--hi-fraction", type=float, default=None,
+                    help="override the workload's hi_fraction (n_hi = hi_fraction x 128)")
+    ap.add_argument("--quantize", action="store_true",
+                    help="time kitty_quantize_pages (prefill of the whole batch) instead of the decode step")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="time only the read-only kernels (HBM read-stream ceiling) over a sweep of launch shapes")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mixed_precision_bit_kitty_amd import binding  # noqa: F401  (fails loudly without the library)
+
+    torch.cuda.set_device(0)
+    if args.ceiling:
+        return bench_ceiling(args)
+    w = _workload(args.workload)
+    if args.hi_fraction is not None:
+        w = w.with_(hi_fraction=args.hi_fraction)
+    if args.quantize:
+        return bench_quantize(args, w)
+    B = args.batch or (max(w.sweep) if args.workload == "batch_sweep" else w.batch)
+    K, W = args.steps, args.warmup
+    r = time_decode(args, w, B, K, W, split=args.split)
+    ctx, Hkv, Hq, n_hi = w.ctx, w.n_kv_heads, w.n_q_heads, w.n_hi
 
     if args.calibrate_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -402,27 +515,43 @@ def main():
         del a, bcopy
 
     khash = source_hash(DECODE_SOURCES)
-    roof = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": committed_traffic(khash, args.workload + _lo_suffix(args), "attention" if args.split else "step"),
-            "kernel": kernel,
-            "bytes_per_launch": int(dec_bytes), "avg_launch_us": round(dec_avg_ms * 1e3, 3),
+    roof = {"bound": "hbm", "achieved": round(r["dec_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(r["dec_gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": committed_traffic(khash, _workload_key(args, w, B), "attention" if args.split else "step"),
+            "kernel": r["kernel"],
+            "bytes_per_launch": int(r["dec_bytes"]), "avg_launch_us": round(r["dec_ms"] * 1e3, 3),
             "kernel_source_sha256_16": khash}
+    L = r["layers"]
     res = {
         "metric": METRIC if args.lo_bit == 2 else METRIC.replace("2-bit-KV", "4-bit-KV (hi_bit 8, lo_bit 4)"),
-        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
-        "ms_per_step": round(ms_step, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "value": round(r["gbs"], 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(r["ms_step"], 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp16", "data": "synthetic",
-        "tokens_per_s": round(B / (ms_step * 1e-3), 1),
-        "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "tokens_per_s": round(B / (r["ms_step"] * 1e-3), 1),
+        "frac_of_hbm_peak": round(r["gbs"] / HBM_PEAK_GBS, 4),
         "config": {"workload": f"{w.name}: one layer, batch {B}, {Hq} query heads, {Hkv} KV heads, head_dim 128, "
                                f"context {ctx}+, hi_fraction {w.hi_fraction} (n_hi {n_hi}), "
                                f"hi_bit {2 * args.lo_bit} / lo_bit {args.lo_bit}, {args.rank_mode} ranking; step = "
                                f"{'append + decode (two launches)' if args.split else 'fused append + decode (one launch)'} "
-                               f"(replayed from HIP graphs of {L} steps); {L} layer caches rotated ({L * layer_bytes / 2**30:.2f} GiB)",
+                               f"(replayed from HIP graphs of {L} steps); {L} layer caches rotated "
+                               f"({L * r['layer_bytes'] / 2**30:.2f} GiB)",
                    "batch": B, "ctx": ctx, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": 128, "n_hi": n_hi,
                    "hi_bit": 2 * args.lo_bit, "lo_bit": args.lo_bit, "rank_mode": args.rank_mode, "layers_rotated": L},
         "roofline": roof,
     }
+    default_run = (args.workload == "batch_sweep" and args.batch is None and not args.split and args.lo_bit == 2
+                   and args.rank_mode == "page" and args.hi_fraction is None)
+    if default_run and not args.no_context:
+        # context beside the headline: the Llama-3-8B-shape step and the read-only ceiling
+        wl = _workload("llama3_8b")
+        r2 = time_decode(args, wl, wl.batch, K, W)
+        res["llama3_8b_b16_ctx4096"] = {
+            "ms_per_step": round(r2["ms_step"], 6), "value": round(r2["gbs"], 1), "unit": "GB/s",
+            "frac_of_hbm_peak": round(r2["gbs"] / HBM_PEAK_GBS, 4), "bytes_per_step": int(r2["bytes"]),
+            "tokens_per_s": round(wl.batch / (r2["ms_step"] * 1e-3), 1),
+            "traffic": committed_traffic(khash, "llama3_8b", "step")}
+        c = read_ceiling([CEILING_DEFAULT])[0]
+        res["read_ceiling"] = c
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w.with_(batch=B), args.cpu_seconds, args.lo_bit, args.rank_mode)

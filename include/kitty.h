@@ -169,16 +169,35 @@ int kitty_append_token(const kitty_config_t* cfg, const kitty_kv_view_t* kv,
 int kitty_decode_workspace_bytes(const kitty_config_t* cfg, int32_t batch, int32_t n_q_heads,
                                  int32_t max_seq_len, size_t* out);
 
+/* The split plan decode attention and the fused step use for this shape on
+ * a device with n_cus compute units (1..256; 0 = the current device): out[0]
+ * = workgroups per (sequence, KV head, group of up to 4 query heads), out[1]
+ * = waves per workgroup, out[2] = the largest workgroup the record size
+ * allows.  Host only, for tests and tuning; the same validation and errors
+ * as kitty_decode_workspace_bytes, and KITTY_ERR_HIP when n_cus = 0 finds no
+ * device.  out: host int32[3]. */
+int kitty_decode_plan(const kitty_config_t* cfg, int32_t batch, int32_t n_q_heads, int32_t max_seq_len,
+                      int32_t n_cus, int32_t* out);
+
 /* Fused decode attention over the quantized cache (Abstract: page
  * dequantization fused into the decode kernels).  q: device fp16
  * [batch][Hq][D], 16-byte aligned, Hq a multiple of Hkv; query head hq reads KV head
- * hq / (Hq / Hkv).  For each sequence, attends over all seq_lens[b] tokens --
- * sealed pages in order, then the fp16 tail: out[b][hq] = softmax(q . k^ /
- * sqrt(D)) . v^ with k^, v^ the dequantized keys and values.  out: device
- * fp32 [batch][Hq][D] (zeros for an empty sequence or an inactive slot,
- * seq_lens[b] < 0).  max_seq_len bounds
- * seq_lens (tokens beyond it are ignored); at most 131103 (4096 pages plus a
- * tail), else KITTY_ERR_UNSUPPORTED.  workspace: device, 256-byte
+ * hq / (Hq / Hkv).  For each sequence, attends over its first
+ * n = min(seq_lens[b], max_seq_len) tokens -- sealed pages in order, then the
+ * fp16 tail: out[b][hq] = softmax(q . k^ / sqrt(D)) . v^ with k^, v^ the
+ * dequantized keys and values.  out: device fp32 [batch][Hq][D] (zeros for
+ * an empty sequence or an inactive slot, seq_lens[b] < 0).  max_seq_len
+ * sizes the split of the pages over the decode waves; tokens at or beyond it
+ * are not attended (when it falls inside a sealed page, that page is
+ * attended up to it); at most 131103 (4096 pages plus a tail), else
+ * KITTY_ERR_UNSUPPORTED.
+ * Inputs are finite fp16 (unchecked).  Every intermediate stays finite for
+ * any finite q, K and V: the query is scaled by a power of two inside the
+ * q * kscale limbs, and a page whose Value steps exceed 255.5 keeps its
+ * softmax weights at most 1 (both exact in fp32).  Accuracy: the outputs
+ * match fp32 attention over k^, v^ to about 2^-20 of max |v^| plus the
+ * effect of that relative error on the logits (about 2^-21 |s|).
+ * workspace: device, 256-byte
  * aligned, at least kitty_decode_workspace_bytes(...) bytes, zero-filled by
  * the caller before its first use (e.g. allocated zeroed); every completed
  * call leaves its counter area zero again, so one workspace serves any
@@ -196,8 +215,8 @@ int kitty_decode_attention(const kitty_config_t* cfg, const kitty_kv_view_t* kv,
  * that entry is >= max_pages or outside the pool, as the append does) and
  * attended as a sealed page; seq_lens[b] becomes n + 1.  Inactive slots
  * (seq_lens[b] < 0) append nothing and attend nothing.  k_new, v_new:
- * device fp16 [batch][Hkv][D], 16-byte aligned.  max_seq_len bounds the
- * length after the append.  Other arguments, the workspace (the same size
+ * device fp16 [batch][Hkv][D], 16-byte aligned.  The query attends the first
+ * min(n + 1, max_seq_len) tokens.  Other arguments, the workspace (the same size
  * and zero-fill rules) and the errors are those of kitty_decode_attention.
  * The result equals the two separate calls' within floating-point rounding
  * (the page sealed by this call is folded in by another wave); the records,

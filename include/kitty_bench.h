@@ -1,0 +1,45 @@
+/*
+ * kitty_bench.h -- measurement entry point of the Kitty library (gfx950):
+ * the HBM read-stream ceiling that the decode kernel's bandwidth is judged
+ * against.  Not part of the cache's hot path; bench.py --ceiling calls it.
+ *
+ * "Kitty: Accurate and Efficient 2-bit KV Cache Quantization with Dynamic
+ * Channel-wise Precision Boost", Abstract: the KV cache is the dominant
+ * memory bottleneck of decode, so the rate at which a kernel can read it is
+ * the figure of merit, and this is the best rate a read-only kernel reaches.
+ */
+#ifndef KITTY_BENCH_H
+#define KITTY_BENCH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  KITTY_READ_VGPR = 0,       /* 16-byte loads into registers, `depth` in flight per lane, grid-stride */
+  KITTY_READ_LDS_RECORDS = 1 /* 3360-byte records streamed into a `depth`-slot LDS ring per wave
+                                with global_load_lds_dwordx4 (the decode kernel's memory path) */
+};
+
+/* Read `bytes` of device memory at `src` once (16-byte aligned, a multiple
+ * of 16; LDS mode: the whole 3360-byte records it holds) with the access
+ * pattern `mode`, on `waves_per_cu` waves per compute unit of the stream's
+ * device (VGPR mode: 4..32, a multiple of 4; depth 1, 2, 4 or 8.  LDS mode:
+ * one workgroup of 1..12 waves per CU; depth 1..4; waves * depth * 3360
+ * bytes of LDS at most 160 KiB).  sink: device uint32 [sink_len], at least
+ * one entry per workgroup (VGPR) or per wave (LDS); the kernels keep every
+ * load live by storing a checksum there only when it equals a constant, so
+ * in practice they write nothing.  Asynchronous on `stream`.  Returns 0,
+ * KITTY_ERR_INVALID_ARG (-1) for arguments outside these ranges (before any
+ * launch) or KITTY_ERR_HIP (-4). */
+int kitty_read_ceiling(const void* src, size_t bytes, int32_t mode, int32_t waves_per_cu, int32_t depth,
+                       uint32_t* sink, size_t sink_len, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KITTY_BENCH_H */

@@ -60,11 +60,18 @@ class kitty_pool_t(ctypes.Structure):
 _lib = None
 
 
-def declared_symbols(header=HEADER):
-    """Names of the functions include/kitty.h declares."""
-    with open(header) as f:
-        text = f.read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(kitty_\w+)\s*\(", text, re.M)))
+BENCH_HEADER = os.path.join(os.path.dirname(PKG), "include", "kitty_bench.h")
+
+
+def declared_symbols(header=None):
+    """Names of the functions include/kitty.h (and kitty_bench.h) declare,
+    or those of one given header."""
+    out = set()
+    for h in ([HEADER, BENCH_HEADER] if header is None else [header]):
+        with open(h) as f:
+            text = f.read()
+        out |= set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(kitty_\w+)\s*\(", text, re.M))
+    return sorted(out)
 
 
 def load(path=None):
@@ -92,6 +99,7 @@ def load(path=None):
         "kitty_quantize_pages": ([cfgp, viewp, vp, vp, i32, vp, vp], ctypes.c_int),
         "kitty_append_token": ([cfgp, viewp, vp, vp, vp], ctypes.c_int),
         "kitty_decode_workspace_bytes": ([cfgp, i32, i32, i32, P(sz)], ctypes.c_int),
+        "kitty_decode_plan": ([cfgp, i32, i32, i32, i32, P(i32)], ctypes.c_int),
         "kitty_decode_attention": ([cfgp, viewp, vp, i32, i32, vp, vp, sz, vp], ctypes.c_int),
         "kitty_decode_step": ([cfgp, viewp, vp, vp, vp, i32, i32, vp, vp, sz, vp], ctypes.c_int),
         "kitty_pool_init": ([P(kitty_pool_t), vp, ctypes.c_int64], ctypes.c_int),
@@ -103,6 +111,17 @@ def load(path=None):
         fn.argtypes = args
         fn.restype = res
     _lib = lib
+    return lib
+
+
+def load_bench():
+    """The library with the measurement entry point of include/kitty_bench.h
+    declared (kitty_read_ceiling)."""
+    lib = load()
+    f = lib.kitty_read_ceiling
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                  ctypes.c_size_t, ctypes.c_void_p]
+    f.restype = ctypes.c_int
     return lib
 
 
@@ -138,6 +157,15 @@ def kitty_decode_workspace_bytes(cfg, batch, n_q_heads, max_seq_len):
     _check(load().kitty_decode_workspace_bytes(ctypes.byref(cfg), batch, n_q_heads, max_seq_len,
                                                ctypes.byref(out)))
     return out.value
+
+
+def kitty_decode_plan(cfg, batch, n_q_heads, max_seq_len, n_cus=0):
+    """(workgroups per unit, waves per workgroup, largest workgroup) of the
+    decode split plan on a device with n_cus compute units (0: the current
+    device)."""
+    out = (ctypes.c_int32 * 3)()
+    _check(load().kitty_decode_plan(ctypes.byref(cfg), batch, n_q_heads, max_seq_len, n_cus, out))
+    return tuple(out)
 
 
 def _ptr(t):

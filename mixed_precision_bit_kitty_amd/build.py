@@ -31,6 +31,8 @@ SOURCES = {
     # which lets the DPP row reductions fold into v_max_f32_dpp
     "decode.hip": ["-fno-honor-nans"],
     "kitty_abi.cpp": ["-x", "hip"],
+    # the read-stream ceiling (measurement only)
+    "ceiling.hip": [],
 }
 
 

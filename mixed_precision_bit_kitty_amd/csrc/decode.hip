@@ -278,15 +278,20 @@ __device__ __forceinline__ float head_of_column(float v_row, int n) {
 // Online softmax step for lane (n, w): raw logits s0, s1 of head w at tokens
 // n and n + 16 of the page; they become probabilities.  The max over the
 // page's 32 tokens is a 16-lane row reduction.  The reference m is raised
-// only when a logit exceeds it by more than kSlack (log2 units), so after the
-// first page a rescale is rare; until then probabilities may reach 2^kSlack,
-// which the fp16 limbs of p and p * vscale carry without overflow.  The PV
-// accumulators hold head n & 3 in column n, so their rescale factor is read
-// from that head's row.
+// only when a logit exceeds it by more than `slack` (log2 units), so after
+// the first page a rescale is rare; until then probabilities may reach
+// 2^slack.  The fp16 limb hi = f16(p_hi * vscale) is finite while
+// p_hi * vscale < 65520: the page's slack is kSlack when every vscale of the
+// page is at most kVsSafe (2^8 * 255.5 < 65504), else 0, which keeps p <= 1
+// and p * vscale <= vscale <= 43680 (the largest fp16 step of a range of two
+// finite fp16 values over 3 levels).  The PV accumulators hold head n & 3 in
+// column n, so their rescale factor is read from that head's row.
 constexpr float kSlack = 8.0f;
-__device__ __forceinline__ void softmax_step(WaveState& st, float& s0, float& s1, float sl2, int n) {
+constexpr float kVsSafe = 255.5f;
+__device__ __forceinline__ void softmax_step(WaveState& st, float& s0, float& s1, float sl2, int n,
+                                             float slack = kSlack) {
   const float mx = row_max16(fmaxf(s0, s1)) * sl2;
-  if (__ballot(mx > st.m + kSlack)) {  // wave-uniform
+  if (__ballot(mx > st.m + slack)) {  // wave-uniform
     const float mnew = fmaxf(st.m, mx);
     const float alpha = __builtin_amdgcn_exp2f(st.m - mnew);
     st.l *= alpha;
@@ -464,15 +469,27 @@ void decode_kernel(DecodeParams p) {
     }
   }
 
+  // Tokens attended: the first seq = min(total, max_seq_len).  When the
+  // bound falls inside a sealed page (not the sequence's tail page), that
+  // page is attended up to the bound (last_lim tokens) and no tail token is.
   const int seq = total > p.max_seq_len ? p.max_seq_len : total;
-  int P = seq / kPageTokens;
-  const int ntail = seq - P * kPageTokens;
-  if (P > p.max_pages) P = p.max_pages;  // now P <= Pm
+  const int pfull = seq / kPageTokens;
+  const int rem = seq - pfull * kPageTokens;
+  const bool part_sealed = rem > 0 && pfull < total / kPageTokens;
+  int P = part_sealed ? pfull + 1 : pfull;  // pages attended, the last one possibly in part
+  int last_lim = part_sealed ? rem : kPageTokens;
+  if (P > p.max_pages) {  // now P <= Pm + 1
+    P = p.max_pages;
+    last_lim = kPageTokens;
+  }
+  const int ntail = part_sealed ? 0 : rem;
   // A seal by this call makes page n0 / 32: the tail wave attends it (when
   // its block table entry is valid; else, like any invalid page, it adds
-  // nothing) and the page waves leave it out.
+  // nothing) and the page waves leave it out.  The tail wave also takes a
+  // sealed page the bound cuts (page pfull, beyond every page wave's range).
   const bool new_page = fused && n0 % kPageTokens == kPageTokens - 1 && P > n0 / kPageTokens;
-  const int p1 = min(p1m, new_page ? P - 1 : P);
+  const bool extra_page = new_page || (part_sealed && P == pfull + 1);
+  const int p1 = min(p1m, extra_page ? P - 1 : P);
   const int npg = p1 > p0 ? p1 - p0 : 0;
   const uint8_t* head_base = p.pages + (int64_t)hk * RB;
   // page ids are int32 and the page stride is below 2^32 (at most 1024 KV
@@ -494,6 +511,32 @@ void decode_kernel(DecodeParams p) {
     if (d < npg) dma_record<NHI, BITS>(rec_of(phys_of(d)), sm.ring[d], lane);
 
   // ---- per-wave constants -------------------------------------------------
+  // Power-of-two scale of the query in the q * kscale limbs: 2^-qe brings
+  // every |q| of the head group to at most 1.49, so that q 2^-qe * kscale
+  // stays below 65504 for every kscale the quantizer can produce (at most
+  // 43680: the step of a range of two finite fp16 values over 3 levels); the
+  // logits are scaled back by 2^qe in fp32, exactly.
+  int qe = 0;
+  {
+    float qa = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qa = fmaxf(qa, fabsf((float)q_prod[j]));
+    qa = row_max16(qa);
+    qa = fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, qa), 0)),
+                     __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, qa), 16))),
+               fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, qa), 32)),
+                     __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, qa), 48))));
+    for (int i = 0; i < 16 && qa > 1.49f; ++i) {  // wave-uniform; 65504 / 2^16 < 1
+      qa *= 0.5f;
+      ++qe;
+    }
+    if (qe) {
+      const float f = __builtin_ldexpf(1.0f, -qe);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) q_prod[j] = (_Float16)((float)q_prod[j] * f);
+    }
+  }
+  const float qsc = __builtin_ldexpf(1.0f, qe);
   const uint32_t m8v = vgpr_const(0x03000300u), m6v = vgpr_const(0x00C000C0u);
   const ExpBits ex_base{vgpr_const(0x44004400u), vgpr_const(0x4C004C00u), m8v, m6v};   // 4 + c, 16 + c
   const ExpBits ex_boost{vgpr_const(0x3C003C00u), vgpr_const(0x44004400u), m8v, m6v};  // (4 + c) / 4, (16 + c) / 4
@@ -560,7 +603,9 @@ void decode_kernel(DecodeParams p) {
     }
     return r;
   };
-  auto qk = [&](const uint8_t* S, const BoostIdx& bi, bool valid, float& s0, float& s1) KITTY_INLINE {
+  // lim: tokens of the page below the attention bound (32 but for a page the
+  // bound cuts)
+  auto qk = [&](const uint8_t* S, const BoostIdx& bi, bool valid, int lim, float& s0, float& s1) KITTY_INLINE {
     // this lane's K base chunk: four words (2-bit) or eight (4-bit: combos A, B of word x at 2x, 2x + 1)
     const u32x4 kw = *reinterpret_cast<const u32x4*>(S + 16 * BITS / 2 * lane);
     const u32x4 kw2 = BITS == 4 ? *reinterpret_cast<const u32x4*>(S + 32 * lane + 16) : u32x4{};
@@ -622,23 +667,38 @@ void decode_kernel(DecodeParams p) {
         acc1 = mfma(bb[k2], unpack_codes4(bw[k2][1], m4v, e4_boost), acc1);
       }
     }
-    // rows 4w (hi limb, with the minimum term) + 4w + 1 (lo limb) of head w
-    const float cst = cmin[0] + coff[0] + coff[1];
-    s0 = valid ? acc0[0] + acc0[1] + cst : -INFINITY;  // token n
-    s1 = valid ? acc1[0] + acc1[1] + cst : -INFINITY;  // token n + 16
+    // rows 4w (hi limb, with the minimum term) + 4w + 1 (lo limb) of head w;
+    // the code terms carry the query scale 2^-qe, the minimum term does not
+    const float cst = __builtin_fmaf(coff[0] + coff[1], qsc, cmin[0]);
+    s0 = valid && n < lim ? __builtin_fmaf(acc0[0] + acc0[1], qsc, cst) : -INFINITY;       // token n
+    s1 = valid && n + 16 < lim ? __builtin_fmaf(acc1[0] + acc1[1], qsc, cst) : -INFINITY;  // token n + 16
   };
   // p * vscale limbs (tokens n, n + 16 of head w, all four groups) and p
   // limbs.  With p = p_hi + p_lo (fp16 limbs), p * vscale = hi + lo where
   // hi = f16(p_hi vscale), lo = f16(p_lo vscale + (p_hi vscale - hi)): the
   // inner residual is exact and lo is rounded once, so the pair carries
   // p * vscale to about 2^-21 relative.
-  auto produce_pt = [&](const uint8_t* S, float s0, float s1) KITTY_INLINE {
-    const PLimbs pl = p_limbs(s0, s1);
-    // all four reads before the first write: the compiler cannot tell the
-    // limb writes from the record, and would otherwise wait for each read
-    half2v vsg[4];
+  // The page's value steps of tokens (2n, 2n + 1) in all four groups (lane
+  // (n, w) and its row neighbours read the same; together the lanes cover
+  // the page's 128 steps), read before the softmax: their maximum sets the
+  // page's slack.
+  struct VScales {
+    half2v g[4];
+  };
+  auto read_vscales = [&](const uint8_t* S) KITTY_INLINE {
+    VScales v;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) vsg[g] = *reinterpret_cast<const half2v*>(S + off_vscale(NHI, BITS) + 2 * (32 * g + 2 * n));
+    for (int g = 0; g < 4; ++g) v.g[g] = *reinterpret_cast<const half2v*>(S + off_vscale(NHI, BITS) + 2 * (32 * g + 2 * n));
+    return v;
+  };
+  auto page_slack = [&](const VScales& v) KITTY_INLINE {
+    const half2v a = __builtin_elementwise_max(__builtin_elementwise_max(v.g[0], v.g[1]),
+                                               __builtin_elementwise_max(v.g[2], v.g[3]));
+    return __ballot((float)a[0] > kVsSafe || (float)a[1] > kVsSafe) ? 0.0f : kSlack;  // steps are >= 0
+  };
+  auto produce_pt = [&](const VScales& vsc, float s0, float s1) KITTY_INLINE {
+    const PLimbs pl = p_limbs(s0, s1);
+    const half2v* vsg = vsc.g;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const half2v vs = vsg[g];
@@ -674,14 +734,18 @@ void decode_kernel(DecodeParams p) {
     st.corr = mfma(a, bg0, st.corr);
   };
   // one page through the whole contraction
-  auto attend_page = [&](const uint8_t* S, bool valid) KITTY_INLINE {
+  // (all the page's reads of the record come before the first limb write:
+  // the compiler cannot tell those writes from the record, and would
+  // otherwise wait for each read)
+  auto attend_page = [&](const uint8_t* S, bool valid, int lim) KITTY_INLINE {
     const BoostIdx bi = boost_idx(S);
+    const VScales vsc = read_vscales(S);
     produce_qt(S);
     wave_lds_sync();
     float s0, s1;
-    qk(S, bi, valid, s0, s1);
-    softmax_step(st, s0, s1, sl2, n);
-    produce_pt(S, s0, s1);
+    qk(S, bi, valid, lim, s0, s1);
+    softmax_step(st, s0, s1, sl2, n, page_slack(vsc));
+    produce_pt(vsc, s0, s1);
     wave_lds_sync();
     pv(S);
   };
@@ -748,7 +812,7 @@ void decode_kernel(DecodeParams p) {
   auto page_step = [&](int i, auto slot_c) KITTY_INLINE {
     constexpr int slot = decltype(slot_c)::value;
     wait_page<NHI, BITS>(min(kRing - 1, npg - 1 - i));
-    attend_page(sm.ring[slot], valid_of(i));
+    attend_page(sm.ring[slot], valid_of(i), kPageTokens);
     if (i + kRing < npg) {  // refill this slot
       wait_lgkm0();
       compiler_fence();
@@ -761,17 +825,29 @@ void decode_kernel(DecodeParams p) {
     if (i + 1 < npg) page_step(i + 1, std::integral_constant<int, 1>{});
   }
 
-  // ---- the tail wave: the page sealed by this call, then the newest tokens -------
-  if (tail_wave) {
-    if (new_page && seal_rec != nullptr) {  // read the record back through the device coherence point
-      wait_lgkm0();  // the quantizer's LDS reads are done before the ring is refilled
-      compiler_fence();
-      wait_vmcnt<0>();  // the record's stores are complete
-      compiler_fence();
-      dma_record<NHI, BITS, 16>(seal_rec, sm.ring[0], lane);
-      wait_page<NHI, BITS>(0);
-      attend_page(sm.ring[0], true);
-      wave_lds_sync();
+  // ---- the tail wave: the last attended page (sealed by this call, or cut by the bound) -------
+  if (tail_wave && extra_page) {
+    if (new_page) {
+      if (seal_rec != nullptr) {  // read the record back through the device coherence point
+        wait_lgkm0();  // the quantizer's LDS reads are done before the ring is refilled
+        compiler_fence();
+        wait_vmcnt<0>();  // the record's stores are complete
+        compiler_fence();
+        dma_record<NHI, BITS, 16>(seal_rec, sm.ring[0], lane);
+        wait_page<NHI, BITS>(0);
+        attend_page(sm.ring[0], true, last_lim);
+        wave_lds_sync();
+      }
+    } else {
+      const int phys = p.block_table[page_row + P - 1];  // wave-uniform
+      if (phys >= 0 && phys < np32) {
+        wait_lgkm0();  // the loop's LDS reads are done before the ring is refilled
+        compiler_fence();
+        dma_record<NHI, BITS>(rec_of(phys), sm.ring[0], lane);
+        wait_page<NHI, BITS>(0);
+        attend_page(sm.ring[0], true, last_lim);
+        wave_lds_sync();
+      }
     }
   }
 
@@ -1005,11 +1081,10 @@ static long wgs_per_cu(long W, int wmax) {
 // of resident workgroups times (pages per wave + 2), the 2 standing for a
 // round's start and merge.  Only the workgroup size changes, so the workspace
 // (sized by n_wg) does not.
-static SplitPlan pack_workgroups(SplitPlan plan, long P, long units, int wmax) {
-  constexpr long kCus = 256;
-  if (plan.n_wg != 1 || plan.wg_waves <= 4 || plan.wg_waves >= wmax || units <= kCus) return plan;
+static SplitPlan pack_workgroups(SplitPlan plan, long P, long units, int wmax, long cus) {
+  if (plan.n_wg != 1 || plan.wg_waves <= 4 || plan.wg_waves >= wmax || units <= cus) return plan;
   auto cost = [&](long W) {
-    const long per_round = kCus * wgs_per_cu(W, wmax);
+    const long per_round = cus * wgs_per_cu(W, wmax);
     return (units + per_round - 1) / per_round * (max_range(P, 1, W) + 2);
   };
   long best = plan.wg_waves, best_cost = cost(best);
@@ -1025,10 +1100,10 @@ static SplitPlan pack_workgroups(SplitPlan plan, long P, long units, int wmax) {
   return plan;
 }
 
-SplitPlan plan_splits(int batch, int n_kv_heads, int n_head_groups, int max_seq_len, int wmax) {
+SplitPlan plan_splits(int batch, int n_kv_heads, int n_head_groups, int max_seq_len, int wmax, int cus) {
   const long P = max_seq_len / kPageTokens;
   const long units = (long)batch * n_kv_heads * n_head_groups;
-  const long resident = (long)wmax * 256;  // waves: up to 3 per SIMD on 256 CUs, as LDS allows
+  const long resident = (long)wmax * cus;  // waves: up to 3 per SIMD on every CU, as LDS allows
   long wpu = resident / units;         // waves per unit, the tail wave included
   if (wpu > P + 1) wpu = P + 1;        // at least one page per page wave
   if (wpu < 2) wpu = 2;
@@ -1043,7 +1118,7 @@ SplitPlan plan_splits(int batch, int n_kv_heads, int n_head_groups, int max_seq_
     // grows, and for every supported length (P <= 4096) it stops well
     // before 16 x 12 waves
     if (max_range(P, n_wg, wg_waves) <= 64 || n_wg * wg_waves >= (long)kMaxWg * wmax)
-      return pack_workgroups(SplitPlan{(int)n_wg, (int)wg_waves}, P, units, wmax);
+      return pack_workgroups(SplitPlan{(int)n_wg, (int)wg_waves}, P, units, wmax, cus);
     ++wpu;
   }
 }

@@ -162,8 +162,11 @@ struct DecodeWorkspace {
   size_t partials, counters, seq_counters, seal_scratch, total;
 };
 
+// The plan for `cus` compute units; the workspace layout always for
+// kitty::kMaxCus, whose plan needs at least as many workgroups (the plan is
+// non-decreasing in the CU count), so one workspace size serves every device.
 static int decode_shape(const kitty_config_t* cfg, int32_t batch, int32_t n_q_heads, int32_t max_seq_len,
-                        kitty::SplitPlan* plan, int* n_head_groups, DecodeWorkspace* ws) {
+                        int cus, kitty::SplitPlan* plan, int* n_head_groups, DecodeWorkspace* ws) {
   if (batch < 1 || batch > 65535) return fail(KITTY_ERR_INVALID_ARG, "batch %d out of range [1, 65535]", batch);
   if (n_q_heads < 1 || n_q_heads % cfg->n_kv_heads != 0)
     return fail(KITTY_ERR_INVALID_ARG, "n_q_heads %d must be a positive multiple of n_kv_heads %d", n_q_heads,
@@ -174,10 +177,12 @@ static int decode_shape(const kitty_config_t* cfg, int32_t batch, int32_t n_q_he
   const int G = n_q_heads / cfg->n_kv_heads;
   *n_head_groups = (G + 3) / 4;
   if ((long)cfg->n_kv_heads * *n_head_groups > 65535) return fail(KITTY_ERR_INVALID_ARG, "too many heads");
-  *plan = kitty::plan_splits(batch, cfg->n_kv_heads, *n_head_groups, max_seq_len,
-                             kitty::decode_max_wg_waves(cfg->n_hi, cfg->lo_bit));
+  const int wmax = kitty::decode_max_wg_waves(cfg->n_hi, cfg->lo_bit);
+  *plan = kitty::plan_splits(batch, cfg->n_kv_heads, *n_head_groups, max_seq_len, wmax, cus);
+  const kitty::SplitPlan widest = kitty::plan_splits(batch, cfg->n_kv_heads, *n_head_groups, max_seq_len, wmax,
+                                                     kitty::kMaxCus);
   auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
-  const size_t part = (size_t)batch * n_q_heads * plan->n_wg * kitty::kPartialStride * sizeof(float);
+  const size_t part = (size_t)batch * n_q_heads * widest.n_wg * kitty::kPartialStride * sizeof(float);
   const size_t cnt = (size_t)batch * cfg->n_kv_heads * *n_head_groups * sizeof(int);
   const size_t seqc = (size_t)batch * kitty::kSeqCounterStride * sizeof(int);
   const size_t seal = (size_t)batch * cfg->n_kv_heads * (*n_head_groups - 1) * kitty::rec_bytes(kitty::boost_slots(cfg->n_hi), cfg->lo_bit);
@@ -196,8 +201,35 @@ int kitty_decode_workspace_bytes(const kitty_config_t* cfg, int32_t batch, int32
   kitty::SplitPlan plan;
   int nhg;
   DecodeWorkspace ws;
-  if (int r = decode_shape(cfg, batch, n_q_heads, max_seq_len, &plan, &nhg, &ws)) return r;
+  if (int r = decode_shape(cfg, batch, n_q_heads, max_seq_len, kitty::kMaxCus, &plan, &nhg, &ws)) return r;
   *out = ws.total;
+  return ok();
+}
+
+// Compute units of the device a stream runs on (at most kitty::kMaxCus), or
+// 0 on failure.
+static int stream_cus(hipStream_t stream) {
+  int dev = 0, cus = 0;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess && hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) return 0;
+  return cus < kitty::kMaxCus ? cus : kitty::kMaxCus;
+}
+
+int kitty_decode_plan(const kitty_config_t* cfg, int32_t batch, int32_t n_q_heads, int32_t max_seq_len,
+                      int32_t n_cus, int32_t* out) {
+  if (int r = check_config(cfg)) return r;
+  if (!out) return fail(KITTY_ERR_INVALID_ARG, "out is null");
+  if (n_cus < 0 || n_cus > kitty::kMaxCus) return fail(KITTY_ERR_INVALID_ARG, "n_cus %d out of range [0, %d]", n_cus, kitty::kMaxCus);
+  kitty::SplitPlan plan;
+  int nhg;
+  DecodeWorkspace ws;
+  if (int r = decode_shape(cfg, batch, n_q_heads, max_seq_len, kitty::kMaxCus, &plan, &nhg, &ws)) return r;
+  int cus = n_cus;
+  if (cus == 0 && (cus = stream_cus(nullptr)) == 0) return fail(KITTY_ERR_HIP, "no device to read the compute unit count from");
+  if (int r = decode_shape(cfg, batch, n_q_heads, max_seq_len, cus, &plan, &nhg, &ws)) return r;
+  out[0] = plan.n_wg;
+  out[1] = plan.wg_waves;
+  out[2] = kitty::decode_max_wg_waves(cfg->n_hi, cfg->lo_bit);
   return ok();
 }
 
@@ -213,10 +245,13 @@ static int decode_launch(const kitty_config_t* cfg, const kitty_kv_view_t* kv, c
   kitty::SplitPlan plan;
   int nhg;
   DecodeWorkspace ws;
-  if (int r = decode_shape(cfg, kv->batch, n_q_heads, max_seq_len, &plan, &nhg, &ws)) return r;
+  if (int r = decode_shape(cfg, kv->batch, n_q_heads, max_seq_len, kitty::kMaxCus, &plan, &nhg, &ws)) return r;
   if (!workspace || !aligned(workspace, 256)) return fail(KITTY_ERR_INVALID_ARG, "workspace null or not 256-byte aligned");
   if (workspace_bytes < ws.total)
     return fail(KITTY_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, ws.total);
+  const int cus = stream_cus(static_cast<hipStream_t>(stream));
+  if (cus == 0) return fail(KITTY_ERR_HIP, "cannot read the compute unit count of the stream's device");
+  if (cus != kitty::kMaxCus && decode_shape(cfg, kv->batch, n_q_heads, max_seq_len, cus, &plan, &nhg, &ws)) return KITTY_ERR_INVALID_ARG;
   uint8_t* wsb = static_cast<uint8_t*>(workspace);
   kitty::DecodeParams p{};
   p.pages = static_cast<uint8_t*>(kv->pages);

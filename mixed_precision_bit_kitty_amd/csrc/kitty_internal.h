@@ -156,8 +156,12 @@ struct SplitPlan {
   int n_wg;
   int wg_waves;
 };
-// wmax: waves per workgroup that the record size allows (decode_max_wg_waves)
-SplitPlan plan_splits(int batch, int n_kv_heads, int n_head_groups, int max_seq_len, int wmax);
+// wmax: waves per workgroup that the record size allows (decode_max_wg_waves);
+// cus: compute units the launch may use.  Every quantity is non-decreasing in
+// max_seq_len and in cus, so a workspace sized for a bound and for
+// kMaxCus serves every shorter call on any device with at most kMaxCus CUs.
+SplitPlan plan_splits(int batch, int n_kv_heads, int n_head_groups, int max_seq_len, int wmax, int cus);
+constexpr int kMaxCus = 256;  // an MI355X (gfx950) has 256 compute units
 int decode_max_wg_waves(int n_hi, int lo_bit);
 
 constexpr int kKeyStatsBytes = 8192;  // running-mode state of one (sequence, KV head)

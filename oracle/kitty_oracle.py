@@ -731,16 +731,19 @@ def attention_f64(q, khat, vhat):
     return out
 
 
-def decode_attention(cache, q, precision="f32", heads=None):
+def decode_attention(cache, q, precision="f32", heads=None, max_len=None):
     """Decode attention for every sequence of the cache: q fp16 [B, Hq, D]
     -> float32 [B, Hq, D].  ``heads`` (optional) restricts to a list of
-    KV heads; the other outputs stay zero."""
+    KV heads; the other outputs stay zero.  ``max_len`` (optional) bounds
+    the tokens attended: the first min(seq_len, max_len) of each sequence."""
     B, Hq, D = q.shape
     out = np.zeros((B, Hq, D), _F32 if precision == "f32" else np.float64)
     G = Hq // cache.n_kv_heads
     fn = attention_f32 if precision == "f32" else attention_f64
     for b in range(B):
         kh, vh = cache.dequant_sequence(b)
+        if max_len is not None:
+            kh, vh = kh[:, :max_len], vh[:, :max_len]
         hs = range(cache.n_kv_heads) if heads is None else heads
         for h in hs:
             out[b, h * G:(h + 1) * G] = fn(q[b, h * G:(h + 1) * G], kh[h:h + 1], vh[h:h + 1])

@@ -18,7 +18,7 @@ FAKE = 0x7F0000000000  # an aligned non-null address that is never dereferenced
 
 def test_exports_every_declared_symbol():
     names = B.declared_symbols()
-    assert len(names) == 12
+    assert len(names) == 14
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -85,8 +85,9 @@ def test_decode_waves_per_workgroup():
     """Waves per decode workgroup that the per-wave LDS (a ring of two
     records) allows on one CU: twelve for 2-bit records, fewer for the
     larger 4-bit ones."""
-    f = ctypes.CDLL(LIB)._ZN5kitty19decode_max_wg_wavesEii
-    f.restype, f.argtypes = ctypes.c_int, [ctypes.c_int32, ctypes.c_int32]
+    def f(n_hi, lo_bit):
+        return B.kitty_decode_plan(B.config(8, n_hi, lo_bit=lo_bit), 1, 32, 4096, 256)[2]
+
     for n_hi in range(0, 129, 16):
         assert f(n_hi, 2) == 12
         w4 = f(n_hi, 4)
@@ -243,10 +244,13 @@ def test_decode_plan_fits_page_id_register():
     """The decode split plan (an internal C++ function of the library) never
     gives a page wave more than 64 pages, the width of the register that
     holds its page ids, under the kernel's age-weighted page shares."""
-    lib = ctypes.CDLL(LIB)
-    f = lib._ZN5kitty11plan_splitsEiiiii
-    f.restype = ctypes.c_uint64
-    f.argtypes = [ctypes.c_int32] * 5
+    def f(batch, hkv, hg, msl, wmax, cus=256):
+        # a configuration whose records allow wmax waves per workgroup
+        cfg = {12: B.config(hkv, 32), 11: B.config(hkv, 32, lo_bit=4), 10: B.config(hkv, 64, lo_bit=4),
+               9: B.config(hkv, 128, lo_bit=4)}[wmax]
+        n_wg, W, wm = B.kitty_decode_plan(cfg, batch, 4 * hg * hkv, msl, cus)
+        assert wm == wmax
+        return n_wg | (W << 32)
 
     def weight(i):
         return 9 if i < 4 else (7 if i < 8 else 5)
@@ -299,3 +303,44 @@ def test_running_mode_arguments():
     page = B.config(8, 32)
     assert B.kitty_record_bytes(run) == B.kitty_record_bytes(page)
     assert B.kitty_decode_workspace_bytes(run, 4, 32, 4096) == B.kitty_decode_workspace_bytes(page, 4, 32, 4096)
+
+
+def test_decode_plan_on_fewer_compute_units():
+    """A device with fewer compute units plans at most as many workgroups per
+    unit as the full 256-CU MI355X, so the workspace (always sized for 256
+    CUs) holds every plan's partials; the plan hook validates like the
+    workspace query."""
+    for cfg in (B.config(8, 32), B.config(8, 13, lo_bit=4), B.config(2, 128)):
+        for batch, hq, msl in ((1, 32, 131103), (4, 32, 32768), (16, 32, 4096), (128, 32, 8192), (3, 16, 999)):
+            full = B.kitty_decode_plan(cfg, batch, hq, msl, 256)
+            for cus in (1, 32, 80, 128, 255):
+                n_wg, W, wm = B.kitty_decode_plan(cfg, batch, hq, msl, cus)
+                assert 1 <= n_wg <= full[0] and 2 <= W <= wm == full[2], (batch, hq, msl, cus)
+    lib = B.load()
+    out = (ctypes.c_int32 * 3)()
+    cfg = B.config(8, 32)
+    assert lib.kitty_decode_plan(ctypes.byref(cfg), 4, 32, 4096, 257, out) == B.KITTY_ERR_INVALID_ARG
+    assert lib.kitty_decode_plan(ctypes.byref(cfg), 4, 30, 4096, 256, out) == B.KITTY_ERR_INVALID_ARG
+    assert lib.kitty_decode_plan(ctypes.byref(cfg), 4, 32, 4096 * 32 + 32, 256, out) == B.KITTY_ERR_UNSUPPORTED
+    assert lib.kitty_decode_plan(ctypes.byref(cfg), 4, 32, 4096, 256, None) == B.KITTY_ERR_INVALID_ARG
+
+
+def test_read_ceiling_rejects_bad_arguments_before_launching():
+    """The measurement entry point (include/kitty_bench.h) validates its
+    arguments before any HIP call (none of these reach a launch)."""
+    lib = B.load_bench()
+    ok_args = dict(src=FAKE, nbytes=1 << 30, mode=0, waves=16, depth=4, sink=FAKE, sink_len=1 << 16)
+
+    def call(**kw):
+        a = dict(ok_args, **kw)
+        return lib.kitty_read_ceiling(a["src"], a["nbytes"], a["mode"], a["waves"], a["depth"], a["sink"],
+                                      a["sink_len"], None)
+
+    bad = B.KITTY_ERR_INVALID_ARG
+    assert call(src=None) == bad and call(sink=None) == bad and call(src=FAKE + 8) == bad
+    assert call(nbytes=0) == bad and call(nbytes=1000) == bad
+    assert call(mode=2) == bad and call(mode=-1) == bad
+    assert call(waves=2) == bad and call(waves=33) == bad and call(waves=6) == bad
+    assert call(depth=3) == bad and call(depth=16) == bad
+    assert call(mode=1, waves=13, depth=2) == bad and call(mode=1, waves=12, depth=5) == bad
+    assert call(mode=1, waves=8, depth=2, nbytes=3344) == bad  # not one whole record

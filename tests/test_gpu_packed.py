@@ -3,8 +3,6 @@ head, head group) units than CUs, so the split plan picks workgroups of 3, 4
 or 12 waves.  Both bit-width pairs and both ranking modes; the fused step and
 append + decode attention against each other and against the oracle (records
 bit-exact, attention within 2e-3)."""
-import ctypes
-
 import numpy as np
 import pytest
 
@@ -26,12 +24,8 @@ def _gpu():
 
 def _plan(batch, hkv, hq, msl, n_hi, lo_bit):
     from mixed_precision_bit_kitty_amd import binding as B
-    so = ctypes.CDLL(B.LIB_PATH)
-    plan, wmax = so._ZN5kitty11plan_splitsEiiiii, so._ZN5kitty19decode_max_wg_wavesEii
-    plan.restype, plan.argtypes = ctypes.c_uint64, [ctypes.c_int32] * 5
-    wmax.restype, wmax.argtypes = ctypes.c_int, [ctypes.c_int32] * 2
-    r = plan(batch, hkv, -(-(hq // hkv) // 4), msl, wmax(n_hi, lo_bit))
-    return r & 0xFFFFFFFF, r >> 32
+    n_wg, waves, _ = B.kitty_decode_plan(B.config(hkv, n_hi, lo_bit=lo_bit), batch, hq, msl)
+    return n_wg, waves
 
 
 # (batch, KV heads, query heads, longest prompt, n_hi, lo_bit, ranking, waves per workgroup)

@@ -63,11 +63,10 @@ def _run(w, lens, steps, ctx, msl=None, check_every=1, n_hi=32):
         if seals or t % check_every == 0 or t == steps - 1:
             assert np.array_equal(host(fused.pool), host(split.pool)), f"step {t}: page pools differ"
             compare_tails(fused, oc)
-            if msl >= int(oc.seq_len.max()):
-                ref = O.decode_attention(oc, x["q_new"][t])
-                err = float(np.abs(a - ref).max())
-                worst = max(worst, err)
-                assert err <= ATOL, f"step {t}: max abs err {err}"
+            ref = O.decode_attention(oc, x["q_new"][t], max_len=msl)
+            err = float(np.abs(a - ref).max())
+            worst = max(worst, err)
+            assert err <= ATOL, f"step {t}: max abs err {err}"
     compare_records(fused, oc)
     return worst
 
@@ -92,17 +91,11 @@ def test_step_several_workgroups():
 def test_step_packed_workgroups():
     # 40 sequences x 8 KV heads = 320 units, more than the 256 CUs hold at
     # one workgroup each: the plan packs 4-wave workgroups, three per CU
-    import ctypes
     from mixed_precision_bit_kitty_amd import binding as B
-    so = ctypes.CDLL(B.LIB_PATH)
-    plan, wmax = so._ZN5kitty11plan_splitsEiiiii, so._ZN5kitty19decode_max_wg_wavesEii
-    plan.restype, plan.argtypes = ctypes.c_uint64, [ctypes.c_int32] * 5
-    wmax.restype, wmax.argtypes = ctypes.c_int, [ctypes.c_int32] * 2
     rng = np.random.default_rng(41)
     lens = [int(n) for n in rng.integers(250, 300, 40)]
     steps = 34
-    r = plan(40, 8, 1, max(lens) + steps, wmax(32, 2))
-    assert (r & 0xFFFFFFFF, r >> 32) == (1, 4)
+    assert B.kitty_decode_plan(B.config(8, 32), 40, 32, max(lens) + steps)[:2] == (1, 4)
     worst = _run(synth.LLAMA3_8B, lens, steps, 300, check_every=8)
     print(f"fused step, packed 4-wave workgroups: max abs err {worst:.3g}")
 
@@ -122,10 +115,21 @@ def test_step_capacity_bound():
 
 
 def test_step_bound_below_length():
-    # a bound below the new length: tokens past it are ignored, in both paths
-    # alike, also on the step that seals page 1 (63 -> 64 with the bound at 40)
+    # a bound below the new length: the first 40 tokens are attended, in both
+    # paths alike and as the oracle truncated at the bound, also on the step
+    # that seals page 1 (63 -> 64) and once page 1 is sealed (the bound then
+    # cuts a sealed page, not the tail)
     w = synth.LLAMA3_8B.with_(n_kv_heads=2, n_q_heads=8)
     _run(w, [60, 20], 6, 64, msl=40)
+
+
+@pytest.mark.parametrize("msl", [31, 32, 64, 75, 100])
+def test_step_bound_inside_sealed_pages(msl):
+    # sequences of 130-200 tokens (four to six sealed pages) under a bound
+    # that falls inside an older sealed page, on a page boundary or inside
+    # the tail: exactly the first min(length, bound) tokens are attended
+    w = synth.LLAMA3_8B.with_(n_kv_heads=2, n_q_heads=8)
+    _run(w, [130, 200, 95, 20], 5, 200, msl=msl)
 
 
 @pytest.mark.parametrize("n_hi", [0, 16, 128])
