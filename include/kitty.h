@@ -21,7 +21,8 @@
  *    touches the device.
  *  - Every pointer named "device" is HIP device memory owned by the caller.
  *    The library allocates nothing, keeps no global mutable state besides the
- *    thread-local error text, and never synchronizes: all work is enqueued
+ *    thread-local error text (and, for kitty_decode_step_noalloc, one static
+ *    device array per GPU), and never synchronizes: all work is enqueued
  *    on `stream` (a hipStream_t; NULL = the default stream) and is
  *    asynchronous to the host.
  *  - fp16 arrays are IEEE binary16 passed as uint16_t.
@@ -224,6 +225,25 @@ int kitty_decode_attention(const kitty_config_t* cfg, const kitty_kv_view_t* kv,
 int kitty_decode_step(const kitty_config_t* cfg, const kitty_kv_view_t* kv, const uint16_t* k_new,
                       const uint16_t* v_new, const uint16_t* q, int32_t n_q_heads, int32_t max_seq_len,
                       float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The fused decode step for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, and harnesses that
+ * forbid hipMalloc.  Exactly kitty_decode_step, except that the workspace is
+ * the library's own: a static device array of KITTY_NOALLOC_SCRATCH_BYTES
+ * per GPU, held from the first call on that GPU until the process ends.  It
+ * allocates nothing (no hipMalloc, hipFree or allocating library call).  The
+ * stream must belong to the current device.  Each call first clears the
+ * arrival counters in that array with a small kernel on `stream` (so two
+ * launches per call), then runs the decode step.  Every call on a GPU shares
+ * that GPU's array: calls that overlap in time on one GPU (other streams,
+ * other threads) race and give undefined results; calls ordered on one
+ * stream are safe.  A shape whose workspace (kitty_decode_workspace_bytes)
+ * exceeds KITTY_NOALLOC_SCRATCH_BYTES returns KITTY_ERR_WORKSPACE before any
+ * HIP call; the other errors are those of kitty_decode_step. */
+#define KITTY_NOALLOC_SCRATCH_BYTES (16u << 20)
+int kitty_decode_step_noalloc(const kitty_config_t* cfg, const kitty_kv_view_t* kv, const uint16_t* k_new,
+                              const uint16_t* v_new, const uint16_t* q, int32_t n_q_heads, int32_t max_seq_len,
+                              float* out, void* stream);
 
 /* Page pool for ragged serving (the page-centric layout of the Abstract
  * lets sequences of any length share one pool).  Host only: these calls

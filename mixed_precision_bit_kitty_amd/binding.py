@@ -102,6 +102,7 @@ def load(path=None):
         "kitty_decode_plan": ([cfgp, i32, i32, i32, i32, P(i32)], ctypes.c_int),
         "kitty_decode_attention": ([cfgp, viewp, vp, i32, i32, vp, vp, sz, vp], ctypes.c_int),
         "kitty_decode_step": ([cfgp, viewp, vp, vp, vp, i32, i32, vp, vp, sz, vp], ctypes.c_int),
+        "kitty_decode_step_noalloc": ([cfgp, viewp, vp, vp, vp, i32, i32, vp, vp], ctypes.c_int),
         "kitty_pool_init": ([P(kitty_pool_t), vp, ctypes.c_int64], ctypes.c_int),
         "kitty_pool_reserve": ([P(kitty_pool_t), vp, i32, i32], ctypes.c_int),
         "kitty_pool_release": ([P(kitty_pool_t), vp, i32], ctypes.c_int),
@@ -211,6 +212,11 @@ def kitty_decode_step(cfg, view, k_new, v_new, q, n_q_heads, max_seq_len, out, w
     _check(load().kitty_decode_step(ctypes.byref(cfg), ctypes.byref(view), _ptr(k_new), _ptr(v_new), _ptr(q),
                                     n_q_heads, max_seq_len, _ptr(out), _ptr(workspace), nbytes,
                                     _stream(stream)))
+
+
+def kitty_decode_step_noalloc(cfg, view, k_new, v_new, q, n_q_heads, max_seq_len, out, stream=None):
+    _check(load().kitty_decode_step_noalloc(ctypes.byref(cfg), ctypes.byref(view), _ptr(k_new), _ptr(v_new),
+                                            _ptr(q), n_q_heads, max_seq_len, _ptr(out), _stream(stream)))
 
 
 class PagePool:

@@ -1123,6 +1123,19 @@ SplitPlan plan_splits(int batch, int n_kv_heads, int n_head_groups, int max_seq_
   }
 }
 
+// Fills n 32-bit words with zero (a kernel rather than hipMemsetAsync, so
+// that a caller may capture it in a HIP graph).
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+hipError_t launch_zero_words(uint32_t* p, size_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const size_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   switch (boost_slots(p.n_hi)) {  // instantiations by boost slots; the seal ranks p.n_hi channels
     case 0: return launch_decode_t<0>(p, stream);

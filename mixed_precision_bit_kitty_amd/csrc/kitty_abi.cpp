@@ -6,6 +6,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "kitty_internal.h"
@@ -299,6 +300,74 @@ int kitty_decode_step(const kitty_config_t* cfg, const kitty_kv_view_t* kv, cons
     return fail(KITTY_ERR_INVALID_ARG, "k_new / v_new null or not 16-byte aligned");
   return decode_launch(cfg, kv, k_new, v_new, q, n_q_heads, max_seq_len, out, workspace, workspace_bytes, stream,
                        "decode_step");
+}
+
+}  // extern "C"
+
+// ---- the fused step without a caller workspace -----------------------------------
+// The decode workspace of kitty_decode_step_noalloc (split partials, arrival
+// counters, seal records) lives in this array, one copy per GPU, held until
+// the process ends.  Host code never uses its name as an address: the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[KITTY_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // the device address of `scratch` on each device, once looked up
+
+// The device address of `scratch` on device `dev` (the current device).
+int scratch_on(int dev, void** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(KITTY_ERR_HIP, "hipGetSymbolAddress of the decode scratch failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KITTY_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int kitty_decode_step_noalloc(const kitty_config_t* cfg, const kitty_kv_view_t* kv, const uint16_t* k_new,
+                              const uint16_t* v_new, const uint16_t* q, int32_t n_q_heads, int32_t max_seq_len,
+                              float* out, void* stream) {
+  // every argument and the scratch size are checked before any HIP call
+  if (int r = check_config(cfg)) return r;
+  if (int r = check_view(cfg, kv)) return r;
+  if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16))
+    return fail(KITTY_ERR_INVALID_ARG, "k_new / v_new null or not 16-byte aligned");
+  if (!q || !aligned(q, 16)) return fail(KITTY_ERR_INVALID_ARG, "q null or not 16-byte aligned");
+  if (!out || !aligned(out, 4)) return fail(KITTY_ERR_INVALID_ARG, "out null or misaligned");
+  kitty::SplitPlan plan;
+  int nhg;
+  DecodeWorkspace ws;
+  if (int r = decode_shape(cfg, kv->batch, n_q_heads, max_seq_len, kitty::kMaxCus, &plan, &nhg, &ws)) return r;
+  if (ws.total > KITTY_NOALLOC_SCRATCH_BYTES)
+    return fail(KITTY_ERR_WORKSPACE, "this shape needs %zu bytes of decode scratch, more than the %zu the "
+                "allocation-free step holds (use kitty_decode_step with a workspace)", ws.total,
+                (size_t)KITTY_NOALLOC_SCRATCH_BYTES);
+  int dev = -1, sdev = -1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(KITTY_ERR_HIP, "no current device (or device id beyond %d)", kMaxDevices - 1);
+  if (hipStreamGetDevice(s, &sdev) == hipSuccess && sdev != dev)
+    return fail(KITTY_ERR_INVALID_ARG, "the stream belongs to device %d, not the current device %d", sdev, dev);
+  void* ptr = nullptr;
+  if (int r = scratch_on(dev, &ptr)) return r;
+  // the arrival counters start at zero: clear them (a completed call also
+  // leaves them zero, but the layout moves with the shape)
+  uint8_t* base = static_cast<uint8_t*>(ptr);
+  (void)hipGetLastError();
+  const hipError_t e = kitty::launch_zero_words(reinterpret_cast<uint32_t*>(base + ws.counters),
+                                                (ws.seal_scratch - ws.counters) / 4, s);
+  if (e != hipSuccess) return fail(KITTY_ERR_HIP, "decode scratch clear failed: %s", hipGetErrorString(e));
+  return decode_launch(cfg, kv, k_new, v_new, q, n_q_heads, max_seq_len, out, ptr, KITTY_NOALLOC_SCRATCH_BYTES,
+                       stream, "decode_step_noalloc");
 }
 
 

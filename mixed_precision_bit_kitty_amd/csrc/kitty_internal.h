@@ -170,5 +170,6 @@ constexpr int kMaxRunningTokens = 1 << 23;  // running mode: exact scores stay b
 hipError_t launch_quantize(const QuantizeParams& p, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_zero_words(uint32_t* p, size_t n, hipStream_t stream);  // p[0..n) = 0 by a kernel
 
 }  // namespace kitty

@@ -18,7 +18,7 @@ FAKE = 0x7F0000000000  # an aligned non-null address that is never dereferenced
 
 def test_exports_every_declared_symbol():
     names = B.declared_symbols()
-    assert len(names) == 14
+    assert len(names) == 15
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -344,3 +344,28 @@ def test_read_ceiling_rejects_bad_arguments_before_launching():
     assert call(depth=3) == bad and call(depth=16) == bad
     assert call(mode=1, waves=13, depth=2) == bad and call(mode=1, waves=12, depth=5) == bad
     assert call(mode=1, waves=8, depth=2, nbytes=3344) == bad  # not one whole record
+
+
+def test_noalloc_step_rejects_before_any_hip_call():
+    """The allocation-free step validates like kitty_decode_step and refuses
+    a shape whose workspace exceeds its static scratch, before any HIP call
+    (so these run without a GPU)."""
+    lib = B.load()
+    cfg = B.config(8, 32)
+    v = _view(batch=4)
+
+    def call(view=v, k=FAKE, vv=FAKE, q=FAKE, hq=32, msl=4096, out=FAKE, c=cfg):
+        return lib.kitty_decode_step_noalloc(ctypes.byref(c), ctypes.byref(view), k, vv, q, hq, msl, out, None)
+
+    assert call(k=None) == B.KITTY_ERR_INVALID_ARG
+    assert call(vv=FAKE + 2) == B.KITTY_ERR_INVALID_ARG
+    assert call(q=None) == B.KITTY_ERR_INVALID_ARG
+    assert call(out=None) == B.KITTY_ERR_INVALID_ARG
+    assert call(hq=30) == B.KITTY_ERR_INVALID_ARG
+    assert call(msl=4096 * 32 + 32) == B.KITTY_ERR_UNSUPPORTED
+    # a shape beyond the 16 MiB scratch: many sequences at the longest length
+    big = _view(batch=4096, max_pages=4097)
+    need = B.kitty_decode_workspace_bytes(cfg, 4096, 32, 4096 * 32)
+    assert need > 16 << 20
+    assert call(view=big, msl=4096 * 32) == B.KITTY_ERR_WORKSPACE
+    assert "scratch" in lib.kitty_last_error().decode()
