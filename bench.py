@@ -453,7 +453,8 @@ def bench_ceiling(args):
 
 def _workload_key(args, w, B):
     """Name of a configuration in the committed counter summaries."""
-    return args.workload + ("" if B == w.batch else f"_b{B}") + _lo_suffix(args)
+    group = "" if args.q_heads is None else f"_g{w.n_q_heads // w.n_kv_heads}"
+    return args.workload + ("" if B == w.batch else f"_b{B}") + group + _lo_suffix(args)
 
 
 def main():
@@ -478,6 +479,8 @@ def main():
                     help="bit-width pair: 2 = (hi_bit 4, lo_bit 2), 4 = (hi_bit 8, lo_bit 4)")
     ap.add_argument("--rank-mode", default="page", choices=["page", "running"],
                     help="boosted channels by each page's variance (page) or the head's running variance (running)")
+    ap.add_argument("--q-heads", type=int, default=None,
+                    help="override the workload's query heads (a multiple of its KV heads: GQA group = q_heads / kv_heads)")
     ap.add_argument("--hi-fraction", type=float, default=None,
                     help="override the workload's hi_fraction (n_hi = hi_fraction x 128)")
     ap.add_argument("--quantize", action="store_true",
@@ -499,6 +502,10 @@ def main():
     w = _workload(args.workload)
     if args.hi_fraction is not None:
         w = w.with_(hi_fraction=args.hi_fraction)
+    if args.q_heads is not None:
+        if args.q_heads < w.n_kv_heads or args.q_heads % w.n_kv_heads:
+            ap.error(f"--q-heads must be a positive multiple of the workload's {w.n_kv_heads} KV heads")
+        w = w.with_(n_q_heads=args.q_heads)
     if args.quantize:
         return bench_quantize(args, w)
     B = args.batch or (max(w.sweep) if args.workload == "batch_sweep" else w.batch)
@@ -540,7 +547,7 @@ def main():
         "roofline": roof,
     }
     default_run = (args.workload == "batch_sweep" and args.batch is None and not args.split and args.lo_bit == 2
-                   and args.rank_mode == "page" and args.hi_fraction is None)
+                   and args.rank_mode == "page" and args.hi_fraction is None and args.q_heads is None)
     if default_run and not args.no_context:
         # context beside the headline: the Llama-3-8B-shape step and the read-only ceiling
         wl = _workload("llama3_8b")
