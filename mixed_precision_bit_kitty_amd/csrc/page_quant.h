@@ -104,6 +104,17 @@ __device__ __forceinline__ float tree32(float (&a)[32]) {
   return a[0];
 }
 
+// The same tree from its second level: a holds the 16 first-level sums.
+__device__ __forceinline__ float tree16(float (&a)[32]) {
+#pragma clang fp contract(off)
+#pragma unroll
+  for (int s = 8; s >= 1; s >>= 1) {
+#pragma unroll
+    for (int i = 0; i < s; ++i) a[i] = a[2 * i] + a[2 * i + 1];
+  }
+  return a[0];
+}
+
 struct Step {
   float inv;     // 1 / step, or 0 for a zero step
   uint16_t s16;  // fp16 step
@@ -121,29 +132,55 @@ __device__ __forceinline__ Step make_step(float mn, float mx, float levels) {
   return st;
 }
 
-// clamp(rne((x - mn) * inv), 0, levels), inserted as byte `byte` of `into`.
-// t = (x - mn) * inv is >= 0 and finite (x >= mn, inv <= 2^24), and
-// min(rne(t), L) = rne(min(t, L)) for an integer L, so the clamp goes first
-// and v_cvt_pk_u8_f32 (round half to even, saturating to [0, 255]; checked
-// on gfx950) rounds and packs in one instruction.
-__device__ __forceinline__ uint32_t code_of(float x, float mn, float inv, float levels, uint32_t byte = 0, uint32_t into = 0) {
+// Float32 arithmetic on fp16 inputs without a separate conversion: one
+// v_fma_mix_f32 widens the fp16 operand (half HI of a 32-bit word) exactly
+// and rounds once, so it gives the value of converting first and then
+// subtracting or adding in float32.  (VALU-only inline asm: the compiler
+// does not form the mixed-precision FMA from a conversion and an add.)
+template <int HI>
+__device__ __forceinline__ float sub_h(uint32_t w, float c) {  // (float)half_HI(w) - c
+  float r;
+  if constexpr (HI) asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(c));
+  else asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(c));
+  return r;
+}
+template <int HI>
+__device__ __forceinline__ float add_hh(uint32_t a, uint32_t b) {  // (float)half_HI(a) + (float)half_HI(b)
+  float r;
+  if constexpr (HI) asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(a), "v"(b));
+  else asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[0,0,0] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// clamp(rne((x - mn) * inv), 0, levels) for the fp16 x in half HI of w,
+// inserted as byte `byte` of `into`.  t = (x - mn) * inv is >= 0 and finite
+// (x >= mn, inv <= 2^24), and min(rne(t), L) = rne(min(t, L)) for an integer
+// L, so the clamp goes first and v_cvt_pk_u8_f32 (round half to even,
+// saturating to [0, 255]; checked on gfx950) rounds and packs in one
+// instruction.
+template <int HI>
+__device__ __forceinline__ uint32_t code_of(uint32_t w, float mn, float inv, float levels, uint32_t byte = 0, uint32_t into = 0) {
 #pragma clang fp contract(off)
-  float t = (x - mn) * inv;
+  float t = sub_h<HI>(w, mn) * inv;
   t = fminf(t, levels);
   return __builtin_amdgcn_cvt_pk_u8_f32(t, byte, into);
 }
 
-// bytes 0, 2, 4, 6 of x (each a 2-bit code) -> bits 0, 2, 4, 6 of the result
-__device__ __forceinline__ uint32_t gather4(uint64_t x) {
-  x &= 0x0003000300030003ull;
-  x |= x >> 14;
-  x |= x >> 28;
-  return (uint32_t)x & 0xFFu;
+// Four 2-bit codes held in bytes of x (each byte <= 3) -> an 8-bit field:
+// two v_dot4_u32_u8 with byte weights 1, 4 (low dword) and 16, 64 (high
+// dword) on the two bytes ODD selects (bytes 0, 2 or 1, 3 of each dword).
+template <int ODD>
+__device__ __forceinline__ uint32_t field4(uint64_t x) {
+  constexpr uint32_t wl = ODD ? 0x04000100u : 0x00040001u, wh = ODD ? 0x40001000u : 0x00400010u;
+  return __builtin_amdgcn_udot4((uint32_t)(x >> 32), wh, __builtin_amdgcn_udot4((uint32_t)x, wl, 0u, false), false);
 }
-// code word from combos A, B given as 8 code bytes each (element e in byte e)
+// code word from combos A, B given as 8 code bytes each (element e in byte
+// e, every byte <= 3): element e of A at bit 16 (e & 1) + 2 (e >> 1), of B
+// 8 bits higher
 __device__ __forceinline__ uint32_t pack_word(uint64_t a, uint64_t b) {
-  return gather4(a) | (gather4(b) << 8) | (gather4(a >> 8) << 16) | (gather4(b >> 8) << 24);
+  return field4<0>(a) | (field4<0>(b) << 8) | (field4<1>(a) << 16) | (field4<1>(b) << 24);
 }
+constexpr uint64_t kLow2 = 0x0303030303030303ull;  // the low two bits of every byte
 
 // bytes 0, 2, 4, 6 of x (each a 4-bit code in its low nibble) -> bits 0, 4, 8, 12
 __device__ __forceinline__ uint32_t gather4_nib(uint64_t x) {
@@ -328,14 +365,12 @@ __device__ __forceinline__ void quantize_keys_wave(RowSrc ks, uint8_t* __restric
   // out as -0 whatever the order, so the extremes are made canonical once at
   // the end (-0 -> +0); the sums need no canonical zeros: a -0 input changes
   // neither m2 nor a code.
-  float x0[32], x1[32];
+  uint32_t xw[32];  // the fp16 pair (channels 2 lane, 2 lane + 1) of each token
   half2v kmn, kmx;
 #pragma unroll
   for (int t = 0; t < 32; ++t) {
-    const uint32_t w2 = *reinterpret_cast<const uint32_t*>(ks.row(t) + 2 * lane);
-    const half2v hv = __builtin_bit_cast(half2v, w2);
-    x0[t] = (float)hv[0];
-    x1[t] = (float)hv[1];
+    xw[t] = *reinterpret_cast<const uint32_t*>(ks.row(t) + 2 * lane);
+    const half2v hv = __builtin_bit_cast(half2v, xw[t]);
     kmn = t == 0 ? hv : hmin2(kmn, hv);
     kmx = t == 0 ? hv : hmax2(kmx, hv);
   }
@@ -355,18 +390,19 @@ __device__ __forceinline__ void quantize_keys_wave(RowSrc ks, uint8_t* __restric
   } else if (NHI == kHeadDim && n == kHeadDim) {
     h0 = h1 = true;
   } else {
+    // the tree's first level adds the fp16 inputs pairwise (tokens 2i, 2i + 1)
     float a[32];
 #pragma unroll
-    for (int t = 0; t < 32; ++t) a[t] = x0[t];
-    const float mu0 = tree32(a) * (1.0f / 32.0f);
+    for (int i = 0; i < 16; ++i) a[i] = add_hh<0>(xw[2 * i], xw[2 * i + 1]);
+    const float mu0 = tree16(a) * (1.0f / 32.0f);
 #pragma unroll
-    for (int t = 0; t < 32; ++t) { float d = x0[t] - mu0; a[t] = d * d; }
+    for (int t = 0; t < 32; ++t) { float d = sub_h<0>(xw[t], mu0); a[t] = d * d; }
     const float m2_0 = tree32(a);
 #pragma unroll
-    for (int t = 0; t < 32; ++t) a[t] = x1[t];
-    const float mu1 = tree32(a) * (1.0f / 32.0f);
+    for (int i = 0; i < 16; ++i) a[i] = add_hh<1>(xw[2 * i], xw[2 * i + 1]);
+    const float mu1 = tree16(a) * (1.0f / 32.0f);
 #pragma unroll
-    for (int t = 0; t < 32; ++t) { float d = x1[t] - mu1; a[t] = d * d; }
+    for (int t = 0; t < 32; ++t) { float d = sub_h<1>(xw[t], mu1); a[t] = d * d; }
     const float m2_1 = tree32(a);
     // m2 >= 0: its bit pattern orders like its value (bit 31 is clear)
     select_top<uint32_t, 30>(__builtin_bit_cast(uint32_t, m2_0), __builtin_bit_cast(uint32_t, m2_1), n, lane, h0, h1);
@@ -391,15 +427,17 @@ __device__ __forceinline__ void quantize_keys_wave(RowSrc ks, uint8_t* __restric
     if (lane >= n && lane < NHI) rec[off_idx(NHI, BITS) + lane] = 0;  // padding slots (n < NHI)
     if (lane + 64 >= n && lane + 64 < NHI) rec[off_idx(NHI, BITS) + lane + 64] = 0;
   }
-  // Codes go to LDS as bytes of which only the low BITS bits are read back:
-  // base = q >> BITS on a boosted channel, q elsewhere; boost = q (low bits).
+  // Codes go to LDS as bytes: base = q >> BITS on a boosted channel, q
+  // elsewhere (BITS bits); boost = q, of which only the low BITS bits are
+  // read back.
   const uint32_t sh0 = h0 ? (uint32_t)BITS : 0u, sh1 = h1 ? (uint32_t)BITS : 0u;
   uint8_t* const bst0 = lds_boost + (w0 ? pos0 : NHI);  // column NHI: a lane's discarded stores
   uint8_t* const bst1 = lds_boost + (w1 ? pos1 : NHI);
 #pragma unroll
   for (int t = 0; t < 32; ++t) {
-    const uint32_t q = code_of(x1[t], mn1, st1.inv, L1, 1, code_of(x0[t], mn0, st0.inv, L0));  // bytes q0, q1
-    const uint32_t base = __builtin_amdgcn_ubfe(q, sh0, 8) | ((q >> sh1) & 0xFF00u);
+    const uint32_t q = code_of<1>(xw[t], mn1, st1.inv, L1, 1, code_of<0>(xw[t], mn0, st0.inv, L0));  // bytes q0, q1
+    // exactly BITS bits per byte (the planes are packed without masking)
+    const uint32_t base = __builtin_amdgcn_ubfe(q, sh0, BITS) | (__builtin_amdgcn_ubfe(q, 8 + sh1, BITS) << 8);
     *reinterpret_cast<uint16_t*>(lds_base + t * 128 + 2 * lane) = (uint16_t)base;
     if (NHI > 0) {
       bst0[t * boost_row(NHI)] = (uint8_t)q;
@@ -457,7 +495,7 @@ __device__ __forceinline__ void quantize_keys_wave(RowSrc ks, uint8_t* __restric
           B &= m;
         }
         if (BITS == 2) {
-          *reinterpret_cast<uint32_t*>(bp + 4 * (lane * nf + bb)) = pack_word(A, B);
+          *reinterpret_cast<uint32_t*>(bp + 4 * (lane * nf + bb)) = pack_word(A & kLow2, B & kLow2);
         } else {
           const u32x2 pr = {pack_word4(A), pack_word4(B)};
           *reinterpret_cast<u32x2*>(bp + 8 * (lane * nf + bb)) = pr;
@@ -472,7 +510,7 @@ __device__ __forceinline__ void quantize_keys_wave(RowSrc ks, uint8_t* __restric
           B &= m;
         }
         if (BITS == 2) {
-          *reinterpret_cast<uint32_t*>(bp + 256 * nf + 4 * lane) = pack_word(A, B);
+          *reinterpret_cast<uint32_t*>(bp + 256 * nf + 4 * lane) = pack_word(A & kLow2, B & kLow2);
         } else {
           const u32x2 pr = {pack_word4(A), pack_word4(B)};
           *reinterpret_cast<u32x2*>(bp + 512 * nf + 8 * lane) = pr;
@@ -537,33 +575,49 @@ __device__ __forceinline__ void quantize_values_wave(RowSrc vs, uint8_t* __restr
     const int g = lane >> 4, u = lane & 15;
     const int c0 = 32 * g + u, c1 = c0 + 16;
     const floatx4* vstep = reinterpret_cast<const floatx4*>(lds + lds_vstep(NHI)) + 16 * g;  // two tokens per read
-    uint32_t a0[32], a1[32];
+    if constexpr (BITS == 2) {
+      // Element e of word w (token tau(w, e)) goes to byte e >> 1 of field
+      // f[w][2 (e & 1) + combo]; a field's four 2-bit codes become its 8 bits
+      // of the word with one v_dot4_u32_u8 (byte weights 1, 4, 16, 64).
+      uint32_t f[4][4] = {};
 #pragma unroll
-    for (int t2 = 0; t2 < 16; ++t2) {
-      const floatx4 st2 = vstep[t2];  // (1 / step, min) of tokens 2 t2 and 2 t2 + 1
+      for (int t2 = 0; t2 < 16; ++t2) {
+        const floatx4 st2 = vstep[t2];  // (1 / step, min) of tokens 2 t2 and 2 t2 + 1
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int t = 2 * t2 + k;
-        const _Float16* r = vs.row(t);
-        const float y0 = (float)r[c0];
-        const float y1 = (float)r[c1];
-        a0[t] = code_of(y0, st2[2 * k + 1], st2[2 * k], kLo);
-        a1[t] = code_of(y1, st2[2 * k + 1], st2[2 * k], kLo);  // codes <= 2^BITS - 1: no masking needed below
-      }
-    }
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      if (BITS == 2) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int t = tau_of(w, e);
-          const int sh = 16 * (e & 1) + 2 * (e >> 1);
-          word |= a0[t] << sh;
-          word |= a1[t] << (sh + 8);
+        for (int k = 0; k < 2; ++k) {
+          const int t = 2 * t2 + k, kap = kappa_of(t), w = kap >> 3, e = kap & 7;
+          const uint16_t* r = reinterpret_cast<const uint16_t*>(vs.row(t));
+          const uint32_t y0 = r[c0], y1 = r[c1];
+          uint32_t& fa = f[w][2 * (e & 1)];
+          uint32_t& fb = f[w][2 * (e & 1) + 1];
+          fa = code_of<0>(y0, st2[2 * k + 1], st2[2 * k], kLo, e >> 1, fa);
+          fb = code_of<0>(y1, st2[2 * k + 1], st2[2 * k], kLo, e >> 1, fb);
         }
+      }
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        constexpr uint32_t kW = 0x40100401u;
+        const uint32_t word = __builtin_amdgcn_udot4(f[w][0], kW, 0u, false) |
+                              (__builtin_amdgcn_udot4(f[w][1], kW, 0u, false) << 8) |
+                              (__builtin_amdgcn_udot4(f[w][2], kW, 0u, false) << 16) |
+                              (__builtin_amdgcn_udot4(f[w][3], kW, 0u, false) << 24);
         *reinterpret_cast<uint32_t*>(rec + off_v(NHI, BITS) + 16 * (16 * w + u) + 4 * g) = word;
-      } else {  // 4-bit: combo A (channel c0) at word 2g, combo B (c1) at 2g + 1 of a 32-byte chunk
+      }
+    } else {  // 4-bit: combo A (channel c0) at word 2g, combo B (c1) at 2g + 1 of a 32-byte chunk
+      uint32_t a0[32], a1[32];
+#pragma unroll
+      for (int t2 = 0; t2 < 16; ++t2) {
+        const floatx4 st2 = vstep[t2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int t = 2 * t2 + k;
+          const uint16_t* r = reinterpret_cast<const uint16_t*>(vs.row(t));
+          a0[t] = code_of<0>(r[c0], st2[2 * k + 1], st2[2 * k], kLo);
+          a1[t] = code_of<0>(r[c1], st2[2 * k + 1], st2[2 * k], kLo);  // codes <= 15: no masking needed below
+        }
+      }
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
         uint32_t wa = 0, wb = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {

@@ -33,11 +33,11 @@ def _diff_fields(got, want, n_hi, lo_bit):
     wk, wv = O.unpack_record(want, n_hi, lo_bit)
     out = []
     for key in gk:
-        d = int(np.sum(np.asarray(gk[key]).view(np.uint8) != np.asarray(wk[key]).view(np.uint8)))
+        d = int(np.sum(np.atleast_1d(gk[key]).view(np.uint8) != np.atleast_1d(wk[key]).view(np.uint8)))
         if d:
             out.append(f"{key}:{d}")
     for key in gv:
-        d = int(np.sum(np.asarray(gv[key]).view(np.uint8) != np.asarray(wv[key]).view(np.uint8)))
+        d = int(np.sum(np.atleast_1d(gv[key]).view(np.uint8) != np.atleast_1d(wv[key]).view(np.uint8)))
         if d:
             out.append(f"{key}:{d}")
     return out
