@@ -395,7 +395,7 @@ def time_decode(args, w, B, K, W, split=False):
             "dec_bytes": dec_bytes, "kernel": kernel, "layers": L, "layer_bytes": layer_bytes}
 
 
-CEILING_DEFAULT = (0, 16, 4)  # mode, waves per CU, loads in flight per lane: the best of the sweep on MI355X
+CEILING_DEFAULT = (0, 8, 4)  # mode, waves per CU, loads in flight per lane: the best of the sweep on MI355X
 CEILING_SWEEP = [(0, w, d) for w in (8, 16, 32) for d in (2, 4, 8)] + \
                 [(1, w, d) for w in (8, 12) for d in (2, 3, 4) if w * d * 3360 <= 160 * 1024]
 
