@@ -189,12 +189,16 @@ struct alignas(16) Lds {  // 16-byte aligned size: every wave's area keeps 16-by
 };
 static_assert(sizeof(float) * 4 * kPartialStride <= kRing * rec_bytes(0), "partial fits over the ring");
 constexpr int kLdsPerCu = 160 * 1024;
-static_assert(sizeof(Lds<128, 2>) * kMaxWgWaves <= kLdsPerCu, "twelve waves' LDS fit one CU (lo_bit 2)");
+// After the waves' areas, one row of 128 fp16 zeros shared by the
+// workgroup: the MFMA operand rows and columns whose results are not used
+// read it.
+constexpr int kZeroRowBytes = 256;
+static_assert(sizeof(Lds<128, 2>) * kMaxWgWaves + kZeroRowBytes <= kLdsPerCu, "twelve waves' LDS fit one CU (lo_bit 2)");
 // Waves whose LDS areas fit one CU: twelve for every 2-bit record, nine to
 // twelve for 4-bit records (a twice larger ring).
 template <int NHI, int BITS>
 constexpr int max_wg_waves() {
-  constexpr int w = kLdsPerCu / (int)sizeof(Lds<NHI, BITS>);
+  constexpr int w = (kLdsPerCu - kZeroRowBytes) / (int)sizeof(Lds<NHI, BITS>);
   return w < kMaxWgWaves ? w : kMaxWgWaves;
 }
 static_assert(max_wg_waves<128, 4>() >= 8, "4-bit records keep two waves per SIMD");
@@ -365,7 +369,7 @@ __host__ __device__ __forceinline__ int weight_prefix(int i, int W) {
 //
 // Lane (n = lane & 15, w = lane >> 4) roles:
 //  * QK^T has the query limbs as rows (row r = 4 head + slot, slots 0/1 = hi/lo
-//    limb, 2/3 repeat them) and the tokens as columns, so lane (n, w) ends with
+//    limb, 2/3 zero) and the tokens as columns, so lane (n, w) ends with
 //    the logits of head w at tokens n (combo A) and n + 16 (combo B);
 //  * PV has channels as rows and (head n & 3, limb (n >> 2) & 1) as columns
 //    0..7, the p limbs for the value-minimum correction as columns 8..15.
@@ -383,6 +387,7 @@ void decode_kernel(DecodeParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   Lds<NHI, BITS>* const all = reinterpret_cast<Lds<NHI, BITS>*>(dyn_lds);
   Lds<NHI, BITS>& sm = all[wave];
+  _Float16* const zrow = reinterpret_cast<_Float16*>(all + p.wg_waves);  // kZeroRowBytes, 16-byte aligned
 
   const int W = p.wg_waves;
   const int n_pw = p.n_wg * W - 1;           // the last wave of this unit also takes the tail
@@ -558,7 +563,15 @@ void decode_kernel(DecodeParams p) {
   const int pk = p_swz(4 * limb + h, 8 * w);  // this lane's operand chunk in its row
   const _Float16* b_src = n < 8 ? &sm.pt[0][limb][h][pk] : &sm.pl[limb][h][pk];
   const int b_stride = n < 8 ? 2 * 4 * 32 : 0;
+  // Columns 8..15 of the PV products are not used (only the correction
+  // MFMA, which takes group 0's operand, needs the p limbs there): for
+  // groups 1..3 those lanes read zeros, which lowers the switching power
+  // as the zero QK rows do.
+  const _Float16* b_rest = n < 8 ? &sm.pt[0][limb][h][pk] : zrow;
 
+  // every wave writes the zero row (the same zeros) before its own first read
+  // of it, which follows its first limb exchange's wait
+  *reinterpret_cast<uint32_t*>(&zrow[2 * lane]) = 0u;
   WaveState st;
   st.m = kNegBig;
   st.l = 0.0f;
@@ -605,13 +618,18 @@ void decode_kernel(DecodeParams p) {
   };
   // lim: tokens of the page below the attention bound (32 but for a page the
   // bound cuts)
+  // QK operand row of this lane: rows 4 head + 0 / 1 carry the hi / lo limb;
+  // rows 4 head + 2 / 3 are not used and read zeros, which lowers the
+  // MFMAs' switching power and with it the clock throttling under load
+  // (about 2% at batch 128, same results)
+  const _Float16* const qrow = (n & 2) ? zrow : sm.qt[al].h[ah];
   auto qk = [&](const uint8_t* S, const BoostIdx& bi, bool valid, int lim, float& s0, float& s1) KITTY_INLINE {
     // this lane's K base chunk: four words (2-bit) or eight (4-bit: combos A, B of word x at 2x, 2x + 1)
     const u32x4 kw = *reinterpret_cast<const u32x4*>(S + 16 * BITS / 2 * lane);
     const u32x4 kw2 = BITS == 4 ? *reinterpret_cast<const u32x4*>(S + 32 * lane + 16) : u32x4{};
     half8 bq[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) bq[kb] = *reinterpret_cast<const half8*>(&sm.qt[al].h[ah][32 * kb + 8 * w]);
+    for (int kb = 0; kb < 4; ++kb) bq[kb] = *reinterpret_cast<const half8*>(&qrow[32 * kb + 8 * w]);
     half8 bb[NB > 0 ? NB : 1];
     u32x2 bw[NB > 0 ? NB : 1];  // 2-bit: one word (both combos); 4-bit: the combo A, B pair
 #pragma unroll
@@ -621,7 +639,7 @@ void decode_kernel(DecodeParams p) {
       if (q0 < NHI) {
         const u32x2 ib = bi.ib[k2];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = sm.qt[al].h[ah][opaque(__builtin_amdgcn_ubfe(ib[j >> 2], 8 * (j & 3), 7))];
+        for (int j = 0; j < 8; ++j) v[j] = qrow[opaque(__builtin_amdgcn_ubfe(ib[j >> 2], 8 * (j & 3), 7))];
       }
       bb[k2] = v;
       if constexpr (BITS == 2) {
@@ -716,8 +734,9 @@ void decode_kernel(DecodeParams p) {
     half8 bg0 = {};
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      // columns 0..7: p * vscale limbs of group g; 8..15: p limbs (for the correction)
-      const half8 bg = *reinterpret_cast<const half8*>(b_src + g * b_stride);
+      // columns 0..7: p * vscale limbs of group g; 8..15: p limbs for the
+      // correction (group 0), zeros (groups 1..3)
+      const half8 bg = *reinterpret_cast<const half8*>(g == 0 ? b_src : b_rest + g * b_stride);
       if (g == 0) bg0 = bg;
       if constexpr (BITS == 2) {
         st.o[2 * g] = mfma(unpack_codes<0>(vw[g], ex_base), bg, st.o[2 * g]);
@@ -1001,10 +1020,11 @@ template <int NHI, int BITS, bool RUN>
 hipError_t launch_decode_nbr(const DecodeParams& p, hipStream_t stream) {
   constexpr int wmax = max_wg_waves<NHI, BITS>();
   if (p.wg_waves < 2 || p.wg_waves > wmax) return hipErrorInvalidValue;
-  const size_t lds = sizeof(Lds<NHI, BITS>) * p.wg_waves;
+  const size_t lds = sizeof(Lds<NHI, BITS>) * p.wg_waves + kZeroRowBytes;
   static const hipError_t attr =  // once per instantiation: allow the largest workgroup's LDS
       hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<NHI, BITS, RUN>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)(sizeof(Lds<NHI, BITS>) * wmax));
+                          hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)(sizeof(Lds<NHI, BITS>) * wmax + kZeroRowBytes));
   if (attr != hipSuccess) return attr;
   dim3 grid(p.n_wg, p.n_kv_heads * p.n_head_groups, p.batch);
   hipLaunchKernelGGL((decode_kernel<NHI, BITS, RUN>), grid, dim3(64 * p.wg_waves), lds, stream, p);
