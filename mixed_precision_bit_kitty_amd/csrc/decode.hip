@@ -10,14 +10,17 @@
 //   sum_t p_t v^_tc = sum_t (p_t vscale_t,g) a_tc + sum_t p_t vmin_t,g ,
 //
 // which run on v_mfma_f32_16x16x32_f16:
-//  * codes become exact fp16 operands off + code with one shift and one
-//    AND-OR per two codes (off = 4 or 16 by bit position, see unpack_codes;
-//    4-bit codes of the (hi_bit 8, lo_bit 4) pair: off = 16, unpack_codes4);
+//  * 2-bit codes become exact fp16 operands with v_cvt_scalef32_pk_f16_fp4:
+//    a code in the low two bits of a nibble is the e2m1 value code / 2, so
+//    one conversion turns a byte's two nibbles into two fp16 codes (see
+//    fp4_operand); 4-bit codes of the (hi_bit 8, lo_bit 4) pair become
+//    off + code with off = 16 (unpack_codes4), and their offset is a
+//    per-page constant that also runs on MFMA;
 //  * the per-page scale goes into the other operand as two fp16 limbs
 //    (hi = f16(x), lo = f16(x - hi)), which together carry the product to
-//    ~22 bits; the limbs sit in different MFMA columns and are summed after;
-//  * the code offsets and the minimum terms are per-page constants that also
-//    run on MFMA (constant A operands), so no VALU reduction is needed.
+//    ~22 bits; the limbs sit in different MFMA rows and are summed after;
+//  * the minimum terms are per-page constants that also run on MFMA
+//    (constant operands), so no VALU reduction is needed.
 //
 // One wave = one (sequence, KV head, group of <= 4 query heads, range of
 // pages); the last wave of each (sequence, KV head, head group) also attends
@@ -86,24 +89,34 @@ __device__ __forceinline__ void wave_lds_sync() {
   asm volatile("" ::: "memory");
 }
 
-// MFMA operand from one code word: elements of combo COMBO (0 = A, 1 = B) as
-// fp16 (off + code), with four shifts and eight AND-ORs for both combos of a
-// word.  Dword d holds elements 2d, 2d+1, whose codes sit at bits 2d + 8*COMBO
-// and 16 + 2d + 8*COMBO.  They move to bits 8/24 (mantissa bits 8..9 under an
-// exponent field E: value 2^(E-15) (1 + c/4)) or to bits 6/22 (2^(E-15)
-// (1 + c/16)), whichever lets two dwords share a shift:
-//   combo A: d0 <<8 (off 4), d1 <<4 (off 16), d2 <<4 (off 4), d3 as is (off 16)
-//   combo B: d0 as is (off 4), d1 >>4 (off 16), d2 >>4 (off 4), d3 >>8 (off 16)
-// so element j carries offset 4 for j in {0,1,4,5} and 16 for j in {2,3,6,7}.
-// The masks and exponent patterns live in VGPRs (ExpBits, made opaque once at
-// kernel start) so that each AND-OR selects to one v_and_or_b32 with three
-// VGPR operands (gfx9 VOP3 takes no literal and at most one SGPR).  The
-// instruction is left to the compiler, not written as inline asm: the hazard
-// recognizer must see every VALU write that an MFMA reads.
-struct ExpBits {
-  uint32_t e4, e16;  // exponent fields giving 4 + c and 16 + c (or a quarter of them)
-  uint32_t m8, m6;   // code masks at bits 8..9 / 24..25 and 6..7 / 22..23
+// MFMA operands from one 2-bit code word.  Element e of combo A sits at bit
+// 16 (e >> 2) + 4 (e & 1) + 2 ((e >> 1) & 1), combo B 8 bits higher, so the
+// word masked to the low two bits of every nibble (`even`) holds elements
+// 0, 1, 4, 5 of both combos in nibbles, and the word shifted right by 2 and
+// masked (`odd`) holds elements 2, 3, 6, 7.  A nibble 00cc is the e2m1 value
+// c / 2; v_cvt_scalef32_pk_f16_fp4 turns the two nibbles of one byte into two
+// fp16 values times `scale` (low nibble into the low half), exactly: scale 2
+// gives the code, scale 1/2 the boost weight code / 4.  Three VALU for the
+// split and eight conversions for both combos' operands (16 codes).
+struct Fp4Word {
+  uint32_t even, odd;
 };
+__device__ __forceinline__ Fp4Word fp4_split(uint32_t w) { return Fp4Word{w & 0x33333333u, (w >> 2) & 0x33333333u}; }
+template <int COMBO>
+__device__ __forceinline__ half8 fp4_operand(Fp4Word s, float scale) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(s.even, scale, COMBO));      // e 0, 1
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(s.odd, scale, COMBO));       // e 2, 3
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(s.even, scale, 2 + COMBO));  // e 4, 5
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(s.odd, scale, 2 + COMBO));   // e 6, 7
+  return __builtin_bit_cast(half8, r);
+}
+// The 4-bit pair's unpack keeps its masks and exponent patterns in VGPRs
+// (made opaque once at kernel start) so that each AND-OR selects to one
+// v_and_or_b32 with three VGPR operands (gfx9 VOP3 takes no literal and at
+// most one SGPR).  The instruction is left to the compiler, not written as
+// inline asm: the hazard recognizer must see every VALU write that an MFMA
+// reads.
 __device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {  // loop-invariant, read by VALU only
   uint32_t r;
   asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(c));
@@ -116,26 +129,6 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
   asm("" : "+v"(x));
   return x;
 }
-template <int COMBO>
-__device__ __forceinline__ half8 unpack_codes(uint32_t w, ExpBits e) {
-  const uint32_t m8 = e.m8, m6 = e.m6;
-  u32x4 r;
-  if (COMBO == 0) {
-    const uint32_t s8 = w << 8, s4 = w << 4;
-    r[0] = and_or(s8, m8, e.e4);
-    r[1] = and_or(s4, m6, e.e16);
-    r[2] = and_or(s4, m8, e.e4);
-    r[3] = and_or(w, m6, e.e16);
-  } else {
-    const uint32_t s4 = w >> 4, s8 = w >> 8;
-    r[0] = and_or(w, m8, e.e4);
-    r[1] = and_or(s4, m6, e.e16);
-    r[2] = and_or(s4, m8, e.e4);
-    r[3] = and_or(s8, m6, e.e16);
-  }
-  return __builtin_bit_cast(half8, r);
-}
-
 // MFMA operand from one 4-bit code word (one combo; element e at bit
 // 16*(e&1) + 4*(e>>1), so dword d's two codes sit at bits 4d and 16 + 4d):
 // each dword's pair moves to mantissa bits 6..9 / 22..25 under exponent
@@ -542,21 +535,19 @@ void decode_kernel(DecodeParams p) {
     }
   }
   const float qsc = __builtin_ldexpf(1.0f, qe);
-  const uint32_t m8v = vgpr_const(0x03000300u), m6v = vgpr_const(0x00C000C0u);
-  const ExpBits ex_base{vgpr_const(0x44004400u), vgpr_const(0x4C004C00u), m8v, m6v};   // 4 + c, 16 + c
-  const ExpBits ex_boost{vgpr_const(0x3C003C00u), vgpr_const(0x44004400u), m8v, m6v};  // (4 + c) / 4, (16 + c) / 4
   // 4-bit codes: mask of mantissa bits 6..9 / 22..25, exponents of 16 + c and (16 + c) / 16
   const uint32_t m4v = BITS == 4 ? vgpr_const(0x03C003C0u) : 0u;
   const uint32_t e4_base = BITS == 4 ? vgpr_const(0x4C004C00u) : 0u;
   const uint32_t e4_boost = BITS == 4 ? vgpr_const(0x3C003C00u) : 0u;
   // base code offsets per element (B operand rows = channels); boost code
   // offsets (weight 2^-lo_bit)
-  const half8 b_off = BITS == 2 ? half8_ab(-4.0f, -16.0f) : half8_ab(-16.0f, -16.0f);
-  const half8 b_offb = BITS == 2 ? half8_ab(-1.0f, -4.0f) : half8_ab(-1.0f, -1.0f);
-  // correction operand: rows 0..3 vmin (x1), rows 4..7 vscale x (-offset / 16)
-  const half8 corr_mul = n < 4 ? half8_ab(1.0f, 1.0f)
-                               : (n < 8 ? (BITS == 2 ? half8_ab(-0.25f, -1.0f) : half8_ab(-1.0f, -1.0f))
-                                        : half8_ab(0.0f, 0.0f));
+  // 4-bit code offsets per element (B operand rows = channels) and boost
+  // code offsets (weight 2^-lo_bit); 2-bit codes carry no offset
+  const half8 b_off = half8_ab(-16.0f, -16.0f);
+  const half8 b_offb = half8_ab(-1.0f, -1.0f);
+  // correction operand: rows 0..3 vmin (x1); 4-bit codes also rows 4..7
+  // vscale x (-offset / 16)
+  const half8 corr_mul = n < 4 ? half8_ab(1.0f, 1.0f) : (n < 8 ? half8_ab(-1.0f, -1.0f) : half8_ab(0.0f, 0.0f));
   const float sl2 = (1.0f / sqrtf((float)kHeadDim)) * kLog2e;
   // PV B operand source: lanes n < 8 read the group's p * vscale limbs, lanes
   // n >= 8 the p limbs (same address for every group)
@@ -658,16 +649,19 @@ void decode_kernel(DecodeParams p) {
     for (int kb = 0; kb < 4; ++kb) {
       const half8 kmin = *reinterpret_cast<const half8*>(S + off_kmin(NHI, BITS) + 2 * (32 * kb + 8 * w));
       cmin = mfma(bq_plain[kb], kmin, cmin);
-      coff = mfma(bq[kb], b_off, coff);
+      if constexpr (BITS == 4) coff = mfma(bq[kb], b_off, coff);
     }
+    if constexpr (BITS == 4) {
 #pragma unroll
-    for (int k2 = 0; k2 < NB; ++k2) coff = mfma(bb[k2], b_offb, coff);
+      for (int k2 = 0; k2 < NB; ++k2) coff = mfma(bb[k2], b_offb, coff);
+    }
     floatx4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       if constexpr (BITS == 2) {
-        acc0 = mfma(bq[kb], unpack_codes<0>(kw[kb], ex_base), acc0);
-        acc1 = mfma(bq[kb], unpack_codes<1>(kw[kb], ex_base), acc1);
+        const Fp4Word f = fp4_split(kw[kb]);
+        acc0 = mfma(bq[kb], fp4_operand<0>(f, 2.0f), acc0);
+        acc1 = mfma(bq[kb], fp4_operand<1>(f, 2.0f), acc1);
       } else {
         const uint32_t wa = kb < 2 ? kw[2 * kb] : kw2[2 * kb - 4];
         const uint32_t wb = kb < 2 ? kw[2 * kb + 1] : kw2[2 * kb - 3];
@@ -678,8 +672,9 @@ void decode_kernel(DecodeParams p) {
 #pragma unroll
     for (int k2 = 0; k2 < NB; ++k2) {
       if constexpr (BITS == 2) {
-        acc0 = mfma(bb[k2], unpack_codes<0>(bw[k2][0], ex_boost), acc0);
-        acc1 = mfma(bb[k2], unpack_codes<1>(bw[k2][0], ex_boost), acc1);
+        const Fp4Word f = fp4_split(bw[k2][0]);
+        acc0 = mfma(bb[k2], fp4_operand<0>(f, 0.5f), acc0);
+        acc1 = mfma(bb[k2], fp4_operand<1>(f, 0.5f), acc1);
       } else {
         acc0 = mfma(bb[k2], unpack_codes4(bw[k2][0], m4v, e4_boost), acc0);
         acc1 = mfma(bb[k2], unpack_codes4(bw[k2][1], m4v, e4_boost), acc1);
@@ -687,7 +682,7 @@ void decode_kernel(DecodeParams p) {
     }
     // rows 4w (hi limb, with the minimum term) + 4w + 1 (lo limb) of head w;
     // the code terms carry the query scale 2^-qe, the minimum term does not
-    const float cst = __builtin_fmaf(coff[0] + coff[1], qsc, cmin[0]);
+    const float cst = BITS == 2 ? cmin[0] : __builtin_fmaf(coff[0] + coff[1], qsc, cmin[0]);
     s0 = valid && n < lim ? __builtin_fmaf(acc0[0] + acc0[1], qsc, cst) : -INFINITY;       // token n
     s1 = valid && n + 16 < lim ? __builtin_fmaf(acc1[0] + acc1[1], qsc, cst) : -INFINITY;  // token n + 16
   };
@@ -739,8 +734,9 @@ void decode_kernel(DecodeParams p) {
       const half8 bg = *reinterpret_cast<const half8*>(g == 0 ? b_src : b_rest + g * b_stride);
       if (g == 0) bg0 = bg;
       if constexpr (BITS == 2) {
-        st.o[2 * g] = mfma(unpack_codes<0>(vw[g], ex_base), bg, st.o[2 * g]);
-        st.o[2 * g + 1] = mfma(unpack_codes<1>(vw[g], ex_base), bg, st.o[2 * g + 1]);
+        const Fp4Word f = fp4_split(vw[g]);
+        st.o[2 * g] = mfma(fp4_operand<0>(f, 2.0f), bg, st.o[2 * g]);
+        st.o[2 * g + 1] = mfma(fp4_operand<1>(f, 2.0f), bg, st.o[2 * g + 1]);
       } else {
         const uint32_t wa = g < 2 ? vw[2 * g] : vw2[2 * g - 4];
         const uint32_t wb = g < 2 ? vw[2 * g + 1] : vw2[2 * g - 3];
@@ -748,8 +744,14 @@ void decode_kernel(DecodeParams p) {
         st.o[2 * g + 1] = mfma(unpack_codes4(wb, m4v, e4_base), bg, st.o[2 * g + 1]);
       }
     }
-    const uint8_t* src = S + (n < 4 ? off_vmin(NHI, BITS) : off_vscale(NHI, BITS)) + 2 * (32 * (n & 3) + 8 * w);
-    const half8 a = *reinterpret_cast<const half8*>(src) * corr_mul;
+    half8 a;
+    if constexpr (BITS == 2) {  // rows 0..3: vmin; the other rows read zeros (2-bit codes carry no offset)
+      const uint8_t* src = n < 4 ? S + off_vmin(NHI, BITS) + 2 * (32 * n + 8 * w) : reinterpret_cast<const uint8_t*>(zrow);
+      a = *reinterpret_cast<const half8*>(src);
+    } else {
+      const uint8_t* src = S + (n < 4 ? off_vmin(NHI, BITS) : off_vscale(NHI, BITS)) + 2 * (32 * (n & 3) + 8 * w);
+      a = *reinterpret_cast<const half8*>(src) * corr_mul;
+    }
     st.corr = mfma(a, bg0, st.corr);
   };
   // one page through the whole contraction

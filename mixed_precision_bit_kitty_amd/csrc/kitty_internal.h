@@ -17,9 +17,13 @@
 //   3072+8n    idx             uint8[n], ascending boosted channel list
 //
 // Code word: 16 two-bit codes for two combos A, B of 8 elements e; element e
-// of A at bit 16*(e&1) + 2*(e>>1), of B at bit 16*(e&1) + 8 + 2*(e>>1).  With
-// this placement a word becomes both combos' MFMA operands (eight dwords of
-// two fp16 values off + code each) with four shifts and eight AND-ORs.
+// of A at bit 16*(e>>2) + 4*(e&1) + 2*((e>>1)&1), of B 8 bits higher.  Byte 0
+// holds A's elements 0..3, byte 1 B's, bytes 2 and 3 their elements 4..7,
+// and in each byte elements 0, 1 (4, 5) sit in the low two bits of its two
+// nibbles, elements 2, 3 (6, 7) in the high two.  With this placement the
+// word masked to the nibbles' low bits, and the word shifted right by 2 and
+// masked, hold e2m1 nibbles 00cc = c / 2, and eight fp4 conversions (two
+// codes each) give both combos' MFMA operands as exact fp16 codes.
 //
 // Chunk c of a 16-byte plane, u = c & 15, w = c >> 4, word x = 0..3:
 //   K base : A = (token u,      channel 32x + 8w + e), B = (token 16 + u, same channel)

@@ -166,19 +166,20 @@ __device__ __forceinline__ uint32_t code_of(uint32_t w, float mn, float inv, flo
   return __builtin_amdgcn_cvt_pk_u8_f32(t, byte, into);
 }
 
-// Four 2-bit codes held in bytes of x (each byte <= 3) -> an 8-bit field:
-// two v_dot4_u32_u8 with byte weights 1, 4 (low dword) and 16, 64 (high
-// dword) on the two bytes ODD selects (bytes 0, 2 or 1, 3 of each dword).
-template <int ODD>
-__device__ __forceinline__ uint32_t field4(uint64_t x) {
-  constexpr uint32_t wl = ODD ? 0x04000100u : 0x00040001u, wh = ODD ? 0x40001000u : 0x00400010u;
-  return __builtin_amdgcn_udot4((uint32_t)(x >> 32), wh, __builtin_amdgcn_udot4((uint32_t)x, wl, 0u, false), false);
-}
+// 2-bit code words: element e of combo A sits at bit 16 (e >> 2) + 4 (e & 1)
+// + 2 ((e >> 1) & 1), combo B 8 bits higher, so byte 0 holds combo A's
+// elements 0..3, byte 1 combo B's, bytes 2 and 3 their elements 4..7; in
+// each byte, elements 0 and 1 (4, 5) take the low two bits of its two
+// nibbles and elements 2 and 3 (6, 7) the high two.  Four codes held in
+// bytes 0..3 of a dword (each <= 3) become their byte of the word with one
+// v_dot4_u32_u8, byte weights 1, 16, 4, 64.
+constexpr uint32_t kField2 = 0x40041001u;
+__device__ __forceinline__ uint32_t field4(uint32_t x) { return __builtin_amdgcn_udot4(x, kField2, 0u, false); }
 // code word from combos A, B given as 8 code bytes each (element e in byte
-// e, every byte <= 3): element e of A at bit 16 (e & 1) + 2 (e >> 1), of B
-// 8 bits higher
+// e, every byte <= 3)
 __device__ __forceinline__ uint32_t pack_word(uint64_t a, uint64_t b) {
-  return field4<0>(a) | (field4<0>(b) << 8) | (field4<1>(a) << 16) | (field4<1>(b) << 24);
+  return field4((uint32_t)a) | (field4((uint32_t)b) << 8) | (field4((uint32_t)(a >> 32)) << 16) |
+         (field4((uint32_t)(b >> 32)) << 24);
 }
 constexpr uint64_t kLow2 = 0x0303030303030303ull;  // the low two bits of every byte
 
@@ -576,9 +577,9 @@ __device__ __forceinline__ void quantize_values_wave(RowSrc vs, uint8_t* __restr
     const int c0 = 32 * g + u, c1 = c0 + 16;
     const floatx4* vstep = reinterpret_cast<const floatx4*>(lds + lds_vstep(NHI)) + 16 * g;  // two tokens per read
     if constexpr (BITS == 2) {
-      // Element e of word w (token tau(w, e)) goes to byte e >> 1 of field
-      // f[w][2 (e & 1) + combo]; a field's four 2-bit codes become its 8 bits
-      // of the word with one v_dot4_u32_u8 (byte weights 1, 4, 16, 64).
+      // Element e of word w (token tau(w, e)) goes to byte e & 3 of field
+      // f[w][2 (e >> 2) + combo], which is byte 2 (e >> 2) + combo of the
+      // word (field4 packs a field's four codes).
       uint32_t f[4][4] = {};
 #pragma unroll
       for (int t2 = 0; t2 < 16; ++t2) {
@@ -588,19 +589,15 @@ __device__ __forceinline__ void quantize_values_wave(RowSrc vs, uint8_t* __restr
           const int t = 2 * t2 + k, kap = kappa_of(t), w = kap >> 3, e = kap & 7;
           const uint16_t* r = reinterpret_cast<const uint16_t*>(vs.row(t));
           const uint32_t y0 = r[c0], y1 = r[c1];
-          uint32_t& fa = f[w][2 * (e & 1)];
-          uint32_t& fb = f[w][2 * (e & 1) + 1];
-          fa = code_of<0>(y0, st2[2 * k + 1], st2[2 * k], kLo, e >> 1, fa);
-          fb = code_of<0>(y1, st2[2 * k + 1], st2[2 * k], kLo, e >> 1, fb);
+          uint32_t& fa = f[w][2 * (e >> 2)];
+          uint32_t& fb = f[w][2 * (e >> 2) + 1];
+          fa = code_of<0>(y0, st2[2 * k + 1], st2[2 * k], kLo, e & 3, fa);
+          fb = code_of<0>(y1, st2[2 * k + 1], st2[2 * k], kLo, e & 3, fb);
         }
       }
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        constexpr uint32_t kW = 0x40100401u;
-        const uint32_t word = __builtin_amdgcn_udot4(f[w][0], kW, 0u, false) |
-                              (__builtin_amdgcn_udot4(f[w][1], kW, 0u, false) << 8) |
-                              (__builtin_amdgcn_udot4(f[w][2], kW, 0u, false) << 16) |
-                              (__builtin_amdgcn_udot4(f[w][3], kW, 0u, false) << 24);
+        const uint32_t word = field4(f[w][0]) | (field4(f[w][1]) << 8) | (field4(f[w][2]) << 16) | (field4(f[w][3]) << 24);
         *reinterpret_cast<uint32_t*>(rec + off_v(NHI, BITS) + 16 * (16 * w + u) + 4 * g) = word;
       }
     } else {  // 4-bit: combo A (channel c0) at word 2g, combo B (c1) at 2g + 1 of a 32-byte chunk

@@ -280,8 +280,12 @@ def dequant_v(a, vscale, vmin):
 #
 # Code words.  Every code plane is a sequence of little-endian 32-bit words
 # holding 16 two-bit codes for two "combos" A and B of 8 elements e = 0..7:
-# element e of combo A sits at bits 16*(e%2) + 2*(e//2), element e of combo B
-# at bits 16*(e%2) + 8 + 2*(e//2).
+# element e of combo A sits at bits 16*(e//4) + 4*(e%2) + 2*((e//2)%2),
+# element e of combo B 8 bits higher.  So byte 0 holds combo A's elements
+# 0..3, byte 1 combo B's 0..3, bytes 2 and 3 their elements 4..7, and each
+# nibble's low two bits hold elements 0, 1 (4, 5), its high two bits
+# elements 2, 3 (6, 7).  (The layout is this repository's choice; the pages
+# give none.)
 #
 # Chunk c (0..63) of a 16-byte plane is word x = 0..3 at byte 16c + 4x, with
 # u = c % 16 and w = c // 16:
@@ -341,13 +345,19 @@ def tau(w, e):
     return 4 * w + e // 2 + 16 * (e % 2)
 
 
+def _bitpos(e):
+    """Bit of element e (0..7) of combo A in a 2-bit code word (combo B: 8
+    higher)."""
+    return 16 * (e // 4) + 4 * (e % 2) + 2 * ((e // 2) % 2)
+
+
 def _word(a8, b8):
     """Pack combos a8, b8 ([..., 8] codes 0..3) into uint32 words."""
     a8 = np.asarray(a8, np.uint32)
     b8 = np.asarray(b8, np.uint32)
     w = np.zeros(a8.shape[:-1], np.uint32)
     for e in range(8):
-        sh = 16 * (e % 2) + 2 * (e // 2)
+        sh = _bitpos(e)
         w |= (a8[..., e] & 3) << np.uint32(sh)
         w |= (b8[..., e] & 3) << np.uint32(sh + 8)
     return w
@@ -359,7 +369,7 @@ def _unword(w):
     a8 = np.zeros(w.shape + (8,), np.uint8)
     b8 = np.zeros(w.shape + (8,), np.uint8)
     for e in range(8):
-        sh = 16 * (e % 2) + 2 * (e // 2)
+        sh = _bitpos(e)
         a8[..., e] = (w >> np.uint32(sh)) & 3
         b8[..., e] = (w >> np.uint32(sh + 8)) & 3
     return a8, b8

@@ -247,8 +247,9 @@ def _tol(vmax, sabs):
     above it (2^-13 of the largest |v^|), plus the first-order effect of the
     logits' rounding: the kernel's logits carry an error of at most about
     2^-19 sabs, where sabs = max over heads of sum_c |q_c| range_c / sqrt(D)
-    (the code contraction runs on fp16 operands off + code, off up to 16,
-    with fp32 accumulation), and a logit error d moves the output by at most
+    (the code contraction runs on fp16 operands with fp32 accumulation: off
+    + code with off = 16 for 4-bit codes, the exact code for 2-bit ones, so
+    this bounds both), and a logit error d moves the output by at most
     2 d max |v^|.  Below logits of ~10^2 the second term is far under the
     first."""
     return ATOL * max(1.0, vmax / 16.0) + 2.0 * 2.0 ** -19 * sabs * vmax

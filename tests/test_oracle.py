@@ -412,41 +412,57 @@ def _one_code_page(plane, t, c, val, n_hi=32):
 
 
 def test_layout_positions_by_hand():
+    # Element e of combo A sits at bit 16*(e//4) + 4*(e%2) + 2*((e//2)%2) of
+    # its word, combo B 8 bits higher.
     # base[token 17][channel 42] = 3: token 17 -> combo B, u = 1; channel 42 =
     # 32*1 + 8*1 + 2 -> x = 1, w = 1, e = 2; chunk 16*1 + 1 = 17, word at
-    # byte 16*17 + 4 = 276; bit 16*0 + 8 + 2*1 = 10 -> byte 277, bits 2..3.
+    # byte 16*17 + 4 = 276; bit 0 + 8 + 0 + 2 = 10 -> byte 277, bits 2..3.
     r = _one_code_page("base", 17, 42, 3)
     nz = np.nonzero(r)[0]
     assert list(nz) == [277] and r[277] == 3 << 2
     # base[token 4][channel 101] = 2: combo A, u = 4; 101 = 96 + 0 + 5 ->
-    # x = 3, w = 0, e = 5; chunk 4, byte 16*4 + 12 = 76; bit 16 + 2*2 = 20 ->
-    # byte 78, bits 4..5.
+    # x = 3, w = 0, e = 5; chunk 4, byte 16*4 + 12 = 76; bit 16 + 4 + 0 = 20
+    # -> byte 78, bits 4..5.
     r = _one_code_page("base", 4, 101, 2)
     assert list(np.nonzero(r)[0]) == [78] and r[78] == 2 << 4
+    # base[token 3][channel 33] = 1: combo A, u = 3; 33 = 32 + 0 + 1 -> x = 1,
+    # w = 0, e = 1; chunk 3, byte 16*3 + 4 = 52; bit 0 + 4 + 0 = 4 -> byte 52,
+    # bits 4..5.
+    r = _one_code_page("base", 3, 33, 1)
+    assert list(np.nonzero(r)[0]) == [52] and r[52] == 1 << 4
     # boost (n_hi = 32, one full block) [token 20][slot 9] = 1: combo B, u = 4;
     # slot 9 = 8*1 + 1 -> w = 1, e = 1; chunk 20; word at 1024 + 4*20 = 1104;
-    # bit 16 + 8 + 0 = 24 -> byte 1107, bit 0.
+    # bit 0 + 8 + 4 + 0 = 12 -> byte 1105, bits 4..5.
     r = _one_code_page("boost", 20, 9, 1)
-    assert list(np.nonzero(r)[0]) == [1107] and r[1107] == 1
+    assert list(np.nonzero(r)[0]) == [1105] and r[1105] == 1 << 4
     # V codes (n_hi = 32: plane at 1280) a[token 22][channel 53] = 3: token 22 =
     # tau(w=1, e=5) (4 + 2 + 16); channel 53 = 16*3 + 5 -> combo B of x = 1,
-    # u = 5; chunk 16 + 5 = 21; word at 1280 + 16*21 + 4 = 1620; bit 16*1 +
-    # 8 + 2*2 = 28 -> byte 1623, bits 4..5.
+    # u = 5; chunk 16 + 5 = 21; word at 1280 + 16*21 + 4 = 1620; bit 16 + 8 +
+    # 4 + 0 = 28 -> byte 1623, bits 4..5.
     r = _one_code_page("a", 22, 53, 3)
     assert list(np.nonzero(r)[0]) == [1623] and r[1623] == 3 << 4
     # a[token 7][channel 2] = 1: token 7 = tau(w=1, e=6) (4 + 3); channel 2 ->
     # combo A of x = 0, u = 2; chunk 18; word at 1280 + 16*18 = 1568; bit
-    # 16*0 + 2*3 = 6 -> byte 1568, bits 6..7.
+    # 16 + 0 + 0 + 2 = 18 -> byte 1570, bits 2..3.
     r = _one_code_page("a", 7, 2, 1)
-    assert list(np.nonzero(r)[0]) == [1568] and r[1568] == 1 << 6
+    assert list(np.nonzero(r)[0]) == [1570] and r[1570] == 1 << 2
+    # a[token 17][channel 20] = 2: token 17 = tau(w=0, e=3) (0 + 1 + 16);
+    # channel 20 = 16 + 4 -> combo B of x = 0, u = 4; chunk 4; word at
+    # 1280 + 16*4 = 1344; bit 0 + 8 + 4 + 2 = 14 -> byte 1345, bits 6..7.
+    r = _one_code_page("a", 17, 20, 2)
+    assert list(np.nonzero(r)[0]) == [1345] and r[1345] == 2 << 6
 
 
 def test_layout_half_boost_block():
     # n_hi = 16: a half block only, lanes 0..31; boost[token 3][slot 15]:
-    # w = 1, e = 7; chunk 16 + 3 = 19; byte 1024 + 4*19 = 1100; bit 16 + 2*3 =
-    # 22 -> byte 1102, bits 6..7.
+    # w = 1, e = 7; chunk 16 + 3 = 19; byte 1024 + 4*19 = 1100; bit 16 + 4 +
+    # 2 = 22 -> byte 1102, bits 6..7.
     r = _one_code_page("boost", 3, 15, 2, n_hi=16)
     assert list(np.nonzero(r)[0]) == [1102] and r[1102] == 2 << 6
+    # boost[token 16][slot 4]: combo B, u = 0, w = 0, e = 4; chunk 0; byte
+    # 1024; bit 16 + 8 + 0 + 0 = 24 -> byte 1027, bits 0..1.
+    r = _one_code_page("boost", 16, 4, 3, n_hi=16)
+    assert list(np.nonzero(r)[0]) == [1027] and r[1027] == 3
 
 
 def test_layout_metadata_offsets():

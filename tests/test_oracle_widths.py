@@ -46,10 +46,10 @@ def test_padding_positions_by_hand():
     # n_hi = 13 -> 16 slots, one half block (lanes 0..31), 3072 + 144 bytes.
     # Every boost code of the 13 real slots is 3: in chunk c = 16w + u (w =
     # slot // 8 for slots 0..15) element e of combo A sits at bit
-    # 16*(e % 2) + 2*(e // 2), of combo B 8 higher.  Chunks 16..31 (w = 1)
-    # hold slots 8..15: elements 5, 6, 7 (slots 13, 14, 15) are padding, at
-    # bits 20, 6, 22 (A) and 28, 14, 30 (B); all other bits of those words
-    # are ones.  Chunks 0..15 (slots 0..7) are all ones.
+    # 16*(e // 4) + 4*(e % 2) + 2*((e // 2) % 2), of combo B 8 higher.
+    # Chunks 16..31 (w = 1) hold slots 8..15: elements 5, 6, 7 (slots 13, 14,
+    # 15) are padding, at bits 20, 18, 22 (A) and 28, 26, 30 (B); all other
+    # bits of those words are ones.  Chunks 0..15 (slots 0..7) are all ones.
     n = 13
     kf = dict(base=np.zeros((32, 128), np.uint8), boost=np.full((32, n), 3, np.uint8),
               kscale=np.zeros(128, np.float16), kmin=np.zeros(128, np.float16),
@@ -60,7 +60,7 @@ def test_padding_positions_by_hand():
     assert r.size == 3072 + 9 * 16
     words = r[1024:1024 + 128].view("<u4")
     pad = 0
-    for b in (20, 6, 22, 28, 14, 30):
+    for b in (20, 18, 22, 28, 26, 30):
         pad |= 3 << b
     for c in range(32):
         want = 0xFFFFFFFF if c < 16 else 0xFFFFFFFF & ~pad
