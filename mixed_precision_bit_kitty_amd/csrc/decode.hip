@@ -10,12 +10,13 @@
 //   sum_t p_t v^_tc = sum_t (p_t vscale_t,g) a_tc + sum_t p_t vmin_t,g ,
 //
 // which run on v_mfma_f32_16x16x32_f16:
-//  * 2-bit codes become exact fp16 operands with v_cvt_scalef32_pk_f16_fp4:
-//    a code in the low two bits of a nibble is the e2m1 value code / 2, so
-//    one conversion turns a byte's two nibbles into two fp16 codes (see
-//    fp4_operand); 4-bit codes of the (hi_bit 8, lo_bit 4) pair become
-//    off + code with off = 16 (unpack_codes4), and their offset is a
-//    per-page constant that also runs on MFMA;
+//  * codes become exact fp16 operands through the fp4/fp8 conversions: a
+//    2-bit code in the low two bits of a nibble is the e2m1 value code / 2
+//    (v_cvt_scalef32_pk_f16_fp4 turns a byte's two nibbles into two fp16
+//    codes, see fp4_operand), and a 4-bit code of the (hi_bit 8, lo_bit 4)
+//    pair in the low nibble of a byte is the e4m3 value code * 2^-9
+//    (v_cvt_scalef32_pk_f16_fp8 turns two such bytes into two fp16 codes,
+//    see fp8_operand); no code offsets;
 //  * the per-page scale goes into the other operand as two fp16 limbs
 //    (hi = f16(x), lo = f16(x - hi)), which together carry the product to
 //    ~22 bits; the limbs sit in different MFMA rows and are summed after;
@@ -111,44 +112,30 @@ __device__ __forceinline__ half8 fp4_operand(Fp4Word s, float scale) {
   r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(s.odd, scale, 2 + COMBO));   // e 6, 7
   return __builtin_bit_cast(half8, r);
 }
-// The 4-bit pair's unpack keeps its masks and exponent patterns in VGPRs
-// (made opaque once at kernel start) so that each AND-OR selects to one
-// v_and_or_b32 with three VGPR operands (gfx9 VOP3 takes no literal and at
-// most one SGPR).  The instruction is left to the compiler, not written as
-// inline asm: the hazard recognizer must see every VALU write that an MFMA
-// reads.
-__device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {  // loop-invariant, read by VALU only
-  uint32_t r;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(c));
-  return r;
-}
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t orv) { return (x & mask) | orv; }
 // A value the compiler may not re-derive (keeps a bitfield extract from being
 // rewritten into shift-and-mask pairs once it is scaled into an address).
 __device__ __forceinline__ uint32_t opaque(uint32_t x) {
   asm("" : "+v"(x));
   return x;
 }
-// MFMA operand from one 4-bit code word (one combo; element e at bit
-// 16*(e&1) + 4*(e>>1), so dword d's two codes sit at bits 4d and 16 + 4d):
-// each dword's pair moves to mantissa bits 6..9 / 22..25 under exponent
-// pattern e, giving 2^(E-15) (1 + c/16): 16 + c for E = 19, 1 + c/16 for
-// E = 15.  Four shifts and four AND-ORs for eight codes.
-__device__ __forceinline__ half8 unpack_codes4(uint32_t w, uint32_t mask, uint32_t e) {
+// MFMA operand from one 4-bit code word (one combo; element e at bit 16 (e
+// >> 2) + 8 (e & 1) + 4 ((e >> 1) & 1), so byte k < 2 holds elements k and
+// k + 2, byte 2 + k elements 4 + k and 6 + k).  The word masked to the low
+// nibble of every byte (`lo`: elements 0, 1, 4, 5) and shifted right by 4
+// and masked (`hi`: 2, 3, 6, 7) holds bytes 0000cccc, the e4m3 value c *
+// 2^-9 (subnormal for c < 8, normal above, linear across the boundary);
+// v_cvt_scalef32_pk_f16_fp8 turns a 16-bit half's two bytes into two fp16
+// values times `scale` (low byte into the low half), exactly: scale 2^9
+// gives the code, 2^5 the boost weight code / 16.  Three VALU and four
+// conversions per word.
+__device__ __forceinline__ half8 fp8_operand(uint32_t w, float scale) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
   u32x4 r;
-  r[0] = and_or(w << 6, mask, e);
-  r[1] = and_or(w << 2, mask, e);
-  r[2] = and_or(w >> 2, mask, e);
-  r[3] = and_or(w >> 6, mask, e);
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, scale, false));  // e 0, 1
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, scale, false));  // e 2, 3
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, scale, true));   // e 4, 5
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, scale, true));   // e 6, 7
   return __builtin_bit_cast(half8, r);
-}
-
-// half8 with value a at elements {0,1,4,5} and b at {2,3,6,7}
-__device__ __forceinline__ half8 half8_ab(float a, float b) {
-  half8 v;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = (_Float16)(((j >> 1) & 1) ? b : a);
-  return v;
 }
 
 // One limb of the q * kscale exchange: [head][channel]; the head stride
@@ -177,7 +164,7 @@ struct alignas(16) Lds {  // 16-byte aligned size: every wave's area keeps 16-by
       _Float16 pl[2][4][32];     // p limbs [limb][head][p_swz(kappa)]
     };
   };
-  float red[2][4][4];           // final corrections [kind][head][group]
+  float red[4][4];              // final value-minimum corrections [head][group]
   int flag;                     // workgroup broadcast of the arrival count (wave 0's copy)
 };
 static_assert(sizeof(float) * 4 * kPartialStride <= kRing * rec_bytes(0), "partial fits over the ring");
@@ -259,7 +246,7 @@ struct WaveState {
   float m;        // running max of the scaled logits of head w (log2 domain)
   float l;        // this lane's share of head w's softmax denominator
   floatx4 o[8];   // PV accumulators, channel blocks of 16
-  floatx4 corr;   // value-minimum / code-offset correction accumulator
+  floatx4 corr;   // value-minimum correction accumulator
 };
 
 // Value of head (n & 3) from a per-head value held by rows (row h = head h).
@@ -536,18 +523,6 @@ void decode_kernel(DecodeParams p) {
   }
   const float qsc = __builtin_ldexpf(1.0f, qe);
   // 4-bit codes: mask of mantissa bits 6..9 / 22..25, exponents of 16 + c and (16 + c) / 16
-  const uint32_t m4v = BITS == 4 ? vgpr_const(0x03C003C0u) : 0u;
-  const uint32_t e4_base = BITS == 4 ? vgpr_const(0x4C004C00u) : 0u;
-  const uint32_t e4_boost = BITS == 4 ? vgpr_const(0x3C003C00u) : 0u;
-  // base code offsets per element (B operand rows = channels); boost code
-  // offsets (weight 2^-lo_bit)
-  // 4-bit code offsets per element (B operand rows = channels) and boost
-  // code offsets (weight 2^-lo_bit); 2-bit codes carry no offset
-  const half8 b_off = half8_ab(-16.0f, -16.0f);
-  const half8 b_offb = half8_ab(-1.0f, -1.0f);
-  // correction operand: rows 0..3 vmin (x1); 4-bit codes also rows 4..7
-  // vscale x (-offset / 16)
-  const half8 corr_mul = n < 4 ? half8_ab(1.0f, 1.0f) : (n < 8 ? half8_ab(-1.0f, -1.0f) : half8_ab(0.0f, 0.0f));
   const float sl2 = (1.0f / sqrtf((float)kHeadDim)) * kLog2e;
   // PV B operand source: lanes n < 8 read the group's p * vscale limbs, lanes
   // n >= 8 the p limbs (same address for every group)
@@ -644,16 +619,11 @@ void decode_kernel(DecodeParams p) {
     // the gathers (a second LDS round trip after the index read) issue with
     // the limb reads, ahead of the MFMAs that do not need them
     __builtin_amdgcn_sched_barrier(0);
-    floatx4 cmin = {0.0f, 0.0f, 0.0f, 0.0f}, coff = {0.0f, 0.0f, 0.0f, 0.0f};
+    floatx4 cmin = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const half8 kmin = *reinterpret_cast<const half8*>(S + off_kmin(NHI, BITS) + 2 * (32 * kb + 8 * w));
       cmin = mfma(bq_plain[kb], kmin, cmin);
-      if constexpr (BITS == 4) coff = mfma(bq[kb], b_off, coff);
-    }
-    if constexpr (BITS == 4) {
-#pragma unroll
-      for (int k2 = 0; k2 < NB; ++k2) coff = mfma(bb[k2], b_offb, coff);
     }
     floatx4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -665,8 +635,8 @@ void decode_kernel(DecodeParams p) {
       } else {
         const uint32_t wa = kb < 2 ? kw[2 * kb] : kw2[2 * kb - 4];
         const uint32_t wb = kb < 2 ? kw[2 * kb + 1] : kw2[2 * kb - 3];
-        acc0 = mfma(bq[kb], unpack_codes4(wa, m4v, e4_base), acc0);
-        acc1 = mfma(bq[kb], unpack_codes4(wb, m4v, e4_base), acc1);
+        acc0 = mfma(bq[kb], fp8_operand(wa, 512.0f), acc0);
+        acc1 = mfma(bq[kb], fp8_operand(wb, 512.0f), acc1);
       }
     }
 #pragma unroll
@@ -676,13 +646,13 @@ void decode_kernel(DecodeParams p) {
         acc0 = mfma(bb[k2], fp4_operand<0>(f, 0.5f), acc0);
         acc1 = mfma(bb[k2], fp4_operand<1>(f, 0.5f), acc1);
       } else {
-        acc0 = mfma(bb[k2], unpack_codes4(bw[k2][0], m4v, e4_boost), acc0);
-        acc1 = mfma(bb[k2], unpack_codes4(bw[k2][1], m4v, e4_boost), acc1);
+        acc0 = mfma(bb[k2], fp8_operand(bw[k2][0], 32.0f), acc0);
+        acc1 = mfma(bb[k2], fp8_operand(bw[k2][1], 32.0f), acc1);
       }
     }
     // rows 4w (hi limb, with the minimum term) + 4w + 1 (lo limb) of head w;
     // the code terms carry the query scale 2^-qe, the minimum term does not
-    const float cst = BITS == 2 ? cmin[0] : __builtin_fmaf(coff[0] + coff[1], qsc, cmin[0]);
+    const float cst = cmin[0];
     s0 = valid && n < lim ? __builtin_fmaf(acc0[0] + acc0[1], qsc, cst) : -INFINITY;       // token n
     s1 = valid && n + 16 < lim ? __builtin_fmaf(acc1[0] + acc1[1], qsc, cst) : -INFINITY;  // token n + 16
   };
@@ -740,18 +710,14 @@ void decode_kernel(DecodeParams p) {
       } else {
         const uint32_t wa = g < 2 ? vw[2 * g] : vw2[2 * g - 4];
         const uint32_t wb = g < 2 ? vw[2 * g + 1] : vw2[2 * g - 3];
-        st.o[2 * g] = mfma(unpack_codes4(wa, m4v, e4_base), bg, st.o[2 * g]);
-        st.o[2 * g + 1] = mfma(unpack_codes4(wb, m4v, e4_base), bg, st.o[2 * g + 1]);
+        st.o[2 * g] = mfma(fp8_operand(wa, 512.0f), bg, st.o[2 * g]);
+        st.o[2 * g + 1] = mfma(fp8_operand(wb, 512.0f), bg, st.o[2 * g + 1]);
       }
     }
-    half8 a;
-    if constexpr (BITS == 2) {  // rows 0..3: vmin; the other rows read zeros (2-bit codes carry no offset)
-      const uint8_t* src = n < 4 ? S + off_vmin(NHI, BITS) + 2 * (32 * n + 8 * w) : reinterpret_cast<const uint8_t*>(zrow);
-      a = *reinterpret_cast<const half8*>(src);
-    } else {
-      const uint8_t* src = S + (n < 4 ? off_vmin(NHI, BITS) : off_vscale(NHI, BITS)) + 2 * (32 * (n & 3) + 8 * w);
-      a = *reinterpret_cast<const half8*>(src) * corr_mul;
-    }
+    // correction operand: rows 0..3 the page's vmin of group n; the other
+    // rows read zeros (the codes carry no offset)
+    const uint8_t* src = n < 4 ? S + off_vmin(NHI, BITS) + 2 * (32 * n + 8 * w) : reinterpret_cast<const uint8_t*>(zrow);
+    const half8 a = *reinterpret_cast<const half8*>(src);
     st.corr = mfma(a, bg0, st.corr);
   };
   // one page through the whole contraction
@@ -875,12 +841,12 @@ void decode_kernel(DecodeParams p) {
   // ---- this wave's partial (m, l, O with corrections) into its LDS area --------
   const float l_row = row_sum16(st.l);  // head w's denominator over this wave's tokens
   const float m_h = head_of_column(st.m, n), l_h = head_of_column(l_row, n);
-  // correction MFMA: rows g (vmin . p) and 4 + g (offset term / 16), columns
-  // 8 + h (hi limb of p) and 12 + h (lo limb); lanes 12..15 add column n - 4.
+  // correction MFMA: rows g (vmin . p), columns 8 + h (hi limb of p) and
+  // 12 + h (lo limb); lanes 12..15 of row group 0 add column n - 4.
 #pragma unroll
   for (int i4 = 0; i4 < 4; ++i4) {
     const float v = st.corr[i4] + dpp<kRowRor4>(st.corr[i4]);
-    if (n >= 12 && w < 2) sm.red[w][n - 12][i4] = v;
+    if (n >= 12 && w == 0) sm.red[n - 12][i4] = v;
   }
   wave_lds_sync();
   // The DPP sums run with every lane active (a DPP read of an inactive lane
@@ -889,7 +855,7 @@ void decode_kernel(DecodeParams p) {
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) {
     const int g = mb >> 1;
-    const float cg = sm.red[0][h][g] + 16.0f * sm.red[1][h][g];
+    const float cg = sm.red[h][g];
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) ov[mb][i4] = st.o[mb][i4] + dpp<kRowRor12>(st.o[mb][i4]) + cg;  // hi + lo column
   }

@@ -182,15 +182,19 @@ __device__ __forceinline__ uint32_t pack_word(uint64_t a, uint64_t b) {
          (field4((uint32_t)(b >> 32)) << 24);
 }
 constexpr uint64_t kLow2 = 0x0303030303030303ull;  // the low two bits of every byte
+constexpr uint64_t kLow4 = 0x0F0F0F0F0F0F0F0Full;  // the low four bits of every byte
 
-// bytes 0, 2, 4, 6 of x (each a 4-bit code in its low nibble) -> bits 0, 4, 8, 12
-__device__ __forceinline__ uint32_t gather4_nib(uint64_t x) {
-  x &= 0x000F000F000F000Full;
-  return (uint32_t)((x | (x >> 12) | (x >> 24) | (x >> 36)) & 0xFFFFu);
+// 4-bit code words: element e of the word's combo sits at bit 16 (e >> 2) +
+// 8 (e & 1) + 4 ((e >> 1) & 1), so byte k of the word (k < 2) holds elements
+// k (low nibble) and k + 2 (high nibble), byte 2 + k elements 4 + k and 6 +
+// k.  From 8 code bytes (element e in byte e, each <= 15): byte 0 of the
+// word is one v_dot4_u32_u8 of the low four bytes with weights 1, 0, 16, 0.
+constexpr uint32_t kEvenNib = 0x00100001u, kOddNib = 0x10000100u;  // byte weights (1, 0, 16, 0), (0, 1, 0, 16)
+__device__ __forceinline__ uint32_t nib2(uint32_t x, uint32_t w) { return __builtin_amdgcn_udot4(x, w, 0u, false); }
+__device__ __forceinline__ uint32_t pack_word4(uint64_t a) {
+  const uint32_t lo = (uint32_t)a, hi = (uint32_t)(a >> 32);
+  return nib2(lo, kEvenNib) | (nib2(lo, kOddNib) << 8) | (nib2(hi, kEvenNib) << 16) | (nib2(hi, kOddNib) << 24);
 }
-// 4-bit code word of one combo given as 8 code bytes (element e in byte e):
-// element e at bit 16 (e & 1) + 4 (e >> 1)
-__device__ __forceinline__ uint32_t pack_word4(uint64_t a) { return gather4_nib(a) | (gather4_nib(a >> 8) << 16); }
 
 // ---- Top-n selection ------------------------------------------------------
 // Lane l holds the keys of channels 2l and 2l + 1 (unsigned; a larger key is
@@ -498,7 +502,7 @@ __device__ __forceinline__ void quantize_keys_wave(RowSrc ks, uint8_t* __restric
         if (BITS == 2) {
           *reinterpret_cast<uint32_t*>(bp + 4 * (lane * nf + bb)) = pack_word(A & kLow2, B & kLow2);
         } else {
-          const u32x2 pr = {pack_word4(A), pack_word4(B)};
+          const u32x2 pr = {pack_word4(A & kLow4), pack_word4(B & kLow4)};
           *reinterpret_cast<u32x2*>(bp + 8 * (lane * nf + bb)) = pr;
         }
       }
@@ -513,7 +517,7 @@ __device__ __forceinline__ void quantize_keys_wave(RowSrc ks, uint8_t* __restric
         if (BITS == 2) {
           *reinterpret_cast<uint32_t*>(bp + 256 * nf + 4 * lane) = pack_word(A & kLow2, B & kLow2);
         } else {
-          const u32x2 pr = {pack_word4(A), pack_word4(B)};
+          const u32x2 pr = {pack_word4(A & kLow4), pack_word4(B & kLow4)};
           *reinterpret_cast<u32x2*>(bp + 512 * nf + 8 * lane) = pr;
         }
       }
@@ -619,7 +623,7 @@ __device__ __forceinline__ void quantize_values_wave(RowSrc vs, uint8_t* __restr
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int t = tau_of(w, e);
-          const int sh = 16 * (e & 1) + 4 * (e >> 1);
+          const int sh = 16 * (e >> 2) + 8 * (e & 1) + 4 * ((e >> 1) & 1);
           wa |= a0[t] << sh;
           wb |= a1[t] << sh;
         }

@@ -297,7 +297,9 @@ def dequant_v(a, vscale, vmin):
 # token kappa // 2 + 16 * (kappa % 2) (see ``tau``).
 #
 # The (8, 4) pair (lo_bit 4) uses 4-bit planes of the same shape: a word
-# holds one combo of 8 elements, element e at bits 16*(e%2) + 4*(e//2), and
+# holds one combo of 8 elements, element e at bits 16*(e//4) + 8*(e%2) +
+# 4*((e//2)%2) (each byte holds two elements, e and e + 2, in its low and high
+# nibble), and
 # a chunk has twice the words, combo A at word 2x and combo B at word 2x + 1
 # (byte 32c + 4(2x + combo)), with the same tokens and channels as above.
 # The boost plane has two words per lane and slot block (byte 8(c*nf + b) +
@@ -381,13 +383,20 @@ _W = _C // 16
 _E = np.arange(8)
 
 
+def _bitpos4(e):
+    """Bit of element e (0..7) in a 4-bit code word: byte 0 holds elements 0
+    (low nibble) and 2 (high), byte 1 elements 1 and 3, bytes 2 and 3
+    elements 4, 6 and 5, 7."""
+    return 16 * (e // 4) + 8 * (e % 2) + 4 * ((e // 2) % 2)
+
+
 def _word4(a8):
     """Pack one combo a8 ([..., 8] codes 0..15) into uint32 words: element e
-    at bits 16*(e%2) + 4*(e//2)."""
+    at bits _bitpos4(e)."""
     a8 = np.asarray(a8, np.uint32)
     w = np.zeros(a8.shape[:-1], np.uint32)
     for e in range(8):
-        w |= (a8[..., e] & 15) << np.uint32(16 * (e % 2) + 4 * (e // 2))
+        w |= (a8[..., e] & 15) << np.uint32(_bitpos4(e))
     return w
 
 
@@ -396,7 +405,7 @@ def _unword4(w):
     w = np.asarray(w, np.uint32)
     a8 = np.zeros(w.shape + (8,), np.uint8)
     for e in range(8):
-        a8[..., e] = (w >> np.uint32(16 * (e % 2) + 4 * (e // 2))) & 15
+        a8[..., e] = (w >> np.uint32(_bitpos4(e))) & 15
     return a8
 
 

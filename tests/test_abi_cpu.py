@@ -93,10 +93,10 @@ def test_decode_waves_per_workgroup():
         w4 = f(n_hi, 4)
         # a wave's area: the ring; the larger of the two q * kscale limb
         # tables (4 x 144 + 8 halves each) and the p limb tables (4 x 2 x 4 x
-        # 32 + 2 x 4 x 32 halves), which share memory; 32 correction floats
+        # 32 + 2 x 4 x 32 halves), which share memory; 16 correction floats
         # and a flag; in 16-byte units.  The workgroup also holds one
         # 256-byte row of zeros.
-        area = -(-(2 * (5120 + 17 * n_hi) + max(2 * 1168, 2 * (256 + 1024)) + 128 + 4) // 16) * 16
+        area = -(-(2 * (5120 + 17 * n_hi) + max(2 * 1168, 2 * (256 + 1024)) + 64 + 4) // 16) * 16
         assert w4 == min(12, (160 * 1024 - 256) // area)
     assert f(0, 4) == 12 and f(128, 4) == 9
 

@@ -143,31 +143,37 @@ def _one_code_record(plane, t, c, val, n_hi):
 
 
 def test_layout_positions_by_hand_eight_four():
+    # Element e of a 4-bit word sits at bits 16*(e//4) + 8*(e%2) + 4*((e//2)%2).
     # base[token 3][channel 77] = 0xA: combo A, u = 3; 77 = 32*2 + 8*1 + 5 ->
     # x = 2, w = 1, e = 5; chunk 16*1 + 3 = 19, word 2x = 4 at byte
-    # 32*19 + 16 = 624; bits 16*1 + 4*2 = 24..27 -> byte 627, low nibble.
+    # 32*19 + 16 = 624; bits 16 + 8 + 0 = 24..27 -> byte 627, low nibble.
     r = _one_code_record("base", 3, 77, 0xA, 32)
     assert list(np.nonzero(r)[0]) == [627] and r[627] == 0xA
     # base[token 19][channel 77]: combo B -> word 5 at byte 628; byte 631.
     r = _one_code_record("base", 19, 77, 0x7, 32)
     assert list(np.nonzero(r)[0]) == [631] and r[631] == 0x7
+    # base[token 0][channel 4] = 0x9: combo A, u = 0; 4 = 0 + 0 + 4 -> x = 0,
+    # w = 0, e = 4; chunk 0, word 0 at byte 0; bits 16 + 0 + 0 = 16..19 ->
+    # byte 2, low nibble.
+    r = _one_code_record("base", 0, 4, 0x9, 32)
+    assert list(np.nonzero(r)[0]) == [2] and r[2] == 0x9
     # a[token 25][channel 38] = 0xC: 25 = tau(2, 3) (4*2 + 1 + 16); 38 =
     # 16*(2*1) + 6 -> combo A, x = 1, u = 6; chunk 16*2 + 6 = 38, word 2 at
     # byte 32*38 + 8 = 1224 of the value plane (which starts at 2048 + 16*32);
-    # bits 16*1 + 4*1 = 20..23 -> byte 1226, high nibble.
+    # bits 0 + 8 + 4 = 12..15 -> byte 1225, high nibble.
     r = _one_code_record("a", 25, 38, 0xC, 32)
-    assert list(np.nonzero(r)[0]) == [2560 + 1226] and r[2560 + 1226] == 0xC0
+    assert list(np.nonzero(r)[0]) == [2560 + 1225] and r[2560 + 1225] == 0xC0
     # boost[token 9][slot 30] = 0x5 (n_hi 32): slot 30 = 8*3 + 6 -> w = 3,
     # e = 6, combo A, chunk 16*3 + 9 = 57; byte 8*57 = 456 of the boost plane
-    # (at 2048); bits 4*3 = 12..15 -> byte 457, high nibble.
+    # (at 2048); bits 16 + 0 + 4 = 20..23 -> byte 458, high nibble.
     r = _one_code_record("boost", 9, 30, 0x5, 32)
-    assert list(np.nonzero(r)[0]) == [2048 + 457] and r[2048 + 457] == 0x50
+    assert list(np.nonzero(r)[0]) == [2048 + 458] and r[2048 + 458] == 0x50
     # boost[token 20][slot 41] = 0x3 (n_hi 48: one full block, then a half):
     # slot 41 = 32 + 8*1 + 1 -> w = 1, e = 1; token 20 = 16 + 4 -> combo B,
-    # chunk 16*1 + 4 = 20; byte 512*1 + 8*20 + 4 = 676; bits 16..19 -> byte
-    # 678, low nibble.
+    # chunk 16*1 + 4 = 20; byte 512*1 + 8*20 + 4 = 676; bits 0 + 8 + 0 =
+    # 8..11 -> byte 677, low nibble.
     r = _one_code_record("boost", 20, 41, 0x3, 48)
-    assert list(np.nonzero(r)[0]) == [2048 + 678] and r[2048 + 678] == 0x3
+    assert list(np.nonzero(r)[0]) == [2048 + 677] and r[2048 + 677] == 0x3
 
 
 def test_layout_metadata_offsets_eight_four():
