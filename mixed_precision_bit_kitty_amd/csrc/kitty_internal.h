@@ -39,7 +39,10 @@
 // The (hi_bit 8, lo_bit 4) pair ("Kitty -- Dynamic Channel-wise
 // Mixed-Precision Keys", table "Tuning avg_bits") stores 4-bit planes of the
 // same shape: a word holds ONE combo of 8 elements, element e at bit
-// 16*(e&1) + 4*(e>>1); a chunk is 32 B, combo A at word 2x and combo B at
+// 16*(e>>2) + 8*(e&1) + 4*((e>>1)&1), so that each byte holds two codes in
+// the low nibbles of the word and of the word shifted right by 4 (e4m3
+// bytes 0000cccc = c * 2^-9 for the fp8 conversion); a chunk is 32 B,
+// combo A at word 2x and combo B at
 // word 2x + 1 (same tokens and channels as above); boost words are pairs at
 // byte 8*(c*nf + b) (+4 for B), the half block at 512*nf + 8c.  Sizes: planes
 // 2048 B, boost 16n B; metadata as above; 5120 + 17n bytes in total.  In
