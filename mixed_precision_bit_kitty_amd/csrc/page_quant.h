@@ -33,6 +33,8 @@
 // nearest even.  Signed zeros of the inputs are read as +0.
 #pragma once
 
+#include <type_traits>
+
 #include "kitty_internal.h"
 
 namespace kitty {
@@ -120,15 +122,35 @@ struct Step {
   uint16_t s16;  // fp16 step
 };
 
-__device__ __forceinline__ Step make_step(float mn, float mx, float levels) {
+// Step of the range [mn, mx] over `levels` (L = 3, 15 or 255; inv_levels =
+// 1 / L rounded to float32): s16 = f16(r / L) with r = mx - mn, and the
+// float32 1 / s16, both correctly rounded, without the division sequence:
+// * r / L: q0 = r (1 / L), the remainder r - q0 L by an FMA (exact), and
+//   q0 + remainder (1 / L) by a second FMA.  This gives the correctly
+//   rounded quotient for every float32 r of the binade [1, 2) and each of
+//   the three L (checked exhaustively), hence for every finite r >= 0 here
+//   (r <= 131008; the steps scale exactly by powers of two, and r = 0 gives
+//   0).
+// * 1 / s: one Newton step y0 + (1 - s y0) y0, two FMAs, from v_rcp_f32
+//   (within 1 ulp) is correctly rounded for every positive finite fp16 s and
+//   every y0 within 1 ulp of 1 / s (checked exhaustively).
+__device__ __forceinline__ Step make_step(float mn, float mx, float levels, float inv_levels) {
 #pragma clang fp contract(off)
-  float r = mx - mn;
-  float q = r / levels;
-  uint16_t s16 = f2h(q);
-  float s = h2f(s16);
+  const float r = mx - mn;
+  const float q0 = r * inv_levels;
+  const float rem = __builtin_fmaf(-q0, levels, r);
+  float q = __builtin_fmaf(rem, inv_levels, q0);
+  // q is rounded to float32 and then to fp16 (two roundings, as the
+  // definition has them): the empty asm keeps the compiler from fusing the
+  // FMA and the conversion into one mixed-precision instruction
+  asm("" : "+v"(q));
+  const uint16_t s16 = f2h(q);
+  const float s = h2f(s16);
+  const float y0 = __builtin_amdgcn_rcpf(s);
+  const float inv = __builtin_fmaf(__builtin_fmaf(-s, y0, 1.0f), y0, y0);
   Step st;
   st.s16 = s16;
-  st.inv = (s != 0.0f) ? 1.0f / s : 0.0f;
+  st.inv = (s != 0.0f) ? inv : 0.0f;
   return st;
 }
 
@@ -157,13 +179,26 @@ __device__ __forceinline__ float add_hh(uint32_t a, uint32_t b) {  // (float)hal
 // (x >= mn, inv <= 2^24), and min(rne(t), L) = rne(min(t, L)) for an integer
 // L, so the clamp goes first and v_cvt_pk_u8_f32 (round half to even,
 // saturating to [0, 255]; checked on gfx950) rounds and packs in one
-// instruction.
-template <int HI>
+// instruction.  CLAMP false leaves the clamp out, for a step that
+// step_bounds_codes accepts.
+template <int HI, bool CLAMP = true>
 __device__ __forceinline__ uint32_t code_of(uint32_t w, float mn, float inv, float levels, uint32_t byte = 0, uint32_t into = 0) {
 #pragma clang fp contract(off)
   float t = sub_h<HI>(w, mn) * inv;
-  t = fminf(t, levels);
+  if constexpr (CLAMP) t = fminf(t, levels);
   return __builtin_amdgcn_cvt_pk_u8_f32(t, byte, into);
+}
+
+// True when the fp16 step s16 of make_step is zero or a normal number.
+// Then no code needs the clamp: for zero, inv = 0 and t = 0; for a normal
+// step, s16 is within 2^-11 (relative) of (max - min) / L, so with x <= max
+// t <= L (1 + 2^-11) (1 + 2^-24)^3 < L + 1/2 for every L <= 255, and
+// round-to-nearest-even gives at most L.  A subnormal step (rounding error up
+// to half its value) and an infinite one (inv = 0 against an infinite
+// difference) keep the clamp.
+__device__ __forceinline__ bool step_bounds_codes(uint16_t s16) {
+  const uint32_t e = s16 & 0x7C00u;
+  return (s16 & 0x7FFFu) == 0u || (e != 0u && e != 0x7C00u);
 }
 
 // 2-bit code words: element e of combo A sits at bit 16 (e >> 2) + 4 (e & 1)
@@ -418,7 +453,8 @@ __device__ __forceinline__ void quantize_keys_wave(RowSrc ks, uint8_t* __restric
 
   // ---------------- Key codes and metadata ---------------------------------
   const float L0 = h0 ? kHi : kLo, L1 = h1 ? kHi : kLo;
-  const Step st0 = make_step(mn0, mx0, L0), st1 = make_step(mn1, mx1, L1);
+  constexpr float kInvLo = 1.0f / kLo, kInvHi = 1.0f / kHi;
+  const Step st0 = make_step(mn0, mx0, L0, h0 ? kInvHi : kInvLo), st1 = make_step(mn1, mx1, L1, h1 ? kInvHi : kInvLo);
   constexpr float kBoostScale = (float)(1 << BITS);  // kscale = 2^lo_bit * step on boosted channels
   const uint16_t ks0 = h0 ? f2h(kBoostScale * h2f(st0.s16)) : st0.s16;
   const uint16_t ks1 = h1 ? f2h(kBoostScale * h2f(st1.s16)) : st1.s16;
@@ -438,17 +474,24 @@ __device__ __forceinline__ void quantize_keys_wave(RowSrc ks, uint8_t* __restric
   const uint32_t sh0 = h0 ? (uint32_t)BITS : 0u, sh1 = h1 ? (uint32_t)BITS : 0u;
   uint8_t* const bst0 = lds_boost + (w0 ? pos0 : NHI);  // column NHI: a lane's discarded stores
   uint8_t* const bst1 = lds_boost + (w1 ? pos1 : NHI);
+  // (two copies of the loop: without the clamp when every step of the wave
+  // allows it, the usual case, and with it)
+  auto key_codes = [&](auto clamp_c) {
+    constexpr bool kClamp = decltype(clamp_c)::value;
 #pragma unroll
-  for (int t = 0; t < 32; ++t) {
-    const uint32_t q = code_of<1>(xw[t], mn1, st1.inv, L1, 1, code_of<0>(xw[t], mn0, st0.inv, L0));  // bytes q0, q1
-    // exactly BITS bits per byte (the planes are packed without masking)
-    const uint32_t base = __builtin_amdgcn_ubfe(q, sh0, BITS) | (__builtin_amdgcn_ubfe(q, 8 + sh1, BITS) << 8);
-    *reinterpret_cast<uint16_t*>(lds_base + t * 128 + 2 * lane) = (uint16_t)base;
-    if (NHI > 0) {
-      bst0[t * boost_row(NHI)] = (uint8_t)q;
-      bst1[t * boost_row(NHI)] = (uint8_t)(q >> 8);
+    for (int t = 0; t < 32; ++t) {
+      const uint32_t q = code_of<1, kClamp>(xw[t], mn1, st1.inv, L1, 1, code_of<0, kClamp>(xw[t], mn0, st0.inv, L0));  // bytes q0, q1
+      // exactly BITS bits per byte (the planes are packed without masking)
+      const uint32_t base = __builtin_amdgcn_ubfe(q, sh0, BITS) | (__builtin_amdgcn_ubfe(q, 8 + sh1, BITS) << 8);
+      *reinterpret_cast<uint16_t*>(lds_base + t * 128 + 2 * lane) = (uint16_t)base;
+      if (NHI > 0) {
+        bst0[t * boost_row(NHI)] = (uint8_t)q;
+        bst1[t * boost_row(NHI)] = (uint8_t)(q >> 8);
+      }
     }
-  }
+  };
+  if (__ballot(!(step_bounds_codes(st0.s16) && step_bounds_codes(st1.s16))) == 0ull) key_codes(std::false_type{});
+  else key_codes(std::true_type{});
 
   // ---------------- Pack Key code planes from LDS ---------------------------
   wave_lds_sync();
@@ -537,6 +580,7 @@ __device__ __forceinline__ void quantize_values_wave(RowSrc vs, uint8_t* __restr
   wave_lds_sync();
 
   // ---------------- Value steps: one (token, group) per lane and pass -------
+  bool bounded = true;  // every step of this lane allows codes without the clamp
   {
     float* vstep = reinterpret_cast<float*>(lds + lds_vstep(NHI));  // [group][token] x (1 / step, min)
     uint16_t* vsc = reinterpret_cast<uint16_t*>(rec + off_vscale(NHI, BITS));
@@ -566,7 +610,8 @@ __device__ __forceinline__ void quantize_values_wave(RowSrc vs, uint8_t* __restr
       mxv = canon2(__builtin_bit_cast(uint32_t, mxv));
       const float mn = fminf((float)mnv[0], (float)mnv[1]);
       const float mx = fmaxf((float)mxv[0], (float)mxv[1]);
-      const Step st = make_step(mn, mx, kLo);
+      const Step st = make_step(mn, mx, kLo, 1.0f / kLo);
+      bounded = bounded && step_bounds_codes(st.s16);
       *reinterpret_cast<float2*>(vstep + 2 * (32 * gp + tp)) = make_float2(st.inv, mn);
       const int kap = kappa_of(tp);
       vsc[32 * gp + kap] = st.s16;
@@ -580,25 +625,33 @@ __device__ __forceinline__ void quantize_values_wave(RowSrc vs, uint8_t* __restr
     const int g = lane >> 4, u = lane & 15;
     const int c0 = 32 * g + u, c1 = c0 + 16;
     const floatx4* vstep = reinterpret_cast<const floatx4*>(lds + lds_vstep(NHI)) + 16 * g;  // two tokens per read
+    // (each code loop in two copies, as for the keys: without the clamp when
+    // every step of the page allows it)
+    const bool clamp = __ballot(!bounded) != 0ull;
     if constexpr (BITS == 2) {
       // Element e of word w (token tau(w, e)) goes to byte e & 3 of field
       // f[w][2 (e >> 2) + combo], which is byte 2 (e >> 2) + combo of the
       // word (field4 packs a field's four codes).
       uint32_t f[4][4] = {};
+      auto value_codes = [&](auto clamp_c) {
+        constexpr bool kClamp = decltype(clamp_c)::value;
 #pragma unroll
-      for (int t2 = 0; t2 < 16; ++t2) {
-        const floatx4 st2 = vstep[t2];  // (1 / step, min) of tokens 2 t2 and 2 t2 + 1
+        for (int t2 = 0; t2 < 16; ++t2) {
+          const floatx4 st2 = vstep[t2];  // (1 / step, min) of tokens 2 t2 and 2 t2 + 1
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const int t = 2 * t2 + k, kap = kappa_of(t), w = kap >> 3, e = kap & 7;
-          const uint16_t* r = reinterpret_cast<const uint16_t*>(vs.row(t));
-          const uint32_t y0 = r[c0], y1 = r[c1];
-          uint32_t& fa = f[w][2 * (e >> 2)];
-          uint32_t& fb = f[w][2 * (e >> 2) + 1];
-          fa = code_of<0>(y0, st2[2 * k + 1], st2[2 * k], kLo, e & 3, fa);
-          fb = code_of<0>(y1, st2[2 * k + 1], st2[2 * k], kLo, e & 3, fb);
+          for (int k = 0; k < 2; ++k) {
+            const int t = 2 * t2 + k, kap = kappa_of(t), w = kap >> 3, e = kap & 7;
+            const uint16_t* r = reinterpret_cast<const uint16_t*>(vs.row(t));
+            const uint32_t y0 = r[c0], y1 = r[c1];
+            uint32_t& fa = f[w][2 * (e >> 2)];
+            uint32_t& fb = f[w][2 * (e >> 2) + 1];
+            fa = code_of<0, kClamp>(y0, st2[2 * k + 1], st2[2 * k], kLo, e & 3, fa);
+            fb = code_of<0, kClamp>(y1, st2[2 * k + 1], st2[2 * k], kLo, e & 3, fb);
+          }
         }
-      }
+      };
+      if (clamp) value_codes(std::true_type{});
+      else value_codes(std::false_type{});
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const uint32_t word = field4(f[w][0]) | (field4(f[w][1]) << 8) | (field4(f[w][2]) << 16) | (field4(f[w][3]) << 24);
@@ -606,17 +659,22 @@ __device__ __forceinline__ void quantize_values_wave(RowSrc vs, uint8_t* __restr
       }
     } else {  // 4-bit: combo A (channel c0) at word 2g, combo B (c1) at 2g + 1 of a 32-byte chunk
       uint32_t a0[32], a1[32];
+      auto value_codes = [&](auto clamp_c) {
+        constexpr bool kClamp = decltype(clamp_c)::value;
 #pragma unroll
-      for (int t2 = 0; t2 < 16; ++t2) {
-        const floatx4 st2 = vstep[t2];
+        for (int t2 = 0; t2 < 16; ++t2) {
+          const floatx4 st2 = vstep[t2];
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const int t = 2 * t2 + k;
-          const uint16_t* r = reinterpret_cast<const uint16_t*>(vs.row(t));
-          a0[t] = code_of<0>(r[c0], st2[2 * k + 1], st2[2 * k], kLo);
-          a1[t] = code_of<0>(r[c1], st2[2 * k + 1], st2[2 * k], kLo);  // codes <= 15: no masking needed below
+          for (int k = 0; k < 2; ++k) {
+            const int t = 2 * t2 + k;
+            const uint16_t* r = reinterpret_cast<const uint16_t*>(vs.row(t));
+            a0[t] = code_of<0, kClamp>(r[c0], st2[2 * k + 1], st2[2 * k], kLo);
+            a1[t] = code_of<0, kClamp>(r[c1], st2[2 * k + 1], st2[2 * k], kLo);  // codes <= 15: no masking needed below
+          }
         }
-      }
+      };
+      if (clamp) value_codes(std::true_type{});
+      else value_codes(std::false_type{});
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         uint32_t wa = 0, wb = 0;

@@ -82,6 +82,8 @@ def test_edge_values():
     v[0, 1, 32:64, :] = (rng.standard_normal((32, 128)) * 60000 / 4).clip(-60000, 60000).astype(np.float16)
     v[0, 0, 40, :] = np.float16(3.0)                         # constant value group row
     v[0, 0, 41, :32] = np.float16(-0.0)
+    v[0, 0, 42, :32] = np.float16(0.0)
+    v[0, 0, 42, 5] = np.float16(7 * 2.0 ** -24)              # value step rounds down -> clamp
     k[0, 0, 64:96, :] = k[0, 0, 64:65, :]                     # identical tokens in a page
     q = (rng.standard_normal((1, 8, 128))).astype(np.float16)
     for n_hi in (0, 32, 128):

@@ -640,6 +640,40 @@ def test_clamp_when_subnormal_step_rounds_down():
         assert float(s16) == (2 * ulp if L == 3 else ulp)
 
 
+def test_clamp_idle_for_normal_steps():
+    # The quantizer kernels leave the clamp out of a page whose steps are all
+    # zero or normal fp16 numbers.  That relies on the largest scaled value,
+    # (max - min) * (1 / step), staying below L + 1/2, so that round to
+    # nearest even never passes L.  It is checked here for every float32
+    # significand of max - min in the binade [1, 2), whose steps are normal;
+    # the float32 operations and the fp16 rounding of a normal step scale
+    # exactly by powers of two, and a random sample over the other binades
+    # with normal steps agrees.
+    def top_scaled(r, L):
+        q = (r / np.float32(L)).astype(np.float32)
+        s16 = q.astype(np.float16)
+        inv = (np.float32(1.0) / s16.astype(np.float32)).astype(np.float32)
+        return (r * inv).astype(np.float32), s16
+
+    r = (np.float32(1.0) + np.arange(2 ** 23, dtype=np.float32) * np.float32(2.0 ** -23)).astype(np.float32)
+    rng = np.random.default_rng(0)
+    rs = np.ldexp(r[rng.integers(0, 2 ** 23, 1 << 20)], rng.integers(-24, 17, 1 << 20)).astype(np.float32)
+    for L in (3, 15, 255):
+        t, s16 = top_scaled(r, L)
+        assert np.all(np.isfinite(s16)) and np.all(np.abs(s16) >= np.float16(2.0 ** -14))
+        assert float(t.max()) < L + 0.5
+        t, s16 = top_scaled(rs, L)
+        normal = np.isfinite(s16) & (s16 >= np.float16(2.0 ** -14))
+        assert normal.sum() > (1 << 19) and float(t[normal].max()) < L + 0.5
+        # the oracle's own codes at the top of such ranges stay exact
+        for x in (np.array([0.0, 1.0], np.float32), np.array([0.0, 1.9990234], np.float32)):
+            q, _ = O.quantize_levels(x, x.min(), x.max(), L)
+            assert q.max() == L
+    # and a subnormal step does need it (the counterexample above)
+    t, _ = top_scaled(np.array([7 * 2.0 ** -24], np.float32), 3)
+    assert float(t[0]) >= 3.5
+
+
 def test_negative_zero_read_as_positive_zero():
     # A page whose minimum is a signed zero stores kmin = +0 (0x0000).
     x = np.abs(_page(6)[0])
