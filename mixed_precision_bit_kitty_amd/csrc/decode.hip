@@ -118,6 +118,19 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
   asm("" : "+v"(x));
   return x;
 }
+typedef __attribute__((address_space(3))) const _Float16 lds_half;  // an fp16 in LDS (32-bit address)
+// base + byte K of d in one VALU instruction (an SDWA add with a byte source
+// select; the compiler splits it into an extract and an add).  VALU-only
+// inline asm.
+template <int K>
+__device__ __forceinline__ uint32_t add_byte(uint32_t d, uint32_t base) {
+  uint32_t r;
+  if constexpr (K == 0) asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0 src1_sel:DWORD" : "=v"(r) : "v"(d), "v"(base));
+  else if constexpr (K == 1) asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:DWORD" : "=v"(r) : "v"(d), "v"(base));
+  else if constexpr (K == 2) asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2 src1_sel:DWORD" : "=v"(r) : "v"(d), "v"(base));
+  else asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3 src1_sel:DWORD" : "=v"(r) : "v"(d), "v"(base));
+  return r;
+}
 // MFMA operand from one 4-bit code word (one combo; element e at bit 16 (e
 // >> 2) + 8 (e & 1) + 4 ((e >> 1) & 1), so byte k < 2 holds elements k and
 // k + 2, byte 2 + k elements 4 + k and 6 + k).  The word masked to the low
@@ -603,9 +616,15 @@ void decode_kernel(DecodeParams p) {
       const int q0 = 32 * k2 + 8 * w;
       half8 v = {};
       if (q0 < NHI) {
-        const u32x2 ib = bi.ib[k2];
+        // byte offsets 2 idx of the eight channels: every index is below
+        // 128, so one shift doubles the four bytes of a word without a
+        // carry, and one SDWA add per channel forms its LDS address
+        const uint32_t d0 = bi.ib[k2][0] << 1, d1 = bi.ib[k2][1] << 1;
+        const uint32_t qb = (uint32_t)(uintptr_t)(const lds_half*)qrow;  // LDS byte address
+        const uint32_t ad[8] = {add_byte<0>(d0, qb), add_byte<1>(d0, qb), add_byte<2>(d0, qb), add_byte<3>(d0, qb),
+                                add_byte<0>(d1, qb), add_byte<1>(d1, qb), add_byte<2>(d1, qb), add_byte<3>(d1, qb)};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = qrow[opaque(__builtin_amdgcn_ubfe(ib[j >> 2], 8 * (j & 3), 7))];
+        for (int j = 0; j < 8; ++j) v[j] = *(const lds_half*)(uintptr_t)ad[j];
       }
       bb[k2] = v;
       if constexpr (BITS == 2) {
@@ -616,15 +635,19 @@ void decode_kernel(DecodeParams p) {
         else bw[k2] = lane < 32 ? *reinterpret_cast<const u32x2*>(S + off_kboost(4) + 512 * NF + 8 * lane) : u32x2{};
       }
     }
-    // the gathers (a second LDS round trip after the index read) issue with
-    // the limb reads, ahead of the MFMAs that do not need them
+    // the gathers (a second LDS round trip after the index read) and, when
+    // registers allow (at most two boost blocks), the minimum reads issue
+    // with the limb reads, ahead of the MFMAs
+    constexpr bool kEarlyMin = NB <= 2;
+    auto kmin_of = [&](int kb) { return *reinterpret_cast<const half8*>(S + off_kmin(NHI, BITS) + 2 * (32 * kb + 8 * w)); };
+    half8 kmins[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      if constexpr (kEarlyMin) kmins[kb] = kmin_of(kb);
     __builtin_amdgcn_sched_barrier(0);
     floatx4 cmin = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const half8 kmin = *reinterpret_cast<const half8*>(S + off_kmin(NHI, BITS) + 2 * (32 * kb + 8 * w));
-      cmin = mfma(bq_plain[kb], kmin, cmin);
-    }
+    for (int kb = 0; kb < 4; ++kb) cmin = mfma(bq_plain[kb], kEarlyMin ? kmins[kb] : kmin_of(kb), cmin);
     floatx4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -696,13 +719,20 @@ void decode_kernel(DecodeParams p) {
   auto pv = [&](const uint8_t* S) KITTY_INLINE {
     const u32x4 vw = *reinterpret_cast<const u32x4*>(S + off_v(NHI, BITS) + 16 * BITS / 2 * lane);
     const u32x4 vw2 = BITS == 4 ? *reinterpret_cast<const u32x4*>(S + off_v(NHI, BITS) + 32 * lane + 16) : u32x4{};
-    half8 bg0 = {};
+    // columns 0..7: p * vscale limbs of group g; 8..15: p limbs for the
+    // correction (group 0), zeros (groups 1..3)
+    half8 bgs[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) bgs[g] = *reinterpret_cast<const half8*>(g == 0 ? b_src : b_rest + g * b_stride);
+    // correction operand: rows 0..3 the page's vmin of group n; the other
+    // rows read zeros (the codes carry no offset)
+    const uint8_t* src = n < 4 ? S + off_vmin(NHI, BITS) + 2 * (32 * n + 8 * w) : reinterpret_cast<const uint8_t*>(zrow);
+    const half8 a = *reinterpret_cast<const half8*>(src);
+    // every operand read is issued before the first MFMA: one LDS round trip
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      // columns 0..7: p * vscale limbs of group g; 8..15: p limbs for the
-      // correction (group 0), zeros (groups 1..3)
-      const half8 bg = *reinterpret_cast<const half8*>(g == 0 ? b_src : b_rest + g * b_stride);
-      if (g == 0) bg0 = bg;
+      const half8 bg = bgs[g];
       if constexpr (BITS == 2) {
         const Fp4Word f = fp4_split(vw[g]);
         st.o[2 * g] = mfma(fp4_operand<0>(f, 2.0f), bg, st.o[2 * g]);
@@ -714,11 +744,7 @@ void decode_kernel(DecodeParams p) {
         st.o[2 * g + 1] = mfma(fp8_operand(wb, 512.0f), bg, st.o[2 * g + 1]);
       }
     }
-    // correction operand: rows 0..3 the page's vmin of group n; the other
-    // rows read zeros (the codes carry no offset)
-    const uint8_t* src = n < 4 ? S + off_vmin(NHI, BITS) + 2 * (32 * n + 8 * w) : reinterpret_cast<const uint8_t*>(zrow);
-    const half8 a = *reinterpret_cast<const half8*>(src);
-    st.corr = mfma(a, bg0, st.corr);
+    st.corr = mfma(a, bgs[0], st.corr);
   };
   // one page through the whole contraction
   // (all the page's reads of the record come before the first limb write:
