@@ -285,6 +285,8 @@ __device__ __forceinline__ float head_of_column(float v_row, int n) {
 // column n, so their rescale factor is read from that head's row.
 constexpr float kSlack = 8.0f;
 constexpr float kVsSafe = 255.5f;
+constexpr uint32_t kVsSafeBits = 0x5BFCu;  // fp16 bits of kVsSafe
+static_assert(kVsSafe == 511.0f / 2.0f, "kVsSafe = 255.5: fp16 0x5BFC (exponent 22, mantissa 0x3FC)");
 __device__ __forceinline__ void softmax_step(WaveState& st, float& s0, float& s1, float sl2, int n,
                                              float slack = kSlack) {
   const float mx = row_max16(fmaxf(s0, s1)) * sl2;
@@ -698,9 +700,14 @@ void decode_kernel(DecodeParams p) {
     return v;
   };
   auto page_slack = [&](const VScales& v) KITTY_INLINE {
-    const half2v a = __builtin_elementwise_max(__builtin_elementwise_max(v.g[0], v.g[1]),
-                                               __builtin_elementwise_max(v.g[2], v.g[3]));
-    return __ballot((float)a[0] > kVsSafe || (float)a[1] > kVsSafe) ? 0.0f : kSlack;  // steps are >= 0
+    // steps are >= 0 (and not NaN), so their fp16 bit patterns order like
+    // their values: an unsigned maximum and one compare with kVsSafe's bits
+    typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+    auto bits = [](half2v x) { return __builtin_bit_cast(u16x2, x); };
+    const u16x2 a = __builtin_elementwise_max(__builtin_elementwise_max(bits(v.g[0]), bits(v.g[1])),
+                                              __builtin_elementwise_max(bits(v.g[2]), bits(v.g[3])));
+    const uint32_t m = a[0] > a[1] ? a[0] : a[1];
+    return __ballot(m > kVsSafeBits) ? 0.0f : kSlack;
   };
   auto produce_pt = [&](const VScales& vsc, float s0, float s1) KITTY_INLINE {
     const PLimbs pl = p_limbs(s0, s1);
