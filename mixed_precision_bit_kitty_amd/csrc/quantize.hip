@@ -67,33 +67,33 @@ __device__ __forceinline__ uint8_t* record_of(const QuantizeParams& p, int b, in
   return p.pages + (int64_t)phys * p.page_bytes + (int64_t)h * rec_bytes(boost_slots(p.n_hi), p.lo_bit);
 }
 
-// Chunk sums without carries or lane masks.  For a = M 2^s (the fixed-point
-// value of one fp16 key, as in accumulate): sum a is kept as sum (a ^ m) plus
-// the count of negative terms (m = -1 for a negative key, and a ^ -1 = -a - 1);
-// sum a^2 is kept as S0 + 2^32 S1, where a^2 = (M M << (2s & 31)) << (2s & 32)
-// adds its shifted product (below 2^53) to S0 or S1.  Neither 64-bit
-// accumulator can overflow within a chunk (256 terms below 2^53).
+// Chunk sums in float64, exactly.  For a = k 2^24 (the fixed-point value of
+// one fp16 key, as in accumulate: an integer, |a| < 2^40) split as a = h 2^20
+// + l with h = trunc(a / 2^20) and |h|, |l| < 2^20 (both with a's sign):
+// a^2 = h^2 2^40 + 2 h l 2^20 + l^2, and every sum below stays an integer of
+// magnitude under 2^46 for a lane's 32 terms, so each float64 add and FMA is
+// exact (float64 runs at the float32 vector rate on this part, and the
+// integer form took 64-bit shifts, masks and carries per term).
 struct ChunkSums {
-  uint64_t x1;    // sum of a ^ m
-  uint32_t nneg;  // negative terms
-  uint64_t s0, s1;
+  double s1;  // sum a
+  double hh;  // sum h^2
+  double hl;  // sum h l (>= 0: h and l share a's sign)
+  double ll;  // sum l^2
 };
 __device__ __forceinline__ void chunk_add(uint32_t h16, ChunkSums& c) {
-  const uint32_t e = (h16 >> 10) & 31u, m = h16 & 1023u;
-  const uint32_t nrm = (e + 31u) >> 5;  // 1 for a normal value (e >= 1), else 0
-  const uint32_t M = m | (nrm << 10);   // with its implicit bit
-  const uint32_t sh = e - nrm;          // a = M 2^sh
-  const uint64_t a = (uint64_t)M << sh;
-  const uint32_t neg = (uint32_t)((int32_t)(h16 << 16) >> 31);  // all ones for a negative key
-  const uint64_t neg64 = ((uint64_t)neg << 32) | neg;
-  c.x1 += a ^ neg64;
-  c.nneg -= neg;
-  const uint32_t sq = 2u * sh;
-  const uint64_t t = (uint64_t)(M * M) << (sq & 31u);
-  const uint32_t him = (uint32_t)((int32_t)(sq << 26) >> 31);  // all ones when sq >= 32
-  const uint64_t hi = ((uint64_t)him << 32) | him;
-  c.s0 += t & ~hi;
-  c.s1 += t & hi;
+  const double a = (double)(float)__builtin_bit_cast(_Float16, (uint16_t)h16) * 16777216.0;  // exact
+  c.s1 += a;
+  const double h = __builtin_trunc(a * 0x1p-20);
+  const double l = __builtin_fma(h, -1048576.0, a);
+  c.hh = __builtin_fma(h, h, c.hh);
+  c.hl = __builtin_fma(h, l, c.hl);
+  c.ll = __builtin_fma(l, l, c.ll);
+}
+// an integral float64 of magnitude below 2^53 as int64, exactly
+__device__ __forceinline__ int64_t exact_i64(double x) {
+  const double hi = __builtin_floor(x * 0x1p-32);
+  const double lo = __builtin_fma(hi, -4294967296.0, x);  // in [0, 2^32)
+  return (int64_t)(((uint64_t)(uint32_t)(int32_t)hi << 32) | (uint64_t)(uint32_t)lo);
 }
 
 // grid (chunks, Hkv, batch), 4 waves.  Lane (cb = lane & 31, tg = lane >> 5)
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256) void key_chunk_kernel(QuantizeParams p) {
   const _Float16* kb = p.k + ((size_t)b * p.n_kv_heads + h) * (size_t)p.S * kHeadDim + 4 * cb;
   ChunkSums acc[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) acc[e] = ChunkSums{0ull, 0u, 0ull, 0ull};
+  for (int e = 0; e < 4; ++e) acc[e] = ChunkSums{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
   for (int pg = 0; pg < 2; ++pg) {
     const int t0 = kChunkTokens * chunk + kPageTokens * (2 * wave + pg);
@@ -132,8 +132,9 @@ __global__ __launch_bounds__(256) void key_chunk_kernel(QuantizeParams p) {
   u128 s2[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    s1[e] = (int64_t)(acc[e].x1 + acc[e].nneg);
-    s2[e] = (u128)acc[e].s0 + ((u128)acc[e].s1 << 32);
+    s1[e] = exact_i64(acc[e].s1);
+    s2[e] = ((u128)(uint64_t)exact_i64(acc[e].hh) << 40) + ((u128)(uint64_t)exact_i64(acc[e].hl) << 21) +
+            (u128)(uint64_t)exact_i64(acc[e].ll);
     s1[e] += (int64_t)shfl_xor_u64((uint64_t)s1[e], 32);  // the other token group
     const uint64_t lo = shfl_xor_u64((uint64_t)s2[e], 32), hi = shfl_xor_u64((uint64_t)(s2[e] >> 64), 32);
     s2[e] += ((u128)hi << 64) | lo;

@@ -12,8 +12,13 @@ of that step.  The kernels use no division instruction:
 * 1 / s as y0 = v_rcp_f32(s) (within 1 ulp), then y = RN(y0 + RN(1 - s y0) y0)
   (two FMAs).
 
-These tests check both against exact rational arithmetic for every input the
-kernels can meet.  Every operation scales exactly by powers of two while its
+The running ranking mode's key statistics kernel sums a = k 2^24 and a^2
+exactly in float64 (a split of a into two halves keeps every term and every
+partial sum an exact float64 integer); the last test checks that against
+Python integers.
+
+The first tests check both steps against exact rational arithmetic for
+every input the kernels can meet.  Every operation scales exactly by powers of two while its
 result stays a normal float32 (r <= 131008, 1 / s <= 2^24 for fp16 steps), so
 all float32 significands of one binade cover r, and all fp16 significands (the
 subnormal ones are normal float32 significands too) cover s.
@@ -98,3 +103,44 @@ def test_reciprocal_by_one_newton_step_is_correctly_rounded():
             assert y == ref, (m, float(c))
             checked += 1
     assert checked >= 2048
+
+
+def _f64_chunk_sums(h16):
+    """The running-mode chunk sums as the key statistics kernel forms them in
+    float64: a = k 2^24, h = trunc(a / 2^20), l = a - h 2^20, then sum a,
+    sum h^2, sum h l and sum l^2 by float64 adds and fused multiply-adds,
+    and the 128-bit s2 = hh 2^40 + hl 2^21 + ll.  numpy's float64 add and
+    multiply round like the kernel's; every product here (below 2^40) and
+    every partial sum (below 2^46) is an exact float64 integer, so the
+    separate multiply and add below equal the kernel's FMAs."""
+    a = h16.view(np.float16).astype(np.float64) * 2.0 ** 24
+    h = np.trunc(a * 2.0 ** -20)
+    l = a - h * 2.0 ** 20
+    s1 = hh = hl = ll = 0.0
+    for i in range(len(a)):
+        s1 += a[i]
+        hh += h[i] * h[i]
+        hl += h[i] * l[i]
+        ll += l[i] * l[i]
+    return int(s1), (int(hh) << 40) + (int(hl) << 21) + int(ll), (h, l)
+
+
+def test_running_chunk_sums_in_float64_are_exact():
+    # against exact integer sums of a and a^2 (a = k 2^24) for 32-term chunks
+    # (one lane's terms of one channel): random keys of every magnitude,
+    # the largest values, mixed signs and subnormals
+    rng = np.random.default_rng(11)
+    finite = np.arange(0x10000, dtype=np.uint32)
+    finite = finite[(finite & 0x7C00) != 0x7C00].astype(np.uint16)  # every finite fp16
+    chunks = [rng.choice(finite, 32) for _ in range(400)]
+    chunks.append(np.full(32, 0x7BFF, np.uint16))  # 65504 everywhere
+    chunks.append(np.full(32, 0xFBFF, np.uint16))  # -65504 everywhere
+    chunks.append(np.array([0x7BFF, 0xFBFF] * 16, np.uint16))
+    chunks.append(np.arange(1, 33, dtype=np.uint16))  # subnormals
+    chunks.append(np.array([0x8000, 0x0000] * 16, np.uint16))  # signed zeros
+    for c in chunks:
+        s1, s2, (h, l) = _f64_chunk_sums(c)
+        ints = [int(Fraction(float(v)) * 2 ** 24) for v in c.view(np.float16)]
+        assert s1 == sum(ints)
+        assert s2 == sum(v * v for v in ints)
+        assert np.all(np.abs(h) < 2 ** 20) and np.all(np.abs(l) < 2 ** 20) and np.all(h * l >= 0)
