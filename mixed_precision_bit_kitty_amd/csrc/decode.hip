@@ -26,17 +26,20 @@
 // One wave = one (sequence, KV head, group of <= 4 query heads, range of
 // pages); the last wave of each (sequence, KV head, head group) also attends
 // over the fp16 tail page (first, while its first pages load) and takes a
-// smaller page range.  Lane l: column n = l & 15, row group w = l >> 4.  QK^T is computed
-// transposed (rows = 16 tokens, columns = head x limb, columns 8..15 repeat
-// 0..7), so after one DPP add every lane holds the logits of tokens
-// tau(w, 0..7) of head n & 3 -- exactly the K slice it feeds to PV.
+// smaller page range.  Lane l: n = l & 15, w = l >> 4.  QK^T has the query
+// limbs as rows (4 head + limb; the other two rows of each head read zeros)
+// and the page's tokens as columns, so lane (n, w) ends with the logits of
+// head w at tokens n and n + 16; PV has the channels as rows and (head,
+// limb) as columns (see decode_kernel).
 //
 // Pages stream through a per-wave LDS ring with global_load_lds_dwordx4
 // (kRing pages in flight); per page the limbs are computed once per
 // (head, channel) and per (head, token, group) and exchanged through LDS.
 // Online softmax runs in the log2 domain and rescales only when the max
-// grows.  Each wave writes (m, l, O) for its page range; the last wave of a
-// (sequence, KV head, head group) merges them (log-sum-exp) into the output.
+// grows past a slack.  Each wave writes (m, l, O) for its page range; the
+// workgroup merges its waves' partials (log-sum-exp), and with several
+// workgroups per (sequence, KV head, head group) the last one to arrive
+// merges theirs into the output.
 #include <type_traits>
 
 #include "kitty_internal.h"
@@ -537,7 +540,6 @@ void decode_kernel(DecodeParams p) {
     }
   }
   const float qsc = __builtin_ldexpf(1.0f, qe);
-  // 4-bit codes: mask of mantissa bits 6..9 / 22..25, exponents of 16 + c and (16 + c) / 16
   const float sl2 = (1.0f / sqrtf((float)kHeadDim)) * kLog2e;
   // PV B operand source: lanes n < 8 read the group's p * vscale limbs, lanes
   // n >= 8 the p limbs (same address for every group)

@@ -29,8 +29,9 @@
 //    words with coalesced 16-byte stores.
 //
 // All float32 arithmetic here is separately rounded (no contraction); the
-// division is the correctly rounded one; fp32 -> fp16 conversion rounds to
-// nearest even.  Signed zeros of the inputs are read as +0.
+// step's quotient and reciprocal are the correctly rounded ones, formed
+// without a division instruction (see make_step); fp32 -> fp16 conversion
+// rounds to nearest even.  Signed zeros of the inputs are read as +0.
 #pragma once
 
 #include <type_traits>
