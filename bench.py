@@ -18,7 +18,8 @@ reported beside the headline as context.  ``--workload`` / ``--batch``
 select another configuration; ``--lo-bit 4`` runs the (hi_bit 8, lo_bit 4)
 pair instead of (4, 2); ``--rank-mode running`` the running-variance ranking
 instead of per-page ranking; ``--ceiling`` times only the read-only kernels
-over a sweep of launch shapes.
+over a sweep of launch shapes, and the prefill quantizer's read-and-write
+stream without its arithmetic.
 To keep reads coming from HBM rather than the 256 MB Infinity Cache, the
 steps rotate over L independent layer caches totalling >= 1 GiB.
 
@@ -441,14 +442,62 @@ def read_ceiling(configs, gib=2, reps=10):
     return out
 
 
+def stream_ceiling(gib=2, read_unit=16384, write_unit=3360, reps=10):
+    """GB/s (read + written bytes) of the prefill quantizer's traffic without
+    its arithmetic: one block per 16 KiB unit (a page-head's fp16 K and V)
+    that writes a 3360-byte record-sized output (kitty_stream_ceiling), over
+    `gib` GiB read; the average of `reps` launches timed with HIP events on
+    the launch stream (after one untimed launch)."""
+    import torch
+    from mixed_precision_bit_kitty_amd import binding
+    lib = binding.load_bench()
+    units = (gib << 30) // read_unit
+    src = torch.empty(units * read_unit, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty(units * write_unit, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        rc = lib.kitty_stream_ceiling(src.data_ptr(), dst.data_ptr(), units, read_unit, write_unit, stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"kitty_stream_ceiling returned {rc}")
+    launch()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        launch()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    moved = units * (read_unit + write_unit)
+    gbs = moved / (ms * 1e-3) / 1e9
+    print(f"[bench] stream ceiling stream_kernel<{read_unit // 2048}>: {ms * 1e3:.1f} us per {units} units "
+          f"({read_unit} B read + {write_unit} B written each), {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.3f} of peak)",
+          file=sys.stderr, flush=True)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"kernel": f"stream_kernel<{read_unit // 2048}>", "units": units, "read_bytes": read_unit,
+            "write_bytes": write_unit, "gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "us": round(ms * 1e3, 2), "bytes": moved}
+
+
 def bench_ceiling(args):
     res = read_ceiling(CEILING_SWEEP)
     best = max(res, key=lambda r: r["gbs"])
     best_lds = max((r for r in res if r["mode"] == "lds_records"), key=lambda r: r["gbs"])
+    stream = stream_ceiling()
+    if args.calibrate_copy:
+        import torch
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        bcopy = torch.empty_like(a)
+        bcopy.copy_(a)
+        torch.cuda.synchronize()
+        print("[bench] calibration copy: 1 GiB read + 1 GiB written", file=sys.stderr, flush=True)
+        del a, bcopy
     print(json.dumps({"metric": "HBM read-stream ceiling: GB/s of read-only kernels over 2 GiB",
                       "value": best["gbs"], "unit": "GB/s", "n_gpus": 1, "higher_is_better": True,
                       "frac_of_hbm_peak": best["frac"], "best": best, "best_lds_records": best_lds,
-                      "sweep": res}), flush=True)
+                      "sweep": res, "read_write_stream": stream}), flush=True)
 
 
 def _workload_key(args, w, B):
@@ -486,7 +535,8 @@ def main():
     ap.add_argument("--quantize", action="store_true",
                     help="time kitty_quantize_pages (prefill of the whole batch) instead of the decode step")
     ap.add_argument("--ceiling", action="store_true",
-                    help="time only the read-only kernels (HBM read-stream ceiling) over a sweep of launch shapes")
+                    help="time only the read-only kernels (HBM read-stream ceiling) over a sweep of launch shapes, "
+                         "and the prefill quantizer's read-and-write stream without its arithmetic")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",

@@ -1,7 +1,8 @@
 /*
- * kitty_bench.h -- measurement entry point of the Kitty library (gfx950):
+ * kitty_bench.h -- measurement entry points of the Kitty library (gfx950):
  * the HBM read-stream ceiling that the decode kernel's bandwidth is judged
- * against.  Not part of the cache's hot path; bench.py --ceiling calls it.
+ * against, and the read-and-write stream of the prefill quantizer.  Not
+ * part of the cache's hot path; bench.py --ceiling calls them.
  *
  * "Kitty: Accurate and Efficient 2-bit KV Cache Quantization with Dynamic
  * Channel-wise Precision Boost", Abstract: the KV cache is the dominant
@@ -18,6 +19,8 @@
 extern "C" {
 #endif
 
+/* Every access of these kernels carries the non-temporal cache hint (the
+ * data is touched once), as the decode and quantize kernels' streams do. */
 enum {
   KITTY_READ_VGPR = 0,       /* 16-byte loads into registers, `depth` in flight per lane, grid-stride */
   KITTY_READ_LDS_RECORDS = 1 /* 3360-byte records streamed into a `depth`-slot LDS ring per wave
@@ -37,6 +40,24 @@ enum {
  * launch) or KITTY_ERR_HIP (-4). */
 int kitty_read_ceiling(const void* src, size_t bytes, int32_t mode, int32_t waves_per_cu, int32_t depth,
                        uint32_t* sink, size_t sink_len, void* stream);
+
+/* The prefill quantizer's memory traffic without its arithmetic, the
+ * ceiling its bandwidth is judged against ("Kitty -- Dynamic Channel-wise
+ * Mixed-Precision Keys", How it works / Prefill phase: every page of fp16
+ * K and V is read once and one packed record is written per page and KV
+ * head).  `units` blocks of 128 threads; block u reads `read_bytes` at
+ * src + u * read_bytes (thread t XORs the 16-byte words t, t + 128, ...,
+ * every load issued before the first use) and writes `write_bytes` at
+ * dst + u * write_bytes: 16-byte word j is thread (j mod 128)'s XOR with
+ * each of its four 32-bit lanes XORed with j, so every load is live and the
+ * writes are real.  src, dst: device memory, 16-byte aligned, not
+ * overlapping; read_bytes = 2048 * w for w in {1, 2, 4, 8, 16, 32};
+ * write_bytes a multiple of 16 in [2048, 65536] (every thread writes, so
+ * every load is needed); 1 <= units < 2^31.
+ * Asynchronous on `stream`.  Returns 0, KITTY_ERR_INVALID_ARG (-1) for
+ * arguments outside these ranges (before any launch) or KITTY_ERR_HIP (-4). */
+int kitty_stream_ceiling(const void* src, void* dst, int64_t units, int32_t read_bytes, int32_t write_bytes,
+                         void* stream);
 
 #ifdef __cplusplus
 }

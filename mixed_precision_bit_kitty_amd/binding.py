@@ -116,12 +116,15 @@ def load(path=None):
 
 
 def load_bench():
-    """The library with the measurement entry point of include/kitty_bench.h
-    declared (kitty_read_ceiling)."""
+    """The library with the measurement entry points of include/kitty_bench.h
+    declared (kitty_read_ceiling, kitty_stream_ceiling)."""
     lib = load()
     f = lib.kitty_read_ceiling
     f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                   ctypes.c_size_t, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    f = lib.kitty_stream_ceiling
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
     f.restype = ctypes.c_int
     return lib
 

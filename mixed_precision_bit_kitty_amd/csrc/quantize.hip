@@ -20,18 +20,20 @@ using namespace pq;
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Copy the 8 KB of a page's values (32 contiguous rows) into LDS with the
-// LDS DMA path, 1 KB per instruction; returns once they have landed.
+// LDS DMA path, 1 KB per instruction, non-temporal (nt: the inputs are read
+// once); returns once they have landed.
+constexpr int kNt = 2;  // the nt bit of the cache-policy operand
 __device__ __forceinline__ void stage_value_page(const _Float16* src, uint8_t* dst, int lane) {
   const uint8_t* s0 = reinterpret_cast<const uint8_t*>(src) + 16 * lane;
   const uint8_t* s1 = s0 + 4096;
-  __builtin_amdgcn_global_load_lds(s0, (lds_void*)dst, 16, 0, 0);
-  __builtin_amdgcn_global_load_lds(s0, (lds_void*)dst, 16, 1024, 0);
-  __builtin_amdgcn_global_load_lds(s0, (lds_void*)dst, 16, 2048, 0);
-  __builtin_amdgcn_global_load_lds(s0, (lds_void*)dst, 16, 3072, 0);
-  __builtin_amdgcn_global_load_lds(s1, (lds_void*)(dst + 4096), 16, 0, 0);
-  __builtin_amdgcn_global_load_lds(s1, (lds_void*)(dst + 4096), 16, 1024, 0);
-  __builtin_amdgcn_global_load_lds(s1, (lds_void*)(dst + 4096), 16, 2048, 0);
-  __builtin_amdgcn_global_load_lds(s1, (lds_void*)(dst + 4096), 16, 3072, 0);
+  __builtin_amdgcn_global_load_lds(s0, (lds_void*)dst, 16, 0, kNt);
+  __builtin_amdgcn_global_load_lds(s0, (lds_void*)dst, 16, 1024, kNt);
+  __builtin_amdgcn_global_load_lds(s0, (lds_void*)dst, 16, 2048, kNt);
+  __builtin_amdgcn_global_load_lds(s0, (lds_void*)dst, 16, 3072, kNt);
+  __builtin_amdgcn_global_load_lds(s1, (lds_void*)(dst + 4096), 16, 0, kNt);
+  __builtin_amdgcn_global_load_lds(s1, (lds_void*)(dst + 4096), 16, 1024, kNt);
+  __builtin_amdgcn_global_load_lds(s1, (lds_void*)(dst + 4096), 16, 2048, kNt);
+  __builtin_amdgcn_global_load_lds(s1, (lds_void*)(dst + 4096), 16, 3072, kNt);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 

@@ -147,6 +147,13 @@ static void entry_validation() {
   CHECK(kitty_read_ceiling(pages, 4096, KITTY_READ_VGPR, 6, 2, sink, 4, nullptr) == KITTY_ERR_INVALID_ARG);
   CHECK(kitty_read_ceiling(pages, 4096, KITTY_READ_LDS_RECORDS, 13, 4, sink, 4, nullptr) == KITTY_ERR_INVALID_ARG);
   CHECK(kitty_read_ceiling(pages, 4096, 7, 8, 2, sink, 4, nullptr) == KITTY_ERR_INVALID_ARG);
+  alignas(256) static uint8_t other[4096];  // a destination apart from the source
+  CHECK(kitty_stream_ceiling(nullptr, other, 4, 2048, 2048, nullptr) == KITTY_ERR_INVALID_ARG);
+  CHECK(kitty_stream_ceiling(pages, other, 4, 3000, 2048, nullptr) == KITTY_ERR_INVALID_ARG);
+  CHECK(kitty_stream_ceiling(pages, other, 4, 2048, 2000, nullptr) == KITTY_ERR_INVALID_ARG);
+  CHECK(kitty_stream_ceiling(pages, other, 0, 2048, 2048, nullptr) == KITTY_ERR_INVALID_ARG);
+  CHECK(kitty_stream_ceiling(pages, pages + 2048, 4, 2048, 2048, nullptr) == KITTY_ERR_INVALID_ARG);  // overlap
+  CHECK(kitty_stream_ceiling(pages, other, (int64_t)1 << 40, 65536, 65536, nullptr) == KITTY_ERR_INVALID_ARG);
 }
 
 // The pool against a plain model: the set of free pages and each row's

@@ -18,7 +18,7 @@ FAKE = 0x7F0000000000  # an aligned non-null address that is never dereferenced
 
 def test_exports_every_declared_symbol():
     names = B.declared_symbols()
-    assert len(names) == 15
+    assert len(names) == 16
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -345,6 +345,25 @@ def test_read_ceiling_rejects_bad_arguments_before_launching():
     assert call(depth=3) == bad and call(depth=16) == bad
     assert call(mode=1, waves=13, depth=2) == bad and call(mode=1, waves=12, depth=5) == bad
     assert call(mode=1, waves=8, depth=2, nbytes=3344) == bad  # not one whole record
+
+
+def test_stream_ceiling_rejects_bad_arguments_before_launching():
+    """The read-and-write measurement entry point validates its arguments
+    before any HIP call."""
+    lib = B.load_bench()
+    ok = dict(src=FAKE, dst=FAKE + (1 << 32), units=1024, rb=16384, wb=3360)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.kitty_stream_ceiling(a["src"], a["dst"], a["units"], a["rb"], a["wb"], None)
+
+    bad = B.KITTY_ERR_INVALID_ARG
+    assert call(src=None) == bad and call(dst=None) == bad
+    assert call(src=FAKE + 8) == bad and call(dst=FAKE + (1 << 32) + 4) == bad
+    assert call(units=0) == bad and call(units=-1) == bad and call(units=1 << 31) == bad
+    assert call(rb=0) == bad and call(rb=2048 * 3) == bad and call(rb=16000) == bad and call(rb=2048 * 64) == bad
+    assert call(wb=2032) == bad and call(wb=3368 + 4) == bad and call(wb=65552) == bad
+    assert call(dst=FAKE + 4096) == bad  # overlaps the source
 
 
 def test_noalloc_step_rejects_before_any_hip_call():
