@@ -481,8 +481,54 @@ def stream_ceiling(gib=2, read_unit=16384, write_unit=3360, reps=10):
             "us": round(ms * 1e3, 2), "bytes": moved}
 
 
+def record_stream_at_size(n_records, waves=12, depth=2, gib=2, reps=20):
+    """The record stream alone (read_lds_kernel: 3360-byte records through a
+    per-wave LDS ring, one workgroup per CU as decode runs) at a decode
+    workload's size: each launch reads a different slice of `n_records`
+    records of a `gib` GiB buffer, so no launch finds its slice in the
+    256 MB Infinity Cache; the average of `reps` launches timed with HIP
+    events after one untimed launch.  The fixed costs of a launch (the first
+    records' latency, the drain) show against the bytes."""
+    import torch
+    from mixed_precision_bit_kitty_amd import binding
+    lib = binding.load_bench()
+    nbytes = n_records * 3360
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    nslices = (gib << 30) // nbytes
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def launch(i):
+        rc = lib.kitty_read_ceiling(buf.data_ptr() + (i % nslices) * nbytes, nbytes, 1, waves, depth, sink.data_ptr(),
+                                    sink.numel(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"kitty_read_ceiling returned {rc}")
+    launch(nslices - 1)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(reps):
+        launch(i)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(f"[bench] record stream read_lds_kernel<{depth}>, {waves} waves/CU: {ms * 1e3:.2f} us per {n_records} records "
+          f"({nbytes / 1e6:.1f} MB), {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.3f} of peak)", file=sys.stderr, flush=True)
+    del buf, sink
+    torch.cuda.empty_cache()
+    return {"kernel": f"read_lds_kernel<{depth}>", "waves_per_cu": waves, "records": n_records, "bytes": nbytes,
+            "us": round(ms * 1e3, 2), "gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+# record counts of the decode workloads (page-heads per launch): llama3_8b
+# (16 x 8 x 128), qwen3_8b (4 x 8 x 1024), batch_sweep at batch 16 and 128
+RECORD_SIZES = {"llama3_8b": 16384, "qwen3_8b": 32768, "batch_sweep_b16": 32768, "batch_sweep_b128": 262144}
+
+
 def bench_ceiling(args):
     res = read_ceiling(CEILING_SWEEP)
+    sized = {k: record_stream_at_size(n) for k, n in RECORD_SIZES.items()}
     best = max(res, key=lambda r: r["gbs"])
     best_lds = max((r for r in res if r["mode"] == "lds_records"), key=lambda r: r["gbs"])
     stream = stream_ceiling()
@@ -497,7 +543,7 @@ def bench_ceiling(args):
     print(json.dumps({"metric": "HBM read-stream ceiling: GB/s of read-only kernels over 2 GiB",
                       "value": best["gbs"], "unit": "GB/s", "n_gpus": 1, "higher_is_better": True,
                       "frac_of_hbm_peak": best["frac"], "best": best, "best_lds_records": best_lds,
-                      "sweep": res, "read_write_stream": stream}), flush=True)
+                      "sweep": res, "read_write_stream": stream, "record_stream_at_size": sized}), flush=True)
 
 
 def _workload_key(args, w, B):
