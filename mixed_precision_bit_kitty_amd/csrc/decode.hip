@@ -115,12 +115,6 @@ __device__ __forceinline__ half8 fp4_operand(Fp4Word s, float scale) {
   r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(s.odd, scale, 2 + COMBO));   // e 6, 7
   return __builtin_bit_cast(half8, r);
 }
-// A value the compiler may not re-derive (keeps a bitfield extract from being
-// rewritten into shift-and-mask pairs once it is scaled into an address).
-__device__ __forceinline__ uint32_t opaque(uint32_t x) {
-  asm("" : "+v"(x));
-  return x;
-}
 typedef __attribute__((address_space(3))) const _Float16 lds_half;  // an fp16 in LDS (32-bit address)
 // base + byte K of d in one VALU instruction (an SDWA add with a byte source
 // select; the compiler splits it into an extract and an add).  VALU-only
@@ -624,10 +618,12 @@ void decode_kernel(DecodeParams p) {
       const int q0 = 32 * k2 + 8 * w;
       half8 v = {};
       if (q0 < NHI) {
-        // byte offsets 2 idx of the eight channels: every index is below
-        // 128, so one shift doubles the four bytes of a word without a
-        // carry, and one SDWA add per channel forms its LDS address
-        const uint32_t d0 = bi.ib[k2][0] << 1, d1 = bi.ib[k2][1] << 1;
+        // byte offsets 2 idx of the eight channels: the index bytes, taken
+        // to their low 7 bits (a channel index is below 128, and the mask
+        // keeps every gather inside its 256-byte row whatever the record
+        // holds), double without a carry across bytes, and one SDWA add
+        // per channel forms its LDS address
+        const uint32_t d0 = (bi.ib[k2][0] & 0x7F7F7F7Fu) << 1, d1 = (bi.ib[k2][1] & 0x7F7F7F7Fu) << 1;
         const uint32_t qb = (uint32_t)(uintptr_t)(const lds_half*)qrow;  // LDS byte address
         const uint32_t ad[8] = {add_byte<0>(d0, qb), add_byte<1>(d0, qb), add_byte<2>(d0, qb), add_byte<3>(d0, qb),
                                 add_byte<0>(d1, qb), add_byte<1>(d1, qb), add_byte<2>(d1, qb), add_byte<3>(d1, qb)};
