@@ -655,6 +655,13 @@ def main():
             "traffic": committed_traffic(khash, "llama3_8b", "step")}
         c = read_ceiling([CEILING_DEFAULT])[0]
         res["read_ceiling"] = c
+        # the same number of records streamed alone (no arithmetic), and the
+        # headline's share of that rate
+        n_rec = B * Hkv * (ctx // 32) if args.lo_bit == 2 and n_hi == 32 else None
+        if n_rec:
+            rs = record_stream_at_size(n_rec)
+            rs["headline_share"] = round(r["gbs"] / rs["gbs"], 4)
+            res["record_stream_same_size"] = rs
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w.with_(batch=B), args.cpu_seconds, args.lo_bit, args.rank_mode)
