@@ -481,14 +481,16 @@ def stream_ceiling(gib=2, read_unit=16384, write_unit=3360, reps=10):
             "us": round(ms * 1e3, 2), "bytes": moved}
 
 
-def record_stream_at_size(n_records, waves=12, depth=2, gib=2, reps=20):
+def record_stream_at_size(n_records, waves=12, depth=2, gib=2, reps=20, heads_order=False):
     """The record stream alone (read_lds_kernel: 3360-byte records through a
     per-wave LDS ring, one workgroup per CU as decode runs) at a decode
     workload's size: each launch reads a different slice of `n_records`
     records of a `gib` GiB buffer, so no launch finds its slice in the
     256 MB Infinity Cache; the average of `reps` launches timed with HIP
     events after one untimed launch.  The fixed costs of a launch (the first
-    records' latency, the drain) show against the bytes."""
+    records' latency, the drain) show against the bytes.  heads_order: the
+    records in the decode kernel's order (8 interleaved per-head streams, a
+    wave reading records 8 apart; KITTY_READ_LDS_HEADS)."""
     import torch
     from mixed_precision_bit_kitty_amd import binding
     lib = binding.load_bench()
@@ -500,8 +502,8 @@ def record_stream_at_size(n_records, waves=12, depth=2, gib=2, reps=20):
     stream = torch.cuda.current_stream()
 
     def launch(i):
-        rc = lib.kitty_read_ceiling(buf.data_ptr() + (i % nslices) * nbytes, nbytes, 1, waves, depth, sink.data_ptr(),
-                                    sink.numel(), stream.cuda_stream)
+        rc = lib.kitty_read_ceiling(buf.data_ptr() + (i % nslices) * nbytes, nbytes, 2 if heads_order else 1, waves,
+                                    depth, sink.data_ptr(), sink.numel(), stream.cuda_stream)
         if rc != 0:
             raise RuntimeError(f"kitty_read_ceiling returned {rc}")
     launch(nslices - 1)
@@ -513,11 +515,13 @@ def record_stream_at_size(n_records, waves=12, depth=2, gib=2, reps=20):
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / reps
     gbs = nbytes / (ms * 1e-3) / 1e9
-    print(f"[bench] record stream read_lds_kernel<{depth}>, {waves} waves/CU: {ms * 1e3:.2f} us per {n_records} records "
+    order = ", heads order" if heads_order else ""
+    print(f"[bench] record stream read_lds_kernel<{depth}>{order}, {waves} waves/CU: {ms * 1e3:.2f} us per {n_records} records "
           f"({nbytes / 1e6:.1f} MB), {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.3f} of peak)", file=sys.stderr, flush=True)
     del buf, sink
     torch.cuda.empty_cache()
-    return {"kernel": f"read_lds_kernel<{depth}>", "waves_per_cu": waves, "records": n_records, "bytes": nbytes,
+    return {"kernel": f"read_lds_kernel<{depth}>", "order": "heads" if heads_order else "contiguous",
+            "waves_per_cu": waves, "records": n_records, "bytes": nbytes,
             "us": round(ms * 1e3, 2), "gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
@@ -529,6 +533,7 @@ RECORD_SIZES = {"llama3_8b": 16384, "qwen3_8b": 32768, "batch_sweep_b16": 32768,
 def bench_ceiling(args):
     res = read_ceiling(CEILING_SWEEP)
     sized = {k: record_stream_at_size(n) for k, n in RECORD_SIZES.items()}
+    sized["batch_sweep_b128_heads_order"] = record_stream_at_size(RECORD_SIZES["batch_sweep_b128"], heads_order=True)
     best = max(res, key=lambda r: r["gbs"])
     best_lds = max((r for r in res if r["mode"] == "lds_records"), key=lambda r: r["gbs"])
     stream = stream_ceiling()

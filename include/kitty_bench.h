@@ -22,15 +22,19 @@ extern "C" {
 /* Every access of these kernels carries the non-temporal cache hint (the
  * data is touched once), as the decode and quantize kernels' streams do. */
 enum {
-  KITTY_READ_VGPR = 0,       /* 16-byte loads into registers, `depth` in flight per lane, grid-stride */
-  KITTY_READ_LDS_RECORDS = 1 /* 3360-byte records streamed into a `depth`-slot LDS ring per wave
-                                with global_load_lds_dwordx4 (the decode kernel's memory path) */
+  KITTY_READ_VGPR = 0,        /* 16-byte loads into registers, `depth` in flight per lane, grid-stride */
+  KITTY_READ_LDS_RECORDS = 1, /* 3360-byte records streamed into a `depth`-slot LDS ring per wave
+                                 with global_load_lds_dwordx4 (the decode kernel's memory path) */
+  KITTY_READ_LDS_HEADS = 2    /* the same, in the decode kernel's order: the records form 8
+                                 interleaved streams (record 8j + h is page j of head h), and
+                                 the sweep takes them one stream after another, so a wave reads
+                                 records 8 apart, as a decode wave reads one KV head's pages */
 };
 
 /* Read `bytes` of device memory at `src` once (16-byte aligned, a multiple
  * of 16; LDS mode: the whole 3360-byte records it holds) with the access
  * pattern `mode`, on `waves_per_cu` waves per compute unit of the stream's
- * device (VGPR mode: 4..32, a multiple of 4; depth 1, 2, 4 or 8.  LDS mode:
+ * device (VGPR mode: 4..32, a multiple of 4; depth 1, 2, 4 or 8.  LDS modes:
  * one workgroup of 1..12 waves per CU; depth 1..4; waves * depth * 3360
  * bytes of LDS at most 160 KiB).  sink: device uint32 [sink_len], at least
  * one entry per workgroup (VGPR) or per wave (LDS); the kernels keep every

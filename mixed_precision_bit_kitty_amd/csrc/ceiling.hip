@@ -70,8 +70,11 @@ __device__ __forceinline__ void dma_rec(const uint8_t* rec, uint8_t* slot, int l
   if (16 * lane < kCeilRec - 3072) __builtin_amdgcn_global_load_lds(s, (lds_void*)slot, 16, 3072, kNt);
 }
 
-// Wave g of G takes records [g * n / G, (g + 1) * n / G) in order.
-template <int DEPTH>
+// Wave g of G takes records [g * n / G, (g + 1) * n / G) of the sweep in
+// order.  HEADS: sweep record r is record 8 (r mod P) + r / P with P =
+// n / 8 (the last n mod 8 records in place), so the sweep takes the 8
+// interleaved streams one after another and a wave reads records 8 apart.
+template <int DEPTH, bool HEADS>
 __global__ __launch_bounds__(64 * 12) void read_lds_kernel(const uint8_t* __restrict__ src, int64_t n_rec,
                                                            uint32_t* sink) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -81,9 +84,11 @@ __global__ __launch_bounds__(64 * 12) void read_lds_kernel(const uint8_t* __rest
   const int64_t r0 = g * n_rec / G, r1 = (g + 1) * n_rec / G;
   uint8_t* ring = lds + (size_t)wave * DEPTH * kCeilSlot;
   const int n = (int)(r1 - r0);
+  const int64_t P8 = n_rec / 8;
+  auto rec = [&](int64_t r) { return HEADS && r < 8 * P8 ? 8 * (r % P8) + r / P8 : r; };  // in [0, n_rec)
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d)
-    if (d < n) dma_rec(src + (r0 + d) * kCeilRec, ring + d * kCeilSlot, lane);
+    if (d < n) dma_rec(src + rec(r0 + d) * kCeilRec, ring + d * kCeilSlot, lane);
   uint32_t acc = 0;
   for (int i = 0; i < n; ++i) {
     const int ahead = min(DEPTH - 1, n - 1 - i);  // records issued after record i
@@ -97,7 +102,7 @@ __global__ __launch_bounds__(64 * 12) void read_lds_kernel(const uint8_t* __rest
     acc ^= *reinterpret_cast<const uint32_t*>(slot + 4 * lane);  // a read of the landed record
     if (i + DEPTH < n) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      dma_rec(src + (r0 + i + DEPTH) * kCeilRec, slot, lane);
+      dma_rec(src + rec(r0 + i + DEPTH) * kCeilRec, slot, lane);
     }
   }
   if (acc == kNever) sink[blockIdx.x * (blockDim.x >> 6) + wave] = acc;
@@ -128,14 +133,24 @@ hipError_t launch_stream(const void* src, void* dst, int64_t units, int nw, hipS
   return hipGetLastError();
 }
 
-template <int DEPTH>
+template <int DEPTH, bool HEADS>
 hipError_t launch_lds(const uint8_t* src, int64_t n_rec, int cus, int waves, uint32_t* sink, hipStream_t s) {
   const size_t lds = (size_t)waves * DEPTH * kCeilSlot;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&read_lds_kernel<DEPTH>),
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&read_lds_kernel<DEPTH, HEADS>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(read_lds_kernel<DEPTH>, dim3(cus), dim3(64 * waves), lds, s, src, n_rec, sink);
+  hipLaunchKernelGGL((read_lds_kernel<DEPTH, HEADS>), dim3(cus), dim3(64 * waves), lds, s, src, n_rec, sink);
   return hipGetLastError();
+}
+template <bool HEADS>
+hipError_t launch_lds_depth(const uint8_t* src, int64_t n_rec, int cus, int waves, int depth, uint32_t* sink,
+                            hipStream_t s) {
+  switch (depth) {
+    case 1: return launch_lds<1, HEADS>(src, n_rec, cus, waves, sink, s);
+    case 2: return launch_lds<2, HEADS>(src, n_rec, cus, waves, sink, s);
+    case 3: return launch_lds<3, HEADS>(src, n_rec, cus, waves, sink, s);
+    default: return launch_lds<4, HEADS>(src, n_rec, cus, waves, sink, s);
+  }
 }
 
 template <int DEPTH>
@@ -154,7 +169,7 @@ extern "C" int kitty_read_ceiling(const void* src, size_t bytes, int32_t mode, i
   if (mode == KITTY_READ_VGPR) {
     if (waves_per_cu < 4 || waves_per_cu > 32 || waves_per_cu % 4) return KITTY_ERR_INVALID_ARG;
     if (depth != 1 && depth != 2 && depth != 4 && depth != 8) return KITTY_ERR_INVALID_ARG;
-  } else if (mode == KITTY_READ_LDS_RECORDS) {
+  } else if (mode == KITTY_READ_LDS_RECORDS || mode == KITTY_READ_LDS_HEADS) {
     if (waves_per_cu < 1 || waves_per_cu > 12 || depth < 1 || depth > 4) return KITTY_ERR_INVALID_ARG;
     if ((size_t)waves_per_cu * depth * kitty::kCeilSlot > 160 * 1024) return KITTY_ERR_INVALID_ARG;
     if (bytes < (size_t)kitty::kCeilRec) return KITTY_ERR_INVALID_ARG;
@@ -179,12 +194,8 @@ extern "C" int kitty_read_ceiling(const void* src, size_t bytes, int32_t mode, i
     if (sink_len < (size_t)cus * waves_per_cu) return KITTY_ERR_INVALID_ARG;
     const int64_t n_rec = (int64_t)(bytes / kitty::kCeilRec);
     const uint8_t* p = static_cast<const uint8_t*>(src);
-    switch (depth) {
-      case 1: e = kitty::launch_lds<1>(p, n_rec, cus, waves_per_cu, sink, s); break;
-      case 2: e = kitty::launch_lds<2>(p, n_rec, cus, waves_per_cu, sink, s); break;
-      case 3: e = kitty::launch_lds<3>(p, n_rec, cus, waves_per_cu, sink, s); break;
-      default: e = kitty::launch_lds<4>(p, n_rec, cus, waves_per_cu, sink, s); break;
-    }
+    e = mode == KITTY_READ_LDS_HEADS ? kitty::launch_lds_depth<true>(p, n_rec, cus, waves_per_cu, depth, sink, s)
+                                     : kitty::launch_lds_depth<false>(p, n_rec, cus, waves_per_cu, depth, sink, s);
   }
   return e == hipSuccess ? KITTY_OK : KITTY_ERR_HIP;
 }

@@ -340,7 +340,8 @@ def test_read_ceiling_rejects_bad_arguments_before_launching():
     bad = B.KITTY_ERR_INVALID_ARG
     assert call(src=None) == bad and call(sink=None) == bad and call(src=FAKE + 8) == bad
     assert call(nbytes=0) == bad and call(nbytes=1000) == bad
-    assert call(mode=2) == bad and call(mode=-1) == bad
+    assert call(mode=3) == bad and call(mode=-1) == bad
+    assert call(mode=2, waves=13, depth=2) == bad  # the heads order has the LDS mode's limits
     assert call(waves=2) == bad and call(waves=33) == bad and call(waves=6) == bad
     assert call(depth=3) == bad and call(depth=16) == bad
     assert call(mode=1, waves=13, depth=2) == bad and call(mode=1, waves=12, depth=5) == bad

@@ -51,7 +51,7 @@ def test_read_ceiling_runs_and_leaves_the_sink():
     src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
     sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
-    for mode, waves, depth in [(0, 8, 4), (0, 32, 8), (1, 12, 3), (1, 8, 4)]:
+    for mode, waves, depth in [(0, 8, 4), (0, 32, 8), (1, 12, 3), (1, 8, 4), (2, 12, 2), (2, 4, 1)]:
         print(f"read ceiling: mode {mode}, {waves} waves/CU, depth {depth}", flush=True)
         rc = lib.kitty_read_ceiling(src.data_ptr(), nbytes, mode, waves, depth, sink.data_ptr(), sink.numel(),
                                     stream.cuda_stream)
