@@ -254,11 +254,11 @@ def test_decode_plan_fits_page_id_register():
         return n_wg | (W << 32)
 
     def weight(i):
-        return 9 if i < 4 else (7 if i < 8 else 5)
+        return 10 if i < 4 else (7 if i < 8 else 4)
 
     def prefix(i, W):
         r = min(i, W)
-        return 9 * min(r, 4) + 7 * min(max(r - 4, 0), 4) + 5 * max(r - 8, 0)
+        return 10 * min(r, 4) + 7 * min(max(r - 4, 0), 4) + 4 * max(r - 8, 0)
 
     def tail(W):  # the last wave of a unit also attends the fp16 tail: a smaller share
         return max(weight(W - 1) - 2, 0)

@@ -32,7 +32,7 @@ def _plan(batch, hkv, hq, msl, n_hi, lo_bit):
 CASES = [
     (20, 16, 32, 200, 32, 2, "page", 3),
     (20, 16, 32, 200, 32, 4, "running", 3),
-    (40, 8, 32, 2060, 13, 2, "page", 12),
+    (33, 8, 32, 3470, 13, 2, "page", 12),
     (24, 16, 64, 660, 100, 4, "page", 4),
     (80, 4, 16, 360, 0, 2, "running", 4),
     (36, 8, 48, 860, 45, 4, "page", 4),
