@@ -401,7 +401,7 @@ void decode_kernel(DecodeParams p) {
   // Pages [0, Pm) of the longest allowed sequence are divided over the page
   // waves in proportion to page_weight (the older waves of a SIMD get more).
   const int Pm = min(p.max_seq_len / kPageTokens, p.max_pages);
-  // (32-bit products: c0 + 9 <= 16 x 84 + 9 and Pm <= 4096)
+  // (32-bit products: c0 + 10 <= 16 x 84 and Pm <= 4096)
   const int tw = tail_weight(W);
   const int wsum = p.n_wg * weight_prefix(W, W) - page_weight(W - 1) + tw;
   const int c0 = (int)blockIdx.x * weight_prefix(W, W) + weight_prefix(wave, W);
