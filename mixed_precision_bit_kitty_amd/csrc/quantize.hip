@@ -72,24 +72,30 @@ __device__ __forceinline__ uint8_t* record_of(const QuantizeParams& p, int b, in
 // Chunk sums in float64, exactly.  For a = k 2^24 (the fixed-point value of
 // one fp16 key, as in accumulate: an integer, |a| < 2^40) split as a = h 2^20
 // + l with h = trunc(a / 2^20) and |h|, |l| < 2^20 (both with a's sign):
-// a^2 = h^2 2^40 + 2 h l 2^20 + l^2, and every sum below stays an integer of
-// magnitude under 2^46 for a lane's 32 terms, so each float64 add and FMA is
-// exact (float64 runs at the float32 vector rate on this part, and the
-// integer form took 64-bit shifts, masks and carries per term).
+// a^2 = h^2 2^40 + 2 h l 2^20 + l^2.  The sums are kept in units that need
+// no per-key scaling: k itself (a = k 2^24), h = trunc(16 k) and
+// r = k - h / 16 (l = r 2^24), so that the float64 values are sum k (a
+// multiple of 2^-24), sum h^2 (an integer), sum h r (a multiple of 2^-24)
+// and sum r^2 (a multiple of 2^-48).  Over a lane's 32 terms each stays
+// below 2^45 of its unit, so every float64 add and FMA is exact, and
+// scaling by 2^24, 2^24 and 2^48 at the end gives the integers sum a,
+// sum h l and sum l^2 (float64 runs at the float32 vector rate on this
+// part, and the integer form took 64-bit shifts, masks and carries per
+// term).
 struct ChunkSums {
-  double s1;  // sum a
+  double s1;  // sum k
   double hh;  // sum h^2
-  double hl;  // sum h l (>= 0: h and l share a's sign)
-  double ll;  // sum l^2
+  double hl;  // sum h r (>= 0: h and r share k's sign)
+  double ll;  // sum r^2
 };
 __device__ __forceinline__ void chunk_add(uint32_t h16, ChunkSums& c) {
-  const double a = (double)(float)__builtin_bit_cast(_Float16, (uint16_t)h16) * 16777216.0;  // exact
-  c.s1 += a;
-  const double h = __builtin_trunc(a * 0x1p-20);
-  const double l = __builtin_fma(h, -1048576.0, a);
+  const double k = (double)(float)__builtin_bit_cast(_Float16, (uint16_t)h16);  // exact
+  c.s1 += k;
+  const double h = __builtin_trunc(k * 16.0);
+  const double r = __builtin_fma(h, -0.0625, k);
   c.hh = __builtin_fma(h, h, c.hh);
-  c.hl = __builtin_fma(h, l, c.hl);
-  c.ll = __builtin_fma(l, l, c.ll);
+  c.hl = __builtin_fma(h, r, c.hl);
+  c.ll = __builtin_fma(r, r, c.ll);
 }
 // an integral float64 of magnitude below 2^53 as int64, exactly
 __device__ __forceinline__ int64_t exact_i64(double x) {
@@ -134,9 +140,9 @@ __global__ __launch_bounds__(256) void key_chunk_kernel(QuantizeParams p) {
   u128 s2[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    s1[e] = exact_i64(acc[e].s1);
-    s2[e] = ((u128)(uint64_t)exact_i64(acc[e].hh) << 40) + ((u128)(uint64_t)exact_i64(acc[e].hl) << 21) +
-            (u128)(uint64_t)exact_i64(acc[e].ll);
+    s1[e] = exact_i64(acc[e].s1 * 0x1p24);
+    s2[e] = ((u128)(uint64_t)exact_i64(acc[e].hh) << 40) + ((u128)(uint64_t)exact_i64(acc[e].hl * 0x1p24) << 21) +
+            (u128)(uint64_t)exact_i64(acc[e].ll * 0x1p48);
     s1[e] += (int64_t)shfl_xor_u64((uint64_t)s1[e], 32);  // the other token group
     const uint64_t lo = shfl_xor_u64((uint64_t)s2[e], 32), hi = shfl_xor_u64((uint64_t)(s2[e] >> 64), 32);
     s2[e] += ((u128)hi << 64) | lo;

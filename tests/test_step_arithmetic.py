@@ -14,8 +14,8 @@ of that step.  The kernels use no division instruction:
 
 The running ranking mode's key statistics kernel sums a = k 2^24 and a^2
 exactly in float64 (a split of a into two halves keeps every term and every
-partial sum an exact float64 integer); the last test checks that against
-Python integers.
+partial sum an exact float64, each a multiple of its own power of two); the
+last test checks that against Python integers.
 
 The first tests check both steps against exact rational arithmetic for
 every input the kernels can meet.  Every operation scales exactly by powers of two while its
@@ -107,22 +107,26 @@ def test_reciprocal_by_one_newton_step_is_correctly_rounded():
 
 def _f64_chunk_sums(h16):
     """The running-mode chunk sums as the key statistics kernel forms them in
-    float64: a = k 2^24, h = trunc(a / 2^20), l = a - h 2^20, then sum a,
-    sum h^2, sum h l and sum l^2 by float64 adds and fused multiply-adds,
-    and the 128-bit s2 = hh 2^40 + hl 2^21 + ll.  numpy's float64 add and
-    multiply round like the kernel's; every product here (below 2^40) and
-    every partial sum (below 2^46) is an exact float64 integer, so the
+    float64: k (the fp16 key), h = trunc(16 k), r = k - h / 16, then sum k,
+    sum h^2, sum h r and sum r^2 by float64 adds and fused multiply-adds,
+    scaled at the end to the integers sum a = 2^24 sum k, sum h l = 2^24
+    sum h r and sum l^2 = 2^48 sum r^2 (a = k 2^24 = h 2^20 + l), and the
+    128-bit s2 = hh 2^40 + hl 2^21 + ll.  numpy's float64 add and multiply
+    round like the kernel's; every product and every partial sum here is
+    an exact float64 (below 2^45 of its unit: 1, 2^-24 or 2^-48), so the
     separate multiply and add below equal the kernel's FMAs."""
-    a = h16.view(np.float16).astype(np.float64) * 2.0 ** 24
-    h = np.trunc(a * 2.0 ** -20)
-    l = a - h * 2.0 ** 20
+    k = h16.view(np.float16).astype(np.float64)
+    h = np.trunc(k * 16.0)
+    r = k - h * 0.0625
     s1 = hh = hl = ll = 0.0
-    for i in range(len(a)):
-        s1 += a[i]
+    for i in range(len(k)):
+        s1 += k[i]
         hh += h[i] * h[i]
-        hl += h[i] * l[i]
-        ll += l[i] * l[i]
-    return int(s1), (int(hh) << 40) + (int(hl) << 21) + int(ll), (h, l)
+        hl += h[i] * r[i]
+        ll += r[i] * r[i]
+    s1, hl, ll = s1 * 2.0 ** 24, hl * 2.0 ** 24, ll * 2.0 ** 48
+    assert s1 == int(s1) and hh == int(hh) and hl == int(hl) and ll == int(ll)
+    return int(s1), (int(hh) << 40) + (int(hl) << 21) + int(ll), (h, r * 2.0 ** 24)
 
 
 def test_running_chunk_sums_in_float64_are_exact():
