@@ -168,50 +168,62 @@ __global__ __launch_bounds__(256) void key_chunk_kernel(QuantizeParams p) {
   }
 }
 
-// grid (Hkv, batch), 2 waves: thread c adds channel c's chunk partials (and
-// the tokens of a chunk without a sealed page), stores the state; wave 0
-// ranks it and stores the mask.
-__global__ __launch_bounds__(128) void key_rank_kernel(QuantizeParams p) {
-  __shared__ int64_t ts1[kHeadDim];
-  __shared__ u128 ts2[kHeadDim];
-  const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x, lane = threadIdx.x & 63;
+// grid (Hkv, batch), 8 waves: thread (part, c) adds channel c's partials
+// of every kRankParts-th run of kRound chunks (part 0 also the tokens of a
+// chunk without a sealed page); the parts' totals meet in LDS, wave 0
+// stores the state, ranks it and stores the mask.
+constexpr int kRankParts = 4;
+__global__ __launch_bounds__(kHeadDim * kRankParts) void key_rank_kernel(QuantizeParams p) {
+  __shared__ int64_t ts1[kRankParts][kHeadDim];
+  __shared__ u128 ts2[kRankParts][kHeadDim];
+  const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x % kHeadDim, part = threadIdx.x / kHeadDim;
+  const int lane = threadIdx.x & 63;
   const int n = prefill_len(p, b);
   if (n < 0) return;  // block-uniform
   const int P = n / kPageTokens;
   int64_t s1 = 0;
   u128 s2 = 0;
   const int chunks = (P + kChunkPages - 1) / kChunkPages;  // chunks with a sealed page
-  for (int j0 = 0; j0 < chunks; j0 += 8) {  // eight chunks per round trip
-    const uint8_t* recs[8];
+  constexpr int kRound = 16;  // chunks per round trip (4096 tokens)
+  for (int j0 = part * kRound; j0 < chunks; j0 += kRankParts * kRound) {
+    const uint8_t* recs[kRound];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) recs[u] = j0 + u < chunks ? record_of(p, b, kChunkPages * (j0 + u), h) : nullptr;
-    int64_t v1[8];
-    uint64_t vlo[8], vhi[8];
+    for (int u = 0; u < kRound; ++u) recs[u] = j0 + u < chunks ? record_of(p, b, kChunkPages * (j0 + u), h) : nullptr;
+    int64_t v1[kRound];
+    uint64_t vlo[kRound], vhi[kRound];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {  // an invalid block table entry: the result is undefined, nothing is read
+    for (int u = 0; u < kRound; ++u) {  // an invalid block table entry: the result is undefined, nothing is read
       v1[u] = recs[u] ? reinterpret_cast<const int64_t*>(recs[u] + kStatsS1)[c] : 0;
       vlo[u] = recs[u] ? reinterpret_cast<const uint64_t*>(recs[u] + kStatsS2Lo)[c] : 0;
       vhi[u] = recs[u] ? reinterpret_cast<const uint64_t*>(recs[u] + kStatsS2Hi)[c] : 0;
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kRound; ++u) {
       s1 += v1[u];
       s2 += ((u128)vhi[u] << 64) | vlo[u];
     }
   }
-  const _Float16* kb = p.k + ((size_t)b * p.n_kv_heads + h) * (size_t)p.S * kHeadDim + c;
-  for (int t = kChunkTokens * chunks; t < n; ++t)  // fewer than 32 tail tokens
-    accumulate(__builtin_bit_cast(uint16_t, kb[(size_t)t * kHeadDim]), s1, s2);
-  ts1[c] = s1;
-  ts2[c] = s2;
+  if (part == 0) {
+    const _Float16* kb = p.k + ((size_t)b * p.n_kv_heads + h) * (size_t)p.S * kHeadDim + c;
+    for (int t = kChunkTokens * chunks; t < n; ++t)  // fewer than 32 tail tokens
+      accumulate(__builtin_bit_cast(uint16_t, kb[(size_t)t * kHeadDim]), s1, s2);
+  }
+  ts1[part][c] = s1;
+  ts2[part][c] = s2;
   __syncthreads();
   uint8_t* st = p.key_stats + ((size_t)b * p.n_kv_heads + h) * kStatsBytes;
   if (threadIdx.x < 64) {
     LaneSums r;
-    r.s1[0] = ts1[2 * lane];
-    r.s1[1] = ts1[2 * lane + 1];
-    r.s2[0] = ts2[2 * lane];
-    r.s2[1] = ts2[2 * lane + 1];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      r.s1[e] = 0;
+      r.s2[e] = 0;
+#pragma unroll
+      for (int q = 0; q < kRankParts; ++q) {
+        r.s1[e] += ts1[q][2 * lane + e];
+        r.s2[e] += ts2[q][2 * lane + e];
+      }
+    }
     store_sums(sums_copy(st, (uint32_t)n), lane, r);
     const RankIn rk = running_rank(r, (uint32_t)n, p.n_hi, lane);
     // mask word m: channel 32m + 2i + j at bit 2i + j, from lanes 16m + i
@@ -327,7 +339,7 @@ hipError_t launch_quantize_t(const QuantizeParams& p, hipStream_t stream) {
   if (p.key_stats) {  // running mode: sums and ranking first, on the same stream
     const int chunks = (p.S / kPageTokens + kChunkPages - 1) / kChunkPages;
     if (chunks > 0) hipLaunchKernelGGL(key_chunk_kernel, dim3(chunks, p.n_kv_heads, p.batch), dim3(256), 0, stream, p);
-    hipLaunchKernelGGL(key_rank_kernel, dim3(p.n_kv_heads, p.batch), dim3(128), 0, stream, p);
+    hipLaunchKernelGGL(key_rank_kernel, dim3(p.n_kv_heads, p.batch), dim3(kHeadDim * kRankParts), 0, stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
