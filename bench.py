@@ -78,9 +78,14 @@ def code_text(text):
     return "\n".join(l for l in lines if l)
 
 
-def source_hash(files=DECODE_SOURCES, read=None):
-    """Hash of the kernel sources' code (comments ignored), naming the
-    kernel build that committed counter summaries were taken on."""
+def source_hash(files=DECODE_SOURCES, read=None, flags=None):
+    """Hash of the kernel sources' code (comments ignored) and of their own
+    compile flags (the build's per-file flags; `flags` maps a file to its
+    flags in place of those), naming the kernel build that committed counter
+    summaries were taken on."""
+    if flags is None:
+        from mixed_precision_bit_kitty_amd import build as kbuild
+        flags = kbuild.SOURCES
     h = hashlib.sha256()
     for f in files:
         if read is None:
@@ -89,6 +94,8 @@ def source_hash(files=DECODE_SOURCES, read=None):
         else:
             text = read(f)
         h.update(code_text(text).encode())
+        if f in flags:
+            h.update(("\0" + " ".join(flags[f])).encode())
     return h.hexdigest()[:16]
 
 

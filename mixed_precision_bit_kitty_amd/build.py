@@ -28,8 +28,10 @@ SOURCES = {
     # finite, so min/max need no NaN-quieting canonicalize of their inputs
     "quantize.hip": ["-ffp-contract=off", "-fno-honor-nans"],
     # inputs are finite: max reductions need no NaN-quieting canonicalize,
-    # which lets the DPP row reductions fold into v_max_f32_dpp
-    "decode.hip": ["-fno-honor-nans"],
+    # which lets the DPP row reductions fold into v_max_f32_dpp; the
+    # scheduler's max-ilp strategy (no spills: 167 of 168 VGPRs) measured
+    # 0.4-6% faster than the default on the decode workloads
+    "decode.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-sched-strategy=max-ilp"],
     "kitty_abi.cpp": ["-x", "hip"],
     # the read-stream ceiling (measurement only)
     "ceiling.hip": [],

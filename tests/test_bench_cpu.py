@@ -23,6 +23,18 @@ def test_code_hash_ignores_comments_only():
     assert bench.source_hash(("a.hip", "b.h"), read=src3.get) != h0
 
 
+def test_code_hash_covers_compile_flags():
+    src = {"a.hip": "int f(int x) { return 2 * x; }\n", "b.h": "#pragma once\n"}
+    h0 = bench.source_hash(("a.hip", "b.h"), read=src.get, flags={"a.hip": ["-O3"]})
+    assert bench.source_hash(("a.hip", "b.h"), read=src.get, flags={"a.hip": ["-O3"]}) == h0
+    assert bench.source_hash(("a.hip", "b.h"), read=src.get, flags={"a.hip": ["-O3", "-mllvm", "-x"]}) != h0
+    # the real hash takes the build's per-file flags of decode.hip
+    from mixed_precision_bit_kitty_amd import build as kbuild
+    other = dict(kbuild.SOURCES)
+    other["decode.hip"] = other["decode.hip"] + ["-DSOMETHING_ELSE"]
+    assert bench.source_hash(bench.DECODE_SOURCES, flags=other) != bench.source_hash(bench.DECODE_SOURCES)
+
+
 def test_committed_traffic_needs_the_same_kernel_code():
     assert bench.committed_traffic("0" * 16, "llama3_8b", "step") is None
     assert bench.committed_traffic(bench.source_hash(bench.DECODE_SOURCES), "no_such_workload", "step") is None
